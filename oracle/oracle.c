@@ -1,0 +1,401 @@
+/*
+ * Draft-correction oracle: a plain, slow, obviously correct CPU implementation
+ * of one corrector pass over a batch of draft blocks.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header or constant with the GPU library and never calls it.
+ *
+ * What it computes, in the order and notation of the DCOCO page ("Contextual
+ * Correction of Parallel Drafts for Speculative Decoding", method details,
+ * steps (1)-(5)):
+ *   (1) per drafted slot, the top-K candidate ids and their drafter logits l;
+ *   (2) b = LN(W_cand E[c]) and g = LN(W_ctx h) with a non-affine LayerNorm,
+ *       z = LN_{gamma,beta}(W_fuse [b; g]) of width r;
+ *   (3) pair state s_p = W_pair [h_p; h_{p+1}], once per adjacent slot pair;
+ *   (4) S_p(a,b) = l_{p+1}(b) + Delta([s_p; z_p^a; z_{p+1}^b; l_p(a); l_{p+1}(b)]),
+ *       Delta a two-layer GELU MLP (3r+2) -> h -> 1;
+ *   (5) the prefix-first walk: slot 1 takes the drafter argmax, then
+ *       k_{p+1} = argmax_b S_p(k_p, b).
+ * The cosine variant (LiLiCorr, section 3.2, Eq. 1) replaces (3)-(4) by
+ *   S_p(a,b) = l_{p+1}(b) + sigma * cos(W_out z_p^a, W_in z_{p+1}^b).
+ *
+ * Readings where the pages are silent (each also listed in the design notes):
+ *   - top-K order is value descending, ties to the lowest token id; values
+ *     compare numerically (-0 == +0, -inf sorts last); NaN is rejected;
+ *   - the walk breaks ties to the lowest candidate index;
+ *   - LayerNorm uses the biased variance over the r features and eps from the
+ *     descriptor; GELU is the exact erf form;
+ *   - the cosine normalises v / max(|v|, 1e-12).
+ *
+ * Precision: every input is read from its stored bits (bfloat16 widened
+ * exactly, or float32); all arithmetic is double precision, with dot products
+ * accumulated in index order.  Parity of every function here is pinned by the
+ * CPU test suite (brute force, closed forms and special cases); nothing here
+ * is "parity unpinned".
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORA_OK = 0, ORA_E_ARG = 1, ORA_E_NAN = 2, ORA_E_NOMEM = 3 };
+enum { ORA_MLP = 0, ORA_COSINE = 1 };
+enum { ORA_BF16 = 0, ORA_F32 = 1 };
+
+typedef struct {
+    int64_t V;
+    int32_t B, K, d, de, r, h, dvec, variant, logits_dtype;
+    double eps, sigma;
+} oracle_desc;
+
+/* Matrices are bfloat16 bit patterns, row-major [out][in]; vectors are float32. */
+typedef struct {
+    const uint16_t *embed, *w_cand, *w_ctx, *w_fuse, *w_pair, *w1, *w_out, *w_in;
+    const float *gamma, *beta, *b1, *w2, *b2;
+} oracle_weights;
+
+static double bf(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static double logit_at(const void *row, int dtype, int64_t v)
+{
+    if (dtype == ORA_BF16) return bf(((const uint16_t *)row)[v]);
+    return (double)((const float *)row)[v];
+}
+
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+int oracle_get_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Number of trainable parameters the MLP corrector reads, from the shapes of
+ * the arrays this file indexes below. */
+int64_t oracle_param_count(const oracle_desc *D)
+{
+    int64_t r = D->r, d = D->d, de = D->de, h = D->h;
+    int64_t n = 0;
+    n += r * de;          /* W_cand */
+    n += r * d;           /* W_ctx */
+    n += r * (2 * r);     /* W_fuse */
+    n += r * (2 * d);     /* W_pair */
+    n += r + r;           /* LN gamma, beta */
+    n += h * (3 * r + 2); /* MLP layer 1 */
+    n += h;               /* b1 */
+    n += h;               /* w2 */
+    n += 1;               /* b2 */
+    return n;
+}
+
+/* ---------------------------------------------------------------- top-K -- */
+
+typedef struct {
+    double v;
+    int32_t id;
+} cand_t;
+
+/* Value descending, then token id ascending: a total order on distinct ids,
+ * so a full sort gives the same result as a stable sort by value. */
+static int cand_cmp(const void *pa, const void *pb)
+{
+    const cand_t *a = (const cand_t *)pa, *b = (const cand_t *)pb;
+    if (a->v > b->v) return -1;
+    if (a->v < b->v) return 1;
+    return (a->id > b->id) - (a->id < b->id);
+}
+
+/* Step (1): the K largest logits of one slot row, full sort of the row. */
+int oracle_topk_row(const void *row, int dtype, int64_t V, int32_t K,
+                    int32_t *ids, double *vals)
+{
+    if (!row || !ids || !vals || V <= 0 || K <= 0 || K > V) return ORA_E_ARG;
+    cand_t *c = (cand_t *)malloc(sizeof(cand_t) * (size_t)V);
+    if (!c) return ORA_E_NOMEM;
+    for (int64_t v = 0; v < V; ++v) {
+        double x = logit_at(row, dtype, v);
+        if (isnan(x)) {
+            free(c);
+            return ORA_E_NAN;
+        }
+        c[v].v = x;
+        c[v].id = (int32_t)v;
+    }
+    qsort(c, (size_t)V, sizeof(cand_t), cand_cmp);
+    for (int32_t k = 0; k < K; ++k) {
+        ids[k] = c[k].id;
+        vals[k] = c[k].v;
+    }
+    free(c);
+    return ORA_OK;
+}
+
+/* Top-K of every drafted slot of n blocks.  Row (i, s) starts at
+ * logits + i*req_stride + s*slot_stride elements (the caller skips the anchor).
+ * ids/vals are [n][B][K]. */
+int oracle_topk(const oracle_desc *D, int32_t n, const void *logits,
+                int64_t req_stride, int64_t slot_stride, int32_t *ids, double *vals)
+{
+    if (!D || !logits || !ids || !vals || n < 0) return ORA_E_ARG;
+    const size_t esz = D->logits_dtype == ORA_BF16 ? 2 : 4;
+    int err = ORA_OK;
+#pragma omp parallel for schedule(dynamic) reduction(| : err)
+    for (int64_t t = 0; t < (int64_t)n * D->B; ++t) {
+        int64_t i = t / D->B, s = t % D->B;
+        const char *row = (const char *)logits + (size_t)(i * req_stride + s * slot_stride) * esz;
+        err |= oracle_topk_row(row, D->logits_dtype, D->V, D->K,
+                               ids + t * D->K, vals + t * D->K);
+    }
+    return err;
+}
+
+/* ------------------------------------------------------- dense helpers -- */
+
+/* y[o] = sum_i W[o][i] x[i] for a bfloat16 matrix with row stride ld. */
+static void matvec_bf(const uint16_t *W, int64_t ld, int rows, int cols,
+                      const double *x, double *y)
+{
+    for (int o = 0; o < rows; ++o) {
+        double acc = 0.0;
+        const uint16_t *w = W + (size_t)o * ld;
+        for (int i = 0; i < cols; ++i) acc += bf(w[i]) * x[i];
+        y[o] = acc;
+    }
+}
+
+/* LayerNorm over m features: (x - mean) / sqrt(var + eps), biased variance;
+ * then gamma * . + beta when gamma is given. */
+void oracle_layernorm(double *x, int m, double eps, const float *gamma, const float *beta)
+{
+    double mean = 0.0, var = 0.0;
+    for (int i = 0; i < m; ++i) mean += x[i];
+    mean /= m;
+    for (int i = 0; i < m; ++i) var += (x[i] - mean) * (x[i] - mean);
+    var /= m;
+    double inv = 1.0 / sqrt(var + eps);
+    for (int i = 0; i < m; ++i) {
+        double y = (x[i] - mean) * inv;
+        if (gamma) y = (double)gamma[i] * y + (double)beta[i];
+        x[i] = y;
+    }
+}
+
+/* GELU(t) = t * Phi(t) = 0.5 t (1 + erf(t / sqrt 2)). */
+double oracle_gelu(double t)
+{
+    return 0.5 * t * (1.0 + erf(t / sqrt(2.0)));
+}
+
+/* ------------------------------------------------ steps (2) and (3) -- */
+
+/* For every block i and drafted slot s (0-based; slot s is the page's slot s+1):
+ *   b[i][s][k] = LN(W_cand E[ids[i][s][k]])            [n][B][K][r]
+ *   g[i][s]    = LN(W_ctx h_s)                          [n][B][r]
+ *   z[i][s][k] = gamma * LN(W_fuse [b; g]) + beta       [n][B][K][r]
+ *   s[i][p]    = W_pair [h_p; h_{p+1}], p = 0..B-2      [n][B-1][r]
+ * Hidden row (i, s) starts at hidden + i*h_req_stride + s*h_slot_stride.
+ * Any output pointer may be NULL. */
+int oracle_represent(const oracle_desc *D, const oracle_weights *W, int32_t n,
+                     const int32_t *ids, const uint16_t *hidden,
+                     int64_t h_req_stride, int64_t h_slot_stride,
+                     double *b_out, double *g_out, double *z_out, double *s_out)
+{
+    if (!D || !W || !ids || !hidden || n < 0) return ORA_E_ARG;
+    const int B = D->B, K = D->K, r = D->r, d = D->d, de = D->de;
+    int err = ORA_OK;
+#pragma omp parallel for schedule(dynamic) reduction(| : err)
+    for (int64_t t = 0; t < (int64_t)n * B; ++t) {
+        int64_t i = t / B, s = t % B;
+        double *x = (double *)malloc(sizeof(double) * (size_t)(2 * (d > de ? d : de) + 3 * r));
+        if (!x) {
+            err |= ORA_E_NOMEM;
+            continue;
+        }
+        double *hx = x;                         /* [h_s; h_{s+1}], later E[c] */
+        double *bg = x + 2 * (d > de ? d : de); /* [b; g] */
+        double *u = bg + 2 * r;                 /* W_fuse [b; g], then z */
+
+        const uint16_t *hs = hidden + (size_t)(i * h_req_stride + s * h_slot_stride);
+        for (int j = 0; j < d; ++j) hx[j] = bf(hs[j]);
+
+        /* g = LN(W_ctx h) */
+        double *g = bg + r;
+        matvec_bf(W->w_ctx, d, r, d, hx, g);
+        oracle_layernorm(g, r, D->eps, NULL, NULL);
+        if (g_out)
+            for (int j = 0; j < r; ++j) g_out[(size_t)t * r + j] = g[j];
+
+        /* s_p = W_pair [h_p; h_{p+1}] for the pair that starts at this slot */
+        if (s + 1 < B && s_out) {
+            const uint16_t *hn = hs + h_slot_stride;
+            for (int j = 0; j < d; ++j) hx[d + j] = bf(hn[j]);
+            double *sp = s_out + ((size_t)i * (B - 1) + s) * r;
+            matvec_bf(W->w_pair, 2 * (int64_t)d, r, 2 * d, hx, sp);
+        }
+
+        for (int k = 0; k < K; ++k) {
+            int32_t tok = ids[t * K + k];
+            if (tok < 0 || tok >= D->V) {
+                err |= ORA_E_ARG;
+                break;
+            }
+            const uint16_t *e = W->embed + (size_t)tok * de;
+            for (int j = 0; j < de; ++j) hx[j] = bf(e[j]);
+            /* b = LN(W_cand e) */
+            double *b = bg;
+            matvec_bf(W->w_cand, de, r, de, hx, b);
+            oracle_layernorm(b, r, D->eps, NULL, NULL);
+            if (b_out)
+                for (int j = 0; j < r; ++j) b_out[((size_t)t * K + k) * r + j] = b[j];
+            /* z = LN_{gamma,beta}(W_fuse [b; g]) */
+            matvec_bf(W->w_fuse, 2 * r, r, 2 * r, bg, u);
+            oracle_layernorm(u, r, D->eps, W->gamma, W->beta);
+            if (z_out)
+                for (int j = 0; j < r; ++j) z_out[((size_t)t * K + k) * r + j] = u[j];
+        }
+        free(x);
+    }
+    return err;
+}
+
+/* ---------------------------------------------------------- step (4) -- */
+
+/* Transition scores for every block i, pair p = 0..B-2 (slots p and p+1),
+ * predecessor candidate a and successor candidate b:
+ *   MLP:    delta = w2 . GELU(W1 x + b1) + b2,
+ *           x = [s_p; z_p^a; z_{p+1}^b; l_p(a); l_{p+1}(b)]
+ *   COSINE: delta = sigma * <o_p^a, i_{p+1}^b>, o = unit(W_out z), i = unit(W_in z)
+ *   S = l_{p+1}(b) + delta.
+ * vals [n][B][K], z [n][B][K][r], s [n][B-1][r] (MLP only);
+ * delta and scores are [n][B-1][K][K] indexed [i][p][a][b]; either may be NULL. */
+int oracle_score(const oracle_desc *D, const oracle_weights *W, int32_t n,
+                 const double *vals, const double *z, const double *s,
+                 double *delta_out, double *scores_out)
+{
+    if (!D || !W || !vals || !z || n < 0) return ORA_E_ARG;
+    const int B = D->B, K = D->K, r = D->r, h = D->h, dv = D->dvec;
+    if (D->variant == ORA_MLP && !s) return ORA_E_ARG;
+    const int nin = 3 * r + 2;
+    int err = ORA_OK;
+#pragma omp parallel for schedule(dynamic) reduction(| : err)
+    for (int64_t t = 0; t < (int64_t)n * (B - 1); ++t) {
+        int64_t i = t / (B - 1), p = t % (B - 1);
+        const double *zp = z + ((size_t)i * B + p) * K * r;
+        const double *zq = z + ((size_t)i * B + p + 1) * K * r;
+        const double *lp = vals + ((size_t)i * B + p) * K;
+        const double *lq = vals + ((size_t)i * B + p + 1) * K;
+        double *buf = (double *)malloc(sizeof(double) * (size_t)(nin + h + 2 * K * (dv > 0 ? dv : 1)));
+        if (!buf) {
+            err |= ORA_E_NOMEM;
+            continue;
+        }
+        double *x = buf, *u = buf + nin;
+        double *ov = u + h, *iv = ov + (size_t)K * (dv > 0 ? dv : 1);
+        if (D->variant == ORA_COSINE) {
+            for (int k = 0; k < K; ++k) {
+                matvec_bf(W->w_out, r, dv, r, zp + (size_t)k * r, ov + (size_t)k * dv);
+                matvec_bf(W->w_in, r, dv, r, zq + (size_t)k * r, iv + (size_t)k * dv);
+                double no = 0.0, ni = 0.0;
+                for (int j = 0; j < dv; ++j) {
+                    no += ov[(size_t)k * dv + j] * ov[(size_t)k * dv + j];
+                    ni += iv[(size_t)k * dv + j] * iv[(size_t)k * dv + j];
+                }
+                no = fmax(sqrt(no), 1e-12);
+                ni = fmax(sqrt(ni), 1e-12);
+                for (int j = 0; j < dv; ++j) {
+                    ov[(size_t)k * dv + j] /= no;
+                    iv[(size_t)k * dv + j] /= ni;
+                }
+            }
+        }
+        for (int a = 0; a < K; ++a) {
+            for (int b = 0; b < K; ++b) {
+                double delta;
+                if (D->variant == ORA_MLP) {
+                    const double *sp = s + ((size_t)i * (B - 1) + p) * r;
+                    for (int j = 0; j < r; ++j) x[j] = sp[j];
+                    for (int j = 0; j < r; ++j) x[r + j] = zp[(size_t)a * r + j];
+                    for (int j = 0; j < r; ++j) x[2 * r + j] = zq[(size_t)b * r + j];
+                    x[3 * r] = lp[a];
+                    x[3 * r + 1] = lq[b];
+                    matvec_bf(W->w1, nin, h, nin, x, u);
+                    delta = 0.0;
+                    for (int j = 0; j < h; ++j)
+                        delta += (double)W->w2[j] * oracle_gelu(u[j] + (double)W->b1[j]);
+                    delta += (double)W->b2[0];
+                } else {
+                    double c = 0.0;
+                    for (int j = 0; j < dv; ++j) c += ov[(size_t)a * dv + j] * iv[(size_t)b * dv + j];
+                    delta = D->sigma * c;
+                }
+                size_t o = (((size_t)i * (B - 1) + p) * K + a) * K + b;
+                if (delta_out) delta_out[o] = delta;
+                if (scores_out) scores_out[o] = lq[b] + delta;
+            }
+        }
+        free(buf);
+    }
+    return err;
+}
+
+/* ---------------------------------------------------------- step (5) -- */
+
+/* Prefix-first walk.  choice[i][0] = 0 (rank 0 is the drafter argmax of slot 1);
+ * choice[i][p+1] = smallest b attaining max_b S[i][p][choice[i][p]][b];
+ * tokens[i][s] = ids[i][s][choice[i][s]].  scores [n][B-1][K][K]. */
+int oracle_walk(const oracle_desc *D, int32_t n, const double *scores, const int32_t *ids,
+                int32_t *tokens, int32_t *choice)
+{
+    if (!D || !scores || !ids || !tokens || !choice || n < 0) return ORA_E_ARG;
+    const int B = D->B, K = D->K;
+    for (int32_t i = 0; i < n; ++i) {
+        int32_t k = 0;
+        choice[(size_t)i * B] = 0;
+        for (int p = 0; p + 1 < B; ++p) {
+            const double *row = scores + ((((size_t)i * (B - 1) + p) * K) + k) * K;
+            int32_t best = 0;
+            for (int b = 1; b < K; ++b)
+                if (row[b] > row[best]) best = b;
+            k = best;
+            choice[(size_t)i * B + p + 1] = k;
+        }
+        for (int sl = 0; sl < B; ++sl)
+            tokens[(size_t)i * B + sl] = ids[((size_t)i * B + sl) * K + choice[(size_t)i * B + sl]];
+    }
+    return ORA_OK;
+}
+
+/* Length of the accepted prefix under a greedy verifier (Faster Decoding,
+ * "Greedy verification"): the number of leading slots whose proposed token
+ * equals the target token. accepted[i] in [0, B]. */
+int oracle_accepted(int32_t n, int32_t B, const int32_t *tokens, const int32_t *targets,
+                    int32_t *accepted)
+{
+    if (!tokens || !targets || !accepted || n < 0 || B < 0) return ORA_E_ARG;
+    for (int32_t i = 0; i < n; ++i) {
+        int32_t a = 0;
+        while (a < B && tokens[(size_t)i * B + a] == targets[(size_t)i * B + a]) ++a;
+        accepted[i] = a;
+    }
+    return ORA_OK;
+}

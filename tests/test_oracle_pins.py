@@ -1,0 +1,399 @@
+"""Pins of the CPU oracle to things other than itself.
+
+Each test checks the oracle against what the pages or the mathematics fix:
+library routines on special cases (NumPy lexsort, torch CPU linear /
+layer_norm / gelu / normalize in float64), brute force on tiny inputs, closed
+forms, invariants, and the numbers the pages print.  A plausible mistake in
+the oracle (a dropped term, a swapped concatenation block, a wrong sign, a
+transposed operand, a reversed tie rule) fails at least one of them.
+"""
+
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from workload import bf16_bits_to_f32, config, f32_to_bf16_bits, gen_inputs, gen_targets
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _t(bits):
+    """bfloat16 bits -> float64 torch tensor."""
+    return torch.from_numpy(bf16_bits_to_f32(bits).astype(np.float64).reshape(np.shape(bits)))
+
+
+def _lexsort_topk(values, K):
+    values = np.asarray(values, dtype=np.float64)
+    ids = np.arange(values.size)
+    order = np.lexsort((ids, -values))  # value descending, then id ascending
+    return order[:K].astype(np.int32), values[order[:K]]
+
+
+# ----------------------------------------------------------------- counts --
+
+def test_param_count_matches_page():
+    g = _golden("dcoco_counts.json")
+    q = g["qwen3_8b"]
+    desc = oracle.OracleDesc(V=151936, B=q["B"], K=q["K"], d=q["d"], de=q["de"], r=q["r"],
+                             h=q["h"], dvec=128)
+    assert oracle.param_count(desc) == g["param_count"]
+    assert 3 * q["r"] + 2 == g["mlp_input_width"]
+
+
+def test_transition_and_node_counts():
+    g = _golden("dcoco_counts.json")
+    cfg = config("tiny", B=g["qwen3_8b"]["B"], K=g["qwen3_8b"]["K"], V=200)
+    x = gen_inputs(cfg)
+    r = oracle.run(cfg, x)
+    assert r["ids"][0].size == g["nodes_per_block"]
+    assert r["scores"][0].size == g["transitions_per_block"]
+
+
+def test_every_parameter_tensor_is_used():
+    """Perturbing any single parameter tensor changes the scores: no term dropped."""
+    cfg = config("tiny")
+    x = gen_inputs(cfg)
+    base = oracle.run(cfg, x)["scores"]
+    for name in ("w_cand", "w_ctx", "w_fuse", "w_pair", "w1", "ln_gamma", "ln_beta",
+                 "b1", "w2", "b2"):
+        y = dict(x)
+        w = {k: v.copy() for k, v in x["weights"].items()}
+        if w[name].dtype == np.uint16:
+            f = bf16_bits_to_f32(w[name]).reshape(w[name].shape) * np.float32(1.5)
+            w[name] = f32_to_bf16_bits(f).reshape(w[name].shape)
+        else:
+            w[name] = (w[name] * np.float32(1.5) + np.float32(0.05)).astype(np.float32)
+        y["weights"] = w
+        assert not np.allclose(oracle.run(cfg, y)["scores"], base, rtol=0, atol=1e-9), name
+    # the embedding table and the hidden states feed the scores too
+    y = dict(x)
+    y["hidden"] = x["hidden"].copy()
+    y["hidden"][0, 2, 5] ^= 0x0100
+    assert not np.allclose(oracle.run(cfg, y)["scores"], base, rtol=0, atol=1e-9)
+
+
+# ----------------------------------------------------------------- top-K --
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_topk_matches_lexsort(dtype):
+    g = np.random.default_rng(7)
+    for trial in range(40):
+        V = int(g.integers(1, 300))
+        K = int(g.integers(1, V + 1))
+        if trial % 3 == 0:
+            vals = g.integers(-3, 4, size=V).astype(np.float32)   # many ties
+        else:
+            vals = g.normal(size=V).astype(np.float32)
+        if dtype == "bf16":
+            row = f32_to_bf16_bits(vals)
+            ref_vals = bf16_bits_to_f32(row)
+        else:
+            row, ref_vals = vals, vals
+        ids, got = oracle.topk_row(row, K)
+        eids, evals = _lexsort_topk(ref_vals, K)
+        np.testing.assert_array_equal(ids, eids)
+        np.testing.assert_array_equal(got, evals)
+
+
+def test_topk_signed_zero_and_inf():
+    # -0 == +0 numerically, so they tie and order by id; -inf sorts last.
+    row = np.array([-0.0, 0.0, -np.inf, -1.0, 0.0, -0.0, -np.inf, np.inf], np.float32)
+    ids, vals = oracle.topk_row(row, 8)
+    assert ids.tolist() == [7, 0, 1, 4, 5, 3, 2, 6]
+    bits = f32_to_bf16_bits(row)
+    ids2, _ = oracle.topk_row(bits, 8)
+    assert ids2.tolist() == [7, 0, 1, 4, 5, 3, 2, 6]
+
+
+def test_topk_k_equals_v_is_a_full_sort():
+    g = np.random.default_rng(3)
+    row = g.normal(size=50).astype(np.float32)
+    ids, vals = oracle.topk_row(row, 50)
+    assert sorted(ids.tolist()) == list(range(50))
+    assert np.all(np.diff(vals) <= 0)
+
+
+def test_topk_rejects_nan():
+    row = np.array([1.0, np.nan, 0.0], np.float32)
+    with pytest.raises(RuntimeError):
+        oracle.topk_row(row, 2)
+
+
+def test_topk_permutation_equivariance():
+    g = np.random.default_rng(11)
+    row = g.normal(size=500).astype(np.float32)   # distinct values: no ties
+    perm = g.permutation(500)
+    ids, vals = oracle.topk_row(row, 10)
+    pid, pvals = oracle.topk_row(row[perm], 10)
+    np.testing.assert_array_equal(perm[pid], ids)
+    np.testing.assert_array_equal(vals, pvals)
+
+
+def test_topk_skips_anchor_rows():
+    cfg = config("tiny")
+    x = gen_inputs(cfg)
+    a = oracle.run(cfg, x)
+    y = dict(x)
+    y["logits"] = x["logits"].copy()
+    y["logits"][:, 0, :] = -5.0
+    y["hidden"] = x["hidden"].copy()
+    y["hidden"][:, 0, :] = 0
+    b = oracle.run(cfg, y)
+    for k in ("ids", "scores", "tokens"):
+        np.testing.assert_array_equal(a[k], b[k])
+
+
+# ------------------------------------------------------ LayerNorm / GELU --
+
+def test_layernorm_matches_torch_and_invariants():
+    g = np.random.default_rng(5)
+    for m in (4, 16, 128):
+        x = g.normal(size=m) * 3 + 1
+        eps = 1e-5
+        y = oracle.layernorm(x, eps)
+        ref = F.layer_norm(torch.from_numpy(x), (m,), eps=eps).numpy()
+        np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+        v = x.var()
+        assert abs(y.mean()) < 1e-12
+        assert abs(y.var() - v / (v + eps)) < 1e-12
+        np.testing.assert_allclose(oracle.layernorm(x + 7.5, eps), y, atol=1e-10)
+        np.testing.assert_allclose(oracle.layernorm(1e4 * x, 0.0), oracle.layernorm(x, 0.0), atol=1e-10)
+        gam = g.normal(size=m).astype(np.float32)
+        bet = g.normal(size=m).astype(np.float32)
+        ya = oracle.layernorm(x, eps, gam, bet)
+        refa = F.layer_norm(torch.from_numpy(x), (m,), torch.from_numpy(gam.astype(np.float64)),
+                            torch.from_numpy(bet.astype(np.float64)), eps=eps).numpy()
+        np.testing.assert_allclose(ya, refa, rtol=1e-12, atol=1e-12)
+
+
+def test_gelu_exact_erf_form():
+    ts = np.linspace(-8, 8, 161)
+    ref = F.gelu(torch.from_numpy(ts), approximate="none").numpy()
+    got = np.array([oracle.gelu(t) for t in ts])
+    np.testing.assert_allclose(got, ref, rtol=1e-14, atol=1e-15)
+    assert oracle.gelu(0.0) == 0.0
+    for t in ts:
+        assert abs(oracle.gelu(t) - oracle.gelu(-t) - t) < 1e-14
+
+
+# ------------------------------------------- projections and the MLP head --
+
+def _torch_reference(cfg, x, r_or):
+    """Steps (2)-(4) with torch CPU library calls in float64, on the oracle's ids."""
+    w = x["weights"]
+    B, K, r = cfg["B"], cfg["K"], cfg["r"]
+    ids = torch.from_numpy(r_or["ids"][0].astype(np.int64))            # [B][K]
+    l = torch.from_numpy(r_or["vals"][0])                              # [B][K]
+    h = _t(x["hidden"][0, 1:])                                         # [B][d]
+    E = _t(x["embed"])
+    b = F.layer_norm(F.linear(E[ids.reshape(-1)], _t(w["w_cand"])), (r,), eps=cfg["ln_eps"]).reshape(B, K, r)
+    g = F.layer_norm(F.linear(h, _t(w["w_ctx"])), (r,), eps=cfg["ln_eps"])          # [B][r]
+    bg = torch.cat([b, g[:, None, :].expand(B, K, r)], dim=-1)
+    gam = torch.from_numpy(w["ln_gamma"].astype(np.float64))
+    bet = torch.from_numpy(w["ln_beta"].astype(np.float64))
+    z = F.layer_norm(F.linear(bg, _t(w["w_fuse"])), (r,), gam, bet, eps=cfg["ln_eps"])
+    s = F.linear(torch.cat([h[:-1], h[1:]], dim=-1), _t(w["w_pair"]))                 # [B-1][r]
+    return dict(b=b, g=g, z=z, s=s, l=l)
+
+
+def test_represent_matches_torch_linear_layernorm():
+    cfg = config("tiny")
+    x = gen_inputs(cfg)
+    r = oracle.run(cfg, x)
+    ref = _torch_reference(cfg, x, r)
+    for k in ("b", "g", "z", "s"):
+        np.testing.assert_allclose(r[k][0], ref[k].numpy(), rtol=1e-10, atol=1e-10, err_msg=k)
+
+
+@pytest.mark.parametrize("head", ["normal", "stress"])
+def test_mlp_scores_match_torch(head):
+    cfg = config("tiny")
+    x = gen_inputs(cfg, head=head)
+    r = oracle.run(cfg, x)
+    ref = _torch_reference(cfg, x, r)
+    w = x["weights"]
+    B, K, r_ = cfg["B"], cfg["K"], cfg["r"]
+    z, s, l = ref["z"], ref["s"], ref["l"]
+    S = np.empty((B - 1, K, K))
+    for p in range(B - 1):
+        xin = torch.cat([
+            s[p][None, None, :].expand(K, K, r_),
+            z[p][:, None, :].expand(K, K, r_),
+            z[p + 1][None, :, :].expand(K, K, r_),
+            l[p][:, None, None].expand(K, K, 1),
+            l[p + 1][None, :, None].expand(K, K, 1),
+        ], dim=-1)
+        hid = F.gelu(F.linear(xin, _t(w["w1"]), torch.from_numpy(w["b1"].astype(np.float64))))
+        delta = F.linear(hid, torch.from_numpy(w["w2"].astype(np.float64))[None, :],
+                         torch.from_numpy(w["b2"].astype(np.float64)))[..., 0]
+        S[p] = (l[p + 1][None, :] + delta).numpy()
+    np.testing.assert_allclose(r["scores"][0], S, rtol=1e-10, atol=1e-10)
+
+
+def _only_block(w1, r, block):
+    """Zero W1 outside one input block (s, z_a, z_b, l_a or l_b)."""
+    cols = {"s": slice(0, r), "za": slice(r, 2 * r), "zb": slice(2 * r, 3 * r),
+            "la": slice(3 * r, 3 * r + 1), "lb": slice(3 * r + 1, 3 * r + 2)}[block]
+    out = np.zeros_like(w1)
+    out[:, cols] = w1[:, cols]
+    return out
+
+
+@pytest.mark.parametrize("block", ["s", "za", "zb", "la", "lb"])
+def test_mlp_concatenation_order(block):
+    """With W1 restricted to one input block, delta depends on exactly the
+    inputs the page puts in that block: s_p alone gives a constant per pair,
+    z_p^a / l_p(a) vary only with a, z_{p+1}^b / l_{p+1}(b) only with b."""
+    cfg = config("tiny")
+    x = gen_inputs(cfg, head="stress")
+    x["weights"]["w1"] = _only_block(x["weights"]["w1"], cfg["r"], block)
+    r = oracle.run(cfg, x)
+    d = r["delta"][0]                                   # [p][a][b]
+    varies_a = np.ptp(d, axis=1).max() > 1e-9
+    varies_b = np.ptp(d, axis=2).max() > 1e-9
+    expect = {"s": (False, False), "za": (True, False), "la": (True, False),
+              "zb": (False, True), "lb": (False, True)}[block]
+    assert (varies_a, varies_b) == expect
+    if block in ("la", "lb"):
+        # closed form: delta = sum_j w2_j GELU(b1_j + W1[j][c] * l) + b2
+        w = x["weights"]
+        c = 3 * cfg["r"] + (0 if block == "la" else 1)
+        col = bf16_bits_to_f32(x["weights"]["w1"][:, c]).astype(np.float64)
+        for p in range(cfg["B"] - 1):
+            for k in range(cfg["K"]):
+                lv = r["vals"][0, p if block == "la" else p + 1, k]
+                pre = torch.from_numpy(w["b1"].astype(np.float64) + col * lv)
+                want = float((torch.from_numpy(w["w2"].astype(np.float64)) * F.gelu(pre)).sum()) + float(w["b2"][0])
+                got = d[p, k, 0] if block == "la" else d[p, 0, k]
+                assert abs(got - want) < 1e-10
+
+
+def test_zero_initialised_output_layer_reproduces_drafter_argmax():
+    """DCOCO: with the MLP output layer zero-initialised every S_p(a,b) equals the
+    successor logit, so the walk returns the drafter's own per-slot argmax."""
+    for name in ("tiny",):
+        cfg = config(name)
+        x = gen_inputs(cfg, head="zero")
+        r = oracle.run(cfg, x)
+        B, K = cfg["B"], cfg["K"]
+        want = np.broadcast_to(r["vals"][:, 1:, None, :], r["scores"].shape)
+        assert np.array_equal(r["scores"], want)
+        assert (r["choice"] == 0).all()
+        lg = x["logits"][0, 1:]
+        np.testing.assert_array_equal(r["tokens"][0], np.argmax(lg, axis=1))
+    # b2 = c shifts every score of a row equally: same walk
+    x = gen_inputs(config("tiny"), head="zero")
+    x["weights"]["b2"] = np.array([3.25], np.float32)
+    r2 = oracle.run(config("tiny"), x)
+    assert (r2["choice"] == 0).all()
+
+
+# -------------------------------------------------------------- the walk --
+
+def _brute_force_walk(S, K):
+    """Among all K^(B-1) paths that start at rank 0, the prefix-first rule picks
+    the one that is lexicographically best on (score of step 1, then step 2, ...),
+    each tie going to the lower candidate index."""
+    Bm1 = S.shape[0]
+    best_key, best = None, None
+    for tail in itertools.product(range(K), repeat=Bm1):
+        path = (0,) + tail
+        key = []
+        for p in range(Bm1):
+            key += [-S[p, path[p], path[p + 1]], path[p + 1]]
+        key = tuple(key)
+        if best_key is None or key < best_key:
+            best_key, best = key, path
+    return np.array(best)
+
+
+def test_walk_matches_brute_force():
+    g = np.random.default_rng(2)
+    for trial in range(30):
+        B, K = int(g.integers(2, 6)), int(g.integers(1, 4))
+        S = g.integers(-2, 3, size=(1, B - 1, K, K)).astype(np.float64)  # many ties
+        if trial % 2:
+            S = g.normal(size=(1, B - 1, K, K))
+        ids = g.integers(0, 100, size=(1, B, K)).astype(np.int32)
+        desc = oracle.OracleDesc(V=100, B=B, K=K, d=32, de=32, r=16, h=16, dvec=16)
+        tokens, choice = oracle.walk(desc, S, ids, 1)
+        want = _brute_force_walk(S[0], K)
+        np.testing.assert_array_equal(choice[0], want)
+        np.testing.assert_array_equal(tokens[0], ids[0, np.arange(B), want])
+
+
+# -------------------------------------------------------- cosine variant --
+
+def test_cosine_scores_match_torch_and_bound():
+    for sigma in (1.0, 8.0):
+        cfg = config("tiny", variant="cosine", sigma=sigma)
+        x = gen_inputs(cfg)
+        r = oracle.run(cfg, x)
+        ref = _torch_reference(cfg, x, r)
+        w = x["weights"]
+        z, l = ref["z"], ref["l"]
+        o = F.normalize(F.linear(z, _t(w["w_out"])), dim=-1, eps=1e-12)
+        i = F.normalize(F.linear(z, _t(w["w_in"])), dim=-1, eps=1e-12)
+        S = l[1:, None, :] + sigma * torch.matmul(o[:-1], i[1:].transpose(1, 2))
+        np.testing.assert_allclose(r["scores"][0], S.numpy(), rtol=1e-10, atol=1e-10)
+        assert np.all(np.abs(r["scores"] - r["vals"][:, 1:, None, :]) <= sigma + 1e-12)
+
+
+def test_cosine_identical_slots_reach_sigma():
+    """With W_in = W_out and two identical slots (same hidden state, same
+    candidates), the out and in vectors of a candidate coincide: cos = 1."""
+    cfg = config("tiny", variant="cosine", sigma=8.0)
+    x = gen_inputs(cfg)
+    x["weights"]["w_in"] = x["weights"]["w_out"].copy()
+    x["logits"] = x["logits"].copy()
+    x["hidden"] = x["hidden"].copy()
+    x["logits"][0, 2] = x["logits"][0, 1]
+    x["hidden"][0, 2] = x["hidden"][0, 1]
+    r = oracle.run(cfg, x)
+    for a in range(cfg["K"]):
+        assert abs(r["scores"][0, 0, a, a] - r["vals"][0, 1, a] - 8.0) < 1e-12
+
+
+# ----------------------------------------------------------------- yield --
+
+def test_yield_worked_example():
+    g = _golden("yield_example.json")
+    np.testing.assert_allclose(oracle.survival(g["conditional"]), g["survival"], rtol=1e-15)
+    assert abs(oracle.expected_yield(g["conditional"]) - g["expected_yield"]) < 1e-12
+    alpha = sum(g["conditional"]) / len(g["conditional"])
+    assert abs(alpha - g["alpha"]) < 1e-15
+    assert abs(oracle.iid_expected_yield(alpha, len(g["conditional"])) - g["iid_expected_yield"]) < 1e-12
+    for a in (0.1, 0.5, 0.9):
+        for gam in (1, 4, 15):
+            assert abs(oracle.iid_expected_yield(a, gam) - (1 - a ** (gam + 1)) / (1 - a)) < 1e-12
+    assert oracle.iid_expected_yield(1.0, 15) == 16.0
+
+
+def test_yield_tail_sum_identity_on_walks():
+    """Sum over blocks of Y = A + 1 equals n + sum_k #{A >= k}: E[Y] = 1 + sum_k s_k
+    holds exactly on any sample (mixed accepted-prefix lengths in one batch)."""
+    cfg = config("tiny", n=64, B=15, K=4, V=300)
+    x = gen_inputs(cfg, head="stress")
+    r = oracle.run(cfg, x)
+    codes = gen_targets(cfg)
+    B = cfg["B"]
+    targets = np.where(codes >= 0, np.take_along_axis(r["ids"], np.maximum(codes, 0)[..., None], 2)[..., 0], -1)
+    A = oracle.accepted_lengths(r["tokens"], targets)
+    assert len(set(A.tolist())) > 2
+    n = A.size
+    lhs = int((A + 1).sum())
+    rhs = n + sum(int((A >= k).sum()) for k in range(1, B + 1))
+    assert lhs == rhs
+    s_k = [float((A >= k).mean()) for k in range(1, B + 1)]
+    assert abs(float((A + 1).mean()) - (1 + sum(s_k))) < 1e-12
