@@ -1,0 +1,416 @@
+// C-ABI of the corrector library: handle, validation, workspace carving and
+// launch sequencing.  Every argument is checked on the host before anything is
+// enqueued, so a call that returns an error has launched nothing.  The library
+// never allocates device memory and never synchronises (except
+// corrector_kernel_times, which waits for timing events by design).
+#include <math.h>
+#include <new>
+#include <string.h>
+
+#include "../../include/corrector.h"
+#include "kernels.h"
+
+using namespace corr;
+
+namespace {
+
+constexpr uint32_t kMagic = 0xC0FFEE17u;
+constexpr uint32_t kDead = 0xDEADDEADu;
+constexpr int kMaxKernels = 8;
+constexpr size_t kAlign = 256;
+
+struct Layout {
+    size_t part_key, part_id, ids, vals, hproj, z, g, s, vout, vin, scores, total;
+    int chunks, splits;
+};
+
+}  // namespace
+
+struct corrector {
+    uint32_t magic;
+    corrector_desc d;
+    corrector_weights w;
+    bool timing;
+    bool events_ready;
+    hipEvent_t ev[2 * kMaxKernels];
+    const char* names[kMaxKernels];
+    int nk;
+};
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int logits_elem_bytes(const corrector_desc& d) { return d.logits_dtype == CORR_DTYPE_BF16 ? 2 : 4; }
+
+// Split of the hidden-width reduction of hproj: a function of d only, so a
+// request's results do not depend on how many requests share the call.
+int choose_splits(const corrector_desc& d) {
+    int s = d.d_hidden / 512;
+    if (s > 16) s = 16;
+    return s < 1 ? 1 : s;
+}
+
+Layout layout(const corrector_desc& d, int32_t n) {
+    Layout L{};
+    const int64_t rows = static_cast<int64_t>(n) * d.slots;
+    const int64_t pairs = static_cast<int64_t>(n) * (d.slots - 1);
+    L.chunks = static_cast<int>((d.vocab + topk_chunk_elems(d.logits_dtype) - 1) /
+                                topk_chunk_elems(d.logits_dtype));
+    L.splits = choose_splits(d);
+    size_t o = 0;
+    auto take = [&](size_t bytes) { size_t at = o; o = up(o + bytes); return at; };
+    L.part_key = take(sizeof(uint32_t) * rows * L.chunks * d.k);
+    L.part_id = take(sizeof(int32_t) * rows * L.chunks * d.k);
+    L.ids = take(sizeof(int32_t) * rows * d.k);
+    L.vals = take(sizeof(float) * rows * d.k);
+    L.hproj = take(sizeof(float) * L.splits * rows * 3 * d.r);
+    L.z = take(sizeof(uint16_t) * rows * d.k * d.r);
+    L.g = take(sizeof(float) * rows * d.r);
+    L.s = take(sizeof(float) * pairs * d.r);
+    const bool cos = d.variant == CORR_VARIANT_COSINE;
+    L.vout = take(cos ? sizeof(float) * rows * d.k * d.d_vec : 0);
+    L.vin = take(cos ? sizeof(float) * rows * d.k * d.d_vec : 0);
+    L.scores = take(sizeof(float) * pairs * d.k * d.k);
+    L.total = o;
+    return L;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+    return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+bool live(const corrector* h) { return h && h->magic == kMagic; }
+
+int check_n(const corrector* h, int32_t n) {
+    if (!live(h)) return CORR_E_HANDLE;
+    if (n < 0 || n > h->d.max_requests) return CORR_E_SHAPE;
+    return CORR_OK;
+}
+
+int check_ws(const corrector* h, int32_t n, const void* ws, size_t bytes) {
+    if (!ws) return CORR_E_NULL;
+    if (!aligned(ws, 16)) return CORR_E_ALIGN;
+    if (bytes < layout(h->d, n).total) return CORR_E_WORKSPACE;
+    return CORR_OK;
+}
+
+int check_logits(const corrector* h, const void* logits, int64_t rs, int64_t ss) {
+    if (!logits) return CORR_E_NULL;
+    if (rs < 0 || ss < 0) return CORR_E_SHAPE;
+    const int64_t e = logits_elem_bytes(h->d);
+    if (!aligned(logits, 16) || (rs * e) % 16 != 0 || (ss * e) % 16 != 0) return CORR_E_ALIGN;
+    return CORR_OK;
+}
+
+int check_hidden(const void* hidden, int64_t rs, int64_t ss) {
+    if (!hidden) return CORR_E_NULL;
+    if (rs < 0 || ss < 0) return CORR_E_SHAPE;
+    if (!aligned(hidden, 16) || (rs * 2) % 16 != 0 || (ss * 2) % 16 != 0) return CORR_E_ALIGN;
+    return CORR_OK;
+}
+
+// Enqueues kernels, optionally bracketed by timing events.
+struct Seq {
+    corrector* h;
+    hipStream_t s;
+    hipError_t err = hipSuccess;
+    int k = 0;
+    template <class F>
+    void operator()(const char* name, F&& f) {
+        if (err != hipSuccess) return;
+        const bool t = h->timing && h->events_ready && k < kMaxKernels;
+        if (t) err = hipEventRecord(h->ev[2 * k], s);
+        if (err == hipSuccess) err = f();
+        if (t && err == hipSuccess) {
+            err = hipEventRecord(h->ev[2 * k + 1], s);
+            h->names[k] = name;
+        }
+        ++k;
+    }
+    int finish() {
+        if (h->timing) h->nk = k < kMaxKernels ? k : kMaxKernels;
+        return err == hipSuccess ? CORR_OK : CORR_E_HIP;
+    }
+};
+
+void enqueue_topk(Seq& q, const corrector* h, const Layout& L, int32_t n, const void* logits,
+                  int64_t rs, int64_t ss, int32_t* ids, float* vals, void* ws) {
+    const corrector_desc& d = h->d;
+    const int64_t rows = static_cast<int64_t>(n) * d.slots;
+    uint32_t* pk = at<uint32_t>(ws, L.part_key);
+    int32_t* pi = at<int32_t>(ws, L.part_id);
+    q("topk_partial", [&] {
+        return launch_topk_partial(d.logits_dtype, logits, rs, ss, d.slots, d.vocab, d.k, L.chunks,
+                                   rows, pk, pi, q.s);
+    });
+    q("topk_merge", [&] { return launch_topk_merge(pk, pi, L.chunks, d.k, rows, ids, vals, q.s); });
+}
+
+void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const int32_t* ids,
+                   const float* vals, const void* hidden, int64_t hrs, int64_t hss, float* scores,
+                   void* ws) {
+    const corrector_desc& d = h->d;
+    const corrector_weights& w = h->w;
+    const int64_t rows = static_cast<int64_t>(n) * d.slots;
+    float* hproj = at<float>(ws, L.hproj);
+    const bool cos = d.variant == CORR_VARIANT_COSINE;
+    q("hproj", [&] {
+        return launch_hproj(static_cast<const uint16_t*>(hidden), hrs, hss, d.slots, rows,
+                            d.d_hidden, d.r, static_cast<const uint16_t*>(w.w_ctx),
+                            cos ? nullptr : static_cast<const uint16_t*>(w.w_pair), L.splits,
+                            hproj, q.s);
+    });
+    CandArgs ca{};
+    ca.ids = ids;
+    ca.embed = static_cast<const uint16_t*>(w.embed);
+    ca.V = d.vocab;
+    ca.de = d.d_embed;
+    ca.K = d.k;
+    ca.r = d.r;
+    ca.rows = rows;
+    ca.w_cand = static_cast<const uint16_t*>(w.w_cand);
+    ca.w_fuse = static_cast<const uint16_t*>(w.w_fuse);
+    ca.gamma = w.ln_gamma;
+    ca.beta = w.ln_beta;
+    ca.eps = d.ln_eps;
+    ca.hproj = hproj;
+    ca.splits = L.splits;
+    ca.z = at<uint16_t>(ws, L.z);
+    ca.g = at<float>(ws, L.g);
+    if (cos) {
+        ca.w_out = static_cast<const uint16_t*>(w.w_out);
+        ca.w_in = static_cast<const uint16_t*>(w.w_in);
+        ca.dvec = d.d_vec;
+        ca.vout = at<float>(ws, L.vout);
+        ca.vin = at<float>(ws, L.vin);
+    }
+    q("cand", [&] { return launch_cand(ca, q.s); });
+    if (d.slots < 2) return;
+    if (cos) {
+        CosArgs c{};
+        c.vout = ca.vout;
+        c.vin = ca.vin;
+        c.vals = vals;
+        c.n = n;
+        c.B = d.slots;
+        c.K = d.k;
+        c.dvec = d.d_vec;
+        c.sigma = d.sigma;
+        c.scores = scores;
+        q("cosine", [&] { return launch_cosine(c, q.s); });
+    } else {
+        MlpArgs m{};
+        m.z = ca.z;
+        m.vals = vals;
+        m.hproj = hproj;
+        m.splits = L.splits;
+        m.n = n;
+        m.B = d.slots;
+        m.K = d.k;
+        m.r = d.r;
+        m.h = d.mlp_hidden;
+        m.w1 = static_cast<const uint16_t*>(w.w1);
+        m.b1 = w.b1;
+        m.w2 = w.w2;
+        m.b2 = w.b2;
+        m.scores = scores;
+        m.s_out = at<float>(ws, L.s);
+        q("mlp", [&] { return launch_mlp(m, q.s); });
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+int corrector_create(const corrector_desc* desc, const corrector_weights* wt, corrector** out) {
+    if (!out) return CORR_E_NULL;
+    *out = nullptr;
+    if (!desc || !wt) return CORR_E_NULL;
+    const corrector_desc& d = *desc;
+    if (d.variant != CORR_VARIANT_MLP && d.variant != CORR_VARIANT_COSINE) return CORR_E_UNSUPPORTED;
+    if (d.logits_dtype != CORR_DTYPE_BF16 && d.logits_dtype != CORR_DTYPE_F32) return CORR_E_UNSUPPORTED;
+    if (d.vocab < 1 || d.vocab > 0x7FFFFFFF) return CORR_E_SHAPE;
+    if (d.slots < 1 || d.slots > 64) return CORR_E_SHAPE;
+    if (d.k < 1 || d.k > 64 || d.k > d.vocab) return CORR_E_SHAPE;
+    if (d.d_hidden < 32 || d.d_hidden % 32 || d.d_hidden > 65536) return CORR_E_SHAPE;
+    if (d.d_embed < 32 || d.d_embed % 32 || d.d_embed > 65536) return CORR_E_SHAPE;
+    if (d.r != 16 && d.r != 32 && d.r != 64 && d.r != 128) return CORR_E_UNSUPPORTED;
+    if (d.max_requests < 1 || static_cast<int64_t>(d.max_requests) * d.slots > (1 << 24)) return CORR_E_SHAPE;
+    if (!(d.ln_eps > 0.f) || !isfinite(d.ln_eps)) return CORR_E_SHAPE;
+    if (d.variant == CORR_VARIANT_MLP) {
+        if (d.mlp_hidden < 16 || d.mlp_hidden > 256 || d.mlp_hidden % 16) return CORR_E_UNSUPPORTED;
+    } else {
+        if (d.d_vec < 16 || d.d_vec > 128 || d.d_vec % 16) return CORR_E_UNSUPPORTED;
+        if (!isfinite(d.sigma)) return CORR_E_SHAPE;
+    }
+    // the top-K merge stages one row's chunk candidates in LDS
+    const int64_t chunks = (d.vocab + topk_chunk_elems(d.logits_dtype) - 1) / topk_chunk_elems(d.logits_dtype);
+    if (chunks * d.k * 8 > 60 * 1024) return CORR_E_UNSUPPORTED;
+
+    const corrector_weights& w = *wt;
+    if (!w.embed || !w.w_cand || !w.w_ctx || !w.w_fuse || !w.ln_gamma || !w.ln_beta) return CORR_E_NULL;
+    if (d.variant == CORR_VARIANT_MLP && (!w.w_pair || !w.w1 || !w.b1 || !w.w2 || !w.b2)) return CORR_E_NULL;
+    if (d.variant == CORR_VARIANT_COSINE && (!w.w_out || !w.w_in)) return CORR_E_NULL;
+    const void* mats[] = {w.embed, w.w_cand, w.w_ctx, w.w_fuse,
+                          d.variant == CORR_VARIANT_MLP ? w.w_pair : w.w_out,
+                          d.variant == CORR_VARIANT_MLP ? w.w1 : w.w_in};
+    for (const void* m : mats)
+        if (!aligned(m, 16)) return CORR_E_ALIGN;
+    if (!aligned(w.ln_gamma, 4) || !aligned(w.ln_beta, 4)) return CORR_E_ALIGN;
+
+    corrector* h = new (std::nothrow) corrector();
+    if (!h) return CORR_E_SHAPE;
+    h->magic = kMagic;
+    h->d = d;
+    h->w = w;
+    h->timing = false;
+    h->events_ready = false;
+    h->nk = 0;
+    *out = h;
+    return CORR_OK;
+}
+
+void corrector_destroy(corrector* h) {
+    if (!live(h)) return;
+    if (h->events_ready)
+        for (hipEvent_t& e : h->ev) (void)hipEventDestroy(e);
+    h->magic = kDead;
+    delete h;
+}
+
+size_t corrector_workspace_bytes(const corrector* h, int32_t n) {
+    if (check_n(h, n) != CORR_OK) return 0;
+    return layout(h->d, n).total;
+}
+
+int corrector_topk(const corrector* hc, int32_t n, const void* logits, int64_t rs, int64_t ss,
+                   int32_t* ids, float* vals, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_n(hc, n);
+    if (rc || n == 0) return rc;
+    if ((rc = check_logits(hc, logits, rs, ss))) return rc;
+    if (!ids || !vals) return CORR_E_NULL;
+    if ((rc = check_ws(hc, n, ws, ws_bytes))) return rc;
+    corrector* h = const_cast<corrector*>(hc);
+    const Layout L = layout(h->d, n);
+    Seq q{h, static_cast<hipStream_t>(stream)};
+    enqueue_topk(q, h, L, n, logits, rs, ss, ids, vals, ws);
+    return q.finish();
+}
+
+int corrector_score(const corrector* hc, int32_t n, const int32_t* ids, const float* vals,
+                    const void* hidden, int64_t hrs, int64_t hss, float* scores, void* ws,
+                    size_t ws_bytes, void* stream) {
+    int rc = check_n(hc, n);
+    if (rc || n == 0) return rc;
+    if (!ids || !vals) return CORR_E_NULL;
+    if ((rc = check_hidden(hidden, hrs, hss))) return rc;
+    if (!scores && hc->d.slots > 1) return CORR_E_NULL;
+    if ((rc = check_ws(hc, n, ws, ws_bytes))) return rc;
+    corrector* h = const_cast<corrector*>(hc);
+    const Layout L = layout(h->d, n);
+    Seq q{h, static_cast<hipStream_t>(stream)};
+    enqueue_score(q, h, L, n, ids, vals, hidden, hrs, hss, scores, ws);
+    return q.finish();
+}
+
+int corrector_walk(const corrector* hc, int32_t n, const float* scores, const int32_t* ids,
+                   int32_t* tokens, int32_t* choice, void* stream) {
+    int rc = check_n(hc, n);
+    if (rc || n == 0) return rc;
+    if (!ids || !tokens || (!scores && hc->d.slots > 1)) return CORR_E_NULL;
+    corrector* h = const_cast<corrector*>(hc);
+    Seq q{h, static_cast<hipStream_t>(stream)};
+    q("walk", [&] { return launch_walk(scores, ids, n, h->d.slots, h->d.k, tokens, choice, q.s); });
+    return q.finish();
+}
+
+int corrector_run(const corrector* hc, int32_t n, const void* logits, int64_t lrs, int64_t lss,
+                  const void* hidden, int64_t hrs, int64_t hss, int32_t* tokens,
+                  int32_t* choice_or_null, int32_t* ids_or_null, float* vals_or_null,
+                  float* scores_or_null, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_n(hc, n);
+    if (rc || n == 0) return rc;
+    if ((rc = check_logits(hc, logits, lrs, lss))) return rc;
+    if ((rc = check_hidden(hidden, hrs, hss))) return rc;
+    if (!tokens) return CORR_E_NULL;
+    if ((rc = check_ws(hc, n, ws, ws_bytes))) return rc;
+    corrector* h = const_cast<corrector*>(hc);
+    const Layout L = layout(h->d, n);
+    int32_t* ids = ids_or_null ? ids_or_null : at<int32_t>(ws, L.ids);
+    float* vals = vals_or_null ? vals_or_null : at<float>(ws, L.vals);
+    float* scores = scores_or_null ? scores_or_null : at<float>(ws, L.scores);
+    Seq q{h, static_cast<hipStream_t>(stream)};
+    enqueue_topk(q, h, L, n, logits, lrs, lss, ids, vals, ws);
+    enqueue_score(q, h, L, n, ids, vals, hidden, hrs, hss, scores, ws);
+    q("walk", [&] { return launch_walk(scores, ids, n, h->d.slots, h->d.k, tokens, choice_or_null, q.s); });
+    return q.finish();
+}
+
+int corrector_intermediates(const corrector* h, int32_t n, const void* ws, size_t ws_bytes,
+                            float* z, float* g, float* s, void* stream) {
+    int rc = check_n(h, n);
+    if (rc || n == 0) return rc;
+    if ((rc = check_ws(h, n, ws, ws_bytes))) return rc;
+    const Layout L = layout(h->d, n);
+    const corrector_desc& d = h->d;
+    const int64_t rows = static_cast<int64_t>(n) * d.slots;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    void* w = const_cast<void*>(ws);
+    hipError_t e = hipSuccess;
+    if (z) e = launch_bf16_to_f32(at<uint16_t>(w, L.z), z, rows * d.k * d.r, st);
+    if (e == hipSuccess && g) e = launch_copy_f32(at<float>(w, L.g), g, rows * d.r, st);
+    if (e == hipSuccess && s && d.variant == CORR_VARIANT_MLP && d.slots > 1)
+        e = launch_copy_f32(at<float>(w, L.s), s, static_cast<int64_t>(n) * (d.slots - 1) * d.r, st);
+    return e == hipSuccess ? CORR_OK : CORR_E_HIP;
+}
+
+int corrector_set_timing(corrector* h, int enabled) {
+    if (!live(h)) return CORR_E_HANDLE;
+    if (enabled && !h->events_ready) {
+        for (int i = 0; i < 2 * kMaxKernels; ++i) {
+            if (hipEventCreate(&h->ev[i]) != hipSuccess) {
+                for (int j = 0; j < i; ++j) (void)hipEventDestroy(h->ev[j]);
+                return CORR_E_HIP;
+            }
+        }
+        h->events_ready = true;
+    }
+    h->timing = enabled != 0;
+    h->nk = 0;
+    return CORR_OK;
+}
+
+int corrector_kernel_times(corrector* h, float* ms, const char** names, int cap) {
+    if (!live(h)) return -CORR_E_HANDLE;
+    if (!h->timing || !h->events_ready) return 0;
+    const int nk = h->nk;
+    if (nk > 0 && hipEventSynchronize(h->ev[2 * nk - 1]) != hipSuccess) return -CORR_E_HIP;
+    for (int k = 0; k < nk && k < cap; ++k) {
+        float t = 0.f;
+        if (hipEventElapsedTime(&t, h->ev[2 * k], h->ev[2 * k + 1]) != hipSuccess) return -CORR_E_HIP;
+        if (ms) ms[k] = t;
+        if (names) names[k] = h->names[k];
+    }
+    return nk;
+}
+
+const char* corrector_status_string(int status) {
+    switch (status) {
+        case CORR_OK: return "ok";
+        case CORR_E_NULL: return "null pointer";
+        case CORR_E_SHAPE: return "size out of range";
+        case CORR_E_UNSUPPORTED: return "unsupported value";
+        case CORR_E_ALIGN: return "misaligned pointer or stride";
+        case CORR_E_WORKSPACE: return "workspace too small";
+        case CORR_E_HIP: return "HIP launch or runtime error";
+        case CORR_E_HANDLE: return "invalid handle";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,101 @@
+// Internal launch interface between the C-ABI layer (corrector.hip) and the
+// kernel files.  Every launcher enqueues on `stream` and returns the HIP
+// launch status; shapes have been validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define CORR_DT_BF16 0
+#define CORR_DT_F32 1
+
+namespace corr {
+
+// ---- top-K (topk.hip)
+int topk_chunk_elems(int dtype);
+hipError_t launch_topk_partial(int dtype, const void* logits, int64_t req_stride,
+                               int64_t slot_stride, int B, int64_t V, int K, int chunks,
+                               int64_t rows, uint32_t* part_key, int32_t* part_id,
+                               hipStream_t stream);
+hipError_t launch_topk_merge(const uint32_t* part_key, const int32_t* part_id, int chunks, int K,
+                             int64_t rows, int32_t* ids, float* vals, hipStream_t stream);
+
+// ---- projections (proj.hip)
+// hproj[sk][row][0:3r) = partial (over d-split sk) of
+//   [W_ctx h_row ; W_pair[:, :d] h_row ; W_pair[:, d:] h_row]
+// (only the W_ctx block when w_pair is null).
+hipError_t launch_hproj(const uint16_t* hidden, int64_t h_req_stride, int64_t h_slot_stride,
+                        int B, int64_t rows, int d, int r, const uint16_t* w_ctx,
+                        const uint16_t* w_pair, int splits, float* hproj, hipStream_t stream);
+
+// Per drafted slot: b = LN(W_cand E[ids]), g = LN(W_ctx h) from hproj,
+// z = gamma * LN(W_fuse [b; g]) + beta stored as bfloat16 [rows][K][r];
+// g stored float32 [rows][r].  Cosine: also unit out/in vectors [rows][K][dvec].
+struct CandArgs {
+    const int32_t* ids;
+    const uint16_t* embed;
+    int64_t V;
+    int de;
+    int K;
+    int r;
+    int64_t rows;
+    const uint16_t* w_cand;
+    const uint16_t* w_fuse;
+    const float* gamma;
+    const float* beta;
+    float eps;
+    const float* hproj;
+    int splits;
+    uint16_t* z;
+    float* g;
+    // cosine only (null otherwise)
+    const uint16_t* w_out;
+    const uint16_t* w_in;
+    int dvec;
+    float* vout;
+    float* vin;
+};
+hipError_t launch_cand(const CandArgs& a, hipStream_t stream);
+
+// ---- transition scores (mlp.hip, cosine.hip)
+struct MlpArgs {
+    const uint16_t* z;      // [n][B][K][r] bfloat16
+    const float* vals;      // [n][B][K]
+    const float* hproj;     // [splits][n*B][3r]
+    int splits;
+    int n;
+    int B;
+    int K;
+    int r;
+    int h;
+    const uint16_t* w1;     // [h][3r+2]
+    const float* b1;
+    const float* w2;
+    const float* b2;
+    float* scores;          // [n][B-1][K][K]
+    float* s_out;           // optional [n][B-1][r]
+};
+hipError_t launch_mlp(const MlpArgs& a, hipStream_t stream);
+
+struct CosArgs {
+    const float* vout;      // [n][B][K][dvec]
+    const float* vin;
+    const float* vals;
+    int n;
+    int B;
+    int K;
+    int dvec;
+    float sigma;
+    float* scores;
+};
+hipError_t launch_cosine(const CosArgs& a, hipStream_t stream);
+
+// ---- walk (walk.hip)
+hipError_t launch_walk(const float* scores, const int32_t* ids, int n, int B, int K,
+                       int32_t* tokens, int32_t* choice, hipStream_t stream);
+
+// ---- intermediates (walk.hip)
+hipError_t launch_bf16_to_f32(const uint16_t* src, float* dst, int64_t count, hipStream_t stream);
+hipError_t launch_copy_f32(const float* src, float* dst, int64_t count, hipStream_t stream);
+
+}  // namespace corr

@@ -1,0 +1,108 @@
+// The cosine transition scores (LiLiCorr section 3.2, Eq. 1, with the
+// drafter's successor logit added as in the DCOCO score), the prefix-first
+// walk (DCOCO method details step (5); LiLiCorr section 3.5, Eq. 8), and small
+// copy kernels used to expose intermediates.
+#include "common.h"
+#include "kernels.h"
+
+namespace corr {
+
+namespace {
+
+// One workgroup per pair: S[a][b] = l_{p+1}(b) + sigma * <o_p^a, i_{p+1}^b>,
+// the vectors already unit-normalised; fp32 dot products in index order.
+__global__ __launch_bounds__(256) void cosine_kernel(CosArgs a) {
+    const int pair = blockIdx.x;
+    const int B = a.B, K = a.K, dv = a.dvec;
+    const int req = pair / (B - 1), p = pair % (B - 1);
+    const int64_t tp = static_cast<int64_t>(req) * B + p, tq = tp + 1;
+    for (int idx = threadIdx.x; idx < K * K; idx += blockDim.x) {
+        const int ia = idx / K, ib = idx % K;
+        const float* o = a.vout + (tp * K + ia) * dv;
+        const float* v = a.vin + (tq * K + ib) * dv;
+        float acc = 0.f;
+        for (int c = 0; c < dv; ++c) acc += o[c] * v[c];
+        a.scores[static_cast<int64_t>(pair) * K * K + idx] = a.vals[tq * K + ib] + a.sigma * acc;
+    }
+}
+
+// One wave per request.  choice[0] = 0 (rank 0 is the drafter argmax of the
+// first drafted slot); then each step takes the largest score in the row of
+// the chosen predecessor, ties to the lowest successor index.
+__global__ __launch_bounds__(64) void walk_kernel(const float* __restrict__ scores,
+                                                  const int32_t* __restrict__ ids, int n, int B,
+                                                  int K, int32_t* __restrict__ tokens,
+                                                  int32_t* __restrict__ choice) {
+    const int req = blockIdx.x;
+    const int l = lane_id();
+    if (req >= n) return;
+    int k = 0;
+    if (l == 0) {
+        if (choice) choice[static_cast<int64_t>(req) * B] = 0;
+        tokens[static_cast<int64_t>(req) * B] = ids[static_cast<int64_t>(req) * B * K];
+    }
+    for (int p = 0; p + 1 < B; ++p) {
+        const float* row = scores + ((static_cast<int64_t>(req) * (B - 1) + p) * K + k) * K;
+        float v = l < K ? row[l] : -INFINITY;
+        int bi = l < K ? l : 0x7FFFFFFF;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            const float ov = __shfl_xor(v, o, kWave);
+            const int oi = __shfl_xor(bi, o, kWave);
+            if (ov > v || (ov == v && oi < bi)) {
+                v = ov;
+                bi = oi;
+            }
+        }
+        k = __shfl(bi, 0, kWave);  // lane 0 always holds an index < K
+        if (l == 0) {
+            const int64_t s = static_cast<int64_t>(req) * B + p + 1;
+            if (choice) choice[s] = k;
+            tokens[s] = ids[s * K + k];
+        }
+    }
+}
+
+__global__ void bf16_to_f32_kernel(const uint16_t* __restrict__ src, float* __restrict__ dst,
+                                   int64_t count) {
+    for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < count;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+        dst[i] = bf16_to_f32(src[i]);
+}
+
+__global__ void copy_f32_kernel(const float* __restrict__ src, float* __restrict__ dst,
+                                int64_t count) {
+    for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < count;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+        dst[i] = src[i];
+}
+
+unsigned grid_for(int64_t count) {
+    const int64_t g = (count + 255) / 256;
+    return static_cast<unsigned>(g < 4096 ? (g < 1 ? 1 : g) : 4096);
+}
+
+}  // namespace
+
+hipError_t launch_cosine(const CosArgs& a, hipStream_t stream) {
+    cosine_kernel<<<dim3(static_cast<unsigned>(a.n * (a.B - 1))), 256, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_walk(const float* scores, const int32_t* ids, int n, int B, int K,
+                       int32_t* tokens, int32_t* choice, hipStream_t stream) {
+    walk_kernel<<<dim3(static_cast<unsigned>(n)), 64, 0, stream>>>(scores, ids, n, B, K, tokens, choice);
+    return hipGetLastError();
+}
+
+hipError_t launch_bf16_to_f32(const uint16_t* src, float* dst, int64_t count, hipStream_t stream) {
+    bf16_to_f32_kernel<<<grid_for(count), 256, 0, stream>>>(src, dst, count);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_f32(const float* src, float* dst, int64_t count, hipStream_t stream) {
+    copy_f32_kernel<<<grid_for(count), 256, 0, stream>>>(src, dst, count);
+    return hipGetLastError();
+}
+
+}  // namespace corr

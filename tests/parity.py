@@ -1,0 +1,165 @@
+"""Shared helpers of the GPU parity tests: cached inputs, one GPU pass through
+the C-ABI, and the comparison gates.
+
+Gates (the oracle is float64, the GPU computes with bf16 MFMA inputs and
+float32 accumulation):
+  * top-K ids and values: exact.
+  * S:     |S_gpu - S_ora| <= TOL * max(|S_ora|, 1)
+  * Delta: |D_gpu - D_ora| <= TOL * max(|D_ora|, rms of D_ora over the pair's
+           K x K tile), with D = S - l_{p+1}(b) on each side; this gate sees
+           errors of the size that decide the walk, which the S gate alone
+           cannot (S is dominated by the successor logit).
+  * walk:  teacher forced; at every step the GPU's successor, given the GPU's
+           own predecessor, must be the oracle's argmax of that row unless the
+           row's top-2 margin is below TOL * max(|S_max|, 1), in which case it
+           must lie within that margin of the row maximum.
+  TOL = 2e-2.
+"""
+
+from __future__ import annotations
+
+import functools
+import os
+
+import numpy as np
+import torch
+
+import oracle
+from draft_correction_amd import device
+from workload import config, gen_inputs
+
+TOL = 2e-2
+
+oracle.set_threads(min(16, os.cpu_count() or 1))
+
+
+@functools.lru_cache(maxsize=4)
+def _inputs(name: str, head: str, ties: bool, overrides: tuple):
+    cfg = config(name, **dict(overrides))
+    return gen_inputs(cfg, head=head, ties=ties)
+
+
+def inputs(name: str, head: str = "normal", ties: bool = False, **overrides):
+    return _inputs(name, head, ties, tuple(sorted(overrides.items())))
+
+
+_dev_cache = {}
+
+
+def dev_inputs(x: dict) -> dict:
+    key = id(x)
+    if key not in _dev_cache:
+        if len(_dev_cache) >= 2:
+            _dev_cache.clear()
+            torch.cuda.empty_cache()
+        _dev_cache[key] = (x, device.inputs_to_device(x))
+    return _dev_cache[key][1]
+
+
+def gpu_run(x: dict, n: int | None = None, first: int = 0, reps: int = 1) -> dict:
+    """One corrector_run over blocks [first, first+n) with every output captured."""
+    cfg = x["cfg"]
+    dev = dev_inputs(x)
+    n = cfg["n"] - first if n is None else n
+    corr = device.make_corrector(cfg, dev, max_requests=max(n, 1))
+    st = device.strides(cfg)
+    B, K = cfg["B"], cfg["K"]
+    tokens = torch.empty((n, B), dtype=torch.int32, device="cuda")
+    choice = torch.empty((n, B), dtype=torch.int32, device="cuda")
+    ids = torch.empty((n, B, K), dtype=torch.int32, device="cuda")
+    vals = torch.empty((n, B, K), dtype=torch.float32, device="cuda")
+    scores = torch.empty((n, max(B - 1, 0), K, K), dtype=torch.float32, device="cuda")
+    ws = corr.new_workspace(n)
+    for _ in range(reps):
+        corr.run(n, dev["logits"], st["l_req"], st["l_slot"], dev["hidden"], st["h_req"], st["h_slot"],
+                 tokens, ws, choice=choice, ids=ids, vals=vals, scores=scores,
+                 l_offset=st["l_off"] + first * st["l_req"], h_offset=st["h_off"] + first * st["h_req"])
+    r = cfg["r"]
+    z = torch.empty((n, B, K, r), dtype=torch.float32, device="cuda")
+    g = torch.empty((n, B, r), dtype=torch.float32, device="cuda")
+    s = torch.empty((n, max(B - 1, 0), r), dtype=torch.float32, device="cuda")
+    corr.intermediates(n, ws, z=z, g=g, s=s)
+    torch.cuda.synchronize()
+    out = dict(tokens=tokens, choice=choice, ids=ids, vals=vals, scores=scores, z=z, g=g, s=s)
+    out = {k: v.cpu().numpy() for k, v in out.items()}
+    corr.close()
+    return out
+
+
+def oracle_run(x: dict, n: int | None = None, first: int = 0) -> dict:
+    return oracle.run(x["cfg"], x, n=n, first=first)
+
+
+# ------------------------------------------------------------------ gates --
+
+def check_topk(gpu: dict, ora: dict, where: str = ""):
+    np.testing.assert_array_equal(gpu["ids"], ora["ids"], err_msg="top-K ids " + where)
+    np.testing.assert_array_equal(gpu["vals"].astype(np.float64), ora["vals"], err_msg="top-K values " + where)
+
+
+def check_scores(gpu: dict, ora: dict, where: str = ""):
+    S_g = gpu["scores"].astype(np.float64)
+    S_o = ora["scores"]
+    assert np.isfinite(S_g).all(), "non-finite GPU scores " + where
+    bad = np.abs(S_g - S_o) > TOL * np.maximum(np.abs(S_o), 1.0)
+    assert not bad.any(), "S gate %s: %d of %d, worst |diff| %.3g" % (
+        where, bad.sum(), bad.size, np.abs(S_g - S_o).max())
+    D_g = S_g - gpu["vals"][:, 1:, None, :].astype(np.float64)
+    D_o = ora["delta"]
+    rms = np.sqrt((D_o ** 2).mean(axis=(2, 3), keepdims=True))
+    lim = TOL * np.maximum(np.abs(D_o), rms)
+    bad = np.abs(D_g - D_o) > lim
+    assert not bad.any(), "Delta gate %s: %d of %d, worst ratio %.3g" % (
+        where, bad.sum(), bad.size, (np.abs(D_g - D_o) / np.maximum(lim, 1e-30)).max())
+
+
+def check_walk(gpu: dict, ora: dict, where: str = "", exact: bool = False):
+    """Teacher-forced walk check; returns (steps, exempt steps, departures from rank 0)."""
+    S_o = ora["scores"]
+    ch = gpu["choice"]
+    n, B = ch.shape
+    steps = exempt = moved = 0
+    for i in range(n):
+        assert ch[i, 0] == 0, where
+        for p in range(B - 1):
+            row = S_o[i, p, ch[i, p]]
+            best = int(np.argmax(row))
+            smax = row[best]
+            tol = TOL * max(abs(smax), 1.0)
+            second = np.max(np.delete(row, best)) if row.size > 1 else -np.inf
+            steps += 1
+            moved += int(ch[i, p + 1] != 0)
+            if exact or smax - second >= tol:
+                assert ch[i, p + 1] == best, "walk %s: request %d step %d: gpu %d oracle %d" % (
+                    where, i, p, ch[i, p + 1], best)
+            else:
+                exempt += 1
+                assert row[ch[i, p + 1]] >= smax - tol, "walk %s: request %d step %d" % (where, i, p)
+        np.testing.assert_array_equal(
+            gpu["tokens"][i], gpu["ids"][i, np.arange(B), ch[i]], err_msg="tokens " + where)
+    return steps, exempt, moved
+
+
+def check_intermediates(gpu: dict, ora: dict, where: str = "", variant: str = "mlp"):
+    z_g, z_o = gpu["z"].astype(np.float64), ora["z"]
+    assert np.all(np.abs(z_g - z_o) <= 1e-2 * np.maximum(np.abs(z_o), 1.0)), \
+        "z %s worst %.3g" % (where, np.abs(z_g - z_o).max())
+    g_g, g_o = gpu["g"].astype(np.float64), ora["g"]
+    assert np.all(np.abs(g_g - g_o) <= 1e-3 * np.maximum(np.abs(g_o), 1.0)), \
+        "g %s worst %.3g" % (where, np.abs(g_g - g_o).max())
+    if variant == "mlp" and ora["s"].size and gpu["s"].size:
+        s_g, s_o = gpu["s"].astype(np.float64), ora["s"]
+        rms = np.sqrt((s_o ** 2).mean())
+        assert np.all(np.abs(s_g - s_o) <= 1e-3 * np.maximum(np.abs(s_o), rms)), \
+            "s %s worst %.3g" % (where, np.abs(s_g - s_o).max())
+
+
+def check_all(gpu: dict, ora: dict, where: str = "", exact_walk: bool = False, variant: str = "mlp"):
+    check_topk(gpu, ora, where)
+    check_intermediates(gpu, ora, where, variant)
+    check_scores(gpu, ora, where)
+    return check_walk(gpu, ora, where, exact=exact_walk)
+
+
+def select(gpu: dict, first: int, n: int) -> dict:
+    return {k: v[first:first + n] for k, v in gpu.items()}

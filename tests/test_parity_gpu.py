@@ -1,0 +1,116 @@
+"""GPU parity: the HIP path through the C-ABI against the CPU oracle.
+
+Every configuration runs the whole pass (corrector_run) and compares top-K
+(exact), the intermediates z / g / s, the transition scores (S and Delta
+gates) and the walk (teacher forced), as described in tests/parity.py.
+Each configuration also runs with the zero-initialised output layer (walk
+and S exact) and with a walk-stress output layer (w2 ~ N(0, 1)) so that the
+walk leaves rank 0 often enough to be tested.
+"""
+
+import numpy as np
+import pytest
+
+import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+# ------------------------------------------------------------------ tiny --
+
+@pytest.mark.parametrize("head", ["normal", "zero", "stress"])
+@pytest.mark.parametrize("ties", [False, True])
+def test_tiny(head, ties):
+    _log("tiny head=%s ties=%s" % (head, ties))
+    x = P.inputs("tiny", head=head, ties=ties)
+    gpu = P.gpu_run(x)
+    ora = P.oracle_run(x)
+    P.check_all(gpu, ora, "tiny/%s" % head, exact_walk=(head == "zero"))
+    if head == "zero":
+        want = np.broadcast_to(gpu["vals"][:, 1:, None, :], gpu["scores"].shape)
+        np.testing.assert_array_equal(gpu["scores"], want)
+        assert (gpu["choice"] == 0).all()
+
+
+@pytest.mark.parametrize("sigma", [1.0, 8.0])
+def test_tiny_cosine(sigma):
+    _log("tiny cosine sigma=%g" % sigma)
+    x = P.inputs("tiny", variant="cosine", sigma=sigma)
+    gpu = P.gpu_run(x)
+    ora = P.oracle_run(x)
+    P.check_all(gpu, ora, "tiny-cos", variant="cosine")
+
+
+# ---------------------------------------------------- Qwen3-8B shape, n=1 --
+
+@pytest.mark.parametrize("head", ["normal", "zero", "stress"])
+def test_b1(head):
+    _log("b1 head=%s" % head)
+    x = P.inputs("b1", head=head)
+    gpu = P.gpu_run(x)
+    ora = P.oracle_run(x)
+    steps, exempt, moved = P.check_all(gpu, ora, "b1/%s" % head, exact_walk=(head == "zero"))
+    _log("  walk steps %d exempt %d moved %d" % (steps, exempt, moved))
+
+
+# ------------------------------------------------------------- batch 32 --
+
+@pytest.mark.parametrize("head", ["normal", "stress"])
+def test_b32(head):
+    _log("b32 head=%s" % head)
+    x = P.inputs("b32", head=head)
+    gpu = P.gpu_run(x)
+    ora = P.oracle_run(x)
+    steps, exempt, moved = P.check_all(gpu, ora, "b32/%s" % head)
+    _log("  walk steps %d exempt %d moved %d" % (steps, exempt, moved))
+    if head == "stress":
+        assert moved > steps // 10
+
+
+def test_b32_batch_invariance_and_determinism():
+    _log("b32 batch invariance")
+    x = P.inputs("b32")
+    full = P.gpu_run(x)
+    again = P.gpu_run(x)
+    for k in ("ids", "vals", "scores", "tokens", "choice", "z"):
+        np.testing.assert_array_equal(full[k], again[k], err_msg="rerun " + k)
+    for i in (0, 17, 31):
+        one = P.gpu_run(x, n=1, first=i)
+        sub = P.select(full, i, 1)
+        for k in ("ids", "vals", "scores", "tokens", "choice", "z", "s", "g"):
+            np.testing.assert_array_equal(one[k], sub[k], err_msg="request %d alone: %s" % (i, k))
+
+
+# ---------------------------------------------------------------- cosine --
+
+@pytest.mark.parametrize("sigma", [1.0, 8.0])
+def test_cosine_b32(sigma):
+    _log("cosine b32 sigma=%g" % sigma)
+    x = P.inputs("cosine", sigma=sigma)
+    gpu = P.gpu_run(x)
+    for i in (0, 15, 31):
+        ora = P.oracle_run(x, n=1, first=i)
+        P.check_all(P.select(gpu, i, 1), ora, "cosine/%d" % i, variant="cosine")
+    bound = np.abs(gpu["scores"] - gpu["vals"][:, 1:, None, :])
+    assert (bound <= sigma * (1 + 1e-5)).all()
+
+
+# ---------------------------------------------------------------- stress --
+
+def test_stress():
+    _log("stress n=256 K=32 d=5120")
+    x = P.inputs("stress")
+    gpu = P.gpu_run(x)
+    # top-K of every row, exact
+    cfg = x["cfg"]
+    ids, vals = P.oracle.topk(P.oracle.OracleDesc.from_config(cfg), x["logits"], cfg["n"],
+                              (cfg["B"] + 1) * cfg["V"], cfg["V"], offset=cfg["V"])
+    P.check_topk(gpu, dict(ids=ids, vals=vals), "stress")
+    # everything else on sampled requests (one per entropy tier)
+    for i in (0, 128, 255):
+        ora = P.oracle_run(x, n=1, first=i)
+        P.check_all(P.select(gpu, i, 1), ora, "stress/%d" % i)

@@ -56,8 +56,8 @@ CONFIGS = {
     "b1": _mk(1, n=1),
     # Same shapes at concurrency 32, three entropy tiers in equal thirds.
     "b32": _mk(2, n=32, tiers=(0.8, 1.1, 1.6)),
-    # Cosine in/out-vector variant at batch 32.
-    "cosine": _mk(3, n=32, tiers=(0.8, 1.1, 1.6), variant="cosine"),
+    # Cosine in/out-vector variant at batch 32, on the batch-32 inputs.
+    "cosine": _mk(3, n=32, tiers=(0.8, 1.1, 1.6), variant="cosine", seed_index=2),
     # Stress: 256 requests, K=32, hidden width 5120, hidden states ~N(0,3).
     "stress": _mk(4, n=256, K=32, d=5120, de=5120, hidden_std=3.0,
                   tiers=(0.8, 1.1, 1.6)),

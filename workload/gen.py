@@ -42,7 +42,8 @@ EMBED_BLOCK = 4096
 
 
 def _rng(cfg: dict, *key: int) -> np.random.Generator:
-    ss = np.random.SeedSequence(entropy=1000 + int(cfg["index"]) + 100 * int(cfg.get("seed", 0)),
+    base = int(cfg.get("seed_index", cfg["index"]))
+    ss = np.random.SeedSequence(entropy=1000 + base + 100 * int(cfg.get("seed", 0)),
                                 spawn_key=tuple(int(k) for k in key))
     return np.random.Generator(np.random.PCG64(ss))
 
