@@ -1,0 +1,226 @@
+"""Throughput of the corrector pass on one GPU.
+
+One step = one corrector_run (top-K, projections, transition scores, walk)
+over one batch of synthetic draft blocks already resident in HBM.  The batch
+rotates over several independently generated input sets (more logits than
+the 256 MB Infinity Cache holds) so the logits stream from HBM.
+
+Prints ONE JSON line: blocks/s, the roofline of the dominant kernel (HIP-event
+timed on the launch stream inside this run), and the CPU oracle timed on the
+host cores on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "corrected draft blocks/s at batch 32 (V=151936,B=16,K=16); % HBM/MFMA peak"
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "draft_correction_amd", "csrc")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_work(cfg: dict, n: int) -> dict:
+    """Bytes a kernel must move and flops it must do, per launch, by definition
+    of its step (not counting re-reads): the unit figures times the units one
+    launch processes."""
+    B, K, V, d, de, r, h = cfg["B"], cfg["K"], cfg["V"], cfg["d"], cfg["de"], cfg["r"], cfg["h"]
+    esz = 2 if cfg["logits_dtype"] == "bf16" else 4
+    rows, pairs = n * B, n * (B - 1)
+    w = {}
+    # top-K: every logit of every drafted slot row read once
+    w["topk_partial"] = dict(bound="hbm", bytes=rows * V * esz, unit="drafted slot row of V logits",
+                             per_unit=V * esz, units=rows)
+    w["topk_merge"] = dict(bound="hbm", bytes=rows * K * 8, per_unit=K * 8, units=rows,
+                           unit="slot row (K ids + values out)")
+    w["hproj"] = dict(bound="hbm", bytes=rows * d * 2 + 3 * r * d * 2, flops=2 * rows * d * 3 * r,
+                      per_unit=d * 2, units=rows, unit="hidden row")
+    w["cand"] = dict(bound="hbm", bytes=rows * K * de * 2 + r * de * 2, flops=2 * rows * K * (de * r + 2 * r * r),
+                     per_unit=de * 2, units=rows * K, unit="gathered embedding row")
+    w["mlp"] = dict(bound="mfma", flops=2 * pairs * K * K * (3 * r + 2) * h, per_unit=2 * (3 * r + 2) * h,
+                    units=pairs * K * K, unit="transition (layer 1)")
+    w["cosine"] = dict(bound="hbm", bytes=pairs * 2 * K * cfg["dvec"] * 4, per_unit=2 * K * cfg["dvec"] * 4,
+                       units=pairs, unit="pair")
+    w["walk"] = dict(bound="hbm", bytes=n * (B - 1) * K * 4, per_unit=(B - 1) * K * 4, units=n,
+                     unit="block (scores rows read)")
+    return w
+
+
+def cpu_baseline(cfg, inputs, min_seconds: float = 10.0, max_passes: int = 8) -> dict:
+    import oracle
+    oracle.build(force=False)
+    threads = oracle.get_threads()
+    n = cfg["n"]
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        oracle.run(cfg, inputs)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or passes >= max_passes:
+            break
+    return {"value": passes * n / el, "unit": "blocks/s", "cores": threads, "kind": "oracle",
+            "sample": "%d full pass(es) of the CPU oracle over one %d-block batch of the same workload "
+                      "(%.1f s, %d OpenMP threads)" % (passes, n, el, threads)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="b32")
+    ap.add_argument("--copies", type=int, default=4, help="independent input sets rotated per step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--head", default="normal")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(requests shard across GPUs with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from draft_correction_amd import device
+    from workload import config, gen_embed, gen_hidden, gen_logits, gen_weights
+
+    cfg = config(args.workload)
+    n = cfg["n"]
+    log("generating %s inputs (%d copies)" % (args.workload, args.copies))
+    t0 = time.perf_counter()
+    embed = gen_embed(cfg)
+    weights = gen_weights(cfg, head=args.head)
+    sets = []
+    for c in range(args.copies):
+        cc = dict(cfg, seed=c)
+        sets.append(dict(logits=gen_logits(cc), hidden=gen_hidden(cc)))
+    log("generated in %.1f s" % (time.perf_counter() - t0))
+
+    torch.cuda.set_device(0)
+    dev_w = device.weights_to_device(weights, embed)
+    dev_sets = [dict(logits=device.tensor(s["logits"]), hidden=device.tensor(s["hidden"])) for s in sets]
+    corr = device.make_corrector(cfg, dict(weights=dev_w), max_requests=n)
+    st = device.strides(cfg)
+    B, K = cfg["B"], cfg["K"]
+    tokens = torch.empty((n, B), dtype=torch.int32, device="cuda")
+    ws = corr.new_workspace(n)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        s = dev_sets[i % len(dev_sets)]
+        corr.run(n, s["logits"], st["l_req"], st["l_slot"], s["hidden"], st["h_req"], st["h_slot"],
+                 tokens, ws, l_offset=st["l_off"], h_offset=st["h_off"], stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # ---- timed region: exactly `steps` passes
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    log("pass: %.2f us (%d steps)" % (ms * 1e3, args.steps))
+
+    # ---- per-kernel durations: HIP events recorded by the library around each
+    # of its launches on the same stream, over the same number of passes
+    corr.set_timing(True)
+    per = {}
+    for i in range(args.steps):
+        step(i)
+        for name, t in corr.kernel_times():
+            per.setdefault(name, []).append(t)
+    corr.set_timing(False)
+    torch.cuda.synchronize()
+    avg = {k: float(np.mean(v)) for k, v in per.items()}
+    for k, v in avg.items():
+        log("  %-14s %8.2f us" % (k, v * 1e3))
+
+    work = algorithmic_work(cfg, n)
+    dom = max(avg, key=avg.get)
+    wk = work[dom]
+    t_s = avg[dom] / 1e3
+    if wk["bound"] == "mfma":
+        achieved, peak, unit = wk["flops"] / t_s / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+    else:
+        achieved, peak, unit = wk["bytes"] / t_s / 1e9, PEAK_HBM_GBS, "GB/s"
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        ent = tr.get("kernels", {}).get(dom)
+        if ent and tr.get("source_hash") == kernel_source_hash() and tr.get("workload") == args.workload:
+            traffic = ent.get("bytes_per_launch")
+    roof = {"bound": wk["bound"], "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": dom,
+            "kernel_us": round(avg[dom] * 1e3, 3)}
+    kernels = {}
+    for k, v in avg.items():
+        wkk = work.get(k, {})
+        ent = {"us": round(v * 1e3, 3)}
+        if "bytes" in wkk:
+            ent["GB/s"] = round(wkk["bytes"] / (v / 1e3) / 1e9, 1)
+        if "flops" in wkk:
+            ent["TFLOP/s"] = round(wkk["flops"] / (v / 1e3) / 1e12, 2)
+        kernels[k] = ent
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        from workload import gen_inputs  # noqa: F401
+        inputs = dict(cfg=cfg, logits=sets[0]["logits"], hidden=sets[0]["hidden"], weights=weights,
+                      embed=embed)
+        cpu = cpu_baseline(cfg, inputs)
+
+    out = {
+        "metric": METRIC,
+        "value": round(n / (ms / 1e3), 1),
+        "unit": "blocks/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "%s: %d requests x %d drafted slots (+anchor), V=%d, K=%d, d=%d, r=%d, "
+                               "MLP %d->%d->1, %s" % (args.workload, n, B, cfg["V"], K, cfg["d"],
+                                                      cfg["r"], 3 * cfg["r"] + 2, cfg["h"], cfg["variant"]),
+                   "global_batch": n, "rotating_input_sets": args.copies},
+        "roofline": roof,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    corr.close()
+
+
+if __name__ == "__main__":
+    main()

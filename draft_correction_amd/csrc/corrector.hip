@@ -67,7 +67,7 @@ Layout layout(const corrector_desc& d, int32_t n) {
     L.ids = take(sizeof(int32_t) * rows * d.k);
     L.vals = take(sizeof(float) * rows * d.k);
     L.hproj = take(sizeof(float) * L.splits * rows * 3 * d.r);
-    L.z = take(sizeof(uint16_t) * rows * d.k * d.r);
+    L.z = take(sizeof(uint16_t) * rows * d.k * 2 * d.r);
     L.g = take(sizeof(float) * rows * d.r);
     L.s = take(sizeof(float) * pairs * d.r);
     const bool cos = d.variant == CORR_VARIANT_COSINE;
@@ -179,7 +179,7 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
     ca.eps = d.ln_eps;
     ca.hproj = hproj;
     ca.splits = L.splits;
-    ca.z = at<uint16_t>(ws, L.z);
+    ca.zhl = at<uint16_t>(ws, L.z);
     ca.g = at<float>(ws, L.g);
     if (cos) {
         ca.w_out = static_cast<const uint16_t*>(w.w_out);
@@ -204,7 +204,7 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
         q("cosine", [&] { return launch_cosine(c, q.s); });
     } else {
         MlpArgs m{};
-        m.z = ca.z;
+        m.zhl = ca.zhl;
         m.vals = vals;
         m.hproj = hproj;
         m.splits = L.splits;
@@ -362,7 +362,7 @@ int corrector_intermediates(const corrector* h, int32_t n, const void* ws, size_
     hipStream_t st = static_cast<hipStream_t>(stream);
     void* w = const_cast<void*>(ws);
     hipError_t e = hipSuccess;
-    if (z) e = launch_bf16_to_f32(at<uint16_t>(w, L.z), z, rows * d.k * d.r, st);
+    if (z) e = launch_zhl_to_f32(at<uint16_t>(w, L.z), z, rows * d.k, d.r, st);
     if (e == hipSuccess && g) e = launch_copy_f32(at<float>(w, L.g), g, rows * d.r, st);
     if (e == hipSuccess && s && d.variant == CORR_VARIANT_MLP && d.slots > 1)
         e = launch_copy_f32(at<float>(w, L.s), s, static_cast<int64_t>(n) * (d.slots - 1) * d.r, st);

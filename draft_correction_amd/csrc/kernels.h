@@ -29,7 +29,8 @@ hipError_t launch_hproj(const uint16_t* hidden, int64_t h_req_stride, int64_t h_
                         const uint16_t* w_pair, int splits, float* hproj, hipStream_t stream);
 
 // Per drafted slot: b = LN(W_cand E[ids]), g = LN(W_ctx h) from hproj,
-// z = gamma * LN(W_fuse [b; g]) + beta stored as bfloat16 [rows][K][r];
+// z = gamma * LN(W_fuse [b; g]) + beta stored as bfloat16 hi/lo halves
+// zhl [rows][K][2r] = [hi(z) | lo(z)] with z = hi + lo to ~2^-16;
 // g stored float32 [rows][r].  Cosine: also unit out/in vectors [rows][K][dvec].
 struct CandArgs {
     const int32_t* ids;
@@ -46,7 +47,7 @@ struct CandArgs {
     float eps;
     const float* hproj;
     int splits;
-    uint16_t* z;
+    uint16_t* zhl;
     float* g;
     // cosine only (null otherwise)
     const uint16_t* w_out;
@@ -59,7 +60,7 @@ hipError_t launch_cand(const CandArgs& a, hipStream_t stream);
 
 // ---- transition scores (mlp.hip, cosine.hip)
 struct MlpArgs {
-    const uint16_t* z;      // [n][B][K][r] bfloat16
+    const uint16_t* zhl;    // [n][B][K][2r] bfloat16 hi | lo
     const float* vals;      // [n][B][K]
     const float* hproj;     // [splits][n*B][3r]
     int splits;
@@ -95,7 +96,7 @@ hipError_t launch_walk(const float* scores, const int32_t* ids, int n, int B, in
                        int32_t* tokens, int32_t* choice, hipStream_t stream);
 
 // ---- intermediates (walk.hip)
-hipError_t launch_bf16_to_f32(const uint16_t* src, float* dst, int64_t count, hipStream_t stream);
+hipError_t launch_zhl_to_f32(const uint16_t* zhl, float* z, int64_t nodes, int r, hipStream_t stream);
 hipError_t launch_copy_f32(const float* src, float* dst, int64_t count, hipStream_t stream);
 
 }  // namespace corr

@@ -2,19 +2,19 @@
 //   S_p(a,b) = l_{p+1}(b) + w2 . GELU(W1 [s_p; z_p^a; z_{p+1}^b; l_p(a); l_{p+1}(b)] + b1) + b2
 // for every adjacent drafted-slot pair p and candidate pair (a, b).
 //
-// One workgroup per pair (4 waves).  The pair state s_p = W_pair,L h_p +
-// W_pair,R h_{p+1} is assembled once from the hproj partials, and its layer-1
-// contribution c_p = W1[:, s-block] s_p + b1 is formed once per pair in fp32
-// and shared by all K^2 transitions.  The dense part of layer 1 runs on MFMA
-// (v_mfma_f32_16x16x32_bf16) with rows (a, b) = [z_p^a ; z_{p+1}^b] (K = 2r)
-// against W1's z columns, which each wave keeps in registers for its 64
-// hidden units.  One extra 32-wide K step carries the remaining terms exactly:
-// A = [l_p(a) hi, lo, l_{p+1}(b) hi, lo, 1, 1, 0...] against
-// B = [w1_la, w1_la, w1_lb, w1_lb, c_p hi, c_p lo, 0...] (hi/lo = bf16 split),
-// so the accumulator ends as the full pre-activation.  The epilogue applies
-// GELU, the 256 -> 1 dot with w2 (lane, then 16-lane butterfly, then the four
-// waves in fixed order) and adds b2 and l_{p+1}(b).  No atomics: results are
-// bit-reproducible.
+// Layer 1 is evaluated through the exact column-block identity
+//   W1 x = (W1_s s_p + b1 + W1_za z_p^a + w_la l_p(a)) + (W1_zb z_{p+1}^b + w_lb l_{p+1}(b))
+//        =              P_p[a]                        +            Q_p[b]
+// so the K^2 x (3r+2) x h product collapses to two K x 2r x h MFMA products
+// per pair plus a K x K broadcast add; the pair state s_p enters once per
+// pair through c_p = W1_s s_p + b1.  The MFMA inputs are z split into bf16
+// hi + lo parts (z = hi + lo to ~2^-16), against the same W1 columns twice, so
+// P and Q carry float32 accuracy.  The epilogue is the GELU over all K^2 x h
+// pre-activations and the h -> 1 dot with w2, one (a, b) per thread with the
+// sum over hidden units in index order: no atomics, bit-reproducible.
+//
+// One workgroup per pair (4 waves).  For K > 16 the hidden units are processed
+// in blocks so that P and Q for one block fit in LDS.
 #include "common.h"
 #include "kernels.h"
 
@@ -22,19 +22,32 @@ namespace corr {
 
 namespace {
 
-__device__ __forceinline__ float gelu_erf(float x) {
-    return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+// GELU(x) = x Phi(x) = max(x, 0) - |x| Phi(-|x|), with Phi(-t) from
+// Abramowitz & Stegun 26.2.17 (Hastings): Phi(-t) = phi(t) (b1 k + ... + b5 k^5),
+// k = 1 / (1 + p t), |error| < 7.5e-8; phi's 1/sqrt(2 pi) is folded into b.
+// In float32 the result is within 4e-7 of the exact erf form everywhere.
+__device__ __forceinline__ float gelu(float x) {
+    const float t = fabsf(x);
+    const float k = __builtin_amdgcn_rcpf(fmaf(0.2316419f, t, 1.0f));
+    float poly = fmaf(k, 0.530702714f, -0.726576013f);  // b5, b4 (times 1/sqrt(2 pi))
+    poly = fmaf(k, poly, 0.710706871f);                 // b3
+    poly = fmaf(k, poly, -0.142248368f);                // b2
+    poly = fmaf(k, poly, 0.127414796f);                 // b1
+    poly *= k;
+    const float e = __builtin_amdgcn_exp2f(t * t * -0.72134752f);  // exp(-t^2 / 2)
+    return fmaxf(x, 0.0f) - (t * e) * poly;
 }
 
-__device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) {
-    hi = f32_to_bf16(v);
-    lo = f32_to_bf16(v - bf16_to_f32(hi));
+// Hidden-unit block so that P and Q ([K][JB] float32 each) fit in ~34 KB.
+__host__ __device__ inline int mlp_jblock(int K, int h) {
+    int jb = (4096 / K) / 16 * 16;
+    if (jb < 16) jb = 16;
+    return jb < h ? jb : h;
 }
 
 template <int R>
 __global__ __launch_bounds__(256) void mlp_kernel(MlpArgs a) {
-    constexpr int KS = 2 * R / 32;  // MFMA K steps over [z_a; z_b]
-    constexpr int ZS = R + 8;       // LDS row stride of z tiles (bf16)
+    constexpr int KS = 2 * R / 32;  // MFMA K steps over [z_hi | z_lo]
     const int l = lane_id();
     const int wave = threadIdx.x >> 6;
     const int tid = threadIdx.x;
@@ -44,18 +57,19 @@ __global__ __launch_bounds__(256) void mlp_kernel(MlpArgs a) {
     const int64_t tp = static_cast<int64_t>(req) * B + p;  // slot rows of the pair
     const int64_t tq = tp + 1;
     const int64_t nslots = static_cast<int64_t>(a.n) * B;
+    const int JB = mlp_jblock(K, h);
+    const int PS = JB + 4;          // LDS row stride of P / Q (floats)
+    const int nin = 3 * R + 2;
 
     __shared__ float sv[128];
     __shared__ float cvec[256];
-    __shared__ __attribute__((aligned(16))) uint16_t bx[256][8];
-    __shared__ float red[4][256];
-    extern __shared__ __attribute__((aligned(16))) uint16_t dyn[];
-    uint16_t* zp = dyn;                       // [K][ZS]
-    uint16_t* zq = zp + K * ZS;               // [K][ZS]
-    float* lp = reinterpret_cast<float*>(zq + K * ZS);  // [K]
-    float* lq = lp + K;                                 // [K]
+    __shared__ __attribute__((aligned(16))) float w2s[256];
+    __shared__ float lp[64], lq[64];
+    extern __shared__ __attribute__((aligned(16))) float dyn[];
+    float* P = dyn;                 // [K][PS]
+    float* Q = dyn + K * PS;        // [K][PS]
 
-    // ---- pair state and staging
+    // ---- pair state, logits, w2
     for (int c = tid; c < R; c += 256) {
         float s = 0.f;
         for (int sk = 0; sk < a.splits; ++sk) s += a.hproj[(sk * nslots + tp) * (3 * R) + R + c];
@@ -63,124 +77,108 @@ __global__ __launch_bounds__(256) void mlp_kernel(MlpArgs a) {
         sv[c] = s;
         if (a.s_out) a.s_out[static_cast<int64_t>(pair) * R + c] = s;
     }
-    for (int idx = tid; idx < K * (R / 8); idx += 256) {
-        const int m = idx / (R / 8), c8 = (idx % (R / 8)) * 8;
-        *reinterpret_cast<u32x4*>(zp + m * ZS + c8) = load16(a.z + (tp * K + m) * R + c8);
-        *reinterpret_cast<u32x4*>(zq + m * ZS + c8) = load16(a.z + (tq * K + m) * R + c8);
-    }
     for (int m = tid; m < K; m += 256) {
         lp[m] = a.vals[tp * K + m];
         lq[m] = a.vals[tq * K + m];
     }
+    for (int j = tid; j < h; j += 256) w2s[j] = a.w2[j];
     __syncthreads();
-
-    // ---- c_p = W1[:, 0:R] s_p + b1 (fp32), and the extra-K-step B rows
-    const int nin = 3 * R + 2;
+    // ---- c_p = W1_s s_p + b1, float32, once per pair
     for (int j = tid; j < h; j += 256) {
         const uint16_t* w = a.w1 + static_cast<int64_t>(j) * nin;
         float acc = a.b1[j];
-        for (int c = 0; c < R; ++c) acc += bf16_to_f32(w[c]) * sv[c];
+        for (int c = 0; c < R; ++c) acc = fmaf(bf16_to_f32(w[c]), sv[c], acc);
         cvec[j] = acc;
-        uint16_t hi, lo;
-        split_bf16(acc, hi, lo);
-        bx[j][0] = w[3 * R];
-        bx[j][1] = w[3 * R];
-        bx[j][2] = w[3 * R + 1];
-        bx[j][3] = w[3 * R + 1];
-        bx[j][4] = hi;
-        bx[j][5] = lo;
-        bx[j][6] = 0;
-        bx[j][7] = 0;
     }
     __syncthreads();
 
-    // ---- this wave's W1 z-column fragments, kept in registers
-    const int nct = h / 16;
     const int kq = 8 * (l >> 4);
-    u32x4 wf[4][KS];
-    u32x4 xf[4];
-    float w2c[4];
+    const int nrt = (K + 15) / 16;
     const u32x4 zero = {0u, 0u, 0u, 0u};
+    const int nidx = K * K;
+    constexpr int kMaxPer = 16;     // (a, b) pairs per thread: K^2 / 256 for K = 64
+    float dacc[kMaxPer];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int ct = wave + 4 * q;
-        const bool ok = ct < nct;
-        const int j = (ok ? ct : 0) * 16 + (l & 15);
-        const uint32_t* w = reinterpret_cast<const uint32_t*>(a.w1 + static_cast<int64_t>(j) * nin + R);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int o = (ks * 32 + kq) / 2;   // dword offset; rows are 4-byte aligned
-            wf[q][ks] = ok ? u32x4{w[o], w[o + 1], w[o + 2], w[o + 3]} : zero;
-        }
-        xf[q] = (ok && l < 16) ? *reinterpret_cast<const u32x4*>(&bx[j][0]) : zero;
-        w2c[q] = ok ? a.w2[j] : 0.f;
-    }
+    for (int q = 0; q < kMaxPer; ++q) dacc[q] = 0.f;
 
-    const uint32_t one2 = 0x3F803F80u;  // two bf16 ones
-    const int nrows = K * K;
-    const int nrt = (nrows + 15) / 16;
-    const float b2 = a.b2[0];
-    for (int rb0 = 0; rb0 < nrt; rb0 += 16) {
-        const int rb1 = min(nrt, rb0 + 16);
-        for (int rt = rb0; rt < rb1; ++rt) {
-            const int m = rt * 16 + (l & 15);
-            const bool valid = m < nrows;
-            const int ia = valid ? m / K : 0, ib = valid ? m % K : 0;
-            u32x4 af[KS];
+    for (int jb0 = 0; jb0 < h; jb0 += JB) {
+        const int jn = min(JB, h - jb0);
+        const int nct = jn / 16;
+        // ---- P (which = 0) and Q (which = 1) for this block of hidden units
+        for (int job = wave; job < 2 * nct; job += 4) {
+            const int which = job / nct, ct = job % nct;
+            const int j = jb0 + ct * 16 + (l & 15);
+            const uint32_t* wrow = reinterpret_cast<const uint32_t*>(
+                a.w1 + static_cast<int64_t>(j) * nin + (which ? 2 * R : R));
+            const int64_t zrow0 = (which ? tq : tp) * K;
+            u32x4 bf[KS];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const int kg = ks * 32 + kq;
-                const uint16_t* src = kg < R ? zp + ia * ZS + kg : zq + ib * ZS + (kg - R);
-                af[ks] = valid ? *reinterpret_cast<const u32x4*>(src) : zero;
+                const int o = ((ks * 32 + kq) % R) / 2;    // same W1 columns for hi and lo
+                bf[ks] = u32x4{wrow[o], wrow[o + 1], wrow[o + 2], wrow[o + 3]};
             }
-            u32x4 ax = zero;
-            if (valid && l < 16) {
-                uint16_t ah, al, bh, bl;
-                split_bf16(lp[ia], ah, al);
-                split_bf16(lq[ib], bh, bl);
-                ax = u32x4{static_cast<uint32_t>(ah) | (static_cast<uint32_t>(al) << 16),
-                           static_cast<uint32_t>(bh) | (static_cast<uint32_t>(bl) << 16), one2, 0u};
-            }
-            float part[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if (wave + 4 * q >= nct) continue;
+            const float wl = bf16_to_f32(a.w1[static_cast<int64_t>(j) * nin + 3 * R + which]);
+            const float cj = which ? 0.f : cvec[j];
+            for (int rt = 0; rt < nrt; ++rt) {
+                const int m = rt * 16 + (l & 15);
+                const uint16_t* zr = a.zhl + (zrow0 + (m < K ? m : 0)) * (2 * R);
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(af[ks], wf[q][ks], acc);
-                acc = mfma16x16x32(ax, xf[q], acc);
+                for (int ks = 0; ks < KS; ++ks) {
+                    const u32x4 av = m < K ? load16(zr + ks * 32 + kq) : zero;
+                    acc = mfma16x16x32(av, bf[ks], acc);
+                }
 #pragma unroll
-                for (int i = 0; i < 4; ++i) part[i] += w2c[q] * gelu_erf(acc[i]);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) part[i] = wave_sum16(part[i]);
-            if ((l & 15) == 0) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) red[wave][(rt - rb0) * 16 + 4 * (l >> 4) + i] = part[i];
-            }
-        }
-        __syncthreads();
-        for (int idx = tid; idx < (rb1 - rb0) * 16; idx += 256) {
-            const int row = rb0 * 16 + idx;
-            if (row < nrows) {
-                const float delta = ((red[0][idx] + red[1][idx]) + red[2][idx]) + red[3][idx] + b2;
-                const int ib = row % K;
-                a.scores[static_cast<int64_t>(pair) * nrows + row] = lq[ib] + delta;
+                for (int i = 0; i < 4; ++i) {
+                    const int mm = rt * 16 + 4 * (l >> 4) + i;
+                    if (mm < K) {
+                        const float lv = which ? lq[mm] : lp[mm];
+                        (which ? Q : P)[mm * PS + ct * 16 + (l & 15)] = acc[i] + fmaf(wl, lv, cj);
+                    }
+                }
             }
         }
         __syncthreads();
+        // ---- GELU and the dot with w2 over this block, one (a, b) per thread
+#pragma unroll
+        for (int q = 0; q < kMaxPer; ++q) {
+            const int idx = tid + 256 * q;
+            if (idx < nidx) {
+                const float* pr = P + (idx / K) * PS;
+                const float* qr = Q + (idx % K) * PS;
+                const float* wr = w2s + jb0;
+                float d = dacc[q];
+                for (int j = 0; j < jn; j += 4) {
+                    const float4 pv = *reinterpret_cast<const float4*>(pr + j);
+                    const float4 qv = *reinterpret_cast<const float4*>(qr + j);
+                    const float4 wv = *reinterpret_cast<const float4*>(wr + j);
+                    d = fmaf(wv.x, gelu(pv.x + qv.x), d);
+                    d = fmaf(wv.y, gelu(pv.y + qv.y), d);
+                    d = fmaf(wv.z, gelu(pv.z + qv.z), d);
+                    d = fmaf(wv.w, gelu(pv.w + qv.w), d);
+                }
+                dacc[q] = d;
+            }
+        }
+        __syncthreads();
+    }
+    const float b2 = a.b2[0];
+#pragma unroll
+    for (int q = 0; q < kMaxPer; ++q) {
+        const int idx = tid + 256 * q;
+        if (idx < nidx) a.scores[static_cast<int64_t>(pair) * nidx + idx] = lq[idx % K] + (dacc[q] + b2);
     }
 }
 
 }  // namespace
 
-size_t mlp_lds_bytes(int K, int r) {
-    return static_cast<size_t>(2) * K * (r + 8) * sizeof(uint16_t) + 2 * K * sizeof(float);
+size_t mlp_lds_bytes(int K, int h) {
+    return static_cast<size_t>(2) * K * (mlp_jblock(K, h) + 4) * sizeof(float);
 }
 
 hipError_t launch_mlp(const MlpArgs& a, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(a.n * (a.B - 1)));
-    const size_t lds = mlp_lds_bytes(a.K, a.r);
+    const size_t lds = mlp_lds_bytes(a.K, a.h);
     switch (a.r) {
         case 16: mlp_kernel<16><<<grid, 256, lds, stream>>>(a); break;
         case 32: mlp_kernel<32><<<grid, 256, lds, stream>>>(a); break;

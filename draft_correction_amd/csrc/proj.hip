@@ -7,11 +7,14 @@
 //          W_pair,L h (for pairs that start at the slot) and the right half
 //          W_pair,R h (for pairs that end at it).  The d reduction is split
 //          over `splits` workgroups; consumers add the partials in split order.
-//   cand   one workgroup per drafted slot (and group of up to 32 candidates):
+//   cand   one workgroup per drafted slot and group of up to 16 candidates:
 //          gathers the candidates' embedding rows E[c], u = W_cand E[c] on
 //          MFMA, b = LN(u) (non-affine), g = LN(W_ctx h) from hproj,
-//          y = W_fuse [b; g] on MFMA, z = gamma * LN(y) + beta, stored bf16.
-//          The cosine variant also forms unit(W_out z) and unit(W_in z).
+//          y = W_fuse [b; g] on MFMA, z = gamma * LN(y) + beta, stored as
+//          bf16 hi | lo halves.  The cosine variant also forms unit(W_out z)
+//          and unit(W_in z).  MFMA operands that are not already bf16 (b, g,
+//          z) are split into hi + lo bf16 parts multiplied by the same weight
+//          columns, so those products carry float32 accuracy.
 // All LayerNorm statistics are fp32 over the r features, biased variance.
 #include "common.h"
 #include "kernels.h"
@@ -85,7 +88,7 @@ __global__ __launch_bounds__(256) void hproj_kernel(
 
 // ------------------------------------------------------------------- cand --
 
-constexpr int kCandRows = 32;  // candidates per workgroup (two 16-row tiles)
+constexpr int kCandRows = 16;  // candidates per workgroup (one 16-row MFMA tile)
 
 // LayerNorm of one row of m <= 128 floats held in LDS, by one wave; writes
 // gamma * y + beta (or y) to dst, which may alias src.
@@ -114,78 +117,81 @@ __host__ __device__ inline int cand_row_stride(int r, int dvec) {
     return (2 * dvec > r ? 2 * dvec : r) + 4;
 }
 
+// Row stride (bf16) of the MFMA operand rows: [x_hi | x_lo] with x = [b; g]
+// (4r wide) or z (2r wide).
+__host__ __device__ inline int cand_op_stride(int r) { return 4 * r + 8; }
+
+// acc = A (16 rows of LDS bf16 [hi | lo], 2 * kin wide) x W^T for one 16-column
+// tile of W ([*][ldw] bf16, rows w_row0 + 0..15, columns 0..kin-1).  The hi and
+// lo halves of A meet the same W columns, so acc ~ A_fp32 x W^T.
+__device__ f32x4 mfma_hilo_tile(const uint16_t* abuf, int as, int M, const uint16_t* W, int ldw,
+                                int w_row0, int kin) {
+    const int l = lane_id();
+    const int kq = 8 * (l >> 4);
+    const int m = l & 15;
+    const uint16_t* wp = W + static_cast<int64_t>(w_row0 + m) * ldw;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < 2 * kin; k0 += 32) {
+        const int kg = k0 + kq;
+        const u32x4 av = m < M ? *reinterpret_cast<const u32x4*>(abuf + m * as + kg) : zero;
+        const u32x4 bv = load16(wp + (kg % kin));
+        acc = mfma16x16x32(av, bv, acc);
+    }
+    return acc;
+}
+
+__device__ __forceinline__ void split_store(uint16_t* row, int width, int c, float v) {
+    const uint16_t hi = f32_to_bf16(v);
+    row[c] = hi;
+    row[width + c] = f32_to_bf16(v - bf16_to_f32(hi));
+}
+
 __global__ __launch_bounds__(256) void cand_kernel(CandArgs a) {
     const int l = lane_id();
     const int wave = threadIdx.x >> 6;
     const int64_t t = blockIdx.x;                 // drafted-slot row
-    const int rg = blockIdx.y;                    // candidate group
-    const int m0 = rg * kCandRows;
+    const int m0 = blockIdx.y * kCandRows;        // first candidate of this group
     const int M = min(kCandRows, a.K - m0);
     const int r = a.r;
     const int nct = r / 16;
     const int kq = 8 * (l >> 4);
 
-    // LDS: u/y rows (fp32, stride r+4), [b; g] / z rows (bf16, stride 2r+8),
-    // g (fp32), hproj-sum scratch.
     extern __shared__ float smem[];
     const int us = cand_row_stride(r, a.vout ? a.dvec : 0);
-    float* ubuf = smem;                                   // [kCandRows][us]
-    float* gbuf = ubuf + kCandRows * us;                  // [r]
-    uint16_t* abuf = reinterpret_cast<uint16_t*>(gbuf + 128);  // [kCandRows][2r+8]
-    const int as = 2 * r + 8;
+    const int as = cand_op_stride(r);
+    float* ubuf = smem;                                        // [16][us] fp32
+    float* gbuf = ubuf + kCandRows * us;                       // [128]
+    uint16_t* abuf = reinterpret_cast<uint16_t*>(gbuf + 128);  // [16][as] bf16
 
-    // ---- u = E[c] W_cand^T (MFMA), rows = this group's candidates
-    const int nrt = (M + 15) / 16;
+    // ---- u = E[c] W_cand^T (MFMA; E and W_cand are bf16, exact products)
     {
-        const uint16_t* ep[2];
-        bool eok[2];
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            const int m = rt * 16 + (l & 15);
-            eok[rt] = rt < nrt && m < M;
-            int64_t tok = eok[rt] ? a.ids[t * a.K + m0 + m] : 0;
-            tok = tok < 0 ? 0 : (tok >= a.V ? a.V - 1 : tok);
-            ep[rt] = a.embed + tok * a.de;
-        }
+        const int m = l & 15;
+        const bool eok = m < M;
+        int64_t tok = eok ? a.ids[t * a.K + m0 + m] : 0;
+        tok = tok < 0 ? 0 : (tok >= a.V ? a.V - 1 : tok);
+        const uint16_t* ep = a.embed + tok * a.de;
         const int ct0 = wave, ct1 = wave + 4;
         const bool c0ok = ct0 < nct, c1ok = ct1 < nct;
-        const uint16_t* wp0 = a.w_cand + static_cast<int64_t>((c0ok ? ct0 : 0) * 16 + (l & 15)) * a.de;
-        const uint16_t* wp1 = a.w_cand + static_cast<int64_t>((c1ok ? ct1 : 0) * 16 + (l & 15)) * a.de;
-        f32x4 acc[2][2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const uint16_t* wp0 = a.w_cand + static_cast<int64_t>((c0ok ? ct0 : 0) * 16 + m) * a.de;
+        const uint16_t* wp1 = a.w_cand + static_cast<int64_t>((c1ok ? ct1 : 0) * 16 + m) * a.de;
+        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
         const u32x4 zero = {0u, 0u, 0u, 0u};
         if (c0ok) {
-
             for (int k0 = 0; k0 < a.de; k0 += 32) {
-                const u32x4 a0 = eok[0] ? load16(ep[0] + k0 + kq) : zero;
-                const u32x4 a1 = (nrt > 1 && eok[1]) ? load16(ep[1] + k0 + kq) : zero;
-                const u32x4 b0 = load16(wp0 + k0 + kq);
-                acc[0][0] = mfma16x16x32(a0, b0, acc[0][0]);
-                if (nrt > 1) acc[1][0] = mfma16x16x32(a1, b0, acc[1][0]);
-                if (c1ok) {
-                    const u32x4 b1 = load16(wp1 + k0 + kq);
-                    acc[0][1] = mfma16x16x32(a0, b1, acc[0][1]);
-                    if (nrt > 1) acc[1][1] = mfma16x16x32(a1, b1, acc[1][1]);
-                }
+                const u32x4 av = eok ? load16(ep + k0 + kq) : zero;
+                acc0 = mfma16x16x32(av, load16(wp0 + k0 + kq), acc0);
+                if (c1ok) acc1 = mfma16x16x32(av, load16(wp1 + k0 + kq), acc1);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int mm = 4 * (l >> 4) + i;
+                ubuf[mm * us + ct0 * 16 + m] = acc0[i];
+                if (c1ok) ubuf[mm * us + ct1 * 16 + m] = acc1[i];
             }
         }
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int ci = 0; ci < 2; ++ci) {
-                const int ct = ci ? ct1 : ct0;
-                if (rt >= nrt || ct >= nct) continue;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int m = rt * 16 + 4 * (l >> 4) + i;
-                    ubuf[m * us + ct * 16 + (l & 15)] = acc[rt][ci][i];
-                }
-            }
     }
-    // ---- g pre-activation: sum of the hproj partials in split order
+    // ---- g pre-activation: the hproj partials summed in split order
     for (int c = threadIdx.x; c < r; c += blockDim.x) {
         float s = 0.f;
         for (int sk = 0; sk < a.splits; ++sk) s += a.hproj[(static_cast<int64_t>(sk) * a.rows + t) * (3 * r) + c];
@@ -193,79 +199,54 @@ __global__ __launch_bounds__(256) void cand_kernel(CandArgs a) {
     }
     __syncthreads();
 
-    // ---- b = LN(u), g = LN(g); write [b; g] as bf16 rows into abuf
+    // ---- b = LN(u), g = LN(g) (non-affine)
     for (int m = wave; m < M; m += 4) wave_layernorm(ubuf + m * us, ubuf + m * us, r, a.eps, nullptr, nullptr);
     if (wave == 0) wave_layernorm(gbuf, gbuf, r, a.eps, nullptr, nullptr);
     __syncthreads();
+    // [b; g] as bf16 hi | lo rows, 4r wide
     for (int idx = threadIdx.x; idx < M * r; idx += blockDim.x) {
         const int m = idx / r, c = idx % r;
-        abuf[m * as + c] = f32_to_bf16(ubuf[m * us + c]);
-        abuf[m * as + r + c] = f32_to_bf16(gbuf[c]);
+        split_store(abuf + m * as, 2 * r, c, ubuf[m * us + c]);
+        split_store(abuf + m * as, 2 * r, r + c, gbuf[c]);
     }
-    if (rg == 0)
+    if (blockIdx.y == 0)
         for (int c = threadIdx.x; c < r; c += blockDim.x) a.g[t * r + c] = gbuf[c];
     __syncthreads();
 
-    // ---- y = [b; g] W_fuse^T (MFMA, K = 2r), into ubuf
-    {
-        const u32x4 zero = {0u, 0u, 0u, 0u};
-        for (int ct = wave; ct < nct; ct += 4) {
-            const uint16_t* wp = a.w_fuse + static_cast<int64_t>(ct * 16 + (l & 15)) * (2 * r);
-            for (int rt = 0; rt < nrt; ++rt) {
-                const int m = rt * 16 + (l & 15);
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                for (int k0 = 0; k0 < 2 * r; k0 += 32) {
-                    const u32x4 av = m < M ? *reinterpret_cast<const u32x4*>(abuf + m * as + k0 + kq) : zero;
-                    acc = mfma16x16x32(av, load16(wp + k0 + kq), acc);
-                }
+    // ---- y = W_fuse [b; g] (MFMA on the hi/lo split, K = 2 x 2r), into ubuf
+    for (int ct = wave; ct < nct; ct += 4) {
+        const f32x4 acc = mfma_hilo_tile(abuf, as, M, a.w_fuse, 2 * r, ct * 16, 2 * r);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int mm = rt * 16 + 4 * (l >> 4) + i;
-                    ubuf[mm * us + ct * 16 + (l & 15)] = acc[i];
-                }
-            }
-        }
+        for (int i = 0; i < 4; ++i) ubuf[(4 * (l >> 4) + i) * us + ct * 16 + (l & 15)] = acc[i];
     }
     __syncthreads();
 
-    // ---- z = gamma * LN(y) + beta; store bf16 (and keep a bf16 copy in abuf)
+    // ---- z = gamma * LN(y) + beta; store as bf16 hi | lo (also kept in abuf)
     for (int m = wave; m < M; m += 4) wave_layernorm(ubuf + m * us, ubuf + m * us, r, a.eps, a.gamma, a.beta);
     __syncthreads();
     for (int idx = threadIdx.x; idx < M * r; idx += blockDim.x) {
         const int m = idx / r, c = idx % r;
-        const uint16_t zb = f32_to_bf16(ubuf[m * us + c]);
-        a.z[(t * a.K + m0 + m) * r + c] = zb;
-        abuf[m * as + c] = zb;
+        const float zv = ubuf[m * us + c];
+        uint16_t* grow = a.zhl + (t * a.K + m0 + m) * (2 * r);
+        const uint16_t hi = f32_to_bf16(zv);
+        const uint16_t lo = f32_to_bf16(zv - bf16_to_f32(hi));
+        grow[c] = hi;
+        grow[r + c] = lo;
+        abuf[m * as + c] = hi;
+        abuf[m * as + r + c] = lo;
     }
     if (!a.vout) return;
     __syncthreads();
 
-    // ---- cosine variant: o = W_out z, i = W_in z (MFMA), then unit vectors
+    // ---- cosine variant: o = W_out z, i = W_in z (MFMA on z hi/lo), unit vectors
     const int dv = a.dvec;
     const int nvt = dv / 16;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
     for (int job = wave; job < 2 * nvt; job += 4) {
         const int which = job / nvt, ct = job % nvt;
-        const uint16_t* wp = (which ? a.w_in : a.w_out) + static_cast<int64_t>(ct * 16 + (l & 15)) * r;
-        for (int rt = 0; rt < nrt; ++rt) {
-            const int m = rt * 16 + (l & 15);
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int k0 = 0; k0 < r; k0 += 32) {
-                u32x4 av = zero, bv = zero;
-                // r may be 16: the upper half of the 32-wide step is padding
-                if (k0 + kq < r) {
-                    if (m < M) av = *reinterpret_cast<const u32x4*>(abuf + m * as + k0 + kq);
-                    bv = load16(wp + k0 + kq);
-                }
-                acc = mfma16x16x32(av, bv, acc);
-            }
+        const f32x4 acc = mfma_hilo_tile(abuf, as, M, which ? a.w_in : a.w_out, r, ct * 16, r);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int mm = rt * 16 + 4 * (l >> 4) + i;
-                // o in ubuf columns [0, dv), i in [dv, 2dv)
-                ubuf[mm * us + which * dv + ct * 16 + (l & 15)] = acc[i];
-            }
-        }
+        for (int i = 0; i < 4; ++i)
+            ubuf[(4 * (l >> 4) + i) * us + which * dv + ct * 16 + (l & 15)] = acc[i];
     }
     __syncthreads();
     for (int job = wave; job < 2 * M; job += 4) {
@@ -298,8 +279,8 @@ hipError_t launch_hproj(const uint16_t* hidden, int64_t h_req_stride, int64_t h_
 }
 
 size_t cand_lds_bytes(int r, int dvec) {
-    const int us = cand_row_stride(r, dvec);
-    return sizeof(float) * (kCandRows * us + 128) + sizeof(uint16_t) * kCandRows * (2 * r + 8);
+    return sizeof(float) * (kCandRows * cand_row_stride(r, dvec) + 128) +
+           sizeof(uint16_t) * kCandRows * cand_op_stride(r);
 }
 
 hipError_t launch_cand(const CandArgs& a, hipStream_t stream) {

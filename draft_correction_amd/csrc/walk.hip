@@ -63,11 +63,15 @@ __global__ __launch_bounds__(64) void walk_kernel(const float* __restrict__ scor
     }
 }
 
-__global__ void bf16_to_f32_kernel(const uint16_t* __restrict__ src, float* __restrict__ dst,
-                                   int64_t count) {
+// z = hi + lo for each node row of the [hi | lo] layout.
+__global__ void zhl_to_f32_kernel(const uint16_t* __restrict__ zhl, float* __restrict__ z,
+                                  int64_t nodes, int r) {
+    const int64_t count = nodes * r;
     for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < count;
-         i += static_cast<int64_t>(gridDim.x) * blockDim.x)
-        dst[i] = bf16_to_f32(src[i]);
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        const int64_t node = i / r, c = i % r;
+        z[i] = bf16_to_f32(zhl[node * 2 * r + c]) + bf16_to_f32(zhl[node * 2 * r + r + c]);
+    }
 }
 
 __global__ void copy_f32_kernel(const float* __restrict__ src, float* __restrict__ dst,
@@ -95,8 +99,8 @@ hipError_t launch_walk(const float* scores, const int32_t* ids, int n, int B, in
     return hipGetLastError();
 }
 
-hipError_t launch_bf16_to_f32(const uint16_t* src, float* dst, int64_t count, hipStream_t stream) {
-    bf16_to_f32_kernel<<<grid_for(count), 256, 0, stream>>>(src, dst, count);
+hipError_t launch_zhl_to_f32(const uint16_t* zhl, float* z, int64_t nodes, int r, hipStream_t stream) {
+    zhl_to_f32_kernel<<<grid_for(nodes * r), 256, 0, stream>>>(zhl, z, nodes, r);
     return hipGetLastError();
 }
 
