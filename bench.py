@@ -104,7 +104,8 @@ def main():
 
     import torch
     from draft_correction_amd import device
-    from workload import config, gen_embed, gen_hidden, gen_logits, gen_weights
+    from workload import config
+    from workload.gen import gen_embed, gen_hidden, gen_logits, gen_weights
 
     cfg = config(args.workload)
     n = cfg["n"]
@@ -192,7 +193,6 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
-        from workload import gen_inputs  # noqa: F401
         inputs = dict(cfg=cfg, logits=sets[0]["logits"], hidden=sets[0]["hidden"], weights=weights,
                       embed=embed)
         cpu = cpu_baseline(cfg, inputs)
