@@ -20,8 +20,8 @@ constexpr int kMaxKernels = 8;
 constexpr size_t kAlign = 256;
 
 struct Layout {
-    size_t part_key, part_id, ids, vals, hproj, z, g, s, vout, vin, scores, total;
-    int chunks, splits;
+    size_t part, ids, vals, hproj, upart, z, g, s, vout, vin, scores, total;
+    int chunks, splits, usplits;
 };
 
 }  // namespace
@@ -45,11 +45,17 @@ size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 int logits_elem_bytes(const corrector_desc& d) { return d.logits_dtype == CORR_DTYPE_BF16 ? 2 : 4; }
 
-// Split of the hidden-width reduction of hproj: a function of d only, so a
+// Splits of the two GEMM reductions (over d for the hidden-state projections,
+// over d_e for the candidate projection): functions of the widths only, so a
 // request's results do not depend on how many requests share the call.
 int choose_splits(const corrector_desc& d) {
     int s = d.d_hidden / 512;
     if (s > 16) s = 16;
+    return s < 1 ? 1 : s;
+}
+int choose_usplits(const corrector_desc& d) {
+    int s = d.d_embed / 1024;
+    if (s > 8) s = 8;
     return s < 1 ? 1 : s;
 }
 
@@ -60,13 +66,14 @@ Layout layout(const corrector_desc& d, int32_t n) {
     L.chunks = static_cast<int>((d.vocab + topk_chunk_elems(d.logits_dtype) - 1) /
                                 topk_chunk_elems(d.logits_dtype));
     L.splits = choose_splits(d);
+    L.usplits = choose_usplits(d);
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o = up(o + bytes); return at; };
-    L.part_key = take(sizeof(uint32_t) * rows * L.chunks * d.k);
-    L.part_id = take(sizeof(int32_t) * rows * L.chunks * d.k);
+    L.part = take(sizeof(uint64_t) * rows * L.chunks * d.k);
     L.ids = take(sizeof(int32_t) * rows * d.k);
     L.vals = take(sizeof(float) * rows * d.k);
     L.hproj = take(sizeof(float) * L.splits * rows * 3 * d.r);
+    L.upart = take(sizeof(float) * L.usplits * rows * d.k * d.r);
     L.z = take(sizeof(uint16_t) * rows * d.k * 2 * d.r);
     L.g = take(sizeof(float) * rows * d.r);
     L.s = take(sizeof(float) * pairs * d.r);
@@ -141,13 +148,12 @@ void enqueue_topk(Seq& q, const corrector* h, const Layout& L, int32_t n, const 
                   int64_t rs, int64_t ss, int32_t* ids, float* vals, void* ws) {
     const corrector_desc& d = h->d;
     const int64_t rows = static_cast<int64_t>(n) * d.slots;
-    uint32_t* pk = at<uint32_t>(ws, L.part_key);
-    int32_t* pi = at<int32_t>(ws, L.part_id);
+    uint64_t* part = at<uint64_t>(ws, L.part);
     q("topk_partial", [&] {
         return launch_topk_partial(d.logits_dtype, logits, rs, ss, d.slots, d.vocab, d.k, L.chunks,
-                                   rows, pk, pi, q.s);
+                                   rows, part, q.s);
     });
-    q("topk_merge", [&] { return launch_topk_merge(pk, pi, L.chunks, d.k, rows, ids, vals, q.s); });
+    q("topk_merge", [&] { return launch_topk_merge(part, L.chunks, d.k, rows, ids, vals, q.s); });
 }
 
 void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const int32_t* ids,
@@ -158,26 +164,52 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
     const int64_t rows = static_cast<int64_t>(n) * d.slots;
     float* hproj = at<float>(ws, L.hproj);
     const bool cos = d.variant == CORR_VARIANT_COSINE;
-    q("hproj", [&] {
-        return launch_hproj(static_cast<const uint16_t*>(hidden), hrs, hss, d.slots, rows,
-                            d.d_hidden, d.r, static_cast<const uint16_t*>(w.w_ctx),
-                            cos ? nullptr : static_cast<const uint16_t*>(w.w_pair), L.splits,
-                            hproj, q.s);
-    });
+    GemmA ha{};
+    ha.mode = GEMM_A_SLOTS;
+    ha.base = static_cast<const uint16_t*>(hidden);
+    ha.B = d.slots;
+    ha.rs = hrs;
+    ha.ss = hss;
+    GemmW hw{};
+    hw.nb = d.r;
+    hw.base[0] = static_cast<const uint16_t*>(w.w_ctx);
+    hw.ld[0] = d.d_hidden;
+    if (!cos) {
+        hw.base[1] = static_cast<const uint16_t*>(w.w_pair);
+        hw.base[2] = static_cast<const uint16_t*>(w.w_pair) + d.d_hidden;
+        hw.ld[1] = hw.ld[2] = 2 * static_cast<int64_t>(d.d_hidden);
+    }
+    // hproj rows: [W_ctx h | W_pair,L h | W_pair,R h] (3r wide); the cosine
+    // variant has no pair state and computes the W_ctx block alone (r wide).
+    const int hn = cos ? d.r : 3 * d.r;
+    q("hproj", [&] { return launch_gemm(ha, hw, rows, hn, d.d_hidden, L.splits, hproj, q.s); });
+    float* upart = at<float>(ws, L.upart);
+    GemmA ua{};
+    ua.mode = GEMM_A_GATHER;
+    ua.base = static_cast<const uint16_t*>(w.embed);
+    ua.lda = d.d_embed;
+    ua.ids = ids;
+    ua.V = d.vocab;
+    GemmW uw{};
+    uw.nb = d.r;
+    uw.base[0] = static_cast<const uint16_t*>(w.w_cand);
+    uw.ld[0] = d.d_embed;
+    q("cand_gemm", [&] { return launch_gemm(ua, uw, rows * d.k, d.r, d.d_embed, L.usplits, upart, q.s); });
     CandArgs ca{};
     ca.ids = ids;
-    ca.embed = static_cast<const uint16_t*>(w.embed);
     ca.V = d.vocab;
-    ca.de = d.d_embed;
     ca.K = d.k;
     ca.r = d.r;
     ca.rows = rows;
-    ca.w_cand = static_cast<const uint16_t*>(w.w_cand);
+    ca.upart = upart;
+    ca.usplits = L.usplits;
+    ca.table = nullptr;
     ca.w_fuse = static_cast<const uint16_t*>(w.w_fuse);
     ca.gamma = w.ln_gamma;
     ca.beta = w.ln_beta;
     ca.eps = d.ln_eps;
     ca.hproj = hproj;
+    ca.hstride = hn;
     ca.splits = L.splits;
     ca.zhl = at<uint16_t>(ws, L.z);
     ca.g = at<float>(ws, L.g);
@@ -248,9 +280,6 @@ int corrector_create(const corrector_desc* desc, const corrector_weights* wt, co
         if (d.d_vec < 16 || d.d_vec > 128 || d.d_vec % 16) return CORR_E_UNSUPPORTED;
         if (!isfinite(d.sigma)) return CORR_E_SHAPE;
     }
-    // the top-K merge stages one row's chunk candidates in LDS
-    const int64_t chunks = (d.vocab + topk_chunk_elems(d.logits_dtype) - 1) / topk_chunk_elems(d.logits_dtype);
-    if (chunks * d.k * 8 > 60 * 1024) return CORR_E_UNSUPPORTED;
 
     const corrector_weights& w = *wt;
     if (!w.embed || !w.w_cand || !w.w_ctx || !w.w_fuse || !w.ln_gamma || !w.ln_beta) return CORR_E_NULL;

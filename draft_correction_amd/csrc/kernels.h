@@ -12,40 +12,56 @@
 namespace corr {
 
 // ---- top-K (topk.hip)
+// part [rows][chunks][K]: each chunk's K best as 64-bit composites
+// (float32-order value key << 32 | inverted token id; 0 = no element).
 int topk_chunk_elems(int dtype);
 hipError_t launch_topk_partial(int dtype, const void* logits, int64_t req_stride,
                                int64_t slot_stride, int B, int64_t V, int K, int chunks,
-                               int64_t rows, uint32_t* part_key, int32_t* part_id,
-                               hipStream_t stream);
-hipError_t launch_topk_merge(const uint32_t* part_key, const int32_t* part_id, int chunks, int K,
-                             int64_t rows, int32_t* ids, float* vals, hipStream_t stream);
+                               int64_t rows, uint64_t* part, hipStream_t stream);
+hipError_t launch_topk_merge(const uint64_t* part, int chunks, int K, int64_t rows, int32_t* ids,
+                             float* vals, hipStream_t stream);
 
 // ---- projections (proj.hip)
-// hproj[sk][row][0:3r) = partial (over d-split sk) of
-//   [W_ctx h_row ; W_pair[:, :d] h_row ; W_pair[:, d:] h_row]
-// (only the W_ctx block when w_pair is null).
-hipError_t launch_hproj(const uint16_t* hidden, int64_t h_req_stride, int64_t h_slot_stride,
-                        int B, int64_t rows, int d, int r, const uint16_t* w_ctx,
-                        const uint16_t* w_pair, int splits, float* hproj, hipStream_t stream);
+// Tiled GEMM C[split][m][n] = sum_k A[m][k] W[n][k] (bf16 in, float32 out).
+#define GEMM_A_DENSE 0
+#define GEMM_A_GATHER 1
+#define GEMM_A_SLOTS 2
+struct GemmA {
+    int mode;
+    const uint16_t* base;
+    int64_t lda;          // DENSE / GATHER row stride
+    const int32_t* ids;   // GATHER: row m is base[clamp(ids[m])]
+    int64_t V;
+    int B;                // SLOTS: row m is base + (m/B)*rs + (m%B)*ss
+    int64_t rs, ss;
+};
+struct GemmW {
+    const uint16_t* base[3];  // row n is base[n / nb] + (n % nb) * ld[n / nb]
+    int64_t ld[3];
+    int nb;
+};
+hipError_t launch_gemm(const GemmA& A, const GemmW& W, int64_t M, int N, int kdim, int splits, float* C,
+                       hipStream_t stream);
 
-// Per drafted slot: b = LN(W_cand E[ids]), g = LN(W_ctx h) from hproj,
+// Per drafted slot: b = LN(u) with u = W_cand E[ids], g = LN(W_ctx h) from hproj,
 // z = gamma * LN(W_fuse [b; g]) + beta stored as bfloat16 hi/lo halves
 // zhl [rows][K][2r] = [hi(z) | lo(z)] with z = hi + lo to ~2^-16;
 // g stored float32 [rows][r].  Cosine: also unit out/in vectors [rows][K][dvec].
 struct CandArgs {
     const int32_t* ids;
-    const uint16_t* embed;
     int64_t V;
-    int de;
     int K;
     int r;
     int64_t rows;
-    const uint16_t* w_cand;
+    const float* upart;   // [usplits][rows*K][r] partials of W_cand E[c] ...
+    int usplits;
+    const float* table;   // ... or, when non-null, the folded table [V][r]
     const uint16_t* w_fuse;
     const float* gamma;
     const float* beta;
     float eps;
-    const float* hproj;
+    const float* hproj;   // [splits][rows][hstride], W_ctx h in columns [0, r)
+    int hstride;
     int splits;
     uint16_t* zhl;
     float* g;

@@ -7,7 +7,7 @@
 //        =              P_p[a]                        +            Q_p[b]
 // so the K^2 x (3r+2) x h product collapses to two K x 2r x h MFMA products
 // per pair plus a K x K broadcast add; the pair state s_p enters once per
-// pair through c_p = W1_s s_p + b1.  The MFMA inputs are z split into bf16
+// pair through c_p = W1_s s_p + b1 (one more MFMA row).  The MFMA inputs are z split into bf16
 // hi + lo parts (z = hi + lo to ~2^-16), against the same W1 columns twice, so
 // P and Q carry float32 accuracy.  The epilogue is the GELU over all K^2 x h
 // pre-activations and the h -> 1 dot with w2, one (a, b) per thread with the
@@ -45,10 +45,61 @@ __host__ __device__ inline int mlp_jblock(int K, int h) {
     return jb < h ? jb : h;
 }
 
+// One 16-column tile of P (which = 0) or Q (which = 1) for hidden units
+// j0 .. j0+15: rows are the K candidates of the slot, computed on MFMA from
+// z hi | lo; P also carries c_p = W1_s s_p + b1, itself one MFMA row over
+// s_p hi | lo (shv).  Written to P/Q in LDS.
+template <int R>
+__device__ __forceinline__ void pq_tile(const MlpArgs& a, int which, int j0, int64_t zrow0, int K,
+                                        const uint16_t* shv, const float* lp, const float* lq, float* dst,
+                                        int dcol, int PS) {
+    constexpr int KS = 2 * R / 32;
+    const int nin = 3 * R + 2;
+    const int l = lane_id();
+    const int kq = 8 * (l >> 4);
+    const int j = j0 + (l & 15);
+    const uint32_t* wz = reinterpret_cast<const uint32_t*>(a.w1 + static_cast<int64_t>(j) * nin + (which ? 2 * R : R));
+    const uint32_t* ws = reinterpret_cast<const uint32_t*>(a.w1 + static_cast<int64_t>(j) * nin);
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    u32x4 bz[KS], bs[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const int o = ((ks * 32 + kq) % R) / 2;   // same W1 columns for hi and lo
+        bz[ks] = u32x4{wz[o], wz[o + 1], wz[o + 2], wz[o + 3]};
+        bs[ks] = which ? zero : u32x4{ws[o], ws[o + 1], ws[o + 2], ws[o + 3]};
+    }
+    const float wl = bf16_to_f32(a.w1[static_cast<int64_t>(j) * nin + 3 * R + which]);
+    float cj = 0.f;
+    if (!which) {
+        // c_p tile: A row 0 = [s_hi | s_lo], other rows zero
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const u32x4 av = (l & 15) == 0 ? *reinterpret_cast<const u32x4*>(shv + ks * 32 + kq) : zero;
+            acc = mfma16x16x32(av, bs[ks], acc);
+        }
+        cj = __shfl(acc[0], l & 15, kWave) + a.b1[j];   // D[0][col] lives in lanes 0..15
+    }
+    const int nrt = (K + 15) / 16;
+    for (int rt = 0; rt < nrt; ++rt) {
+        const int m = rt * 16 + (l & 15);
+        const uint16_t* zr = a.zhl + (zrow0 + (m < K ? m : 0)) * (2 * R);
+        u32x4 af[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) af[ks] = m < K ? load16(zr + ks * 32 + kq) : zero;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(af[ks], bz[ks], acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int mm = rt * 16 + 4 * (l >> 4) + i;
+            if (mm < K) dst[mm * PS + dcol + (l & 15)] = acc[i] + fmaf(wl, which ? lq[mm] : lp[mm], cj);
+        }
+    }
+}
+
 template <int R>
 __global__ __launch_bounds__(256) void mlp_kernel(MlpArgs a) {
-    constexpr int KS = 2 * R / 32;  // MFMA K steps over [z_hi | z_lo]
-    const int l = lane_id();
     const int wave = threadIdx.x >> 6;
     const int tid = threadIdx.x;
     const int B = a.B, K = a.K, h = a.h;
@@ -59,22 +110,22 @@ __global__ __launch_bounds__(256) void mlp_kernel(MlpArgs a) {
     const int64_t nslots = static_cast<int64_t>(a.n) * B;
     const int JB = mlp_jblock(K, h);
     const int PS = JB + 4;          // LDS row stride of P / Q (floats)
-    const int nin = 3 * R + 2;
 
-    __shared__ float sv[128];
-    __shared__ float cvec[256];
+    __shared__ __attribute__((aligned(16))) uint16_t shv[2 * 128];  // s_p as bf16 hi | lo
     __shared__ __attribute__((aligned(16))) float w2s[256];
     __shared__ float lp[64], lq[64];
     extern __shared__ __attribute__((aligned(16))) float dyn[];
     float* P = dyn;                 // [K][PS]
     float* Q = dyn + K * PS;        // [K][PS]
 
-    // ---- pair state, logits, w2
+    // ---- pair state s_p = W_pair,L h_p + W_pair,R h_{p+1}, logits, w2
     for (int c = tid; c < R; c += 256) {
         float s = 0.f;
         for (int sk = 0; sk < a.splits; ++sk) s += a.hproj[(sk * nslots + tp) * (3 * R) + R + c];
         for (int sk = 0; sk < a.splits; ++sk) s += a.hproj[(sk * nslots + tq) * (3 * R) + 2 * R + c];
-        sv[c] = s;
+        const uint16_t hi = f32_to_bf16(s);
+        shv[c] = hi;
+        shv[R + c] = f32_to_bf16(s - bf16_to_f32(hi));
         if (a.s_out) a.s_out[static_cast<int64_t>(pair) * R + c] = s;
     }
     for (int m = tid; m < K; m += 256) {
@@ -83,18 +134,7 @@ __global__ __launch_bounds__(256) void mlp_kernel(MlpArgs a) {
     }
     for (int j = tid; j < h; j += 256) w2s[j] = a.w2[j];
     __syncthreads();
-    // ---- c_p = W1_s s_p + b1, float32, once per pair
-    for (int j = tid; j < h; j += 256) {
-        const uint16_t* w = a.w1 + static_cast<int64_t>(j) * nin;
-        float acc = a.b1[j];
-        for (int c = 0; c < R; ++c) acc = fmaf(bf16_to_f32(w[c]), sv[c], acc);
-        cvec[j] = acc;
-    }
-    __syncthreads();
 
-    const int kq = 8 * (l >> 4);
-    const int nrt = (K + 15) / 16;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
     const int nidx = K * K;
     constexpr int kMaxPer = 16;     // (a, b) pairs per thread: K^2 / 256 for K = 64
     float dacc[kMaxPer];
@@ -104,38 +144,18 @@ __global__ __launch_bounds__(256) void mlp_kernel(MlpArgs a) {
     for (int jb0 = 0; jb0 < h; jb0 += JB) {
         const int jn = min(JB, h - jb0);
         const int nct = jn / 16;
-        // ---- P (which = 0) and Q (which = 1) for this block of hidden units
-        for (int job = wave; job < 2 * nct; job += 4) {
-            const int which = job / nct, ct = job % nct;
-            const int j = jb0 + ct * 16 + (l & 15);
-            const uint32_t* wrow = reinterpret_cast<const uint32_t*>(
-                a.w1 + static_cast<int64_t>(j) * nin + (which ? 2 * R : R));
-            const int64_t zrow0 = (which ? tq : tp) * K;
-            u32x4 bf[KS];
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int o = ((ks * 32 + kq) % R) / 2;    // same W1 columns for hi and lo
-                bf[ks] = u32x4{wrow[o], wrow[o + 1], wrow[o + 2], wrow[o + 3]};
+        // ---- P and Q tiles for this block of hidden units, two tiles per step
+        for (int job = wave; job < 2 * nct; job += 8) {
+            const int job2 = job + 4;
+            {
+                const int which = job / nct, ct = job % nct;
+                pq_tile<R>(a, which, jb0 + ct * 16, (which ? tq : tp) * K, K, shv, lp, lq, which ? Q : P,
+                           ct * 16, PS);
             }
-            const float wl = bf16_to_f32(a.w1[static_cast<int64_t>(j) * nin + 3 * R + which]);
-            const float cj = which ? 0.f : cvec[j];
-            for (int rt = 0; rt < nrt; ++rt) {
-                const int m = rt * 16 + (l & 15);
-                const uint16_t* zr = a.zhl + (zrow0 + (m < K ? m : 0)) * (2 * R);
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const u32x4 av = m < K ? load16(zr + ks * 32 + kq) : zero;
-                    acc = mfma16x16x32(av, bf[ks], acc);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int mm = rt * 16 + 4 * (l >> 4) + i;
-                    if (mm < K) {
-                        const float lv = which ? lq[mm] : lp[mm];
-                        (which ? Q : P)[mm * PS + ct * 16 + (l & 15)] = acc[i] + fmaf(wl, lv, cj);
-                    }
-                }
+            if (job2 < 2 * nct) {
+                const int which = job2 / nct, ct = job2 % nct;
+                pq_tile<R>(a, which, jb0 + ct * 16, (which ? tq : tp) * K, K, shv, lp, lq, which ? Q : P,
+                           ct * 16, PS);
             }
         }
         __syncthreads();

@@ -1,15 +1,17 @@
 // Steps (2) and (3) of the DCOCO method details: the LayerNorm-projected
 // candidate representations and the per-slot halves of the pair state.
 //
-//   hproj  one MFMA GEMM over the drafter hidden states h [rows][d] against the
-//          stacked [W_ctx; W_pair[:, :d]; W_pair[:, d:]] ([3r][d]): each slot's
-//          hidden row is read once and yields W_ctx h (for g), the left half
-//          W_pair,L h (for pairs that start at the slot) and the right half
-//          W_pair,R h (for pairs that end at it).  The d reduction is split
-//          over `splits` workgroups; consumers add the partials in split order.
+//   gemm   a tiled MFMA GEMM used for (i) hproj: the drafter hidden states h
+//          [rows][d] against the stacked [W_ctx; W_pair[:, :d]; W_pair[:, d:]]
+//          ([3r][d]): each slot's hidden row is read once and yields W_ctx h
+//          (for g), the left half W_pair,L h (for pairs that start at the
+//          slot) and the right half W_pair,R h (for pairs that end at it); and
+//          (ii) u = W_cand E[c] over the gathered embedding rows of all
+//          candidates (or over the whole table, to fold it once).  The
+//          reduction is split over a fixed number of workgroups per shape;
+//          consumers add the partials in split order.
 //   cand   one workgroup per drafted slot and group of up to 16 candidates:
-//          gathers the candidates' embedding rows E[c], u = W_cand E[c] on
-//          MFMA, b = LN(u) (non-affine), g = LN(W_ctx h) from hproj,
+//          b = LN(u) (non-affine), g = LN(W_ctx h) from hproj,
 //          y = W_fuse [b; g] on MFMA, z = gamma * LN(y) + beta, stored as
 //          bf16 hi | lo halves.  The cosine variant also forms unit(W_out z)
 //          and unit(W_in z).  MFMA operands that are not already bf16 (b, g,
@@ -23,67 +25,138 @@ namespace corr {
 
 namespace {
 
-// ------------------------------------------------------------------ hproj --
-// Grid: x = waves / 4 (wave -> (row tile, 64-column group)), y = d-split.
-__global__ __launch_bounds__(256) void hproj_kernel(
-    const uint16_t* __restrict__ hidden, int64_t h_req_stride, int64_t h_slot_stride, int B,
-    int64_t rows, int d, int r, const uint16_t* __restrict__ w_ctx,
-    const uint16_t* __restrict__ w_pair, int kper, float* __restrict__ hproj) {
-    const int l = lane_id();
-    const int ncols = 3 * r;                      // output row stride
-    const int ncomp = w_pair ? 3 * r : r;         // columns computed (no pair state: W_ctx only)
-    const int ncg = (ncomp + 63) / 64;
-    const int64_t w = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-    const int64_t nrt = (rows + 15) / 16;
-    if (w >= nrt * ncg) return;
-    const int64_t rt = w / ncg;
-    const int cg = static_cast<int>(w % ncg);
-    const int sk = blockIdx.y;
-    const int k_lo = sk * kper;
-    const int k_hi = min(d, k_lo + kper);
+// ------------------------------------------------------------------- gemm --
+// C[split][m][n] = sum over the split's k range of A[m][k] * W[n][k], float32,
+// for bf16 A and W stored K-contiguous.  A rows are gathered (embedding rows of
+// candidate ids), strided (drafter hidden rows of a slot block) or dense; W
+// rows come from up to three blocks of nb rows.  Tile 64 x 128, K slab 64,
+// double-buffered in LDS with the next slab's global loads in flight during
+// the MFMAs; 4 waves in 2 x 2, each 32 x 64 (2 x 4 v_mfma_f32_16x16x32_bf16).
 
-    const int64_t arow = rt * 16 + (l & 15);
-    const bool arow_ok = arow < rows;
-    const uint16_t* ap = hidden;
-    if (arow_ok) ap = hidden + (arow / B) * h_req_stride + (arow % B) * h_slot_stride;
-    const int kq = 8 * (l >> 4);
+constexpr int kBM = 64, kBN = 128, kBK = 64, kLS = kBK + 8;  // LDS row stride (bf16)
 
-    const uint16_t* bp[4];
-    bool bok[4];
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-        const int col = cg * 64 + ct * 16 + (l & 15);
-        bok[ct] = col < ncomp;
-        const int c = bok[ct] ? col : 0;
-        if (c < r) bp[ct] = w_ctx + static_cast<int64_t>(c) * d;
-        else if (c < 2 * r) bp[ct] = w_pair + static_cast<int64_t>(c - r) * (2 * d);
-        else bp[ct] = w_pair + static_cast<int64_t>(c - 2 * r) * (2 * d) + d;
-    }
-
-    f32x4 acc[4];
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-
-    for (int k0 = k_lo; k0 < k_hi; k0 += 32) {
-        const u32x4 a = arow_ok ? load16(ap + k0 + kq) : zero;
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-            const u32x4 b = bok[ct] ? load16(bp[ct] + k0 + kq) : zero;
-            acc[ct] = mfma16x16x32(a, b, acc[ct]);
+__device__ __forceinline__ const uint16_t* a_row(const GemmA& A, int64_t m) {
+    switch (A.mode) {
+        case GEMM_A_GATHER: {
+            int64_t id = A.ids[m];
+            id = id < 0 ? 0 : (id >= A.V ? A.V - 1 : id);
+            return A.base + id * A.lda;
         }
+        case GEMM_A_SLOTS:
+            return A.base + (m / A.B) * A.rs + (m % A.B) * A.ss;
+        default:
+            return A.base + m * A.lda;
     }
-    float* out = hproj + static_cast<int64_t>(sk) * rows * ncols;
+}
+
+__global__ __launch_bounds__(256) void gemm_kernel(GemmA A, GemmW W, int64_t M, int N, int kper, int kdim,
+                                                   float* __restrict__ C) {
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM * kLS];
+    __shared__ __attribute__((aligned(16))) uint16_t Ws[2][kBN * kLS];
+    const int tid = threadIdx.x;
+    const int l = lane_id();
+    const int wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t m0 = static_cast<int64_t>(blockIdx.x) * kBM;
+    const int n0 = blockIdx.y * kBN;
+    const int split = blockIdx.z;
+    const int k_lo = split * kper;
+    const int k_hi = min(kdim, k_lo + kper);
+
+    // per-thread load assignments: 2 A segments, 4 W segments of 16 bytes
+    const uint16_t* ap[2];
+    bool aok[2];
+    int aoff[2];
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-        const int col = cg * 64 + ct * 16 + (l & 15);
-        if (col >= ncomp) continue;
+    for (int i = 0; i < 2; ++i) {
+        const int seg = tid + 256 * i;
+        const int r = seg >> 3;
+        aoff[i] = r * kLS + (seg & 7) * 8;
+        aok[i] = m0 + r < M;
+        ap[i] = (aok[i] ? a_row(A, m0 + r) : A.base) + (seg & 7) * 8;
+    }
+    const uint16_t* wp[4];
+    bool wok[4];
+    int woff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int seg = tid + 256 * i;
+        const int r = seg >> 3;
+        const int n = n0 + r;
+        woff[i] = r * kLS + (seg & 7) * 8;
+        wok[i] = n < N;
+        const int nn = wok[i] ? n : 0;
+        const int b = nn / W.nb;
+        wp[i] = W.base[b] + static_cast<int64_t>(nn % W.nb) * W.ld[b] + (seg & 7) * 8;
+    }
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    u32x4 ra[2], rw[4];
+    auto load = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int kk = k0 + ((tid + 256 * i) & 7) * 8;
+            ra[i] = (aok[i] && kk < k_hi) ? load16(ap[i] + k0) : zero;
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int64_t row = rt * 16 + 4 * (l >> 4) + i;
-            if (row < rows) out[row * ncols + col] = acc[ct][i];
+            const int kk = k0 + ((tid + 256 * i) & 7) * 8;
+            rw[i] = (wok[i] && kk < k_hi) ? load16(wp[i] + k0) : zero;
         }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4*>(&As[buf][aoff[i]]) = ra[i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&Ws[buf][woff[i]]) = rw[i];
+    };
+
+    f32x4 acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    if (k_lo < k_hi) {
+        load(k_lo);
+        store(0);
     }
+    __syncthreads();
+    const int kq = 8 * (l >> 4);
+    int buf = 0;
+    for (int k0 = k_lo; k0 < k_hi; k0 += kBK) {
+        const bool more = k0 + kBK < k_hi;
+        if (more) load(k0 + kBK);
+#pragma unroll
+        for (int ks = 0; ks < kBK; ks += 32) {
+            u32x4 af[2], wf[4];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                af[i] = *reinterpret_cast<const u32x4*>(&As[buf][(wm * 32 + i * 16 + (l & 15)) * kLS + ks + kq]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                wf[j] = *reinterpret_cast<const u32x4*>(&Ws[buf][(wn * 64 + j * 16 + (l & 15)) * kLS + ks + kq]);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(af[i], wf[j], acc[i][j]);
+        }
+        if (more) store(buf ^ 1);
+        __syncthreads();
+        buf ^= 1;
+    }
+    float* out = C + static_cast<int64_t>(split) * M * N;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int n = n0 + wn * 64 + j * 16 + (l & 15);
+            if (n >= N) continue;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t m = m0 + wm * 32 + i * 16 + 4 * (l >> 4) + e;
+                if (m < M) out[m * N + n] = acc[i][j][e];
+            }
+        }
 }
 
 // ------------------------------------------------------------------- cand --
@@ -155,7 +228,6 @@ __global__ __launch_bounds__(256) void cand_kernel(CandArgs a) {
     const int M = min(kCandRows, a.K - m0);
     const int r = a.r;
     const int nct = r / 16;
-    const int kq = 8 * (l >> 4);
 
     extern __shared__ float smem[];
     const int us = cand_row_stride(r, a.vout ? a.dvec : 0);
@@ -164,37 +236,26 @@ __global__ __launch_bounds__(256) void cand_kernel(CandArgs a) {
     float* gbuf = ubuf + kCandRows * us;                       // [128]
     uint16_t* abuf = reinterpret_cast<uint16_t*>(gbuf + 128);  // [16][as] bf16
 
-    // ---- u = E[c] W_cand^T (MFMA; E and W_cand are bf16, exact products)
-    {
-        const int m = l & 15;
-        const bool eok = m < M;
-        int64_t tok = eok ? a.ids[t * a.K + m0 + m] : 0;
-        tok = tok < 0 ? 0 : (tok >= a.V ? a.V - 1 : tok);
-        const uint16_t* ep = a.embed + tok * a.de;
-        const int ct0 = wave, ct1 = wave + 4;
-        const bool c0ok = ct0 < nct, c1ok = ct1 < nct;
-        const uint16_t* wp0 = a.w_cand + static_cast<int64_t>((c0ok ? ct0 : 0) * 16 + m) * a.de;
-        const uint16_t* wp1 = a.w_cand + static_cast<int64_t>((c1ok ? ct1 : 0) * 16 + m) * a.de;
-        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-        const u32x4 zero = {0u, 0u, 0u, 0u};
-        if (c0ok) {
-            for (int k0 = 0; k0 < a.de; k0 += 32) {
-                const u32x4 av = eok ? load16(ep + k0 + kq) : zero;
-                acc0 = mfma16x16x32(av, load16(wp0 + k0 + kq), acc0);
-                if (c1ok) acc1 = mfma16x16x32(av, load16(wp1 + k0 + kq), acc1);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int mm = 4 * (l >> 4) + i;
-                ubuf[mm * us + ct0 * 16 + m] = acc0[i];
-                if (c1ok) ubuf[mm * us + ct1 * 16 + m] = acc1[i];
-            }
+    // ---- u = W_cand E[c]: the GEMM partials summed in split order, or a row of
+    // the folded table T = E W_cand^T
+    for (int idx = threadIdx.x; idx < M * r; idx += blockDim.x) {
+        const int m = idx / r, c = idx % r;
+        const int64_t node = t * a.K + m0 + m;
+        float u;
+        if (a.table) {
+            int64_t tok = a.ids[node];
+            tok = tok < 0 ? 0 : (tok >= a.V ? a.V - 1 : tok);
+            u = a.table[tok * r + c];
+        } else {
+            u = 0.f;
+            for (int sk = 0; sk < a.usplits; ++sk) u += a.upart[(sk * a.rows * a.K + node) * r + c];
         }
+        ubuf[m * us + c] = u;
     }
     // ---- g pre-activation: the hproj partials summed in split order
     for (int c = threadIdx.x; c < r; c += blockDim.x) {
         float s = 0.f;
-        for (int sk = 0; sk < a.splits; ++sk) s += a.hproj[(static_cast<int64_t>(sk) * a.rows + t) * (3 * r) + c];
+        for (int sk = 0; sk < a.splits; ++sk) s += a.hproj[(static_cast<int64_t>(sk) * a.rows + t) * a.hstride + c];
         gbuf[c] = s;
     }
     __syncthreads();
@@ -266,15 +327,12 @@ __global__ __launch_bounds__(256) void cand_kernel(CandArgs a) {
 
 }  // namespace
 
-hipError_t launch_hproj(const uint16_t* hidden, int64_t h_req_stride, int64_t h_slot_stride,
-                        int B, int64_t rows, int d, int r, const uint16_t* w_ctx,
-                        const uint16_t* w_pair, int splits, float* hproj, hipStream_t stream) {
-    const int ncg = ((w_pair ? 3 * r : r) + 63) / 64;
-    const int64_t waves = ((rows + 15) / 16) * ncg;
-    const int kper = ((d / 32 + splits - 1) / splits) * 32;
-    const dim3 grid(static_cast<unsigned>((waves + 3) / 4), static_cast<unsigned>(splits));
-    hproj_kernel<<<grid, 256, 0, stream>>>(hidden, h_req_stride, h_slot_stride, B, rows, d, r,
-                                           w_ctx, w_pair, kper, hproj);
+hipError_t launch_gemm(const GemmA& A, const GemmW& W, int64_t M, int N, int kdim, int splits, float* C,
+                       hipStream_t stream) {
+    const int kper = ((kdim / 32 + splits - 1) / splits) * 32;
+    const dim3 grid(static_cast<unsigned>((M + kBM - 1) / kBM), static_cast<unsigned>((N + kBN - 1) / kBN),
+                    static_cast<unsigned>(splits));
+    gemm_kernel<<<grid, 256, 0, stream>>>(A, W, M, N, kper, kdim, C);
     return hipGetLastError();
 }
 

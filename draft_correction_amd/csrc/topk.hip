@@ -3,19 +3,21 @@
 //
 // Two launches:
 //   topk_partial  one wave per (row, chunk): a chunk of the row (8192 bf16 or
-//                 4096 float32 logits) is streamed with 16-byte coalesced loads
-//                 into registers.  The wave takes the target-th largest of its
-//                 64 lane maxima as a threshold (a lower bound of the chunk's
-//                 K-th largest value), compacts the few elements at or above
-//                 it into LDS, and selects the exact top-K of the chunk by a
-//                 bitwise search on 48-bit composite keys (value key << 16 |
-//                 inverted local index), so equal values order by id.  If the
-//                 compacted set overflows LDS (heavy ties) the same search runs
-//                 over all register-resident elements instead.
-//   topk_merge    one wave per row: the chunks' candidates (value key, id)
-//                 become 64-bit composites (value key << 32 | inverted id);
-//                 the K largest are found by the same bitwise search and
-//                 written in order.
+//                 4096 float32 logits) is streamed into registers with 16-byte
+//                 coalesced loads.  bf16 path: one packed pass (v_pk_max_i16 /
+//                 v_pk_min_u16 over pairs of logits) gives every lane its
+//                 maximum; the target-th largest lane maximum is a threshold
+//                 at or below the chunk's K-th largest value; a second packed
+//                 pass flags the 16-byte vectors holding an element at or above
+//                 it and stages them in LDS; their elements become 32-bit
+//                 composite keys (order-preserving value key << 16 | inverted
+//                 local index) and a bitwise search selects the exact top-K of
+//                 the chunk.  If the staged set overflows (heavy ties) an exact
+//                 search over every register-resident element takes over.
+//   topk_merge    one wave per row: the chunks' candidates, as 64-bit
+//                 composites (value key << 32 | inverted token id), go through
+//                 the same threshold-then-search selection and the K winners
+//                 are written in order.
 // Keys map float bits to an unsigned integer order with -0 == +0, so the
 // selection is exact integer work: results are bit-identical to a full sort.
 #include "common.h"
@@ -25,121 +27,297 @@ namespace corr {
 
 namespace {
 
-constexpr int kNV = 16;     // 16-byte loads per lane
-constexpr int kCap = 256;   // compacted candidates per wave
+constexpr int kNV = 16;        // 16-byte loads per lane
+constexpr int kCap = 256;      // compacted candidates per wave (float32 path)
+constexpr int kStage = 64;     // staged 16-byte vectors per wave (bf16 path)
+constexpr int kCand16 = 256;   // candidate keys per wave (bf16 path)
 
-template <int DT>
-struct TopkShape {
-    static constexpr int kEPV = DT == CORR_DT_BF16 ? 8 : 4;   // elements per 16-byte load
-    static constexpr int kEPL = kNV * kEPV;                   // elements per lane
-    static constexpr int kChunk = kEPL * kWave;               // elements per wave
-    static constexpr int kElem = DT == CORR_DT_BF16 ? 2 : 4;  // bytes per element
-};
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-// Float32 bits of element j of a 16-byte vector.
-template <int DT>
-__device__ __forceinline__ uint32_t elem_bits(const u32x4& v, int j) {
-    if constexpr (DT == CORR_DT_BF16) {
-        const uint32_t w = v[j >> 1];
-        return (j & 1) ? (w & 0xFFFF0000u) : (w << 16);
-    } else {
-        return v[j];
+__device__ __forceinline__ uint32_t pk_max_i16(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(i16x2, a),
+                                                                  __builtin_bit_cast(i16x2, b)));
+}
+__device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, a),
+                                                                  __builtin_bit_cast(u16x2, b)));
+}
+
+// Order-preserving 16-bit key of a bf16 bit pattern (-0 and +0 share 0x8000;
+// -inf -> 0x007F; the NaN pattern 0xFFFF used for padding -> 0).
+__device__ __forceinline__ uint32_t key16_of(uint32_t x) {
+    return (x & 0x8000u) ? ((x == 0x8000u) ? 0x8000u : (0xFFFFu - x)) : (x | 0x8000u);
+}
+__device__ __forceinline__ uint32_t raw16_of_key16(uint32_t k) {
+    return (k & 0x8000u) ? (k & 0x7FFFu) : (0xFFFFu - k);
+}
+
+// 64-bit merge composite: value key (float32 order) << 32 | inverted token id.
+__device__ __forceinline__ uint64_t merge_comp(uint32_t key32, int64_t gid) {
+    return (static_cast<uint64_t>(key32) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(gid));
+}
+
+// ------------------------------------------------------------- bf16 path --
+
+// Bf16 element `local` of a chunk (0xFFFF, key 0, past the end).
+__device__ __forceinline__ uint32_t chunk_elem(const uint16_t* src, int nvalid, int local) {
+    return local < nvalid ? static_cast<uint32_t>(src[local]) : 0xFFFFu;
+}
+
+// Exact top-`target` of a chunk by a bitwise search over the 32-bit composites
+// of every element, re-read from memory (used only when the threshold admits
+// too many elements, i.e. heavy ties).  Writes the winners unordered and
+// returns how many were written.
+__device__ __noinline__ int topk_bf16_exhaustive(const uint16_t* src, int nvalid, int64_t c0, int K,
+                                                 int target, uint64_t* out) {
+    constexpr int kChunk = kNV * 8 * kWave;
+    const int l = lane_id();
+    uint32_t tc = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t c = tc | (1u << bit);
+        int cnt = 0;
+#pragma unroll 1
+        for (int local0 = 0; local0 < kChunk; local0 += kWave) {
+            const int local = local0 + l;
+            const uint32_t comp = (key16_of(chunk_elem(src, nvalid, local)) << 16) | (0xFFFFu - local);
+            cnt += popc64(ballot(comp >= c));
+        }
+        if (cnt >= target) tc = c;
     }
+    int outn = 0;
+#pragma unroll 1
+    for (int local0 = 0; local0 < kChunk; local0 += kWave) {
+        const int local = local0 + l;
+        const uint32_t k16 = key16_of(chunk_elem(src, nvalid, local));
+        const bool p = ((k16 << 16) | (0xFFFFu - local)) >= tc && k16 != 0u;
+        const uint64_t m = ballot(p);
+        const int pos = outn + prefix_count(m);
+        if (p && pos < K) out[pos] = merge_comp(key_of_bits(raw16_of_key16(k16) << 16), c0 + local);
+        outn += popc64(m);
+    }
+    return outn;
 }
 
-template <int DT>
-__device__ __forceinline__ uint32_t elem_key(const u32x4* raw, int t, int j) {
-    return key_of_bits(elem_bits<DT>(raw[t], j));
-}
-
-template <int DT>
-__global__ __launch_bounds__(256) void topk_partial_kernel(
-    const char* __restrict__ logits, int64_t req_stride, int64_t slot_stride, int B, int64_t V,
-    int K, int chunks, int64_t rows, uint32_t* __restrict__ part_key,
-    int32_t* __restrict__ part_id) {
-    using S = TopkShape<DT>;
-    __shared__ uint64_t cand_all[4][kCap];
+__global__ __launch_bounds__(256) void topk_partial_bf16_kernel(
+    const uint16_t* __restrict__ logits, int64_t req_stride, int64_t slot_stride, int B, int64_t V,
+    int K, int chunks, int64_t rows, uint64_t* __restrict__ part) {
+    constexpr int kChunk = kNV * 8 * kWave;  // 8192 logits per wave
+    __shared__ u32x4 stage_all[4][kStage];
+    __shared__ uint16_t meta_all[4][kStage];
+    __shared__ uint32_t cand_all[4][kCand16];
     const int wave = threadIdx.x >> 6;
     const int l = lane_id();
     const int64_t w = static_cast<int64_t>(blockIdx.x) * 4 + wave;
     if (w >= rows * chunks) return;  // whole wave; this kernel has no block barrier
-    uint64_t* cand = cand_all[wave];
+    u32x4* stage = stage_all[wave];
+    uint16_t* meta = meta_all[wave];
+    uint32_t* cand = cand_all[wave];
     const int64_t row = w / chunks;
     const int chunk = static_cast<int>(w % chunks);
     const int64_t req = row / B, slot = row % B;
-    const int64_t c0 = static_cast<int64_t>(chunk) * S::kChunk;
-    const char* src = logits + (req * req_stride + slot * slot_stride + c0) * S::kElem;
-    const int nvalid = static_cast<int>(min(static_cast<int64_t>(S::kChunk), V - c0));
+    const int64_t c0 = static_cast<int64_t>(chunk) * kChunk;
+    const uint16_t* src = logits + req * req_stride + slot * slot_stride + c0;
+    const int nvalid = static_cast<int>(min(static_cast<int64_t>(kChunk), V - c0));
 
-    // Stream the chunk into registers.  Elements past the row end get a NaN
-    // pattern whose key is <= kKeyFloor, i.e. "no element".
+    // ---- stream the chunk; padding elements get 0xFFFF (key 0: "no element")
     u32x4 raw[kNV];
 #pragma unroll
     for (int t = 0; t < kNV; ++t) {
-        const int e0 = (t * kWave + l) * S::kEPV;
-        if (e0 + S::kEPV <= nvalid) {
+        const int e0 = (t * kWave + l) * 8;
+        if (e0 + 8 <= nvalid) {
             raw[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + t * kWave + l);
         } else {
             u32x4 v = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
-            for (int j = 0; j < S::kEPV; ++j) {
+            for (int j = 0; j < 8; ++j) {
                 if (e0 + j < nvalid) {
-                    if constexpr (DT == CORR_DT_BF16) {
-                        const uint32_t b = reinterpret_cast<const uint16_t*>(src)[e0 + j];
-                        const int q = j >> 1;
-                        v[q] = (j & 1) ? ((v[q] & 0x0000FFFFu) | (b << 16)) : ((v[q] & 0xFFFF0000u) | b);
-                    } else {
-                        v[j] = reinterpret_cast<const uint32_t*>(src)[e0 + j];
-                    }
+                    const uint32_t b = src[e0 + j];
+                    const int q = j >> 1;
+                    v[q] = (j & 1) ? ((v[q] & 0x0000FFFFu) | (b << 16)) : ((v[q] & 0xFFFF0000u) | b);
                 }
             }
             raw[t] = v;
         }
     }
 
-    uint32_t mx = 0;
+    // ---- lane maximum: signed max finds the largest positive, unsigned min the
+    // negative closest to zero; together they give the largest value.
+    uint32_t mxp = 0x80008000u, mnp = 0xFFFFFFFFu;
 #pragma unroll
     for (int t = 0; t < kNV; ++t)
 #pragma unroll
-        for (int j = 0; j < S::kEPV; ++j) mx = max(mx, elem_key<DT>(raw, t, j));
+        for (int q = 0; q < 4; ++q) {
+            mxp = pk_max_i16(mxp, raw[t][q]);
+            mnp = pk_min_u16(mnp, raw[t][q]);
+        }
+    const int mx16 = max(static_cast<int>(static_cast<int16_t>(mxp & 0xFFFFu)),
+                         static_cast<int>(static_cast<int16_t>(mxp >> 16)));
+    const uint32_t mn16 = min(mnp & 0xFFFFu, mnp >> 16);
+    const uint32_t lane_key = key16_of(mx16 >= 0 ? static_cast<uint32_t>(mx16) : mn16);
 
+    // ---- threshold: the target-th largest lane maximum (at least `target`
+    // distinct elements are >= it, so the chunk's top-`target` are too)
     const int target = min(K, nvalid);
-    // thr = target-th largest lane maximum: at least `target` distinct
-    // elements of the chunk are >= thr, so the chunk's top-`target` are too.
     uint32_t thr = 0;
-    for (int bit = 31; bit >= 0; --bit) {
+    for (int bit = 15; bit >= 0; --bit) {
         const uint32_t c = thr | (1u << bit);
-        if (popc64(ballot(mx >= c)) >= target) thr = c;
+        if (popc64(ballot(lane_key >= c)) >= target) thr = c;
     }
-    thr = max(thr, kKeyFloor + 1);
+    thr = max(thr, 1u);
+    // Raw-domain form of "key16 >= thr": positives only (signed compare) when
+    // thr is above zero; otherwise an unsigned bound that admits every
+    // non-negative value, both zeros and negatives down to the threshold.
+    const bool posmode = thr > 0x8000u;
+    const uint32_t tpos = posmode ? thr - 0x8000u - 1u : 0u;                 // raw > tpos
+    const uint32_t uneg = thr == 0x8000u ? 0x8000u : 0xFFFFu - thr;          // raw <= uneg
+    const uint32_t tpos2 = tpos | (tpos << 16);
+    const uint32_t uneg2 = (uneg + 1u) | ((uneg + 1u) << 16);
 
-    // Compact the elements >= thr into LDS, in (load, lane, element) order.
-    int total = 0;
+    // ---- stage the vectors that hold at least one element >= threshold
+    int nst = 0;
 #pragma unroll
     for (int t = 0; t < kNV; ++t) {
+        bool hit = false;
 #pragma unroll
-        for (int j = 0; j < S::kEPV; ++j) {
-            const uint32_t k = elem_key<DT>(raw, t, j);
-            const bool p = k >= thr;
-            const uint64_t m = ballot(p);
-            if (m) {
-                const int pos = total + prefix_count(m);
-                const uint32_t local = static_cast<uint32_t>((t * kWave + l) * S::kEPV + j);
-                if (p && pos < kCap) cand[pos] = (static_cast<uint64_t>(k) << 16) | (0xFFFFu - local);
-                total += popc64(m);
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t x = raw[t][q];
+            hit |= posmode ? (pk_max_i16(x, tpos2) != tpos2) : (pk_min_u16(x, uneg2) != uneg2);
+        }
+        const uint64_t m = ballot(hit);
+        if (m) {
+            const int pos = nst + prefix_count(m);
+            if (hit && pos < kStage) {
+                stage[pos] = raw[t];
+                meta[pos] = static_cast<uint16_t>(t * kWave + l);
             }
+            nst += popc64(m);
         }
     }
     wave_lds_sync();
 
     const int64_t obase = (row * chunks + chunk) * K;
     int outn = 0;
+    bool fast = nst <= kStage;
+    int nc = 0;
+    if (fast) {
+        // elements of the staged vectors that pass, as 32-bit composites
+        u32x4 v = {0u, 0u, 0u, 0u};
+        uint32_t vbase = 0;
+        if (l < nst) {
+            v = stage[l];
+            vbase = static_cast<uint32_t>(meta[l]) * 8u;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t x = (v[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+            const bool pass = l < nst && (posmode ? (static_cast<int>(static_cast<int16_t>(x)) > static_cast<int>(tpos))
+                                                 : (x <= uneg));
+            const uint64_t m = ballot(pass);
+            const int pos = nc + prefix_count(m);
+            if (pass && pos < kCand16) cand[pos] = (key16_of(x) << 16) | (0xFFFFu - (vbase + j));
+            nc += popc64(m);
+        }
+        fast = nc <= kCand16;
+    }
+    if (fast) {
+        wave_lds_sync();
+        uint32_t e[kCand16 / kWave];
+#pragma unroll
+        for (int q = 0; q < kCand16 / kWave; ++q) e[q] = q * kWave + l < nc ? cand[q * kWave + l] : 0u;
+        uint32_t tc = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t c = tc | (1u << bit);
+            int cnt = 0;
+#pragma unroll
+            for (int q = 0; q < kCand16 / kWave; ++q)
+                if (q * kWave < nc) cnt += popc64(ballot(e[q] >= c));
+            if (cnt >= target) tc = c;
+        }
+#pragma unroll
+        for (int q = 0; q < kCand16 / kWave; ++q) {
+            const bool p = e[q] >= tc && e[q] != 0u;
+            const uint64_t m = ballot(p);
+            const int pos = outn + prefix_count(m);
+            if (p && pos < K) {
+                const uint32_t raw16 = raw16_of_key16(e[q] >> 16);
+                part[obase + pos] = merge_comp(key_of_bits(raw16 << 16), c0 + (0xFFFFu - (e[q] & 0xFFFFu)));
+            }
+            outn += popc64(m);
+        }
+    } else {
+        outn = topk_bf16_exhaustive(src, nvalid, c0, K, target, part + obase);
+    }
+    // chunks with fewer than K elements pad with "no element"
+    for (int pos = outn + l; pos < K; pos += kWave) part[obase + pos] = 0ull;
+}
+
+// ---------------------------------------------------------- float32 path --
+// Generic version on 32-bit value keys (used for float32 logits).
+__global__ __launch_bounds__(256) void topk_partial_f32_kernel(
+    const float* __restrict__ logits, int64_t req_stride, int64_t slot_stride, int B, int64_t V,
+    int K, int chunks, int64_t rows, uint64_t* __restrict__ part) {
+    constexpr int kEPV = 4;
+    constexpr int kChunk = kNV * kEPV * kWave;  // 4096 logits per wave
+    __shared__ uint64_t cand_all[4][kCap];
+    const int wave = threadIdx.x >> 6;
+    const int l = lane_id();
+    const int64_t w = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+    if (w >= rows * chunks) return;
+    uint64_t* cand = cand_all[wave];
+    const int64_t row = w / chunks;
+    const int chunk = static_cast<int>(w % chunks);
+    const int64_t req = row / B, slot = row % B;
+    const int64_t c0 = static_cast<int64_t>(chunk) * kChunk;
+    const float* src = logits + req * req_stride + slot * slot_stride + c0;
+    const int nvalid = static_cast<int>(min(static_cast<int64_t>(kChunk), V - c0));
+
+    u32x4 raw[kNV];
+#pragma unroll
+    for (int t = 0; t < kNV; ++t) {
+        const int e0 = (t * kWave + l) * kEPV;
+        if (e0 + kEPV <= nvalid) {
+            raw[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + t * kWave + l);
+        } else {
+            u32x4 v = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};  // key 0
+            for (int j = 0; j < kEPV; ++j)
+                if (e0 + j < nvalid) v[j] = reinterpret_cast<const uint32_t*>(src)[e0 + j];
+            raw[t] = v;
+        }
+    }
+    uint32_t mx = 0;
+#pragma unroll
+    for (int t = 0; t < kNV; ++t)
+#pragma unroll
+        for (int j = 0; j < kEPV; ++j) mx = max(mx, key_of_bits(raw[t][j]));
+    const int target = min(K, nvalid);
+    uint32_t thr = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t c = thr | (1u << bit);
+        if (popc64(ballot(mx >= c)) >= target) thr = c;
+    }
+    thr = max(thr, kKeyFloor + 1);
+    int total = 0;
+#pragma unroll
+    for (int t = 0; t < kNV; ++t)
+#pragma unroll
+        for (int j = 0; j < kEPV; ++j) {
+            const uint32_t k = key_of_bits(raw[t][j]);
+            const bool p = k >= thr;
+            const uint64_t m = ballot(p);
+            if (m) {
+                const int pos = total + prefix_count(m);
+                const uint32_t local = static_cast<uint32_t>((t * kWave + l) * kEPV + j);
+                if (p && pos < kCap) cand[pos] = (static_cast<uint64_t>(k) << 16) | (0xFFFFu - local);
+                total += popc64(m);
+            }
+        }
+    wave_lds_sync();
+    const int64_t obase = (row * chunks + chunk) * K;
+    int outn = 0;
     if (total <= kCap) {
         uint64_t e[kCap / kWave];
 #pragma unroll
-        for (int q = 0; q < kCap / kWave; ++q) {
-            const int idx = q * kWave + l;
-            e[q] = idx < total ? cand[idx] : 0ull;
-        }
+        for (int q = 0; q < kCap / kWave; ++q) e[q] = q * kWave + l < total ? cand[q * kWave + l] : 0ull;
         uint64_t tc = 0;
         for (int bit = 47; bit >= 0; --bit) {
             const uint64_t c = tc | (1ull << bit);
@@ -153,14 +331,11 @@ __global__ __launch_bounds__(256) void topk_partial_kernel(
             const bool p = e[q] >= tc && e[q] != 0ull;
             const uint64_t m = ballot(p);
             const int pos = outn + prefix_count(m);
-            if (p && pos < K) {
-                part_key[obase + pos] = static_cast<uint32_t>(e[q] >> 16);
-                part_id[obase + pos] = static_cast<int32_t>(c0 + (0xFFFFu - (e[q] & 0xFFFFu)));
-            }
+            if (p && pos < K)
+                part[obase + pos] = merge_comp(static_cast<uint32_t>(e[q] >> 16), c0 + (0xFFFFu - (e[q] & 0xFFFFu)));
             outn += popc64(m);
         }
     } else {
-        // Heavy ties at the threshold: exact search over every element.
         uint64_t tc = 0;
         for (int bit = 47; bit >= 0; --bit) {
             const uint64_t c = tc | (1ull << bit);
@@ -168,115 +343,131 @@ __global__ __launch_bounds__(256) void topk_partial_kernel(
 #pragma unroll
             for (int t = 0; t < kNV; ++t)
 #pragma unroll
-                for (int j = 0; j < S::kEPV; ++j) {
-                    const uint32_t local = static_cast<uint32_t>((t * kWave + l) * S::kEPV + j);
-                    const uint64_t comp = (static_cast<uint64_t>(elem_key<DT>(raw, t, j)) << 16) | (0xFFFFu - local);
-                    cnt += popc64(ballot(comp >= c));
+                for (int j = 0; j < kEPV; ++j) {
+                    const uint32_t local = static_cast<uint32_t>((t * kWave + l) * kEPV + j);
+                    cnt += popc64(ballot(((static_cast<uint64_t>(key_of_bits(raw[t][j])) << 16) | (0xFFFFu - local)) >= c));
                 }
             if (cnt >= target) tc = c;
         }
 #pragma unroll
         for (int t = 0; t < kNV; ++t)
 #pragma unroll
-            for (int j = 0; j < S::kEPV; ++j) {
-                const uint32_t local = static_cast<uint32_t>((t * kWave + l) * S::kEPV + j);
-                const uint32_t k = elem_key<DT>(raw, t, j);
-                const uint64_t comp = (static_cast<uint64_t>(k) << 16) | (0xFFFFu - local);
-                const bool p = comp >= tc && k > kKeyFloor;
+            for (int j = 0; j < kEPV; ++j) {
+                const uint32_t local = static_cast<uint32_t>((t * kWave + l) * kEPV + j);
+                const uint32_t k = key_of_bits(raw[t][j]);
+                const bool p = ((static_cast<uint64_t>(k) << 16) | (0xFFFFu - local)) >= tc && k > kKeyFloor;
                 const uint64_t m = ballot(p);
                 const int pos = outn + prefix_count(m);
-                if (p && pos < K) {
-                    part_key[obase + pos] = k;
-                    part_id[obase + pos] = static_cast<int32_t>(c0 + local);
-                }
+                if (p && pos < K) part[obase + pos] = merge_comp(k, c0 + local);
                 outn += popc64(m);
             }
     }
-    // Chunks with fewer than K elements pad with "no element".
-    for (int pos = outn + l; pos < K; pos += kWave) {
-        part_key[obase + pos] = 0u;
-        part_id[obase + pos] = -1;
-    }
+    for (int pos = outn + l; pos < K; pos += kWave) part[obase + pos] = 0ull;
 }
 
-// One wave per row; the row's chunk candidates are staged in dynamic LDS.
-__global__ __launch_bounds__(64) void topk_merge_kernel(
-    const uint32_t* __restrict__ part_key, const int32_t* __restrict__ part_id, int chunks, int K,
-    int64_t rows, int32_t* __restrict__ ids, float* __restrict__ vals) {
-    extern __shared__ uint64_t ent[];
-    __shared__ uint64_t sel[64];
+// ------------------------------------------------------------------ merge --
+// One wave selects the K largest of M 64-bit composites of one row and writes
+// them in order.  Lane maxima give a threshold (K-th largest lane maximum);
+// the entries at or above it (usually K..2K of them) are compacted into LDS
+// and searched bitwise; with more than kMergeCap of them the search runs over
+// all entries.
+constexpr int kMergeCap = 128;
+
+__device__ void merge_row_wave(const uint64_t* __restrict__ ent, int M, int K, uint64_t* sel,
+                               uint64_t* fin, int32_t* __restrict__ ids, float* __restrict__ vals) {
     const int l = lane_id();
-    const int64_t row = blockIdx.x;
-    if (row >= rows) return;
-    const int M = chunks * K;
-    const int64_t ibase = row * M;
-    for (int q = l; q < M; q += kWave) {
-        const uint32_t k = part_key[ibase + q];
-        const int32_t id = part_id[ibase + q];
-        ent[q] = (k > kKeyFloor && id >= 0)
-                     ? ((static_cast<uint64_t>(k) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(id)))
-                     : 0ull;
+    uint64_t lm = 0;
+    for (int q = l; q < M; q += kWave) lm = max(lm, ent[q]);
+    uint64_t thr = 0;
+    for (int bit = 63; bit >= 0; --bit) {
+        const uint64_t c = thr | (1ull << bit);
+        if (popc64(ballot(lm >= c)) >= K) thr = c;
+    }
+    int n = 0;
+    for (int q0 = 0; q0 < M; q0 += kWave) {
+        const int q = q0 + l;
+        const uint64_t e = q < M ? ent[q] : 0ull;
+        const bool p = q < M && e >= thr && e != 0ull;
+        const uint64_t m = ballot(p);
+        const int pos = n + prefix_count(m);
+        if (p && pos < kMergeCap) sel[pos] = e;
+        n += popc64(m);
     }
     wave_lds_sync();
     uint64_t tc = 0;
-    for (int bit = 63; bit >= 0; --bit) {
-        const uint64_t c = tc | (1ull << bit);
-        int cnt = 0;
-        for (int q0 = 0; q0 < M; q0 += kWave) {
-            const int q = q0 + l;
-            cnt += popc64(ballot(q < M && ent[q] >= c));
+    if (n <= kMergeCap) {
+        const uint64_t e0 = l < n ? sel[l] : 0ull;
+        const uint64_t e1 = l + kWave < n ? sel[l + kWave] : 0ull;
+        for (int bit = 63; bit >= 0; --bit) {
+            const uint64_t c = tc | (1ull << bit);
+            if (popc64(ballot(e0 >= c)) + popc64(ballot(e1 >= c)) >= K) tc = c;
         }
-        if (cnt >= K) tc = c;
+    } else {
+        for (int bit = 63; bit >= 0; --bit) {
+            const uint64_t c = tc | (1ull << bit);
+            int cnt = 0;
+            for (int q0 = 0; q0 < M; q0 += kWave) {
+                const int q = q0 + l;
+                cnt += popc64(ballot(q < M && ent[q] >= c));
+            }
+            if (cnt >= K) tc = c;
+        }
     }
+    // exactly K distinct composites are >= tc
     int outn = 0;
     for (int q0 = 0; q0 < M; q0 += kWave) {
         const int q = q0 + l;
-        const bool p = q < M && ent[q] >= tc && ent[q] != 0ull;
+        const uint64_t e = q < M ? ent[q] : 0ull;
+        const bool p = q < M && e >= tc && e != 0ull;
         const uint64_t m = ballot(p);
         const int pos = outn + prefix_count(m);
-        if (p && pos < 64) sel[pos] = ent[q];
+        if (p && pos < K) fin[pos] = e;
         outn += popc64(m);
     }
     wave_lds_sync();
     if (l < K) {
-        const uint64_t me = sel[l];
+        const uint64_t me = fin[l];
         int rank = 0;
-        for (int m2 = 0; m2 < K; ++m2) rank += sel[m2] > me ? 1 : 0;
-        const uint32_t key = static_cast<uint32_t>(me >> 32);
-        const int32_t id = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(me & 0xFFFFFFFFu));
-        ids[row * K + rank] = id;
-        vals[row * K + rank] = __uint_as_float(bits_of_key(key));
+        for (int m2 = 0; m2 < K; ++m2) rank += fin[m2] > me ? 1 : 0;
+        ids[rank] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(me & 0xFFFFFFFFu));
+        vals[rank] = __uint_as_float(bits_of_key(static_cast<uint32_t>(me >> 32)));
     }
+}
+
+__global__ __launch_bounds__(256) void topk_merge_kernel(const uint64_t* __restrict__ part, int chunks,
+                                                         int K, int64_t rows, int32_t* __restrict__ ids,
+                                                         float* __restrict__ vals) {
+    __shared__ uint64_t sel_all[4][kMergeCap];
+    __shared__ uint64_t fin_all[4][64];
+    const int wave = threadIdx.x >> 6;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+    if (row >= rows) return;
+    const int M = chunks * K;
+    merge_row_wave(part + row * M, M, K, sel_all[wave], fin_all[wave], ids + row * K, vals + row * K);
 }
 
 }  // namespace
 
-int topk_chunk_elems(int dtype) {
-    return dtype == CORR_DT_BF16 ? TopkShape<CORR_DT_BF16>::kChunk : TopkShape<CORR_DT_F32>::kChunk;
-}
+int topk_chunk_elems(int dtype) { return dtype == CORR_DT_BF16 ? kNV * 8 * kWave : kNV * 4 * kWave; }
 
 hipError_t launch_topk_partial(int dtype, const void* logits, int64_t req_stride,
                                int64_t slot_stride, int B, int64_t V, int K, int chunks,
-                               int64_t rows, uint32_t* part_key, int32_t* part_id,
-                               hipStream_t stream) {
+                               int64_t rows, uint64_t* part, hipStream_t stream) {
     const int64_t waves = rows * chunks;
     const dim3 grid(static_cast<unsigned>((waves + 3) / 4));
     if (dtype == CORR_DT_BF16)
-        topk_partial_kernel<CORR_DT_BF16><<<grid, 256, 0, stream>>>(
-            static_cast<const char*>(logits), req_stride, slot_stride, B, V, K, chunks, rows,
-            part_key, part_id);
+        topk_partial_bf16_kernel<<<grid, 256, 0, stream>>>(static_cast<const uint16_t*>(logits), req_stride,
+                                                           slot_stride, B, V, K, chunks, rows, part);
     else
-        topk_partial_kernel<CORR_DT_F32><<<grid, 256, 0, stream>>>(
-            static_cast<const char*>(logits), req_stride, slot_stride, B, V, K, chunks, rows,
-            part_key, part_id);
+        topk_partial_f32_kernel<<<grid, 256, 0, stream>>>(static_cast<const float*>(logits), req_stride,
+                                                          slot_stride, B, V, K, chunks, rows, part);
     return hipGetLastError();
 }
 
-hipError_t launch_topk_merge(const uint32_t* part_key, const int32_t* part_id, int chunks, int K,
-                             int64_t rows, int32_t* ids, float* vals, hipStream_t stream) {
-    const size_t lds = static_cast<size_t>(chunks) * K * sizeof(uint64_t);
-    topk_merge_kernel<<<dim3(static_cast<unsigned>(rows)), 64, lds, stream>>>(
-        part_key, part_id, chunks, K, rows, ids, vals);
+hipError_t launch_topk_merge(const uint64_t* part, int chunks, int K, int64_t rows, int32_t* ids,
+                             float* vals, hipStream_t stream) {
+    topk_merge_kernel<<<dim3(static_cast<unsigned>((rows + 3) / 4)), 256, 0, stream>>>(part, chunks, K, rows,
+                                                                                   ids, vals);
     return hipGetLastError();
 }
 

@@ -28,21 +28,37 @@ __global__ __launch_bounds__(256) void cosine_kernel(CosArgs a) {
 
 // One wave per request.  choice[0] = 0 (rank 0 is the drafter argmax of the
 // first drafted slot); then each step takes the largest score in the row of
-// the chosen predecessor, ties to the lowest successor index.
+// the chosen predecessor, ties to the lowest successor index.  When the
+// request's scores fit (lds_rows > 0) they are first copied into LDS with
+// coalesced 16-byte loads, so the dependent steps read LDS, not memory.
 __global__ __launch_bounds__(64) void walk_kernel(const float* __restrict__ scores,
                                                   const int32_t* __restrict__ ids, int n, int B,
                                                   int K, int32_t* __restrict__ tokens,
-                                                  int32_t* __restrict__ choice) {
+                                                  int32_t* __restrict__ choice, int use_lds) {
+    extern __shared__ __attribute__((aligned(16))) float sl[];
     const int req = blockIdx.x;
     const int l = lane_id();
     if (req >= n) return;
+    const int64_t per = static_cast<int64_t>(B - 1) * K * K;
+    const float* base = scores + req * per;
+    if (use_lds) {
+        // per is a multiple of 4 when K is even; odd K copies element-wise
+        if ((K & 1) == 0 && (reinterpret_cast<uintptr_t>(base) & 15) == 0) {
+            for (int64_t i = l; i < per / 4; i += kWave)
+                reinterpret_cast<float4*>(sl)[i] = reinterpret_cast<const float4*>(base)[i];
+        } else {
+            for (int64_t i = l; i < per; i += kWave) sl[i] = base[i];
+        }
+        wave_lds_sync();
+    }
+    const float* src = use_lds ? sl : base;
     int k = 0;
     if (l == 0) {
         if (choice) choice[static_cast<int64_t>(req) * B] = 0;
         tokens[static_cast<int64_t>(req) * B] = ids[static_cast<int64_t>(req) * B * K];
     }
     for (int p = 0; p + 1 < B; ++p) {
-        const float* row = scores + ((static_cast<int64_t>(req) * (B - 1) + p) * K + k) * K;
+        const float* row = src + (static_cast<int64_t>(p) * K + k) * K;
         float v = l < K ? row[l] : -INFINITY;
         int bi = l < K ? l : 0x7FFFFFFF;
 #pragma unroll
@@ -95,7 +111,10 @@ hipError_t launch_cosine(const CosArgs& a, hipStream_t stream) {
 
 hipError_t launch_walk(const float* scores, const int32_t* ids, int n, int B, int K,
                        int32_t* tokens, int32_t* choice, hipStream_t stream) {
-    walk_kernel<<<dim3(static_cast<unsigned>(n)), 64, 0, stream>>>(scores, ids, n, B, K, tokens, choice);
+    const size_t bytes = static_cast<size_t>(B > 1 ? B - 1 : 0) * K * K * sizeof(float);
+    const int use_lds = bytes > 0 && bytes <= 60 * 1024;
+    walk_kernel<<<dim3(static_cast<unsigned>(n)), 64, use_lds ? bytes : 0, stream>>>(scores, ids, n, B, K, tokens,
+                                                                                     choice, use_lds);
     return hipGetLastError();
 }
 
