@@ -20,8 +20,8 @@ constexpr int kMaxKernels = 8;
 constexpr size_t kAlign = 256;
 
 struct Layout {
-    size_t part, ids, vals, hproj, upart, z, g, s, vout, vin, scores, total;
-    int chunks, splits, usplits;
+    size_t part, ids, vals, hproj, z, g, s, vout, vin, mlp_part, scores, total;
+    int chunks, splits;
 };
 
 }  // namespace
@@ -45,19 +45,15 @@ size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 int logits_elem_bytes(const corrector_desc& d) { return d.logits_dtype == CORR_DTYPE_BF16 ? 2 : 4; }
 
-// Splits of the two GEMM reductions (over d for the hidden-state projections,
-// over d_e for the candidate projection): functions of the widths only, so a
-// request's results do not depend on how many requests share the call.
+// Split of the hidden-state projection's reduction over d: a function of d
+// only, so a request's results do not depend on how many requests share the
+// call.
 int choose_splits(const corrector_desc& d) {
     int s = d.d_hidden / 512;
     if (s > 16) s = 16;
     return s < 1 ? 1 : s;
 }
-int choose_usplits(const corrector_desc& d) {
-    int s = d.d_embed / 1024;
-    if (s > 8) s = 8;
-    return s < 1 ? 1 : s;
-}
+
 
 Layout layout(const corrector_desc& d, int32_t n) {
     Layout L{};
@@ -66,17 +62,16 @@ Layout layout(const corrector_desc& d, int32_t n) {
     L.chunks = static_cast<int>((d.vocab + topk_chunk_elems(d.logits_dtype) - 1) /
                                 topk_chunk_elems(d.logits_dtype));
     L.splits = choose_splits(d);
-    L.usplits = choose_usplits(d);
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o = up(o + bytes); return at; };
     L.part = take(sizeof(uint64_t) * rows * L.chunks * d.k);
     L.ids = take(sizeof(int32_t) * rows * d.k);
     L.vals = take(sizeof(float) * rows * d.k);
     L.hproj = take(sizeof(float) * L.splits * rows * 3 * d.r);
-    L.upart = take(sizeof(float) * L.usplits * rows * d.k * d.r);
     L.z = take(sizeof(uint16_t) * rows * d.k * 2 * d.r);
     L.g = take(sizeof(float) * rows * d.r);
     L.s = take(sizeof(float) * pairs * d.r);
+    L.mlp_part = take(d.variant == CORR_VARIANT_MLP ? sizeof(float) * pairs * mlp_blocks(d.mlp_hidden) * d.k * d.k : 0);
     const bool cos = d.variant == CORR_VARIANT_COSINE;
     L.vout = take(cos ? sizeof(float) * rows * d.k * d.d_vec : 0);
     L.vin = take(cos ? sizeof(float) * rows * d.k * d.d_vec : 0);
@@ -156,9 +151,11 @@ void enqueue_topk(Seq& q, const corrector* h, const Layout& L, int32_t n, const 
     q("topk_merge", [&] { return launch_topk_merge(part, L.chunks, d.k, rows, ids, vals, q.s); });
 }
 
+// Steps (2)-(4); with tokens given also step (5) (fused into the MLP finish
+// for the MLP variant, a walk launch for the cosine variant).
 void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const int32_t* ids,
                    const float* vals, const void* hidden, int64_t hrs, int64_t hss, float* scores,
-                   void* ws) {
+                   void* ws, int32_t* tokens, int32_t* choice) {
     const corrector_desc& d = h->d;
     const corrector_weights& w = h->w;
     const int64_t rows = static_cast<int64_t>(n) * d.slots;
@@ -183,26 +180,15 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
     // variant has no pair state and computes the W_ctx block alone (r wide).
     const int hn = cos ? d.r : 3 * d.r;
     q("hproj", [&] { return launch_gemm(ha, hw, rows, hn, d.d_hidden, L.splits, hproj, q.s); });
-    float* upart = at<float>(ws, L.upart);
-    GemmA ua{};
-    ua.mode = GEMM_A_GATHER;
-    ua.base = static_cast<const uint16_t*>(w.embed);
-    ua.lda = d.d_embed;
-    ua.ids = ids;
-    ua.V = d.vocab;
-    GemmW uw{};
-    uw.nb = d.r;
-    uw.base[0] = static_cast<const uint16_t*>(w.w_cand);
-    uw.ld[0] = d.d_embed;
-    q("cand_gemm", [&] { return launch_gemm(ua, uw, rows * d.k, d.r, d.d_embed, L.usplits, upart, q.s); });
     CandArgs ca{};
     ca.ids = ids;
     ca.V = d.vocab;
     ca.K = d.k;
     ca.r = d.r;
     ca.rows = rows;
-    ca.upart = upart;
-    ca.usplits = L.usplits;
+    ca.embed = static_cast<const uint16_t*>(w.embed);
+    ca.de = d.d_embed;
+    ca.w_cand = static_cast<const uint16_t*>(w.w_cand);
     ca.table = nullptr;
     ca.w_fuse = static_cast<const uint16_t*>(w.w_fuse);
     ca.gamma = w.ln_gamma;
@@ -221,7 +207,10 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
         ca.vin = at<float>(ws, L.vin);
     }
     q("cand", [&] { return launch_cand(ca, q.s); });
-    if (d.slots < 2) return;
+    if (d.slots < 2) {
+        if (tokens) q("walk", [&] { return launch_walk(scores, ids, n, d.slots, d.k, tokens, choice, q.s); });
+        return;
+    }
     if (cos) {
         CosArgs c{};
         c.vout = ca.vout;
@@ -234,6 +223,7 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
         c.sigma = d.sigma;
         c.scores = scores;
         q("cosine", [&] { return launch_cosine(c, q.s); });
+        if (tokens) q("walk", [&] { return launch_walk(scores, ids, n, d.slots, d.k, tokens, choice, q.s); });
     } else {
         MlpArgs m{};
         m.zhl = ca.zhl;
@@ -248,10 +238,22 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
         m.w1 = static_cast<const uint16_t*>(w.w1);
         m.b1 = w.b1;
         m.w2 = w.w2;
-        m.b2 = w.b2;
-        m.scores = scores;
+        m.part = at<float>(ws, L.mlp_part);
         m.s_out = at<float>(ws, L.s);
         q("mlp", [&] { return launch_mlp(m, q.s); });
+        FinishArgs f{};
+        f.part = m.part;
+        f.nblk = mlp_blocks(d.mlp_hidden);
+        f.vals = vals;
+        f.b2 = w.b2;
+        f.n = n;
+        f.B = d.slots;
+        f.K = d.k;
+        f.scores = scores;
+        f.ids = ids;
+        f.tokens = tokens;
+        f.choice = choice;
+        q(tokens ? "finish_walk" : "finish", [&] { return launch_finish(f, q.s); });
     }
 }
 
@@ -343,7 +345,7 @@ int corrector_score(const corrector* hc, int32_t n, const int32_t* ids, const fl
     corrector* h = const_cast<corrector*>(hc);
     const Layout L = layout(h->d, n);
     Seq q{h, static_cast<hipStream_t>(stream)};
-    enqueue_score(q, h, L, n, ids, vals, hidden, hrs, hss, scores, ws);
+    enqueue_score(q, h, L, n, ids, vals, hidden, hrs, hss, scores, ws, nullptr, nullptr);
     return q.finish();
 }
 
@@ -375,8 +377,7 @@ int corrector_run(const corrector* hc, int32_t n, const void* logits, int64_t lr
     float* scores = scores_or_null ? scores_or_null : at<float>(ws, L.scores);
     Seq q{h, static_cast<hipStream_t>(stream)};
     enqueue_topk(q, h, L, n, logits, lrs, lss, ids, vals, ws);
-    enqueue_score(q, h, L, n, ids, vals, hidden, hrs, hss, scores, ws);
-    q("walk", [&] { return launch_walk(scores, ids, n, h->d.slots, h->d.k, tokens, choice_or_null, q.s); });
+    enqueue_score(q, h, L, n, ids, vals, hidden, hrs, hss, scores, ws, tokens, choice_or_null);
     return q.finish();
 }
 

@@ -53,9 +53,10 @@ struct CandArgs {
     int K;
     int r;
     int64_t rows;
-    const float* upart;   // [usplits][rows*K][r] partials of W_cand E[c] ...
-    int usplits;
-    const float* table;   // ... or, when non-null, the folded table [V][r]
+    const uint16_t* embed;  // [V][de] bf16, gathered when table is null
+    int de;
+    const uint16_t* w_cand;
+    const float* table;     // when non-null, the folded table [V][r] = E W_cand^T
     const uint16_t* w_fuse;
     const float* gamma;
     const float* beta;
@@ -88,11 +89,28 @@ struct MlpArgs {
     const uint16_t* w1;     // [h][3r+2]
     const float* b1;
     const float* w2;
-    const float* b2;
-    float* scores;          // [n][B-1][K][K]
+    float* part;            // [n*(B-1)][blocks][K][K] partial Delta per hidden-unit block
     float* s_out;           // optional [n][B-1][r]
 };
+int mlp_blocks(int h);
 hipError_t launch_mlp(const MlpArgs& a, hipStream_t stream);
+
+// Sum of the MLP partials in block order + b2 + l_{p+1}(b) -> scores; then,
+// when tokens is non-null, the walk (one workgroup per request).
+struct FinishArgs {
+    const float* part;
+    int nblk;
+    const float* vals;
+    const float* b2;
+    int n;
+    int B;
+    int K;
+    float* scores;
+    const int32_t* ids;
+    int32_t* tokens;
+    int32_t* choice;
+};
+hipError_t launch_finish(const FinishArgs& a, hipStream_t stream);
 
 struct CosArgs {
     const float* vout;      // [n][B][K][dvec]

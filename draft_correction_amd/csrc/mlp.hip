@@ -10,11 +10,13 @@
 // pair through c_p = W1_s s_p + b1 (one more MFMA row).  The MFMA inputs are z split into bf16
 // hi + lo parts (z = hi + lo to ~2^-16), against the same W1 columns twice, so
 // P and Q carry float32 accuracy.  The epilogue is the GELU over all K^2 x h
-// pre-activations and the h -> 1 dot with w2, one (a, b) per thread with the
-// sum over hidden units in index order: no atomics, bit-reproducible.
+// pre-activations and the h -> 1 dot with w2, one (a, b) per thread.
 //
-// One workgroup per pair (4 waves).  For K > 16 the hidden units are processed
-// in blocks so that P and Q for one block fit in LDS.
+// Work is split into (pair, block of 64 hidden units) workgroups, so a pass
+// has (B-1) * n * h/64 of them to balance over the CUs and each block's W1
+// columns are read once per pair.  Each block writes its partial Delta; the
+// finishing kernel adds the blocks in order, adds b2 and l_{p+1}(b) and walks.
+// Every sum runs in a fixed order with no atomics: bit-reproducible.
 #include "common.h"
 #include "kernels.h"
 
@@ -38,12 +40,8 @@ __device__ __forceinline__ float gelu(float x) {
     return fmaxf(x, 0.0f) - (t * e) * poly;
 }
 
-// Hidden-unit block so that P and Q ([K][JB] float32 each) fit in ~34 KB.
-__host__ __device__ inline int mlp_jblock(int K, int h) {
-    int jb = (4096 / K) / 16 * 16;
-    if (jb < 16) jb = 16;
-    return jb < h ? jb : h;
-}
+// Hidden units handled by one workgroup (a multiple of 16 and of 8).
+constexpr int kJB = 64;
 
 // One 16-column tile of P (which = 0) or Q (which = 1) for hidden units
 // j0 .. j0+15: rows are the K candidates of the slot, computed on MFMA from
@@ -98,21 +96,27 @@ __device__ __forceinline__ void pq_tile(const MlpArgs& a, int which, int j0, int
     }
 }
 
+// One workgroup per (pair, block of up to 64 hidden units): P, Q and c_p for
+// the block's units on MFMA, then GELU and the dot with w2 over all K^2
+// candidate pairs; the block's partial Delta goes to part[pair][block][a][b].
 template <int R>
 __global__ __launch_bounds__(256) void mlp_kernel(MlpArgs a) {
     const int wave = threadIdx.x >> 6;
     const int tid = threadIdx.x;
     const int B = a.B, K = a.K, h = a.h;
-    const int pair = blockIdx.x;
+    const int nj = (h + kJB - 1) / kJB;
+    const int item = blockIdx.x;
+    const int pair = item / nj, jblk = item % nj;
+    const int j0 = jblk * kJB;
+    const int jn = min(kJB, h - j0);
     const int req = pair / (B - 1), p = pair % (B - 1);
     const int64_t tp = static_cast<int64_t>(req) * B + p;  // slot rows of the pair
     const int64_t tq = tp + 1;
     const int64_t nslots = static_cast<int64_t>(a.n) * B;
-    const int JB = mlp_jblock(K, h);
-    const int PS = JB + 4;          // LDS row stride of P / Q (floats)
+    constexpr int PS = kJB + 4;     // LDS row stride of P / Q (floats)
 
     __shared__ __attribute__((aligned(16))) uint16_t shv[2 * 128];  // s_p as bf16 hi | lo
-    __shared__ __attribute__((aligned(16))) float w2s[256];
+    __shared__ __attribute__((aligned(16))) float w2s[kJB];
     __shared__ float lp[64], lq[64];
     extern __shared__ __attribute__((aligned(16))) float dyn[];
     float* P = dyn;                 // [K][PS]
@@ -126,79 +130,57 @@ __global__ __launch_bounds__(256) void mlp_kernel(MlpArgs a) {
         const uint16_t hi = f32_to_bf16(s);
         shv[c] = hi;
         shv[R + c] = f32_to_bf16(s - bf16_to_f32(hi));
-        if (a.s_out) a.s_out[static_cast<int64_t>(pair) * R + c] = s;
+        if (a.s_out && jblk == 0) a.s_out[static_cast<int64_t>(pair) * R + c] = s;
     }
     for (int m = tid; m < K; m += 256) {
         lp[m] = a.vals[tp * K + m];
         lq[m] = a.vals[tq * K + m];
     }
-    for (int j = tid; j < h; j += 256) w2s[j] = a.w2[j];
+    for (int j = tid; j < kJB; j += 256) w2s[j] = j < jn ? a.w2[j0 + j] : 0.f;
     __syncthreads();
 
-    const int nidx = K * K;
-    constexpr int kMaxPer = 16;     // (a, b) pairs per thread: K^2 / 256 for K = 64
-    float dacc[kMaxPer];
-#pragma unroll
-    for (int q = 0; q < kMaxPer; ++q) dacc[q] = 0.f;
-
-    for (int jb0 = 0; jb0 < h; jb0 += JB) {
-        const int jn = min(JB, h - jb0);
-        const int nct = jn / 16;
-        // ---- P and Q tiles for this block of hidden units, two tiles per step
-        for (int job = wave; job < 2 * nct; job += 8) {
-            const int job2 = job + 4;
-            {
-                const int which = job / nct, ct = job % nct;
-                pq_tile<R>(a, which, jb0 + ct * 16, (which ? tq : tp) * K, K, shv, lp, lq, which ? Q : P,
-                           ct * 16, PS);
-            }
-            if (job2 < 2 * nct) {
-                const int which = job2 / nct, ct = job2 % nct;
-                pq_tile<R>(a, which, jb0 + ct * 16, (which ? tq : tp) * K, K, shv, lp, lq, which ? Q : P,
-                           ct * 16, PS);
-            }
-        }
-        __syncthreads();
-        // ---- GELU and the dot with w2 over this block, one (a, b) per thread
-#pragma unroll
-        for (int q = 0; q < kMaxPer; ++q) {
-            const int idx = tid + 256 * q;
-            if (idx < nidx) {
-                const float* pr = P + (idx / K) * PS;
-                const float* qr = Q + (idx % K) * PS;
-                const float* wr = w2s + jb0;
-                float d = dacc[q];
-                for (int j = 0; j < jn; j += 4) {
-                    const float4 pv = *reinterpret_cast<const float4*>(pr + j);
-                    const float4 qv = *reinterpret_cast<const float4*>(qr + j);
-                    const float4 wv = *reinterpret_cast<const float4*>(wr + j);
-                    d = fmaf(wv.x, gelu(pv.x + qv.x), d);
-                    d = fmaf(wv.y, gelu(pv.y + qv.y), d);
-                    d = fmaf(wv.z, gelu(pv.z + qv.z), d);
-                    d = fmaf(wv.w, gelu(pv.w + qv.w), d);
-                }
-                dacc[q] = d;
-            }
-        }
-        __syncthreads();
+    // ---- P (with c_p) and Q tiles of this block
+    const int nct = jn / 16;
+    for (int job = wave; job < 2 * nct; job += 4) {
+        const int which = job / nct, ct = job % nct;
+        pq_tile<R>(a, which, j0 + ct * 16, (which ? tq : tp) * K, K, shv, lp, lq, which ? Q : P, ct * 16, PS);
     }
-    const float b2 = a.b2[0];
-#pragma unroll
-    for (int q = 0; q < kMaxPer; ++q) {
-        const int idx = tid + 256 * q;
-        if (idx < nidx) a.scores[static_cast<int64_t>(pair) * nidx + idx] = lq[idx % K] + (dacc[q] + b2);
+    __syncthreads();
+
+    // ---- GELU and the dot with w2, one (a, b) per thread
+    const int nidx = K * K;
+    float* out = a.part + static_cast<int64_t>(item) * nidx;
+    for (int idx = tid; idx < nidx; idx += 256) {
+        const float* pr = P + (idx / K) * PS;
+        const float* qr = Q + (idx % K) * PS;
+        float d0 = 0.f, d1 = 0.f;
+        for (int j = 0; j < jn; j += 8) {
+            const float4 pv0 = *reinterpret_cast<const float4*>(pr + j);
+            const float4 qv0 = *reinterpret_cast<const float4*>(qr + j);
+            const float4 wv0 = *reinterpret_cast<const float4*>(w2s + j);
+            const float4 pv1 = *reinterpret_cast<const float4*>(pr + j + 4);
+            const float4 qv1 = *reinterpret_cast<const float4*>(qr + j + 4);
+            const float4 wv1 = *reinterpret_cast<const float4*>(w2s + j + 4);
+            d0 = fmaf(wv0.x, gelu(pv0.x + qv0.x), d0);
+            d1 = fmaf(wv0.y, gelu(pv0.y + qv0.y), d1);
+            d0 = fmaf(wv0.z, gelu(pv0.z + qv0.z), d0);
+            d1 = fmaf(wv0.w, gelu(pv0.w + qv0.w), d1);
+            d0 = fmaf(wv1.x, gelu(pv1.x + qv1.x), d0);
+            d1 = fmaf(wv1.y, gelu(pv1.y + qv1.y), d1);
+            d0 = fmaf(wv1.z, gelu(pv1.z + qv1.z), d0);
+            d1 = fmaf(wv1.w, gelu(pv1.w + qv1.w), d1);
+        }
+        out[idx] = d0 + d1;
     }
 }
 
 }  // namespace
 
-size_t mlp_lds_bytes(int K, int h) {
-    return static_cast<size_t>(2) * K * (mlp_jblock(K, h) + 4) * sizeof(float);
-}
+int mlp_blocks(int h) { return (h + kJB - 1) / kJB; }
 
 hipError_t launch_mlp(const MlpArgs& a, hipStream_t stream) {
-    const dim3 grid(static_cast<unsigned>(a.n * (a.B - 1)));
-    const size_t lds = mlp_lds_bytes(a.K, a.h);
+    const dim3 grid(static_cast<unsigned>(a.n * (a.B - 1) * mlp_blocks(a.h)));
+    const size_t lds = static_cast<size_t>(2) * a.K * (kJB + 4) * sizeof(float);
     switch (a.r) {
         case 16: mlp_kernel<16><<<grid, 256, lds, stream>>>(a); break;
         case 32: mlp_kernel<32><<<grid, 256, lds, stream>>>(a); break;

@@ -6,12 +6,12 @@
 //          ([3r][d]): each slot's hidden row is read once and yields W_ctx h
 //          (for g), the left half W_pair,L h (for pairs that start at the
 //          slot) and the right half W_pair,R h (for pairs that end at it); and
-//          (ii) u = W_cand E[c] over the gathered embedding rows of all
-//          candidates (or over the whole table, to fold it once).  The
+//          (ii) the folded table E W_cand^T over the whole vocabulary.  The
 //          reduction is split over a fixed number of workgroups per shape;
 //          consumers add the partials in split order.
-//   cand   one workgroup per drafted slot and group of up to 16 candidates:
-//          b = LN(u) (non-affine), g = LN(W_ctx h) from hproj,
+//   cand   one workgroup per 32 candidates: gathers their embedding rows and
+//          forms u = W_cand E[c] on MFMA (LDS-staged, double-buffered slabs
+//          over d_e), b = LN(u) (non-affine), g = LN(W_ctx h) from hproj,
 //          y = W_fuse [b; g] on MFMA, z = gamma * LN(y) + beta, stored as
 //          bf16 hi | lo halves.  The cosine variant also forms unit(W_out z)
 //          and unit(W_in z).  MFMA operands that are not already bf16 (b, g,
@@ -161,16 +161,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmA A, GemmW W, int64_t M, 
 
 // ------------------------------------------------------------------- cand --
 
-constexpr int kCandRows = 16;  // candidates per workgroup (one 16-row MFMA tile)
+constexpr int kCR = 32;                 // candidate rows per workgroup
+constexpr int kCLS = kBK + 8;           // LDS row stride (bf16) of the GEMM slabs
 
-// LayerNorm of one row of m <= 128 floats held in LDS, by one wave; writes
-// gamma * y + beta (or y) to dst, which may alias src.
-__device__ void wave_layernorm(const float* src, float* dst, int m, float eps,
-                               const float* gamma, const float* beta) {
+// LayerNorm over m <= 128 values held two per lane (v0 at index l, v1 at
+// l + 64), by one wave; returns the normalised pair.
+__device__ __forceinline__ void wave_ln_regs(float& v0, float& v1, int m, float eps) {
     const int l = lane_id();
-    float v0 = l < m ? src[l] : 0.f;
-    float v1 = l + 64 < m ? src[l + 64] : 0.f;
-    float s = v0 + v1;
+    float s = (l < m ? v0 : 0.f) + (l + 64 < m ? v1 : 0.f);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, kWave);
     const float mean = s / static_cast<float>(m);
@@ -180,19 +178,22 @@ __device__ void wave_layernorm(const float* src, float* dst, int m, float eps,
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) q += __shfl_xor(q, o, kWave);
     const float inv = 1.0f / sqrtf(q / static_cast<float>(m) + eps);
-    if (l < m) dst[l] = gamma ? gamma[l] * (d0 * inv) + beta[l] : d0 * inv;
-    if (l + 64 < m) dst[l + 64] = gamma ? gamma[l + 64] * (d1 * inv) + beta[l + 64] : d1 * inv;
+    v0 = d0 * inv;
+    v1 = d1 * inv;
 }
 
-// Row stride (floats) of the fp32 staging rows: u / y need r, the cosine
-// out and in vectors need 2 * dvec.
-__host__ __device__ inline int cand_row_stride(int r, int dvec) {
-    return (2 * dvec > r ? 2 * dvec : r) + 4;
+// LayerNorm of one LDS row in place (affine when gamma is given), by one wave.
+__device__ __forceinline__ void wave_layernorm(float* row, int m, float eps, const float* gamma,
+                                               const float* beta) {
+    const int l = lane_id();
+    float v0 = l < m ? row[l] : 0.f, v1 = l + 64 < m ? row[l + 64] : 0.f;
+    wave_ln_regs(v0, v1, m, eps);
+    if (l < m) row[l] = gamma ? fmaf(gamma[l], v0, beta[l]) : v0;
+    if (l + 64 < m) row[l + 64] = gamma ? fmaf(gamma[l + 64], v1, beta[l + 64]) : v1;
 }
 
-// Row stride (bf16) of the MFMA operand rows: [x_hi | x_lo] with x = [b; g]
-// (4r wide) or z (2r wide).
-__host__ __device__ inline int cand_op_stride(int r) { return 4 * r + 8; }
+__host__ __device__ inline int cand_us(int r, int dvec) { return (dvec > r ? dvec : r) + 4; }
+__host__ __device__ inline int cand_as(int r) { return 4 * r + 8; }
 
 // acc = A (16 rows of LDS bf16 [hi | lo], 2 * kin wide) x W^T for one 16-column
 // tile of W ([*][ldw] bf16, rows w_row0 + 0..15, columns 0..kin-1).  The hi and
@@ -207,8 +208,9 @@ __device__ f32x4 mfma_hilo_tile(const uint16_t* abuf, int as, int M, const uint1
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int k0 = 0; k0 < 2 * kin; k0 += 32) {
         const int kg = k0 + kq;
-        const u32x4 av = m < M ? *reinterpret_cast<const u32x4*>(abuf + m * as + kg) : zero;
-        const u32x4 bv = load16(wp + (kg % kin));
+        const bool kin_ok = (kg % kin) + 8 <= kin;  // kin = 16: upper half of the step is padding
+        const u32x4 av = (m < M && kin_ok) ? *reinterpret_cast<const u32x4*>(abuf + m * as + kg) : zero;
+        const u32x4 bv = kin_ok ? load16(wp + (kg % kin)) : zero;
         acc = mfma16x16x32(av, bv, acc);
     }
     return acc;
@@ -220,77 +222,165 @@ __device__ __forceinline__ void split_store(uint16_t* row, int width, int c, flo
     row[width + c] = f32_to_bf16(v - bf16_to_f32(hi));
 }
 
+// One workgroup per 32 consecutive candidates (nodes) of the [rows][K] list:
+//   u = W_cand E[c]   gathered embedding rows x W_cand on MFMA, the whole d_e
+//                     reduction in LDS-staged slabs (or a row of the folded
+//                     table when one is given)
+//   b = LN(u), g = LN(W_ctx h) for the candidate's slot (from hproj)
+//   z = gamma * LN(W_fuse [b; g]) + beta, W_fuse on MFMA over [b; g] hi | lo
+//   stored as bf16 z hi | lo; cosine: unit(W_out z), unit(W_in z).
 __global__ __launch_bounds__(256) void cand_kernel(CandArgs a) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+    const int tid = threadIdx.x;
     const int l = lane_id();
-    const int wave = threadIdx.x >> 6;
-    const int64_t t = blockIdx.x;                 // drafted-slot row
-    const int m0 = blockIdx.y * kCandRows;        // first candidate of this group
-    const int M = min(kCandRows, a.K - m0);
+    const int wave = tid >> 6;
+    const int64_t nodes = a.rows * a.K;
+    const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kCR;
+    const int M = static_cast<int>(min(static_cast<int64_t>(kCR), nodes - n0));
     const int r = a.r;
     const int nct = r / 16;
+    const int kq = 8 * (l >> 4);
+    const int us = cand_us(r, a.vout ? a.dvec : 0);
+    const int as = cand_as(r);
+    float* ubuf = reinterpret_cast<float*>(smem_raw);                       // [kCR][us]
+    uint16_t* abuf = reinterpret_cast<uint16_t*>(smem_raw + kCR * us * 4);  // [kCR][as]
 
-    extern __shared__ float smem[];
-    const int us = cand_row_stride(r, a.vout ? a.dvec : 0);
-    const int as = cand_op_stride(r);
-    float* ubuf = smem;                                        // [16][us] fp32
-    float* gbuf = ubuf + kCandRows * us;                       // [128]
-    uint16_t* abuf = reinterpret_cast<uint16_t*>(gbuf + 128);  // [16][as] bf16
-
-    // ---- u = W_cand E[c]: the GEMM partials summed in split order, or a row of
-    // the folded table T = E W_cand^T
-    for (int idx = threadIdx.x; idx < M * r; idx += blockDim.x) {
-        const int m = idx / r, c = idx % r;
-        const int64_t node = t * a.K + m0 + m;
-        float u;
-        if (a.table) {
-            int64_t tok = a.ids[node];
+    // ---- u
+    if (a.table) {
+        for (int idx = tid; idx < M * r; idx += 256) {
+            const int m = idx / r, c = idx % r;
+            int64_t tok = a.ids[n0 + m];
             tok = tok < 0 ? 0 : (tok >= a.V ? a.V - 1 : tok);
-            u = a.table[tok * r + c];
-        } else {
-            u = 0.f;
-            for (int sk = 0; sk < a.usplits; ++sk) u += a.upart[(sk * a.rows * a.K + node) * r + c];
+            ubuf[m * us + c] = a.table[tok * r + c];
         }
-        ubuf[m * us + c] = u;
-    }
-    // ---- g pre-activation: the hproj partials summed in split order
-    for (int c = threadIdx.x; c < r; c += blockDim.x) {
-        float s = 0.f;
-        for (int sk = 0; sk < a.splits; ++sk) s += a.hproj[(static_cast<int64_t>(sk) * a.rows + t) * a.hstride + c];
-        gbuf[c] = s;
-    }
-    __syncthreads();
-
-    // ---- b = LN(u), g = LN(g) (non-affine)
-    for (int m = wave; m < M; m += 4) wave_layernorm(ubuf + m * us, ubuf + m * us, r, a.eps, nullptr, nullptr);
-    if (wave == 0) wave_layernorm(gbuf, gbuf, r, a.eps, nullptr, nullptr);
-    __syncthreads();
-    // [b; g] as bf16 hi | lo rows, 4r wide
-    for (int idx = threadIdx.x; idx < M * r; idx += blockDim.x) {
-        const int m = idx / r, c = idx % r;
-        split_store(abuf + m * as, 2 * r, c, ubuf[m * us + c]);
-        split_store(abuf + m * as, 2 * r, r + c, gbuf[c]);
-    }
-    if (blockIdx.y == 0)
-        for (int c = threadIdx.x; c < r; c += blockDim.x) a.g[t * r + c] = gbuf[c];
-    __syncthreads();
-
-    // ---- y = W_fuse [b; g] (MFMA on the hi/lo split, K = 2 x 2r), into ubuf
-    for (int ct = wave; ct < nct; ct += 4) {
-        const f32x4 acc = mfma_hilo_tile(abuf, as, M, a.w_fuse, 2 * r, ct * 16, 2 * r);
+    } else {
+        uint16_t* As = reinterpret_cast<uint16_t*>(smem_raw);   // [2][kCR * kCLS]
+        uint16_t* Ws = As + 2 * kCR * kCLS;                      // [2][128 * kCLS]
+        const int ra = tid >> 3, sa = tid & 7;
+        const bool aok = ra < M;
+        int64_t tok = aok ? a.ids[n0 + ra] : 0;
+        tok = tok < 0 ? 0 : (tok >= a.V ? a.V - 1 : tok);
+        const uint16_t* ap = a.embed + tok * a.de + sa * 8;
+        const uint16_t* wp[4];
+        bool wok[4];
+        int woff[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ubuf[(4 * (l >> 4) + i) * us + ct * 16 + (l & 15)] = acc[i];
+        for (int i = 0; i < 4; ++i) {
+            const int seg = tid + 256 * i;
+            const int rw = seg >> 3;
+            wok[i] = rw < r;
+            wp[i] = a.w_cand + static_cast<int64_t>(wok[i] ? rw : 0) * a.de + (seg & 7) * 8;
+            woff[i] = rw * kCLS + (seg & 7) * 8;
+        }
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        u32x4 rA, rW[4];
+        auto load = [&](int k0) {
+            const bool kok = k0 + sa * 8 < a.de;
+            rA = (aok && kok) ? load16(ap + k0) : zero;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rW[i] = (wok[i] && kok) ? load16(wp[i] + k0) : zero;
+        };
+        auto store = [&](int buf) {
+            *reinterpret_cast<u32x4*>(&As[buf * kCR * kCLS + ra * kCLS + sa * 8]) = rA;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&Ws[buf * 128 * kCLS + woff[i]]) = rW[i];
+        };
+        f32x4 acc[2][2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int ct0 = 2 * wave, ct1 = 2 * wave + 1;
+        load(0);
+        store(0);
+        __syncthreads();
+        int buf = 0;
+        for (int k0 = 0; k0 < a.de; k0 += kBK) {
+            const bool more = k0 + kBK < a.de;
+            if (more) load(k0 + kBK);
+            if (ct0 < nct) {
+                const uint16_t* Ab = As + buf * kCR * kCLS;
+                const uint16_t* Wb = Ws + buf * 128 * kCLS;
+#pragma unroll
+                for (int ks = 0; ks < kBK; ks += 32) {
+                    const u32x4 a0 = *reinterpret_cast<const u32x4*>(&Ab[(l & 15) * kCLS + ks + kq]);
+                    const u32x4 a1 = *reinterpret_cast<const u32x4*>(&Ab[(16 + (l & 15)) * kCLS + ks + kq]);
+                    const u32x4 w0 = *reinterpret_cast<const u32x4*>(&Wb[(ct0 * 16 + (l & 15)) * kCLS + ks + kq]);
+                    acc[0][0] = mfma16x16x32(a0, w0, acc[0][0]);
+                    acc[1][0] = mfma16x16x32(a1, w0, acc[1][0]);
+                    if (ct1 < nct) {
+                        const u32x4 w1 = *reinterpret_cast<const u32x4*>(&Wb[(ct1 * 16 + (l & 15)) * kCLS + ks + kq]);
+                        acc[0][1] = mfma16x16x32(a0, w1, acc[0][1]);
+                        acc[1][1] = mfma16x16x32(a1, w1, acc[1][1]);
+                    }
+                }
+            }
+            if (more) store(buf ^ 1);
+            __syncthreads();
+            buf ^= 1;
+        }
+        // the slab buffers are dead after the last barrier; u goes to ubuf
+        if (ct0 < nct) {
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int m = rt * 16 + 4 * (l >> 4) + i;
+                    ubuf[m * us + ct0 * 16 + (l & 15)] = acc[rt][0][i];
+                    if (ct1 < nct) ubuf[m * us + ct1 * 16 + (l & 15)] = acc[rt][1][i];
+                }
+        }
     }
     __syncthreads();
 
-    // ---- z = gamma * LN(y) + beta; store as bf16 hi | lo (also kept in abuf)
-    for (int m = wave; m < M; m += 4) wave_layernorm(ubuf + m * us, ubuf + m * us, r, a.eps, a.gamma, a.beta);
+    // ---- b = LN(u) and g = LN(W_ctx h) per row, as [b; g] hi | lo in abuf
+    for (int m = wave; m < M; m += 4) {
+        float b0 = l < r ? ubuf[m * us + l] : 0.f, b1 = l + 64 < r ? ubuf[m * us + l + 64] : 0.f;
+        wave_ln_regs(b0, b1, r, a.eps);
+        const int64_t node = n0 + m;
+        const int64_t t = node / a.K;
+        float g0 = 0.f, g1 = 0.f;
+        for (int sk = 0; sk < a.splits; ++sk) {
+            const float* hp = a.hproj + (static_cast<int64_t>(sk) * a.rows + t) * a.hstride;
+            if (l < r) g0 += hp[l];
+            if (l + 64 < r) g1 += hp[l + 64];
+        }
+        wave_ln_regs(g0, g1, r, a.eps);
+        if (node % a.K == 0) {
+            if (l < r) a.g[t * r + l] = g0;
+            if (l + 64 < r) a.g[t * r + l + 64] = g1;
+        }
+        uint16_t* arow = abuf + m * as;
+        if (l < r) {
+            split_store(arow, 2 * r, l, b0);
+            split_store(arow, 2 * r, r + l, g0);
+        }
+        if (l + 64 < r) {
+            split_store(arow, 2 * r, l + 64, b1);
+            split_store(arow, 2 * r, r + l + 64, g1);
+        }
+    }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < M * r; idx += blockDim.x) {
+
+    // ---- y = W_fuse [b; g] (MFMA on the hi / lo split), into ubuf
+    const int nrt = (M + 15) / 16;
+    for (int job = wave; job < nrt * nct; job += 4) {
+        const int rt = job / nct, ct = job % nct;
+        const f32x4 acc = mfma_hilo_tile(abuf + rt * 16 * as, as, M - rt * 16, a.w_fuse, 2 * r, ct * 16, 2 * r);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ubuf[(rt * 16 + 4 * (l >> 4) + i) * us + ct * 16 + (l & 15)] = acc[i];
+    }
+    __syncthreads();
+
+    // ---- z = gamma * LN(y) + beta; stored as bf16 hi | lo (and kept in abuf)
+    for (int m = wave; m < M; m += 4) wave_layernorm(ubuf + m * us, r, a.eps, a.gamma, a.beta);
+    __syncthreads();
+    for (int idx = tid; idx < M * r; idx += 256) {
         const int m = idx / r, c = idx % r;
         const float zv = ubuf[m * us + c];
-        uint16_t* grow = a.zhl + (t * a.K + m0 + m) * (2 * r);
         const uint16_t hi = f32_to_bf16(zv);
         const uint16_t lo = f32_to_bf16(zv - bf16_to_f32(hi));
+        uint16_t* grow = a.zhl + (n0 + m) * (2 * r);
         grow[c] = hi;
         grow[r + c] = lo;
         abuf[m * as + c] = hi;
@@ -299,29 +389,31 @@ __global__ __launch_bounds__(256) void cand_kernel(CandArgs a) {
     if (!a.vout) return;
     __syncthreads();
 
-    // ---- cosine variant: o = W_out z, i = W_in z (MFMA on z hi/lo), unit vectors
+    // ---- cosine variant: unit(W_out z) then unit(W_in z), one map at a time
     const int dv = a.dvec;
     const int nvt = dv / 16;
-    for (int job = wave; job < 2 * nvt; job += 4) {
-        const int which = job / nvt, ct = job % nvt;
-        const f32x4 acc = mfma_hilo_tile(abuf, as, M, which ? a.w_in : a.w_out, r, ct * 16, r);
+    for (int which = 0; which < 2; ++which) {
+        for (int job = wave; job < nrt * nvt; job += 4) {
+            const int rt = job / nvt, ct = job % nvt;
+            const f32x4 acc = mfma_hilo_tile(abuf + rt * 16 * as, as, M - rt * 16, which ? a.w_in : a.w_out, r,
+                                             ct * 16, r);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            ubuf[(4 * (l >> 4) + i) * us + which * dv + ct * 16 + (l & 15)] = acc[i];
-    }
-    __syncthreads();
-    for (int job = wave; job < 2 * M; job += 4) {
-        const int m = job >> 1, which = job & 1;
-        const float* v = ubuf + m * us + which * dv;
-        float x0 = l < dv ? v[l] : 0.f;
-        float x1 = l + 64 < dv ? v[l + 64] : 0.f;
-        float q = x0 * x0 + x1 * x1;
+            for (int i = 0; i < 4; ++i) ubuf[(rt * 16 + 4 * (l >> 4) + i) * us + ct * 16 + (l & 15)] = acc[i];
+        }
+        __syncthreads();
+        for (int m = wave; m < M; m += 4) {
+            const float* v = ubuf + m * us;
+            const float x0 = l < dv ? v[l] : 0.f;
+            const float x1 = l + 64 < dv ? v[l + 64] : 0.f;
+            float q = x0 * x0 + x1 * x1;
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) q += __shfl_xor(q, o, kWave);
-        const float inv = 1.0f / fmaxf(sqrtf(q), 1e-12f);
-        float* dst = (which ? a.vin : a.vout) + (t * a.K + m0 + m) * dv;
-        if (l < dv) dst[l] = x0 * inv;
-        if (l + 64 < dv) dst[l + 64] = x1 * inv;
+            for (int o = 32; o >= 1; o >>= 1) q += __shfl_xor(q, o, kWave);
+            const float inv = 1.0f / fmaxf(sqrtf(q), 1e-12f);
+            float* dst = (which ? a.vin : a.vout) + (n0 + m) * dv;
+            if (l < dv) dst[l] = x0 * inv;
+            if (l + 64 < dv) dst[l + 64] = x1 * inv;
+        }
+        __syncthreads();
     }
 }
 
@@ -337,12 +429,14 @@ hipError_t launch_gemm(const GemmA& A, const GemmW& W, int64_t M, int N, int kdi
 }
 
 size_t cand_lds_bytes(int r, int dvec) {
-    return sizeof(float) * (kCandRows * cand_row_stride(r, dvec) + 128) +
-           sizeof(uint16_t) * kCandRows * cand_op_stride(r);
+    const size_t gemm = sizeof(uint16_t) * (2 * kCR * kCLS + 2 * 128 * kCLS);
+    const size_t epi = sizeof(float) * kCR * cand_us(r, dvec) + sizeof(uint16_t) * kCR * cand_as(r);
+    return gemm > epi ? gemm : epi;
 }
 
 hipError_t launch_cand(const CandArgs& a, hipStream_t stream) {
-    const dim3 grid(static_cast<unsigned>(a.rows), static_cast<unsigned>((a.K + kCandRows - 1) / kCandRows));
+    const int64_t nodes = a.rows * a.K;
+    const dim3 grid(static_cast<unsigned>((nodes + kCR - 1) / kCR));
     cand_kernel<<<grid, 256, cand_lds_bytes(a.r, a.vout ? a.dvec : 0), stream>>>(a);
     return hipGetLastError();
 }

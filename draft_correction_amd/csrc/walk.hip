@@ -26,32 +26,13 @@ __global__ __launch_bounds__(256) void cosine_kernel(CosArgs a) {
     }
 }
 
-// One wave per request.  choice[0] = 0 (rank 0 is the drafter argmax of the
-// first drafted slot); then each step takes the largest score in the row of
-// the chosen predecessor, ties to the lowest successor index.  When the
-// request's scores fit (lds_rows > 0) they are first copied into LDS with
-// coalesced 16-byte loads, so the dependent steps read LDS, not memory.
-__global__ __launch_bounds__(64) void walk_kernel(const float* __restrict__ scores,
-                                                  const int32_t* __restrict__ ids, int n, int B,
-                                                  int K, int32_t* __restrict__ tokens,
-                                                  int32_t* __restrict__ choice, int use_lds) {
-    extern __shared__ __attribute__((aligned(16))) float sl[];
-    const int req = blockIdx.x;
+// The prefix-first walk of one request by one wave over its scores `src`
+// ([B-1][K][K], LDS or memory): choice[0] = 0 (rank 0 is the drafter argmax of
+// the first drafted slot); then each step takes the largest score in the row
+// of the chosen predecessor, ties to the lowest successor index.
+__device__ void walk_wave(const float* src, const int32_t* __restrict__ ids, int req, int B, int K,
+                          int32_t* __restrict__ tokens, int32_t* __restrict__ choice) {
     const int l = lane_id();
-    if (req >= n) return;
-    const int64_t per = static_cast<int64_t>(B - 1) * K * K;
-    const float* base = scores + req * per;
-    if (use_lds) {
-        // per is a multiple of 4 when K is even; odd K copies element-wise
-        if ((K & 1) == 0 && (reinterpret_cast<uintptr_t>(base) & 15) == 0) {
-            for (int64_t i = l; i < per / 4; i += kWave)
-                reinterpret_cast<float4*>(sl)[i] = reinterpret_cast<const float4*>(base)[i];
-        } else {
-            for (int64_t i = l; i < per; i += kWave) sl[i] = base[i];
-        }
-        wave_lds_sync();
-    }
-    const float* src = use_lds ? sl : base;
     int k = 0;
     if (l == 0) {
         if (choice) choice[static_cast<int64_t>(req) * B] = 0;
@@ -77,6 +58,69 @@ __global__ __launch_bounds__(64) void walk_kernel(const float* __restrict__ scor
             tokens[s] = ids[s * K + k];
         }
     }
+}
+
+// Walk over precomputed scores, one wave per request.  When the request's
+// scores fit (use_lds) they are first copied into LDS with coalesced 16-byte
+// loads, all issued before any is used, so the dependent steps read LDS.
+__global__ __launch_bounds__(64) void walk_kernel(const float* __restrict__ scores,
+                                                  const int32_t* __restrict__ ids, int n, int B,
+                                                  int K, int32_t* __restrict__ tokens,
+                                                  int32_t* __restrict__ choice, int use_lds) {
+    extern __shared__ __attribute__((aligned(16))) float sl[];
+    const int req = blockIdx.x;
+    const int l = lane_id();
+    if (req >= n) return;
+    const int64_t per = static_cast<int64_t>(B - 1) * K * K;
+    const float* base = scores + req * per;
+    if (use_lds) {
+        if ((per & 3) == 0 && (reinterpret_cast<uintptr_t>(base) & 15) == 0) {
+            const int64_t nv = per / 4;
+            for (int64_t i0 = 0; i0 < nv; i0 += 8 * kWave) {
+                float4 t[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int64_t i = min(i0 + u * kWave + l, nv - 1);  // clamped: always in bounds
+                    t[u] = reinterpret_cast<const float4*>(base)[i];
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int64_t i = i0 + u * kWave + l;
+                    if (i < nv) reinterpret_cast<float4*>(sl)[i] = t[u];
+                }
+            }
+        } else {
+            for (int64_t i = l; i < per; i += kWave) sl[i] = base[i];
+        }
+        wave_lds_sync();
+    }
+    walk_wave(use_lds ? sl : base, ids, req, B, K, tokens, choice);
+}
+
+// One workgroup per request: S = l_{p+1}(b) + (sum of the hidden-block partial
+// Deltas in block order + b2) for all of the request's pairs, written to
+// `scores` (and kept in LDS when it fits); then, with tokens given, the walk.
+__global__ __launch_bounds__(256) void finish_kernel(FinishArgs a, int use_lds) {
+    extern __shared__ __attribute__((aligned(16))) float sS[];
+    const int req = blockIdx.x;
+    const int B = a.B, K = a.K;
+    const int KK = K * K;
+    const int64_t per = static_cast<int64_t>(B - 1) * KK;
+    const float b2 = a.b2[0];
+    for (int64_t idx = threadIdx.x; idx < per; idx += blockDim.x) {
+        const int p = static_cast<int>(idx / KK), e = static_cast<int>(idx % KK);
+        const int64_t pair = static_cast<int64_t>(req) * (B - 1) + p;
+        const float* pp = a.part + pair * a.nblk * KK + e;
+        float d = pp[0];
+        for (int jb = 1; jb < a.nblk; ++jb) d += pp[static_cast<int64_t>(jb) * KK];
+        const float sv = a.vals[(static_cast<int64_t>(req) * B + p + 1) * K + e % K] + (d + b2);
+        a.scores[pair * KK + e] = sv;
+        if (use_lds) sS[idx] = sv;
+    }
+    if (!a.tokens) return;
+    __syncthreads();
+    if ((threadIdx.x >> 6) != 0) return;
+    walk_wave(use_lds ? sS : a.scores + req * per, a.ids, req, B, K, a.tokens, a.choice);
 }
 
 // z = hi + lo for each node row of the [hi | lo] layout.
@@ -109,12 +153,22 @@ hipError_t launch_cosine(const CosArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+static size_t walk_lds_bytes(int B, int K) {
+    const size_t bytes = static_cast<size_t>(B > 1 ? B - 1 : 0) * K * K * sizeof(float);
+    return (bytes > 0 && bytes <= 60 * 1024) ? bytes : 0;
+}
+
 hipError_t launch_walk(const float* scores, const int32_t* ids, int n, int B, int K,
                        int32_t* tokens, int32_t* choice, hipStream_t stream) {
-    const size_t bytes = static_cast<size_t>(B > 1 ? B - 1 : 0) * K * K * sizeof(float);
-    const int use_lds = bytes > 0 && bytes <= 60 * 1024;
-    walk_kernel<<<dim3(static_cast<unsigned>(n)), 64, use_lds ? bytes : 0, stream>>>(scores, ids, n, B, K, tokens,
-                                                                                     choice, use_lds);
+    const size_t lds = walk_lds_bytes(B, K);
+    walk_kernel<<<dim3(static_cast<unsigned>(n)), 64, lds, stream>>>(scores, ids, n, B, K, tokens, choice,
+                                                                     lds > 0);
+    return hipGetLastError();
+}
+
+hipError_t launch_finish(const FinishArgs& a, hipStream_t stream) {
+    const size_t lds = walk_lds_bytes(a.B, a.K);
+    finish_kernel<<<dim3(static_cast<unsigned>(a.n)), 256, lds, stream>>>(a, lds > 0);
     return hipGetLastError();
 }
 
