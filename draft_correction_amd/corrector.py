@@ -25,7 +25,8 @@ STATUS = {0: "CORR_OK", 1: "CORR_E_NULL", 2: "CORR_E_SHAPE", 3: "CORR_E_UNSUPPOR
 SYMBOLS = ("corrector_create", "corrector_destroy", "corrector_workspace_bytes",
            "corrector_topk", "corrector_score", "corrector_walk", "corrector_run",
            "corrector_intermediates", "corrector_set_timing", "corrector_kernel_times",
-           "corrector_status_string")
+           "corrector_status_string", "corrector_table_bytes", "corrector_fold_table",
+           "corrector_use_table")
 
 
 class CorrectorDesc(C.Structure):
@@ -75,10 +76,15 @@ def load(path: str = LIB_PATH):
     lib.corrector_intermediates.argtypes = [P, I32, P, SZ, P, P, P, P]
     lib.corrector_set_timing.argtypes = [P, C.c_int]
     lib.corrector_kernel_times.argtypes = [P, P, P, C.c_int]
+    lib.corrector_table_bytes.argtypes = [P]
+    lib.corrector_table_bytes.restype = SZ
+    lib.corrector_fold_table.argtypes = [P, P, P]
+    lib.corrector_use_table.argtypes = [P, P]
     lib.corrector_status_string.argtypes = [C.c_int]
     lib.corrector_status_string.restype = C.c_char_p
     for fn in ("corrector_topk", "corrector_score", "corrector_walk", "corrector_run",
-               "corrector_intermediates", "corrector_set_timing", "corrector_kernel_times"):
+               "corrector_intermediates", "corrector_set_timing", "corrector_kernel_times",
+               "corrector_fold_table", "corrector_use_table"):
         getattr(lib, fn).restype = C.c_int
     _lib = lib
     return lib
@@ -174,6 +180,16 @@ class Corrector:
     def intermediates(self, n, ws, z=None, g=None, s=None, stream=None):
         _ok("corrector_intermediates", self.lib.corrector_intermediates(
             self.h, n, _p(ws), ws.numel(), _p(z), _p(g), _p(s), _stream(stream)))
+
+    def table_bytes(self) -> int:
+        return int(self.lib.corrector_table_bytes(self.h))
+
+    def fold_table(self, table, stream=None):
+        _ok("corrector_fold_table", self.lib.corrector_fold_table(self.h, _p(table), _stream(stream)))
+
+    def use_table(self, table):
+        self._table = table  # keep the buffer alive while attached
+        _ok("corrector_use_table", self.lib.corrector_use_table(self.h, _p(table)))
 
     def set_timing(self, enabled: bool):
         _ok("corrector_set_timing", self.lib.corrector_set_timing(self.h, 1 if enabled else 0))

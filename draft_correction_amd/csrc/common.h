@@ -83,6 +83,20 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Sum of `n` (<= 16) values v[0], v[stride], ... in index order, with every
+// load issued before the first add (a runtime-length loop would wait one
+// memory round trip per term).
+__device__ __forceinline__ float sum_strided16(const float* v, int64_t stride, int n) {
+    float t[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) t[i] = i < n ? v[i * stride] : 0.f;
+    float s = t[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i)
+        if (i < n) s += t[i];
+    return s;
+}
+
 // ------------------------------------------------------------------- MFMA --
 // v_mfma_f32_16x16x32_bf16, D = A (16x32) * B (32x16) + C, one wave:
 //   lane l supplies A[l % 16][8*(l/16) .. 8*(l/16)+7]

@@ -20,8 +20,8 @@ constexpr int kMaxKernels = 8;
 constexpr size_t kAlign = 256;
 
 struct Layout {
-    size_t part, ids, vals, hproj, z, g, s, vout, vin, mlp_part, scores, total;
-    int chunks, splits;
+    size_t part, ids, vals, hproj, upart, z, g, s, vout, vin, mlp_part, scores, total;
+    int chunks, splits, usplits;
 };
 
 }  // namespace
@@ -35,6 +35,7 @@ struct corrector {
     hipEvent_t ev[2 * kMaxKernels];
     const char* names[kMaxKernels];
     int nk;
+    const float* table;  // folded E W_cand^T [V][r], or null
 };
 
 namespace {
@@ -45,11 +46,16 @@ size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 int logits_elem_bytes(const corrector_desc& d) { return d.logits_dtype == CORR_DTYPE_BF16 ? 2 : 4; }
 
-// Split of the hidden-state projection's reduction over d: a function of d
-// only, so a request's results do not depend on how many requests share the
-// call.
+// Splits of the two GEMM reductions (over d for the hidden-state projections,
+// over d_e for the candidate projection): functions of the widths only, so a
+// request's results do not depend on how many requests share the call.
 int choose_splits(const corrector_desc& d) {
     int s = d.d_hidden / 512;
+    if (s > 16) s = 16;
+    return s < 1 ? 1 : s;
+}
+int choose_usplits(const corrector_desc& d) {
+    int s = d.d_embed / 1024;
     if (s > 16) s = 16;
     return s < 1 ? 1 : s;
 }
@@ -62,12 +68,14 @@ Layout layout(const corrector_desc& d, int32_t n) {
     L.chunks = static_cast<int>((d.vocab + topk_chunk_elems(d.logits_dtype) - 1) /
                                 topk_chunk_elems(d.logits_dtype));
     L.splits = choose_splits(d);
+    L.usplits = choose_usplits(d);
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o = up(o + bytes); return at; };
     L.part = take(sizeof(uint64_t) * rows * L.chunks * d.k);
     L.ids = take(sizeof(int32_t) * rows * d.k);
     L.vals = take(sizeof(float) * rows * d.k);
     L.hproj = take(sizeof(float) * L.splits * rows * 3 * d.r);
+    L.upart = take(sizeof(float) * L.usplits * rows * d.k * d.r);
     L.z = take(sizeof(uint16_t) * rows * d.k * 2 * d.r);
     L.g = take(sizeof(float) * rows * d.r);
     L.s = take(sizeof(float) * pairs * d.r);
@@ -180,16 +188,29 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
     // variant has no pair state and computes the W_ctx block alone (r wide).
     const int hn = cos ? d.r : 3 * d.r;
     q("hproj", [&] { return launch_gemm(ha, hw, rows, hn, d.d_hidden, L.splits, hproj, q.s); });
+    float* upart = at<float>(ws, L.upart);
+    if (!h->table) {
+    GemmA ua{};
+    ua.mode = GEMM_A_GATHER;
+    ua.base = static_cast<const uint16_t*>(w.embed);
+    ua.lda = d.d_embed;
+    ua.ids = ids;
+    ua.V = d.vocab;
+    GemmW uw{};
+    uw.nb = d.r;
+    uw.base[0] = static_cast<const uint16_t*>(w.w_cand);
+    uw.ld[0] = d.d_embed;
+    q("cand_gemm", [&] { return launch_gemm(ua, uw, rows * d.k, d.r, d.d_embed, L.usplits, upart, q.s); });
+    }
     CandArgs ca{};
     ca.ids = ids;
     ca.V = d.vocab;
     ca.K = d.k;
     ca.r = d.r;
     ca.rows = rows;
-    ca.embed = static_cast<const uint16_t*>(w.embed);
-    ca.de = d.d_embed;
-    ca.w_cand = static_cast<const uint16_t*>(w.w_cand);
-    ca.table = nullptr;
+    ca.upart = upart;
+    ca.usplits = L.usplits;
+    ca.table = h->table;
     ca.w_fuse = static_cast<const uint16_t*>(w.w_fuse);
     ca.gamma = w.ln_gamma;
     ca.beta = w.ln_beta;
@@ -302,6 +323,7 @@ int corrector_create(const corrector_desc* desc, const corrector_weights* wt, co
     h->timing = false;
     h->events_ready = false;
     h->nk = 0;
+    h->table = nullptr;
     *out = h;
     return CORR_OK;
 }
@@ -379,6 +401,35 @@ int corrector_run(const corrector* hc, int32_t n, const void* logits, int64_t lr
     enqueue_topk(q, h, L, n, logits, lrs, lss, ids, vals, ws);
     enqueue_score(q, h, L, n, ids, vals, hidden, hrs, hss, scores, ws, tokens, choice_or_null);
     return q.finish();
+}
+
+size_t corrector_table_bytes(const corrector* h) {
+    if (!live(h)) return 0;
+    return sizeof(float) * static_cast<size_t>(h->d.vocab) * h->d.r;
+}
+
+int corrector_fold_table(const corrector* h, float* table, void* stream) {
+    if (!live(h)) return CORR_E_HANDLE;
+    if (!table) return CORR_E_NULL;
+    if (!aligned(table, 16)) return CORR_E_ALIGN;
+    const corrector_desc& d = h->d;
+    GemmA a{};
+    a.mode = GEMM_A_DENSE;
+    a.base = static_cast<const uint16_t*>(h->w.embed);
+    a.lda = d.d_embed;
+    GemmW w{};
+    w.nb = d.r;
+    w.base[0] = static_cast<const uint16_t*>(h->w.w_cand);
+    w.ld[0] = d.d_embed;
+    const hipError_t e = launch_gemm(a, w, d.vocab, d.r, d.d_embed, 1, table, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? CORR_OK : CORR_E_HIP;
+}
+
+int corrector_use_table(corrector* h, const float* table) {
+    if (!live(h)) return CORR_E_HANDLE;
+    if (table && !aligned(table, 16)) return CORR_E_ALIGN;
+    h->table = table;
+    return CORR_OK;
 }
 
 int corrector_intermediates(const corrector* h, int32_t n, const void* ws, size_t ws_bytes,

@@ -53,10 +53,9 @@ struct CandArgs {
     int K;
     int r;
     int64_t rows;
-    const uint16_t* embed;  // [V][de] bf16, gathered when table is null
-    int de;
-    const uint16_t* w_cand;
-    const float* table;     // when non-null, the folded table [V][r] = E W_cand^T
+    const float* upart;     // [usplits][rows*K][r] partials of u = W_cand E[c] ...
+    int usplits;
+    const float* table;     // ... or, when non-null, the folded table [V][r] = E W_cand^T
     const uint16_t* w_fuse;
     const float* gamma;
     const float* beta;

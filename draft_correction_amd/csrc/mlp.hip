@@ -124,9 +124,10 @@ __global__ __launch_bounds__(256) void mlp_kernel(MlpArgs a) {
 
     // ---- pair state s_p = W_pair,L h_p + W_pair,R h_{p+1}, logits, w2
     for (int c = tid; c < R; c += 256) {
-        float s = 0.f;
-        for (int sk = 0; sk < a.splits; ++sk) s += a.hproj[(sk * nslots + tp) * (3 * R) + R + c];
-        for (int sk = 0; sk < a.splits; ++sk) s += a.hproj[(sk * nslots + tq) * (3 * R) + 2 * R + c];
+        const int64_t sstride = nslots * (3 * R);
+        const float sl = sum_strided16(a.hproj + tp * (3 * R) + R + c, sstride, a.splits);
+        const float sr = sum_strided16(a.hproj + tq * (3 * R) + 2 * R + c, sstride, a.splits);
+        const float s = sl + sr;
         const uint16_t hi = f32_to_bf16(s);
         shv[c] = hi;
         shv[R + c] = f32_to_bf16(s - bf16_to_f32(hi));

@@ -6,12 +6,13 @@
 //          ([3r][d]): each slot's hidden row is read once and yields W_ctx h
 //          (for g), the left half W_pair,L h (for pairs that start at the
 //          slot) and the right half W_pair,R h (for pairs that end at it); and
-//          (ii) the folded table E W_cand^T over the whole vocabulary.  The
+//          (ii) the folded table E W_cand^T over the whole vocabulary, and
 //          reduction is split over a fixed number of workgroups per shape;
 //          consumers add the partials in split order.
-//   cand   one workgroup per 32 candidates: gathers their embedding rows and
-//          forms u = W_cand E[c] on MFMA (LDS-staged, double-buffered slabs
-//          over d_e), b = LN(u) (non-affine), g = LN(W_ctx h) from hproj,
+//          (iii) u = W_cand E[c] over the gathered embedding rows of all
+//          candidates.
+//   cand   one workgroup per 32 candidates: b = LN(u) (non-affine),
+//          g = LN(W_ctx h) from hproj,
 //          y = W_fuse [b; g] on MFMA, z = gamma * LN(y) + beta, stored as
 //          bf16 hi | lo halves.  The cosine variant also forms unit(W_out z)
 //          and unit(W_in z).  MFMA operands that are not already bf16 (b, g,
@@ -30,8 +31,9 @@ namespace {
 // for bf16 A and W stored K-contiguous.  A rows are gathered (embedding rows of
 // candidate ids), strided (drafter hidden rows of a slot block) or dense; W
 // rows come from up to three blocks of nb rows.  Tile 64 x 128, K slab 64,
-// double-buffered in LDS with the next slab's global loads in flight during
-// the MFMAs; 4 waves in 2 x 2, each 32 x 64 (2 x 4 v_mfma_f32_16x16x32_bf16).
+// double-buffered in LDS, with the global loads of the next two slabs in
+// flight (two register sets) during the MFMAs; 4 waves in 2 x 2, each 32 x 64
+// (2 x 4 v_mfma_f32_16x16x32_bf16).
 
 constexpr int kBM = 64, kBN = 128, kBK = 64, kLS = kBK + 8;  // LDS row stride (bf16)
 
@@ -90,8 +92,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmA A, GemmW W, int64_t M, 
         wp[i] = W.base[b] + static_cast<int64_t>(nn % W.nb) * W.ld[b] + (seg & 7) * 8;
     }
     const u32x4 zero = {0u, 0u, 0u, 0u};
-    u32x4 ra[2], rw[4];
-    auto load = [&](int k0) {
+    // two register sets of slab data: the slabs two and three ahead of the
+    // one being multiplied are in flight while it runs
+    u32x4 ra0[2], rw0[4], ra1[2], rw1[4];
+    auto load = [&](int k0, u32x4* ra, u32x4* rw) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int kk = k0 + ((tid + 256 * i) & 7) * 8;
@@ -103,7 +107,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmA A, GemmW W, int64_t M, 
             rw[i] = (wok[i] && kk < k_hi) ? load16(wp[i] + k0) : zero;
         }
     };
-    auto store = [&](int buf) {
+    auto store = [&](int buf, const u32x4* ra, const u32x4* rw) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4*>(&As[buf][aoff[i]]) = ra[i];
 #pragma unroll
@@ -115,17 +119,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmA A, GemmW W, int64_t M, 
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    if (k_lo < k_hi) {
-        load(k_lo);
-        store(0);
-    }
-    __syncthreads();
     const int kq = 8 * (l >> 4);
-    int buf = 0;
-    for (int k0 = k_lo; k0 < k_hi; k0 += kBK) {
-        const bool more = k0 + kBK < k_hi;
-        if (more) load(k0 + kBK);
+    auto compute = [&](int buf) {
 #pragma unroll
         for (int ks = 0; ks < kBK; ks += 32) {
             u32x4 af[2], wf[4];
@@ -140,9 +135,27 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmA A, GemmW W, int64_t M, 
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(af[i], wf[j], acc[i][j]);
         }
-        if (more) store(buf ^ 1);
+    };
+
+    const int nslab = k_lo < k_hi ? (k_hi - k_lo + kBK - 1) / kBK : 0;
+    if (nslab > 0) {
+        load(k_lo, ra0, rw0);
+        store(0, ra0, rw0);
+    }
+    if (nslab > 1) load(k_lo + kBK, ra0, rw0);
+    if (nslab > 2) load(k_lo + 2 * kBK, ra1, rw1);
+    __syncthreads();
+    // slab s sits in LDS buffer s & 1; slab s+1 in register set (s & 1) ? 1 : 0
+    for (int s = 0; s < nslab; s += 2) {
+        compute(0);
+        if (s + 1 < nslab) store(1, ra0, rw0);
+        if (s + 3 < nslab) load(k_lo + (s + 3) * kBK, ra0, rw0);
         __syncthreads();
-        buf ^= 1;
+        if (s + 1 >= nslab) break;
+        compute(1);
+        if (s + 2 < nslab) store(0, ra1, rw1);
+        if (s + 4 < nslab) load(k_lo + (s + 4) * kBK, ra1, rw1);
+        __syncthreads();
     }
     float* out = C + static_cast<int64_t>(split) * M * N;
 #pragma unroll
@@ -162,7 +175,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmA A, GemmW W, int64_t M, 
 // ------------------------------------------------------------------- cand --
 
 constexpr int kCR = 32;                 // candidate rows per workgroup
-constexpr int kCLS = kBK + 8;           // LDS row stride (bf16) of the GEMM slabs
 
 // LayerNorm over m <= 128 values held two per lane (v0 at index l, v1 at
 // l + 64), by one wave; returns the normalised pair.
@@ -223,9 +235,8 @@ __device__ __forceinline__ void split_store(uint16_t* row, int width, int c, flo
 }
 
 // One workgroup per 32 consecutive candidates (nodes) of the [rows][K] list:
-//   u = W_cand E[c]   gathered embedding rows x W_cand on MFMA, the whole d_e
-//                     reduction in LDS-staged slabs (or a row of the folded
-//                     table when one is given)
+//   u = W_cand E[c]   the candidate GEMM's split partials summed in order (or
+//                     a row of the folded table when one is given)
 //   b = LN(u), g = LN(W_ctx h) for the candidate's slot (from hproj)
 //   z = gamma * LN(W_fuse [b; g]) + beta, W_fuse on MFMA over [b; g] hi | lo
 //   stored as bf16 z hi | lo; cosine: unit(W_out z), unit(W_in z).
@@ -239,97 +250,23 @@ __global__ __launch_bounds__(256) void cand_kernel(CandArgs a) {
     const int M = static_cast<int>(min(static_cast<int64_t>(kCR), nodes - n0));
     const int r = a.r;
     const int nct = r / 16;
-    const int kq = 8 * (l >> 4);
     const int us = cand_us(r, a.vout ? a.dvec : 0);
     const int as = cand_as(r);
     float* ubuf = reinterpret_cast<float*>(smem_raw);                       // [kCR][us]
     uint16_t* abuf = reinterpret_cast<uint16_t*>(smem_raw + kCR * us * 4);  // [kCR][as]
 
-    // ---- u
-    if (a.table) {
-        for (int idx = tid; idx < M * r; idx += 256) {
-            const int m = idx / r, c = idx % r;
+    // ---- u: a row of the folded table, or the candidate GEMM's split partials
+    for (int idx = tid; idx < M * r; idx += 256) {
+        const int m = idx / r, c = idx % r;
+        float u;
+        if (a.table) {
             int64_t tok = a.ids[n0 + m];
             tok = tok < 0 ? 0 : (tok >= a.V ? a.V - 1 : tok);
-            ubuf[m * us + c] = a.table[tok * r + c];
+            u = a.table[tok * r + c];
+        } else {
+            u = sum_strided16(a.upart + (n0 + m) * r + c, nodes * r, a.usplits);
         }
-    } else {
-        uint16_t* As = reinterpret_cast<uint16_t*>(smem_raw);   // [2][kCR * kCLS]
-        uint16_t* Ws = As + 2 * kCR * kCLS;                      // [2][128 * kCLS]
-        const int ra = tid >> 3, sa = tid & 7;
-        const bool aok = ra < M;
-        int64_t tok = aok ? a.ids[n0 + ra] : 0;
-        tok = tok < 0 ? 0 : (tok >= a.V ? a.V - 1 : tok);
-        const uint16_t* ap = a.embed + tok * a.de + sa * 8;
-        const uint16_t* wp[4];
-        bool wok[4];
-        int woff[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int seg = tid + 256 * i;
-            const int rw = seg >> 3;
-            wok[i] = rw < r;
-            wp[i] = a.w_cand + static_cast<int64_t>(wok[i] ? rw : 0) * a.de + (seg & 7) * 8;
-            woff[i] = rw * kCLS + (seg & 7) * 8;
-        }
-        const u32x4 zero = {0u, 0u, 0u, 0u};
-        u32x4 rA, rW[4];
-        auto load = [&](int k0) {
-            const bool kok = k0 + sa * 8 < a.de;
-            rA = (aok && kok) ? load16(ap + k0) : zero;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) rW[i] = (wok[i] && kok) ? load16(wp[i] + k0) : zero;
-        };
-        auto store = [&](int buf) {
-            *reinterpret_cast<u32x4*>(&As[buf * kCR * kCLS + ra * kCLS + sa * 8]) = rA;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&Ws[buf * 128 * kCLS + woff[i]]) = rW[i];
-        };
-        f32x4 acc[2][2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int ct0 = 2 * wave, ct1 = 2 * wave + 1;
-        load(0);
-        store(0);
-        __syncthreads();
-        int buf = 0;
-        for (int k0 = 0; k0 < a.de; k0 += kBK) {
-            const bool more = k0 + kBK < a.de;
-            if (more) load(k0 + kBK);
-            if (ct0 < nct) {
-                const uint16_t* Ab = As + buf * kCR * kCLS;
-                const uint16_t* Wb = Ws + buf * 128 * kCLS;
-#pragma unroll
-                for (int ks = 0; ks < kBK; ks += 32) {
-                    const u32x4 a0 = *reinterpret_cast<const u32x4*>(&Ab[(l & 15) * kCLS + ks + kq]);
-                    const u32x4 a1 = *reinterpret_cast<const u32x4*>(&Ab[(16 + (l & 15)) * kCLS + ks + kq]);
-                    const u32x4 w0 = *reinterpret_cast<const u32x4*>(&Wb[(ct0 * 16 + (l & 15)) * kCLS + ks + kq]);
-                    acc[0][0] = mfma16x16x32(a0, w0, acc[0][0]);
-                    acc[1][0] = mfma16x16x32(a1, w0, acc[1][0]);
-                    if (ct1 < nct) {
-                        const u32x4 w1 = *reinterpret_cast<const u32x4*>(&Wb[(ct1 * 16 + (l & 15)) * kCLS + ks + kq]);
-                        acc[0][1] = mfma16x16x32(a0, w1, acc[0][1]);
-                        acc[1][1] = mfma16x16x32(a1, w1, acc[1][1]);
-                    }
-                }
-            }
-            if (more) store(buf ^ 1);
-            __syncthreads();
-            buf ^= 1;
-        }
-        // the slab buffers are dead after the last barrier; u goes to ubuf
-        if (ct0 < nct) {
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int m = rt * 16 + 4 * (l >> 4) + i;
-                    ubuf[m * us + ct0 * 16 + (l & 15)] = acc[rt][0][i];
-                    if (ct1 < nct) ubuf[m * us + ct1 * 16 + (l & 15)] = acc[rt][1][i];
-                }
-        }
+        ubuf[m * us + c] = u;
     }
     __syncthreads();
 
@@ -339,12 +276,10 @@ __global__ __launch_bounds__(256) void cand_kernel(CandArgs a) {
         wave_ln_regs(b0, b1, r, a.eps);
         const int64_t node = n0 + m;
         const int64_t t = node / a.K;
-        float g0 = 0.f, g1 = 0.f;
-        for (int sk = 0; sk < a.splits; ++sk) {
-            const float* hp = a.hproj + (static_cast<int64_t>(sk) * a.rows + t) * a.hstride;
-            if (l < r) g0 += hp[l];
-            if (l + 64 < r) g1 += hp[l + 64];
-        }
+        const float* hp = a.hproj + t * a.hstride;
+        const int64_t hs = a.rows * a.hstride;
+        float g0 = l < r ? sum_strided16(hp + l, hs, a.splits) : 0.f;
+        float g1 = l + 64 < r ? sum_strided16(hp + l + 64, hs, a.splits) : 0.f;
         wave_ln_regs(g0, g1, r, a.eps);
         if (node % a.K == 0) {
             if (l < r) a.g[t * r + l] = g0;
@@ -429,9 +364,7 @@ hipError_t launch_gemm(const GemmA& A, const GemmW& W, int64_t M, int N, int kdi
 }
 
 size_t cand_lds_bytes(int r, int dvec) {
-    const size_t gemm = sizeof(uint16_t) * (2 * kCR * kCLS + 2 * 128 * kCLS);
-    const size_t epi = sizeof(float) * kCR * cand_us(r, dvec) + sizeof(uint16_t) * kCR * cand_as(r);
-    return gemm > epi ? gemm : epi;
+    return sizeof(float) * kCR * cand_us(r, dvec) + sizeof(uint16_t) * kCR * cand_as(r);
 }
 
 hipError_t launch_cand(const CandArgs& a, hipStream_t stream) {

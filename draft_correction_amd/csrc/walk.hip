@@ -107,15 +107,27 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a, int use_lds) 
     const int KK = K * K;
     const int64_t per = static_cast<int64_t>(B - 1) * KK;
     const float b2 = a.b2[0];
-    for (int64_t idx = threadIdx.x; idx < per; idx += blockDim.x) {
-        const int p = static_cast<int>(idx / KK), e = static_cast<int>(idx % KK);
-        const int64_t pair = static_cast<int64_t>(req) * (B - 1) + p;
-        const float* pp = a.part + pair * a.nblk * KK + e;
-        float d = pp[0];
-        for (int jb = 1; jb < a.nblk; ++jb) d += pp[static_cast<int64_t>(jb) * KK];
-        const float sv = a.vals[(static_cast<int64_t>(req) * B + p + 1) * K + e % K] + (d + b2);
-        a.scores[pair * KK + e] = sv;
-        if (use_lds) sS[idx] = sv;
+    // 8 elements per thread per round, all loads issued before any is used
+    for (int64_t i0 = 0; i0 < per; i0 += 8 * 256) {
+        float d[8], lv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t idx = min(i0 + u * 256 + threadIdx.x, per - 1);  // clamped: in bounds
+            const int p = static_cast<int>(idx / KK), e = static_cast<int>(idx % KK);
+            const int64_t pair = static_cast<int64_t>(req) * (B - 1) + p;
+            d[u] = sum_strided16(a.part + pair * a.nblk * KK + e, KK, a.nblk);
+            lv[u] = a.vals[(static_cast<int64_t>(req) * B + p + 1) * K + e % K];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t idx = i0 + u * 256 + threadIdx.x;
+            if (idx < per) {
+                const int p = static_cast<int>(idx / KK), e = static_cast<int>(idx % KK);
+                const float sv = lv[u] + (d[u] + b2);
+                a.scores[(static_cast<int64_t>(req) * (B - 1) + p) * KK + e] = sv;
+                if (use_lds) sS[idx] = sv;
+            }
+        }
     }
     if (!a.tokens) return;
     __syncthreads();

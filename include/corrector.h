@@ -184,6 +184,20 @@ int corrector_run(const corrector *h, int32_t n_req, const void *logits, int64_t
                   int32_t *ids_or_null, float *vals_or_null, float *scores_or_null,
                   void *workspace, size_t workspace_bytes, void *stream);
 
+/* Folded candidate projection.  E and W_cand are frozen at inference, so
+ * u = W_cand E[c] can be tabulated once for the whole vocabulary:
+ * T = E W_cand^T, [V][r] float32 (an MFMA GEMM over every embedding row).
+ * corrector_table_bytes gives the size; corrector_fold_table fills a caller
+ * buffer on `stream`; corrector_use_table attaches it (NULL detaches), after
+ * which corrector_score / corrector_run gather rows of T instead of running
+ * the gathered-embedding GEMM each pass.  Results match the unfolded path to
+ * float32 rounding.  Attaching is the one mutation of a handle: it must not
+ * race with calls in flight on the handle.  Errors: CORR_E_NULL, CORR_E_ALIGN
+ * (the table must be 16-byte aligned), CORR_E_HANDLE. */
+size_t corrector_table_bytes(const corrector *h);
+int corrector_fold_table(const corrector *h, float *table, void *stream);
+int corrector_use_table(corrector *h, const float *table);
+
 /* Copy intermediates of the most recent corrector_score / corrector_run that
  * used `workspace` (same handle, same n_req) into caller buffers (float32,
  * any pointer may be NULL): z [n_req][B][K][r] (as stored, bfloat16 widened),

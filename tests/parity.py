@@ -56,12 +56,17 @@ def dev_inputs(x: dict) -> dict:
     return _dev_cache[key][1]
 
 
-def gpu_run(x: dict, n: int | None = None, first: int = 0, reps: int = 1) -> dict:
-    """One corrector_run over blocks [first, first+n) with every output captured."""
+def gpu_run(x: dict, n: int | None = None, first: int = 0, reps: int = 1, fold: bool = False) -> dict:
+    """One corrector_run over blocks [first, first+n) with every output captured.
+    With fold=True the candidate projection reads the folded table E W_cand^T."""
     cfg = x["cfg"]
     dev = dev_inputs(x)
     n = cfg["n"] - first if n is None else n
     corr = device.make_corrector(cfg, dev, max_requests=max(n, 1))
+    if fold:
+        table = torch.empty(corr.table_bytes() // 4, dtype=torch.float32, device="cuda")
+        corr.fold_table(table)
+        corr.use_table(table)
     st = device.strides(cfg)
     B, K = cfg["B"], cfg["K"]
     tokens = torch.empty((n, B), dtype=torch.int32, device="cuda")

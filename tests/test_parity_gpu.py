@@ -114,3 +114,46 @@ def test_stress():
     for i in (0, 128, 255):
         ora = P.oracle_run(x, n=1, first=i)
         P.check_all(P.select(gpu, i, 1), ora, "stress/%d" % i)
+
+
+# ---------------------------------------------------- folded projection --
+
+@pytest.mark.parametrize("name,head", [("tiny", "stress"), ("b1", "stress"), ("b32", "normal"),
+                                       ("b32", "stress")])
+def test_folded_table(name, head):
+    """corrector_fold_table + corrector_use_table: the candidate projection reads
+    rows of E W_cand^T; every gate as for the per-pass projection."""
+    _log("folded %s head=%s" % (name, head))
+    x = P.inputs(name, head=head)
+    gpu = P.gpu_run(x, fold=True)
+    ora = P.oracle_run(x)
+    P.check_all(gpu, ora, "folded/%s/%s" % (name, head))
+
+
+def test_folded_cosine():
+    _log("folded cosine")
+    x = P.inputs("cosine", sigma=8.0)
+    gpu = P.gpu_run(x, fold=True)
+    ora = P.oracle_run(x, n=1, first=7)
+    P.check_all(P.select(gpu, 7, 1), ora, "folded-cos", variant="cosine")
+
+
+def test_fold_table_rows():
+    """Rows of the folded table against a plain float64 product E[v] W_cand^T."""
+    import torch
+    from draft_correction_amd import device
+    from workload import bf16_bits_to_f32
+    x = P.inputs("b1")
+    cfg = x["cfg"]
+    dev = P.dev_inputs(x)
+    corr = device.make_corrector(cfg, dev)
+    table = torch.empty(corr.table_bytes() // 4, dtype=torch.float32, device="cuda")
+    corr.fold_table(table)
+    torch.cuda.synchronize()
+    T = table.view(cfg["V"], cfg["r"]).cpu().numpy()
+    corr.close()
+    rows = np.array([0, 1, 4095, 4096, 77777, cfg["V"] - 1])
+    E = bf16_bits_to_f32(x["embed"][rows]).astype(np.float64).reshape(len(rows), cfg["de"])
+    W = bf16_bits_to_f32(x["weights"]["w_cand"]).astype(np.float64).reshape(cfg["r"], cfg["de"])
+    want = E @ W.T
+    np.testing.assert_allclose(T[rows], want, rtol=1e-4, atol=1e-5 * np.abs(want).max())
