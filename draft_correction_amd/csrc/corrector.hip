@@ -290,7 +290,7 @@ int corrector_create(const corrector_desc* desc, const corrector_weights* wt, co
     if (d.variant != CORR_VARIANT_MLP && d.variant != CORR_VARIANT_COSINE) return CORR_E_UNSUPPORTED;
     if (d.logits_dtype != CORR_DTYPE_BF16 && d.logits_dtype != CORR_DTYPE_F32) return CORR_E_UNSUPPORTED;
     if (d.vocab < 1 || d.vocab > 0x7FFFFFFF) return CORR_E_SHAPE;
-    if (d.slots < 1 || d.slots > 64) return CORR_E_SHAPE;
+    if (d.slots < 1 || d.slots > 64) return CORR_E_SHAPE;  // the walk keeps one slot per lane
     if (d.k < 1 || d.k > 64 || d.k > d.vocab) return CORR_E_SHAPE;
     if (d.d_hidden < 32 || d.d_hidden % 32 || d.d_hidden > 65536) return CORR_E_SHAPE;
     if (d.d_embed < 32 || d.d_embed % 32 || d.d_embed > 65536) return CORR_E_SHAPE;
@@ -303,6 +303,10 @@ int corrector_create(const corrector_desc* desc, const corrector_weights* wt, co
         if (d.d_vec < 16 || d.d_vec > 128 || d.d_vec % 16) return CORR_E_UNSUPPORTED;
         if (!isfinite(d.sigma)) return CORR_E_SHAPE;
     }
+
+    // LDS of the candidate kernel (staging rows for 32 candidates)
+    if (cand_lds_bytes(d.r, d.variant == CORR_VARIANT_COSINE ? d.d_vec : 0, d.k) > 64 * 1024)
+        return CORR_E_UNSUPPORTED;
 
     const corrector_weights& w = *wt;
     if (!w.embed || !w.w_cand || !w.w_ctx || !w.w_fuse || !w.ln_gamma || !w.ln_beta) return CORR_E_NULL;

@@ -72,6 +72,7 @@ struct CandArgs {
     float* vout;
     float* vin;
 };
+size_t cand_lds_bytes(int r, int dvec, int K);
 hipError_t launch_cand(const CandArgs& a, hipStream_t stream);
 
 // ---- transition scores (mlp.hip, cosine.hip)

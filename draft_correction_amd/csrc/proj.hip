@@ -205,25 +205,34 @@ __device__ __forceinline__ void wave_layernorm(float* row, int m, float eps, con
 }
 
 __host__ __device__ inline int cand_us(int r, int dvec) { return (dvec > r ? dvec : r) + 4; }
+// Distinct slots a group of kCR consecutive candidates can touch.
+__host__ __device__ inline int cand_slots(int K) {
+    const int s = (kCR - 1) / K + 2;
+    return s < kCR ? s : kCR;
+}
 __host__ __device__ inline int cand_as(int r) { return 4 * r + 8; }
 
-// acc = A (16 rows of LDS bf16 [hi | lo], 2 * kin wide) x W^T for one 16-column
-// tile of W ([*][ldw] bf16, rows w_row0 + 0..15, columns 0..kin-1).  The hi and
-// lo halves of A meet the same W columns, so acc ~ A_fp32 x W^T.
-__device__ f32x4 mfma_hilo_tile(const uint16_t* abuf, int as, int M, const uint16_t* W, int ldw,
-                                int w_row0, int kin) {
+// acc = A (16 rows of LDS bf16 [hi | lo], 2 * KIN wide) x W^T for one 16-column
+// tile of W ([*][ldw] bf16, rows w_row0 + 0..15, columns 0..KIN-1).  The hi and
+// lo halves of A meet the same W columns, so acc ~ A_fp32 x W^T.  All W
+// fragments are loaded before the first MFMA.
+template <int KIN>
+__device__ __forceinline__ f32x4 mfma_hilo_tile(const uint16_t* abuf, int as, int M, const uint16_t* W,
+                                                int ldw, int w_row0) {
+    constexpr int KS = (2 * KIN + 31) / 32;
     const int l = lane_id();
     const int kq = 8 * (l >> 4);
     const int m = l & 15;
     const uint16_t* wp = W + static_cast<int64_t>(w_row0 + m) * ldw;
     const u32x4 zero = {0u, 0u, 0u, 0u};
+    u32x4 bv[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) bv[ks] = load16(wp + ((ks * 32 + kq) % KIN));
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < 2 * kin; k0 += 32) {
-        const int kg = k0 + kq;
-        const bool kin_ok = (kg % kin) + 8 <= kin;  // kin = 16: upper half of the step is padding
-        const u32x4 av = (m < M && kin_ok) ? *reinterpret_cast<const u32x4*>(abuf + m * as + kg) : zero;
-        const u32x4 bv = kin_ok ? load16(wp + (kg % kin)) : zero;
-        acc = mfma16x16x32(av, bv, acc);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 av = m < M ? *reinterpret_cast<const u32x4*>(abuf + m * as + ks * 32 + kq) : zero;
+        acc = mfma16x16x32(av, bv[ks], acc);
     }
     return acc;
 }
@@ -240,86 +249,108 @@ __device__ __forceinline__ void split_store(uint16_t* row, int width, int c, flo
 //   b = LN(u), g = LN(W_ctx h) for the candidate's slot (from hproj)
 //   z = gamma * LN(W_fuse [b; g]) + beta, W_fuse on MFMA over [b; g] hi | lo
 //   stored as bf16 z hi | lo; cosine: unit(W_out z), unit(W_in z).
+// Loops over r are compile-time so each phase issues all of its loads at once.
+template <int R>
 __global__ __launch_bounds__(256) void cand_kernel(CandArgs a) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+    constexpr int NCT = R / 16;
+    constexpr int PER = kCR * R / 256;      // u elements per thread
     const int tid = threadIdx.x;
     const int l = lane_id();
     const int wave = tid >> 6;
     const int64_t nodes = a.rows * a.K;
     const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kCR;
     const int M = static_cast<int>(min(static_cast<int64_t>(kCR), nodes - n0));
-    const int r = a.r;
-    const int nct = r / 16;
-    const int us = cand_us(r, a.vout ? a.dvec : 0);
-    const int as = cand_as(r);
+    const int us = cand_us(R, a.vout ? a.dvec : 0);
+    const int as = cand_as(R);
     float* ubuf = reinterpret_cast<float*>(smem_raw);                       // [kCR][us]
     uint16_t* abuf = reinterpret_cast<uint16_t*>(smem_raw + kCR * us * 4);  // [kCR][as]
+    float* gs = reinterpret_cast<float*>(smem_raw + kCR * us * 4 + kCR * as * 2);  // [cand_slots(K)][R]
 
     // ---- u: a row of the folded table, or the candidate GEMM's split partials
-    for (int idx = tid; idx < M * r; idx += 256) {
-        const int m = idx / r, c = idx % r;
-        float u;
-        if (a.table) {
-            int64_t tok = a.ids[n0 + m];
-            tok = tok < 0 ? 0 : (tok >= a.V ? a.V - 1 : tok);
-            u = a.table[tok * r + c];
-        } else {
-            u = sum_strided16(a.upart + (n0 + m) * r + c, nodes * r, a.usplits);
+    {
+        float uv[PER];
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int idx = tid + 256 * q;
+            const int m = min(idx / R, M - 1), c = idx % R;  // clamped rows are not stored
+            if (a.table) {
+                int64_t tok = a.ids[n0 + m];
+                tok = tok < 0 ? 0 : (tok >= a.V ? a.V - 1 : tok);
+                uv[q] = a.table[tok * R + c];
+            } else {
+                uv[q] = sum_strided16(a.upart + (n0 + m) * R + c, nodes * R, a.usplits);
+            }
         }
-        ubuf[m * us + c] = u;
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int idx = tid + 256 * q;
+            if (idx / R < M) ubuf[(idx / R) * us + idx % R] = uv[q];
+        }
+    }
+    // ---- g = LN(W_ctx h) once per distinct slot of this group
+    const int64_t t0 = n0 / a.K;
+    const int nslot = static_cast<int>((n0 + M - 1) / a.K - t0 + 1);
+    for (int sl = wave; sl < nslot; sl += 4) {
+        const int64_t t = t0 + sl;
+        const float* hp = a.hproj + t * a.hstride;
+        const int64_t hs = a.rows * a.hstride;
+        float g0 = l < R ? sum_strided16(hp + l, hs, a.splits) : 0.f;
+        float g1 = l + 64 < R ? sum_strided16(hp + l + 64, hs, a.splits) : 0.f;
+        wave_ln_regs(g0, g1, R, a.eps);
+        if (l < R) gs[sl * R + l] = g0;
+        if (l + 64 < R) gs[sl * R + l + 64] = g1;
+        if (t * a.K >= n0) {  // the group holding the slot's first candidate writes g
+            if (l < R) a.g[t * R + l] = g0;
+            if (l + 64 < R) a.g[t * R + l + 64] = g1;
+        }
     }
     __syncthreads();
 
-    // ---- b = LN(u) and g = LN(W_ctx h) per row, as [b; g] hi | lo in abuf
+    // ---- b = LN(u) per row; [b; g] as bf16 hi | lo rows in abuf
     for (int m = wave; m < M; m += 4) {
-        float b0 = l < r ? ubuf[m * us + l] : 0.f, b1 = l + 64 < r ? ubuf[m * us + l + 64] : 0.f;
-        wave_ln_regs(b0, b1, r, a.eps);
-        const int64_t node = n0 + m;
-        const int64_t t = node / a.K;
-        const float* hp = a.hproj + t * a.hstride;
-        const int64_t hs = a.rows * a.hstride;
-        float g0 = l < r ? sum_strided16(hp + l, hs, a.splits) : 0.f;
-        float g1 = l + 64 < r ? sum_strided16(hp + l + 64, hs, a.splits) : 0.f;
-        wave_ln_regs(g0, g1, r, a.eps);
-        if (node % a.K == 0) {
-            if (l < r) a.g[t * r + l] = g0;
-            if (l + 64 < r) a.g[t * r + l + 64] = g1;
-        }
+        float b0 = l < R ? ubuf[m * us + l] : 0.f, b1 = l + 64 < R ? ubuf[m * us + l + 64] : 0.f;
+        wave_ln_regs(b0, b1, R, a.eps);
+        const int sl = static_cast<int>((n0 + m) / a.K - t0);
         uint16_t* arow = abuf + m * as;
-        if (l < r) {
-            split_store(arow, 2 * r, l, b0);
-            split_store(arow, 2 * r, r + l, g0);
+        if (l < R) {
+            split_store(arow, 2 * R, l, b0);
+            split_store(arow, 2 * R, R + l, gs[sl * R + l]);
         }
-        if (l + 64 < r) {
-            split_store(arow, 2 * r, l + 64, b1);
-            split_store(arow, 2 * r, r + l + 64, g1);
+        if (l + 64 < R) {
+            split_store(arow, 2 * R, l + 64, b1);
+            split_store(arow, 2 * R, R + l + 64, gs[sl * R + l + 64]);
         }
     }
     __syncthreads();
 
     // ---- y = W_fuse [b; g] (MFMA on the hi / lo split), into ubuf
     const int nrt = (M + 15) / 16;
-    for (int job = wave; job < nrt * nct; job += 4) {
-        const int rt = job / nct, ct = job % nct;
-        const f32x4 acc = mfma_hilo_tile(abuf + rt * 16 * as, as, M - rt * 16, a.w_fuse, 2 * r, ct * 16, 2 * r);
+    for (int job = wave; job < nrt * NCT; job += 4) {
+        const int rt = job / NCT, ct = job % NCT;
+        const f32x4 acc = mfma_hilo_tile<2 * R>(abuf + rt * 16 * as, as, M - rt * 16, a.w_fuse, 2 * R, ct * 16);
 #pragma unroll
         for (int i = 0; i < 4; ++i) ubuf[(rt * 16 + 4 * (l >> 4) + i) * us + ct * 16 + (l & 15)] = acc[i];
     }
     __syncthreads();
 
     // ---- z = gamma * LN(y) + beta; stored as bf16 hi | lo (and kept in abuf)
-    for (int m = wave; m < M; m += 4) wave_layernorm(ubuf + m * us, r, a.eps, a.gamma, a.beta);
+    for (int m = wave; m < M; m += 4) wave_layernorm(ubuf + m * us, R, a.eps, a.gamma, a.beta);
     __syncthreads();
-    for (int idx = tid; idx < M * r; idx += 256) {
-        const int m = idx / r, c = idx % r;
-        const float zv = ubuf[m * us + c];
-        const uint16_t hi = f32_to_bf16(zv);
-        const uint16_t lo = f32_to_bf16(zv - bf16_to_f32(hi));
-        uint16_t* grow = a.zhl + (n0 + m) * (2 * r);
-        grow[c] = hi;
-        grow[r + c] = lo;
-        abuf[m * as + c] = hi;
-        abuf[m * as + r + c] = lo;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        const int idx = tid + 256 * q;
+        const int m = idx / R, c = idx % R;
+        if (m < M) {
+            const float zv = ubuf[m * us + c];
+            const uint16_t hi = f32_to_bf16(zv);
+            const uint16_t lo = f32_to_bf16(zv - bf16_to_f32(hi));
+            uint16_t* grow = a.zhl + (n0 + m) * (2 * R);
+            grow[c] = hi;
+            grow[R + c] = lo;
+            abuf[m * as + c] = hi;
+            abuf[m * as + R + c] = lo;
+        }
     }
     if (!a.vout) return;
     __syncthreads();
@@ -330,8 +361,8 @@ __global__ __launch_bounds__(256) void cand_kernel(CandArgs a) {
     for (int which = 0; which < 2; ++which) {
         for (int job = wave; job < nrt * nvt; job += 4) {
             const int rt = job / nvt, ct = job % nvt;
-            const f32x4 acc = mfma_hilo_tile(abuf + rt * 16 * as, as, M - rt * 16, which ? a.w_in : a.w_out, r,
-                                             ct * 16, r);
+            const f32x4 acc = mfma_hilo_tile<R>(abuf + rt * 16 * as, as, M - rt * 16, which ? a.w_in : a.w_out, R,
+                                                ct * 16);
 #pragma unroll
             for (int i = 0; i < 4; ++i) ubuf[(rt * 16 + 4 * (l >> 4) + i) * us + ct * 16 + (l & 15)] = acc[i];
         }
@@ -363,14 +394,22 @@ hipError_t launch_gemm(const GemmA& A, const GemmW& W, int64_t M, int N, int kdi
     return hipGetLastError();
 }
 
-size_t cand_lds_bytes(int r, int dvec) {
-    return sizeof(float) * kCR * cand_us(r, dvec) + sizeof(uint16_t) * kCR * cand_as(r);
+size_t cand_lds_bytes(int r, int dvec, int K) {
+    return sizeof(float) * kCR * cand_us(r, dvec) + sizeof(uint16_t) * kCR * cand_as(r) +
+           sizeof(float) * cand_slots(K) * r;
 }
 
 hipError_t launch_cand(const CandArgs& a, hipStream_t stream) {
     const int64_t nodes = a.rows * a.K;
     const dim3 grid(static_cast<unsigned>((nodes + kCR - 1) / kCR));
-    cand_kernel<<<grid, 256, cand_lds_bytes(a.r, a.vout ? a.dvec : 0), stream>>>(a);
+    const size_t lds = cand_lds_bytes(a.r, a.vout ? a.dvec : 0, a.K);
+    switch (a.r) {
+        case 16: cand_kernel<16><<<grid, 256, lds, stream>>>(a); break;
+        case 32: cand_kernel<32><<<grid, 256, lds, stream>>>(a); break;
+        case 64: cand_kernel<64><<<grid, 256, lds, stream>>>(a); break;
+        case 128: cand_kernel<128><<<grid, 256, lds, stream>>>(a); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -34,10 +34,7 @@ __device__ void walk_wave(const float* src, const int32_t* __restrict__ ids, int
                           int32_t* __restrict__ tokens, int32_t* __restrict__ choice) {
     const int l = lane_id();
     int k = 0;
-    if (l == 0) {
-        if (choice) choice[static_cast<int64_t>(req) * B] = 0;
-        tokens[static_cast<int64_t>(req) * B] = ids[static_cast<int64_t>(req) * B * K];
-    }
+    int mych = 0;  // lane s < B keeps choice[s]
     for (int p = 0; p + 1 < B; ++p) {
         const float* row = src + (static_cast<int64_t>(p) * K + k) * K;
         float v = l < K ? row[l] : -INFINITY;
@@ -52,11 +49,13 @@ __device__ void walk_wave(const float* src, const int32_t* __restrict__ ids, int
             }
         }
         k = __shfl(bi, 0, kWave);  // lane 0 always holds an index < K
-        if (l == 0) {
-            const int64_t s = static_cast<int64_t>(req) * B + p + 1;
-            if (choice) choice[s] = k;
-            tokens[s] = ids[s * K + k];
-        }
+        if (l == p + 1) mych = k;
+    }
+    // tokens[s] = ids[s][choice[s]]: one gather per lane after the walk
+    if (l < B) {
+        const int64_t s = static_cast<int64_t>(req) * B + l;
+        if (choice) choice[s] = mych;
+        tokens[s] = ids[s * K + mych];
     }
 }
 
