@@ -83,17 +83,18 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Sum of `n` (<= 16) values v[0], v[stride], ... in index order, with every
-// load issued before the first add (a runtime-length loop would wait one
-// memory round trip per term).
-__device__ __forceinline__ float sum_strided16(const float* v, int64_t stride, int n) {
-    float t[16];
+// Sum of n (1 <= n <= NMAX) values v[0], v[stride], ... in index order.  The
+// loads are unconditional (terms past n re-read term n-1, always in bounds)
+// and the unwanted ones are dropped with selects, so the code is straight-line
+// and every load is issued before the first add.
+template <int NMAX>
+__device__ __forceinline__ float sum_strided(const float* v, int64_t stride, int n) {
+    float t[NMAX];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) t[i] = i < n ? v[i * stride] : 0.f;
+    for (int i = 0; i < NMAX; ++i) t[i] = v[static_cast<int64_t>(i < n ? i : n - 1) * stride];
     float s = t[0];
 #pragma unroll
-    for (int i = 1; i < 16; ++i)
-        if (i < n) s += t[i];
+    for (int i = 1; i < NMAX; ++i) s = i < n ? s + t[i] : s;
     return s;
 }
 

@@ -51,12 +51,12 @@ int logits_elem_bytes(const corrector_desc& d) { return d.logits_dtype == CORR_D
 // request's results do not depend on how many requests share the call.
 int choose_splits(const corrector_desc& d) {
     int s = d.d_hidden / 512;
-    if (s > 16) s = 16;
+    if (s > kMaxSplits) s = kMaxSplits;
     return s < 1 ? 1 : s;
 }
 int choose_usplits(const corrector_desc& d) {
     int s = d.d_embed / 1024;
-    if (s > 16) s = 16;
+    if (s > kMaxUSplits) s = kMaxUSplits;
     return s < 1 ? 1 : s;
 }
 

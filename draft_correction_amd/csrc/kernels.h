@@ -11,6 +11,12 @@
 
 namespace corr {
 
+// Upper bounds of the split-K factors of the two projection GEMMs (the hidden-
+// state projections and the candidate projection); consumers sum that many
+// partials at most.
+constexpr int kMaxSplits = 8;
+constexpr int kMaxUSplits = 4;
+
 // ---- top-K (topk.hip)
 // part [rows][chunks][K]: each chunk's K best as 64-bit composites
 // (float32-order value key << 32 | inverted token id; 0 = no element).

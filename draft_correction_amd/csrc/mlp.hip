@@ -67,6 +67,20 @@ __device__ __forceinline__ void pq_tile(const MlpArgs& a, int which, int j0, int
         bs[ks] = which ? zero : u32x4{ws[o], ws[o + 1], ws[o + 2], ws[o + 3]};
     }
     const float wl = bf16_to_f32(a.w1[static_cast<int64_t>(j) * nin + 3 * R + which]);
+    const float b1j = which ? 0.f : a.b1[j];
+    const int nrt = (K + 15) / 16;
+    // z fragments of a row tile (rows past K read row 0 and are zeroed)
+    auto zfrag = [&](int rt, u32x4* af) {
+        const int m = rt * 16 + (l & 15);
+        const uint16_t* zr = a.zhl + (zrow0 + (m < K ? m : 0)) * (2 * R);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const u32x4 v = load16(zr + ks * 32 + kq);
+            af[ks] = m < K ? v : zero;
+        }
+    };
+    u32x4 af[KS];
+    zfrag(0, af);  // issued with the weight loads above, before any MFMA
     float cj = 0.f;
     if (!which) {
         // c_p tile: A row 0 = [s_hi | s_lo], other rows zero
@@ -76,15 +90,10 @@ __device__ __forceinline__ void pq_tile(const MlpArgs& a, int which, int j0, int
             const u32x4 av = (l & 15) == 0 ? *reinterpret_cast<const u32x4*>(shv + ks * 32 + kq) : zero;
             acc = mfma16x16x32(av, bs[ks], acc);
         }
-        cj = __shfl(acc[0], l & 15, kWave) + a.b1[j];   // D[0][col] lives in lanes 0..15
+        cj = __shfl(acc[0], l & 15, kWave) + b1j;   // D[0][col] lives in lanes 0..15
     }
-    const int nrt = (K + 15) / 16;
     for (int rt = 0; rt < nrt; ++rt) {
-        const int m = rt * 16 + (l & 15);
-        const uint16_t* zr = a.zhl + (zrow0 + (m < K ? m : 0)) * (2 * R);
-        u32x4 af[KS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) af[ks] = m < K ? load16(zr + ks * 32 + kq) : zero;
+        if (rt > 0) zfrag(rt, af);
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(af[ks], bz[ks], acc);
@@ -125,8 +134,8 @@ __global__ __launch_bounds__(256) void mlp_kernel(MlpArgs a) {
     // ---- pair state s_p = W_pair,L h_p + W_pair,R h_{p+1}, logits, w2
     for (int c = tid; c < R; c += 256) {
         const int64_t sstride = nslots * (3 * R);
-        const float sl = sum_strided16(a.hproj + tp * (3 * R) + R + c, sstride, a.splits);
-        const float sr = sum_strided16(a.hproj + tq * (3 * R) + 2 * R + c, sstride, a.splits);
+        const float sl = sum_strided<kMaxSplits>(a.hproj + tp * (3 * R) + R + c, sstride, a.splits);
+        const float sr = sum_strided<kMaxSplits>(a.hproj + tq * (3 * R) + 2 * R + c, sstride, a.splits);
         const float s = sl + sr;
         const uint16_t hi = f32_to_bf16(s);
         shv[c] = hi;

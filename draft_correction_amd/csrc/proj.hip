@@ -279,7 +279,7 @@ __global__ __launch_bounds__(256) void cand_kernel(CandArgs a) {
                 tok = tok < 0 ? 0 : (tok >= a.V ? a.V - 1 : tok);
                 uv[q] = a.table[tok * R + c];
             } else {
-                uv[q] = sum_strided16(a.upart + (n0 + m) * R + c, nodes * R, a.usplits);
+                uv[q] = sum_strided<kMaxUSplits>(a.upart + (n0 + m) * R + c, nodes * R, a.usplits);
             }
         }
 #pragma unroll
@@ -289,14 +289,16 @@ __global__ __launch_bounds__(256) void cand_kernel(CandArgs a) {
         }
     }
     // ---- g = LN(W_ctx h) once per distinct slot of this group
-    const int64_t t0 = n0 / a.K;
-    const int nslot = static_cast<int>((n0 + M - 1) / a.K - t0 + 1);
+    // nodes < 2^30 (rows <= 2^24, K <= 64): 32-bit slot arithmetic
+    const int n0i = static_cast<int>(n0);
+    const int t0 = n0i / a.K;
+    const int nslot = (n0i + M - 1) / a.K - t0 + 1;
     for (int sl = wave; sl < nslot; sl += 4) {
         const int64_t t = t0 + sl;
         const float* hp = a.hproj + t * a.hstride;
         const int64_t hs = a.rows * a.hstride;
-        float g0 = l < R ? sum_strided16(hp + l, hs, a.splits) : 0.f;
-        float g1 = l + 64 < R ? sum_strided16(hp + l + 64, hs, a.splits) : 0.f;
+        float g0 = l < R ? sum_strided<kMaxSplits>(hp + l, hs, a.splits) : 0.f;
+        float g1 = l + 64 < R ? sum_strided<kMaxSplits>(hp + l + 64, hs, a.splits) : 0.f;
         wave_ln_regs(g0, g1, R, a.eps);
         if (l < R) gs[sl * R + l] = g0;
         if (l + 64 < R) gs[sl * R + l + 64] = g1;
@@ -311,7 +313,7 @@ __global__ __launch_bounds__(256) void cand_kernel(CandArgs a) {
     for (int m = wave; m < M; m += 4) {
         float b0 = l < R ? ubuf[m * us + l] : 0.f, b1 = l + 64 < R ? ubuf[m * us + l + 64] : 0.f;
         wave_ln_regs(b0, b1, R, a.eps);
-        const int sl = static_cast<int>((n0 + m) / a.K - t0);
+        const int sl = (n0i + m) / a.K - t0;
         uint16_t* arow = abuf + m * as;
         if (l < R) {
             split_store(arow, 2 * R, l, b0);

@@ -106,24 +106,26 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a, int use_lds) 
     const int KK = K * K;
     const int64_t per = static_cast<int64_t>(B - 1) * KK;
     const float b2 = a.b2[0];
+    const int per32 = static_cast<int>(per);   // (B-1) K^2 < 2^31: 32-bit index math
+    const float* part_req = a.part + static_cast<int64_t>(req) * (B - 1) * a.nblk * KK;
+    const float* vals_req = a.vals + static_cast<int64_t>(req) * B * K;
+    float* scores_req = a.scores + static_cast<int64_t>(req) * per;
     // 8 elements per thread per round, all loads issued before any is used
-    for (int64_t i0 = 0; i0 < per; i0 += 8 * 256) {
+    for (int i0 = 0; i0 < per32; i0 += 8 * 256) {
         float d[8], lv[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            const int64_t idx = min(i0 + u * 256 + threadIdx.x, per - 1);  // clamped: in bounds
-            const int p = static_cast<int>(idx / KK), e = static_cast<int>(idx % KK);
-            const int64_t pair = static_cast<int64_t>(req) * (B - 1) + p;
-            d[u] = sum_strided16(a.part + pair * a.nblk * KK + e, KK, a.nblk);
-            lv[u] = a.vals[(static_cast<int64_t>(req) * B + p + 1) * K + e % K];
+            const int idx = min(i0 + u * 256 + static_cast<int>(threadIdx.x), per32 - 1);  // clamped: in bounds
+            const int p = idx / KK, e = idx - p * KK;
+            d[u] = sum_strided<4>(part_req + (p * a.nblk) * KK + e, KK, a.nblk);
+            lv[u] = vals_req[(p + 1) * K + e % K];
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            const int64_t idx = i0 + u * 256 + threadIdx.x;
-            if (idx < per) {
-                const int p = static_cast<int>(idx / KK), e = static_cast<int>(idx % KK);
+            const int idx = i0 + u * 256 + static_cast<int>(threadIdx.x);
+            if (idx < per32) {
                 const float sv = lv[u] + (d[u] + b2);
-                a.scores[(static_cast<int64_t>(req) * (B - 1) + p) * KK + e] = sv;
+                scores_req[idx] = sv;
                 if (use_lds) sS[idx] = sv;
             }
         }
