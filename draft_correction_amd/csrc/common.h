@@ -76,6 +76,50 @@ __device__ __forceinline__ float wave_sum16(float v) {
     return v;
 }
 
+// ------------------------------------------------------------ DPP rows --
+// Cross-lane moves inside 16-lane rows without LDS (quad_perm, row mirrors).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within each half row
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within each row
+
+// Sum over the 16 lanes of each row, returned to all of them (every lane
+// computes the same additions in the same order, so the results agree bitwise).
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_f<kDppXor1>(v);
+    v += dpp_f<kDppXor2>(v);
+    v += dpp_f<kDppHalfMirror>(v);
+    v += dpp_f<kDppMirror>(v);
+    return v;
+}
+
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, dpp_f<kDppXor1>(v));
+    v = fmaxf(v, dpp_f<kDppXor2>(v));
+    v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp_f<kDppMirror>(v));
+    return v;
+}
+
+// Lowest lane l < n (n <= 64) holding the largest v (wave-uniform result).
+__device__ __forceinline__ int wave_argmax_lowest(float v, int n) {
+    const int l = threadIdx.x & 63;
+    const float x = l < n ? v : -INFINITY;
+    const float m = row16_max(x);
+    float best = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 0));
+    if (n > 16) {
+        best = fmaxf(best, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 16)));
+        best = fmaxf(best, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 32)));
+        best = fmaxf(best, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 48)));
+    }
+    const uint64_t mask = __ballot(l < n && x == best);
+    return mask ? __ffsll(static_cast<unsigned long long>(mask)) - 1 : 0;
+}
+
 // Make this wave's LDS writes visible to its other lanes.
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

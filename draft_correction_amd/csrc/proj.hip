@@ -176,32 +176,24 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmA A, GemmW W, int64_t M, 
 
 constexpr int kCR = 32;                 // candidate rows per workgroup
 
-// LayerNorm over m <= 128 values held two per lane (v0 at index l, v1 at
-// l + 64), by one wave; returns the normalised pair.
-__device__ __forceinline__ void wave_ln_regs(float& v0, float& v1, int m, float eps) {
-    const int l = lane_id();
-    float s = (l < m ? v0 : 0.f) + (l + 64 < m ? v1 : 0.f);
+// LayerNorm of one row of R values held by the 16 lanes of a DPP row, R/16
+// consecutive values per lane; statistics in float32, biased variance.
+template <int R>
+__device__ __forceinline__ void row16_layernorm(float (&v)[R / 16], float eps) {
+    constexpr int VPL = R / 16;
+    float s = 0.f;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, kWave);
-    const float mean = s / static_cast<float>(m);
-    const float d0 = l < m ? v0 - mean : 0.f;
-    const float d1 = l + 64 < m ? v1 - mean : 0.f;
-    float q = d0 * d0 + d1 * d1;
+    for (int i = 0; i < VPL; ++i) s += v[i];
+    const float mean = row16_sum(s) * (1.0f / R);
+    float q = 0.f;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) q += __shfl_xor(q, o, kWave);
-    const float inv = 1.0f / sqrtf(q / static_cast<float>(m) + eps);
-    v0 = d0 * inv;
-    v1 = d1 * inv;
-}
-
-// LayerNorm of one LDS row in place (affine when gamma is given), by one wave.
-__device__ __forceinline__ void wave_layernorm(float* row, int m, float eps, const float* gamma,
-                                               const float* beta) {
-    const int l = lane_id();
-    float v0 = l < m ? row[l] : 0.f, v1 = l + 64 < m ? row[l + 64] : 0.f;
-    wave_ln_regs(v0, v1, m, eps);
-    if (l < m) row[l] = gamma ? fmaf(gamma[l], v0, beta[l]) : v0;
-    if (l + 64 < m) row[l + 64] = gamma ? fmaf(gamma[l + 64], v1, beta[l + 64]) : v1;
+    for (int i = 0; i < VPL; ++i) {
+        v[i] -= mean;
+        q += v[i] * v[i];
+    }
+    const float inv = 1.0f / sqrtf(row16_sum(q) * (1.0f / R) + eps);
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) v[i] *= inv;
 }
 
 __host__ __device__ inline int cand_us(int r, int dvec) { return (dvec > r ? dvec : r) + 4; }
@@ -288,40 +280,46 @@ __global__ __launch_bounds__(256) void cand_kernel(CandArgs a) {
             if (idx / R < M) ubuf[(idx / R) * us + idx % R] = uv[q];
         }
     }
-    // ---- g = LN(W_ctx h) once per distinct slot of this group
     // nodes < 2^30 (rows <= 2^24, K <= 64): 32-bit slot arithmetic
     const int n0i = static_cast<int>(n0);
     const int t0 = n0i / a.K;
     const int nslot = (n0i + M - 1) / a.K - t0 + 1;
-    for (int sl = wave; sl < nslot; sl += 4) {
+    // Rows are processed 16 lanes each (4 per wave, 16 per pass of the
+    // workgroup): lane c16 = l & 15 holds columns c16*VPL .. c16*VPL+VPL-1.
+    constexpr int VPL = R / 16;
+    const int c16 = l & 15;
+    const int rsub = wave * 4 + (l >> 4);   // 0..15
+    // ---- g = LN(W_ctx h) once per distinct slot of this group
+    const int64_t hs = a.rows * a.hstride;
+    for (int sl = rsub; sl < nslot; sl += 16) {
         const int64_t t = t0 + sl;
-        const float* hp = a.hproj + t * a.hstride;
-        const int64_t hs = a.rows * a.hstride;
-        float g0 = l < R ? sum_strided<kMaxSplits>(hp + l, hs, a.splits) : 0.f;
-        float g1 = l + 64 < R ? sum_strided<kMaxSplits>(hp + l + 64, hs, a.splits) : 0.f;
-        wave_ln_regs(g0, g1, R, a.eps);
-        if (l < R) gs[sl * R + l] = g0;
-        if (l + 64 < R) gs[sl * R + l + 64] = g1;
+        const float* hp = a.hproj + t * a.hstride + c16 * VPL;
+        float gv[VPL];
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) gv[i] = sum_strided<kMaxSplits>(hp + i, hs, a.splits);
+        row16_layernorm<R>(gv, a.eps);
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) gs[sl * R + c16 * VPL + i] = gv[i];
         if (t * a.K >= n0) {  // the group holding the slot's first candidate writes g
-            if (l < R) a.g[t * R + l] = g0;
-            if (l + 64 < R) a.g[t * R + l + 64] = g1;
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) a.g[t * R + c16 * VPL + i] = gv[i];
         }
     }
     __syncthreads();
 
     // ---- b = LN(u) per row; [b; g] as bf16 hi | lo rows in abuf
-    for (int m = wave; m < M; m += 4) {
-        float b0 = l < R ? ubuf[m * us + l] : 0.f, b1 = l + 64 < R ? ubuf[m * us + l + 64] : 0.f;
-        wave_ln_regs(b0, b1, R, a.eps);
+    for (int m = rsub; m < M; m += 16) {
+        float bv[VPL];
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) bv[i] = ubuf[m * us + c16 * VPL + i];
+        row16_layernorm<R>(bv, a.eps);
         const int sl = (n0i + m) / a.K - t0;
         uint16_t* arow = abuf + m * as;
-        if (l < R) {
-            split_store(arow, 2 * R, l, b0);
-            split_store(arow, 2 * R, R + l, gs[sl * R + l]);
-        }
-        if (l + 64 < R) {
-            split_store(arow, 2 * R, l + 64, b1);
-            split_store(arow, 2 * R, R + l + 64, gs[sl * R + l + 64]);
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            const int c = c16 * VPL + i;
+            split_store(arow, 2 * R, c, bv[i]);
+            split_store(arow, 2 * R, R + c, gs[sl * R + c]);
         }
     }
     __syncthreads();
@@ -337,17 +335,18 @@ __global__ __launch_bounds__(256) void cand_kernel(CandArgs a) {
     __syncthreads();
 
     // ---- z = gamma * LN(y) + beta; stored as bf16 hi | lo (and kept in abuf)
-    for (int m = wave; m < M; m += 4) wave_layernorm(ubuf + m * us, R, a.eps, a.gamma, a.beta);
-    __syncthreads();
+    for (int m = rsub; m < M; m += 16) {
+        float zv[VPL];
 #pragma unroll
-    for (int q = 0; q < PER; ++q) {
-        const int idx = tid + 256 * q;
-        const int m = idx / R, c = idx % R;
-        if (m < M) {
-            const float zv = ubuf[m * us + c];
-            const uint16_t hi = f32_to_bf16(zv);
-            const uint16_t lo = f32_to_bf16(zv - bf16_to_f32(hi));
-            uint16_t* grow = a.zhl + (n0 + m) * (2 * R);
+        for (int i = 0; i < VPL; ++i) zv[i] = ubuf[m * us + c16 * VPL + i];
+        row16_layernorm<R>(zv, a.eps);
+        uint16_t* grow = a.zhl + (n0 + m) * (2 * R);
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            const int c = c16 * VPL + i;
+            const float z = fmaf(a.gamma[c], zv[i], a.beta[c]);
+            const uint16_t hi = f32_to_bf16(z);
+            const uint16_t lo = f32_to_bf16(z - bf16_to_f32(hi));
             grow[c] = hi;
             grow[R + c] = lo;
             abuf[m * as + c] = hi;
@@ -369,17 +368,15 @@ __global__ __launch_bounds__(256) void cand_kernel(CandArgs a) {
             for (int i = 0; i < 4; ++i) ubuf[(rt * 16 + 4 * (l >> 4) + i) * us + ct * 16 + (l & 15)] = acc[i];
         }
         __syncthreads();
-        for (int m = wave; m < M; m += 4) {
-            const float* v = ubuf + m * us;
-            const float x0 = l < dv ? v[l] : 0.f;
-            const float x1 = l + 64 < dv ? v[l + 64] : 0.f;
-            float q = x0 * x0 + x1 * x1;
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) q += __shfl_xor(q, o, kWave);
-            const float inv = 1.0f / fmaxf(sqrtf(q), 1e-12f);
-            float* dst = (which ? a.vin : a.vout) + (n0 + m) * dv;
-            if (l < dv) dst[l] = x0 * inv;
-            if (l + 64 < dv) dst[l + 64] = x1 * inv;
+        for (int m = rsub; m < M; m += 16) {
+            // dv = 16 * (dv / 16) columns, dv / 16 per lane of the row
+            const int vpl = dv / 16;
+            const float* v = ubuf + m * us + c16 * vpl;
+            float q = 0.f;
+            for (int i = 0; i < vpl; ++i) q += v[i] * v[i];
+            const float inv = 1.0f / fmaxf(sqrtf(row16_sum(q)), 1e-12f);
+            float* dst = (which ? a.vin : a.vout) + (n0 + m) * dv + c16 * vpl;
+            for (int i = 0; i < vpl; ++i) dst[i] = v[i] * inv;
         }
         __syncthreads();
     }

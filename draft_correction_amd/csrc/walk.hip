@@ -37,18 +37,7 @@ __device__ void walk_wave(const float* src, const int32_t* __restrict__ ids, int
     int mych = 0;  // lane s < B keeps choice[s]
     for (int p = 0; p + 1 < B; ++p) {
         const float* row = src + (static_cast<int64_t>(p) * K + k) * K;
-        float v = l < K ? row[l] : -INFINITY;
-        int bi = l < K ? l : 0x7FFFFFFF;
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-            const float ov = __shfl_xor(v, o, kWave);
-            const int oi = __shfl_xor(bi, o, kWave);
-            if (ov > v || (ov == v && oi < bi)) {
-                v = ov;
-                bi = oi;
-            }
-        }
-        k = __shfl(bi, 0, kWave);  // lane 0 always holds an index < K
+        k = wave_argmax_lowest(l < K ? row[l] : 0.f, K);
         if (l == p + 1) mych = k;
     }
     // tokens[s] = ids[s][choice[s]]: one gather per lane after the walk
