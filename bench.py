@@ -108,6 +108,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--head", default="normal")
     ap.add_argument("--no-fold", action="store_true", help="skip the folded-table measurement")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="first run a plain device copy of this many MiB (a known-size reference "
+                         "for hardware traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -146,6 +149,15 @@ def main():
         corr.run(n, s["logits"], st["l_req"], st["l_slot"], s["hidden"], st["h_req"], st["h_slot"],
                  tokens, ws, l_offset=st["l_off"], h_offset=st["h_off"], stream=stream)
 
+    if args.calibrate_copy:
+        nb = args.calibrate_copy << 20
+        src = torch.empty(nb, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: %d bytes read, %d bytes written" % (nb, nb))
+        del src, dst
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()

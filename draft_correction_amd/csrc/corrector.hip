@@ -20,7 +20,7 @@ constexpr int kMaxKernels = 8;
 constexpr size_t kAlign = 256;
 
 struct Layout {
-    size_t part, ids, vals, hproj, upart, z, g, s, vout, vin, mlp_part, scores, total;
+    size_t part, ids, vals, hproj, upart, z, g, s, shl, vout, vin, mlp_part, scores, total;
     int chunks, splits, usplits;
 };
 
@@ -79,6 +79,7 @@ Layout layout(const corrector_desc& d, int32_t n) {
     L.z = take(sizeof(uint16_t) * rows * d.k * 2 * d.r);
     L.g = take(sizeof(float) * rows * d.r);
     L.s = take(sizeof(float) * pairs * d.r);
+    L.shl = take(sizeof(uint16_t) * pairs * 2 * d.r);
     L.mlp_part = take(d.variant == CORR_VARIANT_MLP ? sizeof(float) * pairs * mlp_blocks(d.mlp_hidden) * d.k * d.k : 0);
     const bool cos = d.variant == CORR_VARIANT_COSINE;
     L.vout = take(cos ? sizeof(float) * rows * d.k * d.d_vec : 0);
@@ -220,6 +221,9 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
     ca.splits = L.splits;
     ca.zhl = at<uint16_t>(ws, L.z);
     ca.g = at<float>(ws, L.g);
+    ca.B = d.slots;
+    ca.shl = (!cos && d.slots > 1) ? at<uint16_t>(ws, L.shl) : nullptr;
+    ca.s_out = at<float>(ws, L.s);
     if (cos) {
         ca.w_out = static_cast<const uint16_t*>(w.w_out);
         ca.w_in = static_cast<const uint16_t*>(w.w_in);
@@ -249,8 +253,7 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
         MlpArgs m{};
         m.zhl = ca.zhl;
         m.vals = vals;
-        m.hproj = hproj;
-        m.splits = L.splits;
+        m.shl = ca.shl;
         m.n = n;
         m.B = d.slots;
         m.K = d.k;
@@ -260,7 +263,6 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
         m.b1 = w.b1;
         m.w2 = w.w2;
         m.part = at<float>(ws, L.mlp_part);
-        m.s_out = at<float>(ws, L.s);
         q("mlp", [&] { return launch_mlp(m, q.s); });
         FinishArgs f{};
         f.part = m.part;

@@ -71,6 +71,12 @@ struct CandArgs {
     int splits;
     uint16_t* zhl;
     float* g;
+    // pair state (MLP variant only; null otherwise): s_p = W_pair,L h_p +
+    // W_pair,R h_{p+1} for pairs starting in this group's slots, stored as
+    // bf16 hi | lo shl [n(B-1)][2r] and as float32 s_out [n(B-1)][r]
+    int B;
+    uint16_t* shl;
+    float* s_out;
     // cosine only (null otherwise)
     const uint16_t* w_out;
     const uint16_t* w_in;
@@ -85,8 +91,7 @@ hipError_t launch_cand(const CandArgs& a, hipStream_t stream);
 struct MlpArgs {
     const uint16_t* zhl;    // [n][B][K][2r] bfloat16 hi | lo
     const float* vals;      // [n][B][K]
-    const float* hproj;     // [splits][n*B][3r]
-    int splits;
+    const uint16_t* shl;    // [n(B-1)][2r] pair state, bfloat16 hi | lo
     int n;
     int B;
     int K;
@@ -96,7 +101,6 @@ struct MlpArgs {
     const float* b1;
     const float* w2;
     float* part;            // [n*(B-1)][blocks][K][K] partial Delta per hidden-unit block
-    float* s_out;           // optional [n][B-1][r]
 };
 int mlp_blocks(int h);
 hipError_t launch_mlp(const MlpArgs& a, hipStream_t stream);

@@ -114,14 +114,20 @@ __global__ __launch_bounds__(256) void mlp_kernel(MlpArgs a) {
     const int tid = threadIdx.x;
     const int B = a.B, K = a.K, h = a.h;
     const int nj = (h + kJB - 1) / kJB;
-    const int item = blockIdx.x;
-    const int pair = item / nj, jblk = item % nj;
+    // Consecutive workgroup numbers go to different XCDs (round-robin over 8):
+    // the hidden blocks of one pair are numbered 8 apart so they share an
+    // XCD, and its L2 serves the pair's z rows after the first fetch.
+    const int lin = blockIdx.x;
+    const int xcd = lin % 8, i8 = lin / 8;
+    const int jblk = i8 % nj;
+    const int pair = (i8 / nj) * 8 + xcd;
+    if (pair >= a.n * (B - 1)) return;
+    const int item = pair * nj + jblk;
     const int j0 = jblk * kJB;
     const int jn = min(kJB, h - j0);
     const int req = pair / (B - 1), p = pair % (B - 1);
     const int64_t tp = static_cast<int64_t>(req) * B + p;  // slot rows of the pair
     const int64_t tq = tp + 1;
-    const int64_t nslots = static_cast<int64_t>(a.n) * B;
     constexpr int PS = kJB + 4;     // LDS row stride of P / Q (floats)
 
     __shared__ __attribute__((aligned(16))) uint16_t shv[2 * 128];  // s_p as bf16 hi | lo
@@ -131,17 +137,8 @@ __global__ __launch_bounds__(256) void mlp_kernel(MlpArgs a) {
     float* P = dyn;                 // [K][PS]
     float* Q = dyn + K * PS;        // [K][PS]
 
-    // ---- pair state s_p = W_pair,L h_p + W_pair,R h_{p+1}, logits, w2
-    for (int c = tid; c < R; c += 256) {
-        const int64_t sstride = nslots * (3 * R);
-        const float sl = sum_strided<kMaxSplits>(a.hproj + tp * (3 * R) + R + c, sstride, a.splits);
-        const float sr = sum_strided<kMaxSplits>(a.hproj + tq * (3 * R) + 2 * R + c, sstride, a.splits);
-        const float s = sl + sr;
-        const uint16_t hi = f32_to_bf16(s);
-        shv[c] = hi;
-        shv[R + c] = f32_to_bf16(s - bf16_to_f32(hi));
-        if (a.s_out && jblk == 0) a.s_out[static_cast<int64_t>(pair) * R + c] = s;
-    }
+    // ---- pair state (bf16 hi | lo, computed once per pair), logits, w2
+    for (int c = tid; c < 2 * R; c += 256) shv[c] = a.shl[static_cast<int64_t>(pair) * 2 * R + c];
     for (int m = tid; m < K; m += 256) {
         lp[m] = a.vals[tp * K + m];
         lq[m] = a.vals[tq * K + m];
@@ -189,7 +186,8 @@ __global__ __launch_bounds__(256) void mlp_kernel(MlpArgs a) {
 int mlp_blocks(int h) { return (h + kJB - 1) / kJB; }
 
 hipError_t launch_mlp(const MlpArgs& a, hipStream_t stream) {
-    const dim3 grid(static_cast<unsigned>(a.n * (a.B - 1) * mlp_blocks(a.h)));
+    const int pairs = a.n * (a.B - 1);
+    const dim3 grid(static_cast<unsigned>((pairs + 7) / 8 * 8 * mlp_blocks(a.h)));
     const size_t lds = static_cast<size_t>(2) * a.K * (kJB + 4) * sizeof(float);
     switch (a.r) {
         case 16: mlp_kernel<16><<<grid, 256, lds, stream>>>(a); break;

@@ -51,17 +51,23 @@ __device__ __forceinline__ const uint16_t* a_row(const GemmA& A, int64_t m) {
     }
 }
 
+// Workgroups are numbered so that consecutive numbers (which the dispatcher
+// spreads round-robin over the 8 XCDs) vary the split fastest: with a split
+// count dividing 8 every XCD works on one k-slice, and the k-slice of W and
+// of the A rows is fetched into that XCD's L2 only.
 __global__ __launch_bounds__(256) void gemm_kernel(GemmA A, GemmW W, int64_t M, int N, int kper, int kdim,
-                                                   float* __restrict__ C) {
+                                                   int splits, int ntn, float* __restrict__ C) {
     __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM * kLS];
     __shared__ __attribute__((aligned(16))) uint16_t Ws[2][kBN * kLS];
     const int tid = threadIdx.x;
     const int l = lane_id();
     const int wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int64_t m0 = static_cast<int64_t>(blockIdx.x) * kBM;
-    const int n0 = blockIdx.y * kBN;
-    const int split = blockIdx.z;
+    const int64_t lin = blockIdx.x;
+    const int split = static_cast<int>(lin % splits);
+    const int64_t rest = lin / splits;
+    const int n0 = static_cast<int>(rest % ntn) * kBN;
+    const int64_t m0 = (rest / ntn) * kBM;
     const int k_lo = split * kper;
     const int k_hi = min(kdim, k_lo + kper);
 
@@ -300,9 +306,23 @@ __global__ __launch_bounds__(256) void cand_kernel(CandArgs a) {
         row16_layernorm<R>(gv, a.eps);
 #pragma unroll
         for (int i = 0; i < VPL; ++i) gs[sl * R + c16 * VPL + i] = gv[i];
-        if (t * a.K >= n0) {  // the group holding the slot's first candidate writes g
+        if (t * a.K >= n0) {  // the group holding the slot's first candidate writes g ...
 #pragma unroll
             for (int i = 0; i < VPL; ++i) a.g[t * R + c16 * VPL + i] = gv[i];
+            // ... and the pair state of the pair starting at the slot
+            if (a.shl && (t % a.B) != a.B - 1) {
+                const int64_t pair = (t / a.B) * (a.B - 1) + t % a.B;
+                const float* ul = a.hproj + t * a.hstride + R + c16 * VPL;           // W_pair,L h_t
+                const float* vr = a.hproj + (t + 1) * a.hstride + 2 * R + c16 * VPL; // W_pair,R h_{t+1}
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) {
+                    const float sv = sum_strided<kMaxSplits>(ul + i, hs, a.splits) +
+                                     sum_strided<kMaxSplits>(vr + i, hs, a.splits);
+                    const int c = c16 * VPL + i;
+                    split_store(a.shl + pair * 2 * R, R, c, sv);
+                    a.s_out[pair * R + c] = sv;
+                }
+            }
         }
     }
     __syncthreads();
@@ -387,9 +407,9 @@ __global__ __launch_bounds__(256) void cand_kernel(CandArgs a) {
 hipError_t launch_gemm(const GemmA& A, const GemmW& W, int64_t M, int N, int kdim, int splits, float* C,
                        hipStream_t stream) {
     const int kper = ((kdim / 32 + splits - 1) / splits) * 32;
-    const dim3 grid(static_cast<unsigned>((M + kBM - 1) / kBM), static_cast<unsigned>((N + kBN - 1) / kBN),
-                    static_cast<unsigned>(splits));
-    gemm_kernel<<<grid, 256, 0, stream>>>(A, W, M, N, kper, kdim, C);
+    const int ntn = (N + kBN - 1) / kBN;
+    const int64_t blocks = ((M + kBM - 1) / kBM) * ntn * splits;
+    gemm_kernel<<<dim3(static_cast<unsigned>(blocks)), 256, 0, stream>>>(A, W, M, N, kper, kdim, splits, ntn, C);
     return hipGetLastError();
 }
 
