@@ -81,7 +81,7 @@ def algorithmic_work(cfg: dict, n: int) -> dict:
     return w
 
 
-def cpu_baseline(cfg, inputs, min_seconds: float = 10.0, max_passes: int = 8) -> dict:
+def cpu_baseline(cfg, inputs, min_seconds: float = 12.0, max_passes: int = 64) -> dict:
     import oracle
     oracle.build(force=False)
     threads = oracle.get_threads()

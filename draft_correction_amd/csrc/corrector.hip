@@ -12,6 +12,10 @@
 
 using namespace corr;
 
+namespace corr {
+thread_local LaunchTiming g_launch_timing;
+}
+
 namespace {
 
 constexpr uint32_t kMagic = 0xC0FFEE17u;
@@ -124,7 +128,9 @@ int check_hidden(const void* hidden, int64_t rs, int64_t ss) {
     return CORR_OK;
 }
 
-// Enqueues kernels, optionally bracketed by timing events.
+// Enqueues kernels.  With timing on, each step's launch carries a pair of
+// events that take the kernel's own start and end timestamps; a step that
+// launched nothing records the pair back to back.
 struct Seq {
     corrector* h;
     hipStream_t s;
@@ -134,10 +140,13 @@ struct Seq {
     void operator()(const char* name, F&& f) {
         if (err != hipSuccess) return;
         const bool t = h->timing && h->events_ready && k < kMaxKernels;
-        if (t) err = hipEventRecord(h->ev[2 * k], s);
-        if (err == hipSuccess) err = f();
+        if (t) g_launch_timing = LaunchTiming{h->ev[2 * k], h->ev[2 * k + 1], false};
+        err = f();
+        const bool used = g_launch_timing.used;
+        g_launch_timing = LaunchTiming{};
         if (t && err == hipSuccess) {
-            err = hipEventRecord(h->ev[2 * k + 1], s);
+            if (!used) err = hipEventRecord(h->ev[2 * k], s);
+            if (!used && err == hipSuccess) err = hipEventRecord(h->ev[2 * k + 1], s);
             h->names[k] = name;
         }
         ++k;

@@ -3,6 +3,7 @@
 // launch status; shapes have been validated by the caller.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -10,6 +11,26 @@
 #define CORR_DT_F32 1
 
 namespace corr {
+
+// Optional timing events for the next launch made on this thread.  The host
+// sequencer sets them around one step; launch() hands them to
+// hipExtLaunchKernel, which stamps them with the kernel's own start and end
+// times, and marks them used.
+struct LaunchTiming {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+    bool used = false;
+};
+extern thread_local LaunchTiming g_launch_timing;
+
+template <typename... P, typename... A>
+hipError_t launch(void (*kernel)(P...), dim3 grid, dim3 block, uint32_t lds, hipStream_t stream,
+                  A... args) {
+    LaunchTiming& t = g_launch_timing;
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, stream, t.start, t.stop, 0u, static_cast<P>(args)...);
+    if (t.start) t.used = true;
+    return hipGetLastError();
+}
 
 // Upper bounds of the split-K factors of the two projection GEMMs (the hidden-
 // state projections and the candidate projection); consumers sum that many

@@ -190,13 +190,12 @@ hipError_t launch_mlp(const MlpArgs& a, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>((pairs + 7) / 8 * 8 * mlp_blocks(a.h)));
     const size_t lds = static_cast<size_t>(2) * a.K * (kJB + 4) * sizeof(float);
     switch (a.r) {
-        case 16: mlp_kernel<16><<<grid, 256, lds, stream>>>(a); break;
-        case 32: mlp_kernel<32><<<grid, 256, lds, stream>>>(a); break;
-        case 64: mlp_kernel<64><<<grid, 256, lds, stream>>>(a); break;
-        case 128: mlp_kernel<128><<<grid, 256, lds, stream>>>(a); break;
+        case 16: return launch(mlp_kernel<16>, grid, 256, lds, stream, a);
+        case 32: return launch(mlp_kernel<32>, grid, 256, lds, stream, a);
+        case 64: return launch(mlp_kernel<64>, grid, 256, lds, stream, a);
+        case 128: return launch(mlp_kernel<128>, grid, 256, lds, stream, a);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 }  // namespace corr

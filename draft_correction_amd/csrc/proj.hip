@@ -409,8 +409,8 @@ hipError_t launch_gemm(const GemmA& A, const GemmW& W, int64_t M, int N, int kdi
     const int kper = ((kdim / 32 + splits - 1) / splits) * 32;
     const int ntn = (N + kBN - 1) / kBN;
     const int64_t blocks = ((M + kBM - 1) / kBM) * ntn * splits;
-    gemm_kernel<<<dim3(static_cast<unsigned>(blocks)), 256, 0, stream>>>(A, W, M, N, kper, kdim, splits, ntn, C);
-    return hipGetLastError();
+    return launch(gemm_kernel, dim3(static_cast<unsigned>(blocks)), 256, 0, stream, A, W, M, N, kper, kdim,
+                  splits, ntn, C);
 }
 
 size_t cand_lds_bytes(int r, int dvec, int K) {
@@ -423,13 +423,12 @@ hipError_t launch_cand(const CandArgs& a, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>((nodes + kCR - 1) / kCR));
     const size_t lds = cand_lds_bytes(a.r, a.vout ? a.dvec : 0, a.K);
     switch (a.r) {
-        case 16: cand_kernel<16><<<grid, 256, lds, stream>>>(a); break;
-        case 32: cand_kernel<32><<<grid, 256, lds, stream>>>(a); break;
-        case 64: cand_kernel<64><<<grid, 256, lds, stream>>>(a); break;
-        case 128: cand_kernel<128><<<grid, 256, lds, stream>>>(a); break;
+        case 16: return launch(cand_kernel<16>, grid, 256, lds, stream, a);
+        case 32: return launch(cand_kernel<32>, grid, 256, lds, stream, a);
+        case 64: return launch(cand_kernel<64>, grid, 256, lds, stream, a);
+        case 128: return launch(cand_kernel<128>, grid, 256, lds, stream, a);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 }  // namespace corr

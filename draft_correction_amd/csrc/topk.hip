@@ -456,19 +456,16 @@ hipError_t launch_topk_partial(int dtype, const void* logits, int64_t req_stride
     const int64_t waves = rows * chunks;
     const dim3 grid(static_cast<unsigned>((waves + 3) / 4));
     if (dtype == CORR_DT_BF16)
-        topk_partial_bf16_kernel<<<grid, 256, 0, stream>>>(static_cast<const uint16_t*>(logits), req_stride,
-                                                           slot_stride, B, V, K, chunks, rows, part);
-    else
-        topk_partial_f32_kernel<<<grid, 256, 0, stream>>>(static_cast<const float*>(logits), req_stride,
-                                                          slot_stride, B, V, K, chunks, rows, part);
-    return hipGetLastError();
+        return launch(topk_partial_bf16_kernel, grid, 256, 0, stream, static_cast<const uint16_t*>(logits),
+                      req_stride, slot_stride, B, V, K, chunks, rows, part);
+    return launch(topk_partial_f32_kernel, grid, 256, 0, stream, static_cast<const float*>(logits), req_stride,
+                  slot_stride, B, V, K, chunks, rows, part);
 }
 
 hipError_t launch_topk_merge(const uint64_t* part, int chunks, int K, int64_t rows, int32_t* ids,
                              float* vals, hipStream_t stream) {
-    topk_merge_kernel<<<dim3(static_cast<unsigned>((rows + 3) / 4)), 256, 0, stream>>>(part, chunks, K, rows,
-                                                                                   ids, vals);
-    return hipGetLastError();
+    return launch(topk_merge_kernel, dim3(static_cast<unsigned>((rows + 3) / 4)), 256, 0, stream, part, chunks,
+                  K, rows, ids, vals);
 }
 
 }  // namespace corr

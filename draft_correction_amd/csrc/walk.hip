@@ -151,8 +151,7 @@ unsigned grid_for(int64_t count) {
 }  // namespace
 
 hipError_t launch_cosine(const CosArgs& a, hipStream_t stream) {
-    cosine_kernel<<<dim3(static_cast<unsigned>(a.n * (a.B - 1))), 256, 0, stream>>>(a);
-    return hipGetLastError();
+    return launch(cosine_kernel, dim3(static_cast<unsigned>(a.n * (a.B - 1))), 256, 0, stream, a);
 }
 
 static size_t walk_lds_bytes(int B, int K) {
@@ -163,25 +162,22 @@ static size_t walk_lds_bytes(int B, int K) {
 hipError_t launch_walk(const float* scores, const int32_t* ids, int n, int B, int K,
                        int32_t* tokens, int32_t* choice, hipStream_t stream) {
     const size_t lds = walk_lds_bytes(B, K);
-    walk_kernel<<<dim3(static_cast<unsigned>(n)), 64, lds, stream>>>(scores, ids, n, B, K, tokens, choice,
-                                                                     lds > 0);
-    return hipGetLastError();
+    return launch(walk_kernel, dim3(static_cast<unsigned>(n)), 64, static_cast<uint32_t>(lds), stream, scores,
+                  ids, n, B, K, tokens, choice, lds > 0);
 }
 
 hipError_t launch_finish(const FinishArgs& a, hipStream_t stream) {
     const size_t lds = walk_lds_bytes(a.B, a.K);
-    finish_kernel<<<dim3(static_cast<unsigned>(a.n)), 256, lds, stream>>>(a, lds > 0);
-    return hipGetLastError();
+    return launch(finish_kernel, dim3(static_cast<unsigned>(a.n)), 256, static_cast<uint32_t>(lds), stream, a,
+                  lds > 0);
 }
 
 hipError_t launch_zhl_to_f32(const uint16_t* zhl, float* z, int64_t nodes, int r, hipStream_t stream) {
-    zhl_to_f32_kernel<<<grid_for(nodes * r), 256, 0, stream>>>(zhl, z, nodes, r);
-    return hipGetLastError();
+    return launch(zhl_to_f32_kernel, dim3(grid_for(nodes * r)), 256, 0, stream, zhl, z, nodes, r);
 }
 
 hipError_t launch_copy_f32(const float* src, float* dst, int64_t count, hipStream_t stream) {
-    copy_f32_kernel<<<grid_for(count), 256, 0, stream>>>(src, dst, count);
-    return hipGetLastError();
+    return launch(copy_f32_kernel, dim3(grid_for(count)), 256, 0, stream, src, dst, count);
 }
 
 }  // namespace corr
