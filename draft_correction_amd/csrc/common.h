@@ -57,9 +57,8 @@ __device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
 
 // Number of set bits of m in lanes below the calling lane.
 __device__ __forceinline__ int prefix_count(uint64_t m) {
-    const int l = lane_id();
-    const uint64_t below = (l == 0) ? 0ull : (~0ull >> (64 - l));
-    return __popcll(m & below);
+    return static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u)));
 }
 
 template <typename T>

@@ -307,6 +307,11 @@ int corrector_create(const corrector_desc* desc, const corrector_weights* wt, co
     if (d.d_embed < 32 || d.d_embed % 32 || d.d_embed > 65536) return CORR_E_SHAPE;
     if (d.r != 16 && d.r != 32 && d.r != 64 && d.r != 128) return CORR_E_UNSUPPORTED;
     if (d.max_requests < 1 || static_cast<int64_t>(d.max_requests) * d.slots > (1 << 24)) return CORR_E_SHAPE;
+    // chunk numbers of the top-K are 32-bit
+    if (static_cast<int64_t>(d.max_requests) * d.slots *
+            ((d.vocab + topk_chunk_elems(d.logits_dtype) - 1) / topk_chunk_elems(d.logits_dtype)) >
+        0x7FFFFFFF)
+        return CORR_E_SHAPE;
     if (!(d.ln_eps > 0.f) || !isfinite(d.ln_eps)) return CORR_E_SHAPE;
     if (d.variant == CORR_VARIANT_MLP) {
         if (d.mlp_hidden < 16 || d.mlp_hidden > 256 || d.mlp_hidden % 16) return CORR_E_UNSUPPORTED;

@@ -67,9 +67,9 @@ __device__ __forceinline__ uint32_t chunk_elem(const uint16_t* src, int nvalid, 
 
 // Exact top-`target` of a chunk by a bitwise search over the 32-bit composites
 // of every element, re-read from memory (used only when the threshold admits
-// too many elements, i.e. heavy ties).  Writes the winners unordered and
-// returns how many were written.
-__device__ __noinline__ int topk_bf16_exhaustive(const uint16_t* src, int nvalid, int64_t c0, int K,
+// too many elements, i.e. heavy ties).  Writes the winners unordered to the
+// wave's LDS output list and returns how many there are.
+__device__ __forceinline__ int topk_bf16_exhaustive(const uint16_t* src, int nvalid, int64_t c0, int K,
                                                  int target, uint64_t* out) {
     constexpr int kChunk = kNV * 8 * kWave;
     const int l = lane_id();
@@ -99,39 +99,37 @@ __device__ __noinline__ int topk_bf16_exhaustive(const uint16_t* src, int nvalid
     return outn;
 }
 
-__global__ __launch_bounds__(256) void topk_partial_bf16_kernel(
-    const uint16_t* __restrict__ logits, int64_t req_stride, int64_t slot_stride, int B, int64_t V,
-    int K, int chunks, int64_t rows, uint64_t* __restrict__ part) {
-    constexpr int kChunk = kNV * 8 * kWave;  // 8192 logits per wave
-    __shared__ u32x4 stage_all[4][kStage];
-    __shared__ uint16_t meta_all[4][kStage];
-    __shared__ uint32_t cand_all[4][kCand16];
-    const int wave = threadIdx.x >> 6;
-    const int l = lane_id();
-    const int64_t w = static_cast<int64_t>(blockIdx.x) * 4 + wave;
-    if (w >= rows * chunks) return;  // whole wave; this kernel has no block barrier
-    u32x4* stage = stage_all[wave];
-    uint16_t* meta = meta_all[wave];
-    uint32_t* cand = cand_all[wave];
-    const int64_t row = w / chunks;
-    const int chunk = static_cast<int>(w % chunks);
-    const int64_t req = row / B, slot = row % B;
-    const int64_t c0 = static_cast<int64_t>(chunk) * kChunk;
-    const uint16_t* src = logits + req * req_stride + slot * slot_stride + c0;
-    const int nvalid = static_cast<int>(min(static_cast<int64_t>(kChunk), V - c0));
+// One chunk of one drafted row: kNV * 512 consecutive logits (fewer at the
+// end of the row).  Chunk numbers are wave-uniform, so all of this is scalar.
+struct Chunk {
+    const uint16_t* src;
+    int nvalid;
+    uint32_t row, chunk;
+};
 
-    // ---- stream the chunk; padding elements get 0xFFFF (key 0: "no element")
-    u32x4 raw[kNV];
+// Issues the 16-byte loads of a full chunk into registers.
+__device__ __forceinline__ void load_full_chunk(u32x4 (&raw)[kNV], const uint16_t* src) {
+    const int l = lane_id();
+    const u32x4* p = reinterpret_cast<const u32x4*>(src);
+#pragma unroll
+    for (int t = 0; t < kNV; ++t) raw[t] = __builtin_nontemporal_load(p + t * kWave + l);
+}
+
+// Loads the last, shorter chunk of a row; elements past the end of the row
+// read as 0xFFFF (key 0: "no element").
+__device__ __forceinline__ void load_ragged_chunk(u32x4 (&raw)[kNV], const Chunk& c) {
+    const int l = lane_id();
+    const u32x4* src = reinterpret_cast<const u32x4*>(c.src);
 #pragma unroll
     for (int t = 0; t < kNV; ++t) {
         const int e0 = (t * kWave + l) * 8;
-        if (e0 + 8 <= nvalid) {
-            raw[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + t * kWave + l);
+        if (e0 + 8 <= c.nvalid) {
+            raw[t] = __builtin_nontemporal_load(src + t * kWave + l);
         } else {
             u32x4 v = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
             for (int j = 0; j < 8; ++j) {
-                if (e0 + j < nvalid) {
-                    const uint32_t b = src[e0 + j];
+                if (e0 + j < c.nvalid) {
+                    const uint32_t b = c.src[e0 + j];
                     const int q = j >> 1;
                     v[q] = (j & 1) ? ((v[q] & 0x0000FFFFu) | (b << 16)) : ((v[q] & 0xFFFF0000u) | b);
                 }
@@ -139,6 +137,48 @@ __global__ __launch_bounds__(256) void topk_partial_bf16_kernel(
             raw[t] = v;
         }
     }
+}
+
+// key16_of without branches: flip the magnitude bits of negatives and the
+// sign bit of non-negatives, then move -0 (0x7FFF after the flip) onto +0.
+__device__ __forceinline__ uint32_t key16_flip(uint32_t x) {
+    const uint32_t k = x ^ ((x & 0x8000u) ? 0xFFFFu : 0x8000u);
+    return k == 0x7FFFu ? 0x8000u : k;
+}
+
+// Bit t set when 16-byte vector t of this lane holds an element at or above
+// the threshold, tested on the packed maximum (positive threshold: signed
+// max against tpos) or packed minimum (otherwise: unsigned min against
+// uneg + 1) of the vector's four words.
+template <bool kPos>
+__device__ __forceinline__ uint32_t hit_mask(const u32x4 (&raw)[kNV], uint32_t bound2) {
+    uint32_t hm = 0;
+#pragma unroll
+    for (int t = 0; t < kNV; ++t) {
+        const u32x4& v = raw[t];
+        bool hit;
+        if (kPos) {
+            const uint32_t m = pk_max_i16(pk_max_i16(v[0], v[1]), pk_max_i16(v[2], v[3]));
+            hit = pk_max_i16(m, bound2) != bound2;
+        } else {
+            const uint32_t m = pk_min_u16(pk_min_u16(v[0], v[1]), pk_min_u16(v[2], v[3]));
+            hit = pk_min_u16(m, bound2) != bound2;
+        }
+        hm |= hit ? (1u << t) : 0u;
+    }
+    return hm;
+}
+
+// The exact top-K of one register-resident chunk, written to part[the chunk's
+// K slots] as merge composites (padded with 0 = "no element").  The LDS lists
+// have one trash slot per lane past their capacity, so every list write is
+// issued by every lane (no branches): lanes with nothing to add write there.
+__device__ __forceinline__ void select_chunk(const u32x4 (&raw)[kNV], const Chunk& c, int K, uint32_t chunks,
+                                             u32x4* stage, uint16_t* meta, uint32_t* cand, uint64_t* outb,
+                                             uint64_t* __restrict__ part) {
+    constexpr int kChunk = kNV * 8 * kWave;
+    const int l = lane_id();
+    const int64_t c0 = static_cast<int64_t>(c.chunk) * kChunk;
 
     // ---- lane maximum: signed max finds the largest positive, unsigned min the
     // negative closest to zero; together they give the largest value.
@@ -157,11 +197,11 @@ __global__ __launch_bounds__(256) void topk_partial_bf16_kernel(
 
     // ---- threshold: the target-th largest lane maximum (at least `target`
     // distinct elements are >= it, so the chunk's top-`target` are too)
-    const int target = min(K, nvalid);
+    const int target = min(K, c.nvalid);
     uint32_t thr = 0;
     for (int bit = 15; bit >= 0; --bit) {
-        const uint32_t c = thr | (1u << bit);
-        if (popc64(ballot(lane_key >= c)) >= target) thr = c;
+        const uint32_t cc = thr | (1u << bit);
+        if (popc64(ballot(lane_key >= cc)) >= target) thr = cc;
     }
     thr = max(thr, 1u);
     // Raw-domain form of "key16 >= thr": positives only (signed compare) when
@@ -170,85 +210,131 @@ __global__ __launch_bounds__(256) void topk_partial_bf16_kernel(
     const bool posmode = thr > 0x8000u;
     const uint32_t tpos = posmode ? thr - 0x8000u - 1u : 0u;                 // raw > tpos
     const uint32_t uneg = thr == 0x8000u ? 0x8000u : 0xFFFFu - thr;          // raw <= uneg
-    const uint32_t tpos2 = tpos | (tpos << 16);
-    const uint32_t uneg2 = (uneg + 1u) | ((uneg + 1u) << 16);
+    const uint32_t hm = posmode ? hit_mask<true>(raw, tpos | (tpos << 16))
+                                : hit_mask<false>(raw, (uneg + 1u) | ((uneg + 1u) << 16));
 
-    // ---- stage the vectors that hold at least one element >= threshold
-    int nst = 0;
+    // ---- slots of the hit vectors: exclusive prefix over lanes of the hit
+    // counts (at most kNV < 32: five bit planes), and their total
+    const uint32_t cnt = __popc(hm);
+    uint32_t base = 0, nst = 0;
 #pragma unroll
-    for (int t = 0; t < kNV; ++t) {
-        bool hit = false;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint32_t x = raw[t][q];
-            hit |= posmode ? (pk_max_i16(x, tpos2) != tpos2) : (pk_min_u16(x, uneg2) != uneg2);
-        }
-        const uint64_t m = ballot(hit);
-        if (m) {
-            const int pos = nst + prefix_count(m);
-            if (hit && pos < kStage) {
-                stage[pos] = raw[t];
-                meta[pos] = static_cast<uint16_t>(t * kWave + l);
-            }
-            nst += popc64(m);
-        }
+    for (int b = 0; b < 5; ++b) {
+        const uint64_t m = ballot((cnt >> b) & 1u);
+        base += static_cast<uint32_t>(prefix_count(m)) << b;
+        nst += static_cast<uint32_t>(popc64(m)) << b;
     }
-    wave_lds_sync();
 
-    const int64_t obase = (row * chunks + chunk) * K;
+    const int64_t obase = (static_cast<int64_t>(c.row) * chunks + c.chunk) * K;
     int outn = 0;
-    bool fast = nst <= kStage;
-    int nc = 0;
+    bool fast = nst <= static_cast<uint32_t>(kStage);
+    uint32_t nc = 0;
     if (fast) {
-        // elements of the staged vectors that pass, as 32-bit composites
-        u32x4 v = {0u, 0u, 0u, 0u};
+        // stage the hit vectors (and their local vector numbers)
+        uint32_t k = base;
+#pragma unroll
+        for (int t = 0; t < kNV; ++t) {
+            const uint32_t hit = (hm >> t) & 1u;
+            const uint32_t slot = hit ? k : kStage + l;
+            stage[slot] = raw[t];
+            meta[slot] = static_cast<uint16_t>(t * kWave + l);
+            k += hit;
+        }
+        wave_lds_sync();
+        // their elements that pass, as 32-bit composites (key16 << 16 |
+        // inverted local index); lanes past the staged count see padding
+        u32x4 v = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
         uint32_t vbase = 0;
-        if (l < nst) {
+        if (static_cast<uint32_t>(l) < nst) {
             v = stage[l];
             vbase = static_cast<uint32_t>(meta[l]) * 8u;
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const uint32_t x = (v[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-            const bool pass = l < nst && (posmode ? (static_cast<int>(static_cast<int16_t>(x)) > static_cast<int>(tpos))
-                                                 : (x <= uneg));
+            const uint32_t k16 = key16_flip((v[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+            const bool pass = k16 >= thr;
             const uint64_t m = ballot(pass);
-            const int pos = nc + prefix_count(m);
-            if (pass && pos < kCand16) cand[pos] = (key16_of(x) << 16) | (0xFFFFu - (vbase + j));
-            nc += popc64(m);
+            const uint32_t pos = nc + static_cast<uint32_t>(prefix_count(m));
+            cand[(pass && pos < static_cast<uint32_t>(kCand16)) ? pos : kCand16 + l] =
+                (k16 << 16) | (0xFFFFu - (vbase + j));
+            nc += static_cast<uint32_t>(popc64(m));
         }
-        fast = nc <= kCand16;
+        fast = nc <= static_cast<uint32_t>(kCand16);
     }
     if (fast) {
         wave_lds_sync();
         uint32_t e[kCand16 / kWave];
 #pragma unroll
-        for (int q = 0; q < kCand16 / kWave; ++q) e[q] = q * kWave + l < nc ? cand[q * kWave + l] : 0u;
+        for (int q = 0; q < kCand16 / kWave; ++q)
+            e[q] = static_cast<uint32_t>(q * kWave + l) < nc ? cand[q * kWave + l] : 0u;
         uint32_t tc = 0;
         for (int bit = 31; bit >= 0; --bit) {
-            const uint32_t c = tc | (1u << bit);
-            int cnt = 0;
+            const uint32_t cc = tc | (1u << bit);
+            int cnt2 = 0;
 #pragma unroll
             for (int q = 0; q < kCand16 / kWave; ++q)
-                if (q * kWave < nc) cnt += popc64(ballot(e[q] >= c));
-            if (cnt >= target) tc = c;
+                if (static_cast<uint32_t>(q * kWave) < nc) cnt2 += popc64(ballot(e[q] >= cc));
+            if (cnt2 >= target) tc = cc;
         }
 #pragma unroll
         for (int q = 0; q < kCand16 / kWave; ++q) {
+            if (static_cast<uint32_t>(q * kWave) >= nc) break;
             const bool p = e[q] >= tc && e[q] != 0u;
             const uint64_t m = ballot(p);
             const int pos = outn + prefix_count(m);
             if (p && pos < K) {
                 const uint32_t raw16 = raw16_of_key16(e[q] >> 16);
-                part[obase + pos] = merge_comp(key_of_bits(raw16 << 16), c0 + (0xFFFFu - (e[q] & 0xFFFFu)));
+                outb[pos] = merge_comp(key_of_bits(raw16 << 16), c0 + (0xFFFFu - (e[q] & 0xFFFFu)));
             }
             outn += popc64(m);
         }
     } else {
-        outn = topk_bf16_exhaustive(src, nvalid, c0, K, target, part + obase);
+        outn = topk_bf16_exhaustive(c.src, c.nvalid, c0, K, target, outb);
     }
-    // chunks with fewer than K elements pad with "no element"
-    for (int pos = outn + l; pos < K; pos += kWave) part[obase + pos] = 0ull;
+    // One store instruction per chunk: lane l writes slot min(l, K-1) (lanes
+    // past K-1 repeat that slot's value); chunks with fewer than K elements
+    // pad with 0 ("no element").
+    wave_lds_sync();
+    const int slot = min(l, K - 1);
+    part[obase + slot] = slot < outn ? outb[slot] : 0ull;
+}
+
+// One wave per chunk.  The full chunks (all but a row's shorter last one) are
+// numbered f = row * full + chunk and come first; the rows' shorter last
+// chunks follow.  Each chunk's result slot is fixed by its (row, chunk).
+__global__ __launch_bounds__(256) void topk_partial_bf16_kernel(
+    const uint16_t* __restrict__ logits, int64_t req_stride, int64_t slot_stride, int B, int64_t V,
+    int K, int chunks, int64_t rows, uint64_t* __restrict__ part) {
+    constexpr int kChunk = kNV * 8 * kWave;
+    __shared__ u32x4 stage_all[4][kStage + kWave];
+    __shared__ uint16_t meta_all[4][kStage + kWave];
+    __shared__ uint32_t cand_all[4][kCand16 + kWave];
+    __shared__ uint64_t out_all[4][kWave];
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t w = blockIdx.x * 4u + wave;
+    const uint32_t uB = static_cast<uint32_t>(B), uch = static_cast<uint32_t>(chunks);
+    const uint32_t nrows = static_cast<uint32_t>(rows);
+    const bool ragged = V % kChunk != 0;
+    const uint32_t full = ragged ? uch - 1u : uch;  // full chunks per row
+    const uint32_t nfull = nrows * full;
+    if (w >= nrows * uch) return;  // whole wave; this kernel has no block barrier
+    Chunk c;
+    if (w < nfull) {
+        c.row = w / full;
+        c.chunk = w - c.row * full;
+    } else {
+        c.row = w - nfull;
+        c.chunk = uch - 1u;
+    }
+    const uint32_t req = c.row / uB, slot = c.row - req * uB;
+    const int64_t c0 = static_cast<int64_t>(c.chunk) * kChunk;
+    c.src = logits + req * req_stride + slot * slot_stride + c0;
+    c.nvalid = static_cast<int>(min(static_cast<int64_t>(kChunk), V - c0));
+    u32x4 raw[kNV];
+    if (w < nfull)
+        load_full_chunk(raw, c.src);
+    else
+        load_ragged_chunk(raw, c);
+    select_chunk(raw, c, K, uch, stage_all[wave], meta_all[wave], cand_all[wave], out_all[wave], part);
 }
 
 // ---------------------------------------------------------- float32 path --
