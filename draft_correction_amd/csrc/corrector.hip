@@ -4,6 +4,8 @@
 // never allocates device memory and never synchronises (except
 // corrector_kernel_times, which waits for timing events by design).
 #include <math.h>
+#include <functional>
+#include <mutex>
 #include <new>
 #include <string.h>
 
@@ -40,6 +42,14 @@ struct corrector {
     const char* names[kMaxKernels];
     int nk;
     const float* table;  // folded E W_cand^T [V][r], or null
+    // Side stream for the hidden-state projection, which does not depend on
+    // the top-K: it is forked from the call's stream and joined back before
+    // the candidate kernel.  Created at first use; `mu` makes each call's
+    // record/wait pairs on the shared events atomic.
+    std::mutex mu;
+    bool side_ready;
+    hipStream_t side;
+    hipEvent_t fork_ev, join_ev;
 };
 
 namespace {
@@ -151,11 +161,40 @@ struct Seq {
         }
         ++k;
     }
+    void record(hipEvent_t e, hipStream_t st) {
+        if (err == hipSuccess) err = hipEventRecord(e, st);
+    }
+    void wait(hipEvent_t e, hipStream_t st) {
+        if (err == hipSuccess) err = hipStreamWaitEvent(st, e, 0);
+    }
     int finish() {
         if (h->timing) h->nk = k < kMaxKernels ? k : kMaxKernels;
         return err == hipSuccess ? CORR_OK : CORR_E_HIP;
     }
 };
+
+// Creates the side stream and its fork/join events on first use (the caller
+// holds h->mu).  Default priority, non-blocking with respect to the NULL
+// stream.  Both streams run on one device, so the events need no system-scope
+// fence.
+hipError_t ensure_side(corrector* h) {
+    if (h->side_ready) return hipSuccess;
+    hipError_t e = hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking);
+    if (e != hipSuccess) return e;
+    e = hipEventCreateWithFlags(&h->fork_ev, hipEventDisableTiming | hipEventDisableSystemFence);
+    if (e != hipSuccess) {
+        (void)hipStreamDestroy(h->side);
+        return e;
+    }
+    e = hipEventCreateWithFlags(&h->join_ev, hipEventDisableTiming | hipEventDisableSystemFence);
+    if (e != hipSuccess) {
+        (void)hipEventDestroy(h->fork_ev);
+        (void)hipStreamDestroy(h->side);
+        return e;
+    }
+    h->side_ready = true;
+    return hipSuccess;
+}
 
 void enqueue_topk(Seq& q, const corrector* h, const Layout& L, int32_t n, const void* logits,
                   int64_t rs, int64_t ss, int32_t* ids, float* vals, void* ws) {
@@ -166,14 +205,17 @@ void enqueue_topk(Seq& q, const corrector* h, const Layout& L, int32_t n, const 
         return launch_topk_partial(d.logits_dtype, logits, rs, ss, d.slots, d.vocab, d.k, L.chunks,
                                    rows, part, q.s);
     });
-    q("topk_merge", [&] { return launch_topk_merge(part, L.chunks, d.k, rows, ids, vals, q.s); });
+    q("topk_merge", [&] { return launch_topk_merge(d.logits_dtype, part, L.chunks, d.k, rows, ids, vals, q.s); });
 }
 
 // Steps (2)-(4); with tokens given also step (5) (fused into the MLP finish
 // for the MLP variant, a walk launch for the cosine variant).
+// `pre` (optional) enqueues work on the call's stream between the fork of the
+// hidden-state projection and the candidate projection (corrector_run puts
+// the top-K there).  The caller holds h->mu and has made the side stream.
 void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const int32_t* ids,
                    const float* vals, const void* hidden, int64_t hrs, int64_t hss, float* scores,
-                   void* ws, int32_t* tokens, int32_t* choice) {
+                   void* ws, int32_t* tokens, int32_t* choice, const std::function<void()>& pre) {
     const corrector_desc& d = h->d;
     const corrector_weights& w = h->w;
     const int64_t rows = static_cast<int64_t>(n) * d.slots;
@@ -196,8 +238,17 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
     }
     // hproj rows: [W_ctx h | W_pair,L h | W_pair,R h] (3r wide); the cosine
     // variant has no pair state and computes the W_ctx block alone (r wide).
+    // It runs on the side stream, overlapping whatever the call's stream
+    // runs until the join before the candidate kernel.
     const int hn = cos ? d.r : 3 * d.r;
+    const hipStream_t main = q.s;
+    q.record(h->fork_ev, main);
+    q.wait(h->fork_ev, h->side);
+    q.s = h->side;
     q("hproj", [&] { return launch_gemm(ha, hw, rows, hn, d.d_hidden, L.splits, hproj, q.s); });
+    q.record(h->join_ev, h->side);
+    q.s = main;
+    if (pre) pre();
     float* upart = at<float>(ws, L.upart);
     if (!h->table) {
     GemmA ua{};
@@ -240,6 +291,7 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
         ca.vout = at<float>(ws, L.vout);
         ca.vin = at<float>(ws, L.vin);
     }
+    q.wait(h->join_ev, main);
     q("cand", [&] { return launch_cand(ca, q.s); });
     if (d.slots < 2) {
         if (tokens) q("walk", [&] { return launch_walk(scores, ids, n, d.slots, d.k, tokens, choice, q.s); });
@@ -344,6 +396,7 @@ int corrector_create(const corrector_desc* desc, const corrector_weights* wt, co
     h->events_ready = false;
     h->nk = 0;
     h->table = nullptr;
+    h->side_ready = false;
     *out = h;
     return CORR_OK;
 }
@@ -352,6 +405,11 @@ void corrector_destroy(corrector* h) {
     if (!live(h)) return;
     if (h->events_ready)
         for (hipEvent_t& e : h->ev) (void)hipEventDestroy(e);
+    if (h->side_ready) {
+        (void)hipEventDestroy(h->fork_ev);
+        (void)hipEventDestroy(h->join_ev);
+        (void)hipStreamDestroy(h->side);
+    }
     h->magic = kDead;
     delete h;
 }
@@ -386,8 +444,10 @@ int corrector_score(const corrector* hc, int32_t n, const int32_t* ids, const fl
     if ((rc = check_ws(hc, n, ws, ws_bytes))) return rc;
     corrector* h = const_cast<corrector*>(hc);
     const Layout L = layout(h->d, n);
+    std::lock_guard<std::mutex> lock(h->mu);
+    if (ensure_side(h) != hipSuccess) return CORR_E_HIP;
     Seq q{h, static_cast<hipStream_t>(stream)};
-    enqueue_score(q, h, L, n, ids, vals, hidden, hrs, hss, scores, ws, nullptr, nullptr);
+    enqueue_score(q, h, L, n, ids, vals, hidden, hrs, hss, scores, ws, nullptr, nullptr, nullptr);
     return q.finish();
 }
 
@@ -417,9 +477,11 @@ int corrector_run(const corrector* hc, int32_t n, const void* logits, int64_t lr
     int32_t* ids = ids_or_null ? ids_or_null : at<int32_t>(ws, L.ids);
     float* vals = vals_or_null ? vals_or_null : at<float>(ws, L.vals);
     float* scores = scores_or_null ? scores_or_null : at<float>(ws, L.scores);
+    std::lock_guard<std::mutex> lock(h->mu);
+    if (ensure_side(h) != hipSuccess) return CORR_E_HIP;
     Seq q{h, static_cast<hipStream_t>(stream)};
-    enqueue_topk(q, h, L, n, logits, lrs, lss, ids, vals, ws);
-    enqueue_score(q, h, L, n, ids, vals, hidden, hrs, hss, scores, ws, tokens, choice_or_null);
+    enqueue_score(q, h, L, n, ids, vals, hidden, hrs, hss, scores, ws, tokens, choice_or_null,
+                  [&] { enqueue_topk(q, h, L, n, logits, lrs, lss, ids, vals, ws); });
     return q.finish();
 }
 

@@ -45,7 +45,7 @@ int topk_chunk_elems(int dtype);
 hipError_t launch_topk_partial(int dtype, const void* logits, int64_t req_stride,
                                int64_t slot_stride, int B, int64_t V, int K, int chunks,
                                int64_t rows, uint64_t* part, hipStream_t stream);
-hipError_t launch_topk_merge(const uint64_t* part, int chunks, int K, int64_t rows, int32_t* ids,
+hipError_t launch_topk_merge(int dtype, const uint64_t* part, int chunks, int K, int64_t rows, int32_t* ids,
                              float* vals, hipStream_t stream);
 
 // ---- projections (proj.hip)

@@ -520,16 +520,103 @@ __device__ void merge_row_wave(const uint64_t* __restrict__ ent, int M, int K, u
     }
 }
 
+// Fast path of the merge for rows of at most kMergePer * 64 candidates, held in
+// registers.  Value keys are compared on their top `kbits` bits: for bf16
+// logits the rest of the float32-order key is fixed by those bits, so the
+// searches are exact with kbits = 16.  Steps: threshold T0 = K-th largest lane
+// maximum; the entries at or above it (at least K) are compacted; T = K-th
+// largest value key among them; the winners are the entries above T plus,
+// among those equal to T, the ones with the largest composites (smallest
+// ids).  Returns false, having written nothing, when more than kMergeCap
+// entries reach T0; the general search then takes over.
+constexpr int kMergePer = 8;
+
+__device__ __forceinline__ bool merge_row_fast(const uint64_t* __restrict__ ent, int M, int K, int kbits,
+                                               uint64_t* sel, uint64_t* fin, int32_t* __restrict__ ids,
+                                               float* __restrict__ vals) {
+    const int l = lane_id();
+    const int lowbit = 32 - kbits;
+    uint64_t e[kMergePer];
+    uint32_t lane_hi = 0;
+#pragma unroll
+    for (int q = 0; q < kMergePer; ++q) {
+        const int i = q * kWave + l;
+        e[q] = i < M ? ent[i] : 0ull;
+        lane_hi = max(lane_hi, static_cast<uint32_t>(e[q] >> 32));
+    }
+    uint32_t t0 = 0;
+    for (int bit = 31; bit >= lowbit; --bit) {
+        const uint32_t c = t0 | (1u << bit);
+        if (popc64(ballot(lane_hi >= c)) >= K) t0 = c;
+    }
+    int n = 0;
+#pragma unroll
+    for (int q = 0; q < kMergePer; ++q) {
+        if (q * kWave >= M) break;
+        const bool p = e[q] != 0ull && static_cast<uint32_t>(e[q] >> 32) >= t0;
+        const uint64_t m = ballot(p);
+        const int pos = n + prefix_count(m);
+        sel[(p && pos < kMergeCap) ? pos : kMergeCap + l] = e[q];
+        n += popc64(m);
+    }
+    if (n > kMergeCap) return false;
+    wave_lds_sync();
+    const uint64_t a0 = l < n ? sel[l] : 0ull;
+    const uint64_t a1 = l + kWave < n ? sel[l + kWave] : 0ull;
+    const uint32_t h0 = static_cast<uint32_t>(a0 >> 32), h1 = static_cast<uint32_t>(a1 >> 32);
+    uint32_t T = 0;
+    for (int bit = 31; bit >= lowbit; --bit) {
+        const uint32_t c = T | (1u << bit);
+        if (popc64(ballot(h0 >= c)) + popc64(ballot(h1 >= c)) >= K) T = c;
+    }
+    const uint32_t tt = T >> lowbit;
+    const bool up0 = a0 != 0ull && (h0 >> lowbit) > tt, up1 = a1 != 0ull && (h1 >> lowbit) > tt;
+    const bool eq0 = a0 != 0ull && (h0 >> lowbit) == tt, eq1 = a1 != 0ull && (h1 >> lowbit) == tt;
+    const int need = K - popc64(ballot(up0)) - popc64(ballot(up1));
+    // among the entries equal to T, the `need` largest low words (inverted ids)
+    uint32_t L = 0;
+    if (popc64(ballot(eq0)) + popc64(ballot(eq1)) > need) {
+        const uint32_t w0 = static_cast<uint32_t>(a0), w1 = static_cast<uint32_t>(a1);
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t c = L | (1u << bit);
+            if (popc64(ballot(eq0 && w0 >= c)) + popc64(ballot(eq1 && w1 >= c)) >= need) L = c;
+        }
+    }
+    const bool win0 = up0 || (eq0 && static_cast<uint32_t>(a0) >= L);
+    const bool win1 = up1 || (eq1 && static_cast<uint32_t>(a1) >= L);
+    const uint64_t m0 = ballot(win0);
+    const int p0 = prefix_count(m0), c0 = popc64(m0);
+    fin[(win0 && p0 < kWave) ? p0 : kWave + l] = a0;
+    const uint64_t m1 = ballot(win1);
+    const int p1 = c0 + prefix_count(m1);
+    fin[(win1 && p1 < kWave) ? p1 : kWave + l] = a1;
+    wave_lds_sync();
+    // exactly K distinct composites won; order them by rank
+    if (l < K) {
+        const uint64_t me = fin[l];
+        int rank = 0;
+        for (int m2 = 0; m2 < K; ++m2) rank += fin[m2] > me ? 1 : 0;
+        ids[rank] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(me & 0xFFFFFFFFu));
+        vals[rank] = __uint_as_float(bits_of_key(static_cast<uint32_t>(me >> 32)));
+    }
+    return true;
+}
+
 __global__ __launch_bounds__(256) void topk_merge_kernel(const uint64_t* __restrict__ part, int chunks,
-                                                         int K, int64_t rows, int32_t* __restrict__ ids,
-                                                         float* __restrict__ vals) {
-    __shared__ uint64_t sel_all[4][kMergeCap];
-    __shared__ uint64_t fin_all[4][64];
-    const int wave = threadIdx.x >> 6;
+                                                         int K, int kbits, int64_t rows,
+                                                         int32_t* __restrict__ ids, float* __restrict__ vals) {
+    __shared__ uint64_t sel_all[4][kMergeCap + kWave];
+    __shared__ uint64_t fin_all[4][2 * kWave];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + wave;
     if (row >= rows) return;
     const int M = chunks * K;
-    merge_row_wave(part + row * M, M, K, sel_all[wave], fin_all[wave], ids + row * K, vals + row * K);
+    const uint64_t* ent = part + row * M;
+    if (M <= kMergePer * kWave &&
+        merge_row_fast(ent, M, K, kbits, sel_all[wave], fin_all[wave], ids + row * K, vals + row * K))
+        return;
+    wave_lds_sync();
+    merge_row_wave(ent, M, K, sel_all[wave], fin_all[wave], ids + row * K, vals + row * K);
 }
 
 }  // namespace
@@ -548,10 +635,11 @@ hipError_t launch_topk_partial(int dtype, const void* logits, int64_t req_stride
                   slot_stride, B, V, K, chunks, rows, part);
 }
 
-hipError_t launch_topk_merge(const uint64_t* part, int chunks, int K, int64_t rows, int32_t* ids,
+hipError_t launch_topk_merge(int dtype, const uint64_t* part, int chunks, int K, int64_t rows, int32_t* ids,
                              float* vals, hipStream_t stream) {
+    const int kbits = dtype == CORR_DT_BF16 ? 16 : 32;
     return launch(topk_merge_kernel, dim3(static_cast<unsigned>((rows + 3) / 4)), 256, 0, stream, part, chunks,
-                  K, rows, ids, vals);
+                  K, kbits, rows, ids, vals);
 }
 
 }  // namespace corr
