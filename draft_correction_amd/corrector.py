@@ -195,7 +195,7 @@ class Corrector:
         _ok("corrector_set_timing", self.lib.corrector_set_timing(self.h, 1 if enabled else 0))
 
     def kernel_times(self):
-        cap = 8
+        cap = 12
         ms = (C.c_float * cap)()
         names = (C.c_char_p * cap)()
         k = self.lib.corrector_kernel_times(self.h, ms, names, cap)

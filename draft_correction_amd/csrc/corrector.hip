@@ -22,11 +22,11 @@ namespace {
 
 constexpr uint32_t kMagic = 0xC0FFEE17u;
 constexpr uint32_t kDead = 0xDEADDEADu;
-constexpr int kMaxKernels = 8;
+constexpr int kMaxKernels = 12;
 constexpr size_t kAlign = 256;
 
 struct Layout {
-    size_t part, ids, vals, hproj, upart, z, g, s, shl, vout, vin, mlp_part, scores, total;
+    size_t part, ids, vals, hproj, upart, z, g, s, shl, uv, cp, vout, vin, mlp_part, scores, total;
     int chunks, splits, usplits;
 };
 
@@ -94,7 +94,10 @@ Layout layout(const corrector_desc& d, int32_t n) {
     L.g = take(sizeof(float) * rows * d.r);
     L.s = take(sizeof(float) * pairs * d.r);
     L.shl = take(sizeof(uint16_t) * pairs * 2 * d.r);
-    L.mlp_part = take(d.variant == CORR_VARIANT_MLP ? sizeof(float) * pairs * mlp_blocks(d.mlp_hidden) * d.k * d.k : 0);
+    const bool mlp = d.variant == CORR_VARIANT_MLP;
+    L.uv = take(mlp ? sizeof(float) * rows * d.k * 2 * d.mlp_hidden : 0);
+    L.cp = take(mlp ? sizeof(float) * pairs * d.mlp_hidden : 0);
+    L.mlp_part = take(mlp ? sizeof(float) * pairs * mlp_blocks(d.mlp_hidden) * d.k * d.k : 0);
     const bool cos = d.variant == CORR_VARIANT_COSINE;
     L.vout = take(cos ? sizeof(float) * rows * d.k * d.d_vec : 0);
     L.vin = take(cos ? sizeof(float) * rows * d.k * d.d_vec : 0);
@@ -311,10 +314,42 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
         q("cosine", [&] { return launch_cosine(c, q.s); });
         if (tokens) q("walk", [&] { return launch_walk(scores, ids, n, d.slots, d.k, tokens, choice, q.s); });
     } else {
+        // U | V = [W1_za; W1_zb] z per candidate and c_p = W1_s s_p per pair,
+        // both over bf16 hi | lo rows (the W1 column block wraps at r)
+        const int nin = 3 * d.r + 2;
+        const uint16_t* w1 = static_cast<const uint16_t*>(w.w1);
+        GemmJob uvj{};
+        uvj.A.mode = GEMM_A_DENSE;
+        uvj.A.base = ca.zhl;
+        uvj.A.lda = 2 * d.r;
+        uvj.W.base[0] = w1 + d.r;
+        uvj.W.base[1] = w1 + 2 * d.r;
+        uvj.W.ld[0] = uvj.W.ld[1] = nin;
+        uvj.W.nb = d.mlp_hidden;
+        uvj.W.kwrap = d.r;
+        uvj.M = rows * d.k;
+        uvj.N = 2 * d.mlp_hidden;
+        uvj.kdim = 2 * d.r;
+        uvj.splits = 1;
+        uvj.C = at<float>(ws, L.uv);
+        GemmJob cpj{};
+        cpj.A.mode = GEMM_A_DENSE;
+        cpj.A.base = ca.shl;
+        cpj.A.lda = 2 * d.r;
+        cpj.W.base[0] = w1;
+        cpj.W.ld[0] = nin;
+        cpj.W.nb = d.mlp_hidden;
+        cpj.W.kwrap = d.r;
+        cpj.M = static_cast<int64_t>(n) * (d.slots - 1);
+        cpj.N = d.mlp_hidden;
+        cpj.kdim = 2 * d.r;
+        cpj.splits = 1;
+        cpj.C = at<float>(ws, L.cp);
+        q("uv_gemm", [&] { return launch_gemm2(uvj, cpj, q.s); });
         MlpArgs m{};
-        m.zhl = ca.zhl;
+        m.uv = uvj.C;
+        m.cp = cpj.C;
         m.vals = vals;
-        m.shl = ca.shl;
         m.n = n;
         m.B = d.slots;
         m.K = d.k;

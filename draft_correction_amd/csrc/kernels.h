@@ -66,9 +66,22 @@ struct GemmW {
     const uint16_t* base[3];  // row n is base[n / nb] + (n % nb) * ld[n / nb]
     int64_t ld[3];
     int nb;
+    int kwrap;                // > 0 (a power of two): column k of W is column k % kwrap, so an
+                              // A row [hi | lo] of 2 * kwrap meets the same W columns twice
+};
+// One GEMM problem; two can share a launch (their workgroups side by side).
+struct GemmJob {
+    GemmA A;
+    GemmW W;
+    int64_t M;
+    int N;
+    int kdim;
+    int splits;
+    float* C;
 };
 hipError_t launch_gemm(const GemmA& A, const GemmW& W, int64_t M, int N, int kdim, int splits, float* C,
                        hipStream_t stream);
+hipError_t launch_gemm2(const GemmJob& j0, const GemmJob& j1, hipStream_t stream);
 
 // Per drafted slot: b = LN(u) with u = W_cand E[ids], g = LN(W_ctx h) from hproj,
 // z = gamma * LN(W_fuse [b; g]) + beta stored as bfloat16 hi/lo halves
@@ -110,9 +123,9 @@ hipError_t launch_cand(const CandArgs& a, hipStream_t stream);
 
 // ---- transition scores (mlp.hip, cosine.hip)
 struct MlpArgs {
-    const uint16_t* zhl;    // [n][B][K][2r] bfloat16 hi | lo
+    const float* uv;        // [n][B][K][2h]: W1_za z | W1_zb z per candidate
+    const float* cp;        // [n(B-1)][h]: W1_s s_p per pair
     const float* vals;      // [n][B][K]
-    const uint16_t* shl;    // [n(B-1)][2r] pair state, bfloat16 hi | lo
     int n;
     int B;
     int K;

@@ -5,18 +5,19 @@
 // Layer 1 is evaluated through the exact column-block identity
 //   W1 x = (W1_s s_p + b1 + W1_za z_p^a + w_la l_p(a)) + (W1_zb z_{p+1}^b + w_lb l_{p+1}(b))
 //        =              P_p[a]                        +            Q_p[b]
-// so the K^2 x (3r+2) x h product collapses to two K x 2r x h MFMA products
-// per pair plus a K x K broadcast add; the pair state s_p enters once per
-// pair through c_p = W1_s s_p + b1 (one more MFMA row).  The MFMA inputs are z split into bf16
-// hi + lo parts (z = hi + lo to ~2^-16), against the same W1 columns twice, so
-// P and Q carry float32 accuracy.  The epilogue is the GELU over all K^2 x h
-// pre-activations and the h -> 1 dot with w2, one (a, b) per thread.
+// so the K^2 x (3r+2) x h product collapses to per-candidate products
+// U = W1_za z and V = W1_zb z (each candidate's z meets the weights once,
+// whichever pairs it belongs to), the per-pair c_p = W1_s s_p, and a K x K
+// broadcast add.  U | V and c_p come from one two-problem MFMA GEMM launch
+// (the projection GEMM, with z and s_p as bf16 hi | lo rows meeting the same
+// W1 columns twice, so they carry float32 accuracy).  This kernel forms P and
+// Q and runs the epilogue: the GELU over all K^2 x h pre-activations and the
+// h -> 1 dot with w2, one (a, b) per thread.
 //
-// Work is split into (pair, block of 64 hidden units) workgroups, so a pass
-// has (B-1) * n * h/64 of them to balance over the CUs and each block's W1
-// columns are read once per pair.  Each block writes its partial Delta; the
-// finishing kernel adds the blocks in order, adds b2 and l_{p+1}(b) and walks.
-// Every sum runs in a fixed order with no atomics: bit-reproducible.
+// Work is split into (pair, block of 64 hidden units) workgroups; each block
+// writes its partial Delta and the finishing kernel adds the blocks in order,
+// adds b2 and l_{p+1}(b) and walks.  Every sum runs in a fixed order with no
+// atomics: bit-reproducible.
 #include "common.h"
 #include "kernels.h"
 
@@ -43,80 +44,19 @@ __device__ __forceinline__ float gelu(float x) {
 // Hidden units handled by one workgroup (a multiple of 16 and of 8).
 constexpr int kJB = 64;
 
-// One 16-column tile of P (which = 0) or Q (which = 1) for hidden units
-// j0 .. j0+15: rows are the K candidates of the slot, computed on MFMA from
-// z hi | lo; P also carries c_p = W1_s s_p + b1, itself one MFMA row over
-// s_p hi | lo (shv).  Written to P/Q in LDS.
-template <int R>
-__device__ __forceinline__ void pq_tile(const MlpArgs& a, int which, int j0, int64_t zrow0, int K,
-                                        const uint16_t* shv, const float* lp, const float* lq, float* dst,
-                                        int dcol, int PS) {
-    constexpr int KS = 2 * R / 32;
-    const int nin = 3 * R + 2;
-    const int l = lane_id();
-    const int kq = 8 * (l >> 4);
-    const int j = j0 + (l & 15);
-    const uint32_t* wz = reinterpret_cast<const uint32_t*>(a.w1 + static_cast<int64_t>(j) * nin + (which ? 2 * R : R));
-    const uint32_t* ws = reinterpret_cast<const uint32_t*>(a.w1 + static_cast<int64_t>(j) * nin);
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    u32x4 bz[KS], bs[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        const int o = ((ks * 32 + kq) % R) / 2;   // same W1 columns for hi and lo
-        bz[ks] = u32x4{wz[o], wz[o + 1], wz[o + 2], wz[o + 3]};
-        bs[ks] = which ? zero : u32x4{ws[o], ws[o + 1], ws[o + 2], ws[o + 3]};
-    }
-    const float wl = bf16_to_f32(a.w1[static_cast<int64_t>(j) * nin + 3 * R + which]);
-    const float b1j = which ? 0.f : a.b1[j];
-    const int nrt = (K + 15) / 16;
-    // z fragments of a row tile (rows past K read row 0 and are zeroed)
-    auto zfrag = [&](int rt, u32x4* af) {
-        const int m = rt * 16 + (l & 15);
-        const uint16_t* zr = a.zhl + (zrow0 + (m < K ? m : 0)) * (2 * R);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const u32x4 v = load16(zr + ks * 32 + kq);
-            af[ks] = m < K ? v : zero;
-        }
-    };
-    u32x4 af[KS];
-    zfrag(0, af);  // issued with the weight loads above, before any MFMA
-    float cj = 0.f;
-    if (!which) {
-        // c_p tile: A row 0 = [s_hi | s_lo], other rows zero
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const u32x4 av = (l & 15) == 0 ? *reinterpret_cast<const u32x4*>(shv + ks * 32 + kq) : zero;
-            acc = mfma16x16x32(av, bs[ks], acc);
-        }
-        cj = __shfl(acc[0], l & 15, kWave) + b1j;   // D[0][col] lives in lanes 0..15
-    }
-    for (int rt = 0; rt < nrt; ++rt) {
-        if (rt > 0) zfrag(rt, af);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(af[ks], bz[ks], acc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int mm = rt * 16 + 4 * (l >> 4) + i;
-            if (mm < K) dst[mm * PS + dcol + (l & 15)] = acc[i] + fmaf(wl, which ? lq[mm] : lp[mm], cj);
-        }
-    }
-}
-
-// One workgroup per (pair, block of up to 64 hidden units): P, Q and c_p for
-// the block's units on MFMA, then GELU and the dot with w2 over all K^2
-// candidate pairs; the block's partial Delta goes to part[pair][block][a][b].
-template <int R>
+// One workgroup per (pair, block of up to 64 hidden units):
+//   P[a][j] = c_p[j] + b1[j] + w_la[j] l_p(a) + U_p[a][j]
+//   Q[b][j] = w_lb[j] l_{p+1}(b) + V_{p+1}[b][j]
+// from the per-candidate products U | V and the per-pair c_p (all loads of a
+// thread issued together), then GELU and the dot with w2 over all K^2
+// candidate pairs, one (a, b) per thread; the block's partial Delta goes to
+// part[pair][block][a][b].
 __global__ __launch_bounds__(256) void mlp_kernel(MlpArgs a) {
-    const int wave = threadIdx.x >> 6;
     const int tid = threadIdx.x;
     const int B = a.B, K = a.K, h = a.h;
     const int nj = (h + kJB - 1) / kJB;
     // Consecutive workgroup numbers go to different XCDs (round-robin over 8):
-    // the hidden blocks of one pair are numbered 8 apart so they share an
-    // XCD, and its L2 serves the pair's z rows after the first fetch.
+    // the hidden blocks of one pair are numbered 8 apart so they share an XCD.
     const int lin = blockIdx.x;
     const int xcd = lin % 8, i8 = lin / 8;
     const int jblk = i8 % nj;
@@ -129,28 +69,48 @@ __global__ __launch_bounds__(256) void mlp_kernel(MlpArgs a) {
     const int64_t tp = static_cast<int64_t>(req) * B + p;  // slot rows of the pair
     const int64_t tq = tp + 1;
     constexpr int PS = kJB + 4;     // LDS row stride of P / Q (floats)
+    const int nin = 3 * a.r + 2;
 
-    __shared__ __attribute__((aligned(16))) uint16_t shv[2 * 128];  // s_p as bf16 hi | lo
     __shared__ __attribute__((aligned(16))) float w2s[kJB];
-    __shared__ float lp[64], lq[64];
     extern __shared__ __attribute__((aligned(16))) float dyn[];
     float* P = dyn;                 // [K][PS]
     float* Q = dyn + K * PS;        // [K][PS]
 
-    // ---- pair state (bf16 hi | lo, computed once per pair), logits, w2
-    for (int c = tid; c < 2 * R; c += 256) shv[c] = a.shl[static_cast<int64_t>(pair) * 2 * R + c];
-    for (int m = tid; m < K; m += 256) {
-        lp[m] = a.vals[tp * K + m];
-        lq[m] = a.vals[tq * K + m];
-    }
-    for (int j = tid; j < kJB; j += 256) w2s[j] = j < jn ? a.w2[j0 + j] : 0.f;
-    __syncthreads();
-
-    // ---- P (with c_p) and Q tiles of this block
-    const int nct = jn / 16;
-    for (int job = wave; job < 2 * nct; job += 4) {
-        const int which = job / nct, ct = job % nct;
-        pq_tile<R>(a, which, j0 + ct * 16, (which ? tq : tp) * K, K, shv, lp, lq, which ? Q : P, ct * 16, PS);
+    // ---- P and Q: thread (rg, cg) fills 4 columns of rows rg, rg + 16, ...
+    {
+        const int cg = tid & 15, rg = tid >> 4;
+        const int c = cg * 4;
+        const bool colok = c < jn;
+        const int cc = colok ? j0 + c : j0;  // clamped columns are not stored
+        float4 cpv = *reinterpret_cast<const float4*>(a.cp + static_cast<int64_t>(pair) * h + cc);
+        const float4 b1v = *reinterpret_cast<const float4*>(a.b1 + cc);
+        float wla[4], wlb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t wrow = static_cast<int64_t>(cc + i) * nin + 3 * a.r;
+            wla[i] = bf16_to_f32(a.w1[wrow]);
+            wlb[i] = bf16_to_f32(a.w1[wrow + 1]);
+        }
+        if (tid < kJB) w2s[tid] = tid < jn ? a.w2[j0 + tid] : 0.f;
+        cpv.x += b1v.x;
+        cpv.y += b1v.y;
+        cpv.z += b1v.z;
+        cpv.w += b1v.w;
+        const int64_t ustride = 2 * static_cast<int64_t>(h);
+        for (int m = rg; m < K; m += 16) {
+            const int64_t np = tp * K + m, nq = tq * K + m;
+            const float4 u = *reinterpret_cast<const float4*>(a.uv + np * ustride + cc);
+            const float4 v = *reinterpret_cast<const float4*>(a.uv + nq * ustride + h + cc);
+            const float lp = a.vals[np], lq = a.vals[nq];
+            if (colok) {
+                *reinterpret_cast<float4*>(P + m * PS + c) =
+                    make_float4(cpv.x + fmaf(wla[0], lp, u.x), cpv.y + fmaf(wla[1], lp, u.y),
+                                cpv.z + fmaf(wla[2], lp, u.z), cpv.w + fmaf(wla[3], lp, u.w));
+                *reinterpret_cast<float4*>(Q + m * PS + c) =
+                    make_float4(fmaf(wlb[0], lq, v.x), fmaf(wlb[1], lq, v.y), fmaf(wlb[2], lq, v.z),
+                                fmaf(wlb[3], lq, v.w));
+            }
+        }
     }
     __syncthreads();
 
@@ -189,13 +149,7 @@ hipError_t launch_mlp(const MlpArgs& a, hipStream_t stream) {
     const int pairs = a.n * (a.B - 1);
     const dim3 grid(static_cast<unsigned>((pairs + 7) / 8 * 8 * mlp_blocks(a.h)));
     const size_t lds = static_cast<size_t>(2) * a.K * (kJB + 4) * sizeof(float);
-    switch (a.r) {
-        case 16: return launch(mlp_kernel<16>, grid, 256, lds, stream, a);
-        case 32: return launch(mlp_kernel<32>, grid, 256, lds, stream, a);
-        case 64: return launch(mlp_kernel<64>, grid, 256, lds, stream, a);
-        case 128: return launch(mlp_kernel<128>, grid, 256, lds, stream, a);
-        default: return hipErrorInvalidValue;
-    }
+    return launch(mlp_kernel, grid, 256, static_cast<uint32_t>(lds), stream, a);
 }
 
 }  // namespace corr

@@ -55,15 +55,20 @@ __device__ __forceinline__ const uint16_t* a_row(const GemmA& A, int64_t m) {
 // spreads round-robin over the 8 XCDs) vary the split fastest: with a split
 // count dividing 8 every XCD works on one k-slice, and the k-slice of W and
 // of the A rows is fetched into that XCD's L2 only.
-__global__ __launch_bounds__(256) void gemm_kernel(GemmA A, GemmW W, int64_t M, int N, int kper, int kdim,
-                                                   int splits, int ntn, float* __restrict__ C) {
+__device__ __forceinline__ void gemm_body(const GemmJob J, int64_t lin) {
+    const GemmA& A = J.A;
+    const GemmW& W = J.W;
+    const int64_t M = J.M;
+    const int N = J.N, kdim = J.kdim, splits = J.splits;
+    float* __restrict__ C = J.C;
+    const int kper = ((kdim / 32 + splits - 1) / splits) * 32;
+    const int ntn = (N + kBN - 1) / kBN;
     __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM * kLS];
     __shared__ __attribute__((aligned(16))) uint16_t Ws[2][kBN * kLS];
     const int tid = threadIdx.x;
     const int l = lane_id();
     const int wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int64_t lin = blockIdx.x;
     const int split = static_cast<int>(lin % splits);
     const int64_t rest = lin / splits;
     const int n0 = static_cast<int>(rest % ntn) * kBN;
@@ -86,6 +91,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmA A, GemmW W, int64_t M, 
     const uint16_t* wp[4];
     bool wok[4];
     int woff[4];
+    const int kmask = W.kwrap > 0 ? W.kwrap - 1 : -1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int seg = tid + 256 * i;
@@ -95,7 +101,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmA A, GemmW W, int64_t M, 
         wok[i] = n < N;
         const int nn = wok[i] ? n : 0;
         const int b = nn / W.nb;
-        wp[i] = W.base[b] + static_cast<int64_t>(nn % W.nb) * W.ld[b] + (seg & 7) * 8;
+        // block select without indexing the argument arrays (keeps them in registers)
+        const uint16_t* wb = b == 0 ? W.base[0] : (b == 1 ? W.base[1] : W.base[2]);
+        const int64_t wld = b == 0 ? W.ld[0] : (b == 1 ? W.ld[1] : W.ld[2]);
+        wp[i] = wb + static_cast<int64_t>(nn % W.nb) * wld;
     }
     const u32x4 zero = {0u, 0u, 0u, 0u};
     // two register sets of slab data: the slabs two and three ahead of the
@@ -110,7 +119,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmA A, GemmW W, int64_t M, 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int kk = k0 + ((tid + 256 * i) & 7) * 8;
-            rw[i] = (wok[i] && kk < k_hi) ? load16(wp[i] + k0) : zero;
+            rw[i] = (wok[i] && kk < k_hi) ? load16(wp[i] + (kk & kmask)) : zero;
         }
     };
     auto store = [&](int buf, const u32x4* ra, const u32x4* rw) {
@@ -176,6 +185,16 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmA A, GemmW W, int64_t M, 
                 if (m < M) out[m * N + n] = acc[i][j][e];
             }
         }
+}
+
+// Two problems per launch: workgroups [0, nblk0) run j0, the rest j1 (the
+// body is instantiated once per problem so each reads its own arguments).
+__global__ __launch_bounds__(256) void gemm_kernel(GemmJob j0, GemmJob j1, int64_t nblk0) {
+    const int64_t b = blockIdx.x;
+    if (b < nblk0)
+        gemm_body(j0, b);
+    else
+        gemm_body(j1, b - nblk0);
 }
 
 // ------------------------------------------------------------------- cand --
@@ -404,13 +423,21 @@ __global__ __launch_bounds__(256) void cand_kernel(CandArgs a) {
 
 }  // namespace
 
+static int64_t gemm_blocks(const GemmJob& j) {
+    return ((j.M + kBM - 1) / kBM) * ((j.N + kBN - 1) / kBN) * j.splits;
+}
+
+hipError_t launch_gemm2(const GemmJob& j0, const GemmJob& j1, hipStream_t stream) {
+    const int64_t b0 = gemm_blocks(j0);
+    return launch(gemm_kernel, dim3(static_cast<unsigned>(b0 + gemm_blocks(j1))), 256, 0, stream, j0, j1, b0);
+}
+
 hipError_t launch_gemm(const GemmA& A, const GemmW& W, int64_t M, int N, int kdim, int splits, float* C,
                        hipStream_t stream) {
-    const int kper = ((kdim / 32 + splits - 1) / splits) * 32;
-    const int ntn = (N + kBN - 1) / kBN;
-    const int64_t blocks = ((M + kBM - 1) / kBM) * ntn * splits;
-    return launch(gemm_kernel, dim3(static_cast<unsigned>(blocks)), 256, 0, stream, A, W, M, N, kper, kdim,
-                  splits, ntn, C);
+    GemmJob j{A, W, M, N, kdim, splits, C};
+    GemmJob none = j;
+    none.M = 0;
+    return launch_gemm2(j, none, stream);
 }
 
 size_t cand_lds_bytes(int r, int dvec, int K) {
