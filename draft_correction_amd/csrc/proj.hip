@@ -76,58 +76,70 @@ __device__ __forceinline__ void gemm_body(const GemmJob J, int64_t lin) {
     const int k_lo = split * kper;
     const int k_hi = min(kdim, k_lo + kper);
 
-    // per-thread load assignments: 2 A segments, 4 W segments of 16 bytes
+    // per-thread load assignments: 2 A segments, 4 W segments of 16 bytes.
+    // Rows past M or N are clamped to the last row (their results are not
+    // stored), so every load is issued unconditionally: the number of loads
+    // in flight is then fixed and each wait for a slab is exact.
     const uint16_t* ap[2];
-    bool aok[2];
     int aoff[2];
+    int sego[6];  // segment column offset within a slab
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int seg = tid + 256 * i;
         const int r = seg >> 3;
         aoff[i] = r * kLS + (seg & 7) * 8;
-        aok[i] = m0 + r < M;
-        ap[i] = (aok[i] ? a_row(A, m0 + r) : A.base) + (seg & 7) * 8;
+        sego[i] = (seg & 7) * 8;
+        ap[i] = a_row(A, min(m0 + r, M - 1));
     }
     const uint16_t* wp[4];
-    bool wok[4];
     int woff[4];
     const int kmask = W.kwrap > 0 ? W.kwrap - 1 : -1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int seg = tid + 256 * i;
         const int r = seg >> 3;
-        const int n = n0 + r;
+        const int nn = min(n0 + r, N - 1);
         woff[i] = r * kLS + (seg & 7) * 8;
-        wok[i] = n < N;
-        const int nn = wok[i] ? n : 0;
+        sego[2 + i] = (seg & 7) * 8;
         const int b = nn / W.nb;
         // block select without indexing the argument arrays (keeps them in registers)
         const uint16_t* wb = b == 0 ? W.base[0] : (b == 1 ? W.base[1] : W.base[2]);
         const int64_t wld = b == 0 ? W.ld[0] : (b == 1 ? W.ld[1] : W.ld[2]);
         wp[i] = wb + static_cast<int64_t>(nn % W.nb) * wld;
     }
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    // two register sets of slab data: the slabs two and three ahead of the
-    // one being multiplied are in flight while it runs
-    u32x4 ra0[2], rw0[4], ra1[2], rw1[4];
-    auto load = [&](int k0, u32x4* ra, u32x4* rw) {
+    const int nslab = k_lo < k_hi ? (k_hi - k_lo + kBK - 1) / kBK : 0;
+    // Slab s covers k_lo + s*kBK .. +kBK-1; k ranges are multiples of 32, so
+    // only the last slab can be half valid.  Its upper half re-reads the
+    // lower half (in bounds) and is zeroed in LDS after the store.  Slab
+    // numbers past the last are clamped to it: those loads are never used.
+    auto load = [&](int sl, u32x4* ra, u32x4* rw) {
+        const int s2 = min(sl, nslab - 1);
+        const int k0 = k_lo + s2 * kBK;
+        const bool half = k0 + kBK > k_hi;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int kk = k0 + ((tid + 256 * i) & 7) * 8;
-            ra[i] = (aok[i] && kk < k_hi) ? load16(ap[i] + k0) : zero;
-        }
+        for (int i = 0; i < 2; ++i) ra[i] = load16(ap[i] + k0 + (half ? (sego[i] & 31) : sego[i]));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int kk = k0 + ((tid + 256 * i) & 7) * 8;
-            rw[i] = (wok[i] && kk < k_hi) ? load16(wp[i] + (kk & kmask)) : zero;
-        }
+        for (int i = 0; i < 4; ++i)
+            rw[i] = load16(wp[i] + ((k0 + (half ? (sego[2 + i] & 31) : sego[2 + i])) & kmask));
     };
-    auto store = [&](int buf, const u32x4* ra, const u32x4* rw) {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    auto store = [&](int buf, int sl, const u32x4* ra, const u32x4* rw) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4*>(&As[buf][aoff[i]]) = ra[i];
 #pragma unroll
         for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&Ws[buf][woff[i]]) = rw[i];
+        if (k_lo + sl * kBK + kBK > k_hi) {  // half slab: clear its upper 32 columns
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                if (sego[i] >= 32) *reinterpret_cast<u32x4*>(&As[buf][aoff[i]]) = zero;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (sego[2 + i] >= 32) *reinterpret_cast<u32x4*>(&Ws[buf][woff[i]]) = zero;
+        }
     };
+    // two register sets of slab data: the slabs one and two ahead of the one
+    // being multiplied are in flight while it runs
+    u32x4 ra0[2], rw0[4], ra1[2], rw1[4];
 
     f32x4 acc[2][4];
 #pragma unroll
@@ -135,42 +147,50 @@ __device__ __forceinline__ void gemm_body(const GemmJob J, int64_t lin) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int kq = 8 * (l >> 4);
+    // All fragments of a slab are read from LDS before its MFMAs, so the
+    // reads overlap one another and the MFMAs issue back to back.
     auto compute = [&](int buf) {
+        constexpr int NKS = kBK / 32;
+        u32x4 af[NKS][2], wf[NKS][4];
 #pragma unroll
-        for (int ks = 0; ks < kBK; ks += 32) {
-            u32x4 af[2], wf[4];
+        for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
             for (int i = 0; i < 2; ++i)
-                af[i] = *reinterpret_cast<const u32x4*>(&As[buf][(wm * 32 + i * 16 + (l & 15)) * kLS + ks + kq]);
+                af[ks][i] =
+                    *reinterpret_cast<const u32x4*>(&As[buf][(wm * 32 + i * 16 + (l & 15)) * kLS + ks * 32 + kq]);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                wf[j] = *reinterpret_cast<const u32x4*>(&Ws[buf][(wn * 64 + j * 16 + (l & 15)) * kLS + ks + kq]);
+                wf[ks][j] =
+                    *reinterpret_cast<const u32x4*>(&Ws[buf][(wn * 64 + j * 16 + (l & 15)) * kLS + ks * 32 + kq]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(af[i], wf[j], acc[i][j]);
-        }
+                for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(af[ks][i], wf[ks][j], acc[i][j]);
     };
 
-    const int nslab = k_lo < k_hi ? (k_hi - k_lo + kBK - 1) / kBK : 0;
     if (nslab > 0) {
-        load(k_lo, ra0, rw0);
-        store(0, ra0, rw0);
-    }
-    if (nslab > 1) load(k_lo + kBK, ra0, rw0);
-    if (nslab > 2) load(k_lo + 2 * kBK, ra1, rw1);
-    __syncthreads();
-    // slab s sits in LDS buffer s & 1; slab s+1 in register set (s & 1) ? 1 : 0
-    for (int s = 0; s < nslab; s += 2) {
-        compute(0);
-        if (s + 1 < nslab) store(1, ra0, rw0);
-        if (s + 3 < nslab) load(k_lo + (s + 3) * kBK, ra0, rw0);
+        load(0, ra0, rw0);
+        load(1, ra1, rw1);
+        store(0, 0, ra0, rw0);
+        load(2, ra0, rw0);
         __syncthreads();
-        if (s + 1 >= nslab) break;
-        compute(1);
-        if (s + 2 < nslab) store(0, ra1, rw1);
-        if (s + 4 < nslab) load(k_lo + (s + 4) * kBK, ra1, rw1);
-        __syncthreads();
+        // slab s sits in LDS buffer s & 1; slab s+1 in register set (s + 1) & 1.
+        // Two slabs per iteration, no exit in between; an odd last slab after.
+        int s = 0;
+        for (; s + 2 <= nslab; s += 2) {
+            compute(0);
+            store(1, s + 1, ra1, rw1);
+            load(s + 3, ra1, rw1);
+            __syncthreads();
+            compute(1);
+            store(0, s + 2, ra0, rw0);
+            load(s + 4, ra0, rw0);
+            __syncthreads();
+        }
+        if (s < nslab) compute(0);
     }
     float* out = C + static_cast<int64_t>(split) * M * N;
 #pragma unroll
@@ -254,6 +274,24 @@ __device__ __forceinline__ f32x4 mfma_hilo_tile(const uint16_t* abuf, int as, in
     return acc;
 }
 
+// As mfma_hilo_tile, with the W fragments already in registers.
+template <int KIN>
+__device__ __forceinline__ f32x4 mfma_hilo_tile_w(const uint16_t* abuf, int as, int M,
+                                                  const u32x4 (&bv)[(2 * KIN + 31) / 32]) {
+    constexpr int KS = (2 * KIN + 31) / 32;
+    const int l = lane_id();
+    const int kq = 8 * (l >> 4);
+    const int m = l & 15;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 av = m < M ? *reinterpret_cast<const u32x4*>(abuf + m * as + ks * 32 + kq) : zero;
+        acc = mfma16x16x32(av, bv[ks], acc);
+    }
+    return acc;
+}
+
 __device__ __forceinline__ void split_store(uint16_t* row, int width, int c, float v) {
     const uint16_t hi = f32_to_bf16(v);
     row[c] = hi;
@@ -283,6 +321,22 @@ __global__ __launch_bounds__(256) void cand_kernel(CandArgs a) {
     float* ubuf = reinterpret_cast<float*>(smem_raw);                       // [kCR][us]
     uint16_t* abuf = reinterpret_cast<uint16_t*>(smem_raw + kCR * us * 4);  // [kCR][as]
     float* gs = reinterpret_cast<float*>(smem_raw + kCR * us * 4 + kCR * as * 2);  // [cand_slots(K)][R]
+
+    // ---- W_fuse fragments of this wave's column tiles (ct = wave + 4c),
+    // issued first so they arrive with the u loads below
+    constexpr int KSF = (2 * (2 * R) + 31) / 32;
+    constexpr int CPW = (NCT + 3) / 4;
+    u32x4 wfr[CPW][KSF];
+    {
+        const int kq = 8 * (l >> 4);
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) {
+            const int ct = min(wave + 4 * c, NCT - 1);  // clamped tiles are not used
+            const uint16_t* wp = a.w_fuse + static_cast<int64_t>(ct * 16 + (l & 15)) * (2 * R);
+#pragma unroll
+            for (int ks = 0; ks < KSF; ++ks) wfr[c][ks] = load16(wp + ((ks * 32 + kq) % (2 * R)));
+        }
+    }
 
     // ---- u: a row of the folded table, or the candidate GEMM's split partials
     {
@@ -365,11 +419,15 @@ __global__ __launch_bounds__(256) void cand_kernel(CandArgs a) {
 
     // ---- y = W_fuse [b; g] (MFMA on the hi / lo split), into ubuf
     const int nrt = (M + 15) / 16;
-    for (int job = wave; job < nrt * NCT; job += 4) {
-        const int rt = job / NCT, ct = job % NCT;
-        const f32x4 acc = mfma_hilo_tile<2 * R>(abuf + rt * 16 * as, as, M - rt * 16, a.w_fuse, 2 * R, ct * 16);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ubuf[(rt * 16 + 4 * (l >> 4) + i) * us + ct * 16 + (l & 15)] = acc[i];
+    for (int c = 0; c < CPW; ++c) {
+        const int ct = wave + 4 * c;
+        if (ct >= NCT) break;
+        for (int rt = 0; rt < nrt; ++rt) {
+            const f32x4 acc = mfma_hilo_tile_w<2 * R>(abuf + rt * 16 * as, as, M - rt * 16, wfr[c]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ubuf[(rt * 16 + 4 * (l >> 4) + i) * us + ct * 16 + (l & 15)] = acc[i];
+        }
     }
     __syncthreads();
 
