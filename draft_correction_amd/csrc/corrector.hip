@@ -199,6 +199,7 @@ hipError_t ensure_side(corrector* h) {
     return hipSuccess;
 }
 
+// Step (1).
 void enqueue_topk(Seq& q, const corrector* h, const Layout& L, int32_t n, const void* logits,
                   int64_t rs, int64_t ss, int32_t* ids, float* vals, void* ws) {
     const corrector_desc& d = h->d;
@@ -249,6 +250,18 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
     q.wait(h->fork_ev, h->side);
     q.s = h->side;
     q("hproj", [&] { return launch_gemm(ha, hw, rows, hn, d.d_hidden, L.splits, hproj, q.s); });
+    SlotArgs sa{};
+    sa.hproj = hproj;
+    sa.hstride = hn;
+    sa.splits = L.splits;
+    sa.rows = rows;
+    sa.r = d.r;
+    sa.B = d.slots;
+    sa.eps = d.ln_eps;
+    sa.g = at<float>(ws, L.g);
+    sa.shl = (!cos && d.slots > 1) ? at<uint16_t>(ws, L.shl) : nullptr;
+    sa.s_out = at<float>(ws, L.s);
+    q("slot_state", [&] { return launch_slot_state(sa, q.s); });
     q.record(h->join_ev, h->side);
     q.s = main;
     if (pre) pre();
@@ -279,14 +292,8 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
     ca.gamma = w.ln_gamma;
     ca.beta = w.ln_beta;
     ca.eps = d.ln_eps;
-    ca.hproj = hproj;
-    ca.hstride = hn;
-    ca.splits = L.splits;
+    ca.g = sa.g;
     ca.zhl = at<uint16_t>(ws, L.z);
-    ca.g = at<float>(ws, L.g);
-    ca.B = d.slots;
-    ca.shl = (!cos && d.slots > 1) ? at<uint16_t>(ws, L.shl) : nullptr;
-    ca.s_out = at<float>(ws, L.s);
     if (cos) {
         ca.w_out = static_cast<const uint16_t*>(w.w_out);
         ca.w_in = static_cast<const uint16_t*>(w.w_in);
@@ -334,7 +341,7 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
         uvj.C = at<float>(ws, L.uv);
         GemmJob cpj{};
         cpj.A.mode = GEMM_A_DENSE;
-        cpj.A.base = ca.shl;
+        cpj.A.base = sa.shl;
         cpj.A.lda = 2 * d.r;
         cpj.W.base[0] = w1;
         cpj.W.ld[0] = nin;

@@ -45,8 +45,28 @@ int topk_chunk_elems(int dtype);
 hipError_t launch_topk_partial(int dtype, const void* logits, int64_t req_stride,
                                int64_t slot_stride, int B, int64_t V, int K, int chunks,
                                int64_t rows, uint64_t* part, hipStream_t stream);
+// Per-slot state from the hidden-state projection partials hproj
+// [splits][rows][hstride] (W_ctx h in columns [0, r); for the MLP variant
+// W_pair,L h in [r, 2r) and W_pair,R h in [2r, 3r)):
+//   g_t = LN(W_ctx h_t) (non-affine)                    -> g [rows][r]
+//   s_p = W_pair,L h_t + W_pair,R h_{t+1} for the pair p starting at slot t
+//                              -> s_out [n(B-1)][r] and shl [n(B-1)][2r] (bf16 hi | lo)
+// shl == null: no pair state (cosine variant).  One wave per slot.
+struct SlotArgs {
+    const float* hproj;     // null: nothing to do
+    int hstride;
+    int splits;
+    int64_t rows;
+    int r;
+    int B;
+    float eps;
+    float* g;
+    uint16_t* shl;
+    float* s_out;
+};
 hipError_t launch_topk_merge(int dtype, const uint64_t* part, int chunks, int K, int64_t rows, int32_t* ids,
                              float* vals, hipStream_t stream);
+hipError_t launch_slot_state(const SlotArgs& sa, hipStream_t stream);
 
 // ---- projections (proj.hip)
 // Tiled GEMM C[split][m][n] = sum_k A[m][k] W[n][k] (bf16 in, float32 out).
@@ -83,10 +103,10 @@ hipError_t launch_gemm(const GemmA& A, const GemmW& W, int64_t M, int N, int kdi
                        hipStream_t stream);
 hipError_t launch_gemm2(const GemmJob& j0, const GemmJob& j1, hipStream_t stream);
 
-// Per drafted slot: b = LN(u) with u = W_cand E[ids], g = LN(W_ctx h) from hproj,
+// Per drafted slot: b = LN(u) with u = W_cand E[ids], g = LN(W_ctx h) per slot,
 // z = gamma * LN(W_fuse [b; g]) + beta stored as bfloat16 hi/lo halves
-// zhl [rows][K][2r] = [hi(z) | lo(z)] with z = hi + lo to ~2^-16;
-// g stored float32 [rows][r].  Cosine: also unit out/in vectors [rows][K][dvec].
+// zhl [rows][K][2r] = [hi(z) | lo(z)] with z = hi + lo to ~2^-16.
+// Cosine: also unit out/in vectors [rows][K][dvec].
 struct CandArgs {
     const int32_t* ids;
     int64_t V;
@@ -100,17 +120,8 @@ struct CandArgs {
     const float* gamma;
     const float* beta;
     float eps;
-    const float* hproj;   // [splits][rows][hstride], W_ctx h in columns [0, r)
-    int hstride;
-    int splits;
+    const float* g;         // [rows][r] LN(W_ctx h) per slot
     uint16_t* zhl;
-    float* g;
-    // pair state (MLP variant only; null otherwise): s_p = W_pair,L h_p +
-    // W_pair,R h_{p+1} for pairs starting in this group's slots, stored as
-    // bf16 hi | lo shl [n(B-1)][2r] and as float32 s_out [n(B-1)][r]
-    int B;
-    uint16_t* shl;
-    float* s_out;
     // cosine only (null otherwise)
     const uint16_t* w_out;
     const uint16_t* w_in;

@@ -368,36 +368,8 @@ __global__ __launch_bounds__(256) void cand_kernel(CandArgs a) {
     constexpr int VPL = R / 16;
     const int c16 = l & 15;
     const int rsub = wave * 4 + (l >> 4);   // 0..15
-    // ---- g = LN(W_ctx h) once per distinct slot of this group
-    const int64_t hs = a.rows * a.hstride;
-    for (int sl = rsub; sl < nslot; sl += 16) {
-        const int64_t t = t0 + sl;
-        const float* hp = a.hproj + t * a.hstride + c16 * VPL;
-        float gv[VPL];
-#pragma unroll
-        for (int i = 0; i < VPL; ++i) gv[i] = sum_strided<kMaxSplits>(hp + i, hs, a.splits);
-        row16_layernorm<R>(gv, a.eps);
-#pragma unroll
-        for (int i = 0; i < VPL; ++i) gs[sl * R + c16 * VPL + i] = gv[i];
-        if (t * a.K >= n0) {  // the group holding the slot's first candidate writes g ...
-#pragma unroll
-            for (int i = 0; i < VPL; ++i) a.g[t * R + c16 * VPL + i] = gv[i];
-            // ... and the pair state of the pair starting at the slot
-            if (a.shl && (t % a.B) != a.B - 1) {
-                const int64_t pair = (t / a.B) * (a.B - 1) + t % a.B;
-                const float* ul = a.hproj + t * a.hstride + R + c16 * VPL;           // W_pair,L h_t
-                const float* vr = a.hproj + (t + 1) * a.hstride + 2 * R + c16 * VPL; // W_pair,R h_{t+1}
-#pragma unroll
-                for (int i = 0; i < VPL; ++i) {
-                    const float sv = sum_strided<kMaxSplits>(ul + i, hs, a.splits) +
-                                     sum_strided<kMaxSplits>(vr + i, hs, a.splits);
-                    const int c = c16 * VPL + i;
-                    split_store(a.shl + pair * 2 * R, R, c, sv);
-                    a.s_out[pair * R + c] = sv;
-                }
-            }
-        }
-    }
+    // ---- g of the group's slots (consecutive, computed per slot beforehand)
+    for (int idx = tid; idx < nslot * R; idx += 256) gs[idx] = a.g[static_cast<int64_t>(t0) * R + idx];
     __syncthreads();
 
     // ---- b = LN(u) per row; [b; g] as bf16 hi | lo rows in abuf
