@@ -309,7 +309,6 @@ template <int R>
 __global__ __launch_bounds__(256) void cand_kernel(CandArgs a) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     constexpr int NCT = R / 16;
-    constexpr int PER = kCR * R / 256;      // u elements per thread
     const int tid = threadIdx.x;
     const int l = lane_id();
     const int wave = tid >> 6;
@@ -339,24 +338,35 @@ __global__ __launch_bounds__(256) void cand_kernel(CandArgs a) {
     }
 
     // ---- u: a row of the folded table, or the candidate GEMM's split partials
+    // (four consecutive columns per thread and load)
     {
-        float uv[PER];
+        constexpr int PER4 = (kCR * R / 4 + 255) / 256;
+        float4 uv[PER4];
 #pragma unroll
-        for (int q = 0; q < PER; ++q) {
-            const int idx = tid + 256 * q;
-            const int m = min(idx / R, M - 1), c = idx % R;  // clamped rows are not stored
+        for (int q = 0; q < PER4; ++q) {
+            const int e = (tid + 256 * q) * 4;
+            const int m = min(e / R, M - 1), c = e % R;  // rows past M are not stored
             if (a.table) {
                 int64_t tok = a.ids[n0 + m];
                 tok = tok < 0 ? 0 : (tok >= a.V ? a.V - 1 : tok);
-                uv[q] = a.table[tok * R + c];
+                uv[q] = *reinterpret_cast<const float4*>(a.table + tok * R + c);
             } else {
-                uv[q] = sum_strided<kMaxUSplits>(a.upart + (n0 + m) * R + c, nodes * R, a.usplits);
+                const float* base = a.upart + (n0 + m) * R + c;
+                float4 t[kMaxUSplits];
+#pragma unroll
+                for (int i = 0; i < kMaxUSplits; ++i)
+                    t[i] = *reinterpret_cast<const float4*>(base + (i < a.usplits ? i : a.usplits - 1) * nodes * R);
+                float4 sum = t[0];
+#pragma unroll
+                for (int i = 1; i < kMaxUSplits; ++i)
+                    if (i < a.usplits) sum = make_float4(sum.x + t[i].x, sum.y + t[i].y, sum.z + t[i].z, sum.w + t[i].w);
+                uv[q] = sum;
             }
         }
 #pragma unroll
-        for (int q = 0; q < PER; ++q) {
-            const int idx = tid + 256 * q;
-            if (idx / R < M) ubuf[(idx / R) * us + idx % R] = uv[q];
+        for (int q = 0; q < PER4; ++q) {
+            const int e = (tid + 256 * q) * 4;
+            if (e / R < M) *reinterpret_cast<float4*>(ubuf + (e / R) * us + e % R) = uv[q];
         }
     }
     // nodes < 2^30 (rows <= 2^24, K <= 64): 32-bit slot arithmetic
