@@ -147,6 +147,8 @@ struct MlpArgs {
     const float* w2;
     float* part;            // [n*(B-1)][blocks][K][K] partial Delta per hidden-unit block
 };
+// Most hidden-unit blocks of the MLP (h <= 256 units in blocks of 64).
+constexpr int kMaxMlpBlocks = 4;
 int mlp_blocks(int h);
 hipError_t launch_mlp(const MlpArgs& a, hipStream_t stream);
 

@@ -43,6 +43,7 @@ __device__ __forceinline__ float gelu(float x) {
 
 // Hidden units handled by one workgroup (a multiple of 16 and of 8).
 constexpr int kJB = 64;
+static_assert(256 / kJB <= kMaxMlpBlocks, "the finishing kernel sums at most kMaxMlpBlocks blocks");
 
 // One workgroup per (pair, block of up to 64 hidden units):
 //   P[a][j] = c_p[j] + b1[j] + w_la[j] l_p(a) + U_p[a][j]

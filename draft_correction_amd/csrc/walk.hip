@@ -99,6 +99,41 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a, int use_lds) 
     const float* part_req = a.part + static_cast<int64_t>(req) * (B - 1) * a.nblk * KK;
     const float* vals_req = a.vals + static_cast<int64_t>(req) * B * K;
     float* scores_req = a.scores + static_cast<int64_t>(req) * per;
+    if ((K & 3) == 0 && ((reinterpret_cast<uintptr_t>(a.scores) | reinterpret_cast<uintptr_t>(a.vals)) & 15) == 0) {
+        // four consecutive elements (one pair, one row a) per float4; four
+        // float4 per thread per round, all loads issued before any is used
+        const int per4 = per32 / 4;
+        for (int i0 = 0; i0 < per4; i0 += 4 * 256) {
+            float4 d[4], lv[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i4 = min(i0 + u * 256 + static_cast<int>(threadIdx.x), per4 - 1);  // clamped: in bounds
+                const int idx = i4 * 4;
+                const int p = idx / KK, e = idx - p * KK;
+                const float* src = part_req + (p * a.nblk) * KK + e;
+                float4 t[kMaxMlpBlocks];
+#pragma unroll
+                for (int b = 0; b < kMaxMlpBlocks; ++b)
+                    t[b] = *reinterpret_cast<const float4*>(src + (b < a.nblk ? b : a.nblk - 1) * KK);
+                float4 acc = t[0];
+#pragma unroll
+                for (int b = 1; b < kMaxMlpBlocks; ++b)
+                    if (b < a.nblk) acc = make_float4(acc.x + t[b].x, acc.y + t[b].y, acc.z + t[b].z, acc.w + t[b].w);
+                d[u] = acc;
+                lv[u] = *reinterpret_cast<const float4*>(vals_req + (p + 1) * K + e % K);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i4 = i0 + u * 256 + static_cast<int>(threadIdx.x);
+                if (i4 < per4) {
+                    const float4 sv = make_float4(lv[u].x + (d[u].x + b2), lv[u].y + (d[u].y + b2),
+                                                  lv[u].z + (d[u].z + b2), lv[u].w + (d[u].w + b2));
+                    reinterpret_cast<float4*>(scores_req)[i4] = sv;
+                    if (use_lds) reinterpret_cast<float4*>(sS)[i4] = sv;
+                }
+            }
+        }
+    } else
     // 8 elements per thread per round, all loads issued before any is used
     for (int i0 = 0; i0 < per32; i0 += 8 * 256) {
         float d[8], lv[8];
@@ -106,7 +141,7 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a, int use_lds) 
         for (int u = 0; u < 8; ++u) {
             const int idx = min(i0 + u * 256 + static_cast<int>(threadIdx.x), per32 - 1);  // clamped: in bounds
             const int p = idx / KK, e = idx - p * KK;
-            d[u] = sum_strided<4>(part_req + (p * a.nblk) * KK + e, KK, a.nblk);
+            d[u] = sum_strided<kMaxMlpBlocks>(part_req + (p * a.nblk) * KK + e, KK, a.nblk);
             lv[u] = vals_req[(p + 1) * K + e % K];
         }
 #pragma unroll
