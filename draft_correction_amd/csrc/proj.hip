@@ -63,8 +63,14 @@ __device__ __forceinline__ void gemm_body(const GemmJob J, int64_t lin) {
     float* __restrict__ C = J.C;
     const int kper = ((kdim / 32 + splits - 1) / splits) * 32;
     const int ntn = (N + kBN - 1) / kBN;
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM * kLS];
-    __shared__ __attribute__((aligned(16))) uint16_t Ws[2][kBN * kLS];
+    // LDS: the double-buffered A and W slabs, reused at the end to stage the
+    // float32 output tile for row-contiguous stores
+    constexpr int kCS = kBN + 4;  // output staging row stride (floats)
+    constexpr int kSlabBytes = 2 * (kBM + kBN) * kLS * 2;
+    constexpr int kOutBytes = kBM * kCS * 4;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kSlabBytes > kOutBytes ? kSlabBytes : kOutBytes];
+    uint16_t (*As)[kBM * kLS] = reinterpret_cast<uint16_t (*)[kBM * kLS]>(smem);
+    uint16_t (*Ws)[kBN * kLS] = reinterpret_cast<uint16_t (*)[kBN * kLS]>(smem + 2 * kBM * kLS * 2);
     const int tid = threadIdx.x;
     const int l = lane_id();
     const int wave = tid >> 6;
@@ -193,18 +199,32 @@ __device__ __forceinline__ void gemm_body(const GemmJob J, int64_t lin) {
         if (s < nslab) compute(0);
     }
     float* out = C + static_cast<int64_t>(split) * M * N;
+    // stage the tile in LDS, then write whole rows as float4
+    float* Cs = reinterpret_cast<float*>(smem);
+    __syncthreads();
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int n = n0 + wn * 64 + j * 16 + (l & 15);
-            if (n >= N) continue;
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t m = m0 + wm * 32 + i * 16 + 4 * (l >> 4) + e;
-                if (m < M) out[m * N + n] = acc[i][j][e];
-            }
+            for (int e = 0; e < 4; ++e)
+                Cs[(wm * 32 + i * 16 + 4 * (l >> 4) + e) * kCS + wn * 64 + j * 16 + (l & 15)] = acc[i][j][e];
+    __syncthreads();
+    if ((N & 3) == 0) {
+#pragma unroll
+        for (int q = 0; q < kBM * kBN / 4 / 256; ++q) {
+            const int f = tid + 256 * q;
+            const int r = f / (kBN / 4), c = (f % (kBN / 4)) * 4;
+            if (m0 + r < M && n0 + c < N)
+                *reinterpret_cast<float4*>(out + (m0 + r) * N + n0 + c) =
+                    *reinterpret_cast<const float4*>(Cs + r * kCS + c);
         }
+    } else {
+        for (int f = tid; f < kBM * kBN; f += 256) {
+            const int r = f / kBN, c = f % kBN;
+            if (m0 + r < M && n0 + c < N) out[(m0 + r) * N + n0 + c] = Cs[r * kCS + c];
+        }
+    }
 }
 
 // Two problems per launch: workgroups [0, nblk0) run j0, the rest j1 (the
