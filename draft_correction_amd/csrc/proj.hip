@@ -36,6 +36,9 @@ namespace {
 // (2 x 4 v_mfma_f32_16x16x32_bf16).
 
 constexpr int kBM = 64, kBN = 128, kBK = 64, kLS = kBK + 8;  // LDS row stride (bf16)
+constexpr int kSegs = kBK / 8;                 // 16-byte segments per slab row
+constexpr int kNA = kBM * kSegs / 256;         // A segments per thread
+constexpr int kNW = kBN * kSegs / 256;         // W segments per thread
 
 __device__ __forceinline__ const uint16_t* a_row(const GemmA& A, int64_t m) {
     switch (A.mode) {
@@ -86,27 +89,27 @@ __device__ __forceinline__ void gemm_body(const GemmJob J, int64_t lin) {
     // Rows past M or N are clamped to the last row (their results are not
     // stored), so every load is issued unconditionally: the number of loads
     // in flight is then fixed and each wait for a slab is exact.
-    const uint16_t* ap[2];
-    int aoff[2];
-    int sego[6];  // segment column offset within a slab
+    const uint16_t* ap[kNA];
+    int aoff[kNA];
+    int sego[kNA + kNW];  // segment column offset within a slab
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < kNA; ++i) {
         const int seg = tid + 256 * i;
-        const int r = seg >> 3;
-        aoff[i] = r * kLS + (seg & 7) * 8;
-        sego[i] = (seg & 7) * 8;
+        const int r = seg / kSegs;
+        aoff[i] = r * kLS + (seg % kSegs) * 8;
+        sego[i] = (seg % kSegs) * 8;
         ap[i] = a_row(A, min(m0 + r, M - 1));
     }
-    const uint16_t* wp[4];
-    int woff[4];
+    const uint16_t* wp[kNW];
+    int woff[kNW];
     const int kmask = W.kwrap > 0 ? W.kwrap - 1 : -1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kNW; ++i) {
         const int seg = tid + 256 * i;
-        const int r = seg >> 3;
+        const int r = seg / kSegs;
         const int nn = min(n0 + r, N - 1);
-        woff[i] = r * kLS + (seg & 7) * 8;
-        sego[2 + i] = (seg & 7) * 8;
+        woff[i] = r * kLS + (seg % kSegs) * 8;
+        sego[kNA + i] = (seg % kSegs) * 8;
         const int b = nn / W.nb;
         // block select without indexing the argument arrays (keeps them in registers)
         const uint16_t* wb = b == 0 ? W.base[0] : (b == 1 ? W.base[1] : W.base[2]);
@@ -123,29 +126,29 @@ __device__ __forceinline__ void gemm_body(const GemmJob J, int64_t lin) {
         const int k0 = k_lo + s2 * kBK;
         const bool half = k0 + kBK > k_hi;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) ra[i] = load16(ap[i] + k0 + (half ? (sego[i] & 31) : sego[i]));
+        for (int i = 0; i < kNA; ++i) ra[i] = load16(ap[i] + k0 + (half ? (sego[i] & 31) : sego[i]));
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            rw[i] = load16(wp[i] + ((k0 + (half ? (sego[2 + i] & 31) : sego[2 + i])) & kmask));
+        for (int i = 0; i < kNW; ++i)
+            rw[i] = load16(wp[i] + ((k0 + (half ? (sego[kNA + i] & 31) : sego[kNA + i])) & kmask));
     };
     const u32x4 zero = {0u, 0u, 0u, 0u};
     auto store = [&](int buf, int sl, const u32x4* ra, const u32x4* rw) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4*>(&As[buf][aoff[i]]) = ra[i];
+        for (int i = 0; i < kNA; ++i) *reinterpret_cast<u32x4*>(&As[buf][aoff[i]]) = ra[i];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&Ws[buf][woff[i]]) = rw[i];
+        for (int i = 0; i < kNW; ++i) *reinterpret_cast<u32x4*>(&Ws[buf][woff[i]]) = rw[i];
         if (k_lo + sl * kBK + kBK > k_hi) {  // half slab: clear its upper 32 columns
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < kNA; ++i)
                 if (sego[i] >= 32) *reinterpret_cast<u32x4*>(&As[buf][aoff[i]]) = zero;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (sego[2 + i] >= 32) *reinterpret_cast<u32x4*>(&Ws[buf][woff[i]]) = zero;
+            for (int i = 0; i < kNW; ++i)
+                if (sego[kNA + i] >= 32) *reinterpret_cast<u32x4*>(&Ws[buf][woff[i]]) = zero;
         }
     };
     // two register sets of slab data: the slabs one and two ahead of the one
     // being multiplied are in flight while it runs
-    u32x4 ra0[2], rw0[4], ra1[2], rw1[4];
+    u32x4 ra0[kNA], rw0[kNW], ra1[kNA], rw1[kNW];
 
     f32x4 acc[2][4];
 #pragma unroll
