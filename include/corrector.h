@@ -29,8 +29,16 @@
  *     host-side validation and launch errors only; a device fault surfaces at
  *     the caller's next synchronisation.  Validation happens before anything
  *     is enqueued, so a call that returns an error has launched nothing.
- *   - A handle is immutable after corrector_create; concurrent calls with one
- *     handle on different streams are safe when each uses its own workspace.
+ *   - corrector_score and corrector_run run the hidden-state projection and the
+ *     per-slot state on a second stream that the handle creates at its first
+ *     such call (default priority): it is forked from `stream` by an event at
+ *     the start of the call and joined back by an event before the candidate
+ *     step, so all of the call's work is ordered after earlier work on
+ *     `stream` and before later work on it, also under stream capture.
+ *   - A handle's weights are fixed after corrector_create; concurrent calls
+ *     with one handle on different streams are safe when each uses its own
+ *     workspace (a lock inside the handle serialises the fork/join of such
+ *     calls; their projections then share the side stream).
  *   - n_req = 0 is a no-op that returns CORR_OK; n_req > max_requests returns
  *     CORR_E_SHAPE.
  *   - Slots are the B drafted positions of a block (the anchor is not one of
