@@ -2,22 +2,23 @@
 // drafted slot, ordered by value descending with ties to the lowest token id.
 //
 // Two launches:
-//   topk_partial  one wave per (row, chunk): a chunk of the row (8192 bf16 or
-//                 4096 float32 logits) is streamed into registers with 16-byte
+//   topk_partial  one wave per (row, chunk): a chunk of the row (6144 bf16 or
+//                 3072 float32 logits) is streamed into registers with 16-byte
 //                 coalesced loads.  bf16 path: one packed pass (v_pk_max_i16 /
 //                 v_pk_min_u16 over pairs of logits) gives every lane its
 //                 maximum; the target-th largest lane maximum is a threshold
-//                 at or below the chunk's K-th largest value; a second packed
-//                 pass flags the 16-byte vectors holding an element at or above
-//                 it and stages them in LDS; their elements become 32-bit
+//                 at or below the chunk's K-th largest value; a per-lane
+//                 bitmask marks the 16-byte vectors holding an element at or
+//                 above it, and those vectors are staged in LDS at slots from
+//                 a prefix sum over lanes; their passing elements become 32-bit
 //                 composite keys (order-preserving value key << 16 | inverted
 //                 local index) and a bitwise search selects the exact top-K of
-//                 the chunk.  If the staged set overflows (heavy ties) an exact
-//                 search over every register-resident element takes over.
+//                 the chunk.  If the staged set overflows (heavy ties) an
+//                 exact search that re-reads the chunk takes over.
 //   topk_merge    one wave per row: the chunks' candidates, as 64-bit
 //                 composites (value key << 32 | inverted token id), go through
-//                 the same threshold-then-search selection and the K winners
-//                 are written in order.
+//                 a threshold-then-search selection and the K winners are
+//                 written in order.
 // Keys map float bits to an unsigned integer order with -0 == +0, so the
 // selection is exact integer work: results are bit-identical to a full sort.
 #include "common.h"
@@ -27,7 +28,7 @@ namespace corr {
 
 namespace {
 
-constexpr int kNV = 16;        // 16-byte loads per lane
+constexpr int kNV = 12;        // 16-byte loads per lane
 constexpr int kCap = 256;      // compacted candidates per wave (float32 path)
 constexpr int kStage = 64;     // staged 16-byte vectors per wave (bf16 path)
 constexpr int kCand16 = 256;   // candidate keys per wave (bf16 path)
@@ -266,14 +267,25 @@ __device__ __forceinline__ void select_chunk(const u32x4 (&raw)[kNV], const Chun
 #pragma unroll
         for (int q = 0; q < kCand16 / kWave; ++q)
             e[q] = static_cast<uint32_t>(q * kWave + l) < nc ? cand[q * kWave + l] : 0u;
-        uint32_t tc = 0;
-        for (int bit = 31; bit >= 0; --bit) {
-            const uint32_t cc = tc | (1u << bit);
+        // bitwise search for the target-th largest composite: the value-key
+        // half first; the index half only when values tie at the boundary
+        auto count_ge = [&](uint32_t cc) {
             int cnt2 = 0;
 #pragma unroll
             for (int q = 0; q < kCand16 / kWave; ++q)
                 if (static_cast<uint32_t>(q * kWave) < nc) cnt2 += popc64(ballot(e[q] >= cc));
-            if (cnt2 >= target) tc = cc;
+            return cnt2;
+        };
+        uint32_t tc = 0;
+        for (int bit = 31; bit >= 16; --bit) {
+            const uint32_t cc = tc | (1u << bit);
+            if (count_ge(cc) >= target) tc = cc;
+        }
+        if (count_ge(tc) > target) {
+            for (int bit = 15; bit >= 0; --bit) {
+                const uint32_t cc = tc | (1u << bit);
+                if (count_ge(cc) >= target) tc = cc;
+            }
         }
 #pragma unroll
         for (int q = 0; q < kCand16 / kWave; ++q) {
