@@ -65,16 +65,14 @@ def algorithmic_work(cfg: dict, n: int) -> dict:
                       per_unit=d * 2, units=rows, unit="hidden row")
     w["cand_gemm"] = dict(bound="hbm", bytes=rows * K * de * 2 + r * de * 2, flops=2 * rows * K * de * r,
                           per_unit=de * 2, units=rows * K, unit="gathered embedding row")
-    w["slot_state"] = dict(bound="hbm", bytes=rows * (3 * r * 4 + r * 4) + pairs * r * (4 + 4),
-                           per_unit=3 * r * 4 + r * 4 + r * 8, units=rows,
-                           unit="slot (3r projections in; g, s_p and its hi|lo split out)")
-    w["cand"] = dict(bound="hbm", bytes=rows * K * r * 4 * 2, flops=2 * rows * K * 2 * r * r,
-                     per_unit=r * 8, units=rows * K, unit="candidate (u in, z out)")
-    # U | V = [W1_za; W1_zb] z per candidate and c_p = W1_s s_p per pair
-    w["uv_gemm"] = dict(bound="hbm", bytes=rows * K * (2 * h * 4 + 2 * r * 2) + pairs * h * 4,
-                        flops=2 * rows * K * 2 * h * r + 2 * pairs * h * r,
-                        per_unit=2 * h * 4 + 2 * r * 2, units=rows * K,
-                        unit="candidate (z hi|lo in, U|V out)")
+    w["slot_state"] = dict(bound="hbm", bytes=rows * (3 * r * 4 + r * 4) + pairs * r * 4,
+                           per_unit=3 * r * 4 + r * 4 + r * 4, units=rows,
+                           unit="slot (3r projections in; g and s_p out)")
+    # the MLP variant's candidate kernel also writes U | V = [W1_za; W1_zb] z
+    uvb = 2 * h * 4 if cfg["variant"] == "mlp" else 0
+    w["cand"] = dict(bound="hbm", bytes=rows * K * (r * 4 * 2 + uvb),
+                     flops=2 * rows * K * (2 * r * r + (2 * h * r if uvb else 0)),
+                     per_unit=r * 8 + uvb, units=rows * K, unit="candidate (u in; z and U|V out)")
     w["finish"] = w["finish_walk"] = dict(bound="hbm", bytes=n * (B - 1) * K * K * 4 * 2,
                                           per_unit=(B - 1) * K * K * 8, units=n, unit="block")
     # the transition MLP epilogue is bound by the vector ALU: K^2 h GELU

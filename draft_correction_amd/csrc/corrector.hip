@@ -26,7 +26,7 @@ constexpr int kMaxKernels = 12;
 constexpr size_t kAlign = 256;
 
 struct Layout {
-    size_t part, ids, vals, hproj, upart, z, g, s, shl, uv, cp, vout, vin, mlp_part, scores, total;
+    size_t part, ids, vals, hproj, upart, z, g, s, uv, vout, vin, mlp_part, scores, total;
     int chunks, splits, usplits;
 };
 
@@ -93,10 +93,8 @@ Layout layout(const corrector_desc& d, int32_t n) {
     L.z = take(sizeof(uint16_t) * rows * d.k * 2 * d.r);
     L.g = take(sizeof(float) * rows * d.r);
     L.s = take(sizeof(float) * pairs * d.r);
-    L.shl = take(sizeof(uint16_t) * pairs * 2 * d.r);
     const bool mlp = d.variant == CORR_VARIANT_MLP;
     L.uv = take(mlp ? sizeof(float) * rows * d.k * 2 * d.mlp_hidden : 0);
-    L.cp = take(mlp ? sizeof(float) * pairs * d.mlp_hidden : 0);
     L.mlp_part = take(mlp ? sizeof(float) * pairs * mlp_blocks(d.mlp_hidden) * d.k * d.k : 0);
     const bool cos = d.variant == CORR_VARIANT_COSINE;
     L.vout = take(cos ? sizeof(float) * rows * d.k * d.d_vec : 0);
@@ -259,9 +257,9 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
     sa.B = d.slots;
     sa.eps = d.ln_eps;
     sa.g = at<float>(ws, L.g);
-    sa.shl = (!cos && d.slots > 1) ? at<uint16_t>(ws, L.shl) : nullptr;
-    sa.s_out = at<float>(ws, L.s);
+    sa.s_out = (!cos && d.slots > 1) ? at<float>(ws, L.s) : nullptr;
     q("slot_state", [&] { return launch_slot_state(sa, q.s); });
+    const bool mlp_pairs = !cos && d.slots > 1;
     q.record(h->join_ev, h->side);
     q.s = main;
     if (pre) pre();
@@ -294,6 +292,11 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
     ca.eps = d.ln_eps;
     ca.g = sa.g;
     ca.zhl = at<uint16_t>(ws, L.z);
+    if (mlp_pairs) {  // the candidate kernel also forms U | V = [W1_za; W1_zb] z
+        ca.w1 = static_cast<const uint16_t*>(w.w1);
+        ca.h = d.mlp_hidden;
+        ca.uv = at<float>(ws, L.uv);
+    }
     if (cos) {
         ca.w_out = static_cast<const uint16_t*>(w.w_out);
         ca.w_in = static_cast<const uint16_t*>(w.w_in);
@@ -321,41 +324,9 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
         q("cosine", [&] { return launch_cosine(c, q.s); });
         if (tokens) q("walk", [&] { return launch_walk(scores, ids, n, d.slots, d.k, tokens, choice, q.s); });
     } else {
-        // U | V = [W1_za; W1_zb] z per candidate and c_p = W1_s s_p per pair,
-        // both over bf16 hi | lo rows (the W1 column block wraps at r)
-        const int nin = 3 * d.r + 2;
-        const uint16_t* w1 = static_cast<const uint16_t*>(w.w1);
-        GemmJob uvj{};
-        uvj.A.mode = GEMM_A_DENSE;
-        uvj.A.base = ca.zhl;
-        uvj.A.lda = 2 * d.r;
-        uvj.W.base[0] = w1 + d.r;
-        uvj.W.base[1] = w1 + 2 * d.r;
-        uvj.W.ld[0] = uvj.W.ld[1] = nin;
-        uvj.W.nb = d.mlp_hidden;
-        uvj.W.kwrap = d.r;
-        uvj.M = rows * d.k;
-        uvj.N = 2 * d.mlp_hidden;
-        uvj.kdim = 2 * d.r;
-        uvj.splits = 1;
-        uvj.C = at<float>(ws, L.uv);
-        GemmJob cpj{};
-        cpj.A.mode = GEMM_A_DENSE;
-        cpj.A.base = sa.shl;
-        cpj.A.lda = 2 * d.r;
-        cpj.W.base[0] = w1;
-        cpj.W.ld[0] = nin;
-        cpj.W.nb = d.mlp_hidden;
-        cpj.W.kwrap = d.r;
-        cpj.M = static_cast<int64_t>(n) * (d.slots - 1);
-        cpj.N = d.mlp_hidden;
-        cpj.kdim = 2 * d.r;
-        cpj.splits = 1;
-        cpj.C = at<float>(ws, L.cp);
-        q("uv_gemm", [&] { return launch_gemm2(uvj, cpj, q.s); });
         MlpArgs m{};
-        m.uv = uvj.C;
-        m.cp = cpj.C;
+        m.uv = ca.uv;
+        m.s = sa.s_out;
         m.vals = vals;
         m.n = n;
         m.B = d.slots;

@@ -50,8 +50,8 @@ hipError_t launch_topk_partial(int dtype, const void* logits, int64_t req_stride
 // W_pair,L h in [r, 2r) and W_pair,R h in [2r, 3r)):
 //   g_t = LN(W_ctx h_t) (non-affine)                    -> g [rows][r]
 //   s_p = W_pair,L h_t + W_pair,R h_{t+1} for the pair p starting at slot t
-//                              -> s_out [n(B-1)][r] and shl [n(B-1)][2r] (bf16 hi | lo)
-// shl == null: no pair state (cosine variant).  One wave per slot.
+//                              -> s_out [n(B-1)][r]
+// s_out == null: no pair state (cosine variant).  One wave per slot.
 struct SlotArgs {
     const float* hproj;     // null: nothing to do
     int hstride;
@@ -61,8 +61,7 @@ struct SlotArgs {
     int B;
     float eps;
     float* g;
-    uint16_t* shl;
-    float* s_out;
+    float* s_out;           // [n(B-1)][r] pair state s_p; null: no pairs to form
 };
 hipError_t launch_topk_merge(int dtype, const uint64_t* part, int chunks, int K, int64_t rows, int32_t* ids,
                              float* vals, hipStream_t stream);
@@ -122,6 +121,10 @@ struct CandArgs {
     float eps;
     const float* g;         // [rows][r] LN(W_ctx h) per slot
     uint16_t* zhl;
+    // MLP variant (null otherwise): U | V = [W1_za; W1_zb] z -> uv [rows*K][2h]
+    const uint16_t* w1;     // [h][3r+2]
+    int h;
+    float* uv;
     // cosine only (null otherwise)
     const uint16_t* w_out;
     const uint16_t* w_in;
@@ -135,7 +138,7 @@ hipError_t launch_cand(const CandArgs& a, hipStream_t stream);
 // ---- transition scores (mlp.hip, cosine.hip)
 struct MlpArgs {
     const float* uv;        // [n][B][K][2h]: W1_za z | W1_zb z per candidate
-    const float* cp;        // [n(B-1)][h]: W1_s s_p per pair
+    const float* s;         // [n(B-1)][r]: pair state s_p (float32)
     const float* vals;      // [n][B][K]
     int n;
     int B;

@@ -7,12 +7,12 @@
 //        =              P_p[a]                        +            Q_p[b]
 // so the K^2 x (3r+2) x h product collapses to per-candidate products
 // U = W1_za z and V = W1_zb z (each candidate's z meets the weights once,
-// whichever pairs it belongs to), the per-pair c_p = W1_s s_p, and a K x K
-// broadcast add.  U | V and c_p come from one two-problem MFMA GEMM launch
-// (the projection GEMM, with z and s_p as bf16 hi | lo rows meeting the same
-// W1 columns twice, so they carry float32 accuracy).  This kernel forms P and
-// Q and runs the epilogue: the GELU over all K^2 x h pre-activations and the
-// h -> 1 dot with w2, one (a, b) per thread.
+// whichever pairs it belongs to; the candidate kernel forms them on MFMA
+// with z as bf16 hi | lo rows, so they carry float32 accuracy), the per-pair
+// c_p = W1_s s_p (float32 dot products here, a quarter of r per thread), and
+// a K x K broadcast add.  This kernel forms P and Q and runs the epilogue:
+// the GELU over all K^2 x h pre-activations and the h -> 1 dot with w2, one
+// (a, b) per thread.
 //
 // Work is split into (pair, block of 64 hidden units) workgroups; each block
 // writes its partial Delta and the finishing kernel adds the blocks in order,
@@ -43,13 +43,14 @@ __device__ __forceinline__ float gelu(float x) {
 
 // Hidden units handled by one workgroup (a multiple of 16 and of 8).
 constexpr int kJB = 64;
+static_assert(256 == 4 * kJB, "four r quarters per hidden unit in the c_p dot");
 static_assert(256 / kJB <= kMaxMlpBlocks, "the finishing kernel sums at most kMaxMlpBlocks blocks");
 
 // One workgroup per (pair, block of up to 64 hidden units):
 //   P[a][j] = c_p[j] + b1[j] + w_la[j] l_p(a) + U_p[a][j]
 //   Q[b][j] = w_lb[j] l_{p+1}(b) + V_{p+1}[b][j]
-// from the per-candidate products U | V and the per-pair c_p (all loads of a
-// thread issued together), then GELU and the dot with w2 over all K^2
+// from the per-candidate products U | V and the pair's c_p (formed here from
+// s_p), then GELU and the dot with w2 over all K^2
 // candidate pairs, one (a, b) per thread; the block's partial Delta goes to
 // part[pair][block][a][b].
 __global__ __launch_bounds__(256) void mlp_kernel(MlpArgs a) {
@@ -77,36 +78,91 @@ __global__ __launch_bounds__(256) void mlp_kernel(MlpArgs a) {
     float* P = dyn;                 // [K][PS]
     float* Q = dyn + K * PS;        // [K][PS]
 
-    // ---- P and Q: thread (rg, cg) fills 4 columns of rows rg, rg + 16, ...
+    __shared__ float cps4[4][kJB];  // c_p partial dots, one per quarter of r
+
+    // ---- operands: thread (rg, cg) forms 4 columns of rows rg, rg + 16, ...;
+    // the first row's U, V and logits load here with everything else
+    const int cg = tid & 15, rg = tid >> 4;
+    const int c = cg * 4;
+    const bool colok = c < jn;
+    const int cc = colok ? j0 + c : j0;  // clamped columns are not stored
+    const int64_t ustride = 2 * static_cast<int64_t>(h);
+    const int m0 = min(rg, K - 1);        // rows past K are not stored
+    const float4 u0 = *reinterpret_cast<const float4*>(a.uv + (tp * K + m0) * ustride + cc);
+    const float4 v0 = *reinterpret_cast<const float4*>(a.uv + (tq * K + m0) * ustride + h + cc);
+    const float lp0 = a.vals[tp * K + m0], lq0 = a.vals[tq * K + m0];
+    const float4 b1v = *reinterpret_cast<const float4*>(a.b1 + cc);
+    float wla[4], wlb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t wrow = static_cast<int64_t>(cc + i) * nin + 3 * a.r;
+        wla[i] = bf16_to_f32(a.w1[wrow]);
+        wlb[i] = bf16_to_f32(a.w1[wrow + 1]);
+    }
+    if (tid < kJB) w2s[tid] = tid < jn ? a.w2[j0 + tid] : 0.f;
+    // c_p = W1_s s_p for the block's units: thread (jj, kq) dots row j0 + jj
+    // of W1_s with s_p over the quarter kq of its r columns, in column order.
+    // W1 rows are 3r + 2 bf16 long (4-byte aligned: r is a multiple of 16),
+    // so they are read in 32-bit words of two columns each.
     {
-        const int cg = tid & 15, rg = tid >> 4;
-        const int c = cg * 4;
-        const bool colok = c < jn;
-        const int cc = colok ? j0 + c : j0;  // clamped columns are not stored
-        float4 cpv = *reinterpret_cast<const float4*>(a.cp + static_cast<int64_t>(pair) * h + cc);
-        const float4 b1v = *reinterpret_cast<const float4*>(a.b1 + cc);
-        float wla[4], wlb[4];
+        const int jj = tid & (kJB - 1), kq = tid / kJB;
+        const int kw = a.r / 4;
+        const uint32_t* wr = reinterpret_cast<const uint32_t*>(
+            a.w1 + static_cast<int64_t>(min(j0 + jj, h - 1)) * nin + kq * kw);
+        const float* sp = a.s + static_cast<int64_t>(pair) * a.r + kq * kw;
+        // every load is issued before the first is used (r <= 128: at most
+        // 8 groups of 4 columns; groups past kw re-read the last and are not
+        // summed)
+        constexpr int kG = 128 / 4 / 4;
+        uint32_t wv[2 * kG];
+        float4 sv[kG];
+#pragma unroll
+        for (int g = 0; g < kG; ++g) {
+            const int k = min(4 * g, kw - 4);
+            wv[2 * g] = wr[k / 2];
+            wv[2 * g + 1] = wr[k / 2 + 1];
+            sv[g] = *reinterpret_cast<const float4*>(sp + k);
+        }
+        float acc = 0.f;
+#pragma unroll
+        for (int g = 0; g < kG; ++g) {
+            if (4 * g < kw) {
+                acc = fmaf(__uint_as_float(wv[2 * g] << 16), sv[g].x, acc);
+                acc = fmaf(__uint_as_float(wv[2 * g] & 0xFFFF0000u), sv[g].y, acc);
+                acc = fmaf(__uint_as_float(wv[2 * g + 1] << 16), sv[g].z, acc);
+                acc = fmaf(__uint_as_float(wv[2 * g + 1] & 0xFFFF0000u), sv[g].w, acc);
+            }
+        }
+        cps4[kq][jj] = acc;
+    }
+    __syncthreads();
+
+    // ---- P = c_p + b1 + w_la l_p(a) + U, Q = w_lb l_{p+1}(b) + V
+    {
+        float cpv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int64_t wrow = static_cast<int64_t>(cc + i) * nin + 3 * a.r;
-            wla[i] = bf16_to_f32(a.w1[wrow]);
-            wlb[i] = bf16_to_f32(a.w1[wrow + 1]);
+            const int jj = min(c + i, kJB - 1);
+            cpv[i] = ((cps4[0][jj] + cps4[1][jj]) + (cps4[2][jj] + cps4[3][jj]));
         }
-        if (tid < kJB) w2s[tid] = tid < jn ? a.w2[j0 + tid] : 0.f;
-        cpv.x += b1v.x;
-        cpv.y += b1v.y;
-        cpv.z += b1v.z;
-        cpv.w += b1v.w;
-        const int64_t ustride = 2 * static_cast<int64_t>(h);
+        cpv[0] += b1v.x;
+        cpv[1] += b1v.y;
+        cpv[2] += b1v.z;
+        cpv[3] += b1v.w;
         for (int m = rg; m < K; m += 16) {
-            const int64_t np = tp * K + m, nq = tq * K + m;
-            const float4 u = *reinterpret_cast<const float4*>(a.uv + np * ustride + cc);
-            const float4 v = *reinterpret_cast<const float4*>(a.uv + nq * ustride + h + cc);
-            const float lp = a.vals[np], lq = a.vals[nq];
+            float4 u = u0, v = v0;
+            float lp = lp0, lq = lq0;
+            if (m != rg) {
+                const int64_t np = tp * K + m, nq = tq * K + m;
+                u = *reinterpret_cast<const float4*>(a.uv + np * ustride + cc);
+                v = *reinterpret_cast<const float4*>(a.uv + nq * ustride + h + cc);
+                lp = a.vals[np];
+                lq = a.vals[nq];
+            }
             if (colok) {
                 *reinterpret_cast<float4*>(P + m * PS + c) =
-                    make_float4(cpv.x + fmaf(wla[0], lp, u.x), cpv.y + fmaf(wla[1], lp, u.y),
-                                cpv.z + fmaf(wla[2], lp, u.z), cpv.w + fmaf(wla[3], lp, u.w));
+                    make_float4(cpv[0] + fmaf(wla[0], lp, u.x), cpv[1] + fmaf(wla[1], lp, u.y),
+                                cpv[2] + fmaf(wla[2], lp, u.z), cpv[3] + fmaf(wla[3], lp, u.w));
                 *reinterpret_cast<float4*>(Q + m * PS + c) =
                     make_float4(fmaf(wlb[0], lq, v.x), fmaf(wlb[1], lq, v.y), fmaf(wlb[2], lq, v.z),
                                 fmaf(wlb[3], lq, v.w));

@@ -634,7 +634,7 @@ __device__ __forceinline__ SlotLoads slot_state_load(const SlotArgs& a, int64_t 
     SlotLoads o;
     const int l = lane_id();
     const int64_t hs = a.rows * a.hstride;
-    const bool pair = a.shl != nullptr && (t % a.B) != a.B - 1;
+    const bool pair = a.s_out != nullptr && (t % a.B) != a.B - 1;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int c = min(l + 64 * i, a.r - 1);  // clamped columns are not stored
@@ -657,20 +657,10 @@ __device__ __forceinline__ void slot_state_finish(const SlotArgs& a, int64_t t, 
     const float inv = 1.0f / sqrtf(var + a.eps);
     if (ok0) a.g[t * a.r + l] = d0 * inv;
     if (ok1) a.g[t * a.r + l + 64] = d1 * inv;
-    if (a.shl != nullptr && (t % a.B) != a.B - 1) {
+    if (a.s_out != nullptr && (t % a.B) != a.B - 1) {
         const int64_t p = (t / a.B) * (a.B - 1) + t % a.B;
-        uint16_t* sh = a.shl + p * 2 * a.r;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int c = l + 64 * i;
-            if (c < a.r) {
-                const float v = o.sv[i];
-                a.s_out[p * a.r + c] = v;
-                const uint16_t hi = f32_to_bf16(v);
-                sh[c] = hi;
-                sh[a.r + c] = f32_to_bf16(v - bf16_to_f32(hi));
-            }
-        }
+        if (ok0) a.s_out[p * a.r + l] = o.sv[0];
+        if (ok1) a.s_out[p * a.r + l + 64] = o.sv[1];
     }
 }
 
