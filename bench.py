@@ -61,13 +61,17 @@ def algorithmic_work(cfg: dict, n: int) -> dict:
                              per_unit=V * esz, units=rows)
     w["topk_merge"] = dict(bound="hbm", bytes=rows * K * 8, per_unit=K * 8, units=rows,
                            unit="slot row (K ids + values out)")
-    w["hproj"] = dict(bound="hbm", bytes=rows * d * 2 + 3 * r * d * 2, flops=2 * rows * d * 3 * r,
+    hn = 3 * r if cfg["variant"] == "mlp" else r
+    w["hproj"] = dict(bound="hbm", bytes=rows * d * 2 + hn * d * 2, flops=2 * rows * d * hn,
                       per_unit=d * 2, units=rows, unit="hidden row")
     w["cand_gemm"] = dict(bound="hbm", bytes=rows * K * de * 2 + r * de * 2, flops=2 * rows * K * de * r,
                           per_unit=de * 2, units=rows * K, unit="gathered embedding row")
-    w["slot_state"] = dict(bound="hbm", bytes=rows * (3 * r * 4 + r * 4) + pairs * r * 4,
-                           per_unit=3 * r * 4 + r * 4 + r * 4, units=rows,
-                           unit="slot (3r projections in; g and s_p out)")
+    # one launch: the gathered candidate projection and the hidden-state
+    # projection side by side
+    w["proj_gemm"] = dict(bound="hbm", bytes=w["cand_gemm"]["bytes"] + w["hproj"]["bytes"],
+                          flops=w["cand_gemm"]["flops"] + w["hproj"]["flops"],
+                          per_unit=de * 2, units=rows * K + rows,
+                          unit="gathered embedding row or hidden row (d_e = d)")
     # the MLP variant's candidate kernel also writes U | V = [W1_za; W1_zb] z
     uvb = 2 * h * 4 if cfg["variant"] == "mlp" else 0
     w["cand"] = dict(bound="hbm", bytes=rows * K * (r * 4 * 2 + uvb),

@@ -42,14 +42,9 @@ struct corrector {
     const char* names[kMaxKernels];
     int nk;
     const float* table;  // folded E W_cand^T [V][r], or null
-    // Side stream for the hidden-state projection, which does not depend on
-    // the top-K: it is forked from the call's stream and joined back before
-    // the candidate kernel.  Created at first use; `mu` makes each call's
-    // record/wait pairs on the shared events atomic.
+    // Serialises calls that record the timing events (a diagnostic mode);
+    // without timing a call touches no mutable handle state.
     std::mutex mu;
-    bool side_ready;
-    hipStream_t side;
-    hipEvent_t fork_ev, join_ev;
 };
 
 namespace {
@@ -174,29 +169,6 @@ struct Seq {
     }
 };
 
-// Creates the side stream and its fork/join events on first use (the caller
-// holds h->mu).  Default priority, non-blocking with respect to the NULL
-// stream.  Both streams run on one device, so the events need no system-scope
-// fence.
-hipError_t ensure_side(corrector* h) {
-    if (h->side_ready) return hipSuccess;
-    hipError_t e = hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking);
-    if (e != hipSuccess) return e;
-    e = hipEventCreateWithFlags(&h->fork_ev, hipEventDisableTiming | hipEventDisableSystemFence);
-    if (e != hipSuccess) {
-        (void)hipStreamDestroy(h->side);
-        return e;
-    }
-    e = hipEventCreateWithFlags(&h->join_ev, hipEventDisableTiming | hipEventDisableSystemFence);
-    if (e != hipSuccess) {
-        (void)hipEventDestroy(h->fork_ev);
-        (void)hipStreamDestroy(h->side);
-        return e;
-    }
-    h->side_ready = true;
-    return hipSuccess;
-}
-
 // Step (1).
 void enqueue_topk(Seq& q, const corrector* h, const Layout& L, int32_t n, const void* logits,
                   int64_t rs, int64_t ss, int32_t* ids, float* vals, void* ws) {
@@ -212,9 +184,10 @@ void enqueue_topk(Seq& q, const corrector* h, const Layout& L, int32_t n, const 
 
 // Steps (2)-(4); with tokens given also step (5) (fused into the MLP finish
 // for the MLP variant, a walk launch for the cosine variant).
-// `pre` (optional) enqueues work on the call's stream between the fork of the
-// hidden-state projection and the candidate projection (corrector_run puts
-// the top-K there).  The caller holds h->mu and has made the side stream.
+// `pre` (optional) enqueues work ahead of the projections on the same stream
+// (corrector_run puts the top-K there).  Everything runs in order on the
+// call's stream: the hidden-state projection shares one GEMM launch with the
+// candidate projection, and the candidate kernel forms the per-slot state.
 void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const int32_t* ids,
                    const float* vals, const void* hidden, int64_t hrs, int64_t hss, float* scores,
                    void* ws, int32_t* tokens, int32_t* choice, const std::function<void()>& pre) {
@@ -223,59 +196,51 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
     const int64_t rows = static_cast<int64_t>(n) * d.slots;
     float* hproj = at<float>(ws, L.hproj);
     const bool cos = d.variant == CORR_VARIANT_COSINE;
-    GemmA ha{};
-    ha.mode = GEMM_A_SLOTS;
-    ha.base = static_cast<const uint16_t*>(hidden);
-    ha.B = d.slots;
-    ha.rs = hrs;
-    ha.ss = hss;
-    GemmW hw{};
-    hw.nb = d.r;
-    hw.base[0] = static_cast<const uint16_t*>(w.w_ctx);
-    hw.ld[0] = d.d_hidden;
-    if (!cos) {
-        hw.base[1] = static_cast<const uint16_t*>(w.w_pair);
-        hw.base[2] = static_cast<const uint16_t*>(w.w_pair) + d.d_hidden;
-        hw.ld[1] = hw.ld[2] = 2 * static_cast<int64_t>(d.d_hidden);
-    }
     // hproj rows: [W_ctx h | W_pair,L h | W_pair,R h] (3r wide); the cosine
     // variant has no pair state and computes the W_ctx block alone (r wide).
-    // It runs on the side stream, overlapping whatever the call's stream
-    // runs until the join before the candidate kernel.
+    GemmJob hj{};
+    hj.A.mode = GEMM_A_SLOTS;
+    hj.A.base = static_cast<const uint16_t*>(hidden);
+    hj.A.B = d.slots;
+    hj.A.rs = hrs;
+    hj.A.ss = hss;
+    hj.W.nb = d.r;
+    hj.W.base[0] = static_cast<const uint16_t*>(w.w_ctx);
+    hj.W.ld[0] = d.d_hidden;
+    if (!cos) {
+        hj.W.base[1] = static_cast<const uint16_t*>(w.w_pair);
+        hj.W.base[2] = static_cast<const uint16_t*>(w.w_pair) + d.d_hidden;
+        hj.W.ld[1] = hj.W.ld[2] = 2 * static_cast<int64_t>(d.d_hidden);
+    }
     const int hn = cos ? d.r : 3 * d.r;
-    const hipStream_t main = q.s;
-    q.record(h->fork_ev, main);
-    q.wait(h->fork_ev, h->side);
-    q.s = h->side;
-    q("hproj", [&] { return launch_gemm(ha, hw, rows, hn, d.d_hidden, L.splits, hproj, q.s); });
-    SlotArgs sa{};
-    sa.hproj = hproj;
-    sa.hstride = hn;
-    sa.splits = L.splits;
-    sa.rows = rows;
-    sa.r = d.r;
-    sa.B = d.slots;
-    sa.eps = d.ln_eps;
-    sa.g = at<float>(ws, L.g);
-    sa.s_out = (!cos && d.slots > 1) ? at<float>(ws, L.s) : nullptr;
-    q("slot_state", [&] { return launch_slot_state(sa, q.s); });
+    hj.M = rows;
+    hj.N = hn;
+    hj.kdim = d.d_hidden;
+    hj.splits = L.splits;
+    hj.C = hproj;
     const bool mlp_pairs = !cos && d.slots > 1;
-    q.record(h->join_ev, h->side);
-    q.s = main;
     if (pre) pre();
     float* upart = at<float>(ws, L.upart);
     if (!h->table) {
-    GemmA ua{};
-    ua.mode = GEMM_A_GATHER;
-    ua.base = static_cast<const uint16_t*>(w.embed);
-    ua.lda = d.d_embed;
-    ua.ids = ids;
-    ua.V = d.vocab;
-    GemmW uw{};
-    uw.nb = d.r;
-    uw.base[0] = static_cast<const uint16_t*>(w.w_cand);
-    uw.ld[0] = d.d_embed;
-    q("cand_gemm", [&] { return launch_gemm(ua, uw, rows * d.k, d.r, d.d_embed, L.usplits, upart, q.s); });
+        // the candidate projection u = W_cand E[c] first (longer workgroups),
+        // the hidden-state projection after it in the same launch
+        GemmJob uj{};
+        uj.A.mode = GEMM_A_GATHER;
+        uj.A.base = static_cast<const uint16_t*>(w.embed);
+        uj.A.lda = d.d_embed;
+        uj.A.ids = ids;
+        uj.A.V = d.vocab;
+        uj.W.nb = d.r;
+        uj.W.base[0] = static_cast<const uint16_t*>(w.w_cand);
+        uj.W.ld[0] = d.d_embed;
+        uj.M = rows * d.k;
+        uj.N = d.r;
+        uj.kdim = d.d_embed;
+        uj.splits = L.usplits;
+        uj.C = upart;
+        q("proj_gemm", [&] { return launch_gemm2(uj, hj, q.s); });
+    } else {
+        q("hproj", [&] { return launch_gemm(hj.A, hj.W, hj.M, hj.N, hj.kdim, hj.splits, hj.C, q.s); });
     }
     CandArgs ca{};
     ca.ids = ids;
@@ -290,7 +255,12 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
     ca.gamma = w.ln_gamma;
     ca.beta = w.ln_beta;
     ca.eps = d.ln_eps;
-    ca.g = sa.g;
+    ca.hproj = hproj;
+    ca.hstride = hn;
+    ca.splits = L.splits;
+    ca.B = d.slots;
+    ca.g_out = at<float>(ws, L.g);
+    ca.s_out = mlp_pairs ? at<float>(ws, L.s) : nullptr;
     ca.zhl = at<uint16_t>(ws, L.z);
     if (mlp_pairs) {  // the candidate kernel also forms U | V = [W1_za; W1_zb] z
         ca.w1 = static_cast<const uint16_t*>(w.w1);
@@ -304,7 +274,6 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
         ca.vout = at<float>(ws, L.vout);
         ca.vin = at<float>(ws, L.vin);
     }
-    q.wait(h->join_ev, main);
     q("cand", [&] { return launch_cand(ca, q.s); });
     if (d.slots < 2) {
         if (tokens) q("walk", [&] { return launch_walk(scores, ids, n, d.slots, d.k, tokens, choice, q.s); });
@@ -326,7 +295,7 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
     } else {
         MlpArgs m{};
         m.uv = ca.uv;
-        m.s = sa.s_out;
+        m.s = ca.s_out;
         m.vals = vals;
         m.n = n;
         m.B = d.slots;
@@ -409,7 +378,6 @@ int corrector_create(const corrector_desc* desc, const corrector_weights* wt, co
     h->events_ready = false;
     h->nk = 0;
     h->table = nullptr;
-    h->side_ready = false;
     *out = h;
     return CORR_OK;
 }
@@ -418,11 +386,6 @@ void corrector_destroy(corrector* h) {
     if (!live(h)) return;
     if (h->events_ready)
         for (hipEvent_t& e : h->ev) (void)hipEventDestroy(e);
-    if (h->side_ready) {
-        (void)hipEventDestroy(h->fork_ev);
-        (void)hipEventDestroy(h->join_ev);
-        (void)hipStreamDestroy(h->side);
-    }
     h->magic = kDead;
     delete h;
 }
@@ -441,6 +404,8 @@ int corrector_topk(const corrector* hc, int32_t n, const void* logits, int64_t r
     if ((rc = check_ws(hc, n, ws, ws_bytes))) return rc;
     corrector* h = const_cast<corrector*>(hc);
     const Layout L = layout(h->d, n);
+    std::unique_lock<std::mutex> lock(h->mu, std::defer_lock);
+    if (h->timing) lock.lock();
     Seq q{h, static_cast<hipStream_t>(stream)};
     enqueue_topk(q, h, L, n, logits, rs, ss, ids, vals, ws);
     return q.finish();
@@ -457,8 +422,8 @@ int corrector_score(const corrector* hc, int32_t n, const int32_t* ids, const fl
     if ((rc = check_ws(hc, n, ws, ws_bytes))) return rc;
     corrector* h = const_cast<corrector*>(hc);
     const Layout L = layout(h->d, n);
-    std::lock_guard<std::mutex> lock(h->mu);
-    if (ensure_side(h) != hipSuccess) return CORR_E_HIP;
+    std::unique_lock<std::mutex> lock(h->mu, std::defer_lock);
+    if (h->timing) lock.lock();
     Seq q{h, static_cast<hipStream_t>(stream)};
     enqueue_score(q, h, L, n, ids, vals, hidden, hrs, hss, scores, ws, nullptr, nullptr, nullptr);
     return q.finish();
@@ -470,6 +435,8 @@ int corrector_walk(const corrector* hc, int32_t n, const float* scores, const in
     if (rc || n == 0) return rc;
     if (!ids || !tokens || (!scores && hc->d.slots > 1)) return CORR_E_NULL;
     corrector* h = const_cast<corrector*>(hc);
+    std::unique_lock<std::mutex> lock(h->mu, std::defer_lock);
+    if (h->timing) lock.lock();
     Seq q{h, static_cast<hipStream_t>(stream)};
     q("walk", [&] { return launch_walk(scores, ids, n, h->d.slots, h->d.k, tokens, choice, q.s); });
     return q.finish();
@@ -490,8 +457,8 @@ int corrector_run(const corrector* hc, int32_t n, const void* logits, int64_t lr
     int32_t* ids = ids_or_null ? ids_or_null : at<int32_t>(ws, L.ids);
     float* vals = vals_or_null ? vals_or_null : at<float>(ws, L.vals);
     float* scores = scores_or_null ? scores_or_null : at<float>(ws, L.scores);
-    std::lock_guard<std::mutex> lock(h->mu);
-    if (ensure_side(h) != hipSuccess) return CORR_E_HIP;
+    std::unique_lock<std::mutex> lock(h->mu, std::defer_lock);
+    if (h->timing) lock.lock();
     Seq q{h, static_cast<hipStream_t>(stream)};
     enqueue_score(q, h, L, n, ids, vals, hidden, hrs, hss, scores, ws, tokens, choice_or_null,
                   [&] { enqueue_topk(q, h, L, n, logits, lrs, lss, ids, vals, ws); });

@@ -45,27 +45,9 @@ int topk_chunk_elems(int dtype);
 hipError_t launch_topk_partial(int dtype, const void* logits, int64_t req_stride,
                                int64_t slot_stride, int B, int64_t V, int K, int chunks,
                                int64_t rows, uint64_t* part, hipStream_t stream);
-// Per-slot state from the hidden-state projection partials hproj
-// [splits][rows][hstride] (W_ctx h in columns [0, r); for the MLP variant
-// W_pair,L h in [r, 2r) and W_pair,R h in [2r, 3r)):
-//   g_t = LN(W_ctx h_t) (non-affine)                    -> g [rows][r]
-//   s_p = W_pair,L h_t + W_pair,R h_{t+1} for the pair p starting at slot t
-//                              -> s_out [n(B-1)][r]
-// s_out == null: no pair state (cosine variant).  One wave per slot.
-struct SlotArgs {
-    const float* hproj;     // null: nothing to do
-    int hstride;
-    int splits;
-    int64_t rows;
-    int r;
-    int B;
-    float eps;
-    float* g;
-    float* s_out;           // [n(B-1)][r] pair state s_p; null: no pairs to form
-};
+// The K winners of every row, in order, from the chunks' composites.
 hipError_t launch_topk_merge(int dtype, const uint64_t* part, int chunks, int K, int64_t rows, int32_t* ids,
                              float* vals, hipStream_t stream);
-hipError_t launch_slot_state(const SlotArgs& sa, hipStream_t stream);
 
 // ---- projections (proj.hip)
 // Tiled GEMM C[split][m][n] = sum_k A[m][k] W[n][k] (bf16 in, float32 out).
@@ -119,7 +101,19 @@ struct CandArgs {
     const float* gamma;
     const float* beta;
     float eps;
-    const float* g;         // [rows][r] LN(W_ctx h) per slot
+    // Per-slot state from the hidden-state projection partials hproj
+    // [splits][rows][hstride] (W_ctx h in columns [0, r), W_pair,L h in
+    // [r, 2r) and W_pair,R h in [2r, 3r) when the variant has pairs): the
+    // kernel forms g = LN(W_ctx h) of the slots its candidates belong to and,
+    // for each slot t whose first candidate it holds, writes g_t to g_out and
+    // (s_out non-null, t not the last drafted slot) the pair state
+    // s_t = W_pair,L h_t + W_pair,R h_{t+1} to s_out.
+    const float* hproj;
+    int hstride;
+    int splits;
+    int B;                  // drafted slots per request
+    float* g_out;           // [rows][r]
+    float* s_out;           // [n(B-1)][r], or null
     uint16_t* zhl;
     // MLP variant (null otherwise): U | V = [W1_za; W1_zb] z -> uv [rows*K][2h]
     const uint16_t* w1;     // [h][3r+2]

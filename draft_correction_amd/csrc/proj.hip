@@ -459,8 +459,39 @@ __global__ __launch_bounds__(256) void cand_kernel(CandArgs a) {
     constexpr int VPL = R / 16;
     const int c16 = l & 15;
     const int rsub = wave * 4 + (l >> 4);   // 0..15
-    // ---- g of the group's slots (consecutive, computed per slot beforehand)
-    for (int idx = tid; idx < nslot * R; idx += 256) gs[idx] = a.g[static_cast<int64_t>(t0) * R + idx];
+    // ---- g = LN(W_ctx h) of the group's slots (consecutive), from the
+    // projection partials summed in split order; slot rows take 16 lanes each
+    {
+        const int64_t hs = a.rows * a.hstride;
+        for (int sl = rsub; sl < nslot; sl += 16) {
+            const int64_t t = t0 + sl;
+            float gv[VPL];
+#pragma unroll
+            for (int i = 0; i < VPL; ++i)
+                gv[i] = sum_strided<kMaxSplits>(a.hproj + t * a.hstride + c16 * VPL + i, hs, a.splits);
+            row16_layernorm<R>(gv, a.eps);
+            // the workgroup holding the slot's first candidate publishes g_t
+            const bool owner = static_cast<int64_t>(t) * a.K >= n0;
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                gs[sl * R + c16 * VPL + i] = gv[i];
+                if (owner) a.g_out[t * R + c16 * VPL + i] = gv[i];
+            }
+        }
+        // ---- pair state s_t = W_pair,L h_t + W_pair,R h_{t+1} for the slots
+        // whose first candidate this workgroup holds (each sum in split order)
+        if (a.s_out) {
+            for (int idx = tid; idx < nslot * R; idx += 256) {
+                const int sl = idx / R, c = idx % R;
+                const int64_t t = t0 + sl;
+                if (t * a.K < n0 || (t % a.B) == a.B - 1) continue;
+                const float* hp = a.hproj + t * a.hstride;
+                const float sv = sum_strided<kMaxSplits>(hp + R + c, hs, a.splits) +
+                                 sum_strided<kMaxSplits>(hp + a.hstride + 2 * R + c, hs, a.splits);
+                a.s_out[((t / a.B) * (a.B - 1) + t % a.B) * R + c] = sv;
+            }
+        }
+    }
     __syncthreads();
 
     // ---- b = LN(u) per row; [b; g] as bf16 hi | lo rows in abuf

@@ -624,46 +624,6 @@ __device__ __forceinline__ float wave_sum64(float v) {
             __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 48)));
 }
 
-// The slot's projection partials, summed in split order (lane l holds
-// columns l and l + 64; r <= 128).
-struct SlotLoads {
-    float gv[2], sv[2];
-};
-
-__device__ __forceinline__ SlotLoads slot_state_load(const SlotArgs& a, int64_t t) {
-    SlotLoads o;
-    const int l = lane_id();
-    const int64_t hs = a.rows * a.hstride;
-    const bool pair = a.s_out != nullptr && (t % a.B) != a.B - 1;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int c = min(l + 64 * i, a.r - 1);  // clamped columns are not stored
-        o.gv[i] = sum_strided<kMaxSplits>(a.hproj + t * a.hstride + c, hs, a.splits);
-        o.sv[i] = 0.f;
-        if (pair)
-            o.sv[i] = sum_strided<kMaxSplits>(a.hproj + t * a.hstride + a.r + c, hs, a.splits) +
-                      sum_strided<kMaxSplits>(a.hproj + (t + 1) * a.hstride + 2 * a.r + c, hs, a.splits);
-    }
-    return o;
-}
-
-__device__ __forceinline__ void slot_state_finish(const SlotArgs& a, int64_t t, const SlotLoads& o) {
-    const int l = lane_id();
-    const bool ok0 = l < a.r, ok1 = l + 64 < a.r;
-    const float inv_r = 1.0f / static_cast<float>(a.r);
-    const float mean = wave_sum64((ok0 ? o.gv[0] : 0.f) + (ok1 ? o.gv[1] : 0.f)) * inv_r;
-    const float d0 = o.gv[0] - mean, d1 = o.gv[1] - mean;
-    const float var = wave_sum64((ok0 ? d0 * d0 : 0.f) + (ok1 ? d1 * d1 : 0.f)) * inv_r;
-    const float inv = 1.0f / sqrtf(var + a.eps);
-    if (ok0) a.g[t * a.r + l] = d0 * inv;
-    if (ok1) a.g[t * a.r + l + 64] = d1 * inv;
-    if (a.s_out != nullptr && (t % a.B) != a.B - 1) {
-        const int64_t p = (t / a.B) * (a.B - 1) + t % a.B;
-        if (ok0) a.s_out[p * a.r + l] = o.sv[0];
-        if (ok1) a.s_out[p * a.r + l + 64] = o.sv[1];
-    }
-}
-
 __global__ __launch_bounds__(256) void topk_merge_kernel(const uint64_t* __restrict__ part, int chunks,
                                                          int K, int kbits, int64_t rows,
                                                          int32_t* __restrict__ ids, float* __restrict__ vals) {
@@ -679,13 +639,6 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(const uint64_t* __restr
         return;
     wave_lds_sync();
     merge_row_wave(ent, M, K, sel_all[wave], fin_all[wave], ids + row * K, vals + row * K);
-}
-
-__global__ __launch_bounds__(256) void slot_state_kernel(SlotArgs sa) {
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + wave;
-    if (row >= sa.rows) return;
-    slot_state_finish(sa, row, slot_state_load(sa, row));
 }
 
 }  // namespace
@@ -711,8 +664,5 @@ hipError_t launch_topk_merge(int dtype, const uint64_t* part, int chunks, int K,
                   K, kbits, rows, ids, vals);
 }
 
-hipError_t launch_slot_state(const SlotArgs& sa, hipStream_t stream) {
-    return launch(slot_state_kernel, dim3(static_cast<unsigned>((sa.rows + 3) / 4)), 256, 0, stream, sa);
-}
 
 }  // namespace corr

@@ -37,8 +37,8 @@
  *     `stream` and before later work on it, also under stream capture.
  *   - A handle's weights are fixed after corrector_create; concurrent calls
  *     with one handle on different streams are safe when each uses its own
- *     workspace (a lock inside the handle serialises the fork/join of such
- *     calls; their projections then share the side stream).
+ *     workspace.  Every step of a call runs in order on the call's stream;
+ *     the library creates no streams of its own.
  *   - n_req = 0 is a no-op that returns CORR_OK; n_req > max_requests returns
  *     CORR_E_SHAPE.
  *   - Slots are the B drafted positions of a block (the anchor is not one of

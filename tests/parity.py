@@ -56,13 +56,17 @@ def dev_inputs(x: dict) -> dict:
     return _dev_cache[key][1]
 
 
-def gpu_run(x: dict, n: int | None = None, first: int = 0, reps: int = 1, fold: bool = False) -> dict:
+def gpu_run(x: dict, n: int | None = None, first: int = 0, reps: int = 1, fold: bool = False,
+            corr=None, ws=None) -> dict:
     """One corrector_run over blocks [first, first+n) with every output captured.
-    With fold=True the candidate projection reads the folded table E W_cand^T."""
+    With fold=True the candidate projection reads the folded table E W_cand^T.
+    `corr` and `ws` (optional) reuse a caller's handle and workspace."""
     cfg = x["cfg"]
     dev = dev_inputs(x)
     n = cfg["n"] - first if n is None else n
-    corr = device.make_corrector(cfg, dev, max_requests=max(n, 1))
+    own = corr is None
+    if own:
+        corr = device.make_corrector(cfg, dev, max_requests=max(n, 1))
     if fold:
         table = torch.empty(corr.table_bytes() // 4, dtype=torch.float32, device="cuda")
         corr.fold_table(table)
@@ -74,7 +78,8 @@ def gpu_run(x: dict, n: int | None = None, first: int = 0, reps: int = 1, fold: 
     ids = torch.empty((n, B, K), dtype=torch.int32, device="cuda")
     vals = torch.empty((n, B, K), dtype=torch.float32, device="cuda")
     scores = torch.empty((n, max(B - 1, 0), K, K), dtype=torch.float32, device="cuda")
-    ws = corr.new_workspace(n)
+    if ws is None:
+        ws = corr.new_workspace(n)
     for _ in range(reps):
         corr.run(n, dev["logits"], st["l_req"], st["l_slot"], dev["hidden"], st["h_req"], st["h_slot"],
                  tokens, ws, choice=choice, ids=ids, vals=vals, scores=scores,
@@ -87,7 +92,8 @@ def gpu_run(x: dict, n: int | None = None, first: int = 0, reps: int = 1, fold: 
     torch.cuda.synchronize()
     out = dict(tokens=tokens, choice=choice, ids=ids, vals=vals, scores=scores, z=z, g=g, s=s)
     out = {k: v.cpu().numpy() for k, v in out.items()}
-    corr.close()
+    if own:
+        corr.close()
     return out
 
 

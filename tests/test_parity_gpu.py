@@ -85,6 +85,25 @@ def test_b32_batch_invariance_and_determinism():
             np.testing.assert_array_equal(one[k], sub[k], err_msg="request %d alone: %s" % (i, k))
 
 
+def test_workspace_reuse_across_calls():
+    """One workspace serves a sequence of calls with different request counts
+    and repeated calls: each call's outputs equal those of a fresh workspace
+    (no state carries over from one call to the next)."""
+    _log("workspace reuse across calls")
+    from draft_correction_amd import device
+    for name, head in (("b32", "stress"), ("cosine", "normal")):
+        x = P.inputs(name, head=head)
+        cfg = x["cfg"]
+        corr = device.make_corrector(cfg, P.dev_inputs(x), max_requests=cfg["n"])
+        ws = corr.new_workspace(cfg["n"])
+        for n, first, reps in ((cfg["n"], 0, 3), (1, 17, 2), (5, 3, 1), (cfg["n"], 0, 1), (2, 30, 2)):
+            got = P.gpu_run(x, n=n, first=first, reps=reps, corr=corr, ws=ws)
+            want = P.gpu_run(x, n=n, first=first)
+            for k in ("ids", "vals", "scores", "tokens", "choice", "z", "s", "g"):
+                np.testing.assert_array_equal(got[k], want[k], err_msg="%s n=%d first=%d: %s" % (name, n, first, k))
+        corr.close()
+
+
 # ---------------------------------------------------------------- cosine --
 
 @pytest.mark.parametrize("sigma", [1.0, 8.0])
