@@ -245,6 +245,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmJob j0, GemmJob j1, int64
 // ------------------------------------------------------------------- cand --
 
 constexpr int kCR = 32;                 // candidate rows per workgroup
+constexpr int kCRT = (kCR + 15) / 16;   // 16-row MFMA tiles per workgroup
+constexpr int kCT = 512;                // threads of a candidate workgroup
+constexpr int kCW = kCT / kWave;        // its waves
+constexpr int kCRows = 4 * kCW;         // 16-lane rows it processes at a time
 
 // LayerNorm of one row of R values held by the 16 lanes of a DPP row, R/16
 // consecutive values per lane; statistics in float32, biased variance.
@@ -317,13 +321,41 @@ __device__ __forceinline__ f32x4 mfma_hilo_tile_w(const uint16_t* abuf, int as, 
     return acc;
 }
 
-__device__ __forceinline__ void split_store(uint16_t* row, int width, int c, float v) {
-    const uint16_t hi = f32_to_bf16(v);
-    row[c] = hi;
-    row[width + c] = f32_to_bf16(v - bf16_to_f32(hi));
+// Splits N float32 values into bf16 hi and lo parts (v ~ hi + lo to 2^-16).
+template <int N>
+__device__ __forceinline__ void split_hilo(const float (&v)[N], uint16_t (&hi)[N], uint16_t (&lo)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        hi[i] = f32_to_bf16(v[i]);
+        lo[i] = f32_to_bf16(v[i] - bf16_to_f32(hi[i]));
+    }
 }
 
-// U | V = [W1_za; W1_zb] z for the workgroup's M (<= 32) candidates, z as
+// Stores N consecutive bf16 values with the widest aligned stores (N * 2
+// bytes; dst is aligned to that size or to 16 bytes).
+template <int N>
+__device__ __forceinline__ void store_bf16s(uint16_t* dst, const uint16_t (&v)[N]) {
+    if constexpr (N % 8 == 0) {
+#pragma unroll
+        for (int j = 0; j < N / 8; ++j) {
+            u32x4 w;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                w[q] = static_cast<uint32_t>(v[8 * j + 2 * q]) | (static_cast<uint32_t>(v[8 * j + 2 * q + 1]) << 16);
+            *reinterpret_cast<u32x4*>(dst + 8 * j) = w;
+        }
+    } else if constexpr (N == 4) {
+        *reinterpret_cast<uint2*>(dst) = make_uint2(static_cast<uint32_t>(v[0]) | (static_cast<uint32_t>(v[1]) << 16),
+                                                   static_cast<uint32_t>(v[2]) | (static_cast<uint32_t>(v[3]) << 16));
+    } else if constexpr (N == 2) {
+        *reinterpret_cast<uint32_t*>(dst) = static_cast<uint32_t>(v[0]) | (static_cast<uint32_t>(v[1]) << 16);
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) dst[i] = v[i];
+    }
+}
+
+// U | V = [W1_za; W1_zb] z for the workgroup's M (<= kCR) candidates, z as
 // bf16 hi | lo rows in abuf (row stride as), written to uv [n0 + m][2h]: the
 // hi and lo halves meet the same W1 columns (those of z_p^a for U, of
 // z_{p+1}^b for V).  Wave w takes the 16-column tiles w, w + 4, ...; the W1
@@ -338,9 +370,9 @@ __device__ __forceinline__ void uv_tiles(const uint16_t* abuf, int as, int M, co
     const int kq = 8 * (l >> 4);
     const int m = l & 15;
     const u32x4 zero = {0u, 0u, 0u, 0u};
-    u32x4 af[2][KS];
+    u32x4 af[kCRT][KS];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < kCRT; ++rt)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
             af[rt][ks] = rt * 16 + m < M ? *reinterpret_cast<const u32x4*>(abuf + (rt * 16 + m) * as + ks * 32 + kq)
@@ -355,17 +387,17 @@ __device__ __forceinline__ void uv_tiles(const uint16_t* abuf, int as, int M, co
     };
     // three tiles' fragments in flight: tile c multiplies while c+1 and c+2 load
     constexpr int kDepth = 3;
-    constexpr int kMaxTiles = 512 / 16 / 4;   // 2h <= 512 columns over 4 waves
+    constexpr int kMaxTiles = 512 / 16 / kCW;   // 2h <= 512 columns over the waves
     u32x4 wf[kDepth][KS];
 #pragma unroll
-    for (int c = 0; c < kDepth - 1; ++c) wload(wave + 4 * c, wf[c]);
+    for (int c = 0; c < kDepth - 1; ++c) wload(wave + kCW * c, wf[c]);
 #pragma unroll
     for (int c = 0; c < kMaxTiles; ++c) {
-        const int ct = wave + 4 * c;
+        const int ct = wave + kCW * c;
         if (ct >= nct) break;
-        wload(ct + 4 * (kDepth - 1), wf[(c + kDepth - 1) % kDepth]);
+        wload(ct + kCW * (kDepth - 1), wf[(c + kDepth - 1) % kDepth]);
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
+        for (int rt = 0; rt < kCRT; ++rt) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(af[rt][ks], wf[c % kDepth][ks], acc);
@@ -378,7 +410,7 @@ __device__ __forceinline__ void uv_tiles(const uint16_t* abuf, int as, int M, co
     }
 }
 
-// One workgroup per 32 consecutive candidates (nodes) of the [rows][K] list:
+// One workgroup per kCR consecutive candidates (nodes) of the [rows][K] list:
 //   u = W_cand E[c]   the candidate GEMM's split partials summed in order (or
 //                     a row of the folded table when one is given)
 //   b = LN(u), g = LN(W_ctx h) for the candidate's slot (from hproj)
@@ -387,7 +419,7 @@ __device__ __forceinline__ void uv_tiles(const uint16_t* abuf, int as, int M, co
 //   cosine: unit(W_out z), unit(W_in z).
 // Loops over r are compile-time so each phase issues all of its loads at once.
 template <int R>
-__global__ __launch_bounds__(256) void cand_kernel(CandArgs a) {
+__global__ __launch_bounds__(kCT) void cand_kernel(CandArgs a) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     constexpr int NCT = R / 16;
     const int tid = threadIdx.x;
@@ -402,112 +434,125 @@ __global__ __launch_bounds__(256) void cand_kernel(CandArgs a) {
     uint16_t* abuf = reinterpret_cast<uint16_t*>(smem_raw + kCR * us * 4);  // [kCR][as]
     float* gs = reinterpret_cast<float*>(smem_raw + kCR * us * 4 + kCR * as * 2);  // [cand_slots(K)][R]
 
-    // ---- W_fuse fragments of this wave's column tiles (ct = wave + 4c),
+    // ---- W_fuse fragments of this wave's column tiles (ct = wave + kCW c),
     // issued first so they arrive with the u loads below
     constexpr int KSF = (2 * (2 * R) + 31) / 32;
-    constexpr int CPW = (NCT + 3) / 4;
+    constexpr int CPW = (NCT + kCW - 1) / kCW;
     u32x4 wfr[CPW][KSF];
     {
         const int kq = 8 * (l >> 4);
 #pragma unroll
         for (int c = 0; c < CPW; ++c) {
-            const int ct = min(wave + 4 * c, NCT - 1);  // clamped tiles are not used
+            const int ct = min(wave + kCW * c, NCT - 1);  // clamped tiles are not used
             const uint16_t* wp = a.w_fuse + static_cast<int64_t>(ct * 16 + (l & 15)) * (2 * R);
 #pragma unroll
             for (int ks = 0; ks < KSF; ++ks) wfr[c][ks] = load16(wp + ((ks * 32 + kq) % (2 * R)));
         }
     }
 
-    // ---- u: a row of the folded table, or the candidate GEMM's split partials
-    // (four consecutive columns per thread and load)
-    {
-        constexpr int PER4 = (kCR * R / 4 + 255) / 256;
-        float4 uv[PER4];
-#pragma unroll
-        for (int q = 0; q < PER4; ++q) {
-            const int e = (tid + 256 * q) * 4;
-            const int m = min(e / R, M - 1), c = e % R;  // rows past M are not stored
-            if (a.table) {
-                int64_t tok = a.ids[n0 + m];
-                tok = tok < 0 ? 0 : (tok >= a.V ? a.V - 1 : tok);
-                uv[q] = *reinterpret_cast<const float4*>(a.table + tok * R + c);
-            } else {
-                const float* base = a.upart + (n0 + m) * R + c;
-                float4 t[kMaxUSplits];
-#pragma unroll
-                for (int i = 0; i < kMaxUSplits; ++i)
-                    t[i] = *reinterpret_cast<const float4*>(base + (i < a.usplits ? i : a.usplits - 1) * nodes * R);
-                float4 sum = t[0];
-#pragma unroll
-                for (int i = 1; i < kMaxUSplits; ++i)
-                    if (i < a.usplits) sum = make_float4(sum.x + t[i].x, sum.y + t[i].y, sum.z + t[i].z, sum.w + t[i].w);
-                uv[q] = sum;
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < PER4; ++q) {
-            const int e = (tid + 256 * q) * 4;
-            if (e / R < M) *reinterpret_cast<float4*>(ubuf + (e / R) * us + e % R) = uv[q];
-        }
-    }
     // nodes < 2^30 (rows <= 2^24, K <= 64): 32-bit slot arithmetic
     const int n0i = static_cast<int>(n0);
     const int t0 = n0i / a.K;
     const int nslot = (n0i + M - 1) / a.K - t0 + 1;
-    // Rows are processed 16 lanes each (4 per wave, 16 per pass of the
+    const int64_t hs = a.rows * a.hstride;
+
+    // ---- u: a row of the folded table, or the candidate GEMM's split
+    // partials (four consecutive columns per thread and load).  The loads are
+    // only issued here; they are summed after the slot-state loads below have
+    // been issued too, so all of the prologue's memory latency overlaps.
+    constexpr int PER4 = (kCR * R / 4 + kCT - 1) / kCT;
+    float4 ut[PER4][kMaxUSplits];
+#pragma unroll
+    for (int q = 0; q < PER4; ++q) {
+        const int e = (tid + kCT * q) * 4;
+        const int m = min(e / R, M - 1), c = e % R;  // rows past M are not stored
+        if (a.table) {
+            int64_t tok = a.ids[n0 + m];
+            tok = tok < 0 ? 0 : (tok >= a.V ? a.V - 1 : tok);
+            ut[q][0] = *reinterpret_cast<const float4*>(a.table + tok * R + c);
+        } else {
+            const float* base = a.upart + (n0 + m) * R + c;
+#pragma unroll
+            for (int i = 0; i < kMaxUSplits; ++i)
+                ut[q][i] = *reinterpret_cast<const float4*>(base + (i < a.usplits ? i : a.usplits - 1) * nodes * R);
+        }
+    }
+
+    // ---- per-slot state from the hidden-state projection partials, each
+    // value summed in split order, spread over all threads: W_ctx h of the
+    // group's slots (into gs, normalised below) and, for the slots whose first
+    // candidate the group holds, g_t (published below) and the pair state
+    // s_t = W_pair,L h_t + W_pair,R h_{t+1}
+    for (int idx = tid; idx < nslot * R; idx += kCT) {
+        const int sl = idx / R, c = idx % R;
+        const int64_t t = t0 + sl;
+        const float* hp = a.hproj + t * a.hstride;
+        const bool pair = a.s_out && t * a.K >= n0 && (t % a.B) != a.B - 1;
+        const float gv = sum_strided<kMaxSplits>(hp + c, hs, a.splits);
+        if (pair) {
+            const float sv = sum_strided<kMaxSplits>(hp + R + c, hs, a.splits) +
+                             sum_strided<kMaxSplits>(hp + a.hstride + 2 * R + c, hs, a.splits);
+            a.s_out[((t / a.B) * (a.B - 1) + t % a.B) * R + c] = sv;
+        }
+        gs[idx] = gv;
+    }
+
+    // ---- u sums (split order) into ubuf
+#pragma unroll
+    for (int q = 0; q < PER4; ++q) {
+        const int e = (tid + kCT * q) * 4;
+        float4 sum = ut[q][0];
+        if (!a.table) {
+#pragma unroll
+            for (int i = 1; i < kMaxUSplits; ++i)
+                if (i < a.usplits)
+                    sum = make_float4(sum.x + ut[q][i].x, sum.y + ut[q][i].y, sum.z + ut[q][i].z, sum.w + ut[q][i].w);
+        }
+        if (e / R < M) *reinterpret_cast<float4*>(ubuf + (e / R) * us + e % R) = sum;
+    }
+    __syncthreads();
+
+    // Rows are processed 16 lanes each (4 per wave, kCRows per pass of the
     // workgroup): lane c16 = l & 15 holds columns c16*VPL .. c16*VPL+VPL-1.
     constexpr int VPL = R / 16;
     const int c16 = l & 15;
-    const int rsub = wave * 4 + (l >> 4);   // 0..15
-    // ---- g = LN(W_ctx h) of the group's slots (consecutive), from the
-    // projection partials summed in split order; slot rows take 16 lanes each
-    {
-        const int64_t hs = a.rows * a.hstride;
-        for (int sl = rsub; sl < nslot; sl += 16) {
-            const int64_t t = t0 + sl;
-            float gv[VPL];
+    const int rsub = wave * 4 + (l >> 4);   // 0..kCRows-1
+    // ---- g = LN(W_ctx h) of the group's slots, in place; the workgroup
+    // holding a slot's first candidate publishes g_t
+    for (int sl = rsub; sl < nslot; sl += kCRows) {
+        const int64_t t = t0 + sl;
+        float gv[VPL];
 #pragma unroll
-            for (int i = 0; i < VPL; ++i)
-                gv[i] = sum_strided<kMaxSplits>(a.hproj + t * a.hstride + c16 * VPL + i, hs, a.splits);
-            row16_layernorm<R>(gv, a.eps);
-            // the workgroup holding the slot's first candidate publishes g_t
-            const bool owner = static_cast<int64_t>(t) * a.K >= n0;
+        for (int i = 0; i < VPL; ++i) gv[i] = gs[sl * R + c16 * VPL + i];
+        row16_layernorm<R>(gv, a.eps);
+        const bool owner = t * a.K >= n0;
 #pragma unroll
-            for (int i = 0; i < VPL; ++i) {
-                gs[sl * R + c16 * VPL + i] = gv[i];
-                if (owner) a.g_out[t * R + c16 * VPL + i] = gv[i];
-            }
-        }
-        // ---- pair state s_t = W_pair,L h_t + W_pair,R h_{t+1} for the slots
-        // whose first candidate this workgroup holds (each sum in split order)
-        if (a.s_out) {
-            for (int idx = tid; idx < nslot * R; idx += 256) {
-                const int sl = idx / R, c = idx % R;
-                const int64_t t = t0 + sl;
-                if (t * a.K < n0 || (t % a.B) == a.B - 1) continue;
-                const float* hp = a.hproj + t * a.hstride;
-                const float sv = sum_strided<kMaxSplits>(hp + R + c, hs, a.splits) +
-                                 sum_strided<kMaxSplits>(hp + a.hstride + 2 * R + c, hs, a.splits);
-                a.s_out[((t / a.B) * (a.B - 1) + t % a.B) * R + c] = sv;
-            }
+        for (int i = 0; i < VPL; ++i) {
+            gs[sl * R + c16 * VPL + i] = gv[i];
+            if (owner) a.g_out[t * R + c16 * VPL + i] = gv[i];
         }
     }
     __syncthreads();
 
     // ---- b = LN(u) per row; [b; g] as bf16 hi | lo rows in abuf
-    for (int m = rsub; m < M; m += 16) {
+    for (int m = rsub; m < M; m += kCRows) {
         float bv[VPL];
 #pragma unroll
         for (int i = 0; i < VPL; ++i) bv[i] = ubuf[m * us + c16 * VPL + i];
         row16_layernorm<R>(bv, a.eps);
         const int sl = (n0i + m) / a.K - t0;
-        uint16_t* arow = abuf + m * as;
+        float gv[VPL];
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-            const int c = c16 * VPL + i;
-            split_store(arow, 2 * R, c, bv[i]);
-            split_store(arow, 2 * R, R + c, gs[sl * R + c]);
-        }
+        for (int i = 0; i < VPL; ++i) gv[i] = gs[sl * R + c16 * VPL + i];
+        // row layout [b hi | g hi | b lo | g lo], each R wide
+        uint16_t* arow = abuf + m * as + c16 * VPL;
+        uint16_t hi[VPL], lo[VPL];
+        split_hilo<VPL>(bv, hi, lo);
+        store_bf16s<VPL>(arow, hi);
+        store_bf16s<VPL>(arow + 2 * R, lo);
+        split_hilo<VPL>(gv, hi, lo);
+        store_bf16s<VPL>(arow + R, hi);
+        store_bf16s<VPL>(arow + 3 * R, lo);
     }
     __syncthreads();
 
@@ -515,7 +560,7 @@ __global__ __launch_bounds__(256) void cand_kernel(CandArgs a) {
     const int nrt = (M + 15) / 16;
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
-        const int ct = wave + 4 * c;
+        const int ct = wave + kCW * c;
         if (ct >= NCT) break;
         for (int rt = 0; rt < nrt; ++rt) {
             const f32x4 acc = mfma_hilo_tile_w<2 * R>(abuf + rt * 16 * as, as, M - rt * 16, wfr[c]);
@@ -526,23 +571,25 @@ __global__ __launch_bounds__(256) void cand_kernel(CandArgs a) {
     __syncthreads();
 
     // ---- z = gamma * LN(y) + beta; stored as bf16 hi | lo (and kept in abuf)
-    for (int m = rsub; m < M; m += 16) {
+    for (int m = rsub; m < M; m += kCRows) {
         float zv[VPL];
 #pragma unroll
         for (int i = 0; i < VPL; ++i) zv[i] = ubuf[m * us + c16 * VPL + i];
         row16_layernorm<R>(zv, a.eps);
-        uint16_t* grow = a.zhl + (n0 + m) * (2 * R);
+        uint16_t* grow = a.zhl + (n0 + m) * (2 * R) + c16 * VPL;
+        uint16_t* arow = abuf + m * as + c16 * VPL;
 #pragma unroll
         for (int i = 0; i < VPL; ++i) {
             const int c = c16 * VPL + i;
-            const float z = fmaf(a.gamma[c], zv[i], a.beta[c]);
-            const uint16_t hi = f32_to_bf16(z);
-            const uint16_t lo = f32_to_bf16(z - bf16_to_f32(hi));
-            grow[c] = hi;
-            grow[R + c] = lo;
-            abuf[m * as + c] = hi;
-            abuf[m * as + R + c] = lo;
+            zv[i] = fmaf(a.gamma[c], zv[i], a.beta[c]);
         }
+        // z as [hi | lo] rows, in memory and in abuf
+        uint16_t hi[VPL], lo[VPL];
+        split_hilo<VPL>(zv, hi, lo);
+        store_bf16s<VPL>(grow, hi);
+        store_bf16s<VPL>(grow + R, lo);
+        store_bf16s<VPL>(arow, hi);
+        store_bf16s<VPL>(arow + R, lo);
     }
     if (a.uv) {
         // ---- MLP variant: the per-candidate layer-1 products U | V of z
@@ -557,7 +604,7 @@ __global__ __launch_bounds__(256) void cand_kernel(CandArgs a) {
     const int dv = a.dvec;
     const int nvt = dv / 16;
     for (int which = 0; which < 2; ++which) {
-        for (int job = wave; job < nrt * nvt; job += 4) {
+        for (int job = wave; job < nrt * nvt; job += kCW) {
             const int rt = job / nvt, ct = job % nvt;
             const f32x4 acc = mfma_hilo_tile<R>(abuf + rt * 16 * as, as, M - rt * 16, which ? a.w_in : a.w_out, R,
                                                 ct * 16);
@@ -565,7 +612,7 @@ __global__ __launch_bounds__(256) void cand_kernel(CandArgs a) {
             for (int i = 0; i < 4; ++i) ubuf[(rt * 16 + 4 * (l >> 4) + i) * us + ct * 16 + (l & 15)] = acc[i];
         }
         __syncthreads();
-        for (int m = rsub; m < M; m += 16) {
+        for (int m = rsub; m < M; m += kCRows) {
             // dv = 16 * (dv / 16) columns, dv / 16 per lane of the row
             const int vpl = dv / 16;
             const float* v = ubuf + m * us + c16 * vpl;
@@ -608,10 +655,10 @@ hipError_t launch_cand(const CandArgs& a, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>((nodes + kCR - 1) / kCR));
     const size_t lds = cand_lds_bytes(a.r, a.vout ? a.dvec : 0, a.K);
     switch (a.r) {
-        case 16: return launch(cand_kernel<16>, grid, 256, lds, stream, a);
-        case 32: return launch(cand_kernel<32>, grid, 256, lds, stream, a);
-        case 64: return launch(cand_kernel<64>, grid, 256, lds, stream, a);
-        case 128: return launch(cand_kernel<128>, grid, 256, lds, stream, a);
+        case 16: return launch(cand_kernel<16>, grid, kCT, lds, stream, a);
+        case 32: return launch(cand_kernel<32>, grid, kCT, lds, stream, a);
+        case 64: return launch(cand_kernel<64>, grid, kCT, lds, stream, a);
+        case 128: return launch(cand_kernel<128>, grid, kCT, lds, stream, a);
         default: return hipErrorInvalidValue;
     }
 }
