@@ -72,6 +72,10 @@ def algorithmic_work(cfg: dict, n: int) -> dict:
                           flops=w["cand_gemm"]["flops"] + w["hproj"]["flops"],
                           per_unit=de * 2, units=rows * K + rows,
                           unit="gathered embedding row or hidden row (d_e = d)")
+    # one launch: the top-K merge and the hidden-state projection side by side
+    w["topk_merge_hproj"] = dict(bound="hbm", bytes=w["topk_merge"]["bytes"] + w["hproj"]["bytes"],
+                                 flops=w["hproj"]["flops"], per_unit=d * 2, units=rows,
+                                 unit="slot row (K winners out; hidden row projected)")
     # the MLP variant's candidate kernel also writes U | V = [W1_za; W1_zb] z
     uvb = 2 * h * 4 if cfg["variant"] == "mlp" else 0
     w["cand"] = dict(bound="hbm", bytes=rows * K * (r * 4 * 2 + uvb),

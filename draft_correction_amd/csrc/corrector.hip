@@ -4,7 +4,6 @@
 // never allocates device memory and never synchronises (except
 // corrector_kernel_times, which waits for timing events by design).
 #include <math.h>
-#include <functional>
 #include <mutex>
 #include <new>
 #include <string.h>
@@ -169,9 +168,10 @@ struct Seq {
     }
 };
 
-// Step (1).
+// Step (1).  With `hj` given, the hidden-state projection runs in the merge
+// launch (it does not depend on the top-K).
 void enqueue_topk(Seq& q, const corrector* h, const Layout& L, int32_t n, const void* logits,
-                  int64_t rs, int64_t ss, int32_t* ids, float* vals, void* ws) {
+                  int64_t rs, int64_t ss, int32_t* ids, float* vals, void* ws, const GemmJob* hj) {
     const corrector_desc& d = h->d;
     const int64_t rows = static_cast<int64_t>(n) * d.slots;
     uint64_t* part = at<uint64_t>(ws, L.part);
@@ -179,25 +179,18 @@ void enqueue_topk(Seq& q, const corrector* h, const Layout& L, int32_t n, const 
         return launch_topk_partial(d.logits_dtype, logits, rs, ss, d.slots, d.vocab, d.k, L.chunks,
                                    rows, part, q.s);
     });
-    q("topk_merge", [&] { return launch_topk_merge(d.logits_dtype, part, L.chunks, d.k, rows, ids, vals, q.s); });
+    q(hj ? "topk_merge_hproj" : "topk_merge",
+      [&] { return launch_topk_merge(d.logits_dtype, part, L.chunks, d.k, rows, ids, vals, hj, q.s); });
 }
 
-// Steps (2)-(4); with tokens given also step (5) (fused into the MLP finish
-// for the MLP variant, a walk launch for the cosine variant).
-// `pre` (optional) enqueues work ahead of the projections on the same stream
-// (corrector_run puts the top-K there).  Everything runs in order on the
-// call's stream: the hidden-state projection shares one GEMM launch with the
-// candidate projection, and the candidate kernel forms the per-slot state.
-void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const int32_t* ids,
-                   const float* vals, const void* hidden, int64_t hrs, int64_t hss, float* scores,
-                   void* ws, int32_t* tokens, int32_t* choice, const std::function<void()>& pre) {
+// The hidden-state projection: hproj rows are [W_ctx h | W_pair,L h |
+// W_pair,R h] (3r wide); the cosine variant has no pair state and computes the
+// W_ctx block alone (r wide).
+GemmJob hproj_job(const corrector* h, const Layout& L, int32_t n, const void* hidden, int64_t hrs, int64_t hss,
+                  void* ws) {
     const corrector_desc& d = h->d;
     const corrector_weights& w = h->w;
-    const int64_t rows = static_cast<int64_t>(n) * d.slots;
-    float* hproj = at<float>(ws, L.hproj);
     const bool cos = d.variant == CORR_VARIANT_COSINE;
-    // hproj rows: [W_ctx h | W_pair,L h | W_pair,R h] (3r wide); the cosine
-    // variant has no pair state and computes the W_ctx block alone (r wide).
     GemmJob hj{};
     hj.A.mode = GEMM_A_SLOTS;
     hj.A.base = static_cast<const uint16_t*>(hidden);
@@ -212,14 +205,30 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
         hj.W.base[2] = static_cast<const uint16_t*>(w.w_pair) + d.d_hidden;
         hj.W.ld[1] = hj.W.ld[2] = 2 * static_cast<int64_t>(d.d_hidden);
     }
-    const int hn = cos ? d.r : 3 * d.r;
-    hj.M = rows;
-    hj.N = hn;
+    hj.M = static_cast<int64_t>(n) * d.slots;
+    hj.N = cos ? d.r : 3 * d.r;
     hj.kdim = d.d_hidden;
     hj.splits = L.splits;
-    hj.C = hproj;
+    hj.C = at<float>(ws, L.hproj);
+    return hj;
+}
+
+// Steps (2)-(4); with tokens given also step (5) (fused into the MLP finish
+// for the MLP variant, a walk launch for the cosine variant).  Everything runs
+// in order on the call's stream.  When `hproj_done` is false the hidden-state
+// projection shares one GEMM launch with the candidate projection; otherwise
+// an earlier launch of the call has produced it.
+void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const int32_t* ids,
+                   const float* vals, const void* hidden, int64_t hrs, int64_t hss, float* scores,
+                   void* ws, int32_t* tokens, int32_t* choice, bool hproj_done) {
+    const corrector_desc& d = h->d;
+    const corrector_weights& w = h->w;
+    const int64_t rows = static_cast<int64_t>(n) * d.slots;
+    float* hproj = at<float>(ws, L.hproj);
+    const bool cos = d.variant == CORR_VARIANT_COSINE;
+    const GemmJob hj = hproj_job(h, L, n, hidden, hrs, hss, ws);
+    const int hn = hj.N;
     const bool mlp_pairs = !cos && d.slots > 1;
-    if (pre) pre();
     float* upart = at<float>(ws, L.upart);
     if (!h->table) {
         // the candidate projection u = W_cand E[c] first (longer workgroups),
@@ -238,8 +247,12 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
         uj.kdim = d.d_embed;
         uj.splits = L.usplits;
         uj.C = upart;
-        q("proj_gemm", [&] { return launch_gemm2(uj, hj, q.s); });
-    } else {
+        if (hproj_done) {
+            q("cand_gemm", [&] { return launch_gemm(uj.A, uj.W, uj.M, uj.N, uj.kdim, uj.splits, uj.C, q.s); });
+        } else {
+            q("proj_gemm", [&] { return launch_gemm2(uj, hj, q.s); });
+        }
+    } else if (!hproj_done) {
         q("hproj", [&] { return launch_gemm(hj.A, hj.W, hj.M, hj.N, hj.kdim, hj.splits, hj.C, q.s); });
     }
     CandArgs ca{};
@@ -407,7 +420,7 @@ int corrector_topk(const corrector* hc, int32_t n, const void* logits, int64_t r
     std::unique_lock<std::mutex> lock(h->mu, std::defer_lock);
     if (h->timing) lock.lock();
     Seq q{h, static_cast<hipStream_t>(stream)};
-    enqueue_topk(q, h, L, n, logits, rs, ss, ids, vals, ws);
+    enqueue_topk(q, h, L, n, logits, rs, ss, ids, vals, ws, nullptr);
     return q.finish();
 }
 
@@ -425,7 +438,7 @@ int corrector_score(const corrector* hc, int32_t n, const int32_t* ids, const fl
     std::unique_lock<std::mutex> lock(h->mu, std::defer_lock);
     if (h->timing) lock.lock();
     Seq q{h, static_cast<hipStream_t>(stream)};
-    enqueue_score(q, h, L, n, ids, vals, hidden, hrs, hss, scores, ws, nullptr, nullptr, nullptr);
+    enqueue_score(q, h, L, n, ids, vals, hidden, hrs, hss, scores, ws, nullptr, nullptr, false);
     return q.finish();
 }
 
@@ -460,8 +473,9 @@ int corrector_run(const corrector* hc, int32_t n, const void* logits, int64_t lr
     std::unique_lock<std::mutex> lock(h->mu, std::defer_lock);
     if (h->timing) lock.lock();
     Seq q{h, static_cast<hipStream_t>(stream)};
-    enqueue_score(q, h, L, n, ids, vals, hidden, hrs, hss, scores, ws, tokens, choice_or_null,
-                  [&] { enqueue_topk(q, h, L, n, logits, lrs, lss, ids, vals, ws); });
+    const GemmJob hj = hproj_job(h, L, n, hidden, hrs, hss, ws);
+    enqueue_topk(q, h, L, n, logits, lrs, lss, ids, vals, ws, &hj);
+    enqueue_score(q, h, L, n, ids, vals, hidden, hrs, hss, scores, ws, tokens, choice_or_null, true);
     return q.finish();
 }
 

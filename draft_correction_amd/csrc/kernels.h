@@ -45,10 +45,6 @@ int topk_chunk_elems(int dtype);
 hipError_t launch_topk_partial(int dtype, const void* logits, int64_t req_stride,
                                int64_t slot_stride, int B, int64_t V, int K, int chunks,
                                int64_t rows, uint64_t* part, hipStream_t stream);
-// The K winners of every row, in order, from the chunks' composites.
-hipError_t launch_topk_merge(int dtype, const uint64_t* part, int chunks, int K, int64_t rows, int32_t* ids,
-                             float* vals, hipStream_t stream);
-
 // ---- projections (proj.hip)
 // Tiled GEMM C[split][m][n] = sum_k A[m][k] W[n][k] (bf16 in, float32 out).
 #define GEMM_A_DENSE 0
@@ -83,6 +79,13 @@ struct GemmJob {
 hipError_t launch_gemm(const GemmA& A, const GemmW& W, int64_t M, int N, int kdim, int splits, float* C,
                        hipStream_t stream);
 hipError_t launch_gemm2(const GemmJob& j0, const GemmJob& j1, hipStream_t stream);
+// Workgroups a GEMM job occupies in a launch.
+int64_t gemm_launch_blocks(const GemmJob& j);
+
+// The K winners of every row, in order, from the chunks' composites; with a
+// GEMM job given, its tiles run in the same launch (after the merge waves).
+hipError_t launch_topk_merge(int dtype, const uint64_t* part, int chunks, int K, int64_t rows, int32_t* ids,
+                             float* vals, const GemmJob* hj, hipStream_t stream);
 
 // Per drafted slot: b = LN(u) with u = W_cand E[ids], g = LN(W_ctx h) per slot,
 // z = gamma * LN(W_fuse [b; g]) + beta stored as bfloat16 hi/lo halves

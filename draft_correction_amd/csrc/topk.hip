@@ -22,6 +22,7 @@
 // Keys map float bits to an unsigned integer order with -0 == +0, so the
 // selection is exact integer work: results are bit-identical to a full sort.
 #include "common.h"
+#include "gemm.h"
 #include "kernels.h"
 
 namespace corr {
@@ -624,21 +625,40 @@ __device__ __forceinline__ float wave_sum64(float v) {
             __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 48)));
 }
 
+// The merge of one row by one wave: the K winners of the row's chunk
+// candidates, in order.  `sel` and `fin` are the wave's LDS lists.
+__device__ __forceinline__ void merge_row(const uint64_t* __restrict__ part, int chunks, int K, int kbits, int64_t row,
+                                          uint64_t* sel, uint64_t* fin, int32_t* __restrict__ ids,
+                                          float* __restrict__ vals) {
+    const int M = chunks * K;
+    const uint64_t* ent = part + row * M;
+    if (M <= kMergePer * kWave && merge_row_fast(ent, M, K, kbits, sel, fin, ids + row * K, vals + row * K))
+        return;
+    wave_lds_sync();
+    merge_row_wave(ent, M, K, sel, fin, ids + row * K, vals + row * K);
+}
+
+// Workgroups [0, nmerge) merge four rows each (one per wave); with a GEMM job
+// given, the workgroups after them run its tiles (the hidden-state
+// projection, which does not depend on the top-K and fills the machine while
+// the few merge waves run).  Both paths take their LDS from one buffer.
 __global__ __launch_bounds__(256) void topk_merge_kernel(const uint64_t* __restrict__ part, int chunks,
                                                          int K, int kbits, int64_t rows,
-                                                         int32_t* __restrict__ ids, float* __restrict__ vals) {
-    __shared__ uint64_t sel_all[4][kMergeCap + kWave];
-    __shared__ uint64_t fin_all[4][2 * kWave];
+                                                         int32_t* __restrict__ ids, float* __restrict__ vals,
+                                                         int64_t nmerge, GemmJob hj) {
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kGemmSmem];
+    static_assert(4 * (kMergeCap + kWave) * 8 + 4 * 2 * kWave * 8 <= kGemmSmem, "merge lists fit the GEMM's LDS");
+    if (static_cast<int64_t>(blockIdx.x) >= nmerge) {
+        gemm_body(hj, static_cast<int64_t>(blockIdx.x) - nmerge, smem);
+        return;
+    }
+    uint64_t (*sel_all)[kMergeCap + kWave] = reinterpret_cast<uint64_t (*)[kMergeCap + kWave]>(smem);
+    uint64_t (*fin_all)[2 * kWave] =
+        reinterpret_cast<uint64_t (*)[2 * kWave]>(smem + 4 * (kMergeCap + kWave) * sizeof(uint64_t));
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + wave;
     if (row >= rows) return;
-    const int M = chunks * K;
-    const uint64_t* ent = part + row * M;
-    if (M <= kMergePer * kWave &&
-        merge_row_fast(ent, M, K, kbits, sel_all[wave], fin_all[wave], ids + row * K, vals + row * K))
-        return;
-    wave_lds_sync();
-    merge_row_wave(ent, M, K, sel_all[wave], fin_all[wave], ids + row * K, vals + row * K);
+    merge_row(part, chunks, K, kbits, row, sel_all[wave], fin_all[wave], ids, vals);
 }
 
 }  // namespace
@@ -658,10 +678,14 @@ hipError_t launch_topk_partial(int dtype, const void* logits, int64_t req_stride
 }
 
 hipError_t launch_topk_merge(int dtype, const uint64_t* part, int chunks, int K, int64_t rows, int32_t* ids,
-                             float* vals, hipStream_t stream) {
+                             float* vals, const GemmJob* hj, hipStream_t stream) {
     const int kbits = dtype == CORR_DT_BF16 ? 16 : 32;
-    return launch(topk_merge_kernel, dim3(static_cast<unsigned>((rows + 3) / 4)), 256, 0, stream, part, chunks,
-                  K, kbits, rows, ids, vals);
+    const int64_t nmerge = (rows + 3) / 4;
+    GemmJob none{};
+    const GemmJob& j = hj ? *hj : none;
+    const int64_t ng = hj ? gemm_launch_blocks(*hj) : 0;
+    return launch(topk_merge_kernel, dim3(static_cast<unsigned>(nmerge + ng)), 256, 0, stream, part, chunks, K,
+                  kbits, rows, ids, vals, nmerge, j);
 }
 
 
