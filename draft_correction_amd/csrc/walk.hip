@@ -48,6 +48,61 @@ __device__ void walk_wave(const float* src, const int32_t* __restrict__ ids, int
     }
 }
 
+// The walk of one request from its scores held in LDS (sS, [B-1][K][K]) by
+// the whole workgroup: first every row's argmax at once (one row per thread,
+// scanning in index order with a strict compare, so ties go to the lowest
+// successor index) into best[p][a]; then one lane follows the chain
+// k_1 = 0, k_{p+1} = best[p][k_p] (B - 1 dependent byte reads); then lanes
+// s < B write choice[s] and gather tokens[s] = ids[s][k_s].  Every thread of
+// the workgroup calls it.
+__device__ void walk_block(const float* sS, uint8_t* best, int* chain, const int32_t* __restrict__ ids, int req,
+                           int B, int K, int32_t* __restrict__ tokens, int32_t* __restrict__ choice) {
+    const int nrows = (B - 1) * K;
+    for (int r = threadIdx.x; r < nrows; r += blockDim.x) {
+        const float* row = sS + r * K;
+        float bv = row[0];
+        int bi = 0;
+        if ((K & 3) == 0) {   // rows are 16-byte aligned
+            for (int b4 = 0; b4 < K / 4; ++b4) {
+                const float4 v = reinterpret_cast<const float4*>(row)[b4];
+                if (v.x > bv) { bv = v.x; bi = 4 * b4; }
+                if (v.y > bv) { bv = v.y; bi = 4 * b4 + 1; }
+                if (v.z > bv) { bv = v.z; bi = 4 * b4 + 2; }
+                if (v.w > bv) { bv = v.w; bi = 4 * b4 + 3; }
+            }
+        } else {
+            for (int b = 1; b < K; ++b)
+                if (row[b] > bv) { bv = row[b]; bi = b; }
+        }
+        best[r] = static_cast<uint8_t>(bi);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int k = 0;
+        chain[0] = 0;
+        for (int p = 0; p + 1 < B; ++p) {
+            k = best[p * K + k];
+            chain[p + 1] = k;
+        }
+    }
+    __syncthreads();
+    for (int t = threadIdx.x; t < B; t += blockDim.x) {
+        const int64_t s = static_cast<int64_t>(req) * B + t;
+        const int ch = chain[t];
+        if (choice) choice[s] = ch;
+        tokens[s] = ids[s * K + ch];
+    }
+}
+
+// LDS layout of a walk with its scores in LDS: the scores, then best
+// ([B-1][K] bytes), then chain ([B] ints, 4-byte aligned).
+__host__ __device__ inline size_t walk_best_offset(int B, int K) {
+    return static_cast<size_t>(B - 1) * K * K * sizeof(float);
+}
+__host__ __device__ inline size_t walk_chain_offset(int B, int K) {
+    return (walk_best_offset(B, K) + static_cast<size_t>(B - 1) * K + 3) / 4 * 4;
+}
+
 // Walk over precomputed scores, one wave per request.  When the request's
 // scores fit (use_lds) they are first copied into LDS with coalesced 16-byte
 // loads, all issued before any is used, so the dependent steps read LDS.
@@ -82,7 +137,13 @@ __global__ __launch_bounds__(64) void walk_kernel(const float* __restrict__ scor
         }
         wave_lds_sync();
     }
-    walk_wave(use_lds ? sl : base, ids, req, B, K, tokens, choice);
+    if (use_lds) {
+        walk_block(sl, reinterpret_cast<uint8_t*>(reinterpret_cast<char*>(sl) + walk_best_offset(B, K)),
+                   reinterpret_cast<int*>(reinterpret_cast<char*>(sl) + walk_chain_offset(B, K)), ids, req, B, K,
+                   tokens, choice);
+        return;
+    }
+    walk_wave(base, ids, req, B, K, tokens, choice);
 }
 
 // One workgroup per request: S = l_{p+1}(b) + (sum of the hidden-block partial
@@ -156,8 +217,14 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a, int use_lds) 
     }
     if (!a.tokens) return;
     __syncthreads();
+    if (use_lds) {
+        walk_block(sS, reinterpret_cast<uint8_t*>(reinterpret_cast<char*>(sS) + walk_best_offset(B, K)),
+                   reinterpret_cast<int*>(reinterpret_cast<char*>(sS) + walk_chain_offset(B, K)), a.ids, req, B,
+                   K, a.tokens, a.choice);
+        return;
+    }
     if ((threadIdx.x >> 6) != 0) return;
-    walk_wave(use_lds ? sS : a.scores + req * per, a.ids, req, B, K, a.tokens, a.choice);
+    walk_wave(a.scores + req * per, a.ids, req, B, K, a.tokens, a.choice);
 }
 
 // z = hi + lo for each node row of the [hi | lo] layout.
@@ -189,9 +256,12 @@ hipError_t launch_cosine(const CosArgs& a, hipStream_t stream) {
     return launch(cosine_kernel, dim3(static_cast<unsigned>(a.n * (a.B - 1))), 256, 0, stream, a);
 }
 
+// Dynamic LDS of a walk that holds the request's scores (and the walk's
+// best and chain arrays), or 0 when they do not fit and the walk reads memory.
 static size_t walk_lds_bytes(int B, int K) {
-    const size_t bytes = static_cast<size_t>(B > 1 ? B - 1 : 0) * K * K * sizeof(float);
-    return (bytes > 0 && bytes <= 60 * 1024) ? bytes : 0;
+    if (B < 2) return 0;
+    const size_t bytes = walk_chain_offset(B, K) + sizeof(int) * B;
+    return bytes <= 60 * 1024 ? bytes : 0;
 }
 
 hipError_t launch_walk(const float* scores, const int32_t* ids, int n, int B, int K,
