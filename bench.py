@@ -28,9 +28,12 @@ METRIC = "corrected draft blocks/s at batch 32 (V=151936,B=16,K=16); % HBM/MFMA 
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 # vector-ALU ceiling for GELU evaluations: 256 CUs x 64 lanes x 2.4 GHz =
-# 39.3 T lane-instructions/s (no packed FP32), at 16 instruction slots per GELU
-# plus 2 x 3 extra slots for its two quarter-rate transcendentals (22 slots)
-PEAK_GELU_T = 256 * 64 * 2.4e9 / 22 / 1e12
+# 39.3 T lane-instructions/s (no packed FP32), at 13 instructions per
+# evaluation in the MLP's inner loop (the add of P and Q, 9 for the GELU
+# itself, the w2 multiply-add, and the two transcendentals v_rcp_f32 and
+# v_exp_f32) plus 2 x 3 extra slots for the quarter-rate transcendentals
+# (19 slots)
+PEAK_GELU_T = 256 * 64 * 2.4e9 / 19 / 1e12
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = os.path.join(ROOT, "draft_correction_amd", "csrc")
 
@@ -84,7 +87,7 @@ def algorithmic_work(cfg: dict, n: int) -> dict:
     w["finish"] = w["finish_walk"] = dict(bound="hbm", bytes=n * (B - 1) * K * K * 4 * 2,
                                           per_unit=(B - 1) * K * K * 8, units=n, unit="block")
     # the transition MLP epilogue is bound by the vector ALU: K^2 h GELU
-    # evaluations per pair (~16 VALU instructions each, 2 of them quarter-rate
+    # evaluations per pair (13 VALU instructions each, 2 of them quarter-rate
     # transcendentals) against 256 CUs x 64 lanes x 2.4 GHz
     w["mlp"] = dict(bound="alu", gelu=pairs * K * K * h, flops=2 * pairs * K * K * h,
                     per_unit=h, units=pairs * K * K, unit="transition (h GELU evaluations)")

@@ -25,20 +25,27 @@ namespace corr {
 
 namespace {
 
-// GELU(x) = x Phi(x) = max(x, 0) - |x| Phi(-|x|), with Phi(-t) from
+// GELU(x) = x Phi(x) = max(x, 0) - t Phi(-t), t = |x|, with Phi(-t) from
 // Abramowitz & Stegun 26.2.17 (Hastings): Phi(-t) = phi(t) (b1 k + ... + b5 k^5),
-// k = 1 / (1 + p t), |error| < 7.5e-8; phi's 1/sqrt(2 pi) is folded into b.
-// In float32 the result is within 4e-7 of the exact erf form everywhere.
-__device__ __forceinline__ float gelu(float x) {
-    const float t = fabsf(x);
-    const float k = __builtin_amdgcn_rcpf(fmaf(0.2316419f, t, 1.0f));
-    float poly = fmaf(k, 0.530702714f, -0.726576013f);  // b5, b4 (times 1/sqrt(2 pi))
-    poly = fmaf(k, poly, 0.710706871f);                 // b3
-    poly = fmaf(k, poly, -0.142248368f);                // b2
-    poly = fmaf(k, poly, 0.127414796f);                 // b1
-    poly *= k;
-    const float e = __builtin_amdgcn_exp2f(t * t * -0.72134752f);  // exp(-t^2 / 2)
-    return fmaxf(x, 0.0f) - (t * e) * poly;
+// k = 1 / (1 + p t), |error| < 7.5e-8.  Two exact rewrites shorten it:
+//   * t k = (1 - k) / p, so t Phi(-t) = exp(-t^2/2) R(k) with the degree-5
+//     polynomial R(k) = (1 - k)(b1 + b2 k + ... + b5 k^4) / (p sqrt(2 pi));
+//   * with y = alpha x, alpha = sqrt(log2(e) / 2), exp(-x^2/2) = 2^(-y^2) and
+//     alpha GELU(x) = max(y, 0) - 2^(-y^2) alpha R(k), k = 1 / (1 + (p/alpha)|y|).
+// The kernel keeps P and Q (so x) scaled by alpha and w2 scaled by 1/alpha,
+// so w2 . GELU(x) = (w2/alpha) . gelu_scaled(alpha x).  Evaluated in float32
+// this is within 1.3e-6 of the exact erf form on [-12, 12].
+constexpr float kGeluAlpha = 0.849321800f;      // sqrt(log2(e) / 2)
+__device__ __forceinline__ float gelu_scaled(float y) {
+    const float t = fabsf(y);
+    const float k = __builtin_amdgcn_rcpf(fmaf(0.272737495f, t, 1.0f));  // p / alpha
+    float r = fmaf(k, -1.94583702f, 4.60984922f);   // alpha R(k), Horner from k^5
+    r = fmaf(k, r, -5.26983972f);
+    r = fmaf(k, r, 3.12738533f);
+    r = fmaf(k, r, -0.988727877f);
+    r = fmaf(k, r, 0.467170075f);
+    const float e = __builtin_amdgcn_exp2f(-(y * y));
+    return fmaf(-e, r, fmaxf(y, 0.0f));
 }
 
 // Hidden units handled by one workgroup (a multiple of 16 and of 8).
@@ -99,7 +106,7 @@ __global__ __launch_bounds__(256) void mlp_kernel(MlpArgs a) {
         wla[i] = bf16_to_f32(a.w1[wrow]);
         wlb[i] = bf16_to_f32(a.w1[wrow + 1]);
     }
-    if (tid < kJB) w2s[tid] = tid < jn ? a.w2[j0 + tid] : 0.f;
+    if (tid < kJB) w2s[tid] = tid < jn ? a.w2[j0 + tid] * (1.0f / kGeluAlpha) : 0.f;   // see gelu_scaled
     // c_p = W1_s s_p for the block's units: thread (jj, kq) dots row j0 + jj
     // of W1_s with s_p over the quarter kq of its r columns, in column order.
     // W1 rows are 3r + 2 bf16 long (4-byte aligned: r is a multiple of 16),
@@ -159,13 +166,14 @@ __global__ __launch_bounds__(256) void mlp_kernel(MlpArgs a) {
                 lp = a.vals[np];
                 lq = a.vals[nq];
             }
-            if (colok) {
+            if (colok) {   // kept scaled by alpha (see gelu_scaled)
+                constexpr float al = kGeluAlpha;
                 *reinterpret_cast<float4*>(P + m * PS + c) =
-                    make_float4(cpv[0] + fmaf(wla[0], lp, u.x), cpv[1] + fmaf(wla[1], lp, u.y),
-                                cpv[2] + fmaf(wla[2], lp, u.z), cpv[3] + fmaf(wla[3], lp, u.w));
+                    make_float4(al * (cpv[0] + fmaf(wla[0], lp, u.x)), al * (cpv[1] + fmaf(wla[1], lp, u.y)),
+                                al * (cpv[2] + fmaf(wla[2], lp, u.z)), al * (cpv[3] + fmaf(wla[3], lp, u.w)));
                 *reinterpret_cast<float4*>(Q + m * PS + c) =
-                    make_float4(fmaf(wlb[0], lq, v.x), fmaf(wlb[1], lq, v.y), fmaf(wlb[2], lq, v.z),
-                                fmaf(wlb[3], lq, v.w));
+                    make_float4(al * fmaf(wlb[0], lq, v.x), al * fmaf(wlb[1], lq, v.y), al * fmaf(wlb[2], lq, v.z),
+                                al * fmaf(wlb[3], lq, v.w));
             }
         }
     }
@@ -185,14 +193,14 @@ __global__ __launch_bounds__(256) void mlp_kernel(MlpArgs a) {
             const float4 pv1 = *reinterpret_cast<const float4*>(pr + j + 4);
             const float4 qv1 = *reinterpret_cast<const float4*>(qr + j + 4);
             const float4 wv1 = *reinterpret_cast<const float4*>(w2s + j + 4);
-            d0 = fmaf(wv0.x, gelu(pv0.x + qv0.x), d0);
-            d1 = fmaf(wv0.y, gelu(pv0.y + qv0.y), d1);
-            d0 = fmaf(wv0.z, gelu(pv0.z + qv0.z), d0);
-            d1 = fmaf(wv0.w, gelu(pv0.w + qv0.w), d1);
-            d0 = fmaf(wv1.x, gelu(pv1.x + qv1.x), d0);
-            d1 = fmaf(wv1.y, gelu(pv1.y + qv1.y), d1);
-            d0 = fmaf(wv1.z, gelu(pv1.z + qv1.z), d0);
-            d1 = fmaf(wv1.w, gelu(pv1.w + qv1.w), d1);
+            d0 = fmaf(wv0.x, gelu_scaled(pv0.x + qv0.x), d0);
+            d1 = fmaf(wv0.y, gelu_scaled(pv0.y + qv0.y), d1);
+            d0 = fmaf(wv0.z, gelu_scaled(pv0.z + qv0.z), d0);
+            d1 = fmaf(wv0.w, gelu_scaled(pv0.w + qv0.w), d1);
+            d0 = fmaf(wv1.x, gelu_scaled(pv1.x + qv1.x), d0);
+            d1 = fmaf(wv1.y, gelu_scaled(pv1.y + qv1.y), d1);
+            d0 = fmaf(wv1.z, gelu_scaled(pv1.z + qv1.z), d0);
+            d1 = fmaf(wv1.w, gelu_scaled(pv1.w + qv1.w), d1);
         }
         out[idx] = d0 + d1;
     }
