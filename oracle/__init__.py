@@ -19,6 +19,7 @@ from .oracle import (  # noqa: F401
     set_threads,
     topk,
     topk_row,
+    viterbi,
     walk,
 )
 from .yieldcalc import expected_yield, iid_expected_yield, survival  # noqa: F401

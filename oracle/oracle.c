@@ -17,6 +17,8 @@
  *       Delta a two-layer GELU MLP (3r+2) -> h -> 1;
  *   (5) the prefix-first walk: slot 1 takes the drafter argmax, then
  *       k_{p+1} = argmax_b S_p(k_p, b).
+ * The Global-Sum path rule (LiLiCorr, appendix E, Eq. 12) replaces (5) by the
+ * path with the largest summed transition score, by dynamic programming.
  * The cosine variant (LiLiCorr, section 3.2, Eq. 1) replaces (3)-(4) by
  *   S_p(a,b) = l_{p+1}(b) + sigma * cos(W_out z_p^a, W_in z_{p+1}^b).
  *
@@ -24,6 +26,9 @@
  *   - top-K order is value descending, ties to the lowest token id; values
  *     compare numerically (-0 == +0, -inf sorts last); NaN is rejected;
  *   - the walk breaks ties to the lowest candidate index;
+ *   - the Global-Sum path keeps slot 1 at rank 0 like the walk, and breaks
+ *     ties to the lowest predecessor index in the sweep and the lowest
+ *     candidate index in the last slot;
  *   - LayerNorm uses the biased variance over the r features and eps from the
  *     descriptor; GELU is the exact erf form;
  *   - the cosine normalises v / max(|v|, 1e-12).
@@ -382,6 +387,61 @@ int oracle_walk(const oracle_desc *D, int32_t n, const double *scores, const int
         for (int sl = 0; sl < B; ++sl)
             tokens[(size_t)i * B + sl] = ids[((size_t)i * B + sl) * K + choice[(size_t)i * B + sl]];
     }
+    return ORA_OK;
+}
+
+/* ------------------------------------------------- Global-Sum path rule -- */
+
+/* The path through the candidate lattice with the largest summed transition
+ * score (LiLiCorr, appendix E, Eq. 12: a path scores as the sum of its
+ * adjacent-slot terms), found exactly by dynamic programming (the Viterbi
+ * algorithm the appendix names).  Slot 1 is fixed at rank 0 (the drafter's
+ * argmax), as in the walk.  Sweeping left to right, best[b] is the largest
+ * score of a path ending at candidate b of the current slot and from[p][b]
+ * the smallest predecessor index attaining it; the last slot takes the
+ * smallest b attaining the largest best[b], and the path is traced back
+ * through `from`.  total[i] (optional) receives the path's summed score. */
+int oracle_viterbi(const oracle_desc *D, int32_t n, const double *scores, const int32_t *ids,
+                   int32_t *tokens, int32_t *choice, double *total)
+{
+    if (!D || !scores || !ids || !tokens || !choice || n < 0) return ORA_E_ARG;
+    const int B = D->B, K = D->K;
+    double *best = malloc(sizeof(double) * (size_t)K);
+    double *next = malloc(sizeof(double) * (size_t)K);
+    int32_t *from = malloc(sizeof(int32_t) * (size_t)(B > 1 ? B - 1 : 1) * K);
+    if (!best || !next || !from) {
+        free(best); free(next); free(from);
+        return ORA_E_NOMEM;
+    }
+    for (int32_t i = 0; i < n; ++i) {
+        for (int a = 0; a < K; ++a) best[a] = a == 0 ? 0.0 : -INFINITY;
+        for (int p = 0; p + 1 < B; ++p) {
+            const double *Sp = scores + ((size_t)i * (B - 1) + p) * K * K;
+            for (int b = 0; b < K; ++b) {
+                int32_t arg = 0;
+                double v = best[0] + Sp[b];
+                for (int a = 1; a < K; ++a) {
+                    const double w = best[a] + Sp[(size_t)a * K + b];
+                    if (w > v) { v = w; arg = a; }
+                }
+                next[b] = v;
+                from[(size_t)p * K + b] = arg;
+            }
+            for (int b = 0; b < K; ++b) best[b] = next[b];
+        }
+        int32_t k = 0;
+        for (int b = 1; b < K; ++b)
+            if (best[b] > best[k]) k = b;
+        if (total) total[i] = best[k];
+        for (int sl = B - 1; sl >= 1; --sl) {
+            choice[(size_t)i * B + sl] = k;
+            k = from[(size_t)(sl - 1) * K + k];
+        }
+        choice[(size_t)i * B] = 0;
+        for (int sl = 0; sl < B; ++sl)
+            tokens[(size_t)i * B + sl] = ids[((size_t)i * B + sl) * K + choice[(size_t)i * B + sl]];
+    }
+    free(best); free(next); free(from);
     return ORA_OK;
 }
 

@@ -57,6 +57,7 @@ def _load():
         lib.oracle_represent.argtypes = [P, P, C.c_int32, P, P, C.c_int64, C.c_int64, P, P, P, P]
         lib.oracle_score.argtypes = [P, P, C.c_int32, P, P, P, P, P]
         lib.oracle_walk.argtypes = [P, C.c_int32, P, P, P, P]
+        lib.oracle_viterbi.argtypes = [P, C.c_int32, P, P, P, P, P]
         lib.oracle_accepted.argtypes = [C.c_int32, C.c_int32, P, P, P]
         lib.oracle_layernorm.argtypes = [P, C.c_int, C.c_double, P, P]
         lib.oracle_gelu.restype = C.c_double
@@ -229,6 +230,21 @@ def walk(desc: OracleDesc, scores, ids, n: int):
     _check(_load().oracle_walk(C.byref(d), n, _ptr(scores), _ptr(ids), _ptr(tokens),
                                _ptr(choice)), "walk")
     return tokens, choice
+
+
+def viterbi(desc: OracleDesc, scores, ids, n: int):
+    """Global-Sum path rule: tokens [n][B], choices [n][B] and the summed
+    transition score [n] of the best path (slot 1 fixed at rank 0)."""
+    keep = _Keep()
+    scores = keep.arr(scores, np.float64)
+    ids = keep.arr(ids, np.int32)
+    tokens = np.empty((n, desc.B), np.int32)
+    choice = np.empty((n, desc.B), np.int32)
+    total = np.empty(n, np.float64)
+    d = desc.c()
+    _check(_load().oracle_viterbi(C.byref(d), n, _ptr(scores), _ptr(ids), _ptr(tokens),
+                                  _ptr(choice), _ptr(total)), "viterbi")
+    return tokens, choice, total
 
 
 def accepted_lengths(tokens, targets) -> np.ndarray:

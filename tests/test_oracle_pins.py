@@ -333,6 +333,88 @@ def test_walk_matches_brute_force():
         np.testing.assert_array_equal(tokens[0], ids[0, np.arange(B), want])
 
 
+# ------------------------------------------------- Global-Sum path rule --
+# LiLiCorr, appendix E, Eq. 12: the path maximising the summed transition
+# scores, by dynamic programming; slot 1 stays at rank 0 as in the walk.
+
+def _paths(B, K):
+    """Every path with slot 1 at rank 0: K^(B-1) tuples of choices."""
+    for tail in itertools.product(range(K), repeat=B - 1):
+        yield (0,) + tail
+
+
+def _path_score(S, path):
+    return sum(S[p, path[p], path[p + 1]] for p in range(len(path) - 1))
+
+
+def _desc(B, K):
+    return oracle.OracleDesc(V=100, B=B, K=K, d=32, de=32, r=16, h=16, dvec=16)
+
+
+def test_viterbi_matches_brute_force():
+    """Continuous random scores (a unique optimum): the same path and total as
+    enumerating all K^(B-1) paths."""
+    g = np.random.default_rng(11)
+    for B, K in ((1, 3), (2, 3), (3, 4), (5, 4), (6, 3), (4, 6)):
+        n = 3
+        S = g.normal(size=(n, max(B - 1, 0), K, K))
+        ids = g.integers(0, 100, size=(n, B, K)).astype(np.int32)
+        tokens, choice, total = oracle.viterbi(_desc(B, K), S, ids, n)
+        for i in range(n):
+            best = max(_paths(B, K), key=lambda c: _path_score(S[i], c))
+            np.testing.assert_array_equal(choice[i], best)
+            np.testing.assert_array_equal(tokens[i], ids[i, np.arange(B), list(best)])
+            assert total[i] == pytest.approx(_path_score(S[i], best), abs=1e-12)
+
+
+def test_viterbi_ties_give_an_optimal_path():
+    """Integer scores (many ties): the returned path attains the brute-force
+    optimum and the reported total is its score."""
+    g = np.random.default_rng(12)
+    for trial in range(20):
+        B, K = int(g.integers(2, 6)), int(g.integers(1, 5))
+        S = g.integers(-2, 3, size=(1, B - 1, K, K)).astype(np.float64)
+        ids = g.integers(0, 100, size=(1, B, K)).astype(np.int32)
+        _, choice, total = oracle.viterbi(_desc(B, K), S, ids, 1)
+        best = max(_path_score(S[0], c) for c in _paths(B, K))
+        assert choice[0, 0] == 0
+        assert _path_score(S[0], choice[0]) == best == total[0]
+
+
+def test_viterbi_zero_head_takes_each_slot_argmax():
+    """With the zero-initialised output layer S_p(a,b) = l_{p+1}(b) (DCOCO core
+    method), so the best path takes every slot's largest logit: rank 0."""
+    x = gen_inputs(config("tiny"), head="zero")
+    ora = oracle.run(x["cfg"], x)
+    desc = oracle.OracleDesc.from_config(x["cfg"])
+    _, choice, total = oracle.viterbi(desc, ora["scores"], ora["ids"], x["cfg"]["n"])
+    assert (choice == 0).all()
+    assert total[0] == pytest.approx(ora["vals"][0, 1:, 0].sum(), abs=1e-12)
+
+
+def test_viterbi_dominates_the_walk_and_ignores_pair_offsets():
+    """The exact maximiser scores at least as high as the greedy walk's path
+    (equal when there is one pair), and adding a constant to every score of a
+    pair shifts the total by that constant without changing the path."""
+    g = np.random.default_rng(13)
+    for B, K in ((2, 5), (4, 4), (8, 3), (15, 4)):
+        n = 4
+        S = g.normal(size=(n, B - 1, K, K))
+        ids = g.integers(0, 100, size=(n, B, K)).astype(np.int32)
+        desc = _desc(B, K)
+        _, choice, total = oracle.viterbi(desc, S, ids, n)
+        _, wchoice = oracle.walk(desc, S, ids, n)
+        for i in range(n):
+            greedy = _path_score(S[i], wchoice[i])
+            assert total[i] >= greedy - 1e-12
+            if B == 2:
+                assert total[i] == pytest.approx(greedy, abs=1e-12)
+        c = g.normal(size=(n, B - 1, 1, 1)) * 5
+        _, choice2, total2 = oracle.viterbi(desc, S + c, ids, n)
+        np.testing.assert_array_equal(choice2, choice)
+        np.testing.assert_allclose(total2, total + c.sum(axis=(1, 2, 3)), atol=1e-9)
+
+
 # -------------------------------------------------------- cosine variant --
 
 def test_cosine_scores_match_torch_and_bound():
