@@ -84,17 +84,20 @@ def algorithmic_work(cfg: dict, n: int) -> dict:
     w["cand"] = dict(bound="hbm", bytes=rows * K * (r * 4 * 2 + uvb),
                      flops=2 * rows * K * (2 * r * r + (2 * h * r if uvb else 0)),
                      per_unit=r * 8 + uvb, units=rows * K, unit="candidate (u in; z and U|V out)")
-    w["finish"] = w["finish_walk"] = dict(bound="hbm", bytes=n * (B - 1) * K * K * 4 * 2,
+    w["finish"] = w["finish_walk"] = w["finish_viterbi"] = dict(bound="hbm", bytes=n * (B - 1) * K * K * 4 * 2,
                                           per_unit=(B - 1) * K * K * 8, units=n, unit="block")
     # the transition MLP epilogue is bound by the vector ALU: K^2 h GELU
     # evaluations per pair (13 VALU instructions each, 2 of them quarter-rate
     # transcendentals) against 256 CUs x 64 lanes x 2.4 GHz
     w["mlp"] = dict(bound="alu", gelu=pairs * K * K * h, flops=2 * pairs * K * K * h,
                     per_unit=h, units=pairs * K * K, unit="transition (h GELU evaluations)")
-    w["cosine"] = dict(bound="hbm", bytes=pairs * 2 * K * cfg["dvec"] * 4, per_unit=2 * K * cfg["dvec"] * 4,
-                       units=pairs, unit="pair")
+    w["cosine"] = w["cosine_walk"] = w["cosine_viterbi"] = dict(
+        bound="hbm", bytes=pairs * 2 * K * cfg["dvec"] * 4, per_unit=2 * K * cfg["dvec"] * 4, units=pairs, unit="pair")
     w["walk"] = dict(bound="hbm", bytes=n * (B - 1) * K * 4, per_unit=(B - 1) * K * 4, units=n,
                      unit="block (scores rows read)")
+    # the Global-Sum path reads every score of the block once
+    w["viterbi"] = dict(bound="hbm", bytes=n * (B - 1) * K * K * 4, per_unit=(B - 1) * K * K * 4, units=n,
+                        unit="block (all scores read)")
     return w
 
 
@@ -124,6 +127,8 @@ def main():
     ap.add_argument("--copies", type=int, default=4, help="independent input sets rotated per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--head", default="normal")
+    ap.add_argument("--path-rule", default="greedy", choices=["greedy", "global_sum"],
+                    help="how the path through the candidate lattice is chosen")
     ap.add_argument("--no-fold", action="store_true", help="skip the folded-table measurement")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of this many MiB (a known-size reference "
@@ -139,7 +144,7 @@ def main():
     from workload import config
     from workload.gen import gen_embed, gen_hidden, gen_logits, gen_weights
 
-    cfg = config(args.workload)
+    cfg = config(args.workload, path_rule=args.path_rule)
     n = cfg["n"]
     log("generating %s inputs (%d copies)" % (args.workload, args.copies))
     t0 = time.perf_counter()
@@ -288,7 +293,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": "%s: %d requests x %d drafted slots (+anchor), V=%d, K=%d, d=%d, r=%d, "
                                "MLP %d->%d->1, %s" % (args.workload, n, B, cfg["V"], K, cfg["d"],
-                                                      cfg["r"], 3 * cfg["r"] + 2, cfg["h"], cfg["variant"]),
+                                                      cfg["r"], 3 * cfg["r"] + 2, cfg["h"], cfg["variant"])
+                               + ("" if args.path_rule == "greedy" else ", Global-Sum path"),
                    "global_batch": n, "rotating_input_sets": args.copies},
         "roofline": roof,
         "kernels": kernels,

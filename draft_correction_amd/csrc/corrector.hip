@@ -11,6 +11,9 @@
 #include "../../include/corrector.h"
 #include "kernels.h"
 
+static_assert(corr::kPathGreedy == CORR_PATH_GREEDY && corr::kPathGlobalSum == CORR_PATH_GLOBAL_SUM,
+              "path rule values");
+
 using namespace corr;
 
 namespace corr {
@@ -168,6 +171,14 @@ struct Seq {
     }
 };
 
+// Step (5) over precomputed scores, by the handle's path rule.
+hipError_t launch_path_rule(const corrector* h, const float* scores, const int32_t* ids, int32_t n, int32_t* tokens,
+                            int32_t* choice, hipStream_t s) {
+    return launch_path(scores, ids, n, h->d.slots, h->d.k, h->d.path_rule, tokens, choice, s);
+}
+
+const char* path_name(const corrector* h) { return h->d.path_rule == CORR_PATH_GLOBAL_SUM ? "viterbi" : "walk"; }
+
 // Step (1).  With `hj` given, the hidden-state projection runs in the merge
 // launch (it does not depend on the top-K).
 void enqueue_topk(Seq& q, const corrector* h, const Layout& L, int32_t n, const void* logits,
@@ -289,7 +300,7 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
     }
     q("cand", [&] { return launch_cand(ca, q.s); });
     if (d.slots < 2) {
-        if (tokens) q("walk", [&] { return launch_walk(scores, ids, n, d.slots, d.k, tokens, choice, q.s); });
+        if (tokens) q(path_name(h), [&] { return launch_path_rule(h, scores, ids, n, tokens, choice, q.s); });
         return;
     }
     if (cos) {
@@ -303,8 +314,16 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
         c.dvec = d.d_vec;
         c.sigma = d.sigma;
         c.scores = scores;
-        q("cosine", [&] { return launch_cosine(c, q.s); });
-        if (tokens) q("walk", [&] { return launch_walk(scores, ids, n, d.slots, d.k, tokens, choice, q.s); });
+        // the path runs inside the cosine launch when the scores fit its LDS
+        const bool fused = tokens && path_fits_lds(d.slots, d.k);
+        c.ids = ids;
+        c.tokens = fused ? tokens : nullptr;
+        c.choice = fused ? choice : nullptr;
+        c.rule = d.path_rule;
+        q(fused ? (d.path_rule == CORR_PATH_GREEDY ? "cosine_walk" : "cosine_viterbi") : "cosine",
+          [&] { return launch_cosine(c, q.s); });
+        if (tokens && !fused)
+            q(path_name(h), [&] { return launch_path_rule(h, scores, ids, n, tokens, choice, q.s); });
     } else {
         MlpArgs m{};
         m.uv = ca.uv;
@@ -330,9 +349,15 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
         f.K = d.k;
         f.scores = scores;
         f.ids = ids;
-        f.tokens = tokens;
-        f.choice = choice;
-        q(tokens ? "finish_walk" : "finish", [&] { return launch_finish(f, q.s); });
+        // the path runs inside the finishing launch when the scores fit its LDS
+        const bool fused = tokens && path_fits_lds(d.slots, d.k);
+        f.tokens = fused ? tokens : nullptr;
+        f.choice = fused ? choice : nullptr;
+        f.rule = d.path_rule;
+        q(fused ? (d.path_rule == CORR_PATH_GREEDY ? "finish_walk" : "finish_viterbi") : "finish",
+          [&] { return launch_finish(f, q.s); });
+        if (tokens && !fused)
+            q(path_name(h), [&] { return launch_path_rule(h, scores, ids, n, tokens, choice, q.s); });
     }
 }
 
@@ -347,6 +372,7 @@ int corrector_create(const corrector_desc* desc, const corrector_weights* wt, co
     const corrector_desc& d = *desc;
     if (d.variant != CORR_VARIANT_MLP && d.variant != CORR_VARIANT_COSINE) return CORR_E_UNSUPPORTED;
     if (d.logits_dtype != CORR_DTYPE_BF16 && d.logits_dtype != CORR_DTYPE_F32) return CORR_E_UNSUPPORTED;
+    if (d.path_rule != CORR_PATH_GREEDY && d.path_rule != CORR_PATH_GLOBAL_SUM) return CORR_E_UNSUPPORTED;
     if (d.vocab < 1 || d.vocab > 0x7FFFFFFF) return CORR_E_SHAPE;
     if (d.slots < 1 || d.slots > 64) return CORR_E_SHAPE;  // the walk keeps one slot per lane
     if (d.k < 1 || d.k > 64 || d.k > d.vocab) return CORR_E_SHAPE;
@@ -451,7 +477,7 @@ int corrector_walk(const corrector* hc, int32_t n, const float* scores, const in
     std::unique_lock<std::mutex> lock(h->mu, std::defer_lock);
     if (h->timing) lock.lock();
     Seq q{h, static_cast<hipStream_t>(stream)};
-    q("walk", [&] { return launch_walk(scores, ids, n, h->d.slots, h->d.k, tokens, choice, q.s); });
+    q(path_name(h), [&] { return launch_path_rule(h, scores, ids, n, tokens, choice, q.s); });
     return q.finish();
 }
 

@@ -12,6 +12,10 @@
 
 namespace corr {
 
+// Path rules (the values of CORR_PATH_GREEDY / CORR_PATH_GLOBAL_SUM).
+constexpr int kPathGreedy = 0;
+constexpr int kPathGlobalSum = 1;
+
 // Optional timing events for the next launch made on this thread.  The host
 // sequencer sets them around one step; launch() hands them to
 // hipExtLaunchKernel, which stamps them with the kernel's own start and end
@@ -152,8 +156,8 @@ constexpr int kMaxMlpBlocks = 4;
 int mlp_blocks(int h);
 hipError_t launch_mlp(const MlpArgs& a, hipStream_t stream);
 
-// Sum of the MLP partials in block order + b2 + l_{p+1}(b) -> scores; then,
-// when tokens is non-null, the walk (one workgroup per request).
+// Sum of the MLP partials in block order + b2 + l_{p+1}(b) -> scores (one
+// workgroup per request).
 struct FinishArgs {
     const float* part;
     int nblk;
@@ -164,8 +168,9 @@ struct FinishArgs {
     int K;
     float* scores;
     const int32_t* ids;
-    int32_t* tokens;
-    int32_t* choice;
+    int32_t* tokens;        // with tokens given (only when path_fits_lds), the
+    int32_t* choice;        // request's path by `rule` follows in the launch
+    int rule;
 };
 hipError_t launch_finish(const FinishArgs& a, hipStream_t stream);
 
@@ -179,12 +184,25 @@ struct CosArgs {
     int dvec;
     float sigma;
     float* scores;
+    // with tokens given (only when path_fits_lds), the request's path by
+    // `rule` follows in the same launch
+    const int32_t* ids;
+    int32_t* tokens;
+    int32_t* choice;
+    int rule;
 };
 hipError_t launch_cosine(const CosArgs& a, hipStream_t stream);
 
-// ---- walk (walk.hip)
-hipError_t launch_walk(const float* scores, const int32_t* ids, int n, int B, int K,
-                       int32_t* tokens, int32_t* choice, hipStream_t stream);
+// ---- paths (walk.hip)
+// Whether a request's scores (plus the path's small arrays) fit one
+// workgroup's LDS; only then do the finishing and cosine kernels run the path
+// themselves.
+bool path_fits_lds(int B, int K);
+// The path of every request over precomputed scores by `rule`
+// (kPathGreedy: the prefix-first walk; kPathGlobalSum: the best
+// summed score by dynamic programming), one wave per request.
+hipError_t launch_path(const float* scores, const int32_t* ids, int n, int B, int K, int rule, int32_t* tokens,
+                       int32_t* choice, hipStream_t stream);
 
 // ---- intermediates (walk.hip)
 hipError_t launch_zhl_to_f32(const uint16_t* zhl, float* z, int64_t nodes, int r, hipStream_t stream);

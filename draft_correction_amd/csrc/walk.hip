@@ -1,7 +1,11 @@
-// The cosine transition scores (LiLiCorr section 3.2, Eq. 1, with the
-// drafter's successor logit added as in the DCOCO score), the prefix-first
-// walk (DCOCO method details step (5); LiLiCorr section 3.5, Eq. 8), and small
-// copy kernels used to expose intermediates.
+// Step (5) and the cosine variant's scores:
+//   - the prefix-first walk (DCOCO method details step (5); LiLiCorr section
+//     3.5, Eq. 8) and the Global-Sum path (LiLiCorr appendix E, Eq. 12: the
+//     path with the largest summed score, by dynamic programming);
+//   - the cosine transition scores (LiLiCorr section 3.2, Eq. 1, with the
+//     drafter's successor logit added as in the DCOCO score);
+//   - the finishing reduction of the MLP's hidden-block partials;
+//   - small copy kernels used to expose intermediates.
 #include "common.h"
 #include "kernels.h"
 
@@ -9,28 +13,11 @@ namespace corr {
 
 namespace {
 
-// One workgroup per pair: S[a][b] = l_{p+1}(b) + sigma * <o_p^a, i_{p+1}^b>,
-// the vectors already unit-normalised; fp32 dot products in index order.
-__global__ __launch_bounds__(256) void cosine_kernel(CosArgs a) {
-    const int pair = blockIdx.x;
-    const int B = a.B, K = a.K, dv = a.dvec;
-    const int req = pair / (B - 1), p = pair % (B - 1);
-    const int64_t tp = static_cast<int64_t>(req) * B + p, tq = tp + 1;
-    for (int idx = threadIdx.x; idx < K * K; idx += blockDim.x) {
-        const int ia = idx / K, ib = idx % K;
-        const float* o = a.vout + (tp * K + ia) * dv;
-        const float* v = a.vin + (tq * K + ib) * dv;
-        float acc = 0.f;
-        for (int c = 0; c < dv; ++c) acc += o[c] * v[c];
-        a.scores[static_cast<int64_t>(pair) * K * K + idx] = a.vals[tq * K + ib] + a.sigma * acc;
-    }
-}
-
 // The prefix-first walk of one request by one wave over its scores `src`
 // ([B-1][K][K], LDS or memory): choice[0] = 0 (rank 0 is the drafter argmax of
 // the first drafted slot); then each step takes the largest score in the row
 // of the chosen predecessor, ties to the lowest successor index.
-__device__ void walk_wave(const float* src, const int32_t* __restrict__ ids, int req, int B, int K,
+__device__ __forceinline__ void walk_wave(const float* src, const int32_t* __restrict__ ids, int req, int B, int K,
                           int32_t* __restrict__ tokens, int32_t* __restrict__ choice) {
     const int l = lane_id();
     int k = 0;
@@ -55,7 +42,7 @@ __device__ void walk_wave(const float* src, const int32_t* __restrict__ ids, int
 // k_1 = 0, k_{p+1} = best[p][k_p] (B - 1 dependent byte reads); then lanes
 // s < B write choice[s] and gather tokens[s] = ids[s][k_s].  Every thread of
 // the workgroup calls it.
-__device__ void walk_block(const float* sS, uint8_t* best, int* chain, const int32_t* __restrict__ ids, int req,
+__device__ __forceinline__ void walk_block(const float* sS, uint8_t* best, int* chain, const int32_t* __restrict__ ids, int req,
                            int B, int K, int32_t* __restrict__ tokens, int32_t* __restrict__ choice) {
     const int nrows = (B - 1) * K;
     for (int r = threadIdx.x; r < nrows; r += blockDim.x) {
@@ -103,18 +90,122 @@ __host__ __device__ inline size_t walk_chain_offset(int B, int K) {
     return (walk_best_offset(B, K) + static_cast<size_t>(B - 1) * K + 3) / 4 * 4;
 }
 
-// Walk over precomputed scores, one wave per request.  When the request's
+// The Global-Sum path of one request by one wave over its scores `src`
+// ([B-1][K][K], LDS or memory).  best[b] is the best score of a path ending at
+// candidate b of the current slot (slot 1: 0 at rank 0 and -inf elsewhere, as
+// the walk fixes slot 1 at the drafter's argmax); it lives in LDS (vb, K
+// floats, 16-byte aligned), written by lanes b < K and read back by every lane
+// as broadcast float4 loads.  Each pair step takes, for every b (one per
+// lane), the largest best[a] + S_p(a, b) over a: the predecessors go in groups
+// of 16, whose column of S is read first and reduced by a (value, index) tree
+// in which the right operand (higher indices) wins only if strictly greater,
+// so ties go to the lowest a; the argmax a goes to from[p][b] (LDS).  The last
+// slot's largest best (lowest index on ties) is traced back through `from` by
+// one lane into chain[] (LDS), and lanes s < B write choice[s] and gather
+// tokens[s] = ids[s][chain[s]].
+__device__ __forceinline__ void viterbi_wave(const float* src, uint8_t* from, int* chain, float* vb,
+                                             const int32_t* __restrict__ ids, int req, int B, int K,
+                                             int32_t* __restrict__ tokens, int32_t* __restrict__ choice) {
+    const int l = lane_id();
+    const int bl = min(l, K - 1);   // lanes past K mirror the last candidate (never used)
+    float bv = l == 0 ? 0.f : -INFINITY;
+    for (int p = 0; p + 1 < B; ++p) {
+        if (l < K) vb[l] = bv;
+        wave_lds_sync();
+        const float* Sp = src + static_cast<int64_t>(p) * K * K;
+        float v = -INFINITY;
+        int arg = 0;
+        for (int a0 = 0; a0 < K; a0 += 16) {
+            float w[16];
+            float4 pv[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)   // vb has room for the whole group (K rounded up to 16)
+                pv[q] = *reinterpret_cast<const float4*>(vb + a0 + 4 * q);
+#pragma unroll
+            for (int u = 0; u < 16; ++u) w[u] = Sp[min(a0 + u, K - 1) * K + bl];   // clamped: past K unused
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const float4 q4 = pv[u / 4];
+                const float pb = (u & 3) == 0 ? q4.x : ((u & 3) == 1 ? q4.y : ((u & 3) == 2 ? q4.z : q4.w));
+                w[u] = a0 + u < K ? pb + w[u] : -INFINITY;
+            }
+            // The group's maximum, then the lowest predecessor that reaches it
+            // (a select sweep over constant indices: no index array to carry).
+            float m = w[0];
+#pragma unroll
+            for (int u = 1; u < 16; ++u) m = fmaxf(m, w[u]);
+            int a = 0;
+#pragma unroll
+            for (int u = 15; u >= 0; --u) a = w[u] == m ? u : a;
+            if (a0 == 0 || m > v) {
+                v = m;
+                arg = a0 + a;
+            }
+        }
+        if (l < K) from[p * K + l] = static_cast<uint8_t>(arg);
+        bv = l < K ? v : -INFINITY;
+        wave_lds_sync();   // every lane has read vb before the next step rewrites it
+    }
+    int k = wave_argmax_lowest(bv, K);
+    wave_lds_sync();
+    if (l == 0) {
+        for (int t = B - 1; t >= 1; --t) {
+            chain[t] = k;
+            k = from[(t - 1) * K + k];
+        }
+        chain[0] = 0;
+    }
+    wave_lds_sync();
+    if (l < B) {
+        const int64_t s_ = static_cast<int64_t>(req) * B + l;
+        const int ch = chain[l];
+        if (choice) choice[s_] = ch;
+        tokens[s_] = ids[s_ * K + ch];
+    }
+}
+
+// LDS of a path over scores held in LDS: the scores, then from/best
+// ([B-1][K] bytes), then chain ([B] ints), then vb (K rounded up to 16
+// floats, 16-byte aligned); without the scores, the last three alone.
+__host__ __device__ inline size_t path_aux_offset(int B, int K, bool scores_in_lds) {
+    return scores_in_lds ? walk_best_offset(B, K) : 0;
+}
+__host__ __device__ inline size_t path_chain_offset(int B, int K, bool scores_in_lds) {
+    return (path_aux_offset(B, K, scores_in_lds) + static_cast<size_t>(B > 1 ? B - 1 : 0) * K + 3) / 4 * 4;
+}
+__host__ __device__ inline size_t path_vb_offset(int B, int K, bool scores_in_lds) {
+    return (path_chain_offset(B, K, scores_in_lds) + sizeof(int) * static_cast<size_t>(B) + 15) / 16 * 16;
+}
+__host__ __device__ inline size_t path_lds_end(int B, int K, bool scores_in_lds) {
+    return path_vb_offset(B, K, scores_in_lds) + sizeof(float) * static_cast<size_t>((K + 15) / 16 * 16);
+}
+
+// The request's path from scores in LDS (every thread of the workgroup
+// calls it): the greedy walk uses the whole workgroup, the Global-Sum
+// dynamic program its first wave.
+__device__ __forceinline__ void path_from_lds(int rule, float* sS, const int32_t* __restrict__ ids, int req, int B, int K,
+                              int32_t* __restrict__ tokens, int32_t* __restrict__ choice) {
+    uint8_t* aux = reinterpret_cast<uint8_t*>(reinterpret_cast<char*>(sS) + path_aux_offset(B, K, true));
+    int* chain = reinterpret_cast<int*>(reinterpret_cast<char*>(sS) + path_chain_offset(B, K, true));
+    if (rule == kPathGlobalSum) {
+        float* vb = reinterpret_cast<float*>(reinterpret_cast<char*>(sS) + path_vb_offset(B, K, true));
+        if ((threadIdx.x >> 6) == 0) viterbi_wave(sS, aux, chain, vb, ids, req, B, K, tokens, choice);
+        return;
+    }
+    walk_block(sS, aux, chain, ids, req, B, K, tokens, choice);
+}
+
+// A path over precomputed scores, one wave per request.  When the request's
 // scores fit (use_lds) they are first copied into LDS with coalesced 16-byte
-// loads, all issued before any is used, so the dependent steps read LDS.
-__global__ __launch_bounds__(64) void walk_kernel(const float* __restrict__ scores,
-                                                  const int32_t* __restrict__ ids, int n, int B,
-                                                  int K, int32_t* __restrict__ tokens,
+// loads, all issued before any is used.
+__global__ __launch_bounds__(64) void path_kernel(const float* __restrict__ scores, const int32_t* __restrict__ ids,
+                                                  int n, int B, int K, int rule, int32_t* __restrict__ tokens,
                                                   int32_t* __restrict__ choice, int use_lds) {
     extern __shared__ __attribute__((aligned(16))) float sl[];
     const int req = blockIdx.x;
     const int l = lane_id();
     if (req >= n) return;
-    const int64_t per = static_cast<int64_t>(B - 1) * K * K;
+    const int64_t per = static_cast<int64_t>(B > 1 ? B - 1 : 0) * K * K;
     const float* base = scores + req * per;
     if (use_lds) {
         if ((per & 3) == 0 && (reinterpret_cast<uintptr_t>(base) & 15) == 0) {
@@ -136,19 +227,86 @@ __global__ __launch_bounds__(64) void walk_kernel(const float* __restrict__ scor
             for (int64_t i = l; i < per; i += kWave) sl[i] = base[i];
         }
         wave_lds_sync();
+        path_from_lds(rule, sl, ids, req, B, K, tokens, choice);
+        return;
     }
-    if (use_lds) {
-        walk_block(sl, reinterpret_cast<uint8_t*>(reinterpret_cast<char*>(sl) + walk_best_offset(B, K)),
-                   reinterpret_cast<int*>(reinterpret_cast<char*>(sl) + walk_chain_offset(B, K)), ids, req, B, K,
-                   tokens, choice);
+    if (rule == kPathGlobalSum) {
+        uint8_t* from = reinterpret_cast<uint8_t*>(sl);
+        int* chain = reinterpret_cast<int*>(reinterpret_cast<char*>(sl) + path_chain_offset(B, K, false));
+        float* vb = reinterpret_cast<float*>(reinterpret_cast<char*>(sl) + path_vb_offset(B, K, false));
+        viterbi_wave(base, from, chain, vb, ids, req, B, K, tokens, choice);
         return;
     }
     walk_wave(base, ids, req, B, K, tokens, choice);
 }
 
+// The cosine scores of one request per workgroup (one wave per job, up to 16):
+//   S_p(a,b) = l_{p+1}(b) + sigma * <o_p^a, i_{p+1}^b>
+// with the unit vectors o (W_out z) and i (W_in z).  Each wave takes (pair,
+// 16 x 16 tile) jobs and forms the tile's dot products on fp32 MFMA
+// (v_mfma_f32_16x16x4_f32): lane group g = lane / 16 covers the dvec / 4
+// consecutive components g*dvec/4 .. of its rows, one component per step,
+// loaded as float4.  The scores go to memory and, when they fit, to LDS; with
+// tokens given the request's path follows from LDS.
+__global__ __launch_bounds__(1024) void cosine_kernel(CosArgs a, int use_lds) {
+    extern __shared__ __attribute__((aligned(16))) float sS[];
+    const int req = blockIdx.x;
+    const int B = a.B, K = a.K, dv = a.dvec;
+    const int KK = K * K;
+    const int l = lane_id();
+    const int wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+    const int g = l >> 4, r16 = l & 15;
+    const int nt = (K + 15) / 16;
+    const int kper = dv / 4;   // dvec is a multiple of 16 and at most 128: kper in {4, 8, ..., 32}
+    const int njobs = (B - 1) * nt * nt;
+    for (int job = wave; job < njobs; job += nwaves) {
+        const int p = job / (nt * nt), ta = (job / nt) % nt, tb = job % nt;
+        const int64_t tp = static_cast<int64_t>(req) * B + p, tq = tp + 1;
+        const float* orow = a.vout + (tp * K + min(ta * 16 + r16, K - 1)) * dv + g * kper;  // clamped rows unused
+        const float* irow = a.vin + (tq * K + min(tb * 16 + r16, K - 1)) * dv + g * kper;
+        // every load of the tile is issued before the first MFMA (steps past
+        // kper re-read the last four components and are not used)
+        float4 o4[8], i4[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int j = min(4 * u, kper - 4);
+            o4[u] = *reinterpret_cast<const float4*>(orow + j);
+            i4[u] = *reinterpret_cast<const float4*>(irow + j);
+        }
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (4 * u >= kper) break;
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(o4[u].x, i4[u].x, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(o4[u].y, i4[u].y, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(o4[u].z, i4[u].z, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(o4[u].w, i4[u].w, acc, 0, 0, 0);
+        }
+        // lane l holds D[4g + i][r16]: predecessor a = ta*16 + 4g + i, successor b = tb*16 + r16
+        const int bb = tb * 16 + r16;
+        if (bb < K) {
+            const float lb = a.vals[tq * K + bb];
+            float* srow = a.scores + (static_cast<int64_t>(req) * (B - 1) + p) * KK;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int aa = ta * 16 + 4 * g + i;
+                if (aa < K) {
+                    const float sv = lb + a.sigma * acc[i];
+                    srow[aa * K + bb] = sv;
+                    if (use_lds) sS[p * KK + aa * K + bb] = sv;
+                }
+            }
+        }
+    }
+    if (!a.tokens || !use_lds) return;
+    __syncthreads();
+    path_from_lds(a.rule, sS, a.ids, req, B, K, a.tokens, a.choice);
+}
+
 // One workgroup per request: S = l_{p+1}(b) + (sum of the hidden-block partial
 // Deltas in block order + b2) for all of the request's pairs, written to
-// `scores` (and kept in LDS when it fits); then, with tokens given, the walk.
+// `scores` (and kept in LDS when it fits); then, with tokens given (only when
+// the scores fit LDS), the request's path by the handle's rule.
 __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a, int use_lds) {
     extern __shared__ __attribute__((aligned(16))) float sS[];
     const int req = blockIdx.x;
@@ -215,16 +373,9 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a, int use_lds) 
             }
         }
     }
-    if (!a.tokens) return;
+    if (!a.tokens || !use_lds) return;
     __syncthreads();
-    if (use_lds) {
-        walk_block(sS, reinterpret_cast<uint8_t*>(reinterpret_cast<char*>(sS) + walk_best_offset(B, K)),
-                   reinterpret_cast<int*>(reinterpret_cast<char*>(sS) + walk_chain_offset(B, K)), a.ids, req, B,
-                   K, a.tokens, a.choice);
-        return;
-    }
-    if ((threadIdx.x >> 6) != 0) return;
-    walk_wave(a.scores + req * per, a.ids, req, B, K, a.tokens, a.choice);
+    path_from_lds(a.rule, sS, a.ids, req, B, K, a.tokens, a.choice);
 }
 
 // z = hi + lo for each node row of the [hi | lo] layout.
@@ -252,27 +403,35 @@ unsigned grid_for(int64_t count) {
 
 }  // namespace
 
-hipError_t launch_cosine(const CosArgs& a, hipStream_t stream) {
-    return launch(cosine_kernel, dim3(static_cast<unsigned>(a.n * (a.B - 1))), 256, 0, stream, a);
-}
-
-// Dynamic LDS of a walk that holds the request's scores (and the walk's
-// best and chain arrays), or 0 when they do not fit and the walk reads memory.
-static size_t walk_lds_bytes(int B, int K) {
+// Dynamic LDS of a path kernel that holds the request's scores (plus its byte
+// and chain arrays), or 0 when they do not fit and the path reads memory.
+static size_t path_lds_bytes(int B, int K) {
     if (B < 2) return 0;
-    const size_t bytes = walk_chain_offset(B, K) + sizeof(int) * B;
+    const size_t bytes = path_lds_end(B, K, true);
     return bytes <= 60 * 1024 ? bytes : 0;
 }
 
-hipError_t launch_walk(const float* scores, const int32_t* ids, int n, int B, int K,
-                       int32_t* tokens, int32_t* choice, hipStream_t stream) {
-    const size_t lds = walk_lds_bytes(B, K);
-    return launch(walk_kernel, dim3(static_cast<unsigned>(n)), 64, static_cast<uint32_t>(lds), stream, scores,
-                  ids, n, B, K, tokens, choice, lds > 0);
+bool path_fits_lds(int B, int K) { return path_lds_bytes(B, K) > 0; }
+
+hipError_t launch_cosine(const CosArgs& a, hipStream_t stream) {
+    const size_t lds = path_lds_bytes(a.B, a.K);
+    const int nt = (a.K + 15) / 16;
+    const int jobs = (a.B - 1) * nt * nt;
+    const int waves = jobs < 1 ? 1 : (jobs > 16 ? 16 : jobs);
+    return launch(cosine_kernel, dim3(static_cast<unsigned>(a.n)), 64 * waves, static_cast<uint32_t>(lds), stream,
+                  a, lds > 0);
+}
+
+hipError_t launch_path(const float* scores, const int32_t* ids, int n, int B, int K, int rule, int32_t* tokens,
+                       int32_t* choice, hipStream_t stream) {
+    const size_t wl = path_lds_bytes(B, K);
+    const size_t lds = wl ? wl : path_lds_end(B, K, false);
+    return launch(path_kernel, dim3(static_cast<unsigned>(n)), 64, static_cast<uint32_t>(lds), stream, scores,
+                  ids, n, B, K, rule, tokens, choice, wl > 0);
 }
 
 hipError_t launch_finish(const FinishArgs& a, hipStream_t stream) {
-    const size_t lds = walk_lds_bytes(a.B, a.K);
+    const size_t lds = path_lds_bytes(a.B, a.K);
     return launch(finish_kernel, dim3(static_cast<unsigned>(a.n)), 256, static_cast<uint32_t>(lds), stream, a,
                   lds > 0);
 }

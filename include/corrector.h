@@ -16,7 +16,9 @@
  *                    two-layer GELU MLP, or the cosine variant
  *                    S_p(a,b) = l_{p+1}(b) + sigma cos(W_out z_p^a, W_in z_{p+1}^b).
  *   corrector_walk   step (5): prefix-first greedy walk; slot 1 takes the
- *                    drafter argmax, then k_{p+1} = argmax_b S_p(k_p, b).
+ *                    drafter argmax, then k_{p+1} = argmax_b S_p(k_p, b); or,
+ *                    by the descriptor's path rule, the Global-Sum path of
+ *                    LiLiCorr appendix E (Eq. 12) by dynamic programming.
  *   corrector_run    all of the above in one call.
  *
  * Conventions shared by every call
@@ -72,6 +74,17 @@ typedef enum {
 
 enum { CORR_VARIANT_MLP = 0, CORR_VARIANT_COSINE = 1 };
 enum { CORR_DTYPE_BF16 = 0, CORR_DTYPE_F32 = 1 };
+/* How a path is chosen through the candidate lattice (slot 1 is always rank 0,
+ * the drafter's argmax):
+ *   CORR_PATH_GREEDY      the prefix-first walk, k_{p+1} = argmax_b S_p(k_p, b)
+ *                         (DCOCO method details step (5); LiLiCorr section
+ *                         3.5, Eq. 8); ties to the lowest candidate index;
+ *   CORR_PATH_GLOBAL_SUM  the path with the largest summed score
+ *                         sum_p S_p(k_p, k_{p+1}) (LiLiCorr appendix E,
+ *                         Eq. 12), found exactly by dynamic programming; ties
+ *                         to the lowest predecessor index in the forward sweep
+ *                         and the lowest index in the last slot. */
+enum { CORR_PATH_GREEDY = 0, CORR_PATH_GLOBAL_SUM = 1 };
 
 /* Shapes and options fixed at create time.
  *   vocab        V, 1 <= K <= V < 2^31.
@@ -86,7 +99,9 @@ enum { CORR_DTYPE_BF16 = 0, CORR_DTYPE_F32 = 1 };
  *   logits_dtype CORR_DTYPE_BF16 or CORR_DTYPE_F32.
  *   max_requests upper bound on n_req for every call; sizes the workspace.
  *   ln_eps       LayerNorm epsilon (> 0).
- *   sigma        cosine scale (cosine only). */
+ *   sigma        cosine scale (cosine only).
+ *   path_rule    CORR_PATH_GREEDY (0, the default of a zeroed struct) or
+ *                CORR_PATH_GLOBAL_SUM; used by corrector_walk and corrector_run. */
 typedef struct {
     int64_t vocab;
     int32_t slots;
@@ -101,6 +116,7 @@ typedef struct {
     int32_t max_requests;
     float ln_eps;
     float sigma;
+    int32_t path_rule;
 } corrector_desc;
 
 /* Borrowed device pointers to the weights; the caller keeps them alive and
@@ -175,9 +191,10 @@ int corrector_score(const corrector *h, int32_t n_req, const int32_t *ids, const
                     const void *hidden, int64_t h_req_stride, int64_t h_slot_stride,
                     float *scores, void *workspace, size_t workspace_bytes, void *stream);
 
-/* Step (5).  scores [n_req][B-1][K][K] and ids [n_req][B][K] as above.
- * Outputs [n_req][B]: tokens[i][s] = ids[i][s][choice[i][s]] and
- * choice[i][s], with choice[i][0] = 0.  choice may be NULL. */
+/* Step (5), by the handle's path rule.  scores [n_req][B-1][K][K] and ids
+ * [n_req][B][K] as above.  Outputs [n_req][B]: tokens[i][s] =
+ * ids[i][s][choice[i][s]] and choice[i][s], with choice[i][0] = 0.  choice may
+ * be NULL. */
 int corrector_walk(const corrector *h, int32_t n_req, const float *scores, const int32_t *ids,
                    int32_t *tokens, int32_t *choice, void *stream);
 

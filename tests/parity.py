@@ -174,3 +174,51 @@ def check_all(gpu: dict, ora: dict, where: str = "", exact_walk: bool = False, v
 
 def select(gpu: dict, first: int, n: int) -> dict:
     return {k: v[first:first + n] for k, v in gpu.items()}
+
+
+# ------------------------------------------------------- Global-Sum path --
+
+def path_scores(S, choice):
+    """Summed transition score of each request's path: S [n][B-1][K][K],
+    choice [n][B]."""
+    n, P = S.shape[0], S.shape[1]
+    i = np.arange(n)[:, None]
+    p = np.arange(P)[None, :]
+    return S[i, p, choice[:, :-1], choice[:, 1:]].sum(axis=1)
+
+
+def check_global_sum(gpu: dict, ora: dict, cfg: dict, where: str = "", exact: bool = False):
+    """Gates of the Global-Sum path (best summed score, slot 1 at rank 0).
+
+    1. The GPU's path is the oracle's dynamic program run on the GPU's own
+       scores (in float64): identical, or (where the float32 sums of the GPU's
+       sweep meet a near tie) a path whose summed score is within rounding of
+       the optimum.
+    2. Against the oracle's scores, the GPU's path loses at most what the score
+       errors can explain: g*(S_ora) - g(S_ora, path_gpu) <= 2 sum_p eps_p,
+       with eps_p the largest |S_gpu - S_ora| of pair p.
+    With `exact` (identical scores on both sides) the paths must be equal.
+    """
+    n, B = gpu["choice"].shape
+    desc = oracle.OracleDesc.from_config(cfg)
+    assert (gpu["choice"][:, 0] == 0).all(), "slot 1 must stay at rank 0 " + where
+    np.testing.assert_array_equal(gpu["tokens"], np.take_along_axis(gpu["ids"], gpu["choice"][:, :, None], 2)[:, :, 0],
+                                  err_msg="tokens follow the choices " + where)
+    if B < 2:
+        return 0
+    S_g = gpu["scores"].astype(np.float64)
+    scale = max(1.0, float(np.abs(S_g).max()))
+    slack = 1e-5 * (B - 1) * scale
+    _, ch_ref, tot_ref = oracle.viterbi(desc, S_g, gpu["ids"], n)
+    diff = (ch_ref != gpu["choice"]).any(axis=1)
+    own = path_scores(S_g, gpu["choice"])
+    assert (np.abs(own[diff] - tot_ref[diff]) <= slack).all(), \
+        "GPU path not optimal for its own scores %s: %s" % (where, np.abs(own - tot_ref).max())
+    assert diff.mean() <= 0.05, "too many near-tie paths %s: %d of %d" % (where, diff.sum(), n)
+    _, ch_o, tot_o = oracle.viterbi(desc, ora["scores"], ora["ids"], n)
+    eps = np.abs(S_g - ora["scores"]).max(axis=(2, 3)).sum(axis=1)
+    lost = tot_o - path_scores(ora["scores"], gpu["choice"])
+    assert (lost <= 2 * eps + slack).all(), "GPU path loses more than the score error %s" % where
+    if exact:
+        np.testing.assert_array_equal(gpu["choice"], ch_o, err_msg="exact path " + where)
+    return int(diff.sum())

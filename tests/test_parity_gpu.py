@@ -106,6 +106,26 @@ def test_workspace_reuse_across_calls():
         corr.close()
 
 
+# ------------------------------------------------------ Global-Sum path --
+
+@pytest.mark.parametrize("name,head", [("tiny", "normal"), ("tiny", "zero"), ("tiny", "stress"), ("b1", "stress"),
+                                       ("b1", "zero"), ("b32", "stress"), ("cosine", "normal")])
+def test_global_sum_path(name, head):
+    """corrector_run with the Global-Sum path rule (LiLiCorr appendix E): the
+    same scores as the walk configuration, a path that is optimal for them."""
+    _log("global-sum %s head=%s" % (name, head))
+    x = P.inputs(name, head=head, path_rule="global_sum")
+    n = 4 if name == "cosine" else None   # the cosine oracle on a sample of requests
+    gpu = P.gpu_run(x, n=n)
+    ora = P.oracle_run(x, n=n)
+    P.check_topk(gpu, ora, name)
+    P.check_scores(gpu, ora, name)
+    near = P.check_global_sum(gpu, ora, x["cfg"], "%s/%s" % (name, head), exact=(head == "zero"))
+    if head == "zero":
+        assert (gpu["choice"] == 0).all()
+    _log("  near-tie paths: %d" % near)
+
+
 # ---------------------------------------------------------------- cosine --
 
 @pytest.mark.parametrize("sigma", [1.0, 8.0])
