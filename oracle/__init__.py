@@ -6,12 +6,16 @@ package, and this package never imports the GPU library.
 """
 
 from .oracle import (  # noqa: F401
+    CONF_FIELDS,
     OracleDesc,
+    confidence,
     accepted_lengths,
     build,
     gelu,
     get_threads,
     layernorm,
+    log_normaliser,
+    log_normaliser_row,
     param_count,
     represent,
     run,

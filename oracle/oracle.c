@@ -21,6 +21,9 @@
  * path with the largest summed transition score, by dynamic programming.
  * The cosine variant (LiLiCorr, section 3.2, Eq. 1) replaces (3)-(4) by
  *   S_p(a,b) = l_{p+1}(b) + sigma * cos(W_out z_p^a, W_in z_{p+1}^b).
+ * Beside step (1), the log-normaliser of each slot row over the whole
+ * vocabulary (LiLiCorr appendix A), from which the candidates' log-probs and
+ * confidence scalars follow.
  *
  * Readings where the pages are silent (each also listed in the design notes):
  *   - top-K order is value descending, ties to the lowest token id; values
@@ -170,6 +173,50 @@ int oracle_topk(const oracle_desc *D, int32_t n, const void *logits,
         const char *row = (const char *)logits + (size_t)(i * req_stride + s * slot_stride) * esz;
         err |= oracle_topk_row(row, D->logits_dtype, D->V, D->K,
                                ids + t * D->K, vals + t * D->K);
+    }
+    return err;
+}
+
+/* ------------------------------------------- vocabulary normalisation -- */
+
+/* LiLiCorr appendix A (Architecture; Serving): the drafter's distribution at a
+ * slot is the softmax of its logits over the whole vocabulary, so every
+ * log-probability needs the row's log-normaliser log Z = log sum_v exp(l_v).
+ * It is computed as m + log sum_v exp(l_v - m) with m the row maximum (the
+ * same quantity, free of overflow), summing in index order.  A row of -inf
+ * gives -inf.  NaN and +inf logits are rejected (ORA_E_NAN). */
+int oracle_log_normaliser_row(const void *row, int dtype, int64_t V, double *logz)
+{
+    if (!row || !logz || V <= 0) return ORA_E_ARG;
+    double m = -INFINITY;
+    for (int64_t v = 0; v < V; ++v) {
+        double x = logit_at(row, dtype, v);
+        if (isnan(x) || x == INFINITY) return ORA_E_NAN;
+        if (x > m) m = x;
+    }
+    if (m == -INFINITY) {
+        *logz = -INFINITY;
+        return ORA_OK;
+    }
+    double sum = 0.0;
+    for (int64_t v = 0; v < V; ++v) sum += exp(logit_at(row, dtype, v) - m);
+    *logz = m + log(sum);
+    return ORA_OK;
+}
+
+/* The log-normaliser of every drafted slot row of n blocks, rows addressed as
+ * in oracle_topk; logz is [n][B]. */
+int oracle_log_normaliser(const oracle_desc *D, int32_t n, const void *logits,
+                          int64_t req_stride, int64_t slot_stride, double *logz)
+{
+    if (!D || !logits || !logz || n < 0) return ORA_E_ARG;
+    const size_t esz = D->logits_dtype == ORA_BF16 ? 2 : 4;
+    int err = ORA_OK;
+#pragma omp parallel for schedule(dynamic) reduction(| : err)
+    for (int64_t t = 0; t < (int64_t)n * D->B; ++t) {
+        int64_t i = t / D->B, s = t % D->B;
+        const char *row = (const char *)logits + (size_t)(i * req_stride + s * slot_stride) * esz;
+        err |= oracle_log_normaliser_row(row, D->logits_dtype, D->V, logz + t);
     }
     return err;
 }

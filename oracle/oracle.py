@@ -54,6 +54,8 @@ def _load():
         lib.oracle_param_count.argtypes = [P]
         lib.oracle_topk_row.argtypes = [P, C.c_int, C.c_int64, C.c_int32, P, P]
         lib.oracle_topk.argtypes = [P, C.c_int32, P, C.c_int64, C.c_int64, P, P]
+        lib.oracle_log_normaliser_row.argtypes = [P, C.c_int, C.c_int64, P]
+        lib.oracle_log_normaliser.argtypes = [P, C.c_int32, P, C.c_int64, C.c_int64, P]
         lib.oracle_represent.argtypes = [P, P, C.c_int32, P, P, C.c_int64, C.c_int64, P, P, P, P]
         lib.oracle_score.argtypes = [P, P, C.c_int32, P, P, P, P, P]
         lib.oracle_walk.argtypes = [P, C.c_int32, P, P, P, P]
@@ -182,6 +184,57 @@ def topk(desc: OracleDesc, logits, n: int, req_stride: int, slot_stride: int, of
     _check(_load().oracle_topk(C.byref(d), n, _ptr(base), req_stride, slot_stride,
                                _ptr(ids), _ptr(vals)), "topk")
     return ids, vals
+
+
+def log_normaliser_row(row) -> float:
+    """log sum_v exp(l_v) of one row (float32 array, or uint16 array of bfloat16 bits)."""
+    row = np.ascontiguousarray(row)
+    dt = 0 if row.dtype == np.uint16 else 1
+    if dt == 1:
+        row = np.ascontiguousarray(row, dtype=np.float32)
+    out = np.empty(1, np.float64)
+    _check(_load().oracle_log_normaliser_row(_ptr(row), dt, row.size, _ptr(out)), "log_normaliser_row")
+    return float(out[0])
+
+
+def log_normaliser(desc: OracleDesc, logits, n: int, req_stride: int, slot_stride: int, offset: int = 0):
+    """log Z of every drafted slot row, [n][B]; rows addressed as in topk."""
+    dt = np.uint16 if desc.logits_dtype == "bf16" else np.float32
+    flat = np.ascontiguousarray(logits, dtype=dt).reshape(-1)
+    logz = np.empty((n, desc.B), np.float64)
+    d = desc.c()
+    _check(_load().oracle_log_normaliser(C.byref(d), n, _ptr(flat[offset:]), req_stride, slot_stride,
+                                         _ptr(logz)), "log_normaliser")
+    return logz
+
+
+CONF_FIELDS = ("logprob", "prob", "gap", "rank", "top")
+
+
+def confidence(vals, logz) -> np.ndarray:
+    """The five confidence scalars of every candidate (LiLiCorr appendix A,
+    Architecture), read from the drafter's distribution at its slot:
+    vals [..., K] are the candidates' logits in top-K order and logz [...] the
+    slot's log-normaliser.  Last axis, in CONF_FIELDS order:
+      logprob  l - log Z;
+      prob     exp(l - log Z);
+      gap      log-prob of the slot's most likely token minus the candidate's
+               (>= 0; the most likely token is rank 0 of the top-K);
+      rank     the candidate's rank r in 0..K-1 scaled to [0, 1] as r / (K-1)
+               (0 when K = 1);
+      top      1 for rank 0, else 0.
+    """
+    vals = np.asarray(vals, dtype=np.float64)
+    logz = np.asarray(logz, dtype=np.float64)
+    K = vals.shape[-1]
+    logp = vals - logz[..., None]
+    out = np.empty(vals.shape + (5,))
+    out[..., 0] = logp
+    out[..., 1] = np.exp(logp)
+    out[..., 2] = logp[..., :1] - logp
+    out[..., 3] = np.arange(K) / max(K - 1, 1)
+    out[..., 4] = (np.arange(K) == 0)
+    return out
 
 
 def represent(desc: OracleDesc, weights: dict, embed, ids, hidden, n: int,

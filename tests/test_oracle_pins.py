@@ -415,6 +415,108 @@ def test_viterbi_dominates_the_walk_and_ignores_pair_offsets():
         np.testing.assert_allclose(total2, total + c.sum(axis=(1, 2, 3)), atol=1e-9)
 
 
+# ------------------------------------------- vocabulary normalisation --
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_log_normaliser_matches_scipy(dtype):
+    from scipy.special import logsumexp
+    rng = np.random.default_rng(5)
+    for V in (1, 7, 1000, 151936):
+        x = (rng.standard_normal(V) * 3 + rng.standard_normal() * 10).astype(np.float32)
+        row = f32_to_bf16_bits(x) if dtype == "bf16" else x
+        exact = bf16_bits_to_f32(row).astype(np.float64) if dtype == "bf16" else x.astype(np.float64)
+        want = logsumexp(exact)
+        assert abs(oracle.log_normaliser_row(row) - want) <= 1e-12 * max(1.0, abs(want))
+
+
+def test_log_normaliser_closed_forms():
+    # uniform row: log(V e^c) = c + log V
+    for c, V in ((0.0, 151936), (-3.5, 1000), (17.25, 5)):
+        got = oracle.log_normaliser_row(np.full(V, c, np.float32))
+        assert abs(got - (c + np.log(V))) <= 1e-12 * max(1.0, abs(got))
+    # two values, a copies of x1 and b copies of x2: log(a e^x1 + b e^x2)
+    x1, x2, a, b = 2.0, -1.0, 3, 40
+    row = np.array([x1] * a + [x2] * b, np.float32)
+    want = np.log(a * np.exp(x1) + b * np.exp(x2))
+    assert abs(oracle.log_normaliser_row(row) - want) <= 1e-13
+    # one finite entry among -inf: that entry; all -inf: -inf
+    row = np.full(64, -np.inf, np.float32)
+    row[17] = 4.5
+    assert oracle.log_normaliser_row(row) == 4.5
+    assert oracle.log_normaliser_row(np.full(64, -np.inf, np.float32)) == -np.inf
+    # near the float32 maximum the sum of exponentials would overflow; the
+    # normaliser is still max + log(count of the maximum)
+    big = np.float32(3.0e38)
+    row = np.array([big, big, -big, 0.0], np.float32)
+    assert abs(oracle.log_normaliser_row(row) - (float(big) + np.log(2.0))) <= 1e-12 * float(big)
+
+
+def test_log_normaliser_rejects_nan_and_pos_inf():
+    for bad in (np.nan, np.inf):
+        row = np.zeros(8, np.float32)
+        row[3] = bad
+        with pytest.raises(RuntimeError):
+            oracle.log_normaliser_row(row)
+
+
+def test_log_normaliser_rows_skip_the_anchor():
+    cfg = config("tiny")
+    x = gen_inputs(cfg)
+    d = oracle.OracleDesc.from_config(cfg)
+    V, B, n = cfg["V"], cfg["B"], cfg["n"]
+    logz = oracle.log_normaliser(d, x["logits"], n, (B + 1) * V, V, offset=V)
+    rows = x["logits"].reshape(n, B + 1, V)
+    for i in range(n):
+        for s in range(B):
+            assert logz[i, s] == oracle.log_normaliser_row(rows[i, s + 1])
+
+
+def test_confidence_worked_example():
+    # logits (2, 1, 0), K = 2: softmax of (2, 1, 0) and log Z = log(e^2 + e + 1)
+    logz = oracle.log_normaliser_row(np.array([2.0, 1.0, 0.0], np.float32))
+    assert abs(logz - 2.40760596444438) <= 1e-13
+    ids, vals = oracle.topk_row(np.array([2.0, 1.0, 0.0], np.float32), 2)
+    c = oracle.confidence(vals, np.float64(logz))
+    want = np.array([[-0.40760596444438013, 0.6652409557748219, 0.0, 0.0, 1.0],
+                     [-1.4076059644443801, 0.24472847105479764, 1.0, 1.0, 0.0]])
+    np.testing.assert_allclose(c, want, rtol=0, atol=1e-13)
+    assert list(oracle.CONF_FIELDS) == ["logprob", "prob", "gap", "rank", "top"]
+
+
+def test_confidence_over_the_whole_vocabulary():
+    """With K = V the candidates are the whole distribution: probabilities sum
+    to one and descend, the gap ascends from zero, ranks span [0, 1] evenly and
+    exactly one candidate is the top choice.  K = 1 has rank 0."""
+    import math
+    rng = np.random.default_rng(8)
+    V = 300
+    row = f32_to_bf16_bits((rng.standard_normal(V) * 2).astype(np.float32))
+    ids, vals = oracle.topk_row(row, V)
+    c = oracle.confidence(vals, oracle.log_normaliser_row(row))
+    assert abs(math.fsum(c[:, 1]) - 1.0) <= 1e-12
+    assert (np.diff(c[:, 1]) <= 0).all() and (np.diff(c[:, 2]) >= 0).all() and c[0, 2] == 0
+    np.testing.assert_allclose(np.exp(c[:, 0]), c[:, 1], rtol=1e-15)
+    np.testing.assert_array_equal(c[:, 3], np.arange(V) / (V - 1))
+    assert c[:, 4].sum() == 1 and c[0, 4] == 1
+    one = oracle.confidence(vals[:1], oracle.log_normaliser_row(row))
+    assert one[0, 3] == 0 and one[0, 4] == 1
+
+
+def test_confidence_shift_invariance():
+    """Softmax ignores a constant added to every logit: log-probs, probabilities
+    and gaps do not move, log Z moves by the constant."""
+    rng = np.random.default_rng(9)
+    x = rng.integers(-40, 40, 500).astype(np.float32) / 4   # exact in float32 after any shift below
+    ids, vals = oracle.topk_row(x, 16)
+    base = oracle.confidence(vals, oracle.log_normaliser_row(x))
+    for c in (7.0, -13.5):
+        ids2, vals2 = oracle.topk_row(x + np.float32(c), 16)
+        lz = oracle.log_normaliser_row(x + np.float32(c))
+        assert abs(lz - (oracle.log_normaliser_row(x) + c)) <= 1e-12
+        np.testing.assert_array_equal(ids2, ids)
+        np.testing.assert_allclose(oracle.confidence(vals2, lz), base, rtol=0, atol=1e-12)
+
+
 # -------------------------------------------------------- cosine variant --
 
 def test_cosine_scores_match_torch_and_bound():
