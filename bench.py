@@ -64,6 +64,11 @@ def algorithmic_work(cfg: dict, n: int) -> dict:
                              per_unit=V * esz, units=rows)
     w["topk_merge"] = dict(bound="hbm", bytes=rows * K * 8, per_unit=K * 8, units=rows,
                            unit="slot row (K ids + values out)")
+    # the fused top-K + normalisation reads the same logits once; its merge
+    # also writes log Z and five confidence scalars per candidate
+    w["topk_partial_lse"] = dict(w["topk_partial"])
+    w["topk_merge_lse"] = dict(bound="hbm", bytes=rows * (K * 8 + 4 + K * 20), per_unit=K * 28 + 4, units=rows,
+                               unit="slot row (K ids, values, 5 scalars and log Z out)")
     hn = 3 * r if cfg["variant"] == "mlp" else r
     w["hproj"] = dict(bound="hbm", bytes=rows * d * 2 + hn * d * 2, flops=2 * rows * d * hn,
                       per_unit=d * 2, units=rows, unit="hidden row")
@@ -101,6 +106,73 @@ def algorithmic_work(cfg: dict, n: int) -> dict:
     return w
 
 
+def measure_topk_softmax(corr, cfg, dev_sets, host_logits, st, stream, steps, warmup, cpu=True) -> dict:
+    """corrector_topk_softmax (with the confidence scalars) over the same
+    rotated logits, beside plain corrector_topk; the partial kernel's HBM rate
+    against the peak; the oracle (top-K, log Z and scalars) on one batch."""
+    import torch
+    n, B, K = cfg["n"], cfg["B"], cfg["K"]
+    ids = torch.empty((n, B, K), dtype=torch.int32, device="cuda")
+    vals = torch.empty((n, B, K), dtype=torch.float32, device="cuda")
+    logz = torch.empty((n, B), dtype=torch.float32, device="cuda")
+    conf = torch.empty((n, B, K, 5), dtype=torch.float32, device="cuda")
+    ws = corr.new_workspace(n)
+
+    def fused(i):
+        corr.topk_softmax(n, dev_sets[i % len(dev_sets)]["logits"], st["l_req"], st["l_slot"], ids, vals, logz, ws,
+                          conf=conf, offset=st["l_off"], stream=stream)
+
+    def plain(i):
+        corr.topk(n, dev_sets[i % len(dev_sets)]["logits"], st["l_req"], st["l_slot"], ids, vals, ws,
+                  offset=st["l_off"], stream=stream)
+
+    out = {}
+    for name, fn in (("fused", fused), ("topk_only", plain)):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(steps):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / steps
+        corr.set_timing(True)
+        per = {}
+        for i in range(steps):
+            fn(i)
+            for k, t in corr.kernel_times():
+                per.setdefault(k, []).append(t)
+        corr.set_timing(False)
+        torch.cuda.synchronize()
+        out[name] = dict(us=round(ms * 1e3, 3), kernels_us={k: round(float(np.mean(v)) * 1e3, 3)
+                                                            for k, v in per.items()})
+    work = algorithmic_work(cfg, n)["topk_partial_lse"]
+    t = out["fused"]["kernels_us"]["topk_partial_lse"] / 1e6
+    gbs = work["bytes"] / t / 1e9
+    res = {"value": round(n * B / (out["fused"]["us"] / 1e6), 1), "unit": "slot rows/s",
+           "call": "corrector_topk_softmax (ids, values, log Z, 5 scalars per candidate)",
+           "us": out["fused"]["us"], "kernels_us": out["fused"]["kernels_us"],
+           "topk_only_us": out["topk_only"]["us"],
+           "roofline": {"bound": "hbm", "kernel": "topk_partial_lse", "achieved": round(gbs, 1),
+                        "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+    if cpu:
+        import oracle
+        oracle.build(force=False)
+        d = oracle.OracleDesc.from_config(cfg)
+        V = cfg["V"]
+        t0 = time.perf_counter()
+        _, ov = oracle.topk(d, host_logits, n, (B + 1) * V, V, offset=V)
+        oz = oracle.log_normaliser(d, host_logits, n, (B + 1) * V, V, offset=V)
+        oracle.confidence(ov, oz)
+        el = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(n * B / el, 1), "unit": "slot rows/s", "cores": oracle.get_threads(),
+                               "kind": "oracle", "sample": "one %d-row batch: full-sort top-K, log Z and scalars "
+                                                           "(%.1f s)" % (n * B, el)}
+    return res
+
+
 def cpu_baseline(cfg, inputs, min_seconds: float = 12.0, max_passes: int = 64) -> dict:
     import oracle
     oracle.build(force=False)
@@ -130,6 +202,8 @@ def main():
     ap.add_argument("--path-rule", default="greedy", choices=["greedy", "global_sum"],
                     help="how the path through the candidate lattice is chosen")
     ap.add_argument("--no-fold", action="store_true", help="skip the folded-table measurement")
+    ap.add_argument("--no-softmax", action="store_true",
+                    help="skip the fused top-K + normalisation measurement")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of this many MiB (a known-size reference "
                          "for hardware traffic counters)")
@@ -241,6 +315,13 @@ def main():
         log("folded pass: %.2f us" % (fms * 1e3))
         del table
 
+    fused_softmax = None
+    if not args.no_softmax:
+        fused_softmax = measure_topk_softmax(corr, cfg, dev_sets, sets[0]["logits"], st, stream, args.steps,
+                                             args.warmup, cpu=not args.no_cpu_baseline)
+        log("fused top-K + normalisation: %.2f us (top-K alone %.2f us)"
+            % (fused_softmax["us"], fused_softmax["topk_only_us"]))
+
     work = algorithmic_work(cfg, n)
     dom = max(avg, key=avg.get)
     wk = work[dom]
@@ -300,6 +381,7 @@ def main():
         "kernels": kernels,
         "cpu_baseline": cpu,
         "folded_table": folded,
+        "fused_softmax": fused_softmax,
     }
     print(json.dumps(out), flush=True)
     corr.close()

@@ -23,7 +23,7 @@ STATUS = {0: "CORR_OK", 1: "CORR_E_NULL", 2: "CORR_E_SHAPE", 3: "CORR_E_UNSUPPOR
 
 # exported symbols declared in include/corrector.h
 SYMBOLS = ("corrector_create", "corrector_destroy", "corrector_workspace_bytes",
-           "corrector_topk", "corrector_score", "corrector_walk", "corrector_run",
+           "corrector_topk", "corrector_topk_softmax", "corrector_score", "corrector_walk", "corrector_run",
            "corrector_intermediates", "corrector_set_timing", "corrector_kernel_times",
            "corrector_status_string", "corrector_table_bytes", "corrector_fold_table",
            "corrector_use_table")
@@ -72,6 +72,7 @@ def load(path: str = LIB_PATH):
     lib.corrector_workspace_bytes.argtypes = [P, I32]
     lib.corrector_workspace_bytes.restype = SZ
     lib.corrector_topk.argtypes = [P, I32, P, I64, I64, P, P, P, SZ, P]
+    lib.corrector_topk_softmax.argtypes = [P, I32, P, I64, I64, P, P, P, P, P, SZ, P]
     lib.corrector_score.argtypes = [P, I32, P, P, P, I64, I64, P, P, SZ, P]
     lib.corrector_walk.argtypes = [P, I32, P, P, P, P, P]
     lib.corrector_run.argtypes = [P, I32, P, I64, I64, P, I64, I64, P, P, P, P, P, P, SZ, P]
@@ -84,7 +85,7 @@ def load(path: str = LIB_PATH):
     lib.corrector_use_table.argtypes = [P, P]
     lib.corrector_status_string.argtypes = [C.c_int]
     lib.corrector_status_string.restype = C.c_char_p
-    for fn in ("corrector_topk", "corrector_score", "corrector_walk", "corrector_run",
+    for fn in ("corrector_topk", "corrector_topk_softmax", "corrector_score", "corrector_walk", "corrector_run",
                "corrector_intermediates", "corrector_set_timing", "corrector_kernel_times",
                "corrector_fold_table", "corrector_use_table"):
         getattr(lib, fn).restype = C.c_int
@@ -157,6 +158,13 @@ class Corrector:
         _ok("corrector_topk", self.lib.corrector_topk(self.h, n, base, req_stride, slot_stride,
                                                       _p(ids), _p(vals), _p(ws), ws.numel(),
                                                       _stream(stream)))
+
+    def topk_softmax(self, n, logits, req_stride, slot_stride, ids, vals, logz, ws, conf=None,
+                     offset: int = 0, stream=None):
+        base = _p(logits) + offset * logits.element_size()
+        _ok("corrector_topk_softmax", self.lib.corrector_topk_softmax(
+            self.h, n, base, req_stride, slot_stride, _p(ids), _p(vals), _p(logz), _p(conf), _p(ws),
+            ws.numel(), _stream(stream)))
 
     def score(self, n, ids, vals, hidden, h_req_stride, h_slot_stride, scores, ws, offset: int = 0,
               stream=None):

@@ -28,7 +28,7 @@ constexpr int kMaxKernels = 12;
 constexpr size_t kAlign = 256;
 
 struct Layout {
-    size_t part, ids, vals, hproj, upart, z, g, s, uv, vout, vin, mlp_part, scores, total;
+    size_t part, lse, ids, vals, hproj, upart, z, g, s, uv, vout, vin, mlp_part, scores, total;
     int chunks, splits, usplits;
 };
 
@@ -83,6 +83,7 @@ Layout layout(const corrector_desc& d, int32_t n) {
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o = up(o + bytes); return at; };
     L.part = take(sizeof(uint64_t) * rows * L.chunks * d.k);
+    L.lse = take(sizeof(float) * 2 * rows * L.chunks);
     L.ids = take(sizeof(int32_t) * rows * d.k);
     L.vals = take(sizeof(float) * rows * d.k);
     L.hproj = take(sizeof(float) * L.splits * rows * 3 * d.r);
@@ -181,17 +182,22 @@ const char* path_name(const corrector* h) { return h->d.path_rule == CORR_PATH_G
 
 // Step (1).  With `hj` given, the hidden-state projection runs in the merge
 // launch (it does not depend on the top-K).
+// Step (1); with logz given, also the rows' log-normalisers (and, with conf,
+// the confidence scalars) from the same pass over the logits.
 void enqueue_topk(Seq& q, const corrector* h, const Layout& L, int32_t n, const void* logits,
-                  int64_t rs, int64_t ss, int32_t* ids, float* vals, void* ws, const GemmJob* hj) {
+                  int64_t rs, int64_t ss, int32_t* ids, float* vals, void* ws, const GemmJob* hj,
+                  float* logz = nullptr, float* conf = nullptr) {
     const corrector_desc& d = h->d;
     const int64_t rows = static_cast<int64_t>(n) * d.slots;
     uint64_t* part = at<uint64_t>(ws, L.part);
-    q("topk_partial", [&] {
+    float2* lse = logz ? at<float2>(ws, L.lse) : nullptr;
+    q(logz ? "topk_partial_lse" : "topk_partial", [&] {
         return launch_topk_partial(d.logits_dtype, logits, rs, ss, d.slots, d.vocab, d.k, L.chunks,
-                                   rows, part, q.s);
+                                   rows, part, lse, q.s);
     });
-    q(hj ? "topk_merge_hproj" : "topk_merge",
-      [&] { return launch_topk_merge(d.logits_dtype, part, L.chunks, d.k, rows, ids, vals, hj, q.s); });
+    q(hj ? "topk_merge_hproj" : (logz ? "topk_merge_lse" : "topk_merge"), [&] {
+        return launch_topk_merge(d.logits_dtype, part, L.chunks, d.k, rows, ids, vals, lse, logz, conf, hj, q.s);
+    });
 }
 
 // The hidden-state projection: hproj rows are [W_ctx h | W_pair,L h |
@@ -447,6 +453,23 @@ int corrector_topk(const corrector* hc, int32_t n, const void* logits, int64_t r
     if (h->timing) lock.lock();
     Seq q{h, static_cast<hipStream_t>(stream)};
     enqueue_topk(q, h, L, n, logits, rs, ss, ids, vals, ws, nullptr);
+    return q.finish();
+}
+
+int corrector_topk_softmax(const corrector* hc, int32_t n, const void* logits, int64_t rs, int64_t ss,
+                           int32_t* ids, float* vals, float* logz, float* conf, void* ws, size_t ws_bytes,
+                           void* stream) {
+    int rc = check_n(hc, n);
+    if (rc || n == 0) return rc;
+    if ((rc = check_logits(hc, logits, rs, ss))) return rc;
+    if (!ids || !vals || !logz) return CORR_E_NULL;
+    if ((rc = check_ws(hc, n, ws, ws_bytes))) return rc;
+    corrector* h = const_cast<corrector*>(hc);
+    const Layout L = layout(h->d, n);
+    std::unique_lock<std::mutex> lock(h->mu, std::defer_lock);
+    if (h->timing) lock.lock();
+    Seq q{h, static_cast<hipStream_t>(stream)};
+    enqueue_topk(q, h, L, n, logits, rs, ss, ids, vals, ws, nullptr, logz, conf);
     return q.finish();
 }
 

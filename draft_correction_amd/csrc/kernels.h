@@ -45,10 +45,13 @@ constexpr int kMaxUSplits = 4;
 // ---- top-K (topk.hip)
 // part [rows][chunks][K]: each chunk's K best as 64-bit composites
 // (float32-order value key << 32 | inverted token id; 0 = no element).
+// lse_part [rows][chunks] (optional): each chunk's (max, sum of exp(l - max)).
 int topk_chunk_elems(int dtype);
 hipError_t launch_topk_partial(int dtype, const void* logits, int64_t req_stride,
                                int64_t slot_stride, int B, int64_t V, int K, int chunks,
-                               int64_t rows, uint64_t* part, hipStream_t stream);
+                               int64_t rows, uint64_t* part, float2* lse_part, hipStream_t stream);
+// Confidence scalars per candidate: log-prob, probability, gap, rank, top flag.
+constexpr int kConfFields = 5;
 // ---- projections (proj.hip)
 // Tiled GEMM C[split][m][n] = sum_k A[m][k] W[n][k] (bf16 in, float32 out).
 #define GEMM_A_DENSE 0
@@ -86,10 +89,12 @@ hipError_t launch_gemm2(const GemmJob& j0, const GemmJob& j1, hipStream_t stream
 // Workgroups a GEMM job occupies in a launch.
 int64_t gemm_launch_blocks(const GemmJob& j);
 
-// The K winners of every row, in order, from the chunks' composites; with a
-// GEMM job given, its tiles run in the same launch (after the merge waves).
+// The K winners of every row, in order, from the chunks' composites; with
+// lse_part given, also logz [rows] and (conf non-null) conf [rows][K][5]; with
+// a GEMM job given, its tiles run in the same launch (after the merge waves).
 hipError_t launch_topk_merge(int dtype, const uint64_t* part, int chunks, int K, int64_t rows, int32_t* ids,
-                             float* vals, const GemmJob* hj, hipStream_t stream);
+                             float* vals, const float2* lse_part, float* logz, float* conf, const GemmJob* hj,
+                             hipStream_t stream);
 
 // Per drafted slot: b = LN(u) with u = W_cand E[ids], g = LN(W_ctx h) per slot,
 // z = gamma * LN(W_fuse [b; g]) + beta stored as bfloat16 hi/lo halves

@@ -21,6 +21,13 @@
 //                 written in order.
 // Keys map float bits to an unsigned integer order with -0 == +0, so the
 // selection is exact integer work: results are bit-identical to a full sort.
+//
+// Optionally (the fused top-K and vocabulary-wide normalisation of LiLiCorr
+// appendix A) every partial wave also leaves its chunk's share of the row's
+// softmax normaliser, the pair (m, s) with m the chunk maximum and
+// s = sum of exp(l - m) over the chunk, from the registers the top-K already
+// holds; the merge wave folds a row's pairs into log Z and writes the
+// candidates' log-probs and confidence scalars.
 #include "common.h"
 #include "gemm.h"
 #include "kernels.h"
@@ -60,7 +67,44 @@ __device__ __forceinline__ uint64_t merge_comp(uint32_t key32, int64_t gid) {
     return (static_cast<uint64_t>(key32) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(gid));
 }
 
-// ------------------------------------------------------------- bf16 path --
+// ------------------------------------------------- softmax normaliser --
+constexpr float kLog2e = 1.44269504088896341f;
+
+// Wave-wide sum and maximum over the 64 lanes, the same value in every lane
+// (fixed combination order, so the results are deterministic).
+__device__ __forceinline__ float wave_sum64(float v) {
+    const float r = row16_sum(v);
+    return (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 0)) +
+            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 16))) +
+           (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 32)) +
+            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 48)));
+}
+__device__ __forceinline__ float wave_max64(float v) {
+    const float r = row16_max(v);
+    return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 0)),
+                       __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 16))),
+                 fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 32)),
+                       __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 48))));
+}
+
+// exp(x - ref) as 2^((x - ref) log2 e); x = -inf gives 0.
+__device__ __forceinline__ float exp_rel(float x, float ref) {
+    return __builtin_amdgcn_exp2f((x - ref) * kLog2e);
+}
+
+// A reference point for sums of exp(x - m): m itself, or 0 when m = -inf (the
+// lane or chunk holds no finite value, every term is 0, and -inf - -inf must
+// not be formed).
+__device__ __forceinline__ float exp_ref(float m) { return m == -INFINITY ? 0.f : m; }
+
+// The chunk's (m, s) from every lane's maximum ml and sum sl of exp(x - ref(ml)).
+__device__ __forceinline__ float2 chunk_expsum(float ml, float sl) {
+    const float m = wave_max64(ml);
+    const float ref = exp_ref(m);
+    return make_float2(m, wave_sum64(sl * exp_rel(exp_ref(ml), ref)));
+}
+
+// --------------------------------------------------------------- bf16 path --
 
 // Bf16 element `local` of a chunk (0xFFFF, key 0, past the end).
 __device__ __forceinline__ uint32_t chunk_elem(const uint16_t* src, int nvalid, int local) {
@@ -171,19 +215,10 @@ __device__ __forceinline__ uint32_t hit_mask(const u32x4 (&raw)[kNV], uint32_t b
     return hm;
 }
 
-// The exact top-K of one register-resident chunk, written to part[the chunk's
-// K slots] as merge composites (padded with 0 = "no element").  The LDS lists
-// have one trash slot per lane past their capacity, so every list write is
-// issued by every lane (no branches): lanes with nothing to add write there.
-__device__ __forceinline__ void select_chunk(const u32x4 (&raw)[kNV], const Chunk& c, int K, uint32_t chunks,
-                                             u32x4* stage, uint16_t* meta, uint32_t* cand, uint64_t* outb,
-                                             uint64_t* __restrict__ part) {
-    constexpr int kChunk = kNV * 8 * kWave;
-    const int l = lane_id();
-    const int64_t c0 = static_cast<int64_t>(c.chunk) * kChunk;
-
-    // ---- lane maximum: signed max finds the largest positive, unsigned min the
-    // negative closest to zero; together they give the largest value.
+// The key16 of the lane's largest element: signed max finds the largest
+// positive, unsigned min the negative closest to zero; together they give the
+// largest value (key 0 when the lane holds padding only).
+__device__ __forceinline__ uint32_t lane_key_bf16(const u32x4 (&raw)[kNV]) {
     uint32_t mxp = 0x80008000u, mnp = 0xFFFFFFFFu;
 #pragma unroll
     for (int t = 0; t < kNV; ++t)
@@ -195,7 +230,62 @@ __device__ __forceinline__ void select_chunk(const u32x4 (&raw)[kNV], const Chun
     const int mx16 = max(static_cast<int>(static_cast<int16_t>(mxp & 0xFFFFu)),
                          static_cast<int>(static_cast<int16_t>(mxp >> 16)));
     const uint32_t mn16 = min(mnp & 0xFFFFu, mnp >> 16);
-    const uint32_t lane_key = key16_of(mx16 >= 0 ? static_cast<uint32_t>(mx16) : mn16);
+    return key16_of(mx16 >= 0 ? static_cast<uint32_t>(mx16) : mn16);
+}
+
+// Sums of exp(x - ref) over a lane's elements take one fma per element:
+// exp(x - ref) = 2^(x log2e - m2) * 2^c with m2 = fl(ref log2e) and
+// c = ref log2e - m2, the rounding of that product, which an fma recovers
+// exactly; the lane's sum of 2^(x log2e - m2) is scaled by 2^c once.  Where
+// ref log2e would overflow (|ref| >= 2^126) the lane subtracts first instead.
+constexpr float kFmaRefLimit = 0x1p126f;
+
+template <bool kPad, bool kFma>
+__device__ __forceinline__ float lane_sum_bf16(const u32x4 (&raw)[kNV], float ref, float m2) {
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int t = 0; t < kNV; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t w = raw[t][q];
+            float lo = __uint_as_float(w << 16), hi = __uint_as_float(w & 0xFFFF0000u);
+            if (kPad) {
+                lo = (w & 0xFFFFu) == 0xFFFFu ? -INFINITY : lo;
+                hi = (w >> 16) == 0xFFFFu ? -INFINITY : hi;
+            }
+            s0 += kFma ? __builtin_amdgcn_exp2f(fmaf(lo, kLog2e, -m2)) : exp_rel(lo, ref);
+            s1 += kFma ? __builtin_amdgcn_exp2f(fmaf(hi, kLog2e, -m2)) : exp_rel(hi, ref);
+        }
+    return s0 + s1;
+}
+
+// The lane's (maximum, sum of exp(x - ref)) over its elements.  kPad: the
+// chunk is a row's last, shorter one, whose padding (0xFFFF) counts as -inf.
+template <bool kPad>
+__device__ __forceinline__ float2 lane_expsum_bf16(const u32x4 (&raw)[kNV], uint32_t lane_key) {
+    const float m = lane_key ? __uint_as_float(raw16_of_key16(lane_key) << 16) : -INFINITY;
+    const float ref = exp_ref(m);
+    float s;
+    if (fabsf(ref) < kFmaRefLimit) {
+        const float m2 = ref * kLog2e;
+        const float c = fmaf(ref, kLog2e, -m2);
+        s = lane_sum_bf16<kPad, true>(raw, ref, m2) * __builtin_amdgcn_exp2f(c);
+    } else {
+        s = lane_sum_bf16<kPad, false>(raw, ref, 0.f);
+    }
+    return make_float2(m, s);
+}
+
+// The exact top-K of one register-resident chunk, written to part[the chunk's
+// K slots] as merge composites (padded with 0 = "no element").  The LDS lists
+// have one trash slot per lane past their capacity, so every list write is
+// issued by every lane (no branches): lanes with nothing to add write there.
+__device__ __forceinline__ void select_chunk(const u32x4 (&raw)[kNV], uint32_t lane_key, const Chunk& c, int K,
+                                             uint32_t chunks, u32x4* stage, uint16_t* meta, uint32_t* cand,
+                                             uint64_t* outb, uint64_t* __restrict__ part) {
+    constexpr int kChunk = kNV * 8 * kWave;
+    const int l = lane_id();
+    const int64_t c0 = static_cast<int64_t>(c.chunk) * kChunk;
 
     // ---- threshold: the target-th largest lane maximum (at least `target`
     // distinct elements are >= it, so the chunk's top-`target` are too)
@@ -314,9 +404,11 @@ __device__ __forceinline__ void select_chunk(const u32x4 (&raw)[kNV], const Chun
 // One wave per chunk.  The full chunks (all but a row's shorter last one) are
 // numbered f = row * full + chunk and come first; the rows' shorter last
 // chunks follow.  Each chunk's result slot is fixed by its (row, chunk).
+// kLse: also write the chunk's normaliser pair to lse_part[row * chunks + chunk].
+template <bool kLse>
 __global__ __launch_bounds__(256) void topk_partial_bf16_kernel(
     const uint16_t* __restrict__ logits, int64_t req_stride, int64_t slot_stride, int B, int64_t V,
-    int K, int chunks, int64_t rows, uint64_t* __restrict__ part) {
+    int K, int chunks, int64_t rows, uint64_t* __restrict__ part, float2* __restrict__ lse_part) {
     constexpr int kChunk = kNV * 8 * kWave;
     __shared__ u32x4 stage_all[4][kStage + kWave];
     __shared__ uint16_t meta_all[4][kStage + kWave];
@@ -347,14 +439,21 @@ __global__ __launch_bounds__(256) void topk_partial_bf16_kernel(
         load_full_chunk(raw, c.src);
     else
         load_ragged_chunk(raw, c);
-    select_chunk(raw, c, K, uch, stage_all[wave], meta_all[wave], cand_all[wave], out_all[wave], part);
+    const uint32_t lane_key = lane_key_bf16(raw);
+    if (kLse) {
+        const float2 ls = w < nfull ? lane_expsum_bf16<false>(raw, lane_key) : lane_expsum_bf16<true>(raw, lane_key);
+        const float2 cs = chunk_expsum(ls.x, ls.y);
+        if (lane_id() == 0) lse_part[static_cast<int64_t>(c.row) * uch + c.chunk] = cs;
+    }
+    select_chunk(raw, lane_key, c, K, uch, stage_all[wave], meta_all[wave], cand_all[wave], out_all[wave], part);
 }
 
 // ---------------------------------------------------------- float32 path --
 // Generic version on 32-bit value keys (used for float32 logits).
+template <bool kLse>
 __global__ __launch_bounds__(256) void topk_partial_f32_kernel(
     const float* __restrict__ logits, int64_t req_stride, int64_t slot_stride, int B, int64_t V,
-    int K, int chunks, int64_t rows, uint64_t* __restrict__ part) {
+    int K, int chunks, int64_t rows, uint64_t* __restrict__ part, float2* __restrict__ lse_part) {
     constexpr int kEPV = 4;
     constexpr int kChunk = kNV * kEPV * kWave;  // 4096 logits per wave
     __shared__ uint64_t cand_all[4][kCap];
@@ -388,6 +487,26 @@ __global__ __launch_bounds__(256) void topk_partial_f32_kernel(
     for (int t = 0; t < kNV; ++t)
 #pragma unroll
         for (int j = 0; j < kEPV; ++j) mx = max(mx, key_of_bits(raw[t][j]));
+    if (kLse) {
+        // padding (0xFFFFFFFF, key 0) counts as -inf
+        const float m = mx > kKeyFloor ? __uint_as_float(bits_of_key(mx)) : -INFINITY;
+        const float ref = exp_ref(m);
+        const bool fma_ok = fabsf(ref) < kFmaRefLimit;
+        const float m2 = fma_ok ? ref * kLog2e : 0.f;
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int t = 0; t < kNV; ++t)
+#pragma unroll
+            for (int j = 0; j < kEPV; j += 2) {
+                const float x0 = raw[t][j] == 0xFFFFFFFFu ? -INFINITY : __uint_as_float(raw[t][j]);
+                const float x1 = raw[t][j + 1] == 0xFFFFFFFFu ? -INFINITY : __uint_as_float(raw[t][j + 1]);
+                s0 += fma_ok ? __builtin_amdgcn_exp2f(fmaf(x0, kLog2e, -m2)) : exp_rel(x0, ref);
+                s1 += fma_ok ? __builtin_amdgcn_exp2f(fmaf(x1, kLog2e, -m2)) : exp_rel(x1, ref);
+            }
+        const float sc = fma_ok ? __builtin_amdgcn_exp2f(fmaf(ref, kLog2e, -m2)) : 1.f;
+        const float2 cs = chunk_expsum(m, (s0 + s1) * sc);
+        if (l == 0) lse_part[row * chunks + chunk] = cs;
+    }
     const int target = min(K, nvalid);
     uint32_t thr = 0;
     for (int bit = 31; bit >= 0; --bit) {
@@ -472,8 +591,53 @@ __global__ __launch_bounds__(256) void topk_partial_f32_kernel(
 // all entries.
 constexpr int kMergeCap = 128;
 
+// The K winners (fin, exactly K distinct composites) in top-K order: lane l <
+// K finds its rank among them and writes id and value; with conf given, also
+// the candidate's five confidence scalars from the row's log-normaliser:
+// log-prob, probability, gap to the rank-0 logit, rank / (K-1), top flag.
+__device__ __forceinline__ void write_ranked(const uint64_t* fin, int K, int32_t* __restrict__ ids,
+                                             float* __restrict__ vals, float* __restrict__ conf, float logz) {
+    const int l = lane_id();
+    int rank = 0;
+    float v = -INFINITY;
+    if (l < K) {
+        const uint64_t me = fin[l];
+        for (int m2 = 0; m2 < K; ++m2) rank += fin[m2] > me ? 1 : 0;
+        v = __uint_as_float(bits_of_key(static_cast<uint32_t>(me >> 32)));
+        ids[rank] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(me & 0xFFFFFFFFu));
+        vals[rank] = v;
+    }
+    if (conf) {
+        const float top = wave_max64(v);   // the rank-0 value: lanes past K hold -inf
+        if (l < K) {
+            const float lp = v - logz;
+            float* c = conf + rank * kConfFields;
+            c[0] = lp;
+            c[1] = expf(lp);
+            c[2] = top - v;
+            c[3] = K > 1 ? static_cast<float>(rank) / static_cast<float>(K - 1) : 0.f;
+            c[4] = rank == 0 ? 1.f : 0.f;
+        }
+    }
+}
+
+// log Z of one row from its chunks' (m, s) pairs: M = max m, then
+// log Z = M + ln(sum_c s_c exp(m_c - M)); -inf when no chunk has a finite value.
+__device__ __forceinline__ float row_log_normaliser(const float2* __restrict__ p, int chunks) {
+    const int l = lane_id();
+    float mx = -INFINITY;
+    for (int q = l; q < chunks; q += kWave) mx = fmaxf(mx, p[q].x);
+    const float M = wave_max64(mx);
+    const float ref = exp_ref(M);
+    float sum = 0.f;
+    for (int q = l; q < chunks; q += kWave) sum += p[q].y * exp_rel(exp_ref(p[q].x), ref);
+    const float S = wave_sum64(sum);
+    return M == -INFINITY ? -INFINITY : M + logf(S);
+}
+
 __device__ void merge_row_wave(const uint64_t* __restrict__ ent, int M, int K, uint64_t* sel,
-                               uint64_t* fin, int32_t* __restrict__ ids, float* __restrict__ vals) {
+                               uint64_t* fin, int32_t* __restrict__ ids, float* __restrict__ vals,
+                               float* __restrict__ conf, float logz) {
     const int l = lane_id();
     uint64_t lm = 0;
     for (int q = l; q < M; q += kWave) lm = max(lm, ent[q]);
@@ -524,13 +688,7 @@ __device__ void merge_row_wave(const uint64_t* __restrict__ ent, int M, int K, u
         outn += popc64(m);
     }
     wave_lds_sync();
-    if (l < K) {
-        const uint64_t me = fin[l];
-        int rank = 0;
-        for (int m2 = 0; m2 < K; ++m2) rank += fin[m2] > me ? 1 : 0;
-        ids[rank] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(me & 0xFFFFFFFFu));
-        vals[rank] = __uint_as_float(bits_of_key(static_cast<uint32_t>(me >> 32)));
-    }
+    write_ranked(fin, K, ids, vals, conf, logz);
 }
 
 // Fast path of the merge for rows of at most kMergePer * 64 candidates, held in
@@ -546,7 +704,7 @@ constexpr int kMergePer = 8;
 
 __device__ __forceinline__ bool merge_row_fast(const uint64_t* __restrict__ ent, int M, int K, int kbits,
                                                uint64_t* sel, uint64_t* fin, int32_t* __restrict__ ids,
-                                               float* __restrict__ vals) {
+                                               float* __restrict__ vals, float* __restrict__ conf, float logz) {
     const int l = lane_id();
     const int lowbit = 32 - kbits;
     uint64_t e[kMergePer];
@@ -605,37 +763,30 @@ __device__ __forceinline__ bool merge_row_fast(const uint64_t* __restrict__ ent,
     fin[(win1 && p1 < kWave) ? p1 : kWave + l] = a1;
     wave_lds_sync();
     // exactly K distinct composites won; order them by rank
-    if (l < K) {
-        const uint64_t me = fin[l];
-        int rank = 0;
-        for (int m2 = 0; m2 < K; ++m2) rank += fin[m2] > me ? 1 : 0;
-        ids[rank] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(me & 0xFFFFFFFFu));
-        vals[rank] = __uint_as_float(bits_of_key(static_cast<uint32_t>(me >> 32)));
-    }
+    write_ranked(fin, K, ids, vals, conf, logz);
     return true;
 }
 
-// ------------------------------------------------------------ slot state --
-// Wave-wide sum over the 64 lanes, the same value in every lane.
-__device__ __forceinline__ float wave_sum64(float v) {
-    const float r = row16_sum(v);
-    return (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 0)) +
-            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 16))) +
-           (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 32)) +
-            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 48)));
-}
-
 // The merge of one row by one wave: the K winners of the row's chunk
-// candidates, in order.  `sel` and `fin` are the wave's LDS lists.
+// candidates, in order.  `sel` and `fin` are the wave's LDS lists.  With the
+// normaliser pairs given (lse_part), also the row's log Z and, when conf is
+// given, the candidates' confidence scalars.
 __device__ __forceinline__ void merge_row(const uint64_t* __restrict__ part, int chunks, int K, int kbits, int64_t row,
                                           uint64_t* sel, uint64_t* fin, int32_t* __restrict__ ids,
-                                          float* __restrict__ vals) {
+                                          float* __restrict__ vals, const float2* __restrict__ lse_part,
+                                          float* __restrict__ logz, float* __restrict__ conf) {
     const int M = chunks * K;
     const uint64_t* ent = part + row * M;
-    if (M <= kMergePer * kWave && merge_row_fast(ent, M, K, kbits, sel, fin, ids + row * K, vals + row * K))
+    float lz = 0.f;
+    if (lse_part) {
+        lz = row_log_normaliser(lse_part + row * chunks, chunks);
+        if (lane_id() == 0) logz[row] = lz;
+    }
+    float* rc = conf ? conf + row * K * kConfFields : nullptr;
+    if (M <= kMergePer * kWave && merge_row_fast(ent, M, K, kbits, sel, fin, ids + row * K, vals + row * K, rc, lz))
         return;
     wave_lds_sync();
-    merge_row_wave(ent, M, K, sel, fin, ids + row * K, vals + row * K);
+    merge_row_wave(ent, M, K, sel, fin, ids + row * K, vals + row * K, rc, lz);
 }
 
 // Workgroups [0, nmerge) merge four rows each (one per wave); with a GEMM job
@@ -645,6 +796,8 @@ __device__ __forceinline__ void merge_row(const uint64_t* __restrict__ part, int
 __global__ __launch_bounds__(256) void topk_merge_kernel(const uint64_t* __restrict__ part, int chunks,
                                                          int K, int kbits, int64_t rows,
                                                          int32_t* __restrict__ ids, float* __restrict__ vals,
+                                                         const float2* __restrict__ lse_part,
+                                                         float* __restrict__ logz, float* __restrict__ conf,
                                                          int64_t nmerge, GemmJob hj) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[kGemmSmem];
     static_assert(4 * (kMergeCap + kWave) * 8 + 4 * 2 * kWave * 8 <= kGemmSmem, "merge lists fit the GEMM's LDS");
@@ -658,7 +811,7 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(const uint64_t* __restr
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + wave;
     if (row >= rows) return;
-    merge_row(part, chunks, K, kbits, row, sel_all[wave], fin_all[wave], ids, vals);
+    merge_row(part, chunks, K, kbits, row, sel_all[wave], fin_all[wave], ids, vals, lse_part, logz, conf);
 }
 
 }  // namespace
@@ -667,25 +820,32 @@ int topk_chunk_elems(int dtype) { return dtype == CORR_DT_BF16 ? kNV * 8 * kWave
 
 hipError_t launch_topk_partial(int dtype, const void* logits, int64_t req_stride,
                                int64_t slot_stride, int B, int64_t V, int K, int chunks,
-                               int64_t rows, uint64_t* part, hipStream_t stream) {
+                               int64_t rows, uint64_t* part, float2* lse_part, hipStream_t stream) {
     const int64_t waves = rows * chunks;
     const dim3 grid(static_cast<unsigned>((waves + 3) / 4));
+    const uint16_t* lb = static_cast<const uint16_t*>(logits);
+    const float* lf = static_cast<const float*>(logits);
     if (dtype == CORR_DT_BF16)
-        return launch(topk_partial_bf16_kernel, grid, 256, 0, stream, static_cast<const uint16_t*>(logits),
-                      req_stride, slot_stride, B, V, K, chunks, rows, part);
-    return launch(topk_partial_f32_kernel, grid, 256, 0, stream, static_cast<const float*>(logits), req_stride,
-                  slot_stride, B, V, K, chunks, rows, part);
+        return lse_part ? launch(topk_partial_bf16_kernel<true>, grid, 256, 0, stream, lb, req_stride, slot_stride,
+                                 B, V, K, chunks, rows, part, lse_part)
+                        : launch(topk_partial_bf16_kernel<false>, grid, 256, 0, stream, lb, req_stride,
+                                 slot_stride, B, V, K, chunks, rows, part, lse_part);
+    return lse_part ? launch(topk_partial_f32_kernel<true>, grid, 256, 0, stream, lf, req_stride, slot_stride, B, V,
+                             K, chunks, rows, part, lse_part)
+                    : launch(topk_partial_f32_kernel<false>, grid, 256, 0, stream, lf, req_stride, slot_stride, B,
+                             V, K, chunks, rows, part, lse_part);
 }
 
 hipError_t launch_topk_merge(int dtype, const uint64_t* part, int chunks, int K, int64_t rows, int32_t* ids,
-                             float* vals, const GemmJob* hj, hipStream_t stream) {
+                             float* vals, const float2* lse_part, float* logz, float* conf, const GemmJob* hj,
+                             hipStream_t stream) {
     const int kbits = dtype == CORR_DT_BF16 ? 16 : 32;
     const int64_t nmerge = (rows + 3) / 4;
     GemmJob none{};
     const GemmJob& j = hj ? *hj : none;
     const int64_t ng = hj ? gemm_launch_blocks(*hj) : 0;
     return launch(topk_merge_kernel, dim3(static_cast<unsigned>(nmerge + ng)), 256, 0, stream, part, chunks, K,
-                  kbits, rows, ids, vals, nmerge, j);
+                  kbits, rows, ids, vals, lse_part, logz, conf, nmerge, j);
 }
 
 

@@ -8,6 +8,9 @@
  * section 3.5, Eq. 8:
  *
  *   corrector_topk   step (1): top-K candidate ids and drafter logits per slot.
+ *   corrector_topk_softmax  step (1) fused with the vocabulary-wide
+ *                    normalisation of each slot row (LiLiCorr appendix A):
+ *                    log Z per row and the candidates' confidence scalars.
  *   corrector_score  steps (2)-(4): candidate representations
  *                    b = LN(W_cand E[c]), g = LN(W_ctx h), z = LN_{gamma,beta}
  *                    (W_fuse [b; g]); pair state s_p = W_pair [h_p; h_{p+1}];
@@ -31,12 +34,6 @@
  *     host-side validation and launch errors only; a device fault surfaces at
  *     the caller's next synchronisation.  Validation happens before anything
  *     is enqueued, so a call that returns an error has launched nothing.
- *   - corrector_score and corrector_run run the hidden-state projection and the
- *     per-slot state on a second stream that the handle creates at its first
- *     such call (default priority): it is forked from `stream` by an event at
- *     the start of the call and joined back by an event before the candidate
- *     step, so all of the call's work is ordered after earlier work on
- *     `stream` and before later work on it, also under stream capture.
  *   - A handle's weights are fixed after corrector_create; concurrent calls
  *     with one handle on different streams are safe when each uses its own
  *     workspace.  Every step of a call runs in order on the call's stream;
@@ -179,6 +176,26 @@ size_t corrector_workspace_bytes(const corrector *h, int32_t n_req);
 int corrector_topk(const corrector *h, int32_t n_req, const void *logits,
                    int64_t req_stride, int64_t slot_stride, int32_t *ids, float *vals,
                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* Step (1) fused with the vocabulary-wide normalisation of every slot row
+ * (LiLiCorr appendix A: "Serving" fuses top-K extraction with the logit
+ * normalisation in one kernel; "Architecture" lists the confidence scalars
+ * the head reads from the drafter's distribution).  Arguments, ids and vals
+ * as for corrector_topk, plus outputs
+ *   logz [n_req][B] float32: log sum_v exp(l_v) over the row's V logits
+ *        (-inf for a row of -inf); required;
+ *   conf_or_null [n_req][B][K][5] float32, written when non-NULL; per
+ *        candidate in top-K order: log-prob l - logz, probability
+ *        exp(l - logz), gap (the rank-0 logit minus this one, >= 0), rank
+ *        r / (K-1) in [0, 1] (0 when K = 1), and 1 for rank 0 else 0.
+ * The logits are read once: every chunk's maximum and sum of exponentials
+ * come from the registers its top-K pass already holds.  Logits must be
+ * finite or -inf (+inf and NaN give unspecified values).  Errors as for
+ * corrector_topk; logz NULL gives CORR_E_NULL. */
+int corrector_topk_softmax(const corrector *h, int32_t n_req, const void *logits,
+                           int64_t req_stride, int64_t slot_stride, int32_t *ids, float *vals,
+                           float *logz, float *conf_or_null, void *workspace,
+                           size_t workspace_bytes, void *stream);
 
 /* Steps (2)-(4).  ids/vals as produced by corrector_topk ([n_req][B][K]).
  * hidden: bfloat16 row (i, s) starts at hidden + i*h_req_stride +

@@ -125,6 +125,15 @@ def test_calls_validate_before_launch(lib):
     assert lib.corrector_topk(h, 4, FAKE, 16 * 151936, 151936, FAKE, FAKE, FAKE, need - 1, None) == 5
     assert lib.corrector_topk(h, 1, FAKE, 16 * 151936, 151936, FAKE, FAKE, None, need, None) == 1
     assert lib.corrector_topk(h, 1, FAKE, 16 * 151936, 151936, FAKE, FAKE, FAKE + 4, need, None) == 4
+    # fused top-K + normalisation: logz required, conf optional; same checks as top-K
+    assert lib.corrector_topk_softmax(h, 1, FAKE, 16 * 151936, 151936, FAKE, FAKE, None, None, FAKE, need,
+                                      None) == 1
+    assert lib.corrector_topk_softmax(h, 5, FAKE, 16 * 151936, 151936, FAKE, FAKE, FAKE, None, FAKE, need,
+                                      None) == 2
+    assert lib.corrector_topk_softmax(h, 1, FAKE + 2, 0, 151936, FAKE, FAKE, FAKE, FAKE, FAKE, need, None) == 4
+    assert lib.corrector_topk_softmax(h, 4, FAKE, 16 * 151936, 151936, FAKE, FAKE, FAKE, None, FAKE, need - 1,
+                                      None) == 5
+    assert lib.corrector_topk_softmax(h, 0, None, 0, 0, None, None, None, None, None, 0, None) == 0
     # score: hidden alignment, null scores
     assert lib.corrector_score(h, 1, FAKE, FAKE, FAKE + 2, 0, 4096, FAKE, FAKE, need, None) == 4
     assert lib.corrector_score(h, 1, FAKE, FAKE, FAKE, 0, 4096, None, FAKE, need, None) == 1
@@ -138,6 +147,7 @@ def test_calls_validate_before_launch(lib):
 
 def test_destroyed_and_null_handles(lib):
     assert lib.corrector_topk(None, 1, FAKE, 0, 0, FAKE, FAKE, FAKE, 1 << 30, None) == 7
+    assert lib.corrector_topk_softmax(None, 1, FAKE, 0, 0, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == 7
     assert lib.corrector_workspace_bytes(None, 1) == 0
     lib.corrector_destroy(None)
 
