@@ -162,14 +162,19 @@ def measure_topk_softmax(corr, cfg, dev_sets, host_logits, st, stream, steps, wa
         oracle.build(force=False)
         d = oracle.OracleDesc.from_config(cfg)
         V = cfg["V"]
-        t0 = time.perf_counter()
-        _, ov = oracle.topk(d, host_logits, n, (B + 1) * V, V, offset=V)
-        oz = oracle.log_normaliser(d, host_logits, n, (B + 1) * V, V, offset=V)
-        oracle.confidence(ov, oz)
-        el = time.perf_counter() - t0
-        res["cpu_baseline"] = {"value": round(n * B / el, 1), "unit": "slot rows/s", "cores": oracle.get_threads(),
-                               "kind": "oracle", "sample": "one %d-row batch: full-sort top-K, log Z and scalars "
-                                                           "(%.1f s)" % (n * B, el)}
+        t0, reps = time.perf_counter(), 0
+        while True:
+            _, ov = oracle.topk(d, host_logits, n, (B + 1) * V, V, offset=V)
+            oz = oracle.log_normaliser(d, host_logits, n, (B + 1) * V, V, offset=V)
+            oracle.confidence(ov, oz)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= 5.0 or reps >= 64:
+                break
+        res["cpu_baseline"] = {"value": round(reps * n * B / el, 1), "unit": "slot rows/s",
+                               "cores": oracle.get_threads(), "kind": "oracle",
+                               "sample": "%d pass(es) over one %d-row batch: full-sort top-K, log Z and scalars "
+                                         "(%.1f s)" % (reps, n * B, el)}
     return res
 
 
