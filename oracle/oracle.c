@@ -447,11 +447,16 @@ int oracle_walk(const oracle_desc *D, int32_t n, const double *scores, const int
  * score of a path ending at candidate b of the current slot and from[p][b]
  * the smallest predecessor index attaining it; the last slot takes the
  * smallest b attaining the largest best[b], and the path is traced back
- * through `from`.  total[i] (optional) receives the path's summed score. */
+ * through `from`.  total[i] (optional) receives the path's summed score.
+ *
+ * lambda weights pair p's term by lambda^p.  lambda = 1 is the Global-Sum
+ * rule of Eq. 12.  The DCOCO page's Geometric rule (lambda = 0.75) is named
+ * there without a formula; it is read here as this geometrically discounted
+ * sum, which favours the early slots that prefix acceptance rewards. */
 int oracle_viterbi(const oracle_desc *D, int32_t n, const double *scores, const int32_t *ids,
-                   int32_t *tokens, int32_t *choice, double *total)
+                   double lambda, int32_t *tokens, int32_t *choice, double *total)
 {
-    if (!D || !scores || !ids || !tokens || !choice || n < 0) return ORA_E_ARG;
+    if (!D || !scores || !ids || !tokens || !choice || n < 0 || !(lambda > 0.0)) return ORA_E_ARG;
     const int B = D->B, K = D->K;
     double *best = malloc(sizeof(double) * (size_t)K);
     double *next = malloc(sizeof(double) * (size_t)K);
@@ -464,11 +469,12 @@ int oracle_viterbi(const oracle_desc *D, int32_t n, const double *scores, const 
         for (int a = 0; a < K; ++a) best[a] = a == 0 ? 0.0 : -INFINITY;
         for (int p = 0; p + 1 < B; ++p) {
             const double *Sp = scores + ((size_t)i * (B - 1) + p) * K * K;
+            const double wp = pow(lambda, p);
             for (int b = 0; b < K; ++b) {
                 int32_t arg = 0;
-                double v = best[0] + Sp[b];
+                double v = best[0] + wp * Sp[b];
                 for (int a = 1; a < K; ++a) {
-                    const double w = best[a] + Sp[(size_t)a * K + b];
+                    const double w = best[a] + wp * Sp[(size_t)a * K + b];
                     if (w > v) { v = w; arg = a; }
                 }
                 next[b] = v;

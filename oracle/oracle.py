@@ -59,7 +59,7 @@ def _load():
         lib.oracle_represent.argtypes = [P, P, C.c_int32, P, P, C.c_int64, C.c_int64, P, P, P, P]
         lib.oracle_score.argtypes = [P, P, C.c_int32, P, P, P, P, P]
         lib.oracle_walk.argtypes = [P, C.c_int32, P, P, P, P]
-        lib.oracle_viterbi.argtypes = [P, C.c_int32, P, P, P, P, P]
+        lib.oracle_viterbi.argtypes = [P, C.c_int32, P, P, C.c_double, P, P, P]
         lib.oracle_accepted.argtypes = [C.c_int32, C.c_int32, P, P, P]
         lib.oracle_layernorm.argtypes = [P, C.c_int, C.c_double, P, P]
         lib.oracle_gelu.restype = C.c_double
@@ -285,9 +285,11 @@ def walk(desc: OracleDesc, scores, ids, n: int):
     return tokens, choice
 
 
-def viterbi(desc: OracleDesc, scores, ids, n: int):
-    """Global-Sum path rule: tokens [n][B], choices [n][B] and the summed
-    transition score [n] of the best path (slot 1 fixed at rank 0)."""
+def viterbi(desc: OracleDesc, scores, ids, n: int, lam: float = 1.0):
+    """Global-Sum path rule (lam = 1): tokens [n][B], choices [n][B] and the
+    summed transition score [n] of the best path (slot 1 fixed at rank 0).
+    With lam < 1, pair p's term is weighted by lam**p (the Geometric rule as
+    read here) and total is the weighted sum."""
     keep = _Keep()
     scores = keep.arr(scores, np.float64)
     ids = keep.arr(ids, np.int32)
@@ -295,7 +297,7 @@ def viterbi(desc: OracleDesc, scores, ids, n: int):
     choice = np.empty((n, desc.B), np.int32)
     total = np.empty(n, np.float64)
     d = desc.c()
-    _check(_load().oracle_viterbi(C.byref(d), n, _ptr(scores), _ptr(ids), _ptr(tokens),
+    _check(_load().oracle_viterbi(C.byref(d), n, _ptr(scores), _ptr(ids), float(lam), _ptr(tokens),
                                   _ptr(choice), _ptr(total)), "viterbi")
     return tokens, choice, total
 

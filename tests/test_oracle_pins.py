@@ -415,6 +415,56 @@ def test_viterbi_dominates_the_walk_and_ignores_pair_offsets():
         np.testing.assert_allclose(total2, total + c.sum(axis=(1, 2, 3)), atol=1e-9)
 
 
+# ---------------------------------------------- Geometric path rule --
+# The DCOCO page names a Geometric rule (lambda = 0.75) without a formula; it
+# is read as the path maximising sum_p lambda^p S_p(c_p, c_{p+1}).  These pins
+# fix the oracle to that reading (which itself is unpinned by the pages).
+
+def _discounted(S, path, lam):
+    return sum(lam ** p * S[p, path[p], path[p + 1]] for p in range(len(path) - 1))
+
+
+def test_geometric_matches_brute_force():
+    g = np.random.default_rng(21)
+    for lam in (0.75, 0.3, 1.0):
+        for B, K in ((2, 3), (3, 4), (5, 4), (6, 3)):
+            n = 3
+            S = g.normal(size=(n, B - 1, K, K))
+            ids = g.integers(0, 100, size=(n, B, K)).astype(np.int32)
+            tokens, choice, total = oracle.viterbi(_desc(B, K), S, ids, n, lam=lam)
+            for i in range(n):
+                best = max(_paths(B, K), key=lambda c: _discounted(S[i], c, lam))
+                np.testing.assert_array_equal(choice[i], best)
+                assert total[i] == pytest.approx(_discounted(S[i], best, lam), abs=1e-12)
+
+
+def test_geometric_small_lambda_is_the_walk():
+    """For small lambda the discounted sum orders paths lexicographically by
+    (step 1, step 2, ...), which is the prefix-first walk; weighting the
+    steps the other way round would not give it.  Each pair's K x K tile is a
+    permutation of 0..K^2-1 (gaps >= 1, range K^2-1, and rows with different
+    maxima, so the continuation matters), and lambda = 1/(2K^2) makes every
+    step outweigh all later ones together:
+    sum_{q>p} lambda^(q-p) (K^2-1) < 1.  The shapes keep lambda^(B-2) well
+    above float64 resolution next to the totals."""
+    g = np.random.default_rng(22)
+    for B, K in ((4, 4), (8, 3), (15, 2), (6, 6)):
+        n = 6
+        S = np.argsort(g.random(size=(n, B - 1, K * K)), axis=-1).reshape(n, B - 1, K, K).astype(np.float64)
+        ids = g.integers(0, 100, size=(n, B, K)).astype(np.int32)
+        _, choice, _ = oracle.viterbi(_desc(B, K), S, ids, n, lam=1.0 / (2 * K * K))
+        _, wchoice = oracle.walk(_desc(B, K), S, ids, n)
+        np.testing.assert_array_equal(choice, wchoice)
+
+
+def test_geometric_rejects_non_positive_lambda():
+    S = np.zeros((1, 2, 3, 3))
+    ids = np.zeros((1, 3, 3), np.int32)
+    for lam in (0.0, -0.5):
+        with pytest.raises(RuntimeError):
+            oracle.viterbi(_desc(3, 3), S, ids, 1, lam=lam)
+
+
 # ------------------------------------------- vocabulary normalisation --
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
