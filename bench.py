@@ -204,8 +204,9 @@ def main():
     ap.add_argument("--copies", type=int, default=4, help="independent input sets rotated per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--head", default="normal")
-    ap.add_argument("--path-rule", default="greedy", choices=["greedy", "global_sum"],
+    ap.add_argument("--path-rule", default="greedy", choices=["greedy", "global_sum", "geometric"],
                     help="how the path through the candidate lattice is chosen")
+    ap.add_argument("--path-lambda", type=float, default=0.75, help="lambda of the Geometric path rule")
     ap.add_argument("--no-fold", action="store_true", help="skip the folded-table measurement")
     ap.add_argument("--no-softmax", action="store_true",
                     help="skip the fused top-K + normalisation measurement")
@@ -223,7 +224,7 @@ def main():
     from workload import config
     from workload.gen import gen_embed, gen_hidden, gen_logits, gen_weights
 
-    cfg = config(args.workload, path_rule=args.path_rule)
+    cfg = config(args.workload, path_rule=args.path_rule, path_lambda=args.path_lambda)
     n = cfg["n"]
     log("generating %s inputs (%d copies)" % (args.workload, args.copies))
     t0 = time.perf_counter()
@@ -380,7 +381,8 @@ def main():
         "config": {"workload": "%s: %d requests x %d drafted slots (+anchor), V=%d, K=%d, d=%d, r=%d, "
                                "MLP %d->%d->1, %s" % (args.workload, n, B, cfg["V"], K, cfg["d"],
                                                       cfg["r"], 3 * cfg["r"] + 2, cfg["h"], cfg["variant"])
-                               + ("" if args.path_rule == "greedy" else ", Global-Sum path"),
+                               + {"greedy": "", "global_sum": ", Global-Sum path",
+                                  "geometric": ", Geometric path (lambda %g)" % args.path_lambda}[args.path_rule],
                    "global_batch": n, "rotating_input_sets": args.copies},
         "roofline": roof,
         "kernels": kernels,

@@ -12,9 +12,10 @@
 
 namespace corr {
 
-// Path rules (the values of CORR_PATH_GREEDY / CORR_PATH_GLOBAL_SUM).
+// Path rules (the values of CORR_PATH_GREEDY / _GLOBAL_SUM / _GEOMETRIC).
 constexpr int kPathGreedy = 0;
 constexpr int kPathGlobalSum = 1;
+constexpr int kPathGeometric = 2;
 
 // Optional timing events for the next launch made on this thread.  The host
 // sequencer sets them around one step; launch() hands them to
@@ -176,6 +177,7 @@ struct FinishArgs {
     int32_t* tokens;        // with tokens given (only when path_fits_lds), the
     int32_t* choice;        // request's path by `rule` follows in the launch
     int rule;
+    float lam;              // the Geometric rule's discount
 };
 hipError_t launch_finish(const FinishArgs& a, hipStream_t stream);
 
@@ -195,6 +197,7 @@ struct CosArgs {
     int32_t* tokens;
     int32_t* choice;
     int rule;
+    float lam;
 };
 hipError_t launch_cosine(const CosArgs& a, hipStream_t stream);
 
@@ -205,9 +208,10 @@ hipError_t launch_cosine(const CosArgs& a, hipStream_t stream);
 bool path_fits_lds(int B, int K);
 // The path of every request over precomputed scores by `rule`
 // (kPathGreedy: the prefix-first walk; kPathGlobalSum: the best
-// summed score by dynamic programming), one wave per request.
-hipError_t launch_path(const float* scores, const int32_t* ids, int n, int B, int K, int rule, int32_t* tokens,
-                       int32_t* choice, hipStream_t stream);
+// summed score by dynamic programming; kPathGeometric: the same with pair p
+// weighted by lam^p), one wave per request.
+hipError_t launch_path(const float* scores, const int32_t* ids, int n, int B, int K, int rule, float lam,
+                       int32_t* tokens, int32_t* choice, hipStream_t stream);
 
 // ---- intermediates (walk.hip)
 hipError_t launch_zhl_to_f32(const uint16_t* zhl, float* z, int64_t nodes, int r, hipStream_t stream);

@@ -104,12 +104,13 @@ __host__ __device__ inline size_t walk_chain_offset(int B, int K) {
 // one lane into chain[] (LDS), and lanes s < B write choice[s] and gather
 // tokens[s] = ids[s][chain[s]].
 __device__ __forceinline__ void viterbi_wave(const float* src, uint8_t* from, int* chain, float* vb,
-                                             const int32_t* __restrict__ ids, int req, int B, int K,
+                                             const int32_t* __restrict__ ids, int req, int B, int K, float lam,
                                              int32_t* __restrict__ tokens, int32_t* __restrict__ choice) {
     const int l = lane_id();
     const int bl = min(l, K - 1);   // lanes past K mirror the last candidate (never used)
     float bv = l == 0 ? 0.f : -INFINITY;
-    for (int p = 0; p + 1 < B; ++p) {
+    float wp = 1.f;                  // lam^p (1 for the Global-Sum rule: fmaf(1, s, b) is b + s)
+    for (int p = 0; p + 1 < B; ++p, wp *= lam) {
         if (l < K) vb[l] = bv;
         wave_lds_sync();
         const float* Sp = src + static_cast<int64_t>(p) * K * K;
@@ -127,7 +128,7 @@ __device__ __forceinline__ void viterbi_wave(const float* src, uint8_t* from, in
             for (int u = 0; u < 16; ++u) {
                 const float4 q4 = pv[u / 4];
                 const float pb = (u & 3) == 0 ? q4.x : ((u & 3) == 1 ? q4.y : ((u & 3) == 2 ? q4.z : q4.w));
-                w[u] = a0 + u < K ? pb + w[u] : -INFINITY;
+                w[u] = a0 + u < K ? fmaf(wp, w[u], pb) : -INFINITY;
             }
             // The group's maximum, then the lowest predecessor that reaches it
             // (a select sweep over constant indices: no index array to carry).
@@ -183,13 +184,15 @@ __host__ __device__ inline size_t path_lds_end(int B, int K, bool scores_in_lds)
 // The request's path from scores in LDS (every thread of the workgroup
 // calls it): the greedy walk uses the whole workgroup, the Global-Sum
 // dynamic program its first wave.
-__device__ __forceinline__ void path_from_lds(int rule, float* sS, const int32_t* __restrict__ ids, int req, int B, int K,
-                              int32_t* __restrict__ tokens, int32_t* __restrict__ choice) {
+__device__ __forceinline__ void path_from_lds(int rule, float lam, float* sS, const int32_t* __restrict__ ids, int req,
+                                              int B, int K, int32_t* __restrict__ tokens,
+                                              int32_t* __restrict__ choice) {
     uint8_t* aux = reinterpret_cast<uint8_t*>(reinterpret_cast<char*>(sS) + path_aux_offset(B, K, true));
     int* chain = reinterpret_cast<int*>(reinterpret_cast<char*>(sS) + path_chain_offset(B, K, true));
-    if (rule == kPathGlobalSum) {
+    if (rule != kPathGreedy) {
         float* vb = reinterpret_cast<float*>(reinterpret_cast<char*>(sS) + path_vb_offset(B, K, true));
-        if ((threadIdx.x >> 6) == 0) viterbi_wave(sS, aux, chain, vb, ids, req, B, K, tokens, choice);
+        if ((threadIdx.x >> 6) == 0)
+            viterbi_wave(sS, aux, chain, vb, ids, req, B, K, rule == kPathGeometric ? lam : 1.f, tokens, choice);
         return;
     }
     walk_block(sS, aux, chain, ids, req, B, K, tokens, choice);
@@ -199,8 +202,9 @@ __device__ __forceinline__ void path_from_lds(int rule, float* sS, const int32_t
 // scores fit (use_lds) they are first copied into LDS with coalesced 16-byte
 // loads, all issued before any is used.
 __global__ __launch_bounds__(64) void path_kernel(const float* __restrict__ scores, const int32_t* __restrict__ ids,
-                                                  int n, int B, int K, int rule, int32_t* __restrict__ tokens,
-                                                  int32_t* __restrict__ choice, int use_lds) {
+                                                  int n, int B, int K, int rule, float lam,
+                                                  int32_t* __restrict__ tokens, int32_t* __restrict__ choice,
+                                                  int use_lds) {
     extern __shared__ __attribute__((aligned(16))) float sl[];
     const int req = blockIdx.x;
     const int l = lane_id();
@@ -227,14 +231,14 @@ __global__ __launch_bounds__(64) void path_kernel(const float* __restrict__ scor
             for (int64_t i = l; i < per; i += kWave) sl[i] = base[i];
         }
         wave_lds_sync();
-        path_from_lds(rule, sl, ids, req, B, K, tokens, choice);
+        path_from_lds(rule, lam, sl, ids, req, B, K, tokens, choice);
         return;
     }
-    if (rule == kPathGlobalSum) {
+    if (rule != kPathGreedy) {
         uint8_t* from = reinterpret_cast<uint8_t*>(sl);
         int* chain = reinterpret_cast<int*>(reinterpret_cast<char*>(sl) + path_chain_offset(B, K, false));
         float* vb = reinterpret_cast<float*>(reinterpret_cast<char*>(sl) + path_vb_offset(B, K, false));
-        viterbi_wave(base, from, chain, vb, ids, req, B, K, tokens, choice);
+        viterbi_wave(base, from, chain, vb, ids, req, B, K, rule == kPathGeometric ? lam : 1.f, tokens, choice);
         return;
     }
     walk_wave(base, ids, req, B, K, tokens, choice);
@@ -300,7 +304,7 @@ __global__ __launch_bounds__(1024) void cosine_kernel(CosArgs a, int use_lds) {
     }
     if (!a.tokens || !use_lds) return;
     __syncthreads();
-    path_from_lds(a.rule, sS, a.ids, req, B, K, a.tokens, a.choice);
+    path_from_lds(a.rule, a.lam, sS, a.ids, req, B, K, a.tokens, a.choice);
 }
 
 // One workgroup per request: S = l_{p+1}(b) + (sum of the hidden-block partial
@@ -375,7 +379,7 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a, int use_lds) 
     }
     if (!a.tokens || !use_lds) return;
     __syncthreads();
-    path_from_lds(a.rule, sS, a.ids, req, B, K, a.tokens, a.choice);
+    path_from_lds(a.rule, a.lam, sS, a.ids, req, B, K, a.tokens, a.choice);
 }
 
 // z = hi + lo for each node row of the [hi | lo] layout.
@@ -422,12 +426,12 @@ hipError_t launch_cosine(const CosArgs& a, hipStream_t stream) {
                   a, lds > 0);
 }
 
-hipError_t launch_path(const float* scores, const int32_t* ids, int n, int B, int K, int rule, int32_t* tokens,
-                       int32_t* choice, hipStream_t stream) {
+hipError_t launch_path(const float* scores, const int32_t* ids, int n, int B, int K, int rule, float lam,
+                       int32_t* tokens, int32_t* choice, hipStream_t stream) {
     const size_t wl = path_lds_bytes(B, K);
     const size_t lds = wl ? wl : path_lds_end(B, K, false);
     return launch(path_kernel, dim3(static_cast<unsigned>(n)), 64, static_cast<uint32_t>(lds), stream, scores,
-                  ids, n, B, K, rule, tokens, choice, wl > 0);
+                  ids, n, B, K, rule, lam, tokens, choice, wl > 0);
 }
 
 hipError_t launch_finish(const FinishArgs& a, hipStream_t stream) {

@@ -80,8 +80,15 @@ enum { CORR_DTYPE_BF16 = 0, CORR_DTYPE_F32 = 1 };
  *                         sum_p S_p(k_p, k_{p+1}) (LiLiCorr appendix E,
  *                         Eq. 12), found exactly by dynamic programming; ties
  *                         to the lowest predecessor index in the forward sweep
- *                         and the lowest index in the last slot. */
-enum { CORR_PATH_GREEDY = 0, CORR_PATH_GLOBAL_SUM = 1 };
+ *                         and the lowest index in the last slot;
+ *   CORR_PATH_GEOMETRIC   the path with the largest discounted score
+ *                         sum_p lambda^p S_p(k_p, k_{p+1}), lambda from the
+ *                         descriptor, by the same dynamic program and ties.
+ *                         The DCOCO page compares a Geometric rule with
+ *                         lambda = 0.75 against the walk (path-rule table) but
+ *                         gives no formula; this discounted sum is the
+ *                         reading implemented. */
+enum { CORR_PATH_GREEDY = 0, CORR_PATH_GLOBAL_SUM = 1, CORR_PATH_GEOMETRIC = 2 };
 
 /* Shapes and options fixed at create time.
  *   vocab        V, 1 <= K <= V < 2^31.
@@ -97,8 +104,11 @@ enum { CORR_PATH_GREEDY = 0, CORR_PATH_GLOBAL_SUM = 1 };
  *   max_requests upper bound on n_req for every call; sizes the workspace.
  *   ln_eps       LayerNorm epsilon (> 0).
  *   sigma        cosine scale (cosine only).
- *   path_rule    CORR_PATH_GREEDY (0, the default of a zeroed struct) or
- *                CORR_PATH_GLOBAL_SUM; used by corrector_walk and corrector_run. */
+ *   path_rule    CORR_PATH_GREEDY (0, the default of a zeroed struct),
+ *                CORR_PATH_GLOBAL_SUM or CORR_PATH_GEOMETRIC; used by
+ *                corrector_walk and corrector_run.
+ *   path_lambda  lambda of CORR_PATH_GEOMETRIC, 0 < lambda <= 1 (otherwise
+ *                CORR_E_SHAPE); ignored by the other rules. */
 typedef struct {
     int64_t vocab;
     int32_t slots;
@@ -114,6 +124,7 @@ typedef struct {
     float ln_eps;
     float sigma;
     int32_t path_rule;
+    float path_lambda;
 } corrector_desc;
 
 /* Borrowed device pointers to the weights; the caller keeps them alive and

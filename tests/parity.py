@@ -178,17 +178,19 @@ def select(gpu: dict, first: int, n: int) -> dict:
 
 # ------------------------------------------------------- Global-Sum path --
 
-def path_scores(S, choice):
+def path_scores(S, choice, lam: float = 1.0):
     """Summed transition score of each request's path: S [n][B-1][K][K],
-    choice [n][B]."""
+    choice [n][B]; pair p weighted by lam**p."""
     n, P = S.shape[0], S.shape[1]
     i = np.arange(n)[:, None]
     p = np.arange(P)[None, :]
-    return S[i, p, choice[:, :-1], choice[:, 1:]].sum(axis=1)
+    return (S[i, p, choice[:, :-1], choice[:, 1:]] * lam ** np.arange(P)[None, :]).sum(axis=1)
 
 
-def check_global_sum(gpu: dict, ora: dict, cfg: dict, where: str = "", exact: bool = False):
-    """Gates of the Global-Sum path (best summed score, slot 1 at rank 0).
+def check_global_sum(gpu: dict, ora: dict, cfg: dict, where: str = "", exact: bool = False, lam: float = 1.0):
+    """Gates of the Global-Sum path (best summed score, slot 1 at rank 0), or
+    with lam < 1 of the Geometric path (pair p weighted by lam**p; the sums
+    below are then the weighted sums and eps_p is weighted the same way).
 
     1. The GPU's path is the oracle's dynamic program run on the GPU's own
        scores (in float64): identical, or (where the float32 sums of the GPU's
@@ -209,15 +211,15 @@ def check_global_sum(gpu: dict, ora: dict, cfg: dict, where: str = "", exact: bo
     S_g = gpu["scores"].astype(np.float64)
     scale = max(1.0, float(np.abs(S_g).max()))
     slack = 1e-5 * (B - 1) * scale
-    _, ch_ref, tot_ref = oracle.viterbi(desc, S_g, gpu["ids"], n)
+    _, ch_ref, tot_ref = oracle.viterbi(desc, S_g, gpu["ids"], n, lam=lam)
     diff = (ch_ref != gpu["choice"]).any(axis=1)
-    own = path_scores(S_g, gpu["choice"])
+    own = path_scores(S_g, gpu["choice"], lam)
     assert (np.abs(own[diff] - tot_ref[diff]) <= slack).all(), \
         "GPU path not optimal for its own scores %s: %s" % (where, np.abs(own - tot_ref).max())
     assert diff.mean() <= 0.05, "too many near-tie paths %s: %d of %d" % (where, diff.sum(), n)
-    _, ch_o, tot_o = oracle.viterbi(desc, ora["scores"], ora["ids"], n)
-    eps = np.abs(S_g - ora["scores"]).max(axis=(2, 3)).sum(axis=1)
-    lost = tot_o - path_scores(ora["scores"], gpu["choice"])
+    _, ch_o, tot_o = oracle.viterbi(desc, ora["scores"], ora["ids"], n, lam=lam)
+    eps = (np.abs(S_g - ora["scores"]).max(axis=(2, 3)) * lam ** np.arange(B - 1)[None, :]).sum(axis=1)
+    lost = tot_o - path_scores(ora["scores"], gpu["choice"], lam)
     assert (lost <= 2 * eps + slack).all(), "GPU path loses more than the score error %s" % where
     if exact:
         np.testing.assert_array_equal(gpu["choice"], ch_o, err_msg="exact path " + where)

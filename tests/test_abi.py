@@ -41,7 +41,7 @@ def test_exports_every_declared_call(lib):
 def _desc(**kw):
     base = dict(vocab=151936, slots=15, k=16, d_hidden=4096, d_embed=4096, r=128, mlp_hidden=256,
                 d_vec=128, variant=0, logits_dtype=0, max_requests=32, ln_eps=1e-5, sigma=1.0,
-                path_rule=0)
+                path_rule=0, path_lambda=0.75)
     base.update(kw)
     return corr.CorrectorDesc(*[base[f] for f, _ in corr.CorrectorDesc._fields_])
 
@@ -73,18 +73,32 @@ def test_create_and_workspace(lib):
     ("vocab", 0, 2), ("k", 0, 2), ("k", 65, 2), ("slots", 0, 2), ("d_hidden", 100, 2),
     ("d_embed", 0, 2), ("r", 96, 3), ("mlp_hidden", 8, 3), ("mlp_hidden", 512, 3),
     ("variant", 2, 3), ("logits_dtype", 5, 3), ("max_requests", 0, 2), ("ln_eps", 0.0, 2),
-    ("path_rule", 2, 3), ("path_rule", -1, 3),
+    ("path_rule", 3, 3), ("path_rule", -1, 3),
 ])
 def test_create_rejects_bad_desc(lib, field, value, code):
     rc, h = _create(lib, _desc(**{field: value}), _weights())
     assert rc == code and not h.value
 
 
-def test_create_accepts_both_path_rules(lib):
-    for rule in (0, 1):
+def test_create_accepts_every_path_rule(lib):
+    for rule in (0, 1, 2):
         rc, h = _create(lib, _desc(path_rule=rule), _weights())
         assert rc == 0 and h.value
         lib.corrector_destroy(h)
+
+
+def test_geometric_lambda_range(lib):
+    for lam in (0.0, -0.5, 1.5, float("nan"), float("inf")):
+        rc, h = _create(lib, _desc(path_rule=2, path_lambda=lam), _weights())
+        assert rc == 2 and not h.value, lam
+    for lam in (1e-3, 1.0):
+        rc, h = _create(lib, _desc(path_rule=2, path_lambda=lam), _weights())
+        assert rc == 0
+        lib.corrector_destroy(h)
+    # the other rules ignore lambda
+    rc, h = _create(lib, _desc(path_rule=1, path_lambda=0.0), _weights())
+    assert rc == 0
+    lib.corrector_destroy(h)
 
 
 def test_create_rejects_k_above_v(lib):

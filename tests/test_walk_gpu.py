@@ -1,0 +1,91 @@
+"""corrector_walk on caller-supplied scores, on the GPU, against the oracle,
+for every path rule: the prefix-first walk (DCOCO method details step (5))
+exactly, and the Global-Sum (LiLiCorr appendix E, Eq. 12) and Geometric
+(lambda = 0.75, a discounted sum) paths as optimal for the scores given.
+
+Shapes cover one-wave groups of 16 predecessors with a ragged last group
+(K = 37), K = 1, B = 1 and 2, and scores too large for one workgroup's LDS
+(B = K = 64: 1 MB per request), which the path kernel reads from memory
+instead of staging.  Integer-valued scores force ties.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from draft_correction_amd import device
+from workload import config, gen_weights
+
+pytestmark = pytest.mark.gpu
+
+LAM = {"greedy": 1.0, "global_sum": 1.0, "geometric": 0.75}
+
+
+def _walk(S, ids, rule):
+    n, Bm1, K, _ = S.shape
+    B = Bm1 + 1
+    cfg = config("tiny", B=B, K=K, V=max(1000, K), n=n, path_rule=rule, path_lambda=LAM[rule])
+    emb = np.zeros((cfg["V"], cfg["de"]), np.uint16)
+    corr = device.make_corrector(cfg, dict(weights=device.weights_to_device(gen_weights(cfg), emb)), max_requests=n)
+    tokens = torch.empty((n, B), dtype=torch.int32, device="cuda")
+    choice = torch.empty((n, B), dtype=torch.int32, device="cuda")
+    s = torch.from_numpy(np.ascontiguousarray(S, dtype=np.float32)).cuda()
+    i = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).cuda()
+    corr.walk(n, s if Bm1 > 0 else None, i, tokens, choice)
+    torch.cuda.synchronize()
+    corr.close()
+    return tokens.cpu().numpy(), choice.cpu().numpy(), cfg
+
+
+def _weighted(S, choice, lam):
+    n, P = S.shape[0], S.shape[1]
+    i = np.arange(n)[:, None]
+    p = np.arange(P)[None, :]
+    return (S[i, p, choice[:, :-1], choice[:, 1:]] * lam ** np.arange(P)[None, :]).sum(axis=1)
+
+
+def _check(S, ids, rule, where, ties=False):
+    tokens, choice, cfg = _walk(S, ids, rule)
+    n, B = choice.shape
+    desc = oracle.OracleDesc.from_config(cfg)
+    S64 = S.astype(np.float32).astype(np.float64)
+    np.testing.assert_array_equal(tokens, np.take_along_axis(ids, choice[:, :, None], 2)[:, :, 0],
+                                  err_msg="tokens follow the choices " + where)
+    assert (choice[:, 0] == 0).all()
+    if rule == "greedy":
+        want_t, want_c = oracle.walk(desc, S64, ids, n)
+        np.testing.assert_array_equal(choice, want_c, err_msg="walk " + where)
+        np.testing.assert_array_equal(tokens, want_t, err_msg="walk tokens " + where)
+        return
+    lam = LAM[rule]
+    _, want_c, want_tot = oracle.viterbi(desc, S64, ids, n, lam=lam)
+    if B < 2:
+        np.testing.assert_array_equal(choice, want_c)
+        return
+    # float32 sums on the GPU: the same path, or one within rounding of the optimum
+    scale = max(1.0, float(np.abs(S64).max()))
+    got = _weighted(S64, choice, lam)
+    assert (np.abs(got - want_tot) <= 1e-5 * (B - 1) * scale).all(), "%s: not optimal" % where
+    # Continuous scores: near-ties that rounding may resolve either way are
+    # rare, as long as every pair's weight lam^p stays well above float32
+    # resolution of the total (at lam = 0.75 and B = 64 the last pairs weigh
+    # ~1e-8 and the GPU can only be optimal to rounding there).
+    if not ties and lam ** (B - 2) >= 1e-3:
+        same = (choice == want_c).all(axis=1)
+        assert same.mean() >= 0.6, "%s: %d of %d paths differ" % (where, (~same).sum(), n)
+
+
+@pytest.mark.parametrize("rule", ["greedy", "global_sum", "geometric"])
+@pytest.mark.parametrize("B,K", [(15, 16), (15, 37), (5, 1), (1, 8), (2, 64), (64, 64)])
+def test_walk_rules(rule, B, K):
+    print("walk %s B=%d K=%d" % (rule, B, K), flush=True)
+    g = np.random.default_rng(B * 100 + K)
+    n = 8 if B * K * K <= 64 * 64 * 16 else 3
+    S = g.normal(size=(n, B - 1, K, K)).astype(np.float32)
+    ids = g.integers(0, 1000, size=(n, B, K)).astype(np.int32)
+    _check(S, ids, rule, "normal %s B=%d K=%d" % (rule, B, K))
+    # integer scores: ties everywhere (the walk resolves them to the lowest
+    # index, exactly; the dynamic programs return an optimal path)
+    S = g.integers(-2, 3, size=(n, B - 1, K, K)).astype(np.float32)
+    _check(S, ids, rule, "ties %s B=%d K=%d" % (rule, B, K), ties=True)
