@@ -352,7 +352,31 @@ __device__ __forceinline__ void select_chunk(const u32x4 (&raw)[kNV], uint32_t l
         }
         fast = nc <= static_cast<uint32_t>(kCand16);
     }
-    if (fast) {
+    if (fast && nc <= static_cast<uint32_t>(kWave)) {
+        // the usual case: at most one candidate per lane, so each step of the
+        // bitwise search is one compare, one ballot and one popcount
+        wave_lds_sync();
+        const uint32_t e0 = static_cast<uint32_t>(l) < nc ? cand[l] : 0u;
+        uint32_t tc = 0;
+        for (int bit = 31; bit >= 16; --bit) {
+            const uint32_t cc = tc | (1u << bit);
+            if (popc64(ballot(e0 >= cc)) >= target) tc = cc;
+        }
+        if (popc64(ballot(e0 >= tc)) > target) {
+            for (int bit = 15; bit >= 0; --bit) {
+                const uint32_t cc = tc | (1u << bit);
+                if (popc64(ballot(e0 >= cc)) >= target) tc = cc;
+            }
+        }
+        const bool p = e0 >= tc && e0 != 0u;
+        const uint64_t m = ballot(p);
+        const int pos = prefix_count(m);
+        if (p && pos < K) {
+            const uint32_t raw16 = raw16_of_key16(e0 >> 16);
+            outb[pos] = merge_comp(key_of_bits(raw16 << 16), c0 + (0xFFFFu - (e0 & 0xFFFFu)));
+        }
+        outn = popc64(m);
+    } else if (fast) {
         wave_lds_sync();
         uint32_t e[kCand16 / kWave];
 #pragma unroll
@@ -405,17 +429,24 @@ __device__ __forceinline__ void select_chunk(const u32x4 (&raw)[kNV], uint32_t l
 // numbered f = row * full + chunk and come first; the rows' shorter last
 // chunks follow.  Each chunk's result slot is fixed by its (row, chunk).
 // kLse: also write the chunk's normaliser pair to lse_part[row * chunks + chunk].
+// Workgroups hold four waves, or one with kLse: that form needs more registers
+// (fewer waves per SIMD), and single-wave workgroups free their slots as soon
+// as their one wave ends instead of waiting for the slowest of four.
 template <bool kLse>
-__global__ __launch_bounds__(256) void topk_partial_bf16_kernel(
+constexpr int partial_waves_per_block() { return kLse ? 1 : 4; }
+
+template <bool kLse>
+__global__ __launch_bounds__(64 * partial_waves_per_block<kLse>()) void topk_partial_bf16_kernel(
     const uint16_t* __restrict__ logits, int64_t req_stride, int64_t slot_stride, int B, int64_t V,
     int K, int chunks, int64_t rows, uint64_t* __restrict__ part, float2* __restrict__ lse_part) {
     constexpr int kChunk = kNV * 8 * kWave;
-    __shared__ u32x4 stage_all[4][kStage + kWave];
-    __shared__ uint16_t meta_all[4][kStage + kWave];
-    __shared__ uint32_t cand_all[4][kCand16 + kWave];
-    __shared__ uint64_t out_all[4][kWave];
-    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t w = blockIdx.x * 4u + wave;
+    constexpr int kWPB = partial_waves_per_block<kLse>();
+    __shared__ u32x4 stage_all[kWPB][kStage + kWave];
+    __shared__ uint16_t meta_all[kWPB][kStage + kWave];
+    __shared__ uint32_t cand_all[kWPB][kCand16 + kWave];
+    __shared__ uint64_t out_all[kWPB][kWave];
+    const uint32_t wave = kWPB == 1 ? 0u : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t w = blockIdx.x * static_cast<uint32_t>(kWPB) + wave;
     const uint32_t uB = static_cast<uint32_t>(B), uch = static_cast<uint32_t>(chunks);
     const uint32_t nrows = static_cast<uint32_t>(rows);
     const bool ragged = V % kChunk != 0;
@@ -825,11 +856,15 @@ hipError_t launch_topk_partial(int dtype, const void* logits, int64_t req_stride
     const dim3 grid(static_cast<unsigned>((waves + 3) / 4));
     const uint16_t* lb = static_cast<const uint16_t*>(logits);
     const float* lf = static_cast<const float*>(logits);
-    if (dtype == CORR_DT_BF16)
-        return lse_part ? launch(topk_partial_bf16_kernel<true>, grid, 256, 0, stream, lb, req_stride, slot_stride,
-                                 B, V, K, chunks, rows, part, lse_part)
-                        : launch(topk_partial_bf16_kernel<false>, grid, 256, 0, stream, lb, req_stride,
-                                 slot_stride, B, V, K, chunks, rows, part, lse_part);
+    if (dtype == CORR_DT_BF16) {
+        constexpr int w1 = partial_waves_per_block<true>(), w4 = partial_waves_per_block<false>();
+        return lse_part ? launch(topk_partial_bf16_kernel<true>, dim3(static_cast<unsigned>((waves + w1 - 1) / w1)),
+                                 64 * w1, 0, stream, lb, req_stride, slot_stride, B, V, K, chunks, rows, part,
+                                 lse_part)
+                        : launch(topk_partial_bf16_kernel<false>, dim3(static_cast<unsigned>((waves + w4 - 1) / w4)),
+                                 64 * w4, 0, stream, lb, req_stride, slot_stride, B, V, K, chunks, rows, part,
+                                 lse_part);
+    }
     return lse_part ? launch(topk_partial_f32_kernel<true>, grid, 256, 0, stream, lf, req_stride, slot_stride, B, V,
                              K, chunks, rows, part, lse_part)
                     : launch(topk_partial_f32_kernel<false>, grid, 256, 0, stream, lf, req_stride, slot_stride, B,
