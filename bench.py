@@ -178,6 +178,45 @@ def measure_topk_softmax(corr, cfg, dev_sets, host_logits, st, stream, steps, wa
     return res
 
 
+def measure_ceilings(steps: int = 20) -> dict:
+    """The box's own reference ceilings: a large device-to-device copy (HBM
+    read + write) and a large bf16 matrix product through PyTorch's library
+    GEMM (MFMA).  Context for the roofline fractions, not part of the path."""
+    import torch
+    out = {}
+    nb = 2 << 30
+    src = torch.empty(nb, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    t = a.elapsed_time(b) / steps / 1e3
+    out["copy"] = {"bytes": 2 * nb, "us": round(t * 1e6, 1), "GB/s": round(2 * nb / t / 1e9, 1),
+                   "what": "torch copy_ of 2 GiB (read + write)"}
+    del src, dst
+    n = 8192
+    x = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    y = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(x, y)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(steps):
+        torch.matmul(x, y)
+    b.record()
+    torch.cuda.synchronize()
+    t = a.elapsed_time(b) / steps / 1e3
+    out["gemm_bf16"] = {"flops": 2 * n ** 3, "us": round(t * 1e6, 1), "TFLOP/s": round(2 * n ** 3 / t / 1e12, 1),
+                        "what": "torch.matmul bf16 8192 x 8192 x 8192"}
+    return out
+
+
 def cpu_baseline(cfg, inputs, min_seconds: float = 12.0, max_passes: int = 64) -> dict:
     import oracle
     oracle.build(force=False)
@@ -208,6 +247,8 @@ def main():
                     help="how the path through the candidate lattice is chosen")
     ap.add_argument("--path-lambda", type=float, default=0.75, help="lambda of the Geometric path rule")
     ap.add_argument("--no-fold", action="store_true", help="skip the folded-table measurement")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="also measure the box's copy and large-GEMM ceilings (reference figures)")
     ap.add_argument("--no-softmax", action="store_true",
                     help="skip the fused top-K + normalisation measurement")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -390,6 +431,9 @@ def main():
         "folded_table": folded,
         "fused_softmax": fused_softmax,
     }
+    if args.ceilings:
+        out["ceilings"] = measure_ceilings()
+        log("ceilings: %s" % json.dumps(out["ceilings"]))
     print(json.dumps(out), flush=True)
     corr.close()
 

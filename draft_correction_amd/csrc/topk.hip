@@ -38,7 +38,8 @@ namespace {
 
 constexpr int kNV = 12;        // 16-byte loads per lane
 constexpr int kCap = 256;      // compacted candidates per wave (float32 path)
-constexpr int kStage = 64;     // staged 16-byte vectors per wave (bf16 path)
+constexpr int kStage = 64;     // staged 16-byte vectors per wave (bf16 path, K <= 16)
+constexpr int kStageWide = 128; // the same for K > 16
 constexpr int kCand16 = 256;   // candidate keys per wave (bf16 path)
 
 typedef short i16x2 __attribute__((ext_vector_type(2)));
@@ -106,44 +107,6 @@ __device__ __forceinline__ float2 chunk_expsum(float ml, float sl) {
 
 // --------------------------------------------------------------- bf16 path --
 
-// Bf16 element `local` of a chunk (0xFFFF, key 0, past the end).
-__device__ __forceinline__ uint32_t chunk_elem(const uint16_t* src, int nvalid, int local) {
-    return local < nvalid ? static_cast<uint32_t>(src[local]) : 0xFFFFu;
-}
-
-// Exact top-`target` of a chunk by a bitwise search over the 32-bit composites
-// of every element, re-read from memory (used only when the threshold admits
-// too many elements, i.e. heavy ties).  Writes the winners unordered to the
-// wave's LDS output list and returns how many there are.
-__device__ __forceinline__ int topk_bf16_exhaustive(const uint16_t* src, int nvalid, int64_t c0, int K,
-                                                 int target, uint64_t* out) {
-    constexpr int kChunk = kNV * 8 * kWave;
-    const int l = lane_id();
-    uint32_t tc = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t c = tc | (1u << bit);
-        int cnt = 0;
-#pragma unroll 1
-        for (int local0 = 0; local0 < kChunk; local0 += kWave) {
-            const int local = local0 + l;
-            const uint32_t comp = (key16_of(chunk_elem(src, nvalid, local)) << 16) | (0xFFFFu - local);
-            cnt += popc64(ballot(comp >= c));
-        }
-        if (cnt >= target) tc = c;
-    }
-    int outn = 0;
-#pragma unroll 1
-    for (int local0 = 0; local0 < kChunk; local0 += kWave) {
-        const int local = local0 + l;
-        const uint32_t k16 = key16_of(chunk_elem(src, nvalid, local));
-        const bool p = ((k16 << 16) | (0xFFFFu - local)) >= tc && k16 != 0u;
-        const uint64_t m = ballot(p);
-        const int pos = outn + prefix_count(m);
-        if (p && pos < K) out[pos] = merge_comp(key_of_bits(raw16_of_key16(k16) << 16), c0 + local);
-        outn += popc64(m);
-    }
-    return outn;
-}
 
 // One chunk of one drafted row: kNV * 512 consecutive logits (fewer at the
 // end of the row).  Chunk numbers are wave-uniform, so all of this is scalar.
@@ -190,6 +153,104 @@ __device__ __forceinline__ void load_ragged_chunk(u32x4 (&raw)[kNV], const Chunk
 __device__ __forceinline__ uint32_t key16_flip(uint32_t x) {
     const uint32_t k = x ^ ((x & 0x8000u) ? 0xFFFFu : 0x8000u);
     return k == 0x7FFFu ? 0x8000u : k;
+}
+
+// Vector t of this lane's share of a chunk, loaded again (16 bytes; the
+// elements past the end of a row's last chunk read as 0xFFFF, key 0).
+__device__ __forceinline__ u32x4 chunk_vec(const Chunk& c, int t) {
+    const int l = lane_id();
+    const int e0 = (t * kWave + l) * 8;
+    if (e0 + 8 <= c.nvalid) return load16(c.src + e0);
+    u32x4 v = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+    for (int j = 0; j < 8; ++j) {
+        if (e0 + j < c.nvalid) {
+            const uint32_t b = c.src[e0 + j];
+            const int q = j >> 1;
+            v[q] = (j & 1) ? ((v[q] & 0x0000FFFFu) | (b << 16)) : ((v[q] & 0xFFFF0000u) | b);
+        }
+    }
+    return v;
+}
+
+// Exact top-`target` of a chunk without the threshold and staging (used when
+// too many elements reach the lane-maximum threshold, i.e. heavy ties):
+// T = the target-th largest value key by a bitwise search over every element
+// (per-lane counts summed over the wave), then every element above T and, of
+// those equal to T, the ones with the lowest local indices (vector-major:
+// vector t*64 + lane, then its 8 elements).  Each pass loads the chunk again
+// with coalesced 16-byte loads, half of it in flight at a time (the compiler
+// barriers keep the loads inside the pass and bound what is live, so this
+// rarely used path needs fewer registers than the usual one).  Writes the
+// winners unordered to `out` and returns how many there are.
+__device__ __forceinline__ int topk_bf16_reread(const Chunk& c, int64_t c0, int K, int target, uint64_t* out) {
+    const int l = lane_id();
+    constexpr int kHalf = kNV / 2;
+    auto count_ge = [&](uint32_t cc) {
+        int cnt = 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            asm volatile("" ::: "memory");
+            u32x4 v[kHalf];
+#pragma unroll
+            for (int t = 0; t < kHalf; ++t) v[t] = chunk_vec(c, h * kHalf + t);
+#pragma unroll
+            for (int t = 0; t < kHalf; ++t) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) cnt += key16_flip((v[t][j >> 1] >> (16 * (j & 1))) & 0xFFFFu) >= cc;
+                asm volatile("" : "+v"(cnt));   // one vector's compares at a time
+            }
+        }
+        return static_cast<int>(wave_sum64(static_cast<float>(cnt)));   // <= 6144: exact in float
+    };
+    uint32_t T = 0;
+    for (int bit = 15; bit >= 0; --bit) {
+        const uint32_t cc = T | (1u << bit);
+        if (count_ge(cc) >= target) T = cc;
+    }
+    T = max(T, 1u);  // key 0 is padding, never a winner
+    const int ngt = T < 0xFFFFu ? count_ge(T + 1u) : 0;
+    const int need = target - ngt;   // >= 1 elements equal to T
+    int ogt = 0, oeq = 0;
+    for (int t = 0; t < kNV; ++t) {   // one vector at a time (rolled)
+        asm volatile("" ::: "memory");
+        const u32x4 vt = chunk_vec(c, t);
+        // elements above T, any order
+        int eqn = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t k = key16_flip((vt[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+            const bool gt = k > T;
+            const uint64_t m = ballot(gt);
+            const int pos = ogt + prefix_count(m);
+            if (gt && pos < K)
+                out[pos] = merge_comp(key_of_bits(raw16_of_key16(k) << 16),
+                                      c0 + (static_cast<int64_t>(t * kWave + l) * 8 + j));
+            ogt += popc64(m);
+            eqn += k == T;
+        }
+        // elements equal to T in index order: this lane's first slot is the
+        // count of equal elements in lower lanes (four bit planes: <= 8 each)
+        int base = 0, tot = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const uint64_t m = ballot((eqn >> b) & 1);
+            base += prefix_count(m) << b;
+            tot += popc64(m) << b;
+        }
+        int r = oeq + base;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t k = key16_flip((vt[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+            if (k == T) {
+                if (r < need)
+                    out[ngt + r] = merge_comp(key_of_bits(raw16_of_key16(k) << 16),
+                                              c0 + (static_cast<int64_t>(t * kWave + l) * 8 + j));
+                ++r;
+            }
+        }
+        oeq += tot;
+    }
+    return ngt + min(oeq, need);
 }
 
 // Bit t set when 16-byte vector t of this lane holds an element at or above
@@ -280,6 +341,7 @@ __device__ __forceinline__ float2 lane_expsum_bf16(const u32x4 (&raw)[kNV], uint
 // K slots] as merge composites (padded with 0 = "no element").  The LDS lists
 // have one trash slot per lane past their capacity, so every list write is
 // issued by every lane (no branches): lanes with nothing to add write there.
+template <int kSt>
 __device__ __forceinline__ void select_chunk(const u32x4 (&raw)[kNV], uint32_t lane_key, const Chunk& c, int K,
                                              uint32_t chunks, u32x4* stage, uint16_t* meta, uint32_t* cand,
                                              uint64_t* outb, uint64_t* __restrict__ part) {
@@ -318,7 +380,7 @@ __device__ __forceinline__ void select_chunk(const u32x4 (&raw)[kNV], uint32_t l
 
     const int64_t obase = (static_cast<int64_t>(c.row) * chunks + c.chunk) * K;
     int outn = 0;
-    bool fast = nst <= static_cast<uint32_t>(kStage);
+    bool fast = nst <= static_cast<uint32_t>(kSt);
     uint32_t nc = 0;
     if (fast) {
         // stage the hit vectors (and their local vector numbers)
@@ -326,7 +388,7 @@ __device__ __forceinline__ void select_chunk(const u32x4 (&raw)[kNV], uint32_t l
 #pragma unroll
         for (int t = 0; t < kNV; ++t) {
             const uint32_t hit = (hm >> t) & 1u;
-            const uint32_t slot = hit ? k : kStage + l;
+            const uint32_t slot = hit ? k : kSt + l;
             stage[slot] = raw[t];
             meta[slot] = static_cast<uint16_t>(t * kWave + l);
             k += hit;
@@ -415,7 +477,7 @@ __device__ __forceinline__ void select_chunk(const u32x4 (&raw)[kNV], uint32_t l
             outn += popc64(m);
         }
     } else {
-        outn = topk_bf16_exhaustive(c.src, c.nvalid, c0, K, target, outb);
+        outn = topk_bf16_reread(c, c0, K, target, outb);
     }
     // One store instruction per chunk: lane l writes slot min(l, K-1) (lanes
     // past K-1 repeat that slot's value); chunks with fewer than K elements
@@ -435,14 +497,14 @@ __device__ __forceinline__ void select_chunk(const u32x4 (&raw)[kNV], uint32_t l
 template <bool kLse>
 constexpr int partial_waves_per_block() { return kLse ? 1 : 4; }
 
-template <bool kLse>
+template <bool kLse, int kSt>
 __global__ __launch_bounds__(64 * partial_waves_per_block<kLse>()) void topk_partial_bf16_kernel(
     const uint16_t* __restrict__ logits, int64_t req_stride, int64_t slot_stride, int B, int64_t V,
     int K, int chunks, int64_t rows, uint64_t* __restrict__ part, float2* __restrict__ lse_part) {
     constexpr int kChunk = kNV * 8 * kWave;
     constexpr int kWPB = partial_waves_per_block<kLse>();
-    __shared__ u32x4 stage_all[kWPB][kStage + kWave];
-    __shared__ uint16_t meta_all[kWPB][kStage + kWave];
+    __shared__ u32x4 stage_all[kWPB][kSt + kWave];
+    __shared__ uint16_t meta_all[kWPB][kSt + kWave];
     __shared__ uint32_t cand_all[kWPB][kCand16 + kWave];
     __shared__ uint64_t out_all[kWPB][kWave];
     const uint32_t wave = kWPB == 1 ? 0u : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -476,7 +538,7 @@ __global__ __launch_bounds__(64 * partial_waves_per_block<kLse>()) void topk_par
         const float2 cs = chunk_expsum(ls.x, ls.y);
         if (lane_id() == 0) lse_part[static_cast<int64_t>(c.row) * uch + c.chunk] = cs;
     }
-    select_chunk(raw, lane_key, c, K, uch, stage_all[wave], meta_all[wave], cand_all[wave], out_all[wave], part);
+    select_chunk<kSt>(raw, lane_key, c, K, uch, stage_all[wave], meta_all[wave], cand_all[wave], out_all[wave], part);
 }
 
 // ---------------------------------------------------------- float32 path --
@@ -723,7 +785,7 @@ __device__ void merge_row_wave(const uint64_t* __restrict__ ent, int M, int K, u
 }
 
 // Fast path of the merge for rows of at most kMergePer * 64 candidates, held in
-// registers.  Value keys are compared on their top `kbits` bits: for bf16
+// registers (the merge launch's register count is set by its GEMM tiles).  Value keys are compared on their top `kbits` bits: for bf16
 // logits the rest of the float32-order key is fixed by those bits, so the
 // searches are exact with kbits = 16.  Steps: threshold T0 = K-th largest lane
 // maximum; the entries at or above it (at least K) are compacted; T = K-th
@@ -731,7 +793,7 @@ __device__ void merge_row_wave(const uint64_t* __restrict__ ent, int M, int K, u
 // among those equal to T, the ones with the largest composites (smallest
 // ids).  Returns false, having written nothing, when more than kMergeCap
 // entries reach T0; the general search then takes over.
-constexpr int kMergePer = 8;
+constexpr int kMergePer = 16;   // up to 1024 candidates per row (64 chunks at K = 16, 32 at K = 32)
 
 __device__ __forceinline__ bool merge_row_fast(const uint64_t* __restrict__ ent, int M, int K, int kbits,
                                                uint64_t* sel, uint64_t* fin, int32_t* __restrict__ ids,
@@ -857,13 +919,20 @@ hipError_t launch_topk_partial(int dtype, const void* logits, int64_t req_stride
     const uint16_t* lb = static_cast<const uint16_t*>(logits);
     const float* lf = static_cast<const float*>(logits);
     if (dtype == CORR_DT_BF16) {
+        // the staging area holds the vectors reaching the lane-maximum
+        // threshold: about K of them, so larger K gets the wider area
         constexpr int w1 = partial_waves_per_block<true>(), w4 = partial_waves_per_block<false>();
-        return lse_part ? launch(topk_partial_bf16_kernel<true>, dim3(static_cast<unsigned>((waves + w1 - 1) / w1)),
-                                 64 * w1, 0, stream, lb, req_stride, slot_stride, B, V, K, chunks, rows, part,
-                                 lse_part)
-                        : launch(topk_partial_bf16_kernel<false>, dim3(static_cast<unsigned>((waves + w4 - 1) / w4)),
-                                 64 * w4, 0, stream, lb, req_stride, slot_stride, B, V, K, chunks, rows, part,
-                                 lse_part);
+        const dim3 g1(static_cast<unsigned>((waves + w1 - 1) / w1)), g4(static_cast<unsigned>((waves + w4 - 1) / w4));
+        const bool wide = K > 16;
+        if (lse_part)
+            return wide ? launch(topk_partial_bf16_kernel<true, kStageWide>, g1, 64 * w1, 0, stream, lb, req_stride,
+                                 slot_stride, B, V, K, chunks, rows, part, lse_part)
+                        : launch(topk_partial_bf16_kernel<true, kStage>, g1, 64 * w1, 0, stream, lb, req_stride,
+                                 slot_stride, B, V, K, chunks, rows, part, lse_part);
+        return wide ? launch(topk_partial_bf16_kernel<false, kStageWide>, g4, 64 * w4, 0, stream, lb, req_stride,
+                             slot_stride, B, V, K, chunks, rows, part, lse_part)
+                    : launch(topk_partial_bf16_kernel<false, kStage>, g4, 64 * w4, 0, stream, lb, req_stride,
+                             slot_stride, B, V, K, chunks, rows, part, lse_part);
     }
     return lse_part ? launch(topk_partial_f32_kernel<true>, grid, 256, 0, stream, lf, req_stride, slot_stride, B, V,
                              K, chunks, rows, part, lse_part)
