@@ -33,7 +33,7 @@ PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 # itself, the w2 multiply-add, and the two transcendentals v_rcp_f32 and
 # v_exp_f32) plus 2 x 3 extra slots for the quarter-rate transcendentals
 # (19 slots)
-PEAK_GELU_T = 256 * 64 * 2.4e9 / 19 / 1e12
+PEAK_GELU_T = 256 * 64 * 2.4e9 / 13 / 1e12   # 13 VALU issue slots per evaluation (see the design notes)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = os.path.join(ROOT, "draft_correction_amd", "csrc")
 
