@@ -10,6 +10,7 @@ from .oracle import (  # noqa: F401
     OracleDesc,
     confidence,
     accepted_lengths,
+    beam,
     build,
     gelu,
     get_threads,

@@ -18,7 +18,8 @@
  *   (5) the prefix-first walk: slot 1 takes the drafter argmax, then
  *       k_{p+1} = argmax_b S_p(k_p, b).
  * The Global-Sum path rule (LiLiCorr, appendix E, Eq. 12) replaces (5) by the
- * path with the largest summed transition score, by dynamic programming.
+ * path with the largest summed transition score, by dynamic programming; a
+ * narrow beam search over the same score is a further rule.
  * The cosine variant (LiLiCorr, section 3.2, Eq. 1) replaces (3)-(4) by
  *   S_p(a,b) = l_{p+1}(b) + sigma * cos(W_out z_p^a, W_in z_{p+1}^b).
  * Beside step (1), the log-normaliser of each slot row over the whole
@@ -495,6 +496,83 @@ int oracle_viterbi(const oracle_desc *D, int32_t n, const double *scores, const 
             tokens[(size_t)i * B + sl] = ids[((size_t)i * B + sl) * K + choice[(size_t)i * B + sl]];
     }
     free(best); free(next); free(from);
+    return ORA_OK;
+}
+
+/* Beam search over the candidate lattice (the critique on the DCOCO page,
+ * weakness (2): the single-path walk cannot look ahead, so widen it into a
+ * narrow beam of 2-4 paths at O(B K beam) cost).  The page gives no path
+ * score; the one read here is the summed transition score of the Global-Sum
+ * rule, slot 1 fixed at rank 0 as in the walk.  The beam starts as the single
+ * path (0) with score 0; at pair p every beam path i extends by every
+ * successor b with score g_i + S_p(last_i, b), and the W best extensions are
+ * kept, ordered by score descending, then beam index ascending, then b
+ * ascending.  The answer is the first path of the final beam.  Scores are
+ * float32 and each extension's score is one float32 addition (the kernel's
+ * precision, so that both sides rank the same numbers).  W = 1 is the greedy
+ * walk; a W of at least K^(B-1) keeps every path.  total[i] (optional)
+ * receives the chosen path's score. */
+typedef struct {
+    float g;
+    int32_t beam, b;
+} beam_cand_t;
+
+static int beam_cmp(const void *pa, const void *pb)
+{
+    const beam_cand_t *a = (const beam_cand_t *)pa, *b = (const beam_cand_t *)pb;
+    if (a->g > b->g) return -1;
+    if (a->g < b->g) return 1;
+    if (a->beam != b->beam) return a->beam < b->beam ? -1 : 1;
+    return (a->b > b->b) - (a->b < b->b);
+}
+
+int oracle_beam(const oracle_desc *D, int32_t n, const float *scores, const int32_t *ids, int32_t W,
+                int32_t *tokens, int32_t *choice, float *total)
+{
+    if (!D || !scores || !ids || !tokens || !choice || n < 0 || W < 1) return ORA_E_ARG;
+    const int B = D->B, K = D->K;
+    const size_t ncand = (size_t)W * K;
+    float *g = malloc(sizeof(float) * W), *g2 = malloc(sizeof(float) * W);
+    int32_t *path = malloc(sizeof(int32_t) * W * B), *path2 = malloc(sizeof(int32_t) * W * B);
+    beam_cand_t *cand = malloc(sizeof(beam_cand_t) * ncand);
+    if (!g || !g2 || !path || !path2 || !cand) {
+        free(g); free(g2); free(path); free(path2); free(cand);
+        return ORA_E_NOMEM;
+    }
+    for (int32_t i = 0; i < n; ++i) {
+        int nb = 1;
+        g[0] = 0.f;
+        path[0] = 0;
+        for (int p = 0; p + 1 < B; ++p) {
+            const float *Sp = scores + ((size_t)i * (B - 1) + p) * K * K;
+            size_t nc = 0;
+            for (int bi = 0; bi < nb; ++bi) {
+                const int last = path[(size_t)bi * B + p];
+                for (int b = 0; b < K; ++b) {
+                    cand[nc].g = g[bi] + Sp[(size_t)last * K + b];   /* one float32 addition */
+                    cand[nc].beam = bi;
+                    cand[nc].b = b;
+                    ++nc;
+                }
+            }
+            qsort(cand, nc, sizeof(beam_cand_t), beam_cmp);
+            const int keep = (int)(nc < (size_t)W ? nc : (size_t)W);
+            for (int k = 0; k < keep; ++k) {
+                g2[k] = cand[k].g;
+                memcpy(path2 + (size_t)k * B, path + (size_t)cand[k].beam * B, sizeof(int32_t) * (p + 1));
+                path2[(size_t)k * B + p + 1] = cand[k].b;
+            }
+            nb = keep;
+            float *tg = g; g = g2; g2 = tg;
+            int32_t *tp = path; path = path2; path2 = tp;
+        }
+        if (total) total[i] = g[0];
+        for (int sl = 0; sl < B; ++sl) {
+            choice[(size_t)i * B + sl] = path[sl];
+            tokens[(size_t)i * B + sl] = ids[((size_t)i * B + sl) * K + path[sl]];
+        }
+    }
+    free(g); free(g2); free(path); free(path2); free(cand);
     return ORA_OK;
 }
 

@@ -60,6 +60,7 @@ def _load():
         lib.oracle_score.argtypes = [P, P, C.c_int32, P, P, P, P, P]
         lib.oracle_walk.argtypes = [P, C.c_int32, P, P, P, P]
         lib.oracle_viterbi.argtypes = [P, C.c_int32, P, P, C.c_double, P, P, P]
+        lib.oracle_beam.argtypes = [P, C.c_int32, P, P, C.c_int32, P, P, P]
         lib.oracle_accepted.argtypes = [C.c_int32, C.c_int32, P, P, P]
         lib.oracle_layernorm.argtypes = [P, C.c_int, C.c_double, P, P]
         lib.oracle_gelu.restype = C.c_double
@@ -299,6 +300,22 @@ def viterbi(desc: OracleDesc, scores, ids, n: int, lam: float = 1.0):
     d = desc.c()
     _check(_load().oracle_viterbi(C.byref(d), n, _ptr(scores), _ptr(ids), float(lam), _ptr(tokens),
                                   _ptr(choice), _ptr(total)), "viterbi")
+    return tokens, choice, total
+
+
+def beam(desc: OracleDesc, scores, ids, n: int, width: int):
+    """Beam search of the given width over float32 scores (summed transition
+    score, slot 1 at rank 0): tokens [n][B], choices [n][B] and the chosen
+    path's float32 score [n]."""
+    keep = _Keep()
+    scores = keep.arr(scores, np.float32)
+    ids = keep.arr(ids, np.int32)
+    tokens = np.empty((n, desc.B), np.int32)
+    choice = np.empty((n, desc.B), np.int32)
+    total = np.empty(n, np.float32)
+    d = desc.c()
+    _check(_load().oracle_beam(C.byref(d), n, _ptr(scores), _ptr(ids), int(width), _ptr(tokens), _ptr(choice),
+                               _ptr(total)), "beam")
     return tokens, choice, total
 
 

@@ -465,6 +465,67 @@ def test_geometric_rejects_non_positive_lambda():
             oracle.viterbi(_desc(3, 3), S, ids, 1, lam=lam)
 
 
+# ------------------------------------------------------- beam search --
+# The critique on the DCOCO page (weakness 2) proposes widening the walk into
+# a beam of 2-4 paths; read as beam search on the summed transition score.
+
+def test_beam_width_one_is_the_walk():
+    """W = 1 keeps the single best extension at every step: the prefix-first
+    walk, ties (integer scores) included."""
+    g = np.random.default_rng(31)
+    for trial in range(40):
+        B, K = int(g.integers(2, 9)), int(g.integers(1, 7))
+        S = g.integers(-3, 4, size=(3, B - 1, K, K)).astype(np.float32)
+        ids = g.integers(0, 100, size=(3, B, K)).astype(np.int32)
+        t1, c1, _ = oracle.beam(_desc(B, K), S, ids, 3, 1)
+        t2, c2 = oracle.walk(_desc(B, K), S.astype(np.float64), ids, 3)
+        np.testing.assert_array_equal(c1, c2)
+        np.testing.assert_array_equal(t1, t2)
+
+
+def test_beam_covering_every_path_is_the_optimum():
+    """A width of K^(B-1) keeps every path, so the answer has the brute-force
+    best summed score (integer scores: float32 sums are exact)."""
+    g = np.random.default_rng(32)
+    for B, K in ((2, 3), (3, 3), (4, 2), (4, 3)):
+        S = g.integers(-5, 6, size=(2, B - 1, K, K)).astype(np.float32)
+        ids = g.integers(0, 100, size=(2, B, K)).astype(np.int32)
+        _, choice, total = oracle.beam(_desc(B, K), S, ids, 2, K ** (B - 1))
+        for i in range(2):
+            best = max(_path_score(S[i].astype(np.float64), c) for c in _paths(B, K))
+            assert total[i] == best == _path_score(S[i].astype(np.float64), choice[i])
+
+
+def test_beam_worked_example_beats_the_walk():
+    """From rank 0 the walk takes successor 0 (5 > 4) and then can only add 0;
+    a beam of two keeps the runner-up, whose next step is worth 10: 4 + 10."""
+    S = np.zeros((1, 2, 2, 2), np.float32)
+    S[0, 0, 0] = [5.0, 4.0]          # pair 0, from rank 0
+    S[0, 1, 0] = [0.0, 0.0]          # pair 1, from candidate 0
+    S[0, 1, 1] = [10.0, 0.0]         # pair 1, from candidate 1
+    ids = np.arange(6, dtype=np.int32).reshape(1, 3, 2)
+    _, c1, t1 = oracle.beam(_desc(3, 2), S, ids, 1, 1)
+    _, c2, t2 = oracle.beam(_desc(3, 2), S, ids, 1, 2)
+    np.testing.assert_array_equal(c1[0], [0, 0, 0])
+    np.testing.assert_array_equal(c2[0], [0, 1, 0])
+    assert (t1[0], t2[0]) == (5.0, 14.0)
+
+
+def test_beam_tie_order_and_float32_sums():
+    """Equal extension scores go to the lower beam index, then the lower
+    successor; sums are single float32 additions (1 + 2^-24 rounds to 1)."""
+    S = np.zeros((1, 2, 2, 2), np.float32)
+    S[0, 0, 0] = [1.0, 1.0]                  # two equal first steps: beam 0 is b = 0
+    S[0, 1, 0] = [0.0, 0.0]                  # from beam 0: 1 + 0
+    S[0, 1, 1] = [2.0 ** -24, 0.0]           # from beam 1: 1 + 2^-24, which is 1 in float32
+    ids = np.zeros((1, 3, 2), np.int32)
+    _, c, t = oracle.beam(_desc(3, 2), S, ids, 1, 2)
+    # every extension scores exactly 1.0 in float32, so beam 0 and successor 0
+    # win (summed in float64, beam 1's 1 + 2^-24 would win instead)
+    np.testing.assert_array_equal(c[0], [0, 0, 0])
+    assert t[0] == np.float32(1.0)
+
+
 # ------------------------------------------- vocabulary normalisation --
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
