@@ -89,19 +89,19 @@ def algorithmic_work(cfg: dict, n: int) -> dict:
     w["cand"] = dict(bound="hbm", bytes=rows * K * (r * 4 * 2 + uvb),
                      flops=2 * rows * K * (2 * r * r + (2 * h * r if uvb else 0)),
                      per_unit=r * 8 + uvb, units=rows * K, unit="candidate (u in; z and U|V out)")
-    w["finish"] = w["finish_walk"] = w["finish_viterbi"] = dict(bound="hbm", bytes=n * (B - 1) * K * K * 4 * 2,
+    w["finish"] = w["finish_walk"] = w["finish_viterbi"] = w["finish_beam"] = dict(bound="hbm", bytes=n * (B - 1) * K * K * 4 * 2,
                                           per_unit=(B - 1) * K * K * 8, units=n, unit="block")
     # the transition MLP epilogue is bound by the vector ALU: K^2 h GELU
     # evaluations per pair (13 VALU instructions each, 2 of them quarter-rate
     # transcendentals) against 256 CUs x 64 lanes x 2.4 GHz
     w["mlp"] = dict(bound="alu", gelu=pairs * K * K * h, flops=2 * pairs * K * K * h,
                     per_unit=h, units=pairs * K * K, unit="transition (h GELU evaluations)")
-    w["cosine"] = w["cosine_walk"] = w["cosine_viterbi"] = dict(
+    w["cosine"] = w["cosine_walk"] = w["cosine_viterbi"] = w["cosine_beam"] = dict(
         bound="hbm", bytes=pairs * 2 * K * cfg["dvec"] * 4, per_unit=2 * K * cfg["dvec"] * 4, units=pairs, unit="pair")
     w["walk"] = dict(bound="hbm", bytes=n * (B - 1) * K * 4, per_unit=(B - 1) * K * 4, units=n,
                      unit="block (scores rows read)")
     # the Global-Sum path reads every score of the block once
-    w["viterbi"] = dict(bound="hbm", bytes=n * (B - 1) * K * K * 4, per_unit=(B - 1) * K * K * 4, units=n,
+    w["viterbi"] = w["beam"] = dict(bound="hbm", bytes=n * (B - 1) * K * K * 4, per_unit=(B - 1) * K * K * 4, units=n,
                         unit="block (all scores read)")
     return w
 
@@ -243,9 +243,10 @@ def main():
     ap.add_argument("--copies", type=int, default=4, help="independent input sets rotated per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--head", default="normal")
-    ap.add_argument("--path-rule", default="greedy", choices=["greedy", "global_sum", "geometric"],
+    ap.add_argument("--path-rule", default="greedy", choices=["greedy", "global_sum", "geometric", "beam"],
                     help="how the path through the candidate lattice is chosen")
     ap.add_argument("--path-lambda", type=float, default=0.75, help="lambda of the Geometric path rule")
+    ap.add_argument("--beam-width", type=int, default=4, help="width of the beam path rule (1..4)")
     ap.add_argument("--no-fold", action="store_true", help="skip the folded-table measurement")
     ap.add_argument("--ceilings", action="store_true",
                     help="also measure the box's copy and large-GEMM ceilings (reference figures)")
@@ -265,7 +266,7 @@ def main():
     from workload import config
     from workload.gen import gen_embed, gen_hidden, gen_logits, gen_weights
 
-    cfg = config(args.workload, path_rule=args.path_rule, path_lambda=args.path_lambda)
+    cfg = config(args.workload, path_rule=args.path_rule, path_lambda=args.path_lambda, beam_width=args.beam_width)
     n = cfg["n"]
     log("generating %s inputs (%d copies)" % (args.workload, args.copies))
     t0 = time.perf_counter()
@@ -423,7 +424,8 @@ def main():
                                "MLP %d->%d->1, %s" % (args.workload, n, B, cfg["V"], K, cfg["d"],
                                                       cfg["r"], 3 * cfg["r"] + 2, cfg["h"], cfg["variant"])
                                + {"greedy": "", "global_sum": ", Global-Sum path",
-                                  "geometric": ", Geometric path (lambda %g)" % args.path_lambda}[args.path_rule],
+                                  "geometric": ", Geometric path (lambda %g)" % args.path_lambda,
+                                  "beam": ", beam path (width %d)" % args.beam_width}[args.path_rule],
                    "global_batch": n, "rotating_input_sets": args.copies},
         "roofline": roof,
         "kernels": kernels,

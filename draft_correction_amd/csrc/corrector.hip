@@ -12,7 +12,7 @@
 #include "kernels.h"
 
 static_assert(corr::kPathGreedy == CORR_PATH_GREEDY && corr::kPathGlobalSum == CORR_PATH_GLOBAL_SUM &&
-                  corr::kPathGeometric == CORR_PATH_GEOMETRIC,
+                  corr::kPathGeometric == CORR_PATH_GEOMETRIC && corr::kPathBeam == CORR_PATH_BEAM,
               "kernel path-rule values match the header");
 
 using namespace corr;
@@ -176,10 +176,13 @@ struct Seq {
 // Step (5) over precomputed scores, by the handle's path rule.
 hipError_t launch_path_rule(const corrector* h, const float* scores, const int32_t* ids, int32_t n, int32_t* tokens,
                             int32_t* choice, hipStream_t s) {
-    return launch_path(scores, ids, n, h->d.slots, h->d.k, h->d.path_rule, h->d.path_lambda, tokens, choice, s);
+    return launch_path(scores, ids, n, h->d.slots, h->d.k, h->d.path_rule, h->d.path_lambda, h->d.beam_width, tokens,
+                       choice, s);
 }
 
-const char* path_name(const corrector* h) { return h->d.path_rule == CORR_PATH_GREEDY ? "walk" : "viterbi"; }
+const char* path_name(const corrector* h) {
+    return h->d.path_rule == CORR_PATH_GREEDY ? "walk" : (h->d.path_rule == CORR_PATH_BEAM ? "beam" : "viterbi");
+}
 
 // Step (1).  With `hj` given, the hidden-state projection runs in the merge
 // launch (it does not depend on the top-K).
@@ -328,7 +331,10 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
         c.choice = fused ? choice : nullptr;
         c.rule = d.path_rule;
         c.lam = d.path_lambda;
-        q(fused ? (d.path_rule == CORR_PATH_GREEDY ? "cosine_walk" : "cosine_viterbi") : "cosine",
+        c.beam = d.beam_width;
+        q(fused ? (d.path_rule == CORR_PATH_GREEDY ? "cosine_walk"
+                                                    : (d.path_rule == CORR_PATH_BEAM ? "cosine_beam" : "cosine_viterbi"))
+                : "cosine",
           [&] { return launch_cosine(c, q.s); });
         if (tokens && !fused)
             q(path_name(h), [&] { return launch_path_rule(h, scores, ids, n, tokens, choice, q.s); });
@@ -363,7 +369,10 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
         f.choice = fused ? choice : nullptr;
         f.rule = d.path_rule;
         f.lam = d.path_lambda;
-        q(fused ? (d.path_rule == CORR_PATH_GREEDY ? "finish_walk" : "finish_viterbi") : "finish",
+        f.beam = d.beam_width;
+        q(fused ? (d.path_rule == CORR_PATH_GREEDY ? "finish_walk"
+                                                    : (d.path_rule == CORR_PATH_BEAM ? "finish_beam" : "finish_viterbi"))
+                : "finish",
           [&] { return launch_finish(f, q.s); });
         if (tokens && !fused)
             q(path_name(h), [&] { return launch_path_rule(h, scores, ids, n, tokens, choice, q.s); });
@@ -381,9 +390,11 @@ int corrector_create(const corrector_desc* desc, const corrector_weights* wt, co
     const corrector_desc& d = *desc;
     if (d.variant != CORR_VARIANT_MLP && d.variant != CORR_VARIANT_COSINE) return CORR_E_UNSUPPORTED;
     if (d.logits_dtype != CORR_DTYPE_BF16 && d.logits_dtype != CORR_DTYPE_F32) return CORR_E_UNSUPPORTED;
-    if (d.path_rule != CORR_PATH_GREEDY && d.path_rule != CORR_PATH_GLOBAL_SUM && d.path_rule != CORR_PATH_GEOMETRIC)
+    if (d.path_rule != CORR_PATH_GREEDY && d.path_rule != CORR_PATH_GLOBAL_SUM && d.path_rule != CORR_PATH_GEOMETRIC &&
+        d.path_rule != CORR_PATH_BEAM)
         return CORR_E_UNSUPPORTED;
     if (d.path_rule == CORR_PATH_GEOMETRIC && !(d.path_lambda > 0.f && d.path_lambda <= 1.f)) return CORR_E_SHAPE;
+    if (d.path_rule == CORR_PATH_BEAM && (d.beam_width < 1 || d.beam_width > 4)) return CORR_E_SHAPE;
     if (d.vocab < 1 || d.vocab > 0x7FFFFFFF) return CORR_E_SHAPE;
     if (d.slots < 1 || d.slots > 64) return CORR_E_SHAPE;  // the walk keeps one slot per lane
     if (d.k < 1 || d.k > 64 || d.k > d.vocab) return CORR_E_SHAPE;

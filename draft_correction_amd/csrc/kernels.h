@@ -12,10 +12,11 @@
 
 namespace corr {
 
-// Path rules (the values of CORR_PATH_GREEDY / _GLOBAL_SUM / _GEOMETRIC).
+// Path rules (the values of CORR_PATH_GREEDY / _GLOBAL_SUM / _GEOMETRIC / _BEAM).
 constexpr int kPathGreedy = 0;
 constexpr int kPathGlobalSum = 1;
 constexpr int kPathGeometric = 2;
+constexpr int kPathBeam = 3;
 
 // Optional timing events for the next launch made on this thread.  The host
 // sequencer sets them around one step; launch() hands them to
@@ -178,6 +179,7 @@ struct FinishArgs {
     int32_t* choice;        // request's path by `rule` follows in the launch
     int rule;
     float lam;              // the Geometric rule's discount
+    int beam;               // the beam rule's width (1..4)
 };
 hipError_t launch_finish(const FinishArgs& a, hipStream_t stream);
 
@@ -198,6 +200,7 @@ struct CosArgs {
     int32_t* choice;
     int rule;
     float lam;
+    int beam;
 };
 hipError_t launch_cosine(const CosArgs& a, hipStream_t stream);
 
@@ -209,8 +212,9 @@ bool path_fits_lds(int B, int K);
 // The path of every request over precomputed scores by `rule`
 // (kPathGreedy: the prefix-first walk; kPathGlobalSum: the best
 // summed score by dynamic programming; kPathGeometric: the same with pair p
-// weighted by lam^p), one wave per request.
-hipError_t launch_path(const float* scores, const int32_t* ids, int n, int B, int K, int rule, float lam,
+// weighted by lam^p; kPathBeam: beam search of width `beam`), one wave per
+// request.
+hipError_t launch_path(const float* scores, const int32_t* ids, int n, int B, int K, int rule, float lam, int beam,
                        int32_t* tokens, int32_t* choice, hipStream_t stream);
 
 // ---- intermediates (walk.hip)

@@ -177,18 +177,133 @@ __host__ __device__ inline size_t path_chain_offset(int B, int K, bool scores_in
 __host__ __device__ inline size_t path_vb_offset(int B, int K, bool scores_in_lds) {
     return (path_chain_offset(B, K, scores_in_lds) + sizeof(int) * static_cast<size_t>(B) + 15) / 16 * 16;
 }
-__host__ __device__ inline size_t path_lds_end(int B, int K, bool scores_in_lds) {
+__host__ __device__ inline size_t path_beam_offset(int B, int K, bool scores_in_lds) {
     return path_vb_offset(B, K, scores_in_lds) + sizeof(float) * static_cast<size_t>((K + 15) / 16 * 16);
+}
+// the beam's backpointers: [B-1][4] (parent, successor) byte pairs
+__host__ __device__ inline size_t path_lds_end(int B, int K, bool scores_in_lds) {
+    return path_beam_offset(B, K, scores_in_lds) + static_cast<size_t>(B > 1 ? B - 1 : 0) * 8;
+}
+
+// Largest value over the wave, the same in every lane.
+__device__ __forceinline__ float wave_max_all(float v) {
+    const float m = row16_max(v);
+    return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 0)),
+                       __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 16))),
+                 fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 32)),
+                       __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 48))));
+}
+
+// Beam search of width W (1..4) by one wave over the request's scores `src`
+// ([B-1][K][K], LDS or memory): the beam starts as the single path (rank 0)
+// with score 0; at pair p, extension c = i*K + b of beam path i by successor
+// b scores g_i + S_p(last_i, b) (one float32 addition), lane l holding
+// extensions l, l + 64, l + 128, l + 192; W rounds each take the largest
+// remaining score, the lowest c among equals (beam index, then successor), so
+// the kept paths are ordered as the rounds found them.  Beam scores and last
+// candidates are wave-uniform registers; the (parent, successor) of every
+// kept path goes to LDS (bp, [B-1][4][2] bytes) and the first path of the
+// last step is traced back through it.
+__device__ __forceinline__ void beam_wave(const float* src, uint8_t* bp, int* chain, const int32_t* __restrict__ ids,
+                                          int req, int B, int K, int W, int32_t* __restrict__ tokens,
+                                          int32_t* __restrict__ choice) {
+    const int l = lane_id();
+    float g[4] = {0.f, 0.f, 0.f, 0.f};
+    int last[4] = {0, 0, 0, 0};
+    int nb = 1;
+    for (int p = 0; p + 1 < B; ++p) {
+        const float* Sp = src + static_cast<int64_t>(p) * K * K;
+        const int nc = nb * K;
+        float cv[4];
+        bool ok[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = j * kWave + l;
+            const int i = (c >= K) + (c >= 2 * K) + (c >= 3 * K);
+            const int b = c - i * K;
+            ok[j] = c < nc;
+            const float gi = i == 0 ? g[0] : (i == 1 ? g[1] : (i == 2 ? g[2] : g[3]));
+            const int li = i == 0 ? last[0] : (i == 1 ? last[1] : (i == 2 ? last[2] : last[3]));
+            cv[j] = ok[j] ? gi + Sp[li * K + b] : -INFINITY;
+        }
+        const int keep = min(W, nc);
+        float ng[4] = {0.f, 0.f, 0.f, 0.f};
+        int nl[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            if (r >= keep) break;
+            // this lane's best remaining extension (the lowest j among equals)
+            float bs = -INFINITY;
+            int bj = -1;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (ok[j] && (bj < 0 || cv[j] > bs)) {
+                    bs = cv[j];
+                    bj = j;
+                }
+            const float M = wave_max_all(bs);
+            // the lowest c = j*64 + lane whose score is M: the lowest j first
+            int wj = 0, wl = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint64_t m = ballot(bj == j && bs == M);
+                if (m) {
+                    wj = j;
+                    wl = __ffsll(static_cast<unsigned long long>(m)) - 1;
+                    break;
+                }
+            }
+            const int wc = wj * kWave + wl;
+            const int wi = (wc >= K) + (wc >= 2 * K) + (wc >= 3 * K);
+            const int wb = wc - wi * K;
+            ng[r] = M;
+            nl[r] = wb;
+            if (l == 0) {
+                bp[(p * 4 + r) * 2] = static_cast<uint8_t>(wi);
+                bp[(p * 4 + r) * 2 + 1] = static_cast<uint8_t>(wb);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (j == wj && l == wl) ok[j] = false;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            g[r] = ng[r];
+            last[r] = nl[r];
+        }
+        nb = keep;
+    }
+    wave_lds_sync();
+    if (l == 0) {
+        int r = 0;
+        for (int p = B - 2; p >= 0; --p) {
+            chain[p + 1] = bp[(p * 4 + r) * 2 + 1];
+            r = bp[(p * 4 + r) * 2];
+        }
+        chain[0] = 0;
+    }
+    wave_lds_sync();
+    if (l < B) {
+        const int64_t s_ = static_cast<int64_t>(req) * B + l;
+        const int ch = chain[l];
+        if (choice) choice[s_] = ch;
+        tokens[s_] = ids[s_ * K + ch];
+    }
 }
 
 // The request's path from scores in LDS (every thread of the workgroup
 // calls it): the greedy walk uses the whole workgroup, the Global-Sum
 // dynamic program its first wave.
-__device__ __forceinline__ void path_from_lds(int rule, float lam, float* sS, const int32_t* __restrict__ ids, int req,
+__device__ __forceinline__ void path_from_lds(int rule, float lam, int beam, float* sS, const int32_t* __restrict__ ids, int req,
                                               int B, int K, int32_t* __restrict__ tokens,
                                               int32_t* __restrict__ choice) {
     uint8_t* aux = reinterpret_cast<uint8_t*>(reinterpret_cast<char*>(sS) + path_aux_offset(B, K, true));
     int* chain = reinterpret_cast<int*>(reinterpret_cast<char*>(sS) + path_chain_offset(B, K, true));
+    if (rule == kPathBeam) {
+        uint8_t* bp = reinterpret_cast<uint8_t*>(reinterpret_cast<char*>(sS) + path_beam_offset(B, K, true));
+        if ((threadIdx.x >> 6) == 0) beam_wave(sS, bp, chain, ids, req, B, K, beam, tokens, choice);
+        return;
+    }
     if (rule != kPathGreedy) {
         float* vb = reinterpret_cast<float*>(reinterpret_cast<char*>(sS) + path_vb_offset(B, K, true));
         if ((threadIdx.x >> 6) == 0)
@@ -202,7 +317,7 @@ __device__ __forceinline__ void path_from_lds(int rule, float lam, float* sS, co
 // scores fit (use_lds) they are first copied into LDS with coalesced 16-byte
 // loads, all issued before any is used.
 __global__ __launch_bounds__(64) void path_kernel(const float* __restrict__ scores, const int32_t* __restrict__ ids,
-                                                  int n, int B, int K, int rule, float lam,
+                                                  int n, int B, int K, int rule, float lam, int beam,
                                                   int32_t* __restrict__ tokens, int32_t* __restrict__ choice,
                                                   int use_lds) {
     extern __shared__ __attribute__((aligned(16))) float sl[];
@@ -231,7 +346,13 @@ __global__ __launch_bounds__(64) void path_kernel(const float* __restrict__ scor
             for (int64_t i = l; i < per; i += kWave) sl[i] = base[i];
         }
         wave_lds_sync();
-        path_from_lds(rule, lam, sl, ids, req, B, K, tokens, choice);
+        path_from_lds(rule, lam, beam, sl, ids, req, B, K, tokens, choice);
+        return;
+    }
+    if (rule == kPathBeam) {
+        int* chain = reinterpret_cast<int*>(reinterpret_cast<char*>(sl) + path_chain_offset(B, K, false));
+        uint8_t* bp = reinterpret_cast<uint8_t*>(reinterpret_cast<char*>(sl) + path_beam_offset(B, K, false));
+        beam_wave(base, bp, chain, ids, req, B, K, beam, tokens, choice);
         return;
     }
     if (rule != kPathGreedy) {
@@ -304,7 +425,7 @@ __global__ __launch_bounds__(1024) void cosine_kernel(CosArgs a, int use_lds) {
     }
     if (!a.tokens || !use_lds) return;
     __syncthreads();
-    path_from_lds(a.rule, a.lam, sS, a.ids, req, B, K, a.tokens, a.choice);
+    path_from_lds(a.rule, a.lam, a.beam, sS, a.ids, req, B, K, a.tokens, a.choice);
 }
 
 // One workgroup per request: S = l_{p+1}(b) + (sum of the hidden-block partial
@@ -379,7 +500,7 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a, int use_lds) 
     }
     if (!a.tokens || !use_lds) return;
     __syncthreads();
-    path_from_lds(a.rule, a.lam, sS, a.ids, req, B, K, a.tokens, a.choice);
+    path_from_lds(a.rule, a.lam, a.beam, sS, a.ids, req, B, K, a.tokens, a.choice);
 }
 
 // z = hi + lo for each node row of the [hi | lo] layout.
@@ -426,12 +547,12 @@ hipError_t launch_cosine(const CosArgs& a, hipStream_t stream) {
                   a, lds > 0);
 }
 
-hipError_t launch_path(const float* scores, const int32_t* ids, int n, int B, int K, int rule, float lam,
+hipError_t launch_path(const float* scores, const int32_t* ids, int n, int B, int K, int rule, float lam, int beam,
                        int32_t* tokens, int32_t* choice, hipStream_t stream) {
     const size_t wl = path_lds_bytes(B, K);
     const size_t lds = wl ? wl : path_lds_end(B, K, false);
     return launch(path_kernel, dim3(static_cast<unsigned>(n)), 64, static_cast<uint32_t>(lds), stream, scores,
-                  ids, n, B, K, rule, lam, tokens, choice, wl > 0);
+                  ids, n, B, K, rule, lam, beam, tokens, choice, wl > 0);
 }
 
 hipError_t launch_finish(const FinishArgs& a, hipStream_t stream) {

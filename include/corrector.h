@@ -87,8 +87,15 @@ enum { CORR_DTYPE_BF16 = 0, CORR_DTYPE_F32 = 1 };
  *                         The DCOCO page compares a Geometric rule with
  *                         lambda = 0.75 against the walk (path-rule table) but
  *                         gives no formula; this discounted sum is the
- *                         reading implemented. */
-enum { CORR_PATH_GREEDY = 0, CORR_PATH_GLOBAL_SUM = 1, CORR_PATH_GEOMETRIC = 2 };
+ *                         reading implemented;
+ *   CORR_PATH_BEAM        beam search of width beam_width over the summed
+ *                         score (the DCOCO page's critique suggests widening
+ *                         the walk into a beam of 2-4): each step keeps the
+ *                         beam_width best extensions g + S_p(last, b), summed
+ *                         in float32, ordered by score, then beam index,
+ *                         then b; the answer is the best final path.  Width 1
+ *                         is the walk. */
+enum { CORR_PATH_GREEDY = 0, CORR_PATH_GLOBAL_SUM = 1, CORR_PATH_GEOMETRIC = 2, CORR_PATH_BEAM = 3 };
 
 /* Shapes and options fixed at create time.
  *   vocab        V, 1 <= K <= V < 2^31.
@@ -105,10 +112,12 @@ enum { CORR_PATH_GREEDY = 0, CORR_PATH_GLOBAL_SUM = 1, CORR_PATH_GEOMETRIC = 2 }
  *   ln_eps       LayerNorm epsilon (> 0).
  *   sigma        cosine scale (cosine only).
  *   path_rule    CORR_PATH_GREEDY (0, the default of a zeroed struct),
- *                CORR_PATH_GLOBAL_SUM or CORR_PATH_GEOMETRIC; used by
+ *                CORR_PATH_GLOBAL_SUM, CORR_PATH_GEOMETRIC or CORR_PATH_BEAM; used by
  *                corrector_walk and corrector_run.
  *   path_lambda  lambda of CORR_PATH_GEOMETRIC, 0 < lambda <= 1 (otherwise
- *                CORR_E_SHAPE); ignored by the other rules. */
+ *                CORR_E_SHAPE); ignored by the other rules.
+ *   beam_width   width of CORR_PATH_BEAM, 1..4 (otherwise CORR_E_SHAPE);
+ *                ignored by the other rules. */
 typedef struct {
     int64_t vocab;
     int32_t slots;
@@ -125,6 +134,7 @@ typedef struct {
     float sigma;
     int32_t path_rule;
     float path_lambda;
+    int32_t beam_width;
 } corrector_desc;
 
 /* Borrowed device pointers to the weights; the caller keeps them alive and

@@ -187,6 +187,17 @@ def path_scores(S, choice, lam: float = 1.0):
     return (S[i, p, choice[:, :-1], choice[:, 1:]] * lam ** np.arange(P)[None, :]).sum(axis=1)
 
 
+def check_beam(gpu: dict, cfg: dict, where: str = ""):
+    """The beam-search path: the oracle's beam search run on the GPU's own
+    float32 scores must give the same choices and tokens (both sides rank the
+    same float32 sums)."""
+    n, B = gpu["choice"].shape
+    desc = oracle.OracleDesc.from_config(cfg)
+    t, c, _ = oracle.beam(desc, gpu["scores"], gpu["ids"], n, cfg.get("beam_width", 4))
+    np.testing.assert_array_equal(gpu["choice"], c, err_msg="beam path " + where)
+    np.testing.assert_array_equal(gpu["tokens"], t, err_msg="beam tokens " + where)
+
+
 def check_global_sum(gpu: dict, ora: dict, cfg: dict, where: str = "", exact: bool = False, lam: float = 1.0):
     """Gates of the Global-Sum path (best summed score, slot 1 at rank 0), or
     with lam < 1 of the Geometric path (pair p weighted by lam**p; the sums

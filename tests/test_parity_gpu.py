@@ -108,7 +108,7 @@ def test_workspace_reuse_across_calls():
 
 # ------------------------------------------------------ Global-Sum path --
 
-@pytest.mark.parametrize("rule", ["global_sum", "geometric"])
+@pytest.mark.parametrize("rule", ["global_sum", "geometric", "beam"])
 @pytest.mark.parametrize("name,head", [("tiny", "normal"), ("tiny", "zero"), ("tiny", "stress"), ("b1", "stress"),
                                        ("b1", "zero"), ("b32", "stress"), ("cosine", "normal")])
 def test_global_sum_path(name, head, rule):
@@ -117,12 +117,17 @@ def test_global_sum_path(name, head, rule):
     as the walk configuration, a path that is optimal for them."""
     _log("%s %s head=%s" % (rule, name, head))
     lam = 0.75 if rule == "geometric" else 1.0
-    x = P.inputs(name, head=head, path_rule=rule, path_lambda=lam)
+    x = P.inputs(name, head=head, path_rule=rule, path_lambda=lam, beam_width=3)
     n = 4 if name == "cosine" else None   # the cosine oracle on a sample of requests
     gpu = P.gpu_run(x, n=n)
     ora = P.oracle_run(x, n=n)
     P.check_topk(gpu, ora, name)
     P.check_scores(gpu, ora, name)
+    if rule == "beam":
+        P.check_beam(gpu, x["cfg"], "%s/%s" % (name, head))
+        if head == "zero":
+            assert (gpu["choice"] == 0).all()
+        return
     near = P.check_global_sum(gpu, ora, x["cfg"], "%s/%s/%s" % (rule, name, head), exact=(head == "zero"), lam=lam)
     if head == "zero":
         assert (gpu["choice"] == 0).all()

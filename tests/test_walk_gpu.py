@@ -1,5 +1,6 @@
 """corrector_walk on caller-supplied scores, on the GPU, against the oracle,
 for every path rule: the prefix-first walk (DCOCO method details step (5))
+and the beam search (widths 1, 2, 4; float32 extension sums on both sides)
 exactly, and the Global-Sum (LiLiCorr appendix E, Eq. 12) and Geometric
 (lambda = 0.75, a discounted sum) paths as optimal for the scores given.
 
@@ -19,13 +20,15 @@ from workload import config, gen_weights
 
 pytestmark = pytest.mark.gpu
 
-LAM = {"greedy": 1.0, "global_sum": 1.0, "geometric": 0.75}
+LAM = {"greedy": 1.0, "global_sum": 1.0, "geometric": 0.75, "beam1": 1.0, "beam2": 1.0, "beam4": 1.0}
 
 
 def _walk(S, ids, rule):
     n, Bm1, K, _ = S.shape
     B = Bm1 + 1
-    cfg = config("tiny", B=B, K=K, V=max(1000, K), n=n, path_rule=rule, path_lambda=LAM[rule])
+    width = int(rule[4:]) if rule.startswith("beam") else 4
+    cfg = config("tiny", B=B, K=K, V=max(1000, K), n=n, path_rule="beam" if rule.startswith("beam") else rule,
+                 path_lambda=LAM[rule], beam_width=width)
     emb = np.zeros((cfg["V"], cfg["de"]), np.uint16)
     corr = device.make_corrector(cfg, dict(weights=device.weights_to_device(gen_weights(cfg), emb)), max_requests=n)
     tokens = torch.empty((n, B), dtype=torch.int32, device="cuda")
@@ -53,6 +56,11 @@ def _check(S, ids, rule, where, ties=False):
     np.testing.assert_array_equal(tokens, np.take_along_axis(ids, choice[:, :, None], 2)[:, :, 0],
                                   err_msg="tokens follow the choices " + where)
     assert (choice[:, 0] == 0).all()
+    if rule.startswith("beam"):
+        want_t, want_c, _ = oracle.beam(desc, S.astype(np.float32), ids, n, int(rule[4:]))
+        np.testing.assert_array_equal(choice, want_c, err_msg="beam " + where)
+        np.testing.assert_array_equal(tokens, want_t, err_msg="beam tokens " + where)
+        return
     if rule == "greedy":
         want_t, want_c = oracle.walk(desc, S64, ids, n)
         np.testing.assert_array_equal(choice, want_c, err_msg="walk " + where)
@@ -76,7 +84,7 @@ def _check(S, ids, rule, where, ties=False):
         assert same.mean() >= 0.6, "%s: %d of %d paths differ" % (where, (~same).sum(), n)
 
 
-@pytest.mark.parametrize("rule", ["greedy", "global_sum", "geometric"])
+@pytest.mark.parametrize("rule", ["greedy", "global_sum", "geometric", "beam1", "beam2", "beam4"])
 @pytest.mark.parametrize("B,K", [(15, 16), (15, 37), (5, 1), (1, 8), (2, 64), (64, 64)])
 def test_walk_rules(rule, B, K):
     print("walk %s B=%d K=%d" % (rule, B, K), flush=True)
