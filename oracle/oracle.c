@@ -59,6 +59,7 @@ typedef struct {
     int64_t V;
     int32_t B, K, d, de, r, h, dvec, variant, logits_dtype;
     double eps, sigma;
+    int32_t top_m;   /* successors scored per predecessor (0: all K) */
 } oracle_desc;
 
 /* Matrices are bfloat16 bit patterns, row-major [out][in]; vectors are float32. */
@@ -349,6 +350,12 @@ int oracle_score(const oracle_desc *D, const oracle_weights *W, int32_t n,
     const int B = D->B, K = D->K, r = D->r, h = D->h, dv = D->dvec;
     if (D->variant == ORA_MLP && !s) return ORA_E_ARG;
     const int nin = 3 * r + 2;
+    /* Top-m successor sparsification (the DCOCO page's critique, weakness 3:
+     * keep only the top-m successors of each predecessor, O(B K m) instead of
+     * O(B K^2)).  The successors kept are the first m of the next slot's
+     * top-K, i.e. ranked by the drafter; the others are not scored and get
+     * S = Delta = -inf, so no path rule can choose them. */
+    const int mk = (D->top_m > 0 && D->top_m < K) ? D->top_m : K;
     int err = ORA_OK;
 #pragma omp parallel for schedule(dynamic) reduction(| : err)
     for (int64_t t = 0; t < (int64_t)n * (B - 1); ++t) {
@@ -384,6 +391,12 @@ int oracle_score(const oracle_desc *D, const oracle_weights *W, int32_t n,
         for (int a = 0; a < K; ++a) {
             for (int b = 0; b < K; ++b) {
                 double delta;
+                if (b >= mk) {
+                    size_t o = (((size_t)i * (B - 1) + p) * K + a) * K + b;
+                    if (delta_out) delta_out[o] = -INFINITY;
+                    if (scores_out) scores_out[o] = -INFINITY;
+                    continue;
+                }
                 if (D->variant == ORA_MLP) {
                     const double *sp = s + ((size_t)i * (B - 1) + p) * r;
                     for (int j = 0; j < r; ++j) x[j] = sp[j];

@@ -34,7 +34,7 @@ class _Desc(C.Structure):
     _fields_ = [("V", C.c_int64), ("B", C.c_int32), ("K", C.c_int32), ("d", C.c_int32),
                 ("de", C.c_int32), ("r", C.c_int32), ("h", C.c_int32), ("dvec", C.c_int32),
                 ("variant", C.c_int32), ("logits_dtype", C.c_int32),
-                ("eps", C.c_double), ("sigma", C.c_double)]
+                ("eps", C.c_double), ("sigma", C.c_double), ("top_m", C.c_int32)]
 
 
 class _Weights(C.Structure):
@@ -94,17 +94,19 @@ class OracleDesc:
     logits_dtype: str = "bf16"
     eps: float = 1e-5
     sigma: float = 1.0
+    top_m: int = 0
 
     @classmethod
     def from_config(cls, cfg: dict) -> "OracleDesc":
         return cls(V=cfg["V"], B=cfg["B"], K=cfg["K"], d=cfg["d"], de=cfg["de"], r=cfg["r"],
                    h=cfg["h"], dvec=cfg["dvec"], variant=cfg["variant"],
-                   logits_dtype=cfg["logits_dtype"], eps=cfg["ln_eps"], sigma=cfg["sigma"])
+                   logits_dtype=cfg["logits_dtype"], eps=cfg["ln_eps"], sigma=cfg["sigma"],
+                   top_m=cfg.get("succ_top_m", 0))
 
     def c(self) -> _Desc:
         return _Desc(self.V, self.B, self.K, self.d, self.de, self.r, self.h, self.dvec,
                      0 if self.variant == "mlp" else 1,
-                     0 if self.logits_dtype == "bf16" else 1, self.eps, self.sigma)
+                     0 if self.logits_dtype == "bf16" else 1, self.eps, self.sigma, self.top_m)
 
 
 class _Keep:

@@ -526,6 +526,35 @@ def test_beam_tie_order_and_float32_sums():
     assert t[0] == np.float32(1.0)
 
 
+# ---------------------------------------- top-m successor sparsification --
+# The critique on the DCOCO page (weakness 3) proposes scoring only the top-m
+# successors of each predecessor (O(BKm) instead of O(BK^2)); read as the
+# first m of the next slot's top-K (the drafter's ranking).
+
+@pytest.mark.parametrize("variant", ["mlp", "cosine"])
+def test_top_m_keeps_the_first_m_successors(variant):
+    x = gen_inputs(config("tiny", K=6, variant=variant), head="stress")
+    dense = oracle.run(x["cfg"], x)
+    for m in (0, 6, 9):   # 0 and m >= K: every successor
+        got = oracle.run(dict(x["cfg"], succ_top_m=m), x)
+        np.testing.assert_array_equal(got["scores"], dense["scores"])
+    for m in (1, 2, 5):
+        got = oracle.run(dict(x["cfg"], succ_top_m=m), x)
+        S, D = got["scores"], got["delta"]
+        np.testing.assert_array_equal(S[..., :m], dense["scores"][..., :m])
+        np.testing.assert_array_equal(D[..., :m], dense["delta"][..., :m])
+        assert np.isneginf(S[..., m:]).all() and np.isneginf(D[..., m:]).all()
+        assert np.isfinite(S).sum() == S.shape[0] * S.shape[1] * 6 * m
+        # no path rule can choose a dropped successor
+        desc = oracle.OracleDesc.from_config(dict(x["cfg"], succ_top_m=m))
+        n = x["cfg"]["n"]
+        _, walk_c = oracle.walk(desc, S, got["ids"], n)
+        _, vit_c, _ = oracle.viterbi(desc, S, got["ids"], n)
+        _, beam_c, _ = oracle.beam(desc, S.astype(np.float32), got["ids"], n, 3)
+        for c in (walk_c, vit_c, beam_c):
+            assert (c[:, 1:] < m).all()
+
+
 # ------------------------------------------- vocabulary normalisation --
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
