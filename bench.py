@@ -91,11 +91,13 @@ def algorithmic_work(cfg: dict, n: int) -> dict:
                      per_unit=r * 8 + uvb, units=rows * K, unit="candidate (u in; z and U|V out)")
     w["finish"] = w["finish_walk"] = w["finish_viterbi"] = w["finish_beam"] = dict(bound="hbm", bytes=n * (B - 1) * K * K * 4 * 2,
                                           per_unit=(B - 1) * K * K * 8, units=n, unit="block")
-    # the transition MLP epilogue is bound by the vector ALU: K^2 h GELU
-    # evaluations per pair (13 VALU instructions each, 2 of them quarter-rate
-    # transcendentals) against 256 CUs x 64 lanes x 2.4 GHz
-    w["mlp"] = dict(bound="alu", gelu=pairs * K * K * h, flops=2 * pairs * K * K * h,
-                    per_unit=h, units=pairs * K * K, unit="transition (h GELU evaluations)")
+    # the transition MLP epilogue is bound by the vector ALU: K m h GELU
+    # evaluations per pair (m = K unless sparsified; 13 VALU issue slots each)
+    # against 256 CUs x 64 lanes x 2.4 GHz
+    ms = cfg.get("succ_top_m", 0)
+    ms = ms if 0 < ms < K else K   # successors scored per predecessor
+    w["mlp"] = dict(bound="alu", gelu=pairs * K * ms * h, flops=2 * pairs * K * ms * h,
+                    per_unit=h, units=pairs * K * ms, unit="transition (h GELU evaluations)")
     w["cosine"] = w["cosine_walk"] = w["cosine_viterbi"] = w["cosine_beam"] = dict(
         bound="hbm", bytes=pairs * 2 * K * cfg["dvec"] * 4, per_unit=2 * K * cfg["dvec"] * 4, units=pairs, unit="pair")
     w["walk"] = dict(bound="hbm", bytes=n * (B - 1) * K * 4, per_unit=(B - 1) * K * 4, units=n,
@@ -247,6 +249,8 @@ def main():
                     help="how the path through the candidate lattice is chosen")
     ap.add_argument("--path-lambda", type=float, default=0.75, help="lambda of the Geometric path rule")
     ap.add_argument("--beam-width", type=int, default=4, help="width of the beam path rule (1..4)")
+    ap.add_argument("--top-m", type=int, default=0,
+                    help="score only the first m successors of each predecessor (0: all K)")
     ap.add_argument("--no-fold", action="store_true", help="skip the folded-table measurement")
     ap.add_argument("--ceilings", action="store_true",
                     help="also measure the box's copy and large-GEMM ceilings (reference figures)")
@@ -266,7 +270,8 @@ def main():
     from workload import config
     from workload.gen import gen_embed, gen_hidden, gen_logits, gen_weights
 
-    cfg = config(args.workload, path_rule=args.path_rule, path_lambda=args.path_lambda, beam_width=args.beam_width)
+    cfg = config(args.workload, path_rule=args.path_rule, path_lambda=args.path_lambda, beam_width=args.beam_width,
+                 succ_top_m=args.top_m)
     n = cfg["n"]
     log("generating %s inputs (%d copies)" % (args.workload, args.copies))
     t0 = time.perf_counter()
@@ -425,7 +430,8 @@ def main():
                                                       cfg["r"], 3 * cfg["r"] + 2, cfg["h"], cfg["variant"])
                                + {"greedy": "", "global_sum": ", Global-Sum path",
                                   "geometric": ", Geometric path (lambda %g)" % args.path_lambda,
-                                  "beam": ", beam path (width %d)" % args.beam_width}[args.path_rule],
+                                  "beam": ", beam path (width %d)" % args.beam_width}[args.path_rule]
+                               + (", top-%d successors scored" % args.top_m if 0 < args.top_m < cfg["K"] else ""),
                    "global_batch": n, "rotating_input_sets": args.copies},
         "roofline": roof,
         "kernels": kernels,

@@ -35,7 +35,7 @@ class CorrectorDesc(C.Structure):
                 ("mlp_hidden", C.c_int32), ("d_vec", C.c_int32), ("variant", C.c_int32),
                 ("logits_dtype", C.c_int32), ("max_requests", C.c_int32),
                 ("ln_eps", C.c_float), ("sigma", C.c_float), ("path_rule", C.c_int32),
-                ("path_lambda", C.c_float), ("beam_width", C.c_int32)]
+                ("path_lambda", C.c_float), ("beam_width", C.c_int32), ("succ_top_m", C.c_int32)]
 
 PATH_RULES = {"greedy": 0, "global_sum": 1, "geometric": 2, "beam": 3}
 
@@ -120,7 +120,7 @@ def make_desc(cfg: dict, max_requests: int) -> CorrectorDesc:
                          cfg.get("h", 0), cfg.get("dvec", 0), VARIANTS[cfg["variant"]],
                          DTYPES[cfg["logits_dtype"]], max_requests, cfg.get("ln_eps", 1e-5),
                          cfg.get("sigma", 1.0), PATH_RULES[cfg.get("path_rule", "greedy")],
-                         cfg.get("path_lambda", 0.75), cfg.get("beam_width", 4))
+                         cfg.get("path_lambda", 0.75), cfg.get("beam_width", 4), cfg.get("succ_top_m", 0))
 
 
 class Corrector:

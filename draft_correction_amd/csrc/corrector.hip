@@ -66,6 +66,9 @@ int choose_splits(const corrector_desc& d) {
     if (s > kMaxSplits) s = kMaxSplits;
     return s < 1 ? 1 : s;
 }
+// Successors scored per predecessor: the first m of the next slot's top-K.
+int succ_m(const corrector_desc& d) { return d.succ_top_m > 0 && d.succ_top_m < d.k ? d.succ_top_m : d.k; }
+
 int choose_usplits(const corrector_desc& d) {
     int s = d.d_embed / 1024;
     if (s > kMaxUSplits) s = kMaxUSplits;
@@ -323,6 +326,7 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
         c.K = d.k;
         c.dvec = d.d_vec;
         c.sigma = d.sigma;
+        c.m = succ_m(d);
         c.scores = scores;
         // the path runs inside the cosine launch when the scores fit its LDS
         const bool fused = tokens && path_fits_lds(d.slots, d.k);
@@ -352,10 +356,12 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
         m.b1 = w.b1;
         m.w2 = w.w2;
         m.part = at<float>(ws, L.mlp_part);
+        m.m = succ_m(d);
         q("mlp", [&] { return launch_mlp(m, q.s); });
         FinishArgs f{};
         f.part = m.part;
         f.nblk = mlp_blocks(d.mlp_hidden);
+        f.m = succ_m(d);
         f.vals = vals;
         f.b2 = w.b2;
         f.n = n;
@@ -395,6 +401,7 @@ int corrector_create(const corrector_desc* desc, const corrector_weights* wt, co
         return CORR_E_UNSUPPORTED;
     if (d.path_rule == CORR_PATH_GEOMETRIC && !(d.path_lambda > 0.f && d.path_lambda <= 1.f)) return CORR_E_SHAPE;
     if (d.path_rule == CORR_PATH_BEAM && (d.beam_width < 1 || d.beam_width > 4)) return CORR_E_SHAPE;
+    if (d.succ_top_m < 0 || d.succ_top_m > d.k) return CORR_E_SHAPE;
     if (d.vocab < 1 || d.vocab > 0x7FFFFFFF) return CORR_E_SHAPE;
     if (d.slots < 1 || d.slots > 64) return CORR_E_SHAPE;  // the walk keeps one slot per lane
     if (d.k < 1 || d.k > 64 || d.k > d.vocab) return CORR_E_SHAPE;

@@ -157,6 +157,7 @@ struct MlpArgs {
     const float* b1;
     const float* w2;
     float* part;            // [n*(B-1)][blocks][K][K] partial Delta per hidden-unit block
+    int m;                  // successors scored per predecessor (b < m; 1..K)
 };
 // Most hidden-unit blocks of the MLP (h <= 256 units in blocks of 64).
 constexpr int kMaxMlpBlocks = 4;
@@ -168,6 +169,7 @@ hipError_t launch_mlp(const MlpArgs& a, hipStream_t stream);
 struct FinishArgs {
     const float* part;
     int nblk;
+    int m;                  // successors scored (b < m); S = -inf for the others
     const float* vals;
     const float* b2;
     int n;
@@ -192,6 +194,7 @@ struct CosArgs {
     int K;
     int dvec;
     float sigma;
+    int m;                  // successors scored (b < m); S = -inf for the others
     float* scores;
     // with tokens given (only when path_fits_lds), the request's path by
     // `rule` follows in the same launch

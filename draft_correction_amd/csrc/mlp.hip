@@ -57,8 +57,9 @@ static_assert(256 / kJB <= kMaxMlpBlocks, "the finishing kernel sums at most kMa
 //   P[a][j] = c_p[j] + b1[j] + w_la[j] l_p(a) + U_p[a][j]
 //   Q[b][j] = w_lb[j] l_{p+1}(b) + V_{p+1}[b][j]
 // from the per-candidate products U | V and the pair's c_p (formed here from
-// s_p), then GELU and the dot with w2 over all K^2
-// candidate pairs, one (a, b) per thread; the block's partial Delta goes to
+// s_p), then GELU and the dot with w2 over the K x m
+// candidate pairs (successors b < m; m = K unless sparsified), one (a, b) per
+// thread; the block's partial Delta goes to
 // part[pair][block][a][b].
 __global__ __launch_bounds__(256) void mlp_kernel(MlpArgs a) {
     const int tid = threadIdx.x;
@@ -180,11 +181,13 @@ __global__ __launch_bounds__(256) void mlp_kernel(MlpArgs a) {
     __syncthreads();
 
     // ---- GELU and the dot with w2, one (a, b) per thread
-    const int nidx = K * K;
-    float* out = a.part + static_cast<int64_t>(item) * nidx;
+    const int ms = a.m;
+    const int nidx = K * ms;
+    float* out = a.part + static_cast<int64_t>(item) * K * K;
     for (int idx = tid; idx < nidx; idx += 256) {
-        const float* pr = P + (idx / K) * PS;
-        const float* qr = Q + (idx % K) * PS;
+        const int aa = idx / ms, bb = idx - aa * ms;
+        const float* pr = P + aa * PS;
+        const float* qr = Q + bb * PS;
         float d0 = 0.f, d1 = 0.f;
         for (int j = 0; j < jn; j += 8) {
             const float4 pv0 = *reinterpret_cast<const float4*>(pr + j);
@@ -202,7 +205,7 @@ __global__ __launch_bounds__(256) void mlp_kernel(MlpArgs a) {
             d0 = fmaf(wv1.z, gelu_scaled(pv1.z + qv1.z), d0);
             d1 = fmaf(wv1.w, gelu_scaled(pv1.w + qv1.w), d1);
         }
-        out[idx] = d0 + d1;
+        out[aa * K + bb] = d0 + d1;
     }
 }
 

@@ -416,7 +416,7 @@ __global__ __launch_bounds__(1024) void cosine_kernel(CosArgs a, int use_lds) {
             for (int i = 0; i < 4; ++i) {
                 const int aa = ta * 16 + 4 * g + i;
                 if (aa < K) {
-                    const float sv = lb + a.sigma * acc[i];
+                    const float sv = bb < a.m ? lb + a.sigma * acc[i] : -INFINITY;
                     srow[aa * K + bb] = sv;
                     if (use_lds) sS[p * KK + aa * K + bb] = sv;
                 }
@@ -470,8 +470,11 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a, int use_lds) 
             for (int u = 0; u < 4; ++u) {
                 const int i4 = i0 + u * 256 + static_cast<int>(threadIdx.x);
                 if (i4 < per4) {
-                    const float4 sv = make_float4(lv[u].x + (d[u].x + b2), lv[u].y + (d[u].y + b2),
-                                                  lv[u].z + (d[u].z + b2), lv[u].w + (d[u].w + b2));
+                    const int b0 = (i4 * 4) % K;   // successor of the first element (K % 4 == 0)
+                    const float4 sv = make_float4(b0 < a.m ? lv[u].x + (d[u].x + b2) : -INFINITY,
+                                                  b0 + 1 < a.m ? lv[u].y + (d[u].y + b2) : -INFINITY,
+                                                  b0 + 2 < a.m ? lv[u].z + (d[u].z + b2) : -INFINITY,
+                                                  b0 + 3 < a.m ? lv[u].w + (d[u].w + b2) : -INFINITY);
                     reinterpret_cast<float4*>(scores_req)[i4] = sv;
                     if (use_lds) reinterpret_cast<float4*>(sS)[i4] = sv;
                 }
@@ -492,7 +495,7 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a, int use_lds) 
         for (int u = 0; u < 8; ++u) {
             const int idx = i0 + u * 256 + static_cast<int>(threadIdx.x);
             if (idx < per32) {
-                const float sv = lv[u] + (d[u] + b2);
+                const float sv = idx % K < a.m ? lv[u] + (d[u] + b2) : -INFINITY;
                 scores_req[idx] = sv;
                 if (use_lds) sS[idx] = sv;
             }

@@ -117,7 +117,13 @@ enum { CORR_PATH_GREEDY = 0, CORR_PATH_GLOBAL_SUM = 1, CORR_PATH_GEOMETRIC = 2, 
  *   path_lambda  lambda of CORR_PATH_GEOMETRIC, 0 < lambda <= 1 (otherwise
  *                CORR_E_SHAPE); ignored by the other rules.
  *   beam_width   width of CORR_PATH_BEAM, 1..4 (otherwise CORR_E_SHAPE);
- *                ignored by the other rules. */
+ *                ignored by the other rules.
+ *   succ_top_m   successors scored per predecessor: 0 (or K) scores all K;
+ *                1 <= m < K scores only the first m candidates of the next
+ *                slot (the drafter's top-m) and writes S = -inf for the
+ *                others, cutting the transition MLP to K*m evaluations per
+ *                pair (the DCOCO page's critique, weakness 3).  Outside
+ *                0..K: CORR_E_SHAPE. */
 typedef struct {
     int64_t vocab;
     int32_t slots;
@@ -135,6 +141,7 @@ typedef struct {
     int32_t path_rule;
     float path_lambda;
     int32_t beam_width;
+    int32_t succ_top_m;
 } corrector_desc;
 
 /* Borrowed device pointers to the weights; the caller keeps them alive and

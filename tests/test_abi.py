@@ -41,7 +41,7 @@ def test_exports_every_declared_call(lib):
 def _desc(**kw):
     base = dict(vocab=151936, slots=15, k=16, d_hidden=4096, d_embed=4096, r=128, mlp_hidden=256,
                 d_vec=128, variant=0, logits_dtype=0, max_requests=32, ln_eps=1e-5, sigma=1.0,
-                path_rule=0, path_lambda=0.75, beam_width=4)
+                path_rule=0, path_lambda=0.75, beam_width=4, succ_top_m=0)
     base.update(kw)
     return corr.CorrectorDesc(*[base[f] for f, _ in corr.CorrectorDesc._fields_])
 
@@ -73,7 +73,7 @@ def test_create_and_workspace(lib):
     ("vocab", 0, 2), ("k", 0, 2), ("k", 65, 2), ("slots", 0, 2), ("d_hidden", 100, 2),
     ("d_embed", 0, 2), ("r", 96, 3), ("mlp_hidden", 8, 3), ("mlp_hidden", 512, 3),
     ("variant", 2, 3), ("logits_dtype", 5, 3), ("max_requests", 0, 2), ("ln_eps", 0.0, 2),
-    ("path_rule", 4, 3), ("path_rule", -1, 3),
+    ("path_rule", 4, 3), ("path_rule", -1, 3), ("succ_top_m", -1, 2), ("succ_top_m", 17, 2),
 ])
 def test_create_rejects_bad_desc(lib, field, value, code):
     rc, h = _create(lib, _desc(**{field: value}), _weights())

@@ -134,6 +134,27 @@ def test_global_sum_path(name, head, rule):
     _log("  near-tie paths: %d" % near)
 
 
+# ------------------------------------------- top-m successor sparsification --
+
+@pytest.mark.parametrize("name,head,m", [("tiny", "stress", 2), ("b1", "stress", 8), ("b32", "normal", 8),
+                                         ("b32", "stress", 4), ("cosine", "normal", 8)])
+def test_top_m_successors(name, head, m):
+    """Only the first m successors of each pair are scored (the rest are -inf);
+    the kept scores pass the usual gates and the walk never leaves them."""
+    _log("top-m %s head=%s m=%d" % (name, head, m))
+    x = P.inputs(name, head=head, succ_top_m=m)
+    n = 4 if name == "cosine" else None
+    gpu = P.gpu_run(x, n=n)
+    ora = P.oracle_run(x, n=n)
+    P.check_topk(gpu, ora, name)
+    assert np.isneginf(gpu["scores"][..., m:]).all()
+    kept_g = dict(gpu, scores=gpu["scores"][..., :m], vals=gpu["vals"][..., :m])
+    kept_o = dict(ora, scores=ora["scores"][..., :m], delta=ora["delta"][..., :m])
+    P.check_scores(kept_g, kept_o, "%s/m=%d" % (name, m))
+    P.check_walk(gpu, ora, "%s/m=%d" % (name, m))
+    assert (gpu["choice"][:, 1:] < m).all()
+
+
 # ---------------------------------------------------------------- cosine --
 
 @pytest.mark.parametrize("sigma", [1.0, 8.0])
