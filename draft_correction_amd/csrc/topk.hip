@@ -487,9 +487,11 @@ __device__ __forceinline__ void select_chunk(const u32x4 (&raw)[kNV], uint32_t l
     part[obase + slot] = slot < outn ? outb[slot] : 0ull;
 }
 
-// One wave per chunk.  The full chunks (all but a row's shorter last one) are
-// numbered f = row * full + chunk and come first; the rows' shorter last
-// chunks follow.  Each chunk's result slot is fixed by its (row, chunk).
+// One wave per chunk.  The rows' shorter last chunks (when V is not a multiple
+// of the chunk) come first: their loads take the slower ragged path, which
+// then overlaps the other chunks instead of lengthening the kernel's tail.
+// The full chunks follow, numbered f = row * full + chunk.  Each chunk's
+// result slot is fixed by its (row, chunk).
 // kLse: also write the chunk's normaliser pair to lse_part[row * chunks + chunk].
 // Workgroups hold four waves, or one with kLse: that form needs more registers
 // (fewer waves per SIMD), and single-wave workgroups free their slots as soon
@@ -513,14 +515,16 @@ __global__ __launch_bounds__(64 * partial_waves_per_block<kLse>()) void topk_par
     const uint32_t nrows = static_cast<uint32_t>(rows);
     const bool ragged = V % kChunk != 0;
     const uint32_t full = ragged ? uch - 1u : uch;  // full chunks per row
-    const uint32_t nfull = nrows * full;
+    const uint32_t nrag = ragged ? nrows : 0u;      // shorter last chunks, one per row
     if (w >= nrows * uch) return;  // whole wave; this kernel has no block barrier
     Chunk c;
-    if (w < nfull) {
-        c.row = w / full;
-        c.chunk = w - c.row * full;
+    const bool isfull = w >= nrag;
+    if (isfull) {
+        const uint32_t f = w - nrag;
+        c.row = f / full;
+        c.chunk = f - c.row * full;
     } else {
-        c.row = w - nfull;
+        c.row = w;
         c.chunk = uch - 1u;
     }
     const uint32_t req = c.row / uB, slot = c.row - req * uB;
@@ -528,13 +532,13 @@ __global__ __launch_bounds__(64 * partial_waves_per_block<kLse>()) void topk_par
     c.src = logits + req * req_stride + slot * slot_stride + c0;
     c.nvalid = static_cast<int>(min(static_cast<int64_t>(kChunk), V - c0));
     u32x4 raw[kNV];
-    if (w < nfull)
+    if (isfull)
         load_full_chunk(raw, c.src);
     else
         load_ragged_chunk(raw, c);
     const uint32_t lane_key = lane_key_bf16(raw);
     if (kLse) {
-        const float2 ls = w < nfull ? lane_expsum_bf16<false>(raw, lane_key) : lane_expsum_bf16<true>(raw, lane_key);
+        const float2 ls = isfull ? lane_expsum_bf16<false>(raw, lane_key) : lane_expsum_bf16<true>(raw, lane_key);
         const float2 cs = chunk_expsum(ls.x, ls.y);
         if (lane_id() == 0) lse_part[static_cast<int64_t>(c.row) * uch + c.chunk] = cs;
     }
