@@ -449,6 +449,7 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a, int use_lds) 
         const int per4 = per32 / 4;
         for (int i0 = 0; i0 < per4; i0 += 4 * 256) {
             float4 d[4], lv[4];
+            int bq[4];   // successor of each float4's first element
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int i4 = min(i0 + u * 256 + static_cast<int>(threadIdx.x), per4 - 1);  // clamped: in bounds
@@ -464,17 +465,20 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a, int use_lds) 
                 for (int b = 1; b < kMaxMlpBlocks; ++b)
                     if (b < a.nblk) acc = make_float4(acc.x + t[b].x, acc.y + t[b].y, acc.z + t[b].z, acc.w + t[b].w);
                 d[u] = acc;
-                lv[u] = *reinterpret_cast<const float4*>(vals_req + (p + 1) * K + e % K);
+                bq[u] = e % K;
+                lv[u] = *reinterpret_cast<const float4*>(vals_req + (p + 1) * K + bq[u]);
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int i4 = i0 + u * 256 + static_cast<int>(threadIdx.x);
                 if (i4 < per4) {
-                    const int b0 = (i4 * 4) % K;   // successor of the first element (K % 4 == 0)
-                    const float4 sv = make_float4(b0 < a.m ? lv[u].x + (d[u].x + b2) : -INFINITY,
-                                                  b0 + 1 < a.m ? lv[u].y + (d[u].y + b2) : -INFINITY,
-                                                  b0 + 2 < a.m ? lv[u].z + (d[u].z + b2) : -INFINITY,
-                                                  b0 + 3 < a.m ? lv[u].w + (d[u].w + b2) : -INFINITY);
+                    float4 sv = make_float4(lv[u].x + (d[u].x + b2), lv[u].y + (d[u].y + b2),
+                                            lv[u].z + (d[u].z + b2), lv[u].w + (d[u].w + b2));
+                    if (a.m < K) {   // successors b >= m are not scored (K % 4 == 0 here)
+                        const int b0 = bq[u];
+                        sv = make_float4(b0 < a.m ? sv.x : -INFINITY, b0 + 1 < a.m ? sv.y : -INFINITY,
+                                         b0 + 2 < a.m ? sv.z : -INFINITY, b0 + 3 < a.m ? sv.w : -INFINITY);
+                    }
                     reinterpret_cast<float4*>(scores_req)[i4] = sv;
                     if (use_lds) reinterpret_cast<float4*>(sS)[i4] = sv;
                 }
@@ -484,18 +488,20 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a, int use_lds) 
     // 8 elements per thread per round, all loads issued before any is used
     for (int i0 = 0; i0 < per32; i0 += 8 * 256) {
         float d[8], lv[8];
+        int bq[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int idx = min(i0 + u * 256 + static_cast<int>(threadIdx.x), per32 - 1);  // clamped: in bounds
             const int p = idx / KK, e = idx - p * KK;
             d[u] = sum_strided<kMaxMlpBlocks>(part_req + (p * a.nblk) * KK + e, KK, a.nblk);
-            lv[u] = vals_req[(p + 1) * K + e % K];
+            bq[u] = e % K;
+            lv[u] = vals_req[(p + 1) * K + bq[u]];
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int idx = i0 + u * 256 + static_cast<int>(threadIdx.x);
             if (idx < per32) {
-                const float sv = idx % K < a.m ? lv[u] + (d[u] + b2) : -INFINITY;
+                const float sv = bq[u] < a.m ? lv[u] + (d[u] + b2) : -INFINITY;
                 scores_req[idx] = sv;
                 if (use_lds) sS[idx] = sv;
             }
