@@ -272,7 +272,7 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
         uj.splits = L.usplits;
         uj.C = upart;
         if (hproj_done) {
-            q("cand_gemm", [&] { return launch_gemm(uj.A, uj.W, uj.M, uj.N, uj.kdim, uj.splits, uj.C, q.s); });
+            q("cand_gemm", [&] { return launch_gemm_gather(uj, q.s); });
         } else {
             q("proj_gemm", [&] { return launch_gemm2(uj, hj, q.s); });
         }

@@ -88,6 +88,9 @@ struct GemmJob {
 hipError_t launch_gemm(const GemmA& A, const GemmW& W, int64_t M, int N, int kdim, int splits, float* C,
                        hipStream_t stream);
 hipError_t launch_gemm2(const GemmJob& j0, const GemmJob& j1, hipStream_t stream);
+// The same product for one job on 128 x 128 tiles with loads going straight
+// to LDS (the candidate projection); identical partials.  W.kwrap must be 0.
+hipError_t launch_gemm_gather(const GemmJob& j, hipStream_t stream);
 // Workgroups a GEMM job occupies in a launch.
 int64_t gemm_launch_blocks(const GemmJob& j);
 

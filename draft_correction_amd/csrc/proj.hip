@@ -40,6 +40,190 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmJob j0, GemmJob j1, int64
         gemm_body(j1, b - nblk0, smem);
 }
 
+// ------------------------------------------------------------ gather gemm --
+// The candidate projection u = W_cand E[c]: 128 x 128 output tiles of one
+// k-split per 512-thread workgroup (8 waves, 4 along m x 2 along n, each
+// 32 x 64 as 2 x 4 v_mfma_f32_16x16x32_bf16).  The gathered embedding rows
+// and the W rows go from memory straight into LDS (global_load_lds_dwordx4:
+// no registers held while they are in flight) through a ring of four
+// [A | W] stages of 64-deep k-slabs; three slabs are in flight while one is
+// multiplied, and one workgroup barrier per slab orders the ring.  Each
+// output is accumulated in the same k order as gemm_body (slab by slab, the
+// two 32-wide halves of a slab in turn), so the two give identical partials.
+
+constexpr int kGM = 128, kGN = 128, kGK = 64;    // tile rows, columns, slab depth
+constexpr int kGThreads = 512;
+constexpr int kGStage = kGM * kGK;               // bf16 per A (= per W) stage
+constexpr int kGStages = 4;
+static_assert(kGM == kGN, "A and W stages share one size");
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(1))) void* global_void_ptr;
+
+// Segment p (16 bytes) of stage row r holds k-segment p ^ gswz(r), so the
+// 8 (or 16) rows that one fragment read touches at a time sit in distinct
+// LDS banks; a load instruction still covers whole 128-byte row pieces.
+__device__ __forceinline__ int gswz(int r) { return ((r >> 1) + 4 * (r & 1)) & 7; }
+
+// One 16-byte load per lane from g into LDS at lds + 16 * lane (lds is the
+// same for the whole wave).
+__device__ __forceinline__ void lds_dma16(const uint16_t* g, uint16_t* lds) {
+    __builtin_amdgcn_global_load_lds((global_void_ptr)(g), (lds_void_ptr)(lds), 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) with the other counters unconstrained.
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(n >= 0 && n < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0xF70);
+}
+
+__global__ __launch_bounds__(kGThreads) void gemm_gather_kernel(GemmJob J) {
+    // the ring: stage s is [A slab | W slab]; after the loop the first
+    // 72 KB stage the output tiles
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[kGStages * 2 * kGStage];
+    const GemmA& A = J.A;
+    const GemmW& W = J.W;
+    const int64_t M = J.M;
+    const int N = J.N, kdim = J.kdim, splits = J.splits;
+    const int tid = threadIdx.x, l = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    // split fastest, as in gemm_body: consecutive workgroups (spread over the
+    // XCDs) take different k-slices
+    const int64_t lin = blockIdx.x;
+    const int split = static_cast<int>(lin % splits);
+    const int64_t rest = lin / splits;
+    const int ntn = (N + kGN - 1) / kGN;
+    const int n0 = static_cast<int>(rest % ntn) * kGN;
+    const int64_t m0 = (rest / ntn) * kGM;
+    const int kper = ((kdim / 32 + splits - 1) / splits) * 32;
+    const int k_lo = split * kper;
+    const int k_hi = min(kdim, k_lo + kper);
+    const int nslab = k_lo < k_hi ? (k_hi - k_lo + kGK - 1) / kGK : 0;
+
+    // Wave w fills 8-row blocks 2w and 2w + 1 of each stage's A and W slabs,
+    // one instruction per block: lane l takes row 8b + l/8 and places its
+    // 16 bytes at position l % 8 of that row, i.e. k-segment
+    // (l % 8) ^ gswz(row).  Rows past M or N repeat the last row (their
+    // results are not stored).
+    const uint16_t* ga[2];
+    const uint16_t* gw[2];
+    int segk[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int row = (2 * wave + i) * 8 + (l >> 3);
+        segk[i] = ((l & 7) ^ gswz(row)) * 8;
+        ga[i] = a_row(A, min(m0 + row, M - 1));
+        const int nn = min(n0 + row, N - 1);
+        const int b = nn / W.nb;
+        const uint16_t* wb = b == 0 ? W.base[0] : (b == 1 ? W.base[1] : W.base[2]);
+        const int64_t wld = b == 0 ? W.ld[0] : (b == 1 ? W.ld[1] : W.ld[2]);
+        gw[i] = wb + static_cast<int64_t>(nn % W.nb) * wld;
+    }
+    auto stage_a = [&](int st) { return smem + st * 2 * kGStage; };
+    auto stage_w = [&](int st) { return smem + st * 2 * kGStage + kGStage; };
+    // k ranges are multiples of 32, so only a split's last slab can be half
+    // valid; its loads then re-read the valid half (in bounds) and only the
+    // first 32-wide half is multiplied.
+    auto issue = [&](int s) {
+        const int k0 = k_lo + s * kGK;
+        const bool half = k0 + kGK > k_hi;
+        uint16_t* sa = stage_a(s % kGStages);
+        uint16_t* sw = stage_w(s % kGStages);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int ko = k0 + (half ? (segk[i] & 31) : segk[i]);
+            lds_dma16(ga[i] + ko, sa + (2 * wave + i) * 8 * kGK);
+            lds_dma16(gw[i] + ko, sw + (2 * wave + i) * 8 * kGK);
+        }
+    };
+    // Fragments: lane l reads row l % 16 of a 16-row tile, k-segment
+    // 4 ks + l / 16 of the slab, at position (4 ks + l / 16) ^ gswz(l % 16).
+    const int q = l >> 4;
+    const int sz = gswz(l & 15);
+    const int off[2] = {(l & 15) * kGK + ((q ^ sz) * 8), (l & 15) * kGK + (((4 + q) ^ sz) * 8)};
+    f32x4 acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto lds_addr = [](const uint16_t* p) {
+        return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const uint16_t*)(p)));
+    };
+    // The fragment reads are written as inline assembly, so the compiler sees
+    // no LDS read that it would have to order after the direct loads still in
+    // flight (it would wait for all of them, later slabs included); the
+    // per-slab vmcnt waits and the barrier order them instead.
+    auto mma_half = [&](uint32_t ab, uint32_t wb) {
+        u32x4 af0, af1, wf0, wf1, wf2, wf3;
+        asm volatile(
+            "ds_read_b128 %0, %6\n\t"
+            "ds_read_b128 %1, %6 offset:2048\n\t"
+            "ds_read_b128 %2, %7\n\t"
+            "ds_read_b128 %3, %7 offset:2048\n\t"
+            "ds_read_b128 %4, %7 offset:4096\n\t"
+            "ds_read_b128 %5, %7 offset:6144\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(af0), "=&v"(af1), "=&v"(wf0), "=&v"(wf1), "=&v"(wf2), "=&v"(wf3)
+            : "v"(ab), "v"(wb));
+        const u32x4 af[2] = {af0, af1}, wf[4] = {wf0, wf1, wf2, wf3};
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(af[i], wf[j], acc[i][j]);
+    };
+    for (int s = 0; s < kGStages - 1 && s < nslab; ++s) issue(s);
+    for (int s = 0; s < nslab; ++s) {
+        // this wave's loads of slab s have landed once no more than those of
+        // the slabs issued after it (four instructions each) are pending
+        switch (min(kGStages - 2, nslab - 1 - s)) {
+            case 0: wait_vmcnt<0>(); break;
+            case 1: wait_vmcnt<4>(); break;
+            default: wait_vmcnt<8>(); break;
+        }
+        // workgroup barrier without a memory fence (a fence would wait for
+        // every load in flight): every wave's slab s has landed, and every
+        // wave has finished reading slab s - 1, whose stage is refilled next
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (s + kGStages - 1 < nslab) issue(s + kGStages - 1);
+        const uint32_t ab = lds_addr(stage_a(s % kGStages) + wm * 32 * kGK);
+        const uint32_t wb = lds_addr(stage_w(s % kGStages) + wn * 64 * kGK);
+        mma_half(ab + 2 * off[0], wb + 2 * off[0]);
+        if (k_lo + s * kGK + kGK <= k_hi) mma_half(ab + 2 * off[1], wb + 2 * off[1]);
+    }
+    // Output: each wave stages its 32 x 64 tile (9 KB) once every wave has
+    // finished its reads, then writes whole rows; the partials are written
+    // nontemporally (read once, by the next kernel).
+    __syncthreads();
+    constexpr int kRS = 64 + 4;                  // staging row stride (floats)
+    float* cs = reinterpret_cast<float*>(smem + wave * 4608);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) cs[(i * 16 + 4 * q + e) * kRS + j * 16 + (l & 15)] = acc[i][j][e];
+    __builtin_amdgcn_wave_barrier();
+    float* out = J.C + static_cast<int64_t>(split) * M * N;
+    const int64_t r0 = m0 + wm * 32;
+    const int c0 = n0 + wn * 64 + (l & 15) * 4;
+    f32x4 v[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) v[t] = *reinterpret_cast<const f32x4*>(cs + (t * 4 + q) * kRS + (l & 15) * 4);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const int64_t r = r0 + t * 4 + q;
+        if (r < M && c0 + 3 < N) {
+            __builtin_nontemporal_store(v[t], reinterpret_cast<f32x4*>(out + r * N + c0));
+        } else {
+            for (int e = 0; e < 4; ++e)
+                if (r < M && c0 + e < N) out[r * N + c0 + e] = v[t][e];
+        }
+    }
+}
+
 // ------------------------------------------------------------------- cand --
 
 constexpr int kCR = 32;                 // candidate rows per workgroup
@@ -433,6 +617,12 @@ int64_t gemm_launch_blocks(const GemmJob& j) {
 hipError_t launch_gemm2(const GemmJob& j0, const GemmJob& j1, hipStream_t stream) {
     const int64_t b0 = gemm_launch_blocks(j0);
     return launch(gemm_kernel, dim3(static_cast<unsigned>(b0 + gemm_launch_blocks(j1))), 256, 0, stream, j0, j1, b0);
+}
+
+hipError_t launch_gemm_gather(const GemmJob& j, hipStream_t stream) {
+    if (j.W.kwrap > 0 || j.kdim % 32 != 0) return hipErrorInvalidValue;
+    const int64_t blocks = ((j.M + kGM - 1) / kGM) * ((j.N + kGN - 1) / kGN) * j.splits;
+    return launch(gemm_gather_kernel, dim3(static_cast<unsigned>(blocks)), kGThreads, 0, stream, j);
 }
 
 hipError_t launch_gemm(const GemmA& A, const GemmW& W, int64_t M, int N, int kdim, int splits, float* C,
