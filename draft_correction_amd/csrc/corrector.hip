@@ -29,7 +29,7 @@ constexpr int kMaxKernels = 12;
 constexpr size_t kAlign = 256;
 
 struct Layout {
-    size_t part, lse, ids, vals, hproj, upart, z, g, s, uv, vout, vin, mlp_part, scores, total;
+    size_t part, lse, ids, vals, hproj, upart, z, g, s, vout, vin, mlp_part, scores, total;
     int chunks, splits, usplits;
 };
 
@@ -96,7 +96,6 @@ Layout layout(const corrector_desc& d, int32_t n) {
     L.g = take(sizeof(float) * rows * d.r);
     L.s = take(sizeof(float) * pairs * d.r);
     const bool mlp = d.variant == CORR_VARIANT_MLP;
-    L.uv = take(mlp ? sizeof(float) * rows * d.k * 2 * d.mlp_hidden : 0);
     L.mlp_part = take(mlp ? sizeof(float) * pairs * mlp_blocks(d.mlp_hidden) * d.k * d.k : 0);
     const bool cos = d.variant == CORR_VARIANT_COSINE;
     L.vout = take(cos ? sizeof(float) * rows * d.k * d.d_vec : 0);
@@ -299,11 +298,6 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
     ca.g_out = at<float>(ws, L.g);
     ca.s_out = mlp_pairs ? at<float>(ws, L.s) : nullptr;
     ca.zhl = at<uint16_t>(ws, L.z);
-    if (mlp_pairs) {  // the candidate kernel also forms U | V = [W1_za; W1_zb] z
-        ca.w1 = static_cast<const uint16_t*>(w.w1);
-        ca.h = d.mlp_hidden;
-        ca.uv = at<float>(ws, L.uv);
-    }
     if (cos) {
         ca.w_out = static_cast<const uint16_t*>(w.w_out);
         ca.w_in = static_cast<const uint16_t*>(w.w_in);
@@ -344,7 +338,7 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
             q(path_name(h), [&] { return launch_path_rule(h, scores, ids, n, tokens, choice, q.s); });
     } else {
         MlpArgs m{};
-        m.uv = ca.uv;
+        m.zhl = ca.zhl;
         m.s = ca.s_out;
         m.vals = vals;
         m.n = n;

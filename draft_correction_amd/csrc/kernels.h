@@ -131,11 +131,7 @@ struct CandArgs {
     int B;                  // drafted slots per request
     float* g_out;           // [rows][r]
     float* s_out;           // [n(B-1)][r], or null
-    uint16_t* zhl;
-    // MLP variant (null otherwise): U | V = [W1_za; W1_zb] z -> uv [rows*K][2h]
-    const uint16_t* w1;     // [h][3r+2]
-    int h;
-    float* uv;
+    uint16_t* zhl;          // [rows][K][2r] bf16 [hi | lo] rows of z
     // cosine only (null otherwise)
     const uint16_t* w_out;
     const uint16_t* w_in;
@@ -148,7 +144,7 @@ hipError_t launch_cand(const CandArgs& a, hipStream_t stream);
 
 // ---- transition scores (mlp.hip, cosine.hip)
 struct MlpArgs {
-    const float* uv;        // [n][B][K][2h]: W1_za z | W1_zb z per candidate
+    const uint16_t* zhl;    // [n][B][K][2r] bf16: z as [hi | lo] rows (the candidate kernel's output)
     const float* s;         // [n(B-1)][r]: pair state s_p (float32)
     const float* vals;      // [n][B][K]
     int n;
@@ -165,6 +161,7 @@ struct MlpArgs {
 // Most hidden-unit blocks of the MLP (h <= 256 units in blocks of 64).
 constexpr int kMaxMlpBlocks = 4;
 int mlp_blocks(int h);
+size_t mlp_lds_bytes(int K, int r);
 hipError_t launch_mlp(const MlpArgs& a, hipStream_t stream);
 
 // Sum of the MLP partials in block order + b2 + l_{p+1}(b) -> scores (one

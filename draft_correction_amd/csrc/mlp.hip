@@ -6,13 +6,13 @@
 //   W1 x = (W1_s s_p + b1 + W1_za z_p^a + w_la l_p(a)) + (W1_zb z_{p+1}^b + w_lb l_{p+1}(b))
 //        =              P_p[a]                        +            Q_p[b]
 // so the K^2 x (3r+2) x h product collapses to per-candidate products
-// U = W1_za z and V = W1_zb z (each candidate's z meets the weights once,
-// whichever pairs it belongs to; the candidate kernel forms them on MFMA
-// with z as bf16 hi | lo rows, so they carry float32 accuracy), the per-pair
-// c_p = W1_s s_p (float32 dot products here, a quarter of r per thread), and
-// a K x K broadcast add.  This kernel forms P and Q and runs the epilogue:
-// the GELU over all K^2 x h pre-activations and the h -> 1 dot with w2, one
-// (a, b) per thread.
+// U = W1_za z and V = W1_zb z, the per-pair c_p = W1_s s_p (float32 dot
+// products, a quarter of r per thread), and a K x K broadcast add.  Each
+// candidate's U (for the pair it starts) and V (for the pair it ends) over a
+// block of hidden units is needed by one workgroup only, so the workgroup
+// forms them itself on MFMA, from z as bf16 hi | lo rows (float32
+// accuracy), then forms P and Q and runs the epilogue: the GELU over all
+// K^2 x h pre-activations and the h -> 1 dot with w2, one (a, b) per thread.
 //
 // Work is split into (pair, block of 64 hidden units) workgroups; each block
 // writes its partial Delta and the finishing kernel adds the blocks in order,
@@ -53,15 +53,31 @@ constexpr int kJB = 64;
 static_assert(256 == 4 * kJB, "four r quarters per hidden unit in the c_p dot");
 static_assert(256 / kJB <= kMaxMlpBlocks, "the finishing kernel sums at most kMaxMlpBlocks blocks");
 
+typedef __attribute__((address_space(3))) void* mlp_lds_ptr;
+typedef __attribute__((address_space(1))) void* mlp_global_ptr;
+
+// A staged z row holds its 2r bf16 values unpadded; segment s (16 bytes) of
+// row a sits at position s ^ (a & mask), mask = min(7, segments - 1), so the
+// eight rows one fragment read touches at a time sit in distinct banks
+// (r >= 32) while every segment stays inside its row.
+template <int ZSEG>
+__device__ __forceinline__ int zpos(int a, int s) { return s ^ (a & (ZSEG < 8 ? ZSEG - 1 : 7)); }
+
 // One workgroup per (pair, block of up to 64 hidden units):
+//   U_p[a][j] = W1_za[j] z_p^a,  V_{p+1}[b][j] = W1_zb[j] z_{p+1}^b   (MFMA)
 //   P[a][j] = c_p[j] + b1[j] + w_la[j] l_p(a) + U_p[a][j]
 //   Q[b][j] = w_lb[j] l_{p+1}(b) + V_{p+1}[b][j]
-// from the per-candidate products U | V and the pair's c_p (formed here from
-// s_p), then GELU and the dot with w2 over the K x m
-// candidate pairs (successors b < m; m = K unless sparsified), one (a, b) per
-// thread; the block's partial Delta goes to
-// part[pair][block][a][b].
-__global__ __launch_bounds__(256) void mlp_kernel(MlpArgs a) {
+// with c_p = W1_s s_p formed here too, then GELU and the dot with w2 over the
+// K x m candidate pairs (successors b < m; m = K unless sparsified), one
+// (a, b) per thread; the block's partial Delta goes to part[pair][block][a][b].
+// U and V are accumulated exactly as a 16 x 16 tile product over the 2r
+// values [hi(z) | lo(z)] in k order, the hi and lo halves meeting the same
+// W1 columns.
+template <int R>
+__global__ __launch_bounds__(256, 6) void mlp_kernel(MlpArgs a) {
+    constexpr int KS = 2 * R / 32;          // 32-wide k-steps over [hi | lo]
+    constexpr int KD = R >= 32 ? R / 32 : 1;  // distinct W1 fragments (hi and lo share them)
+    constexpr int ZSEG = 2 * R / 8;         // 16-byte segments per z row
     const int tid = threadIdx.x;
     const int B = a.B, K = a.K, h = a.h;
     const int nj = (h + kJB - 1) / kJB;
@@ -79,102 +95,122 @@ __global__ __launch_bounds__(256) void mlp_kernel(MlpArgs a) {
     const int64_t tp = static_cast<int64_t>(req) * B + p;  // slot rows of the pair
     const int64_t tq = tp + 1;
     constexpr int PS = kJB + 4;     // LDS row stride of P / Q (floats)
-    const int nin = 3 * a.r + 2;
+    const int nin = 3 * R + 2;
+    const int l = tid & 63, wave = tid >> 6;
 
     __shared__ __attribute__((aligned(16))) float w2s[kJB];
     extern __shared__ __attribute__((aligned(16))) float dyn[];
     float* P = dyn;                 // [K][PS]
     float* Q = dyn + K * PS;        // [K][PS]
+    // z rows of slot p then slot p + 1: [2K][2r] bf16, segments permuted by zpos
+    uint16_t* zs = reinterpret_cast<uint16_t*>(dyn + 2 * K * PS);
+    __shared__ __attribute__((aligned(16))) float sps[R];   // the pair state s_p
 
     __shared__ float cps4[4][kJB];  // c_p partial dots, one per quarter of r
 
-    // ---- operands: thread (rg, cg) forms 4 columns of rows rg, rg + 16, ...;
-    // the first row's U, V and logits load here with everything else
-    const int cg = tid & 15, rg = tid >> 4;
-    const int c = cg * 4;
-    const bool colok = c < jn;
-    const int cc = colok ? j0 + c : j0;  // clamped columns are not stored
-    const int64_t ustride = 2 * static_cast<int64_t>(h);
-    const int m0 = min(rg, K - 1);        // rows past K are not stored
-    const float4 u0 = *reinterpret_cast<const float4*>(a.uv + (tp * K + m0) * ustride + cc);
-    const float4 v0 = *reinterpret_cast<const float4*>(a.uv + (tq * K + m0) * ustride + h + cc);
-    const float lp0 = a.vals[tp * K + m0], lq0 = a.vals[tq * K + m0];
-    const float4 b1v = *reinterpret_cast<const float4*>(a.b1 + cc);
-    float wla[4], wlb[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t wrow = static_cast<int64_t>(cc + i) * nin + 3 * a.r;
-        wla[i] = bf16_to_f32(a.w1[wrow]);
-        wlb[i] = bf16_to_f32(a.w1[wrow + 1]);
+    // ---- z rows of both slots straight into LDS (no registers held while
+    // in flight): slot p's K rows and slot p + 1's K rows are contiguous in
+    // zhl (rows tp K .. tp K + 2K - 1).  A wave instruction moves 64
+    // segments to 64 consecutive LDS positions; lanes past the last segment
+    // take no part.
+    {
+        const int nseg = 2 * K * ZSEG;
+        for (int s0 = wave * 64; s0 < nseg; s0 += 4 * 64) {
+            const int sg = s0 + l;                 // LDS position (row-major)
+            if (sg < nseg) {
+                const int row = sg / ZSEG, pos = sg % ZSEG;
+                const uint16_t* src = a.zhl + (tp * K + row) * (2 * R) + zpos<ZSEG>(row, pos) * 8;
+                __builtin_amdgcn_global_load_lds((mlp_global_ptr)(src), (mlp_lds_ptr)(zs + s0 * 8), 16, 0, 0);
+            }
+        }
+        // s_p (r floats, r / 4 segments) the same way, by the last wave
+        if (wave == 3 && l < R / 4)
+            __builtin_amdgcn_global_load_lds((mlp_global_ptr)(a.s + static_cast<int64_t>(pair) * R + 4 * l),
+                                             (mlp_lds_ptr)(sps), 16, 0, 0);
     }
+
+    // ---- per-lane operands of the U | V tiles: wave w owns hidden units
+    // j0 + 16 w .. + 15 of the block (columns past jn are formed from the
+    // last valid unit and not stored)
+    const int jl = min(16 * wave + (l & 15), jn - 1);   // this lane's unit within the block
+    const bool wave_on = 16 * wave < jn;
+    // W1_za | W1_zb fragments of this lane's unit
+    u32x4 bu[KD], bv[KD];
+    {
+        const uint16_t* wr = a.w1 + static_cast<int64_t>(j0 + jl) * nin;
+        const int kq = 8 * (l >> 4);
+#pragma unroll
+        for (int d = 0; d < KD; ++d) {
+            bu[d] = load16(wr + R + ((d * 32 + kq) % R));
+            bv[d] = load16(wr + 2 * R + ((d * 32 + kq) % R));
+        }
+    }
+    const float wla = bf16_to_f32(a.w1[static_cast<int64_t>(j0 + jl) * nin + 3 * R]);
+    const float wlb = bf16_to_f32(a.w1[static_cast<int64_t>(j0 + jl) * nin + 3 * R + 1]);
+    const float b1j = a.b1[j0 + jl];
     if (tid < kJB) w2s[tid] = tid < jn ? a.w2[j0 + tid] * (1.0f / kGeluAlpha) : 0.f;   // see gelu_scaled
     // c_p = W1_s s_p for the block's units: thread (jj, kq) dots row j0 + jj
     // of W1_s with s_p over the quarter kq of its r columns, in column order.
     // W1 rows are 3r + 2 bf16 long (4-byte aligned: r is a multiple of 16),
-    // so they are read in 32-bit words of two columns each.
+    // so they are read in 32-bit words of two columns each; s_p is read from
+    // LDS once every load of the workgroup has landed.
+    const int jj = tid & (kJB - 1), kqc = tid / kJB;
+    constexpr int kw = R / 4;
+    constexpr int kG = kw / 4;
+    uint32_t wv[2 * kG];
     {
-        const int jj = tid & (kJB - 1), kq = tid / kJB;
-        const int kw = a.r / 4;
         const uint32_t* wr = reinterpret_cast<const uint32_t*>(
-            a.w1 + static_cast<int64_t>(min(j0 + jj, h - 1)) * nin + kq * kw);
-        const float* sp = a.s + static_cast<int64_t>(pair) * a.r + kq * kw;
-        // every load is issued before the first is used (r <= 128: at most
-        // 8 groups of 4 columns; groups past kw re-read the last and are not
-        // summed)
-        constexpr int kG = 128 / 4 / 4;
-        uint32_t wv[2 * kG];
-        float4 sv[kG];
+            a.w1 + static_cast<int64_t>(min(j0 + jj, h - 1)) * nin + kqc * kw);
 #pragma unroll
-        for (int g = 0; g < kG; ++g) {
-            const int k = min(4 * g, kw - 4);
-            wv[2 * g] = wr[k / 2];
-            wv[2 * g + 1] = wr[k / 2 + 1];
-            sv[g] = *reinterpret_cast<const float4*>(sp + k);
-        }
+        for (int g = 0; g < 2 * kG; ++g) wv[g] = wr[g];
+    }
+    __syncthreads();   // every load has landed: z rows and s_p in LDS
+    {
+        const float* sp = sps + kqc * kw;
         float acc = 0.f;
 #pragma unroll
         for (int g = 0; g < kG; ++g) {
-            if (4 * g < kw) {
-                acc = fmaf(__uint_as_float(wv[2 * g] << 16), sv[g].x, acc);
-                acc = fmaf(__uint_as_float(wv[2 * g] & 0xFFFF0000u), sv[g].y, acc);
-                acc = fmaf(__uint_as_float(wv[2 * g + 1] << 16), sv[g].z, acc);
-                acc = fmaf(__uint_as_float(wv[2 * g + 1] & 0xFFFF0000u), sv[g].w, acc);
-            }
+            const float4 sv = *reinterpret_cast<const float4*>(sp + 4 * g);
+            acc = fmaf(__uint_as_float(wv[2 * g] << 16), sv.x, acc);
+            acc = fmaf(__uint_as_float(wv[2 * g] & 0xFFFF0000u), sv.y, acc);
+            acc = fmaf(__uint_as_float(wv[2 * g + 1] << 16), sv.z, acc);
+            acc = fmaf(__uint_as_float(wv[2 * g + 1] & 0xFFFF0000u), sv.w, acc);
         }
-        cps4[kq][jj] = acc;
+        cps4[kqc][jj] = acc;
     }
-    __syncthreads();
+    __syncthreads();   // c_p partials
 
-    // ---- P = c_p + b1 + w_la l_p(a) + U, Q = w_lb l_{p+1}(b) + V
-    {
-        float cpv[4];
+    // ---- U | V tiles on MFMA, then P and Q in the tiles' lane layout
+    // (lane l holds rows 4 (l/16) + i, unit l % 16 of a 16 x 16 tile)
+    if (wave_on) {
+        const float cp = ((cps4[0][jl] + cps4[1][jl]) + (cps4[2][jl] + cps4[3][jl])) + b1j;
+        const int kq = 8 * (l >> 4);
+        const int jc = 16 * wave + (l & 15);            // column in P / Q
+        for (int rt = 0; rt * 16 < K; ++rt) {
+            const int ar = min(rt * 16 + (l & 15), K - 1);   // fragment row (rows past K are not stored)
+            f32x4 accu = {0.f, 0.f, 0.f, 0.f}, accv = {0.f, 0.f, 0.f, 0.f};
+            // one k-step's z fragments in registers at a time (the compiler
+            // barrier keeps the reads from being hoisted together)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int jj = min(c + i, kJB - 1);
-            cpv[i] = ((cps4[0][jj] + cps4[1][jj]) + (cps4[2][jj] + cps4[3][jj]));
-        }
-        cpv[0] += b1v.x;
-        cpv[1] += b1v.y;
-        cpv[2] += b1v.z;
-        cpv[3] += b1v.w;
-        for (int m = rg; m < K; m += 16) {
-            float4 u = u0, v = v0;
-            float lp = lp0, lq = lq0;
-            if (m != rg) {
-                const int64_t np = tp * K + m, nq = tq * K + m;
-                u = *reinterpret_cast<const float4*>(a.uv + np * ustride + cc);
-                v = *reinterpret_cast<const float4*>(a.uv + nq * ustride + h + cc);
-                lp = a.vals[np];
-                lq = a.vals[nq];
+            for (int ks = 0; ks < KS; ++ks) {
+                const int sgi = (ks * 32 + kq) / 8;
+                const u32x4 zu = *reinterpret_cast<const u32x4*>(zs + (ar * ZSEG + zpos<ZSEG>(ar, sgi)) * 8);
+                const u32x4 zv = *reinterpret_cast<const u32x4*>(zs + ((K + ar) * ZSEG + zpos<ZSEG>(K + ar, sgi)) * 8);
+                accu = mfma16x16x32(zu, bu[ks % KD], accu);
+                accv = mfma16x16x32(zv, bv[ks % KD], accv);
+                asm volatile("" ::: "memory");
             }
-            if (colok) {   // kept scaled by alpha (see gelu_scaled)
-                constexpr float al = kGeluAlpha;
-                *reinterpret_cast<float4*>(P + m * PS + c) =
-                    make_float4(al * (cpv[0] + fmaf(wla[0], lp, u.x)), al * (cpv[1] + fmaf(wla[1], lp, u.y)),
-                                al * (cpv[2] + fmaf(wla[2], lp, u.z)), al * (cpv[3] + fmaf(wla[3], lp, u.w)));
-                *reinterpret_cast<float4*>(Q + m * PS + c) =
-                    make_float4(al * fmaf(wlb[0], lq, v.x), al * fmaf(wlb[1], lq, v.y), al * fmaf(wlb[2], lq, v.z),
-                                al * fmaf(wlb[3], lq, v.w));
+            if (jc < jn) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int m = rt * 16 + 4 * (l >> 4) + i;
+                    if (m < K) {   // kept scaled by alpha (see gelu_scaled)
+                        constexpr float al = kGeluAlpha;
+                        const float lp = a.vals[tp * K + m], lq = a.vals[tq * K + m];
+                        P[m * PS + jc] = al * (cp + fmaf(wla, lp, accu[i]));
+                        Q[m * PS + jc] = al * fmaf(wlb, lq, accv[i]);
+                    }
+                }
             }
         }
     }
@@ -213,11 +249,21 @@ __global__ __launch_bounds__(256) void mlp_kernel(MlpArgs a) {
 
 int mlp_blocks(int h) { return (h + kJB - 1) / kJB; }
 
+size_t mlp_lds_bytes(int K, int r) {
+    return static_cast<size_t>(2) * K * (kJB + 4) * sizeof(float) + static_cast<size_t>(2) * K * 2 * r * sizeof(uint16_t);
+}
+
 hipError_t launch_mlp(const MlpArgs& a, hipStream_t stream) {
     const int pairs = a.n * (a.B - 1);
     const dim3 grid(static_cast<unsigned>((pairs + 7) / 8 * 8 * mlp_blocks(a.h)));
-    const size_t lds = static_cast<size_t>(2) * a.K * (kJB + 4) * sizeof(float);
-    return launch(mlp_kernel, grid, 256, static_cast<uint32_t>(lds), stream, a);
+    const uint32_t lds = static_cast<uint32_t>(mlp_lds_bytes(a.K, a.r));
+    switch (a.r) {
+        case 16: return launch(mlp_kernel<16>, grid, 256, lds, stream, a);
+        case 32: return launch(mlp_kernel<32>, grid, 256, lds, stream, a);
+        case 64: return launch(mlp_kernel<64>, grid, 256, lds, stream, a);
+        case 128: return launch(mlp_kernel<128>, grid, 256, lds, stream, a);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace corr

@@ -14,11 +14,10 @@
 //   cand   one workgroup per 32 candidates: b = LN(u) (non-affine),
 //          g = LN(W_ctx h) from hproj,
 //          y = W_fuse [b; g] on MFMA, z = gamma * LN(y) + beta, stored as
-//          bf16 hi | lo halves.  The MLP variant also forms the layer-1
-//          products U | V = [W1_za; W1_zb] z of every candidate; the cosine
-//          variant forms unit(W_out z) and unit(W_in z).  MFMA operands that
-//          are not already bf16 (b, g,
-//          z) are split into hi + lo bf16 parts multiplied by the same weight
+//          bf16 hi | lo halves (the MLP kernel forms its layer-1 products
+//          from them); the cosine variant also forms unit(W_out z) and
+//          unit(W_in z).  MFMA operands that are not already bf16 (b, g, z)
+//          are split into hi + lo bf16 parts multiplied by the same weight
 //          columns, so those products carry float32 accuracy.
 // All LayerNorm statistics are fp32 over the r features, biased variance.
 #include "common.h"
@@ -337,68 +336,12 @@ __device__ __forceinline__ void store_bf16s(uint16_t* dst, const uint16_t (&v)[N
     }
 }
 
-// U | V = [W1_za; W1_zb] z for the workgroup's M (<= kCR) candidates, z as
-// bf16 hi | lo rows in abuf (row stride as), written to uv [n0 + m][2h]: the
-// hi and lo halves meet the same W1 columns (those of z_p^a for U, of
-// z_{p+1}^b for V).  Wave w takes the 16-column tiles w, w + 4, ...; the W1
-// fragments of its next two tiles are loaded while the current one multiplies.
-template <int R>
-__device__ __forceinline__ void uv_tiles(const uint16_t* abuf, int as, int M, const uint16_t* w1, int h,
-                                         float* uv_rows) {
-    constexpr int KS = 2 * R / 32;
-    const int nin = 3 * R + 2;
-    const int l = lane_id();
-    const int wave = threadIdx.x >> 6;
-    const int kq = 8 * (l >> 4);
-    const int m = l & 15;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    u32x4 af[kCRT][KS];
-#pragma unroll
-    for (int rt = 0; rt < kCRT; ++rt)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            af[rt][ks] = rt * 16 + m < M ? *reinterpret_cast<const u32x4*>(abuf + (rt * 16 + m) * as + ks * 32 + kq)
-                                         : zero;
-    const int nct = 2 * h / 16;
-    auto wload = [&](int ct, u32x4 (&wf)[KS]) {
-        const int col = min(ct, nct - 1) * 16 + (l & 15);   // clamped tiles are not used
-        const bool v = col >= h;
-        const uint16_t* wr = w1 + static_cast<int64_t>(v ? col - h : col) * nin + (v ? 2 * R : R);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) wf[ks] = load16(wr + ((ks * 32 + kq) % R));
-    };
-    // three tiles' fragments in flight: tile c multiplies while c+1 and c+2 load
-    constexpr int kDepth = 3;
-    constexpr int kMaxTiles = 512 / 16 / kCW;   // 2h <= 512 columns over the waves
-    u32x4 wf[kDepth][KS];
-#pragma unroll
-    for (int c = 0; c < kDepth - 1; ++c) wload(wave + kCW * c, wf[c]);
-#pragma unroll
-    for (int c = 0; c < kMaxTiles; ++c) {
-        const int ct = wave + kCW * c;
-        if (ct >= nct) break;
-        wload(ct + kCW * (kDepth - 1), wf[(c + kDepth - 1) % kDepth]);
-#pragma unroll
-        for (int rt = 0; rt < kCRT; ++rt) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(af[rt][ks], wf[c % kDepth][ks], acc);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int mm = rt * 16 + 4 * (l >> 4) + i;
-                if (mm < M) uv_rows[static_cast<int64_t>(mm) * 2 * h + ct * 16 + (l & 15)] = acc[i];
-            }
-        }
-    }
-}
-
 // One workgroup per kCR consecutive candidates (nodes) of the [rows][K] list:
 //   u = W_cand E[c]   the candidate GEMM's split partials summed in order (or
 //                     a row of the folded table when one is given)
 //   b = LN(u), g = LN(W_ctx h) for the candidate's slot (from hproj)
 //   z = gamma * LN(W_fuse [b; g]) + beta, W_fuse on MFMA over [b; g] hi | lo
-//   stored as bf16 z hi | lo; MLP: U | V = [W1_za; W1_zb] z on MFMA;
-//   cosine: unit(W_out z), unit(W_in z).
+//   stored as bf16 z hi | lo; cosine: unit(W_out z), unit(W_in z).
 // Loops over r are compile-time so each phase issues all of its loads at once.
 template <int R>
 __global__ __launch_bounds__(kCT) void cand_kernel(CandArgs a) {
@@ -572,12 +515,6 @@ __global__ __launch_bounds__(kCT) void cand_kernel(CandArgs a) {
         store_bf16s<VPL>(grow + R, lo);
         store_bf16s<VPL>(arow, hi);
         store_bf16s<VPL>(arow + R, lo);
-    }
-    if (a.uv) {
-        // ---- MLP variant: the per-candidate layer-1 products U | V of z
-        __syncthreads();
-        uv_tiles<R>(abuf, as, M, a.w1, a.h, a.uv + n0 * 2 * a.h);
-        return;
     }
     if (!a.vout) return;
     __syncthreads();
