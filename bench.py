@@ -84,11 +84,9 @@ def algorithmic_work(cfg: dict, n: int) -> dict:
     w["topk_merge_hproj"] = dict(bound="hbm", bytes=w["topk_merge"]["bytes"] + w["hproj"]["bytes"],
                                  flops=w["hproj"]["flops"], per_unit=d * 2, units=rows,
                                  unit="slot row (K winners out; hidden row projected)")
-    # the MLP variant's candidate kernel also writes U | V = [W1_za; W1_zb] z
-    uvb = 2 * h * 4 if cfg["variant"] == "mlp" else 0
-    w["cand"] = dict(bound="hbm", bytes=rows * K * (r * 4 * 2 + uvb),
-                     flops=2 * rows * K * (2 * r * r + (2 * h * r if uvb else 0)),
-                     per_unit=r * 8 + uvb, units=rows * K, unit="candidate (u in; z and U|V out)")
+    # the candidate kernel reads the split partials of u and writes z (hi | lo)
+    w["cand"] = dict(bound="hbm", bytes=rows * K * (r * 4 * 2), flops=2 * rows * K * 2 * r * r,
+                     per_unit=r * 8, units=rows * K, unit="candidate (u in; z out)")
     w["finish"] = w["finish_walk"] = w["finish_viterbi"] = w["finish_beam"] = dict(bound="hbm", bytes=n * (B - 1) * K * K * 4 * 2,
                                           per_unit=(B - 1) * K * K * 8, units=n, unit="block")
     # the transition MLP epilogue is bound by the vector ALU: K m h GELU
@@ -96,6 +94,8 @@ def algorithmic_work(cfg: dict, n: int) -> dict:
     # against 256 CUs x 64 lanes x 2.4 GHz
     ms = cfg.get("succ_top_m", 0)
     ms = ms if 0 < ms < K else K   # successors scored per predecessor
+    # (its prologue also forms U = W1_za z and V = W1_zb z of the pair's
+    # candidates on MFMA: 2 K h r multiply-adds per pair, small next to these)
     w["mlp"] = dict(bound="alu", gelu=pairs * K * ms * h, flops=2 * pairs * K * ms * h,
                     per_unit=h, units=pairs * K * ms, unit="transition (h GELU evaluations)")
     w["cosine"] = w["cosine_walk"] = w["cosine_viterbi"] = w["cosine_beam"] = dict(
