@@ -63,70 +63,84 @@ typedef __attribute__((address_space(1))) void* mlp_global_ptr;
 template <int ZSEG>
 __device__ __forceinline__ int zpos(int a, int s) { return s ^ (a & (ZSEG < 8 ? ZSEG - 1 : 7)); }
 
-// One workgroup per (pair, block of up to 64 hidden units):
+// One workgroup per (two adjacent pairs p0, p0 + 1 of a request, block of up
+// to 64 hidden units); the last group of a request with an odd pair count
+// holds one pair.  For each pair p of the group:
 //   U_p[a][j] = W1_za[j] z_p^a,  V_{p+1}[b][j] = W1_zb[j] z_{p+1}^b   (MFMA)
 //   P[a][j] = c_p[j] + b1[j] + w_la[j] l_p(a) + U_p[a][j]
 //   Q[b][j] = w_lb[j] l_{p+1}(b) + V_{p+1}[b][j]
 // with c_p = W1_s s_p formed here too, then GELU and the dot with w2 over the
 // K x m candidate pairs (successors b < m; m = K unless sparsified), one
-// (a, b) per thread; the block's partial Delta goes to part[pair][block][a][b].
-// U and V are accumulated exactly as a 16 x 16 tile product over the 2r
-// values [hi(z) | lo(z)] in k order, the hi and lo halves meeting the same
-// W1 columns.
-template <int R>
-__global__ __launch_bounds__(256, 6) void mlp_kernel(MlpArgs a) {
+// (a, b) per thread; each pair's partial Delta for the block goes to
+// part[pair][block][a][b].  The two pairs share the W1 fragments and the z
+// rows of their middle slot.  U and V are accumulated exactly as a 16 x 16
+// tile product over the 2r values [hi(z) | lo(z)] in k order, the hi and lo
+// halves meeting the same W1 columns.
+template <int R, int KT>
+__global__ __launch_bounds__(256, KT > 2 ? 4 : 5) void mlp_kernel(MlpArgs a) {
     constexpr int KS = 2 * R / 32;          // 32-wide k-steps over [hi | lo]
     constexpr int KD = R >= 32 ? R / 32 : 1;  // distinct W1 fragments (hi and lo share them)
     constexpr int ZSEG = 2 * R / 8;         // 16-byte segments per z row
     const int tid = threadIdx.x;
     const int B = a.B, K = a.K, h = a.h;
     const int nj = (h + kJB - 1) / kJB;
+    const int G = B / 2;                    // pair groups per request: ceil((B - 1) / 2)
     // Consecutive workgroup numbers go to different XCDs (round-robin over 8):
-    // the hidden blocks of one pair are numbered 8 apart so they share an XCD.
+    // the hidden blocks of one group are numbered 8 apart so they share an XCD.
     const int lin = blockIdx.x;
     const int xcd = lin % 8, i8 = lin / 8;
     const int jblk = i8 % nj;
-    const int pair = (i8 / nj) * 8 + xcd;
-    if (pair >= a.n * (B - 1)) return;
-    const int item = pair * nj + jblk;
+    const int grp = (i8 / nj) * 8 + xcd;
+    if (grp >= a.n * G) return;
+    const int req = grp / G, p0 = 2 * (grp % G);
+    const int np = min(2, B - 1 - p0);      // pairs in this group
+    const int pair0 = req * (B - 1) + p0;
+    const int64_t t0 = static_cast<int64_t>(req) * B + p0;   // slot row of the first pair's predecessor
     const int j0 = jblk * kJB;
     const int jn = min(kJB, h - j0);
-    const int req = pair / (B - 1), p = pair % (B - 1);
-    const int64_t tp = static_cast<int64_t>(req) * B + p;  // slot rows of the pair
-    const int64_t tq = tp + 1;
     constexpr int PS = kJB + 4;     // LDS row stride of P / Q (floats)
     const int nin = 3 * R + 2;
     const int l = tid & 63, wave = tid >> 6;
 
     __shared__ __attribute__((aligned(16))) float w2s[kJB];
+    __shared__ __attribute__((aligned(16))) float sps[2][R];    // the pair states s_p
+    __shared__ float cps4[2][4][kJB];   // c_p partial dots, one per quarter of r
+    __shared__ float lv[3 * 64];        // the candidates' logits l of slots t0 .. t0 + np (K <= 64)
+    // First the z rows of the group's slots t0 .. t0 + np ([(np + 1) K][2r]
+    // bf16, segments permuted by zpos); once the U | V products are formed,
+    // the same memory holds P [2][K][PS] and Q [2][K][PS].
     extern __shared__ __attribute__((aligned(16))) float dyn[];
-    float* P = dyn;                 // [K][PS]
-    float* Q = dyn + K * PS;        // [K][PS]
-    // z rows of slot p then slot p + 1: [2K][2r] bf16, segments permuted by zpos
-    uint16_t* zs = reinterpret_cast<uint16_t*>(dyn + 2 * K * PS);
-    __shared__ __attribute__((aligned(16))) float sps[R];   // the pair state s_p
+    uint16_t* zs = reinterpret_cast<uint16_t*>(dyn);
+    float* Pb = dyn;
+    float* Qb = dyn + 2 * K * PS;
 
-    __shared__ float cps4[4][kJB];  // c_p partial dots, one per quarter of r
-
-    // ---- z rows of both slots straight into LDS (no registers held while
-    // in flight): slot p's K rows and slot p + 1's K rows are contiguous in
-    // zhl (rows tp K .. tp K + 2K - 1).  A wave instruction moves 64
-    // segments to 64 consecutive LDS positions; lanes past the last segment
-    // take no part.
+    // ---- z rows straight into LDS (no registers held while in flight):
+    // the slots' rows are contiguous in zhl.  A wave instruction moves 64
+    // segments to 64 consecutive LDS positions; lanes past the last take no
+    // part.  Then the pair states s_p, r / 4 segments each.
     {
-        const int nseg = 2 * K * ZSEG;
+        const int nseg = (np + 1) * K * ZSEG;
         for (int s0 = wave * 64; s0 < nseg; s0 += 4 * 64) {
-            const int sg = s0 + l;                 // LDS position (row-major)
+            const int sg = s0 + l;
             if (sg < nseg) {
                 const int row = sg / ZSEG, pos = sg % ZSEG;
-                const uint16_t* src = a.zhl + (tp * K + row) * (2 * R) + zpos<ZSEG>(row, pos) * 8;
+                const uint16_t* src = a.zhl + (t0 * K + row) * (2 * R) + zpos<ZSEG>(row, pos) * 8;
                 __builtin_amdgcn_global_load_lds((mlp_global_ptr)(src), (mlp_lds_ptr)(zs + s0 * 8), 16, 0, 0);
             }
         }
-        // s_p (r floats, r / 4 segments) the same way, by the last wave
-        if (wave == 3 && l < R / 4)
-            __builtin_amdgcn_global_load_lds((mlp_global_ptr)(a.s + static_cast<int64_t>(pair) * R + 4 * l),
-                                             (mlp_lds_ptr)(sps), 16, 0, 0);
+        if (wave >= 4 - np && l < R / 4) {
+            const int i = 3 - wave;   // wave 3: the first pair, wave 2: the second
+            __builtin_amdgcn_global_load_lds((mlp_global_ptr)(a.s + static_cast<int64_t>(pair0 + i) * R + 4 * l),
+                                             (mlp_lds_ptr)(sps[i]), 16, 0, 0);
+        }
+        // the slots' logits, 4 bytes per lane (waves 0 and 1, 64 values each)
+        const int nl = (np + 1) * K;
+        if (wave < 2 && wave * 64 < nl && wave * 64 + l < nl)
+            __builtin_amdgcn_global_load_lds((mlp_global_ptr)(a.vals + t0 * K + wave * 64 + l),
+                                             (mlp_lds_ptr)(lv + wave * 64), 4, 0, 0);
+        if (nl > 128 && wave == 2 && 128 + l < nl)
+            __builtin_amdgcn_global_load_lds((mlp_global_ptr)(a.vals + t0 * K + 128 + l),
+                                             (mlp_lds_ptr)(lv + 128), 4, 0, 0);
     }
 
     // ---- per-lane operands of the U | V tiles: wave w owns hidden units
@@ -134,7 +148,7 @@ __global__ __launch_bounds__(256, 6) void mlp_kernel(MlpArgs a) {
     // last valid unit and not stored)
     const int jl = min(16 * wave + (l & 15), jn - 1);   // this lane's unit within the block
     const bool wave_on = 16 * wave < jn;
-    // W1_za | W1_zb fragments of this lane's unit
+    // W1_za | W1_zb fragments of this lane's unit (shared by both pairs)
     u32x4 bu[KD], bv[KD];
     {
         const uint16_t* wr = a.w1 + static_cast<int64_t>(j0 + jl) * nin;
@@ -165,8 +179,8 @@ __global__ __launch_bounds__(256, 6) void mlp_kernel(MlpArgs a) {
         for (int g = 0; g < 2 * kG; ++g) wv[g] = wr[g];
     }
     __syncthreads();   // every load has landed: z rows and s_p in LDS
-    {
-        const float* sp = sps + kqc * kw;
+    for (int i = 0; i < np; ++i) {
+        const float* sp = sps[i] + kqc * kw;
         float acc = 0.f;
 #pragma unroll
         for (int g = 0; g < kG; ++g) {
@@ -176,39 +190,60 @@ __global__ __launch_bounds__(256, 6) void mlp_kernel(MlpArgs a) {
             acc = fmaf(__uint_as_float(wv[2 * g + 1] << 16), sv.z, acc);
             acc = fmaf(__uint_as_float(wv[2 * g + 1] & 0xFFFF0000u), sv.w, acc);
         }
-        cps4[kqc][jj] = acc;
+        cps4[i][kqc][jj] = acc;
     }
-    __syncthreads();   // c_p partials
 
-    // ---- U | V tiles on MFMA, then P and Q in the tiles' lane layout
-    // (lane l holds rows 4 (l/16) + i, unit l % 16 of a 16 x 16 tile)
+    // ---- U | V tiles on MFMA (lane l holds rows 4 (l/16) + i, unit l % 16
+    // of a 16 x 16 tile): U of pair i from slot t0 + i, V from slot t0 + i + 1
+    f32x4 accu[2][KT], accv[2][KT];
     if (wave_on) {
-        const float cp = ((cps4[0][jl] + cps4[1][jl]) + (cps4[2][jl] + cps4[3][jl])) + b1j;
         const int kq = 8 * (l >> 4);
-        const int jc = 16 * wave + (l & 15);            // column in P / Q
-        for (int rt = 0; rt * 16 < K; ++rt) {
-            const int ar = min(rt * 16 + (l & 15), K - 1);   // fragment row (rows past K are not stored)
-            f32x4 accu = {0.f, 0.f, 0.f, 0.f}, accv = {0.f, 0.f, 0.f, 0.f};
-            // one k-step's z fragments in registers at a time (the compiler
-            // barrier keeps the reads from being hoisted together)
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int sgi = (ks * 32 + kq) / 8;
-                const u32x4 zu = *reinterpret_cast<const u32x4*>(zs + (ar * ZSEG + zpos<ZSEG>(ar, sgi)) * 8);
-                const u32x4 zv = *reinterpret_cast<const u32x4*>(zs + ((K + ar) * ZSEG + zpos<ZSEG>(K + ar, sgi)) * 8);
-                accu = mfma16x16x32(zu, bu[ks % KD], accu);
-                accv = mfma16x16x32(zv, bv[ks % KD], accv);
-                asm volatile("" ::: "memory");
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int rt = 0; rt < KT; ++rt) {
+                accu[i][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                accv[i][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (i < np && rt * 16 < K) {
+                    // fragment rows past K repeat row K - 1 (not stored)
+                    const int ar = i * K + min(rt * 16 + (l & 15), K - 1);
+                    const int br = ar + K;
+                    // one k-step's z fragments in registers at a time (the
+                    // compiler barrier keeps the reads from being hoisted together)
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) {
+                        const int sgi = (ks * 32 + kq) / 8;
+                        const u32x4 zu = *reinterpret_cast<const u32x4*>(zs + (ar * ZSEG + zpos<ZSEG>(ar, sgi)) * 8);
+                        const u32x4 zv = *reinterpret_cast<const u32x4*>(zs + (br * ZSEG + zpos<ZSEG>(br, sgi)) * 8);
+                        accu[i][rt] = mfma16x16x32(zu, bu[ks % KD], accu[i][rt]);
+                        accv[i][rt] = mfma16x16x32(zv, bv[ks % KD], accv[i][rt]);
+                        asm volatile("" ::: "memory");
+                    }
+                }
             }
-            if (jc < jn) {
+    }
+    __syncthreads();   // the z rows are no longer read; P / Q take their place
+
+    // ---- P and Q in the tiles' lane layout
+    if (wave_on) {
+        const int jc = 16 * wave + (l & 15);            // column in P / Q
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int m = rt * 16 + 4 * (l >> 4) + i;
+        for (int i = 0; i < 2; ++i) {
+            if (i >= np) break;
+            const float cp = ((cps4[i][0][jl] + cps4[i][1][jl]) + (cps4[i][2][jl] + cps4[i][3][jl])) + b1j;
+            float* P = Pb + i * K * PS;
+            float* Q = Qb + i * K * PS;
+#pragma unroll
+            for (int rt = 0; rt < KT; ++rt) {
+                if (rt * 16 >= K || jc >= jn) break;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int m = rt * 16 + 4 * (l >> 4) + e;
                     if (m < K) {   // kept scaled by alpha (see gelu_scaled)
                         constexpr float al = kGeluAlpha;
-                        const float lp = a.vals[tp * K + m], lq = a.vals[tq * K + m];
-                        P[m * PS + jc] = al * (cp + fmaf(wla, lp, accu[i]));
-                        Q[m * PS + jc] = al * fmaf(wlb, lq, accv[i]);
+                        const float lp = lv[i * K + m], lq = lv[(i + 1) * K + m];
+                        P[m * PS + jc] = al * (cp + fmaf(wla, lp, accu[i][rt][e]));
+                        Q[m * PS + jc] = al * fmaf(wlb, lq, accv[i][rt][e]);
                     }
                 }
             }
@@ -216,22 +251,29 @@ __global__ __launch_bounds__(256, 6) void mlp_kernel(MlpArgs a) {
     }
     __syncthreads();
 
-    // ---- GELU and the dot with w2, one (a, b) per thread
+    // ---- GELU and the dot with w2: each thread takes successors b and b + 1
+    // of one predecessor a of one pair, so the P row and w2 are read once for
+    // both (each sum keeps its own order)
     const int ms = a.m;
-    const int nidx = K * ms;
-    float* out = a.part + static_cast<int64_t>(item) * K * K;
-    for (int idx = tid; idx < nidx; idx += 256) {
-        const int aa = idx / ms, bb = idx - aa * ms;
-        const float* pr = P + aa * PS;
-        const float* qr = Q + bb * PS;
-        float d0 = 0.f, d1 = 0.f;
+    const int mh = (ms + 1) / 2;
+    const int per = K * mh;
+    for (int idx = tid; idx < np * per; idx += 256) {
+        const int i = idx / per, r = idx - i * per;
+        const int aa = r / mh, bb = 2 * (r - aa * mh);
+        const bool two = bb + 1 < ms;
+        const float* pr = Pb + i * K * PS + aa * PS;
+        const float* qr = Qb + i * K * PS + bb * PS;
+        const float* qs = Qb + i * K * PS + (two ? bb + 1 : bb) * PS;
+        float d0 = 0.f, d1 = 0.f, e0 = 0.f, e1 = 0.f;
         for (int j = 0; j < jn; j += 8) {
             const float4 pv0 = *reinterpret_cast<const float4*>(pr + j);
-            const float4 qv0 = *reinterpret_cast<const float4*>(qr + j);
-            const float4 wv0 = *reinterpret_cast<const float4*>(w2s + j);
             const float4 pv1 = *reinterpret_cast<const float4*>(pr + j + 4);
-            const float4 qv1 = *reinterpret_cast<const float4*>(qr + j + 4);
+            const float4 wv0 = *reinterpret_cast<const float4*>(w2s + j);
             const float4 wv1 = *reinterpret_cast<const float4*>(w2s + j + 4);
+            const float4 qv0 = *reinterpret_cast<const float4*>(qr + j);
+            const float4 qv1 = *reinterpret_cast<const float4*>(qr + j + 4);
+            const float4 sv0 = *reinterpret_cast<const float4*>(qs + j);
+            const float4 sv1 = *reinterpret_cast<const float4*>(qs + j + 4);
             d0 = fmaf(wv0.x, gelu_scaled(pv0.x + qv0.x), d0);
             d1 = fmaf(wv0.y, gelu_scaled(pv0.y + qv0.y), d1);
             d0 = fmaf(wv0.z, gelu_scaled(pv0.z + qv0.z), d0);
@@ -240,8 +282,18 @@ __global__ __launch_bounds__(256, 6) void mlp_kernel(MlpArgs a) {
             d1 = fmaf(wv1.y, gelu_scaled(pv1.y + qv1.y), d1);
             d0 = fmaf(wv1.z, gelu_scaled(pv1.z + qv1.z), d0);
             d1 = fmaf(wv1.w, gelu_scaled(pv1.w + qv1.w), d1);
+            e0 = fmaf(wv0.x, gelu_scaled(pv0.x + sv0.x), e0);
+            e1 = fmaf(wv0.y, gelu_scaled(pv0.y + sv0.y), e1);
+            e0 = fmaf(wv0.z, gelu_scaled(pv0.z + sv0.z), e0);
+            e1 = fmaf(wv0.w, gelu_scaled(pv0.w + sv0.w), e1);
+            e0 = fmaf(wv1.x, gelu_scaled(pv1.x + sv1.x), e0);
+            e1 = fmaf(wv1.y, gelu_scaled(pv1.y + sv1.y), e1);
+            e0 = fmaf(wv1.z, gelu_scaled(pv1.z + sv1.z), e0);
+            e1 = fmaf(wv1.w, gelu_scaled(pv1.w + sv1.w), e1);
         }
-        out[aa * K + bb] = d0 + d1;
+        float* out = a.part + (static_cast<int64_t>(pair0 + i) * nj + jblk) * K * K + aa * K + bb;
+        out[0] = d0 + d1;
+        if (two) out[1] = e0 + e1;
     }
 }
 
@@ -250,18 +302,28 @@ __global__ __launch_bounds__(256, 6) void mlp_kernel(MlpArgs a) {
 int mlp_blocks(int h) { return (h + kJB - 1) / kJB; }
 
 size_t mlp_lds_bytes(int K, int r) {
-    return static_cast<size_t>(2) * K * (kJB + 4) * sizeof(float) + static_cast<size_t>(2) * K * 2 * r * sizeof(uint16_t);
+    // z rows of three slots, or P and Q of two pairs, whichever is larger
+    const size_t z = static_cast<size_t>(3) * K * 2 * r * sizeof(uint16_t);
+    const size_t pq = static_cast<size_t>(4) * K * (kJB + 4) * sizeof(float);
+    return z > pq ? z : pq;
+}
+
+template <int R>
+hipError_t launch_mlp_r(const MlpArgs& a, dim3 grid, uint32_t lds, hipStream_t stream) {
+    if (a.K <= 16) return launch(mlp_kernel<R, 1>, grid, 256, lds, stream, a);
+    if (a.K <= 32) return launch(mlp_kernel<R, 2>, grid, 256, lds, stream, a);
+    return launch(mlp_kernel<R, 4>, grid, 256, lds, stream, a);
 }
 
 hipError_t launch_mlp(const MlpArgs& a, hipStream_t stream) {
-    const int pairs = a.n * (a.B - 1);
-    const dim3 grid(static_cast<unsigned>((pairs + 7) / 8 * 8 * mlp_blocks(a.h)));
+    const int groups = a.n * (a.B / 2);   // pairs taken two at a time per request
+    const dim3 grid(static_cast<unsigned>((groups + 7) / 8 * 8 * mlp_blocks(a.h)));
     const uint32_t lds = static_cast<uint32_t>(mlp_lds_bytes(a.K, a.r));
     switch (a.r) {
-        case 16: return launch(mlp_kernel<16>, grid, 256, lds, stream, a);
-        case 32: return launch(mlp_kernel<32>, grid, 256, lds, stream, a);
-        case 64: return launch(mlp_kernel<64>, grid, 256, lds, stream, a);
-        case 128: return launch(mlp_kernel<128>, grid, 256, lds, stream, a);
+        case 16: return launch_mlp_r<16>(a, grid, lds, stream);
+        case 32: return launch_mlp_r<32>(a, grid, lds, stream);
+        case 64: return launch_mlp_r<64>(a, grid, lds, stream);
+        case 128: return launch_mlp_r<128>(a, grid, lds, stream);
         default: return hipErrorInvalidValue;
     }
 }

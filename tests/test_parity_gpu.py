@@ -36,6 +36,18 @@ def test_tiny(head, ties):
         assert (gpu["choice"] == 0).all()
 
 
+@pytest.mark.parametrize("B,n", [(2, 3), (4, 2), (7, 2)])
+def test_tiny_pair_counts(B, n):
+    """1, 3 and 6 adjacent pairs per request (the MLP kernel takes the pairs
+    of a request two at a time; an odd count leaves a single last pair), and
+    several requests per call."""
+    _log("tiny B=%d n=%d" % (B, n))
+    x = P.inputs("tiny", head="stress", B=B, n=n)
+    gpu = P.gpu_run(x)
+    ora = P.oracle_run(x)
+    P.check_all(gpu, ora, "tiny/B=%d/n=%d" % (B, n))
+
+
 @pytest.mark.parametrize("sigma", [1.0, 8.0])
 def test_tiny_cosine(sigma):
     _log("tiny cosine sigma=%g" % sigma)
