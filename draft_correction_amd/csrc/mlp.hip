@@ -63,28 +63,29 @@ typedef __attribute__((address_space(1))) void* mlp_global_ptr;
 template <int ZSEG>
 __device__ __forceinline__ int zpos(int a, int s) { return s ^ (a & (ZSEG < 8 ? ZSEG - 1 : 7)); }
 
-// One workgroup per (two adjacent pairs p0, p0 + 1 of a request, block of up
-// to 64 hidden units); the last group of a request with an odd pair count
-// holds one pair.  For each pair p of the group:
+// One workgroup per (NP adjacent pairs p0 .. p0 + NP - 1 of a request, block
+// of up to 64 hidden units); the last group of a request may hold fewer.  For
+// each pair p of the group:
 //   U_p[a][j] = W1_za[j] z_p^a,  V_{p+1}[b][j] = W1_zb[j] z_{p+1}^b   (MFMA)
 //   P[a][j] = c_p[j] + b1[j] + w_la[j] l_p(a) + U_p[a][j]
 //   Q[b][j] = w_lb[j] l_{p+1}(b) + V_{p+1}[b][j]
 // with c_p = W1_s s_p formed here too, then GELU and the dot with w2 over the
 // K x m candidate pairs (successors b < m; m = K unless sparsified), one
 // (a, b) per thread; each pair's partial Delta for the block goes to
-// part[pair][block][a][b].  The two pairs share the W1 fragments and the z
-// rows of their middle slot.  U and V are accumulated exactly as a 16 x 16
+// part[pair][block][a][b].  With two pairs per group they share the W1
+// fragments and the z rows of their middle slot; one pair per group gives
+// twice the workgroups, which spread the GELU work evenly over the CUs.  U and V are accumulated exactly as a 16 x 16
 // tile product over the 2r values [hi(z) | lo(z)] in k order, the hi and lo
 // halves meeting the same W1 columns.
-template <int R, int KT>
-__global__ __launch_bounds__(256, KT > 2 ? 4 : 5) void mlp_kernel(MlpArgs a) {
+template <int R, int KT, int NP>
+__global__ __launch_bounds__(256, KT > 2 ? 4 : (NP == 1 ? 7 : 5)) void mlp_kernel(MlpArgs a) {
     constexpr int KS = 2 * R / 32;          // 32-wide k-steps over [hi | lo]
     constexpr int KD = R >= 32 ? R / 32 : 1;  // distinct W1 fragments (hi and lo share them)
     constexpr int ZSEG = 2 * R / 8;         // 16-byte segments per z row
     const int tid = threadIdx.x;
     const int B = a.B, K = a.K, h = a.h;
     const int nj = (h + kJB - 1) / kJB;
-    const int G = B / 2;                    // pair groups per request: ceil((B - 1) / 2)
+    const int G = (B - 1 + NP - 1) / NP;    // pair groups per request
     // Consecutive workgroup numbers go to different XCDs (round-robin over 8):
     // the hidden blocks of one group are numbered 8 apart so they share an XCD.
     const int lin = blockIdx.x;
@@ -92,8 +93,8 @@ __global__ __launch_bounds__(256, KT > 2 ? 4 : 5) void mlp_kernel(MlpArgs a) {
     const int jblk = i8 % nj;
     const int grp = (i8 / nj) * 8 + xcd;
     if (grp >= a.n * G) return;
-    const int req = grp / G, p0 = 2 * (grp % G);
-    const int np = min(2, B - 1 - p0);      // pairs in this group
+    const int req = grp / G, p0 = NP * (grp % G);
+    const int np = min(NP, B - 1 - p0);     // pairs in this group
     const int pair0 = req * (B - 1) + p0;
     const int64_t t0 = static_cast<int64_t>(req) * B + p0;   // slot row of the first pair's predecessor
     const int j0 = jblk * kJB;
@@ -103,16 +104,16 @@ __global__ __launch_bounds__(256, KT > 2 ? 4 : 5) void mlp_kernel(MlpArgs a) {
     const int l = tid & 63, wave = tid >> 6;
 
     __shared__ __attribute__((aligned(16))) float w2s[kJB];
-    __shared__ __attribute__((aligned(16))) float sps[2][R];    // the pair states s_p
-    __shared__ float cps4[2][4][kJB];   // c_p partial dots, one per quarter of r
+    __shared__ __attribute__((aligned(16))) float sps[NP][R];   // the pair states s_p
+    __shared__ float cps4[NP][4][kJB];  // c_p partial dots, one per quarter of r
     __shared__ float lv[3 * 64];        // the candidates' logits l of slots t0 .. t0 + np (K <= 64)
     // First the z rows of the group's slots t0 .. t0 + np ([(np + 1) K][2r]
     // bf16, segments permuted by zpos); once the U | V products are formed,
-    // the same memory holds P [2][K][PS] and Q [2][K][PS].
+    // the same memory holds P [NP][K][PS] and Q [NP][K][PS].
     extern __shared__ __attribute__((aligned(16))) float dyn[];
     uint16_t* zs = reinterpret_cast<uint16_t*>(dyn);
     float* Pb = dyn;
-    float* Qb = dyn + 2 * K * PS;
+    float* Qb = dyn + NP * K * PS;
 
     // ---- z rows straight into LDS (no registers held while in flight):
     // the slots' rows are contiguous in zhl.  A wave instruction moves 64
@@ -195,11 +196,11 @@ __global__ __launch_bounds__(256, KT > 2 ? 4 : 5) void mlp_kernel(MlpArgs a) {
 
     // ---- U | V tiles on MFMA (lane l holds rows 4 (l/16) + i, unit l % 16
     // of a 16 x 16 tile): U of pair i from slot t0 + i, V from slot t0 + i + 1
-    f32x4 accu[2][KT], accv[2][KT];
+    f32x4 accu[NP][KT], accv[NP][KT];
     if (wave_on) {
         const int kq = 8 * (l >> 4);
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < NP; ++i)
 #pragma unroll
             for (int rt = 0; rt < KT; ++rt) {
                 accu[i][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -228,7 +229,7 @@ __global__ __launch_bounds__(256, KT > 2 ? 4 : 5) void mlp_kernel(MlpArgs a) {
     if (wave_on) {
         const int jc = 16 * wave + (l & 15);            // column in P / Q
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < NP; ++i) {
             if (i >= np) break;
             const float cp = ((cps4[i][0][jl] + cps4[i][1][jl]) + (cps4[i][2][jl] + cps4[i][3][jl])) + b1j;
             float* P = Pb + i * K * PS;
@@ -301,22 +302,25 @@ __global__ __launch_bounds__(256, KT > 2 ? 4 : 5) void mlp_kernel(MlpArgs a) {
 
 int mlp_blocks(int h) { return (h + kJB - 1) / kJB; }
 
+// Pairs per MLP workgroup.
+constexpr int kMlpPairs = 2;
+
 size_t mlp_lds_bytes(int K, int r) {
-    // z rows of three slots, or P and Q of two pairs, whichever is larger
-    const size_t z = static_cast<size_t>(3) * K * 2 * r * sizeof(uint16_t);
-    const size_t pq = static_cast<size_t>(4) * K * (kJB + 4) * sizeof(float);
+    // z rows of the group's slots, or P and Q of its pairs, whichever is larger
+    const size_t z = static_cast<size_t>(kMlpPairs + 1) * K * 2 * r * sizeof(uint16_t);
+    const size_t pq = static_cast<size_t>(2 * kMlpPairs) * K * (kJB + 4) * sizeof(float);
     return z > pq ? z : pq;
 }
 
 template <int R>
 hipError_t launch_mlp_r(const MlpArgs& a, dim3 grid, uint32_t lds, hipStream_t stream) {
-    if (a.K <= 16) return launch(mlp_kernel<R, 1>, grid, 256, lds, stream, a);
-    if (a.K <= 32) return launch(mlp_kernel<R, 2>, grid, 256, lds, stream, a);
-    return launch(mlp_kernel<R, 4>, grid, 256, lds, stream, a);
+    if (a.K <= 16) return launch(mlp_kernel<R, 1, kMlpPairs>, grid, 256, lds, stream, a);
+    if (a.K <= 32) return launch(mlp_kernel<R, 2, kMlpPairs>, grid, 256, lds, stream, a);
+    return launch(mlp_kernel<R, 4, kMlpPairs>, grid, 256, lds, stream, a);
 }
 
 hipError_t launch_mlp(const MlpArgs& a, hipStream_t stream) {
-    const int groups = a.n * (a.B / 2);   // pairs taken two at a time per request
+    const int groups = a.n * ((a.B - 1 + kMlpPairs - 1) / kMlpPairs);
     const dim3 grid(static_cast<unsigned>((groups + 7) / 8 * 8 * mlp_blocks(a.h)));
     const uint32_t lds = static_cast<uint32_t>(mlp_lds_bytes(a.K, a.r));
     switch (a.r) {
