@@ -48,6 +48,18 @@ def test_tiny_pair_counts(B, n):
     P.check_all(gpu, ora, "tiny/B=%d/n=%d" % (B, n))
 
 
+@pytest.mark.parametrize("de", [96, 1056, 2080])
+def test_tiny_embed_widths(de):
+    """Candidate projections whose k-split ends in a half 64-deep slab (d_e =
+    96: one split; 1056: one split of 16.5 slabs; 2080: two splits of 1056 and
+    1024), over a ragged last tile of gathered rows (n B K = 60)."""
+    _log("tiny d_e=%d" % de)
+    x = P.inputs("tiny", head="stress", de=de, n=3, B=5)
+    gpu = P.gpu_run(x)
+    ora = P.oracle_run(x)
+    P.check_all(gpu, ora, "tiny/de=%d" % de)
+
+
 @pytest.mark.parametrize("sigma", [1.0, 8.0])
 def test_tiny_cosine(sigma):
     _log("tiny cosine sigma=%g" % sigma)
