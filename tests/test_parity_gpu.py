@@ -48,6 +48,17 @@ def test_tiny_pair_counts(B, n):
     P.check_all(gpu, ora, "tiny/B=%d/n=%d" % (B, n))
 
 
+@pytest.mark.parametrize("K", [37, 64])
+def test_tiny_wide_k(K):
+    """K = 37 (three 16-row tiles, the last ragged, in the MLP's U | V
+    products; odd logit rows) and K = 64 (four tiles)."""
+    _log("tiny K=%d" % K)
+    x = P.inputs("tiny", head="stress", K=K, n=2, B=4)
+    gpu = P.gpu_run(x)
+    ora = P.oracle_run(x)
+    P.check_all(gpu, ora, "tiny/K=%d" % K)
+
+
 @pytest.mark.parametrize("de", [96, 1056, 2080])
 def test_tiny_embed_widths(de):
     """Candidate projections whose k-split ends in a half 64-deep slab (d_e =
