@@ -48,6 +48,17 @@ def test_tiny_pair_counts(B, n):
     P.check_all(gpu, ora, "tiny/B=%d/n=%d" % (B, n))
 
 
+@pytest.mark.parametrize("r", [32, 64])
+def test_tiny_rep_widths(r):
+    """Representation widths r = 32 and 64 (the other compiled instances of
+    the candidate and MLP kernels)."""
+    _log("tiny r=%d" % r)
+    x = P.inputs("tiny", head="stress", r=r, n=2, B=4)
+    gpu = P.gpu_run(x)
+    ora = P.oracle_run(x)
+    P.check_all(gpu, ora, "tiny/r=%d" % r)
+
+
 @pytest.mark.parametrize("K", [37, 64])
 def test_tiny_wide_k(K):
     """K = 37 (three 16-row tiles, the last ragged, in the MLP's U | V
