@@ -39,9 +39,12 @@
  *
  * Precision: every input is read from its stored bits (bfloat16 widened
  * exactly, or float32); all arithmetic is double precision, with dot products
- * accumulated in index order.  Parity of every function here is pinned by the
- * CPU test suite (brute force, closed forms and special cases); nothing here
- * is "parity unpinned".
+ * accumulated in index order.  Every function here is pinned by the CPU test
+ * suite to something other than itself (brute force, closed forms, special
+ * cases, hand-worked examples).  One rule is a reading rather than a formula
+ * of the pages: the Geometric path (a lambda^p-discounted sum, named by the
+ * DCOCO page's path-rule table without a formula) is pinned to that reading,
+ * but whether the reading is the page's rule is parity unpinned.
  */
 #include <math.h>
 #include <stdint.h>

@@ -704,6 +704,53 @@ def test_yield_worked_example():
     assert oracle.iid_expected_yield(1.0, 15) == 16.0
 
 
+def test_accepted_prefix_hand_worked():
+    """Greedy verification (Faster Decoding, "Verification can be parallel even
+    when generation is sequential"): the verifier accepts draft positions in
+    order until the first mismatch, so A is the length of the leading run of
+    matches, not the number of matching positions.  Each expected value below
+    is worked by hand from that definition."""
+    T = lambda *rows: np.array(rows, dtype=np.int32)  # noqa: E731
+    cases = [
+        # (tokens, targets, A)
+        ([5, 11, 7, 9], [5, 12, 7, 9], 1),      # a later run of matches after a miss does not count
+        ([5, 11, 7, 9], [5, 11, 7, 9], 4),      # every position accepted: A = B
+        ([4, 11, 7, 9], [5, 11, 7, 9], 0),      # the first position misses
+        ([5, 11, 7, 9], [5, 11, 7, 8], 3),      # only the last misses
+        ([5, 11, 7, 9], [5, 11, 3, 9], 2),      # a miss in the middle
+        ([1, 2, 3, 4], [-1, 2, 3, 4], 0),       # an out-of-pool target (-1) never matches
+    ]
+    for tok, tgt, want in cases:
+        got = oracle.accepted_lengths(T(tok), T(tgt))
+        assert got.tolist() == [want], (tok, tgt, got, want)
+    # all six as one batch: each block is judged on its own row
+    got = oracle.accepted_lengths(T(*[c[0] for c in cases]), T(*[c[1] for c in cases]))
+    assert got.tolist() == [c[2] for c in cases]
+    # B = 1 and empty batches
+    assert oracle.accepted_lengths(T([3]), T([3])).tolist() == [1]
+    assert oracle.accepted_lengths(T([3]), T([2])).tolist() == [0]
+    assert oracle.accepted_lengths(np.zeros((0, 4), np.int32), np.zeros((0, 4), np.int32)).size == 0
+
+
+def test_accepted_prefix_brute_force():
+    """Against a different formulation of the same definition: A is the
+    largest k such that the first k positions all match, found by trying every
+    k from B down to 0 on random token rows with planted mismatches."""
+    rng = np.random.default_rng(7)
+    n, B = 400, 15
+    targets = rng.integers(0, 6, size=(n, B)).astype(np.int32)
+    tokens = targets.copy()
+    flip = rng.random((n, B)) < 0.15
+    tokens[flip] += 1
+    got = oracle.accepted_lengths(tokens, targets)
+    for i in range(n):
+        want = max(k for k in range(B + 1) if (tokens[i, :k] == targets[i, :k]).all())
+        assert got[i] == want
+    # a sample where matches after the first miss are common, so a count of
+    # matching positions would disagree with the prefix length
+    assert ((tokens == targets).sum(axis=1) != got).sum() > n // 4
+
+
 def test_yield_tail_sum_identity_on_walks():
     """Sum over blocks of Y = A + 1 equals n + sum_k #{A >= k}: E[Y] = 1 + sum_k s_k
     holds exactly on any sample (mixed accepted-prefix lengths in one batch)."""
