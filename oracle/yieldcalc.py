@@ -1,10 +1,12 @@
 """Expected token yield of one draft-verify cycle.
 
 Faster Decoding, "Verification can be parallel even when generation is
-sequential": with s_k the probability that the first k draft positions are
-all accepted, a cycle that emits the accepted prefix plus one corrected or
-bonus token yields E[Y] = 1 + sum_{k=1..gamma} s_k; with a constant
-conditional acceptance probability alpha this is sum_{k=0..gamma} alpha^k.
+sequential": s_k, the probability that the first k draft positions are all
+accepted, is the product of the first k conditional acceptance probabilities;
+a cycle emits the accepted prefix plus one corrected or bonus token, so its
+expected yield is E[Y] = 1 + sum_{k=1..gamma} s_k.  With a constant
+conditional acceptance alpha the sum is geometric:
+E[Y] = (1 - alpha^(gamma+1)) / (1 - alpha), and gamma + 1 at alpha = 1.
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 """
@@ -13,21 +15,24 @@ from __future__ import annotations
 
 from typing import Sequence
 
+import numpy as np
+
 
 def survival(conditional: Sequence[float]) -> list:
-    """Prefix survival s_k = product of the first k conditional acceptances."""
-    out, alive = [], 1.0
-    for p in conditional:
-        alive *= float(p)
-        out.append(alive)
-    return out
+    """Prefix survival s_1..s_gamma: cumulative products of the conditional
+    acceptance probabilities."""
+    return np.cumprod(np.asarray(conditional, dtype=np.float64)).tolist()
 
 
 def expected_yield(conditional: Sequence[float]) -> float:
     """E[Y] = 1 + sum_k s_k."""
-    return 1.0 + sum(survival(conditional))
+    return 1.0 + float(np.sum(survival(conditional)))
 
 
 def iid_expected_yield(alpha: float, gamma: int) -> float:
-    """E[Y] under a constant conditional acceptance alpha: sum_{k=0..gamma} alpha^k."""
-    return sum(float(alpha) ** k for k in range(gamma + 1))
+    """E[Y] for a constant conditional acceptance alpha over gamma positions:
+    the geometric series 1 + alpha + ... + alpha^gamma in closed form."""
+    alpha = float(alpha)
+    if alpha == 1.0:
+        return float(gamma + 1)
+    return (1.0 - alpha ** (gamma + 1)) / (1.0 - alpha)
