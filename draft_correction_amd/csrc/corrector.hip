@@ -7,6 +7,7 @@
 #include <mutex>
 #include <new>
 #include <string.h>
+#include <unordered_set>
 
 #include "../../include/corrector.h"
 #include "kernels.h"
@@ -23,8 +24,6 @@ thread_local LaunchTiming g_launch_timing;
 
 namespace {
 
-constexpr uint32_t kMagic = 0xC0FFEE17u;
-constexpr uint32_t kDead = 0xDEADDEADu;
 constexpr int kMaxKernels = 12;
 constexpr size_t kAlign = 256;
 
@@ -36,7 +35,6 @@ struct Layout {
 }  // namespace
 
 struct corrector {
-    uint32_t magic;
     corrector_desc d;
     corrector_weights w;
     bool timing;
@@ -110,7 +108,22 @@ T* at(void* ws, size_t off) {
     return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
-bool live(const corrector* h) { return h && h->magic == kMagic; }
+// Handles of live correctors.  A handle is checked against this set before
+// anything reads through it, so a destroyed handle is rejected without its
+// freed memory being touched.  (A later corrector_create may reuse the
+// address; the stale pointer then names the new corrector, as with any
+// pointer handle.)
+std::mutex g_live_mu;
+std::unordered_set<const corrector*>& live_set() {
+    static std::unordered_set<const corrector*>* s = new std::unordered_set<const corrector*>();
+    return *s;
+}
+
+bool live(const corrector* h) {
+    if (!h) return false;
+    std::lock_guard<std::mutex> lock(g_live_mu);
+    return live_set().count(h) != 0;
+}
 
 int check_n(const corrector* h, int32_t n) {
     if (!live(h)) return CORR_E_HANDLE;
@@ -433,22 +446,33 @@ int corrector_create(const corrector_desc* desc, const corrector_weights* wt, co
 
     corrector* h = new (std::nothrow) corrector();
     if (!h) return CORR_E_SHAPE;
-    h->magic = kMagic;
     h->d = d;
     h->w = w;
     h->timing = false;
     h->events_ready = false;
     h->nk = 0;
     h->table = nullptr;
+    try {
+        std::lock_guard<std::mutex> lock(g_live_mu);
+        live_set().insert(h);
+    } catch (...) {
+        delete h;
+        return CORR_E_SHAPE;
+    }
     *out = h;
     return CORR_OK;
 }
 
 void corrector_destroy(corrector* h) {
-    if (!live(h)) return;
+    if (!h) return;
+    {
+        // unregister first: a second destroy (or any later call) with this
+        // handle is rejected without reading *h
+        std::lock_guard<std::mutex> lock(g_live_mu);
+        if (live_set().erase(h) == 0) return;
+    }
     if (h->events_ready)
         for (hipEvent_t& e : h->ev) (void)hipEventDestroy(e);
-    h->magic = kDead;
     delete h;
 }
 

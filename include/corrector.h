@@ -27,7 +27,8 @@
  * Conventions shared by every call
  *   - Every data pointer is a DEVICE pointer owned by the caller.  The library
  *     never allocates device memory, never synchronises and keeps no global
- *     state, so a sequence of calls can be captured into a HIP graph.
+ *     device state, so a sequence of calls can be captured into a HIP graph.
+ *     Its one process-wide host structure is the registry of live handles.
  *   - `stream` is a hipStream_t passed as void* (NULL = default stream).  All
  *     work is enqueued on it and the call returns without waiting.
  *   - Return value: CORR_OK (0) or a positive corrector_status.  It reports
@@ -66,7 +67,8 @@ typedef enum {
     CORR_E_ALIGN = 4,       /* a pointer or stride breaks an alignment rule */
     CORR_E_WORKSPACE = 5,   /* the workspace is smaller than required */
     CORR_E_HIP = 6,         /* a HIP launch or runtime call failed */
-    CORR_E_HANDLE = 7       /* the handle is not a live corrector */
+    CORR_E_HANDLE = 7       /* the handle is not a live corrector (never created,
+                               or already destroyed) */
 } corrector_status;
 
 enum { CORR_VARIANT_MLP = 0, CORR_VARIANT_COSINE = 1 };
@@ -184,7 +186,13 @@ typedef struct corrector corrector;
 int corrector_create(const corrector_desc *desc, const corrector_weights *weights,
                      corrector **out);
 
-/* Free the handle (host memory only).  NULL is ignored. */
+/* Free the handle (host memory only).  NULL, and a handle that is not live
+ * (for example one already destroyed), are ignored.  Live handles are kept in
+ * a registry: every call given a destroyed handle returns CORR_E_HANDLE (0
+ * for the size queries) without reading the freed handle, unless a later
+ * corrector_create has returned the same address, in which case the pointer
+ * names that new corrector.  Destroying a handle while a call on it is in
+ * progress on another thread is a caller error. */
 void corrector_destroy(corrector *h);
 
 /* Bytes of device workspace every call on `h` needs for n_req requests

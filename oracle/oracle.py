@@ -16,6 +16,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# A prebuilt variant of the same source (the sanitizer build of the tests) is
+# loaded instead when this names it; it is then never rebuilt here.
+_LIB_OVERRIDE = os.environ.get("DRAFT_ORACLE_LIB")
 
 _lib = None
 
@@ -46,9 +49,12 @@ class _Weights(C.Structure):
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build(force=True)
-        lib = C.CDLL(_LIB)
+        if _LIB_OVERRIDE:
+            lib = C.CDLL(_LIB_OVERRIDE)
+        else:
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build(force=True)
+            lib = C.CDLL(_LIB)
         P = C.c_void_p
         lib.oracle_param_count.restype = C.c_int64
         lib.oracle_param_count.argtypes = [P]
