@@ -219,21 +219,171 @@ def measure_ceilings(steps: int = 20) -> dict:
     return out
 
 
-def cpu_baseline(cfg, inputs, min_seconds: float = 12.0, max_passes: int = 64) -> dict:
+def _median_pass_seconds(cfg, inputs, n: int, reps: int = 3) -> float:
+    import oracle
+    ts = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        oracle.run(cfg, inputs, n=n)
+        ts.append(time.perf_counter() - t0)
+    return float(np.median(ts))
+
+
+def cpu_baseline(cfg, inputs, single_blocks: int = 4) -> dict:
+    """The CPU oracle on the host cores: the median of 3 full passes over the
+    batch with every OpenMP thread, and the median of 3 passes over its first
+    `single_blocks` blocks with one thread (the oracle's cost is linear in the
+    blocks of a pass)."""
     import oracle
     oracle.build(force=False)
     threads = oracle.get_threads()
     n = cfg["n"]
-    passes, t0 = 0, time.perf_counter()
-    while True:
-        oracle.run(cfg, inputs)
-        passes += 1
-        el = time.perf_counter() - t0
-        if el >= min_seconds or passes >= max_passes:
-            break
-    return {"value": passes * n / el, "unit": "blocks/s", "cores": threads, "kind": "oracle",
-            "sample": "%d full pass(es) of the CPU oracle over one %d-block batch of the same workload "
-                      "(%.1f s, %d OpenMP threads)" % (passes, n, el, threads)}
+    t_all = _median_pass_seconds(cfg, inputs, n)
+    oracle.set_threads(1)
+    try:
+        ns = min(single_blocks, n)
+        t_one = _median_pass_seconds(cfg, inputs, ns)
+    finally:
+        oracle.set_threads(threads)
+    cpu = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
+    return {"value": n / t_all, "unit": "blocks/s", "cores": threads, "kind": "oracle",
+            "sample": "median of 3 full passes of the CPU oracle over one %d-block batch of the same workload "
+                      "(%.2f s each, %d OpenMP threads)" % (n, t_all, threads),
+            "single_thread": {"value": round(ns / t_one, 3), "unit": "blocks/s", "cores": 1,
+                              "sample": "median of 3 passes over the first %d blocks of the batch, one thread "
+                                        "(%.2f s each)" % (ns, t_one)},
+            "cpu_model": cpu}
+
+
+def measure_pass(corr, cfg, dev_sets, st, stream, steps: int, warmup: int) -> dict:
+    """Back-to-back corrector_run passes over the rotated input sets: the
+    pass time over exactly `steps` passes (HIP events around the whole
+    region), then per-kernel durations from the library's kernel-stamped
+    events over the same number of passes."""
+    import torch
+    n, B = cfg["n"], cfg["B"]
+    tokens = torch.empty((n, B), dtype=torch.int32, device="cuda")
+    ws = corr.new_workspace(n)
+
+    def step(i):
+        s = dev_sets[i % len(dev_sets)]
+        corr.run(n, s["logits"], st["l_req"], st["l_slot"], s["hidden"], st["h_req"], st["h_slot"],
+                 tokens, ws, l_offset=st["l_off"], h_offset=st["h_off"], stream=stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    corr.set_timing(True)
+    per = {}
+    for i in range(steps):
+        step(i)
+        for name, t in corr.kernel_times():
+            per.setdefault(name, []).append(t)
+    corr.set_timing(False)
+    torch.cuda.synchronize()
+    return {"ms": ms, "kernels_ms": {k: float(np.mean(v)) for k, v in per.items()}}
+
+
+def measure_graph(corr, cfg, dev_sets, st, stream, steps: int, warmup: int) -> dict:
+    """The same pass captured into graphs (one per rotated input set, each
+    capturing one corrector_run on that set's buffers) and replayed `steps`
+    times back to back: the pass time without per-launch host work."""
+    import torch
+    n, B = cfg["n"], cfg["B"]
+    tokens = torch.empty((n, B), dtype=torch.int32, device="cuda")
+    ws = corr.new_workspace(n)
+    s0 = dev_sets[0]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        corr.run(n, s0["logits"], st["l_req"], st["l_slot"], s0["hidden"], st["h_req"], st["h_slot"], tokens, ws,
+                 l_offset=st["l_off"], h_offset=st["h_off"], stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for s in dev_sets:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            corr.run(n, s["logits"], st["l_req"], st["l_slot"], s["hidden"], st["h_req"], st["h_slot"], tokens, ws,
+                     l_offset=st["l_off"], h_offset=st["h_off"])
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    cur = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(cur)
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    e1.record(cur)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del graphs
+    return {"us": round(ms * 1e3, 3), "value": round(n / (ms / 1e3), 1),
+            "note": "one graph per rotated input set, each capturing one corrector_run; replays back to back"}
+
+
+def roofline_of(work: dict, name: str, ms: float, traffic=None) -> dict:
+    wk = work[name]
+    t_s = ms / 1e3
+    if wk["bound"] == "mfma":
+        achieved, peak, unit = wk["flops"] / t_s / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+    elif wk["bound"] == "alu":
+        achieved, peak, unit = wk["gelu"] / t_s / 1e12, PEAK_GELU_T, "T GELU/s"
+    else:
+        achieved, peak, unit = wk["bytes"] / t_s / 1e9, PEAK_HBM_GBS, "GB/s"
+    return {"bound": wk["bound"], "achieved": round(achieved, 2), "peak": round(peak, 3), "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": name, "kernel_us": round(ms * 1e3, 3)}
+
+
+def kernel_table(work: dict, kms: dict) -> dict:
+    kernels = {}
+    for k, v in kms.items():
+        wkk = work.get(k, {})
+        ent = {"us": round(v * 1e3, 3)}
+        if "bytes" in wkk:
+            ent["GB/s"] = round(wkk["bytes"] / (v / 1e3) / 1e9, 1)
+        if "flops" in wkk:
+            ent["TFLOP/s"] = round(wkk["flops"] / (v / 1e3) / 1e12, 2)
+        if "gelu" in wkk:
+            ent["T GELU/s"] = round(wkk["gelu"] / (v / 1e3) / 1e12, 3)
+        kernels[k] = ent
+    return kernels
+
+
+def load_workload(name: str, copies: int, args, head: str):
+    """Synthetic inputs of a named workload (several independent input sets),
+    weights and the embedding table, on the device."""
+    from draft_correction_amd import device
+    from workload import config
+    from workload.gen import gen_embed, gen_hidden, gen_logits, gen_weights
+    cfg = config(name, path_rule=args.path_rule, path_lambda=args.path_lambda, beam_width=args.beam_width,
+                 succ_top_m=args.top_m)
+    t0 = time.perf_counter()
+    embed = gen_embed(cfg)
+    weights = gen_weights(cfg, head=head)
+    sets = []
+    for c in range(copies):
+        cc = dict(cfg, seed=c)
+        sets.append(dict(logits=gen_logits(cc), hidden=gen_hidden(cc)))
+    log("generated %s inputs (%d copies) in %.1f s" % (name, copies, time.perf_counter() - t0))
+    dev_w = device.weights_to_device(weights, embed)
+    dev_sets = [dict(logits=device.tensor(s["logits"]), hidden=device.tensor(s["hidden"])) for s in sets]
+    corr = device.make_corrector(cfg, dict(weights=dev_w), max_requests=cfg["n"])
+    return cfg, corr, dev_sets, sets, weights, embed, dev_w
 
 
 def main():
@@ -252,6 +402,8 @@ def main():
     ap.add_argument("--top-m", type=int, default=0,
                     help="score only the first m successors of each predecessor (0: all K)")
     ap.add_argument("--no-fold", action="store_true", help="skip the folded-table measurement")
+    ap.add_argument("--no-b1", action="store_true", help="skip the batch-1 measurement")
+    ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay measurements")
     ap.add_argument("--ceilings", action="store_true",
                     help="also measure the box's copy and large-GEMM ceilings (reference figures)")
     ap.add_argument("--no-softmax", action="store_true",
@@ -267,36 +419,12 @@ def main():
 
     import torch
     from draft_correction_amd import device
-    from workload import config
-    from workload.gen import gen_embed, gen_hidden, gen_logits, gen_weights
-
-    cfg = config(args.workload, path_rule=args.path_rule, path_lambda=args.path_lambda, beam_width=args.beam_width,
-                 succ_top_m=args.top_m)
-    n = cfg["n"]
-    log("generating %s inputs (%d copies)" % (args.workload, args.copies))
-    t0 = time.perf_counter()
-    embed = gen_embed(cfg)
-    weights = gen_weights(cfg, head=args.head)
-    sets = []
-    for c in range(args.copies):
-        cc = dict(cfg, seed=c)
-        sets.append(dict(logits=gen_logits(cc), hidden=gen_hidden(cc)))
-    log("generated in %.1f s" % (time.perf_counter() - t0))
 
     torch.cuda.set_device(0)
-    dev_w = device.weights_to_device(weights, embed)
-    dev_sets = [dict(logits=device.tensor(s["logits"]), hidden=device.tensor(s["hidden"])) for s in sets]
-    corr = device.make_corrector(cfg, dict(weights=dev_w), max_requests=n)
+    cfg, corr, dev_sets, sets, weights, embed, dev_w = load_workload(args.workload, args.copies, args, args.head)
+    n, B, K = cfg["n"], cfg["B"], cfg["K"]
     st = device.strides(cfg)
-    B, K = cfg["B"], cfg["K"]
-    tokens = torch.empty((n, B), dtype=torch.int32, device="cuda")
-    ws = corr.new_workspace(n)
     stream = torch.cuda.current_stream()
-
-    def step(i):
-        s = dev_sets[i % len(dev_sets)]
-        corr.run(n, s["logits"], st["l_req"], st["l_slot"], s["hidden"], st["h_req"], st["h_slot"],
-                 tokens, ws, l_offset=st["l_off"], h_offset=st["h_off"], stream=stream)
 
     if args.calibrate_copy:
         nb = args.calibrate_copy << 20
@@ -307,33 +435,20 @@ def main():
         torch.cuda.synchronize()
         log("copy calibration: %d bytes read, %d bytes written" % (nb, nb))
         del src, dst
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    # ---- timed region: exactly `steps` passes
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
-    log("pass: %.2f us (%d steps)" % (ms * 1e3, args.steps))
 
-    # ---- per-kernel durations: HIP events recorded by the library around each
-    # of its launches on the same stream, over the same number of passes
-    corr.set_timing(True)
-    per = {}
-    for i in range(args.steps):
-        step(i)
-        for name, t in corr.kernel_times():
-            per.setdefault(name, []).append(t)
-    corr.set_timing(False)
-    torch.cuda.synchronize()
-    avg = {k: float(np.mean(v)) for k, v in per.items()}
+    # ---- timed region: exactly `steps` passes, then per-kernel durations
+    # (HIP events stamped by the library around each of its launches, on the
+    # same stream, over the same number of passes)
+    main_pass = measure_pass(corr, cfg, dev_sets, st, stream, args.steps, args.warmup)
+    ms, avg = main_pass["ms"], main_pass["kernels_ms"]
+    log("pass: %.2f us (%d steps)" % (ms * 1e3, args.steps))
     for k, v in avg.items():
-        log("  %-14s %8.2f us" % (k, v * 1e3))
+        log("  %-16s %8.2f us" % (k, v * 1e3))
+
+    graph = None
+    if not args.no_graph:
+        graph = measure_graph(corr, cfg, dev_sets, st, stream, args.steps, args.warmup)
+        log("graph-replayed pass: %.2f us" % graph["us"])
 
     # ---- the same pass with the folded candidate projection (E W_cand^T
     # tabulated once; the table is computed outside the timed region)
@@ -342,30 +457,14 @@ def main():
         table = torch.empty(corr.table_bytes() // 4, dtype=torch.float32, device="cuda")
         corr.fold_table(table, stream=stream)
         corr.use_table(table)
-        for i in range(args.warmup):
-            step(i)
-        torch.cuda.synchronize()
-        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        f0.record(stream)
-        for i in range(args.steps):
-            step(i)
-        f1.record(stream)
-        torch.cuda.synchronize()
-        fms = f0.elapsed_time(f1) / args.steps
-        corr.set_timing(True)
-        fper = {}
-        for i in range(args.steps):
-            step(i)
-            for name, t in corr.kernel_times():
-                fper.setdefault(name, []).append(t)
-        corr.set_timing(False)
+        fp = measure_pass(corr, cfg, dev_sets, st, stream, args.steps, args.warmup)
         corr.use_table(None)
         torch.cuda.synchronize()
-        folded = {"value": round(n / (fms / 1e3), 1), "ms_per_step": round(fms, 5),
-                  "kernels_us": {k: round(float(np.mean(v)) * 1e3, 3) for k, v in fper.items()},
+        folded = {"value": round(n / (fp["ms"] / 1e3), 1), "ms_per_step": round(fp["ms"], 5),
+                  "kernels_us": {k: round(v * 1e3, 3) for k, v in fp["kernels_ms"].items()},
                   "note": "candidate projection gathers rows of the folded table E W_cand^T "
                           "(computed once, outside the timed region)"}
-        log("folded pass: %.2f us" % (fms * 1e3))
+        log("folded pass: %.2f us" % (fp["ms"] * 1e3))
         del table
 
     fused_softmax = None
@@ -377,14 +476,6 @@ def main():
 
     work = algorithmic_work(cfg, n)
     dom = max(avg, key=avg.get)
-    wk = work[dom]
-    t_s = avg[dom] / 1e3
-    if wk["bound"] == "mfma":
-        achieved, peak, unit = wk["flops"] / t_s / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
-    elif wk["bound"] == "alu":
-        achieved, peak, unit = wk["gelu"] / t_s / 1e12, PEAK_GELU_T, "T GELU/s"
-    else:
-        achieved, peak, unit = wk["bytes"] / t_s / 1e9, PEAK_HBM_GBS, "GB/s"
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
@@ -392,18 +483,29 @@ def main():
         ent = tr.get("kernels", {}).get(dom)
         if ent and tr.get("source_hash") == kernel_source_hash() and tr.get("workload") == args.workload:
             traffic = ent.get("bytes_per_launch")
-    roof = {"bound": wk["bound"], "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-            "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": dom,
-            "kernel_us": round(avg[dom] * 1e3, 3)}
-    kernels = {}
-    for k, v in avg.items():
-        wkk = work.get(k, {})
-        ent = {"us": round(v * 1e3, 3)}
-        if "bytes" in wkk:
-            ent["GB/s"] = round(wkk["bytes"] / (v / 1e3) / 1e9, 1)
-        if "flops" in wkk:
-            ent["TFLOP/s"] = round(wkk["flops"] / (v / 1e3) / 1e12, 2)
-        kernels[k] = ent
+    roof = roofline_of(work, dom, avg[dom], traffic)
+    roof_mlp = roofline_of(work, "mlp", avg["mlp"]) if "mlp" in avg else None
+    kernels = kernel_table(work, avg)
+
+    # ---- batch 1 (the pages' concurrency-1 serving point), same run
+    b1 = None
+    if not args.no_b1 and args.workload != "b1":
+        del dev_sets
+        torch.cuda.empty_cache()
+        cfg1, corr1, dev1, _, _, _, _ = load_workload("b1", args.copies, args, args.head)
+        st1 = device.strides(cfg1)
+        p1 = measure_pass(corr1, cfg1, dev1, st1, stream, args.steps, args.warmup)
+        work1 = algorithmic_work(cfg1, 1)
+        b1 = {"value": round(1 / (p1["ms"] / 1e3), 1), "unit": "blocks/s", "ms_per_step": round(p1["ms"], 5),
+              "us": round(p1["ms"] * 1e3, 3), "kernels": kernel_table(work1, p1["kernels_ms"]),
+              "config": {"workload": "b1: 1 request x %d drafted slots (+anchor), V=%d, K=%d, d=%d, r=%d"
+                                     % (cfg1["B"], cfg1["V"], cfg1["K"], cfg1["d"], cfg1["r"])}}
+        log("b1 pass: %.2f us" % b1["us"])
+        if not args.no_graph:
+            b1["graph"] = measure_graph(corr1, cfg1, dev1, st1, stream, args.steps, args.warmup)
+            log("b1 graph-replayed pass: %.2f us" % b1["graph"]["us"])
+        corr1.close()
+        del dev1
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -434,8 +536,11 @@ def main():
                                + (", top-%d successors scored" % args.top_m if 0 < args.top_m < cfg["K"] else ""),
                    "global_batch": n, "rotating_input_sets": args.copies},
         "roofline": roof,
+        "roofline_mlp": roof_mlp,
         "kernels": kernels,
         "cpu_baseline": cpu,
+        "b1": b1,
+        "graph": graph,
         "folded_table": folded,
         "fused_softmax": fused_softmax,
     }

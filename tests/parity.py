@@ -97,6 +97,42 @@ def gpu_run(x: dict, n: int | None = None, first: int = 0, reps: int = 1, fold: 
     return out
 
 
+def gpu_chain(x: dict, n: int | None = None, first: int = 0, fold: bool = False) -> dict:
+    """The pass as three C-ABI calls on one workspace: corrector_topk, then
+    corrector_score on its ids and values, then corrector_walk on those
+    scores; outputs as from gpu_run.  With fold=True a folded table is
+    attached, so corrector_score gathers its rows."""
+    cfg = x["cfg"]
+    dev = dev_inputs(x)
+    n = cfg["n"] - first if n is None else n
+    corr = device.make_corrector(cfg, dev, max_requests=max(n, 1))
+    if fold:
+        table = torch.empty(corr.table_bytes() // 4, dtype=torch.float32, device="cuda")
+        corr.fold_table(table)
+        corr.use_table(table)
+    st = device.strides(cfg)
+    B, K, r = cfg["B"], cfg["K"], cfg["r"]
+    ids = torch.empty((n, B, K), dtype=torch.int32, device="cuda")
+    vals = torch.empty((n, B, K), dtype=torch.float32, device="cuda")
+    scores = torch.empty((n, max(B - 1, 0), K, K), dtype=torch.float32, device="cuda")
+    tokens = torch.empty((n, B), dtype=torch.int32, device="cuda")
+    choice = torch.empty((n, B), dtype=torch.int32, device="cuda")
+    ws = corr.new_workspace(n)
+    corr.topk(n, dev["logits"], st["l_req"], st["l_slot"], ids, vals, ws, offset=st["l_off"] + first * st["l_req"])
+    corr.score(n, ids, vals, dev["hidden"], st["h_req"], st["h_slot"], scores, ws,
+               offset=st["h_off"] + first * st["h_req"])
+    z = torch.empty((n, B, K, r), dtype=torch.float32, device="cuda")
+    g = torch.empty((n, B, r), dtype=torch.float32, device="cuda")
+    s = torch.empty((n, max(B - 1, 0), r), dtype=torch.float32, device="cuda")
+    corr.intermediates(n, ws, z=z, g=g, s=s)
+    corr.walk(n, scores, ids, tokens, choice)
+    torch.cuda.synchronize()
+    out = dict(tokens=tokens, choice=choice, ids=ids, vals=vals, scores=scores, z=z, g=g, s=s)
+    out = {k: v.cpu().numpy() for k, v in out.items()}
+    corr.close()
+    return out
+
+
 def oracle_run(x: dict, n: int | None = None, first: int = 0) -> dict:
     return oracle.run(x["cfg"], x, n=n, first=first)
 
@@ -196,6 +232,74 @@ def check_beam(gpu: dict, cfg: dict, where: str = ""):
     t, c, _ = oracle.beam(desc, gpu["scores"], gpu["ids"], n, cfg.get("beam_width", 4))
     np.testing.assert_array_equal(gpu["choice"], c, err_msg="beam path " + where)
     np.testing.assert_array_equal(gpu["tokens"], t, err_msg="beam tokens " + where)
+
+
+def _beam_steps(S, width: int):
+    """Beam search of one request over float32 scores S [B-1][K][K] (summed
+    transition score, slot 1 at rank 0; extensions ranked by score
+    descending, then beam index, then successor), returning the kept paths
+    after every step (a list of tuples of candidate indices)."""
+    beams = [(np.float32(0.0), (0,))]
+    kept = []
+    P, K = S.shape[0], S.shape[2]
+    for p in range(P):
+        ext = []
+        for bi, (g, path) in enumerate(beams):
+            row = S[p, path[-1]]
+            for b in range(K):
+                ext.append((np.float32(g + row[b]), bi, b, path + (b,)))
+        ext.sort(key=lambda e: (-float(e[0]), e[1], e[2]))
+        beams = [(e[0], e[3]) for e in ext[:width]]
+        kept.append([e[3] for e in ext[:width]])
+    return kept
+
+
+def check_beam_bound(gpu: dict, ora: dict, cfg: dict, where: str = ""):
+    """Ties the beam path back to the oracle's float64 scores.  Until the
+    first step where the beams kept on the GPU's scores and on the oracle's
+    (rounded to float32) differ, both hold the same paths, and each partial
+    sum differs between the two by at most sum_{q<=p} eps_q (eps_q the largest
+    |S_gpu - S_ora| of pair q).  A ranking can only flip between extensions
+    whose oracle sums lie within twice that of each other, so at the first
+    differing step every path kept only on the GPU side must lie within
+    2 sum_{q<=p} eps_q (plus float32 rounding) of every path kept only on the
+    oracle side.  Requests whose beams never differ end on the same path.
+    Returns the number of requests whose beams differ somewhere."""
+    width = cfg.get("beam_width", 4)
+    n, B = gpu["choice"].shape
+    if B < 2:
+        return 0
+    S_g = gpu["scores"]
+    S_o = ora["scores"]
+    diverged = 0
+    for i in range(n):
+        eps = np.cumsum(np.abs(S_g[i].astype(np.float64) - S_o[i]).max(axis=(1, 2)))
+        kg = _beam_steps(S_g[i], width)
+        ko = _beam_steps(S_o[i].astype(np.float32), width)
+        assert tuple(gpu["choice"][i]) == kg[-1][0], "beam replay disagrees with the GPU path %s" % where
+        def total(path, p):
+            return sum(S_o[i, q, path[q], path[q + 1]] for q in range(p + 1))
+
+        def slack(p):
+            return 2 * eps[p] + 1e-5 * (p + 1) * max(1.0, float(np.abs(S_o[i, :p + 1]).max()))
+        for p in range(B - 1):
+            only_g = set(kg[p]) - set(ko[p])
+            only_o = set(ko[p]) - set(kg[p])
+            if not only_g and not only_o:
+                continue
+            diverged += 1
+            worst = max(total(a, p) - total(b, p) for a in only_o for b in only_g)
+            assert worst <= slack(p), "beam %s: request %d step %d: ranking flip of %.3g beyond the score error %.3g" % (
+                where, i, p, worst, slack(p))
+            break
+        else:
+            # the same paths were kept at every step; the best of the last
+            # step can still differ where two final sums nearly tie
+            mine, theirs = tuple(gpu["choice"][i]), ko[-1][0]
+            if mine != theirs:
+                diverged += 1
+                assert total(theirs, B - 2) - total(mine, B - 2) <= slack(B - 2), "beam %s: request %d" % (where, i)
+    return diverged
 
 
 def check_global_sum(gpu: dict, ora: dict, cfg: dict, where: str = "", exact: bool = False, lam: float = 1.0):

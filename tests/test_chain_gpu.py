@@ -1,0 +1,53 @@
+"""GPU parity of the pass run as separate C-ABI calls: corrector_topk, then
+corrector_score on the ids and values it wrote, then corrector_walk on those
+scores.  corrector_score enqueues its own launches (the hidden-state
+projection shares the candidate projection's launch, or runs alone when a
+folded table is attached), so this covers a launch sequence corrector_run
+does not use.  Every gate of tests/parity.py applies, against the oracle."""
+
+import numpy as np
+import pytest
+
+import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+@pytest.mark.parametrize("fold", [False, True])
+@pytest.mark.parametrize("name,head,n", [("tiny", "normal", None), ("tiny", "stress", None), ("b1", "stress", None),
+                                         ("b1", "zero", None), ("b32", "stress", None), ("b32", "normal", None)])
+def test_chain(name, head, n, fold):
+    _log("chain %s head=%s fold=%s" % (name, head, fold))
+    x = P.inputs(name, head=head)
+    gpu = P.gpu_chain(x, n=n, fold=fold)
+    ora = P.oracle_run(x, n=n)
+    steps, exempt, moved = P.check_all(gpu, ora, "chain/%s/%s/fold=%s" % (name, head, fold),
+                                       exact_walk=(head == "zero"))
+    _log("  walk steps %d exempt %d moved %d" % (steps, exempt, moved))
+    if head == "stress" and name != "tiny":
+        assert moved > 0
+
+
+@pytest.mark.parametrize("fold", [False, True])
+def test_chain_matches_run(fold):
+    """The split calls and corrector_run compute the same thing with the same
+    kernels' arithmetic: identical outputs, bit for bit."""
+    _log("chain vs run fold=%s" % fold)
+    x = P.inputs("b32", head="stress")
+    a = P.gpu_chain(x, fold=fold)
+    b = P.gpu_run(x, fold=fold)
+    for k in ("ids", "vals", "scores", "tokens", "choice", "z", "g", "s"):
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+
+
+@pytest.mark.parametrize("fold", [False, True])
+def test_chain_cosine(fold):
+    _log("chain cosine fold=%s" % fold)
+    x = P.inputs("cosine", sigma=8.0)
+    gpu = P.gpu_chain(x, n=4, first=9, fold=fold)
+    ora = P.oracle_run(x, n=4, first=9)
+    P.check_all(gpu, ora, "chain/cosine", variant="cosine")
