@@ -24,7 +24,7 @@ STATUS = {0: "CORR_OK", 1: "CORR_E_NULL", 2: "CORR_E_SHAPE", 3: "CORR_E_UNSUPPOR
 # exported symbols declared in include/corrector.h
 SYMBOLS = ("corrector_create", "corrector_destroy", "corrector_workspace_bytes",
            "corrector_topk", "corrector_topk_softmax", "corrector_score", "corrector_walk", "corrector_run",
-           "corrector_intermediates", "corrector_set_timing", "corrector_kernel_times",
+           "corrector_run_static", "corrector_intermediates", "corrector_set_timing", "corrector_kernel_times",
            "corrector_status_string", "corrector_table_bytes", "corrector_fold_table",
            "corrector_use_table")
 
@@ -77,6 +77,7 @@ def load(path: str = LIB_PATH):
     lib.corrector_score.argtypes = [P, I32, P, P, P, I64, I64, P, P, SZ, P]
     lib.corrector_walk.argtypes = [P, I32, P, P, P, P, P]
     lib.corrector_run.argtypes = [P, I32, P, I64, I64, P, I64, I64, P, P, P, P, P, P, SZ, P]
+    lib.corrector_run_static.argtypes = [P, I32, P, I64, I64, P, I64, I64, P, P, P, P, P, P]
     lib.corrector_intermediates.argtypes = [P, I32, P, SZ, P, P, P, P]
     lib.corrector_set_timing.argtypes = [P, C.c_int]
     lib.corrector_kernel_times.argtypes = [P, P, P, C.c_int]
@@ -87,7 +88,7 @@ def load(path: str = LIB_PATH):
     lib.corrector_status_string.argtypes = [C.c_int]
     lib.corrector_status_string.restype = C.c_char_p
     for fn in ("corrector_topk", "corrector_topk_softmax", "corrector_score", "corrector_walk", "corrector_run",
-               "corrector_intermediates", "corrector_set_timing", "corrector_kernel_times",
+               "corrector_run_static", "corrector_intermediates", "corrector_set_timing", "corrector_kernel_times",
                "corrector_fold_table", "corrector_use_table"):
         getattr(lib, fn).restype = C.c_int
     _lib = lib
@@ -188,6 +189,16 @@ class Corrector:
                                                     h_req_stride, h_slot_stride, _p(tokens),
                                                     _p(choice), _p(ids), _p(vals), _p(scores),
                                                     _p(ws), ws.numel(), _stream(stream)))
+
+    def run_static(self, n, logits, l_req_stride, l_slot_stride, hidden, h_req_stride, h_slot_stride,
+                   tokens, choice=None, ids=None, vals=None, scores=None, l_offset: int = 0,
+                   h_offset: int = 0, stream=None):
+        """corrector_run_static: the library's own static workspace (no allocation)."""
+        lb = _p(logits) + l_offset * logits.element_size()
+        hb = _p(hidden) + h_offset * hidden.element_size()
+        _ok("corrector_run_static", self.lib.corrector_run_static(
+            self.h, n, lb, l_req_stride, l_slot_stride, hb, h_req_stride, h_slot_stride, _p(tokens), _p(choice),
+            _p(ids), _p(vals), _p(scores), _stream(stream)))
 
     def intermediates(self, n, ws, z=None, g=None, s=None, stream=None):
         _ok("corrector_intermediates", self.lib.corrector_intermediates(

@@ -392,6 +392,37 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
     }
 }
 
+int run_checked(const corrector* hc, int32_t n, const void* logits, int64_t lrs, int64_t lss, const void* hidden,
+                int64_t hrs, int64_t hss, int32_t* tokens, int32_t* choice_or_null, int32_t* ids_or_null,
+                float* vals_or_null, float* scores_or_null, void* ws, void* stream);
+
+// ---- the workspace of corrector_run_static, for callers that cannot
+// allocate.  Each GPU the library runs on holds its own copy of `scratch`
+// until the process ends.  In host code the array's name is only a host-side
+// stand-in: its device address on a device is looked up once per device
+// (hipGetSymbolAddress with that device current) and kept in
+// g_scratch_ptr[device]; only that address is ever handed to kernels.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of `scratch` (looked up on its first use).
+int static_scratch(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return CORR_E_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return CORR_E_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return CORR_E_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return CORR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -555,6 +586,34 @@ int corrector_run(const corrector* hc, int32_t n, const void* logits, int64_t lr
     if ((rc = check_hidden(hidden, hrs, hss))) return rc;
     if (!tokens) return CORR_E_NULL;
     if ((rc = check_ws(hc, n, ws, ws_bytes))) return rc;
+    return run_checked(hc, n, logits, lrs, lss, hidden, hrs, hss, tokens, choice_or_null, ids_or_null, vals_or_null,
+                       scores_or_null, ws, stream);
+}
+
+int corrector_run_static(const corrector* hc, int32_t n, const void* logits, int64_t lrs, int64_t lss,
+                         const void* hidden, int64_t hrs, int64_t hss, int32_t* tokens, int32_t* choice_or_null,
+                         int32_t* ids_or_null, float* vals_or_null, float* scores_or_null, void* stream) {
+    int rc = check_n(hc, n);
+    if (rc || n == 0) return rc;
+    if ((rc = check_logits(hc, logits, lrs, lss))) return rc;
+    if ((rc = check_hidden(hidden, hrs, hss))) return rc;
+    if (!tokens) return CORR_E_NULL;
+    if (layout(hc->d, n).total > kStaticScratchBytes) return CORR_E_WORKSPACE;
+    void* ws = nullptr;
+    if ((rc = static_scratch(&ws))) return rc;
+    return run_checked(hc, n, logits, lrs, lss, hidden, hrs, hss, tokens, choice_or_null, ids_or_null, vals_or_null,
+                       scores_or_null, ws, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// corrector_run after validation: every step on the call's stream, with `ws`
+// as the workspace (at least layout(n).total bytes, 16-byte aligned).
+int run_checked(const corrector* hc, int32_t n, const void* logits, int64_t lrs, int64_t lss, const void* hidden,
+                int64_t hrs, int64_t hss, int32_t* tokens, int32_t* choice_or_null, int32_t* ids_or_null,
+                float* vals_or_null, float* scores_or_null, void* ws, void* stream) {
     corrector* h = const_cast<corrector*>(hc);
     const Layout L = layout(h->d, n);
     int32_t* ids = ids_or_null ? ids_or_null : at<int32_t>(ws, L.ids);
@@ -568,6 +627,10 @@ int corrector_run(const corrector* hc, int32_t n, const void* logits, int64_t lr
     enqueue_score(q, h, L, n, ids, vals, hidden, hrs, hss, scores, ws, tokens, choice_or_null, true);
     return q.finish();
 }
+
+}  // namespace
+
+extern "C" {
 
 size_t corrector_table_bytes(const corrector* h) {
     if (!live(h)) return 0;

@@ -262,6 +262,27 @@ int corrector_run(const corrector *h, int32_t n_req, const void *logits, int64_t
                   int32_t *ids_or_null, float *vals_or_null, float *scores_or_null,
                   void *workspace, size_t workspace_bytes, void *stream);
 
+/* corrector_run for callers that cannot allocate device memory: code under
+ * graph capture, serving loops that must not allocate, harnesses that forbid
+ * hipMalloc.  There is no workspace argument; the workspace is a static
+ * device array of the library, 64 MiB on each GPU the library runs on (held
+ * until the process ends).  Arguments, outputs and errors are those of
+ * corrector_run; an n_req whose corrector_workspace_bytes exceeds 64 MiB
+ * returns CORR_E_WORKSPACE with nothing launched (32 requests at the DCOCO
+ * Qwen3-8B shape need 28.6 MiB for the MLP variant, 34.4 MiB for the cosine
+ * variant).  The current device must be the stream's device.  The first call
+ * on a device looks up that device's copy of the array (CORR_E_HIP if that
+ * fails), so it should not be the first call made under a graph capture.
+ * Every call on one GPU uses that GPU's one array: calls that overlap on one
+ * GPU (on other streams or threads, with any handle) race and their results
+ * are undefined, so serialise them.  The array needs no initialisation and
+ * keeps whatever the last call left in it. */
+int corrector_run_static(const corrector *h, int32_t n_req, const void *logits, int64_t l_req_stride,
+                         int64_t l_slot_stride, const void *hidden, int64_t h_req_stride,
+                         int64_t h_slot_stride, int32_t *tokens, int32_t *choice_or_null,
+                         int32_t *ids_or_null, float *vals_or_null, float *scores_or_null,
+                         void *stream);
+
 /* Folded candidate projection.  E and W_cand are frozen at inference, so
  * u = W_cand E[c] can be tabulated once for the whole vocabulary:
  * T = E W_cand^T, [V][r] float32 (an MFMA GEMM over every embedding row).

@@ -188,6 +188,12 @@ static void argument_checks(corrector *h)
            CORR_E_NULL);
     EXPECT(corrector_run(h, 1, p, B1 * V, V, p, B1 * 64, 64, ip, NULL, NULL, NULL, NULL, p, ws - 1, NULL) ==
            CORR_E_WORKSPACE);
+    EXPECT(corrector_run_static(h, 1, p, B1 * V, V, p, B1 * 64, 64, NULL, NULL, NULL, NULL, NULL, NULL) ==
+           CORR_E_NULL);
+    EXPECT(corrector_run_static(h, 1, (char *)p + 4, B1 * V, V, p, B1 * 64, 64, ip, NULL, NULL, NULL, NULL, NULL) ==
+           CORR_E_ALIGN);
+    EXPECT(corrector_run_static(h, d.max_requests + 1, p, B1 * V, V, p, B1 * 64, 64, ip, NULL, NULL, NULL, NULL,
+                                NULL) == CORR_E_SHAPE);
     EXPECT(corrector_intermediates(h, 1, p, 8, NULL, NULL, NULL, NULL) == CORR_E_WORKSPACE);
     EXPECT(corrector_fold_table(h, NULL, NULL) == CORR_E_NULL);
     EXPECT(corrector_fold_table(h, (float *)((char *)p + 4), NULL) == CORR_E_ALIGN);
@@ -225,6 +231,24 @@ static void handle_lifecycle(void)
     EXPECT(corrector_workspace_bytes(b, 1) > 0);
     corrector_destroy(b);
     EXPECT(corrector_workspace_bytes(b, 1) == 0);
+    EXPECT(corrector_run_static(b, 1, arena, 0, 0, arena, 0, 0, (int32_t *)arena, NULL, NULL, NULL, NULL, NULL) ==
+           CORR_E_HANDLE);
+    /* a batch whose workspace exceeds the static array is refused on the host */
+    corrector_desc big = base_desc();
+    big.vocab = 151936;
+    big.slots = 15;
+    big.k = 64;
+    big.d_hidden = 4096;
+    big.d_embed = 4096;
+    big.r = 128;
+    big.mlp_hidden = 256;
+    big.max_requests = 4096;
+    corrector *c;
+    EXPECT(create_with(big, w, &c) == CORR_OK);
+    EXPECT(corrector_workspace_bytes(c, 4096) > ((size_t)64 << 20));
+    EXPECT(corrector_run_static(c, 4096, arena, 0, 0, arena, 0, 0, (int32_t *)arena, NULL, NULL, NULL, NULL, NULL) ==
+           CORR_E_WORKSPACE);
+    corrector_destroy(c);
     /* a pointer that never was a handle */
     EXPECT(corrector_workspace_bytes((const corrector *)arena, 1) == 0);
     corrector_destroy((corrector *)arena);
