@@ -27,13 +27,13 @@ sys.path.insert(0, ROOT)
 METRIC = "corrected draft blocks/s at batch 32 (V=151936,B=16,K=16); % HBM/MFMA peak"
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
-# vector-ALU ceiling for GELU evaluations: 256 CUs x 64 lanes x 2.4 GHz =
-# 39.3 T lane-instructions/s (no packed FP32), at 13 instructions per
-# evaluation in the MLP's inner loop (the add of P and Q, 9 for the GELU
-# itself, the w2 multiply-add, and the two transcendentals v_rcp_f32 and
-# v_exp_f32) plus 2 x 3 extra slots for the quarter-rate transcendentals
-# (19 slots)
-PEAK_GELU_T = 256 * 64 * 2.4e9 / 13 / 1e12   # 13 VALU issue slots per evaluation (see the design notes)
+# vector-ALU ceiling for GELU evaluations: the published float32 vector rate
+# (157.3 TFLOP/s = 78.6 T lane multiply-adds/s: 256 CUs x 128 lanes x 2.4 GHz),
+# at 17 issue slots per evaluation in the MLP's inner loop: 9 single-rate
+# instructions (the add of P and Q, 7 for the GELU itself, the w2
+# multiply-add) and the two transcendentals v_rcp_f32 and v_exp_f32 at a
+# quarter of that rate (4 slots each)
+PEAK_GELU_T = 256 * 128 * 2.4e9 / 17 / 1e12   # 4.63 T evaluations/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = os.path.join(ROOT, "draft_correction_amd", "csrc")
 
@@ -90,7 +90,7 @@ def algorithmic_work(cfg: dict, n: int) -> dict:
     w["finish"] = w["finish_walk"] = w["finish_viterbi"] = w["finish_beam"] = dict(bound="hbm", bytes=n * (B - 1) * K * K * 4 * 2,
                                           per_unit=(B - 1) * K * K * 8, units=n, unit="block")
     # the transition MLP epilogue is bound by the vector ALU: K m h GELU
-    # evaluations per pair (m = K unless sparsified; 13 VALU issue slots each)
+    # evaluations per pair (m = K unless sparsified; 17 VALU issue slots each)
     # against 256 CUs x 64 lanes x 2.4 GHz
     ms = cfg.get("succ_top_m", 0)
     ms = ms if 0 < ms < K else K   # successors scored per predecessor

@@ -155,13 +155,12 @@ struct MlpArgs {
     const uint16_t* w1;     // [h][3r+2]
     const float* b1;
     const float* w2;
-    float* part;            // [n*(B-1)][blocks][K][K] partial Delta per hidden-unit block
+    float* part;            // [n*(B-1)][blocks][K][K] partial Delta per hidden-unit block (b < m written)
     int m;                  // successors scored per predecessor (b < m; 1..K)
 };
 // Most hidden-unit blocks of the MLP (h <= 256 units in blocks of 64).
 constexpr int kMaxMlpBlocks = 4;
 int mlp_blocks(int h);
-size_t mlp_lds_bytes(int K, int r);
 hipError_t launch_mlp(const MlpArgs& a, hipStream_t stream);
 
 // Sum of the MLP partials in block order + b2 + l_{p+1}(b) -> scores (one
