@@ -246,6 +246,7 @@ GemmJob hproj_job(const corrector* h, const Layout& L, int32_t n, const void* hi
     hj.kdim = d.d_hidden;
     hj.splits = L.splits;
     hj.C = at<float>(ws, L.hproj);
+    gemm_pick_small(hj, 64, 128);
     return hj;
 }
 
@@ -283,6 +284,7 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
         uj.kdim = d.d_embed;
         uj.splits = L.usplits;
         uj.C = upart;
+        gemm_pick_small(uj, hproj_done ? 128 : 64, 128);
         if (hproj_done) {
             q("cand_gemm", [&] { return launch_gemm_gather(uj, q.s); });
         } else {

@@ -217,6 +217,92 @@ __device__ __forceinline__ void gemm_body(const GemmJob J, int64_t lin, unsigned
     }
 }
 
+// ---------------------------------------------------------------- small --
+// The same product for calls with few rows: wave t of the launch computes
+// one 16 x 16 output tile of one k-split (split fastest), its A and W
+// fragments loaded straight into registers, eight 32-wide k-steps in flight
+// while the previous eight are multiplied.  Each output takes the same
+// sequence of v_mfma_f32_16x16x32_bf16 over the split's k-steps, on the same
+// lane layout, as gemm_body, so the partials are identical.
+constexpr int kSmallDepth = 8;
+
+__device__ __forceinline__ int64_t gemm_small_tiles(const GemmJob& J) {
+    return ((J.M + 15) / 16) * ((J.N + 15) / 16) * J.splits;
+}
+
+__device__ __forceinline__ void gemm_small_body(const GemmJob J, int64_t t) {
+    if (t >= gemm_small_tiles(J)) return;
+    const GemmA& A = J.A;
+    const GemmW& W = J.W;
+    const int64_t M = J.M;
+    const int N = J.N, kdim = J.kdim, splits = J.splits;
+    const int l = lane_id();
+    const int kper = ((kdim / 32 + splits - 1) / splits) * 32;
+    const int ntn = (N + 15) / 16;
+    const int split = static_cast<int>(t % splits);
+    const int64_t rest = t / splits;
+    const int n0 = static_cast<int>(rest % ntn) * 16;
+    const int64_t m0 = (rest / ntn) * 16;
+    const int k_lo = split * kper;
+    const int k_hi = min(kdim, k_lo + kper);
+    const int nks = k_lo < k_hi ? (k_hi - k_lo) / 32 : 0;
+    const int kq = 8 * (l >> 4);
+    // rows past M or N repeat the last row (their results are not stored)
+    const uint16_t* ap = a_row(A, min(m0 + (l & 15), M - 1)) + k_lo + kq;
+    const int nn = min(n0 + (l & 15), N - 1);
+    const int b = nn / W.nb;
+    const uint16_t* wb = b == 0 ? W.base[0] : (b == 1 ? W.base[1] : W.base[2]);
+    const int64_t wld = b == 0 ? W.ld[0] : (b == 1 ? W.ld[1] : W.ld[2]);
+    const uint16_t* wp = wb + static_cast<int64_t>(nn % W.nb) * wld;
+    const int kmask = W.kwrap > 0 ? W.kwrap - 1 : -1;
+    // k-steps past the split's last are clamped to it: loaded, never used
+    auto ld = [&](int ks0, u32x4 (&a)[kSmallDepth], u32x4 (&w)[kSmallDepth]) {
+#pragma unroll
+        for (int i = 0; i < kSmallDepth; ++i) {
+            const int ks = min(ks0 + i, nks - 1);
+            a[i] = load16(ap + 32 * ks);
+            w[i] = load16(wp + ((k_lo + 32 * ks + kq) & kmask));
+        }
+    };
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (nks > 0) {
+        u32x4 a0[kSmallDepth], w0[kSmallDepth], a1[kSmallDepth], w1[kSmallDepth];
+        ld(0, a0, w0);
+        for (int ks = 0; ks < nks; ks += 2 * kSmallDepth) {
+            ld(ks + kSmallDepth, a1, w1);
+#pragma unroll
+            for (int i = 0; i < kSmallDepth; ++i)
+                if (ks + i < nks) acc = mfma16x16x32(a0[i], w0[i], acc);
+            ld(ks + 2 * kSmallDepth, a0, w0);
+#pragma unroll
+            for (int i = 0; i < kSmallDepth; ++i)
+                if (ks + kSmallDepth + i < nks) acc = mfma16x16x32(a1[i], w1[i], acc);
+        }
+    }
+    // lane l holds rows 4 (l / 16) + e of column l % 16
+    float* out = J.C + static_cast<int64_t>(split) * M * N;
+    const int c = n0 + (l & 15);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int64_t r = m0 + 4 * (l >> 4) + e;
+        if (r < M && c < N) out[r * N + c] = acc[e];
+    }
+}
+
+// Workgroups of 256 threads a GEMM job occupies in a launch (tiled or small).
+__host__ __device__ inline int64_t gemm_blocks_256(const GemmJob& j) {
+    if (j.small) return (((j.M + 15) / 16) * ((j.N + 15) / 16) * j.splits + 3) / 4;
+    return ((j.M + kBM - 1) / kBM) * ((j.N + kBN - 1) / kBN) * j.splits;
+}
+
+// Workgroup lin of a job, tiled or small (256 threads; smem: kGemmSmem bytes).
+__device__ __forceinline__ void gemm_any_body(const GemmJob& J, int64_t lin, unsigned char* smem) {
+    if (J.small)
+        gemm_small_body(J, lin * 4 + (threadIdx.x >> 6));
+    else
+        gemm_body(J, lin, smem);
+}
+
 }  // namespace
 
 }  // namespace corr

@@ -84,7 +84,12 @@ struct GemmJob {
     int kdim;
     int splits;
     float* C;
+    int small;            // 1: one 16 x 16 output tile per wave, operands straight to
+                          // registers (few rows); identical partials either way
 };
+// Sets j.small when the one-wave-per-16x16-tile form moves fewer operand bytes
+// per CU than tiles of bm x bn (the launch's tiled form).
+void gemm_pick_small(GemmJob& j, int bm, int bn);
 hipError_t launch_gemm(const GemmA& A, const GemmW& W, int64_t M, int N, int kdim, int splits, float* C,
                        hipStream_t stream);
 hipError_t launch_gemm2(const GemmJob& j0, const GemmJob& j1, hipStream_t stream);

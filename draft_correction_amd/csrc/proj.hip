@@ -34,9 +34,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmJob j0, GemmJob j1, int64
     __shared__ __attribute__((aligned(16))) unsigned char smem[kGemmSmem];
     const int64_t b = blockIdx.x;
     if (b < nblk0)
-        gemm_body(j0, b, smem);
+        gemm_any_body(j0, b, smem);
     else
-        gemm_body(j1, b - nblk0, smem);
+        gemm_any_body(j1, b - nblk0, smem);
 }
 
 // ------------------------------------------------------------ gather gemm --
@@ -75,6 +75,77 @@ template <int n>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(n >= 0 && n < 64, "vmcnt");
     __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0xF70);
+}
+
+// The candidate projection in its small form: one wave per workgroup and
+// 16 x 16 output tile of one k-split (split fastest), as gemm_small_body, but
+// with every k-step of a round of up to kSmallRound loaded at once straight
+// into LDS (global_load_lds_dwordx4: the lanes' A and W fragments of a k-step,
+// 1 KB each, land lane-linearly, which is also the layout the MFMA reads back,
+// bank-conflict free), so a wave waits for memory once per round instead of
+// once per few k-steps.  Same MFMA sequence per output: identical partials.
+constexpr int kSmallRound = 32;   // k-steps per round (64 KB of LDS)
+
+__global__ __launch_bounds__(64) void gemm_small_kernel(GemmJob J) {
+    __shared__ __attribute__((aligned(1024))) uint16_t st[2 * kSmallRound * 512];
+    const int64_t t = blockIdx.x;
+    if (t >= gemm_small_tiles(J)) return;
+    const GemmA& A = J.A;
+    const GemmW& W = J.W;
+    const int64_t M = J.M;
+    const int N = J.N, kdim = J.kdim, splits = J.splits;
+    const int l = threadIdx.x;
+    const int kper = ((kdim / 32 + splits - 1) / splits) * 32;
+    const int ntn = (N + 15) / 16;
+    const int split = static_cast<int>(t % splits);
+    const int64_t rest = t / splits;
+    const int n0 = static_cast<int>(rest % ntn) * 16;
+    const int64_t m0 = (rest / ntn) * 16;
+    const int k_lo = split * kper;
+    const int k_hi = min(kdim, k_lo + kper);
+    const int nks = k_lo < k_hi ? (k_hi - k_lo) / 32 : 0;
+    const int kq = 8 * (l >> 4);
+    // rows past M or N repeat the last row (their results are not stored)
+    const uint16_t* ap = a_row(A, min(m0 + (l & 15), M - 1)) + k_lo + kq;
+    const int nn = min(n0 + (l & 15), N - 1);
+    const int b = nn / W.nb;
+    const uint16_t* wb = b == 0 ? W.base[0] : (b == 1 ? W.base[1] : W.base[2]);
+    const int64_t wld = b == 0 ? W.ld[0] : (b == 1 ? W.ld[1] : W.ld[2]);
+    const uint16_t* wp = wb + static_cast<int64_t>(nn % W.nb) * wld + k_lo + kq;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int c0 = 0; c0 < nks; c0 += kSmallRound) {
+        const int nc = min(kSmallRound, nks - c0);
+        // the previous round's fragment reads are complete before its LDS is refilled
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+        for (int i = 0; i < nc; ++i) {
+            lds_dma16(ap + 32 * (c0 + i), st + i * 512);
+            lds_dma16(wp + 32 * (c0 + i), st + (kSmallRound + i) * 512);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the round has landed
+        asm volatile("" ::: "memory");
+        // eight k-steps' fragments read at a time (reads past the round's
+        // last k-step stay inside the buffer and are not used)
+        for (int i0 = 0; i0 < nc; i0 += 8) {
+            u32x4 a[8], w[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int i = min(i0 + j, kSmallRound - 1);
+                a[j] = *reinterpret_cast<const u32x4*>(st + i * 512 + 8 * l);
+                w[j] = *reinterpret_cast<const u32x4*>(st + (kSmallRound + i) * 512 + 8 * l);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (i0 + j < nc) acc = mfma16x16x32(a[j], w[j], acc);
+        }
+    }
+    // lane l holds rows 4 (l / 16) + e of column l % 16
+    float* out = J.C + static_cast<int64_t>(split) * M * N;
+    const int c = n0 + (l & 15);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int64_t r = m0 + 4 * (l >> 4) + e;
+        if (r < M && c < N) out[r * N + c] = acc[e];
+    }
 }
 
 __global__ __launch_bounds__(kGThreads) void gemm_gather_kernel(GemmJob J) {
@@ -547,8 +618,20 @@ __global__ __launch_bounds__(kCT) void cand_kernel(CandArgs a) {
 
 }  // namespace
 
-int64_t gemm_launch_blocks(const GemmJob& j) {
-    return ((j.M + kBM - 1) / kBM) * ((j.N + kBN - 1) / kBN) * j.splits;
+int64_t gemm_launch_blocks(const GemmJob& j) { return gemm_blocks_256(j); }
+
+static int64_t small_tiles(const GemmJob& j) { return ((j.M + 15) / 16) * ((j.N + 15) / 16) * j.splits; }
+
+void gemm_pick_small(GemmJob& j, int bm, int bn) {
+    // operand bytes per CU (256 CUs): a tiled workgroup reads bm + bn rows of
+    // its k-range, and the workgroups run in ceil(blocks / 256) rounds; the
+    // small form spreads 32 rows of a k-range per 16 x 16 tile over all CUs
+    const int64_t kper = ((j.kdim / 32 + j.splits - 1) / j.splits) * 32;
+    const int64_t blocks = ((j.M + bm - 1) / bm) * ((j.N + bn - 1) / bn) * j.splits;
+    const int64_t tiles = ((j.M + 15) / 16) * ((j.N + 15) / 16) * j.splits;
+    const int64_t tiled = (bm + bn) * kper * ((blocks + 255) / 256);
+    const int64_t small = (tiles * 32 * kper + 255) / 256;
+    j.small = j.M > 0 && small < tiled ? 1 : 0;
 }
 
 hipError_t launch_gemm2(const GemmJob& j0, const GemmJob& j1, hipStream_t stream) {
@@ -558,13 +641,14 @@ hipError_t launch_gemm2(const GemmJob& j0, const GemmJob& j1, hipStream_t stream
 
 hipError_t launch_gemm_gather(const GemmJob& j, hipStream_t stream) {
     if (j.W.kwrap > 0 || j.kdim % 32 != 0) return hipErrorInvalidValue;
+    if (j.small) return launch(gemm_small_kernel, dim3(static_cast<unsigned>(small_tiles(j))), 64, 0, stream, j);
     const int64_t blocks = ((j.M + kGM - 1) / kGM) * ((j.N + kGN - 1) / kGN) * j.splits;
     return launch(gemm_gather_kernel, dim3(static_cast<unsigned>(blocks)), kGThreads, 0, stream, j);
 }
 
 hipError_t launch_gemm(const GemmA& A, const GemmW& W, int64_t M, int N, int kdim, int splits, float* C,
                        hipStream_t stream) {
-    GemmJob j{A, W, M, N, kdim, splits, C};
+    GemmJob j{A, W, M, N, kdim, splits, C, 0};
     GemmJob none = j;
     none.M = 0;
     return launch_gemm2(j, none, stream);

@@ -899,7 +899,7 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(const uint64_t* __restr
     __shared__ __attribute__((aligned(16))) unsigned char smem[kGemmSmem];
     static_assert(4 * (kMergeCap + kWave) * 8 + 4 * 2 * kWave * 8 <= kGemmSmem, "merge lists fit the GEMM's LDS");
     if (static_cast<int64_t>(blockIdx.x) >= nmerge) {
-        gemm_body(hj, static_cast<int64_t>(blockIdx.x) - nmerge, smem);
+        gemm_any_body(hj, static_cast<int64_t>(blockIdx.x) - nmerge, smem);
         return;
     }
     uint64_t (*sel_all)[kMergeCap + kWave] = reinterpret_cast<uint64_t (*)[kMergeCap + kWave]>(smem);
