@@ -14,10 +14,12 @@
 // accuracy), then forms P and Q and runs the epilogue: the GELU over all
 // K^2 x h pre-activations and the h -> 1 dot with w2, one (a, b) per thread.
 //
-// Work is split into (pair, block of 64 hidden units) workgroups; each block
-// writes its partial Delta and the finishing kernel adds the blocks in order,
-// adds b2 and l_{p+1}(b) and walks.  Every sum runs in a fixed order with no
-// atomics: bit-reproducible.
+// Work is split by (pairs, block of 64 hidden units): for K <= 16 each
+// workgroup streams a run of pairs through a producer / consumer split of its
+// waves (mlp_ws_kernel), for larger K each takes two adjacent pairs
+// (mlp_kernel).  Each block writes its partial Delta and the finishing kernel
+// adds the blocks in order, adds b2 and l_{p+1}(b) and walks.  Every sum runs
+// in a fixed order with no atomics: bit-reproducible.
 #include "common.h"
 #include "kernels.h"
 
@@ -66,260 +68,249 @@ typedef __attribute__((address_space(1))) void* mlp_global_ptr;
 template <int ZSEG>
 __device__ __forceinline__ int zpos(int a, int s) { return s ^ (a & (ZSEG < 8 ? ZSEG - 1 : 7)); }
 
-// Shapes of one instance: K <= 16 KT candidates, NT threads, chunks of at
-// most C pairs (their z rows, P, Q and results fill the LDS).
-template <int R, int KT>
-struct MlpShape {
-    static constexpr int NT = KT == 1 ? 1024 : 512;
-    static constexpr int KMAX = 16 * KT;
-    static constexpr int C = KT == 1 ? 7 : (KT == 2 ? 3 : 1);
-};
+// ------------------------------------------------------------- K > 16 --
+static_assert(256 == 4 * kJB, "four r quarters per hidden unit in the c_p dot of mlp_kernel");
 
-// The transition MLP for K > 16.  The G workgroups form nj equal groups, one per block
-// of 64 hidden units; workgroup w of group jb = w / (G / nj) takes a
-// contiguous run of the pairs, in chunks of at most C consecutive pairs of
-// one request (slots t0 .. t0 + np).  For each chunk:
-//   1. the z rows of the np + 1 slots (bf16 [hi | lo], float32 accuracy),
-//      the pair states and the slots' logits go straight into LDS;
-//   2. c_p[j] = W1_s[j] s_p for every pair (float32 dots, an eighth of r
-//      per thread), then on MFMA U[a][j] = W1_za[j] z_p^a (waves with
-//      (w / 4) even) and V[b][j] = W1_zb[j] z_{p+1}^b (odd), each wave one
-//      16-unit column tile, the pairs split between the groups of eight
-//      waves, and from them
-//        P[a][j] = c_p[j] + b1[j] + w_la[j] l_p(a) + U[a][j]
-//        Q[b][j] = w_lb[j] l_{p+1}(b) + V[b][j];
-//   3. GELU(P[a] + Q[b]) and the dot with w2 over the block for every pair
-//      and K x m candidate pairs (successors b < m), eight threads per
-//      (a, b, b + 1), each over 8 units, their sums added in a fixed order;
-//   4. the partial Deltas go to part[pair][block][a][b] and the finishing
-//      kernel adds the blocks in order.
-template <int R, int KT>
-__global__ __launch_bounds__((MlpShape<R, KT>::NT), 1) void mlp_chunk_kernel(MlpArgs a) {
-    using S = MlpShape<R, KT>;
-    constexpr int NT = S::NT, KMAX = S::KMAX, C = S::C;
-    constexpr int KS = 2 * R / 32;              // 32-wide k-steps over [hi | lo]
-    constexpr int KD = R >= 32 ? R / 32 : 1;    // distinct W1 fragments (hi and lo share them)
-    constexpr int ZSEG = 2 * R / 8;             // 16-byte segments per z row
-    constexpr int NW = NT / 64;                 // waves
-    static_assert(NW >= 8, "two groups of four column-tile waves");
-    // z rows of the chunk's slots, then P and Q of its pairs, then results
-    __shared__ __attribute__((aligned(16))) uint16_t zbuf[(C + 1) * KMAX * 2 * R];
-    __shared__ __attribute__((aligned(16))) float pq[C * 2 * KMAX * kPS];
-    __shared__ __attribute__((aligned(16))) float res[C * KMAX * KMAX];
-    __shared__ __attribute__((aligned(16))) float sp[C * R];
-    __shared__ __attribute__((aligned(16))) float lv[(C + 1) * KMAX];
-    __shared__ __attribute__((aligned(16))) float w2s[kJB];
-    __shared__ float cps[C][8][kJB];
-
-    const int tid = threadIdx.x, l = tid & 63, wave = tid >> 6;
+// One workgroup per (NP adjacent pairs p0 .. p0 + NP - 1 of a request, block
+// of up to 64 hidden units); the last group of a request may hold fewer.  For
+// each pair p of the group:
+//   U_p[a][j] = W1_za[j] z_p^a,  V_{p+1}[b][j] = W1_zb[j] z_{p+1}^b   (MFMA)
+//   P[a][j] = c_p[j] + b1[j] + w_la[j] l_p(a) + U_p[a][j]
+//   Q[b][j] = w_lb[j] l_{p+1}(b) + V_{p+1}[b][j]
+// with c_p = W1_s s_p formed here too, then GELU and the dot with w2 over the
+// K x m candidate pairs (successors b < m; m = K unless sparsified), one
+// (a, b) per thread; each pair's partial Delta for the block goes to
+// part[pair][block][a][b].  With two pairs per group they share the W1
+// fragments and the z rows of their middle slot; one pair per group gives
+// twice the workgroups, which spread the GELU work evenly over the CUs.  U and V are accumulated exactly as a 16 x 16
+// tile product over the 2r values [hi(z) | lo(z)] in k order, the hi and lo
+// halves meeting the same W1 columns.
+template <int R, int KT, int NP>
+__global__ __launch_bounds__(256, KT > 2 ? 4 : (NP == 1 ? 7 : 5)) void mlp_kernel(MlpArgs a) {
+    constexpr int KS = 2 * R / 32;          // 32-wide k-steps over [hi | lo]
+    constexpr int KD = R >= 32 ? R / 32 : 1;  // distinct W1 fragments (hi and lo share them)
+    constexpr int ZSEG = 2 * R / 8;         // 16-byte segments per z row
+    const int tid = threadIdx.x;
     const int B = a.B, K = a.K, h = a.h;
     const int nj = (h + kJB - 1) / kJB;
-    const int P = a.n * (B - 1);
-    // this workgroup's block and run of pairs [q_lo, q_hi) (pairs per call < 2^24)
-    const int per = gridDim.x / nj;             // workgroups per block
-    const int jb = blockIdx.x / per, wi = blockIdx.x - jb * per;
-    const int q_lo = static_cast<int>(static_cast<int64_t>(wi) * P / per);
-    const int q_hi = static_cast<int>(static_cast<int64_t>(wi + 1) * P / per);
-    if (jb >= nj || q_lo >= q_hi) return;
-    const int j0 = jb * kJB, jn = min(kJB, h - j0);
-    const int ms = a.m;
-    const int mh = (ms + 1) / 2;
-    const int TP = K * mh * 8;                  // GELU tasks per pair
+    const int G = (B - 1 + NP - 1) / NP;    // pair groups per request
+    // Consecutive workgroup numbers go to different XCDs (round-robin over 8):
+    // the hidden blocks of one group are numbered 8 apart so they share an XCD.
+    const int lin = blockIdx.x;
+    const int xcd = lin % 8, i8 = lin / 8;
+    const int jblk = i8 % nj;
+    const int grp = (i8 / nj) * 8 + xcd;
+    if (grp >= a.n * G) return;
+    const int req = grp / G, p0 = NP * (grp % G);
+    const int np = min(NP, B - 1 - p0);     // pairs in this group
+    const int pair0 = req * (B - 1) + p0;
+    const int64_t t0 = static_cast<int64_t>(req) * B + p0;   // slot row of the first pair's predecessor
+    const int j0 = jblk * kJB;
+    const int jn = min(kJB, h - j0);
+    constexpr int PS = kJB + 4;     // LDS row stride of P / Q (floats)
     const int nin = 3 * R + 2;
+    const int l = tid & 63, wave = tid >> 6;
 
-    // ---- the block's W1 slices in registers, for the whole run:
-    //   MFMA waves: wave w takes column tile g = w % 4 (units 16 g .. 16 g + 15)
-    //   of U (w / 4 even) or V (odd), for the pairs i with i % NG == w / 8
-    //   (NG groups of eight waves)
-    constexpr int NG = NW / 8;
-    const int g = wave & 3;
-    const bool isu = ((wave >> 2) & 1) == 0;
-    const int ph = wave >> 3;
-    const bool mfma_wave = 16 * g < jn;
-    const int jl = min(16 * g + (l & 15), jn - 1);   // the lane's unit (clamped: not stored)
-    u32x4 bw[KD];
+    __shared__ __attribute__((aligned(16))) float w2s[kJB];
+    __shared__ __attribute__((aligned(16))) float sps[NP][R];   // the pair states s_p
+    __shared__ float cps4[NP][4][kJB];  // c_p partial dots, one per quarter of r
+    __shared__ float lv[3 * 64];        // the candidates' logits l of slots t0 .. t0 + np (K <= 64)
+    // First the z rows of the group's slots t0 .. t0 + np ([(np + 1) K][2r]
+    // bf16, segments permuted by zpos); once the U | V products are formed,
+    // the same memory holds P [NP][K][PS] and Q [NP][K][PS].
+    extern __shared__ __attribute__((aligned(16))) float dyn[];
+    uint16_t* zs = reinterpret_cast<uint16_t*>(dyn);
+    float* Pb = dyn;
+    float* Qb = dyn + NP * K * PS;
+
+    // ---- z rows straight into LDS (no registers held while in flight):
+    // the slots' rows are contiguous in zhl.  A wave instruction moves 64
+    // segments to 64 consecutive LDS positions; lanes past the last take no
+    // part.  Then the pair states s_p, r / 4 segments each.
     {
-        const uint16_t* wr = a.w1 + static_cast<int64_t>(j0 + jl) * nin + (isu ? R : 2 * R);
+        const int nseg = (np + 1) * K * ZSEG;
+        for (int s0 = wave * 64; s0 < nseg; s0 += 4 * 64) {
+            const int sg = s0 + l;
+            if (sg < nseg) {
+                const int row = sg / ZSEG, pos = sg % ZSEG;
+                const uint16_t* src = a.zhl + (t0 * K + row) * (2 * R) + zpos<ZSEG>(row, pos) * 8;
+                __builtin_amdgcn_global_load_lds((mlp_global_ptr)(src), (mlp_lds_ptr)(zs + s0 * 8), 16, 0, 0);
+            }
+        }
+        if (wave >= 4 - np && l < R / 4) {
+            const int i = 3 - wave;   // wave 3: the first pair, wave 2: the second
+            __builtin_amdgcn_global_load_lds((mlp_global_ptr)(a.s + static_cast<int64_t>(pair0 + i) * R + 4 * l),
+                                             (mlp_lds_ptr)(sps[i]), 16, 0, 0);
+        }
+        // the slots' logits, 4 bytes per lane (waves 0 and 1, 64 values each)
+        const int nl = (np + 1) * K;
+        if (wave < 2 && wave * 64 < nl && wave * 64 + l < nl)
+            __builtin_amdgcn_global_load_lds((mlp_global_ptr)(a.vals + t0 * K + wave * 64 + l),
+                                             (mlp_lds_ptr)(lv + wave * 64), 4, 0, 0);
+        if (nl > 128 && wave == 2 && 128 + l < nl)
+            __builtin_amdgcn_global_load_lds((mlp_global_ptr)(a.vals + t0 * K + 128 + l),
+                                             (mlp_lds_ptr)(lv + 128), 4, 0, 0);
+    }
+
+    // ---- per-lane operands of the U | V tiles: wave w owns hidden units
+    // j0 + 16 w .. + 15 of the block (columns past jn are formed from the
+    // last valid unit and not stored)
+    const int jl = min(16 * wave + (l & 15), jn - 1);   // this lane's unit within the block
+    const bool wave_on = 16 * wave < jn;
+    // W1_za | W1_zb fragments of this lane's unit (shared by both pairs)
+    u32x4 bu[KD], bv[KD];
+    {
+        const uint16_t* wr = a.w1 + static_cast<int64_t>(j0 + jl) * nin;
         const int kq = 8 * (l >> 4);
 #pragma unroll
-        for (int d = 0; d < KD; ++d) bw[d] = load16(wr + ((d * 32 + kq) % R));
+        for (int d = 0; d < KD; ++d) {
+            bu[d] = load16(wr + R + ((d * 32 + kq) % R));
+            bv[d] = load16(wr + 2 * R + ((d * 32 + kq) % R));
+        }
     }
-    const float wl = bf16_to_f32(a.w1[static_cast<int64_t>(j0 + jl) * nin + 3 * R + (isu ? 0 : 1)]);
+    const float wla = bf16_to_f32(a.w1[static_cast<int64_t>(j0 + jl) * nin + 3 * R]);
+    const float wlb = bf16_to_f32(a.w1[static_cast<int64_t>(j0 + jl) * nin + 3 * R + 1]);
     const float b1j = a.b1[j0 + jl];
-    // c_p: thread (unit jj, eighth e8 of r, pair parity cq) dots W1_s row
-    // j0 + jj with s_p over columns e8 R/8 .. e8 R/8 + R/8 - 1, read as
-    // 32-bit words of two columns
-    const int jj = tid & (kJB - 1), e8 = (tid >> 6) & 7, cq = tid >> 9;
-    constexpr int NCQ = NT / 512;               // pair parities of the c_p threads
-    uint32_t ws[R / 16];
-    {
-        const uint32_t* wsr = reinterpret_cast<const uint32_t*>(a.w1 + static_cast<int64_t>(j0 + min(jj, jn - 1)) * nin +
-                                                                e8 * (R / 8));
-#pragma unroll
-        for (int q = 0; q < R / 16; ++q) ws[q] = wsr[q];
-    }
     if (tid < kJB) w2s[tid] = tid < jn ? a.w2[j0 + tid] * (1.0f / kGeluAlpha) : 0.f;   // see gelu_scaled
-
-    for (int c0 = q_lo; c0 < q_hi;) {
-        // the chunk: pairs c0 .. c0 + np - 1 of one request, slots t0 .. t0 + np
-        const int req = c0 / (B - 1), p0 = c0 - req * (B - 1);
-        const int np = min(min(C, q_hi - c0), B - 1 - p0);
-        const int64_t t0 = static_cast<int64_t>(req) * B + p0;
-        // ---- 1. direct loads into LDS: each wave instruction fills 64
-        // consecutive 16-byte (or 4-byte) positions; lanes past the end take
-        // no part
-        {
-            const uint16_t* zsrc = a.zhl + t0 * K * (2 * R);
-            const int nseg = (np + 1) * K * ZSEG;
-            for (int s0 = wave * 64; s0 < nseg; s0 += NT) {
-                const int sg = s0 + l;
-                if (sg < nseg) {
-                    const int row = sg / ZSEG, pos = sg - row * ZSEG;
-                    __builtin_amdgcn_global_load_lds((mlp_global_ptr)(zsrc + row * (2 * R) + zpos<ZSEG>(row, pos) * 8),
-                                                     (mlp_lds_ptr)(zbuf + s0 * 8), 16, 0, 0);
-                }
-            }
-            const int nsp = np * (R / 4);       // pair states: consecutive pairs are contiguous
-            for (int s0 = wave * 64; s0 < nsp; s0 += NT)
-                if (s0 + l < nsp)
-                    __builtin_amdgcn_global_load_lds(
-                        (mlp_global_ptr)(a.s + static_cast<int64_t>(c0) * R + 4 * (s0 + l)), (mlp_lds_ptr)(sp + 4 * s0),
-                        16, 0, 0);
-            const int nl = (np + 1) * K;        // the slots' logits
-            for (int s0 = wave * 64; s0 < nl; s0 += NT)
-                if (s0 + l < nl)
-                    __builtin_amdgcn_global_load_lds((mlp_global_ptr)(a.vals + t0 * K + s0 + l), (mlp_lds_ptr)(lv + s0),
-                                                     4, 0, 0);
-        }
-        __syncthreads();   // every load has landed (and the previous chunk's results are stored)
-
-        // ---- 2. c_p partial dots of every pair, column order
-        for (int i = cq; i < np; i += NCQ) {
-            float c = 0.f;
+    // c_p = W1_s s_p for the block's units: thread (jj, kq) dots row j0 + jj
+    // of W1_s with s_p over the quarter kq of its r columns, in column order.
+    // W1 rows are 3r + 2 bf16 long (4-byte aligned: r is a multiple of 16),
+    // so they are read in 32-bit words of two columns each; s_p is read from
+    // LDS once every load of the workgroup has landed.
+    const int jj = tid & (kJB - 1), kqc = tid / kJB;
+    constexpr int kw = R / 4;
+    constexpr int kG = kw / 4;
+    uint32_t wv[2 * kG];
+    {
+        const uint32_t* wr = reinterpret_cast<const uint32_t*>(
+            a.w1 + static_cast<int64_t>(min(j0 + jj, h - 1)) * nin + kqc * kw);
 #pragma unroll
-            for (int q = 0; q < R / 16; ++q) {
-                const float2 sv = *reinterpret_cast<const float2*>(&sp[i * R + e8 * (R / 8) + 2 * q]);
-                c = fmaf(__uint_as_float(ws[q] << 16), sv.x, c);
-                c = fmaf(__uint_as_float(ws[q] & 0xFFFF0000u), sv.y, c);
-            }
-            cps[i][e8][jj] = c;
-        }
-        __syncthreads();
-        // U | V column tiles (lane l holds rows 4 (l / 16) + e, unit 16 g + l % 16)
-        // and P | Q from them, kept scaled by alpha (see gelu_scaled)
-        if (mfma_wave) {
-            const int kq = 8 * (l >> 4);
-            const int jc = 16 * g + (l & 15);
-            for (int i = ph; i < np; i += NG) {
-                float cp = 0.f;
-                if (isu)
-                    cp = (((cps[i][0][jl] + cps[i][1][jl]) + (cps[i][2][jl] + cps[i][3][jl])) +
-                          ((cps[i][4][jl] + cps[i][5][jl]) + (cps[i][6][jl] + cps[i][7][jl]))) + b1j;
-                const int slot = isu ? i : i + 1;
-                const int dst = (2 * i + (isu ? 0 : 1)) * KMAX * kPS;
+        for (int g = 0; g < 2 * kG; ++g) wv[g] = wr[g];
+    }
+    __syncthreads();   // every load has landed: z rows and s_p in LDS
+    for (int i = 0; i < np; ++i) {
+        const float* sp = sps[i] + kqc * kw;
+        float acc = 0.f;
 #pragma unroll
-                for (int rt = 0; rt < KT; ++rt) {
-                    if (rt * 16 >= K) break;
+        for (int g = 0; g < kG; ++g) {
+            const float4 sv = *reinterpret_cast<const float4*>(sp + 4 * g);
+            acc = fmaf(__uint_as_float(wv[2 * g] << 16), sv.x, acc);
+            acc = fmaf(__uint_as_float(wv[2 * g] & 0xFFFF0000u), sv.y, acc);
+            acc = fmaf(__uint_as_float(wv[2 * g + 1] << 16), sv.z, acc);
+            acc = fmaf(__uint_as_float(wv[2 * g + 1] & 0xFFFF0000u), sv.w, acc);
+        }
+        cps4[i][kqc][jj] = acc;
+    }
+
+    // ---- U | V tiles on MFMA (lane l holds rows 4 (l/16) + i, unit l % 16
+    // of a 16 x 16 tile): U of pair i from slot t0 + i, V from slot t0 + i + 1
+    f32x4 accu[NP][KT], accv[NP][KT];
+    if (wave_on) {
+        const int kq = 8 * (l >> 4);
+#pragma unroll
+        for (int i = 0; i < NP; ++i)
+#pragma unroll
+            for (int rt = 0; rt < KT; ++rt) {
+                accu[i][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                accv[i][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (i < np && rt * 16 < K) {
                     // fragment rows past K repeat row K - 1 (not stored)
-                    const int ar = slot * K + min(rt * 16 + (l & 15), K - 1);
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                    const int ar = i * K + min(rt * 16 + (l & 15), K - 1);
+                    const int br = ar + K;
+                    // one k-step's z fragments in registers at a time (the
+                    // compiler barrier keeps the reads from being hoisted together)
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks) {
                         const int sgi = (ks * 32 + kq) / 8;
-                        const u32x4 zf = *reinterpret_cast<const u32x4*>(&zbuf[(ar * ZSEG + zpos<ZSEG>(ar, sgi)) * 8]);
-                        acc = mfma16x16x32(zf, bw[ks % KD], acc);
+                        const u32x4 zu = *reinterpret_cast<const u32x4*>(zs + (ar * ZSEG + zpos<ZSEG>(ar, sgi)) * 8);
+                        const u32x4 zv = *reinterpret_cast<const u32x4*>(zs + (br * ZSEG + zpos<ZSEG>(br, sgi)) * 8);
+                        accu[i][rt] = mfma16x16x32(zu, bu[ks % KD], accu[i][rt]);
+                        accv[i][rt] = mfma16x16x32(zv, bv[ks % KD], accv[i][rt]);
+                        asm volatile("" ::: "memory");
                     }
-                    if (jc < jn) {
+                }
+            }
+    }
+    __syncthreads();   // the z rows are no longer read; P / Q take their place
+
+    // ---- P and Q in the tiles' lane layout
+    if (wave_on) {
+        const int jc = 16 * wave + (l & 15);            // column in P / Q
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int m = rt * 16 + 4 * (l >> 4) + e;
-                            if (m < K) {
-                                constexpr float al = kGeluAlpha;
-                                const float lm = lv[slot * K + m];
-                                pq[dst + static_cast<int>(__umul24(m, kPS)) + jc] =
-                                    isu ? al * (cp + fmaf(wl, lm, acc[e])) : al * fmaf(wl, lm, acc[e]);
-                            }
-                        }
+        for (int i = 0; i < NP; ++i) {
+            if (i >= np) break;
+            const float cp = ((cps4[i][0][jl] + cps4[i][1][jl]) + (cps4[i][2][jl] + cps4[i][3][jl])) + b1j;
+            float* P = Pb + i * K * PS;
+            float* Q = Qb + i * K * PS;
+#pragma unroll
+            for (int rt = 0; rt < KT; ++rt) {
+                if (rt * 16 >= K || jc >= jn) break;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int m = rt * 16 + 4 * (l >> 4) + e;
+                    if (m < K) {   // kept scaled by alpha (see gelu_scaled)
+                        constexpr float al = kGeluAlpha;
+                        const float lp = lv[i * K + m], lq = lv[(i + 1) * K + m];
+                        P[m * PS + jc] = al * (cp + fmaf(wla, lp, accu[i][rt][e]));
+                        Q[m * PS + jc] = al * fmaf(wlb, lq, accv[i][rt][e]);
                     }
                 }
             }
         }
-        __syncthreads();
+    }
+    __syncthreads();
 
-        // ---- 3. GELU and the dot with w2: task t is (pair i, predecessor a,
-        // successors b and b + 1, eighth t % 8 of the block's units); the
-        // eight partial sums meet in a fixed order within each aligned group
-        // of eight lanes.  (24-bit products for the small index arithmetic:
-        // the 64-bit multiply-add the compiler otherwise picks reads a
-        // second, unrelated register.)
-        const int T = np * TP;
-#pragma unroll 1
-        for (int t = tid; t < T; t += NT) {
-            const int i = t / TP, r8 = t - static_cast<int>(__umul24(i, TP));
-            const int q = r8 & 7, rest = r8 >> 3;
-            const int aa = rest / mh, bb = 2 * (rest - static_cast<int>(__umul24(aa, mh)));
-            const bool two = bb + 1 < ms;
-            const int j = 8 * q;
-            float d0 = 0.f, d1 = 0.f, e0 = 0.f, e1 = 0.f;
-            if (j < jn) {
-                const int pb = static_cast<int>(__umul24(2 * i, KMAX * kPS));
-                const int pr = pb + static_cast<int>(__umul24(aa, kPS)) + j;
-                const int qr = pb + static_cast<int>(__umul24(KMAX + bb, kPS)) + j;
-                const int qs = qr + (two ? kPS : 0);
-                const float4 pv0 = *reinterpret_cast<const float4*>(&pq[pr]);
-                const float4 pv1 = *reinterpret_cast<const float4*>(&pq[pr + 4]);
-                const float4 wv0 = *reinterpret_cast<const float4*>(&w2s[j]);
-                const float4 wv1 = *reinterpret_cast<const float4*>(&w2s[j + 4]);
-                const float4 qv0 = *reinterpret_cast<const float4*>(&pq[qr]);
-                const float4 qv1 = *reinterpret_cast<const float4*>(&pq[qr + 4]);
-                const float4 sv0 = *reinterpret_cast<const float4*>(&pq[qs]);
-                const float4 sv1 = *reinterpret_cast<const float4*>(&pq[qs + 4]);
-                d0 = fmaf(wv0.x, gelu_scaled(pv0.x + qv0.x), d0);
-                d1 = fmaf(wv0.y, gelu_scaled(pv0.y + qv0.y), d1);
-                d0 = fmaf(wv0.z, gelu_scaled(pv0.z + qv0.z), d0);
-                d1 = fmaf(wv0.w, gelu_scaled(pv0.w + qv0.w), d1);
-                d0 = fmaf(wv1.x, gelu_scaled(pv1.x + qv1.x), d0);
-                d1 = fmaf(wv1.y, gelu_scaled(pv1.y + qv1.y), d1);
-                d0 = fmaf(wv1.z, gelu_scaled(pv1.z + qv1.z), d0);
-                d1 = fmaf(wv1.w, gelu_scaled(pv1.w + qv1.w), d1);
-                e0 = fmaf(wv0.x, gelu_scaled(pv0.x + sv0.x), e0);
-                e1 = fmaf(wv0.y, gelu_scaled(pv0.y + sv0.y), e1);
-                e0 = fmaf(wv0.z, gelu_scaled(pv0.z + sv0.z), e0);
-                e1 = fmaf(wv0.w, gelu_scaled(pv0.w + sv0.w), e1);
-                e0 = fmaf(wv1.x, gelu_scaled(pv1.x + sv1.x), e0);
-                e1 = fmaf(wv1.y, gelu_scaled(pv1.y + sv1.y), e1);
-                e0 = fmaf(wv1.z, gelu_scaled(pv1.z + sv1.z), e0);
-                e1 = fmaf(wv1.w, gelu_scaled(pv1.w + sv1.w), e1);
-            }
-            float v = d0 + d1, w = e0 + e1;
-            v += dpp_f<kDppXor1>(v);
-            w += dpp_f<kDppXor1>(w);
-            v += dpp_f<kDppXor2>(v);
-            w += dpp_f<kDppXor2>(w);
-            v += dpp_f<kDppHalfMirror>(v);
-            w += dpp_f<kDppHalfMirror>(w);
-            if (q == 0) {
-                const int o = static_cast<int>(__umul24(i, KMAX * KMAX)) + static_cast<int>(__umul24(aa, K)) + bb;
-                res[o] = v;
-                if (two) res[o + 1] = w;
-            }
+    // ---- GELU and the dot with w2: each thread takes successors b and b + 1
+    // of one predecessor a of one pair, so the P row and w2 are read once for
+    // both (each sum keeps its own order)
+    const int ms = a.m;
+    const int mh = (ms + 1) / 2;
+    const int per = K * mh;
+    for (int idx = tid; idx < np * per; idx += 256) {
+        const int i = idx / per, r = idx - i * per;
+        const int aa = r / mh, bb = 2 * (r - aa * mh);
+        const bool two = bb + 1 < ms;
+        const float* pr = Pb + i * K * PS + aa * PS;
+        const float* qr = Qb + i * K * PS + bb * PS;
+        const float* qs = Qb + i * K * PS + (two ? bb + 1 : bb) * PS;
+        float d0 = 0.f, d1 = 0.f, e0 = 0.f, e1 = 0.f;
+        for (int j = 0; j < jn; j += 8) {
+            const float4 pv0 = *reinterpret_cast<const float4*>(pr + j);
+            const float4 pv1 = *reinterpret_cast<const float4*>(pr + j + 4);
+            const float4 wv0 = *reinterpret_cast<const float4*>(w2s + j);
+            const float4 wv1 = *reinterpret_cast<const float4*>(w2s + j + 4);
+            const float4 qv0 = *reinterpret_cast<const float4*>(qr + j);
+            const float4 qv1 = *reinterpret_cast<const float4*>(qr + j + 4);
+            const float4 sv0 = *reinterpret_cast<const float4*>(qs + j);
+            const float4 sv1 = *reinterpret_cast<const float4*>(qs + j + 4);
+            d0 = fmaf(wv0.x, gelu_scaled(pv0.x + qv0.x), d0);
+            d1 = fmaf(wv0.y, gelu_scaled(pv0.y + qv0.y), d1);
+            d0 = fmaf(wv0.z, gelu_scaled(pv0.z + qv0.z), d0);
+            d1 = fmaf(wv0.w, gelu_scaled(pv0.w + qv0.w), d1);
+            d0 = fmaf(wv1.x, gelu_scaled(pv1.x + qv1.x), d0);
+            d1 = fmaf(wv1.y, gelu_scaled(pv1.y + qv1.y), d1);
+            d0 = fmaf(wv1.z, gelu_scaled(pv1.z + qv1.z), d0);
+            d1 = fmaf(wv1.w, gelu_scaled(pv1.w + qv1.w), d1);
+            e0 = fmaf(wv0.x, gelu_scaled(pv0.x + sv0.x), e0);
+            e1 = fmaf(wv0.y, gelu_scaled(pv0.y + sv0.y), e1);
+            e0 = fmaf(wv0.z, gelu_scaled(pv0.z + sv0.z), e0);
+            e1 = fmaf(wv0.w, gelu_scaled(pv0.w + sv0.w), e1);
+            e0 = fmaf(wv1.x, gelu_scaled(pv1.x + sv1.x), e0);
+            e1 = fmaf(wv1.y, gelu_scaled(pv1.y + sv1.y), e1);
+            e0 = fmaf(wv1.z, gelu_scaled(pv1.z + sv1.z), e0);
+            e1 = fmaf(wv1.w, gelu_scaled(pv1.w + sv1.w), e1);
         }
-        __syncthreads();
-        // ---- 4. the chunk's partial Deltas, each pair's K x K contiguous
-        for (int e = tid; e < np * K * K; e += NT) {
-            const int i = e / (K * K), r = e - i * K * K;
-            if (r % K < ms)
-                a.part[(static_cast<int64_t>(c0 + i) * nj + jb) * K * K + r] = res[i * KMAX * KMAX + r];
-        }
-        c0 += np;
+        float* out = a.part + (static_cast<int64_t>(pair0 + i) * nj + jblk) * K * K + aa * K + bb;
+        out[0] = d0 + d1;
+        if (two) out[1] = e0 + e1;
     }
 }
 
 // ------------------------------------------------------------- K <= 16 --
 // The transition MLP for K <= 16, with a workgroup's waves split by role.
-// Work assignment and arithmetic are those of mlp_chunk_kernel (nj equal
-// groups of workgroups, one per block of 64 hidden units, each a contiguous
-// run of pairs), but the run is streamed one pair at a time:
+// The launch's workgroups form nj equal groups, one per block of 64 hidden
+// units; each workgroup takes a contiguous run of the pairs (at most 256
+// workgroups, one per CU) and streams it one pair at a time:
 //   - waves 12-15 (producers) load the next pair's z rows, pair state and
 //     logits into registers (coalesced 16-byte loads) while they finish the
 //     current one, write them to LDS, form c_p and the U | V tiles (each
@@ -648,27 +639,44 @@ __global__ __launch_bounds__(kWsThreads, 1) void mlp_ws_kernel(MlpArgs a) {
 
 int mlp_blocks(int h) { return (h + kJB - 1) / kJB; }
 
+// Pairs per workgroup of the K > 16 kernel.
+constexpr int kMlpPairs = 2;
+
+// Dynamic LDS of the K > 16 kernel: the z rows of the group's slots, or P and
+// Q of its pairs, whichever is larger.
+static size_t mlp_lds_bytes(int K, int r) {
+    const size_t z = static_cast<size_t>(kMlpPairs + 1) * K * 2 * r * sizeof(uint16_t);
+    const size_t pq = static_cast<size_t>(2 * kMlpPairs) * K * (kJB + 4) * sizeof(float);
+    return z > pq ? z : pq;
+}
+
 template <int R>
-hipError_t launch_mlp_r(const MlpArgs& a, dim3 grid, hipStream_t stream) {
-    if (a.K <= 16) return launch(mlp_ws_kernel<R>, grid, kWsThreads, 0, stream, a);
-    if (a.K <= 32) return launch(mlp_chunk_kernel<R, 2>, grid, MlpShape<R, 2>::NT, 0, stream, a);
-    return launch(mlp_chunk_kernel<R, 4>, grid, MlpShape<R, 4>::NT, 0, stream, a);
+hipError_t launch_mlp_r(const MlpArgs& a, hipStream_t stream) {
+    const int nj = mlp_blocks(a.h);
+    if (a.K <= 16) {
+        // nj equal groups of workgroups, one per block of hidden units, each
+        // workgroup a run of at least one pair
+        const int64_t pairs = static_cast<int64_t>(a.n) * (a.B - 1);
+        int64_t per = kMlpGrid / nj;
+        if (per > pairs) per = pairs;
+        return launch(mlp_ws_kernel<R>, dim3(static_cast<unsigned>(per * nj)), kWsThreads, 0, stream, a);
+    }
+    // one workgroup per (group of kMlpPairs pairs, block); groups rounded up to
+    // eight so that the blocks of a group share an XCD
+    const int groups = a.n * ((a.B - 1 + kMlpPairs - 1) / kMlpPairs);
+    const dim3 grid(static_cast<unsigned>((groups + 7) / 8 * 8 * nj));
+    const uint32_t lds = static_cast<uint32_t>(mlp_lds_bytes(a.K, a.r));
+    if (a.K <= 32) return launch(mlp_kernel<R, 2, kMlpPairs>, grid, 256, lds, stream, a);
+    return launch(mlp_kernel<R, 4, kMlpPairs>, grid, 256, lds, stream, a);
 }
 
 hipError_t launch_mlp(const MlpArgs& a, hipStream_t stream) {
     if (a.B < 2 || a.n < 1) return hipSuccess;
-    // nj equal groups of workgroups, one per block of hidden units, each
-    // workgroup a run of at least one pair
-    const int nj = mlp_blocks(a.h);
-    const int64_t pairs = static_cast<int64_t>(a.n) * (a.B - 1);
-    int64_t per = kMlpGrid / nj;
-    if (per > pairs) per = pairs;
-    const dim3 grid(static_cast<unsigned>(per * nj));
     switch (a.r) {
-        case 16: return launch_mlp_r<16>(a, grid, stream);
-        case 32: return launch_mlp_r<32>(a, grid, stream);
-        case 64: return launch_mlp_r<64>(a, grid, stream);
-        case 128: return launch_mlp_r<128>(a, grid, stream);
+        case 16: return launch_mlp_r<16>(a, stream);
+        case 32: return launch_mlp_r<32>(a, stream);
+        case 64: return launch_mlp_r<64>(a, stream);
+        case 128: return launch_mlp_r<128>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }
