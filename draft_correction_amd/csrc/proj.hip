@@ -297,7 +297,6 @@ __global__ __launch_bounds__(kGThreads) void gemm_gather_kernel(GemmJob J) {
 // ------------------------------------------------------------------- cand --
 
 constexpr int kCR = 32;                 // candidate rows per workgroup
-constexpr int kCRT = (kCR + 15) / 16;   // 16-row MFMA tiles per workgroup
 constexpr int kCT = 512;                // threads of a candidate workgroup
 constexpr int kCW = kCT / kWave;        // its waves
 constexpr int kCRows = 4 * kCW;         // 16-lane rows it processes at a time
