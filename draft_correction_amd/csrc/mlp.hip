@@ -325,6 +325,7 @@ __global__ __launch_bounds__(256, KT > 2 ? 4 : (NP == 1 ? 7 : 5)) void mlp_kerne
 // ones.  No workgroup barrier is used after the roles split; every wait on
 // a counter is bounded (kSpinLimit sleeps), so the workgroup always ends.
 constexpr int kRing = 3;            // P | Q buffers
+constexpr int kMaxRun = 64;         // pairs per workgroup, at most (their c_p are formed up front)
 constexpr int kProd = 4;            // producer waves
 constexpr int kCons = 12;           // consumer waves
 constexpr int kWsThreads = 64 * (kProd + kCons);
@@ -348,10 +349,11 @@ __global__ __launch_bounds__(kWsThreads, 1) void mlp_ws_kernel(MlpArgs a) {
     constexpr int PT = 64 * kProd;              // producer threads
     constexpr int ZPT = (2 * KMAX * ZSEG + PT - 1) / PT;   // z segments per producer thread, at most
     constexpr int PQ = 2 * KMAX * kPS;          // floats of one P | Q buffer
-    static_assert(2 * KMAX <= PT && R / 4 <= PT, "one logit and one s_p segment per producer thread");
+    static_assert(2 * KMAX <= PT, "one logit per producer thread");
     __shared__ __attribute__((aligned(16))) uint16_t zbuf[2 * KMAX * 2 * R];
     __shared__ __attribute__((aligned(16))) float ring[kRing * PQ];
-    __shared__ __attribute__((aligned(16))) float sp[R];
+    __shared__ float cpr[kMaxRun][kJB];         // c_p + b1 of every pair of the run
+    __shared__ __attribute__((aligned(16))) float spa[kMaxRun * R];   // the run's pair states
     __shared__ float lv[2 * KMAX];
     __shared__ __attribute__((aligned(16))) float w2s[kJB];
     // the block's W1_s rows as 32-bit words of two columns, rows padded
@@ -364,6 +366,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void mlp_ws_kernel(MlpArgs a) {
     __shared__ int ready[kRing];                // generation (unit index + 1) of each buffer's contents
     __shared__ int freed[kRing];                // consumer waves done with each buffer, cumulative
     __shared__ int pbar;                        // producer-wave barrier count
+    __shared__ int cpn[kMaxRun];                // consumer waves done with each pair's c_p (4 when formed)
 
     const int tid = threadIdx.x, l = tid & 63, wave = tid >> 6;
     const int B = a.B, K = a.K, h = a.h;
@@ -406,15 +409,23 @@ __global__ __launch_bounds__(kWsThreads, 1) void mlp_ws_kernel(MlpArgs a) {
     const int pt = tid - 64 * kCons;            // producer thread 0 .. PT - 1 (negative: consumer)
     const int nseg = 2 * K * ZSEG;
     u32x4 zr[ZPT];
-    float4 spr;
     float lvr;
     auto fetch = [&](const Coord& c) {
         const uint16_t* zsrc = a.zhl + static_cast<int64_t>(c.t0) * K * (2 * R);
 #pragma unroll
         for (int i = 0; i < ZPT; ++i) zr[i] = load16(zsrc + min(pt + i * PT, nseg - 1) * 8);   // clamped: not written
-        spr = *reinterpret_cast<const float4*>(a.s + static_cast<int64_t>(c.pair) * R + 4 * min(pt, R / 4 - 1));
         lvr = a.vals[static_cast<int64_t>(c.t0) * K + min(pt, 2 * K - 1)];
     };
+    // the run's pair states (consecutive pairs are contiguous) straight into
+    // LDS, for the c_p of every pair below
+    {
+        const int nsp = n * (R / 4);
+        const float* ssrc = a.s + static_cast<int64_t>(q_lo) * R;
+        for (int s0 = wave * 64; s0 < nsp; s0 += kWsThreads)
+            if (s0 + l < nsp)
+                __builtin_amdgcn_global_load_lds((mlp_global_ptr)(ssrc + 4 * (s0 + l)), (mlp_lds_ptr)(spa + 4 * s0), 16,
+                                                 0, 0);
+    }
     if (wave >= kCons) fetch(first(q_lo));
 
     if (tid < kJB) w2s[tid] = tid < jn ? a.w2[j0 + tid] * (1.0f / kGeluAlpha) : 0.f;   // see gelu_scaled
@@ -433,8 +444,50 @@ __global__ __launch_bounds__(kWsThreads, 1) void mlp_ws_kernel(MlpArgs a) {
         ready[tid] = 0;
         freed[tid] = 0;
     }
+    if (tid < kMaxRun) cpn[tid] = 0;
     if (tid == 0) pbar = 0;
     __syncthreads();
+
+    // ---- c_p + b1 of every pair of the run (n <= kMaxRun), formed by the
+    // consumer waves, in pair order, while the producers stage and multiply
+    // the first pairs: job (pair i, group ug of 16 units) per wave; lane l
+    // dots a quarter l / 16 of r of unit 16 ug + l % 16 (W1_s words and s_p
+    // from LDS), column order, and the four quarters are added in a fixed
+    // order across lanes l, l ^ 16, l ^ 32, l ^ 48.  cpn[i] counts the jobs
+    // of pair i done; the producers wait for 4 before writing its P.
+    for (int job = wave; wave < kCons && job < n * (kJB / 16); job += kCons) {
+        const int i = job >> 2, ug = job & 3;
+        const int jl = min(16 * ug + (l & 15), jn - 1);   // clamped: past jn not used
+        constexpr int WQ = R / 8;           // words of a quarter of r
+        const int e4 = l >> 4;
+        const float* sq = spa + i * R + e4 * (R / 4);
+        float acc = 0.f;
+        if constexpr (WQ % 2 == 0) {
+#pragma unroll
+            for (int q2 = 0; q2 < WQ / 2; ++q2) {
+                const float4 sv = *reinterpret_cast<const float4*>(sq + 4 * q2);
+                const uint32_t w0 = wsl[jl * WSW + e4 * WQ + 2 * q2], w1 = wsl[jl * WSW + e4 * WQ + 2 * q2 + 1];
+                acc = fmaf(__uint_as_float(w0 << 16), sv.x, acc);
+                acc = fmaf(__uint_as_float(w0 & 0xFFFF0000u), sv.y, acc);
+                acc = fmaf(__uint_as_float(w1 << 16), sv.z, acc);
+                acc = fmaf(__uint_as_float(w1 & 0xFFFF0000u), sv.w, acc);
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < WQ; ++q) {
+                const float2 sv = *reinterpret_cast<const float2*>(sq + 2 * q);
+                const uint32_t w = wsl[jl * WSW + e4 * WQ + q];
+                acc = fmaf(__uint_as_float(w << 16), sv.x, acc);
+                acc = fmaf(__uint_as_float(w & 0xFFFF0000u), sv.y, acc);
+            }
+        }
+        acc += __shfl_xor(acc, 16, 64);
+        acc += __shfl_xor(acc, 32, 64);
+        if (l < 16) cpr[i][16 * ug + l] = acc + a.b1[j0 + jl];
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the c_p are in LDS
+        asm volatile("" ::: "memory");
+        if (l == 0) atomicAdd(&cpn[i], 1);
+    }
 
     if (wave >= kCons) {
         // ================================================= producers ==
@@ -457,7 +510,20 @@ __global__ __launch_bounds__(kWsThreads, 1) void mlp_ws_kernel(MlpArgs a) {
         const int jl = min(16 * pw + (l & 15), jn - 1);
         const float wla = bf16_to_f32(a.w1[static_cast<int64_t>(j0 + jl) * nin + 3 * R]);
         const float wlb = bf16_to_f32(a.w1[static_cast<int64_t>(j0 + jl) * nin + 3 * R + 1]);
-        const float b1j = a.b1[j0 + jl];
+        // the wave's W1_za and W1_zb fragments, the same for every pair (the
+        // [hi | lo] halves of z meet the same R / 32 column fragments)
+        constexpr int KD = R >= 32 ? R / 32 : 1;
+        u32x4 bu[KD], bv[KD];
+        {
+            const int wrow = (16 * pw + (l & 15)) * WZ;   // the lane's unit (rows past jn are not stored)
+            const int kq = 8 * (l >> 4);
+#pragma unroll
+            for (int d = 0; d < KD; ++d) {
+                const int wcol = (d * 32 + kq) % R;
+                bu[d] = *reinterpret_cast<const u32x4*>(&wza[wrow + wcol]);
+                bv[d] = *reinterpret_cast<const u32x4*>(&wzb[wrow + wcol]);
+            }
+        }
         Coord c = first(q_lo);
         for (int u = 0; u < n; ++u) {
             const int slot = u % kRing;
@@ -470,43 +536,11 @@ __global__ __launch_bounds__(kWsThreads, 1) void mlp_ws_kernel(MlpArgs a) {
                     *reinterpret_cast<u32x4*>(&zbuf[(row * ZSEG + zpos<ZSEG>(row, pos)) * 8]) = zr[i];
                 }
             }
-            if (pt < R / 4) *reinterpret_cast<float4*>(&sp[4 * pt]) = spr;
             if (pt < 2 * K) lv[pt] = lvr;
-            pbarrier();                           // z rows, s_p and logits in LDS
+            pbarrier();                           // z rows and logits in LDS
             if (u + 1 < n) {
                 c = step(c);
                 fetch(c);
-            }
-            // c_p of the lane's unit 16 pw + l % 16 (zero past jn is not
-            // stored): a quarter l / 16 of r per lane, column order, then the
-            // four quarters added in a fixed order across lanes l, l ^ 16,
-            // l ^ 32, l ^ 48 (every lane gets the same sum)
-            float cp;
-            {
-                constexpr int WQ = R / 8;           // words of a quarter of r
-                const int e4 = l >> 4;
-                uint32_t wv[WQ];
-                if constexpr (WQ % 4 == 0) {
-#pragma unroll
-                    for (int q4 = 0; q4 < WQ / 4; ++q4) {
-                        const u32x4 w4 = *reinterpret_cast<const u32x4*>(&wsl[jl * WSW + e4 * WQ + 4 * q4]);
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) wv[4 * q4 + q] = w4[q];
-                    }
-                } else {
-#pragma unroll
-                    for (int q = 0; q < WQ; ++q) wv[q] = wsl[jl * WSW + e4 * WQ + q];
-                }
-                float acc = 0.f;
-#pragma unroll
-                for (int q = 0; q < WQ; ++q) {
-                    const float2 sv = *reinterpret_cast<const float2*>(&sp[e4 * (R / 4) + 2 * q]);
-                    acc = fmaf(__uint_as_float(wv[q] << 16), sv.x, acc);
-                    acc = fmaf(__uint_as_float(wv[q] & 0xFFFF0000u), sv.y, acc);
-                }
-                acc += __shfl_xor(acc, 16, 64);
-                acc += __shfl_xor(acc, 32, 64);
-                cp = acc + b1j;
             }
             // U (slot 0 rows) and V (slot 1 rows) of the wave's column tile;
             // fragment rows past K repeat row K - 1 (not stored)
@@ -514,23 +548,22 @@ __global__ __launch_bounds__(kWsThreads, 1) void mlp_ws_kernel(MlpArgs a) {
             if (tile_on) {
                 const int kq = 8 * (l >> 4);
                 const int ra = min(l & 15, K - 1), rb = K + ra;
-                const int wrow = (16 * pw + (l & 15)) * WZ;   // the lane's unit (rows past jn are not stored)
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     const int sgi = (ks * 32 + kq) / 8;
-                    const int wcol = (ks * 32 + kq) % R;       // the hi and lo halves meet the same columns
                     const u32x4 za = *reinterpret_cast<const u32x4*>(&zbuf[(ra * ZSEG + zpos<ZSEG>(ra, sgi)) * 8]);
                     const u32x4 zb = *reinterpret_cast<const u32x4*>(&zbuf[(rb * ZSEG + zpos<ZSEG>(rb, sgi)) * 8]);
-                    const u32x4 bu = *reinterpret_cast<const u32x4*>(&wza[wrow + wcol]);
-                    const u32x4 bv = *reinterpret_cast<const u32x4*>(&wzb[wrow + wcol]);
-                    au = mfma16x16x32(za, bu, au);
-                    av = mfma16x16x32(zb, bv, av);
+                    au = mfma16x16x32(za, bu[ks % KD], au);
+                    av = mfma16x16x32(zb, bv[ks % KD], av);
                 }
             }
             // the buffer is free once every consumer wave is done with its
             // previous contents (pair u - kRing)
             spin_until(as_lds(&freed[slot]), kCons * (u / kRing));
-            // P and Q, kept scaled by alpha (see gelu_scaled)
+            // P and Q, kept scaled by alpha (see gelu_scaled), P once the
+            // pair's c_p are formed
+            spin_until(as_lds(&cpn[u]), kJB / 16);
+            const float cp = cpr[u][16 * pw + (l & 15)];   // c_p + b1 of the lane's unit
             const int jc = 16 * pw + (l & 15);
             if (tile_on && jc < jn) {
                 float* buf = ring + slot * PQ;
@@ -658,6 +691,7 @@ hipError_t launch_mlp_r(const MlpArgs& a, hipStream_t stream) {
         // workgroup a run of at least one pair
         const int64_t pairs = static_cast<int64_t>(a.n) * (a.B - 1);
         int64_t per = kMlpGrid / nj;
+        if (per * kMaxRun < pairs) per = (pairs + kMaxRun - 1) / kMaxRun;   // runs of at most kMaxRun pairs
         if (per > pairs) per = pairs;
         return launch(mlp_ws_kernel<R>, dim3(static_cast<unsigned>(per * nj)), kWsThreads, 0, stream, a);
     }
