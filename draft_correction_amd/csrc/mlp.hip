@@ -311,19 +311,21 @@ __global__ __launch_bounds__(256, KT > 2 ? 4 : (NP == 1 ? 7 : 5)) void mlp_kerne
 // The launch's workgroups form nj equal groups, one per block of 64 hidden
 // units; each workgroup takes a contiguous run of the pairs (at most 256
 // workgroups, one per CU) and streams it one pair at a time:
-//   - waves 12-15 (producers) load the next pair's z rows, pair state and
-//     logits into registers (coalesced 16-byte loads) while they finish the
-//     current one, write them to LDS, form c_p and the U | V tiles (each
-//     producer wave one 16-unit column tile of both, its lanes splitting
-//     the c_p dots of the tile's units in quarters of r) and write P | Q
-//     into one of kRing LDS buffers;
-//   - waves 0-11 (consumers) run each pair's GELU loop as soon as its buffer
-//     is ready and store its partial Deltas.
+//   - waves 12-15 (producers) load the next pair's z rows and logits into
+//     registers (coalesced 16-byte loads) while they finish the current one,
+//     write them to LDS, form the U | V tiles (each producer wave one 16-unit
+//     column tile of both, its W1 fragments held in registers) and write
+//     P | Q into one of kRing LDS buffers;
+//   - waves 0-11 (consumers) first form c_p + b1 of every pair of the run,
+//     in pair order (the producers wait for a pair's before writing its P),
+//     then run each pair's GELU loop as soon as its buffer is ready and
+//     store its partial Deltas.
 // The two sides meet through LDS counters (the generation written into a
 // buffer, and how many consumer waves are done with it), so the loads and
 // matrix products of later pairs overlap the vector-ALU work of earlier
-// ones.  No workgroup barrier is used after the roles split; every wait on
-// a counter is bounded (kSpinLimit sleeps), so the workgroup always ends.
+// ones.  No workgroup barrier is used after the roles split (the producers
+// meet through an LDS counter of their own); every wait on a counter is
+// bounded (kSpinLimit sleeps), so the workgroup always ends.
 constexpr int kRing = 3;            // P | Q buffers
 constexpr int kMaxRun = 64;         // pairs per workgroup, at most (their c_p are formed up front)
 constexpr int kProd = 4;            // producer waves
