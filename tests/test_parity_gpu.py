@@ -250,6 +250,23 @@ def test_stress(head):
         assert total_moved > 0
 
 
+def test_long_runs():
+    """Many requests at K = 16 and the full hidden width (400 blocks of a small
+    vocabulary and d): the K <= 16 MLP's workgroups then take runs of 64 pairs,
+    the most one holds (more workgroups than CUs), across request boundaries.
+    Sampled requests against the oracle, the first and last included, with the
+    walk-stress head so the walk moves."""
+    _log("long runs n=400 K=16 h=256")
+    x = P.inputs("b1", head="stress", n=400, V=4096, d=64, de=64)
+    gpu = P.gpu_run(x)
+    total_moved = 0
+    for i in (0, 1, 63, 64, 199, 398, 399):
+        ora = P.oracle_run(x, n=1, first=i)
+        steps, exempt, moved = P.check_all(P.select(gpu, i, 1), ora, "long runs/%d" % i)
+        total_moved += moved
+    assert total_moved > 0
+
+
 # ---------------------------------------------------- folded projection --
 
 @pytest.mark.parametrize("name,head", [("tiny", "stress"), ("b1", "stress"), ("b32", "normal"),
