@@ -54,8 +54,9 @@ __device__ __forceinline__ float gelu_scaled(float y) {
 constexpr int kJB = 64;
 static_assert(256 / kJB <= kMaxMlpBlocks, "the finishing kernel sums at most kMaxMlpBlocks blocks");
 constexpr int kPS = kJB + 4;        // LDS row stride of P / Q (floats)
-// Workgroups of one launch, at most: one per CU, each running a contiguous
-// share of the pairs of one block of hidden units.
+// Workgroups of a launch for K <= 16: one per CU, each running a contiguous
+// share of the pairs of one block of hidden units (more when a share would
+// exceed kMaxRun pairs).
 constexpr int kMlpGrid = 256;
 
 typedef __attribute__((address_space(3))) void* mlp_lds_ptr;
@@ -309,8 +310,9 @@ __global__ __launch_bounds__(256, KT > 2 ? 4 : (NP == 1 ? 7 : 5)) void mlp_kerne
 // ------------------------------------------------------------- K <= 16 --
 // The transition MLP for K <= 16, with a workgroup's waves split by role.
 // The launch's workgroups form nj equal groups, one per block of 64 hidden
-// units; each workgroup takes a contiguous run of the pairs (at most 256
-// workgroups, one per CU) and streams it one pair at a time:
+// units; each workgroup takes a contiguous run of at most kMaxRun pairs (256
+// workgroups, one per CU, unless the runs would be longer) and streams it one
+// pair at a time:
 //   - waves 12-15 (producers) load the next pair's z rows and logits into
 //     registers (coalesced 16-byte loads) while they finish the current one,
 //     write them to LDS, form the U | V tiles (each producer wave one 16-unit
@@ -365,7 +367,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void mlp_ws_kernel(MlpArgs a) {
     constexpr int WZ = R + 8;
     __shared__ __attribute__((aligned(16))) uint16_t wza[kJB * WZ];
     __shared__ __attribute__((aligned(16))) uint16_t wzb[kJB * WZ];
-    __shared__ int ready[kRing];                // generation (unit index + 1) of each buffer's contents
+    __shared__ int ready[kRing];                // generation (pair index in the run + 1) of each buffer's contents
     __shared__ int freed[kRing];                // consumer waves done with each buffer, cumulative
     __shared__ int pbar;                        // producer-wave barrier count
     __shared__ int cpn[kMaxRun];                // consumer waves done with each pair's c_p (4 when formed)
