@@ -333,6 +333,7 @@ constexpr int kMaxRun = 64;         // pairs per workgroup, at most (their c_p a
 constexpr int kProd = 4;            // producer waves
 constexpr int kCons = 12;           // consumer waves
 constexpr int kWsThreads = 64 * (kProd + kCons);
+static_assert(kCons % 4 == 0 && kProd == 4, "a wave's units (16 (wave % 4) ..) are the same in every c_p job and P | Q tile");
 constexpr unsigned kSpinLimit = 1u << 22;
 
 // Waits until the LDS counter reaches `target` (counters only grow).  The
@@ -363,10 +364,6 @@ __global__ __launch_bounds__(kWsThreads, 1) void mlp_ws_kernel(MlpArgs a) {
     // the block's W1_s rows as 32-bit words of two columns, rows padded
     constexpr int WSW = R / 2 + 4;
     __shared__ __attribute__((aligned(16))) uint32_t wsl[kJB * WSW];
-    // the block's W1_za and W1_zb rows (bf16), rows padded by 16 bytes
-    constexpr int WZ = R + 8;
-    __shared__ __attribute__((aligned(16))) uint16_t wza[kJB * WZ];
-    __shared__ __attribute__((aligned(16))) uint16_t wzb[kJB * WZ];
     __shared__ int ready[kRing];                // generation (pair index in the run + 1) of each buffer's contents
     __shared__ int freed[kRing];                // consumer waves done with each buffer, cumulative
     __shared__ int pbar;                        // producer-wave barrier count
@@ -432,17 +429,37 @@ __global__ __launch_bounds__(kWsThreads, 1) void mlp_ws_kernel(MlpArgs a) {
     }
     if (wave >= kCons) fetch(first(q_lo));
 
-    if (tid < kJB) w2s[tid] = tid < jn ? a.w2[j0 + tid] * (1.0f / kGeluAlpha) : 0.f;   // see gelu_scaled
-    for (int idx = tid; idx < kJB * (R / 2); idx += kWsThreads) {
-        const int jj = idx / (R / 2), w = idx - jj * (R / 2);
-        wsl[jj * WSW + w] =
-            reinterpret_cast<const uint32_t*>(a.w1 + static_cast<int64_t>(j0 + min(jj, jn - 1)) * nin)[w];
+    // the block's W1_s slice straight into LDS as well, one instruction per
+    // row (its r bf16 at column 0, r / 2 four-byte words; rows are 4-byte
+    // aligned: nin is even), so every load of the prologue is in flight at
+    // once; rows past jn repeat row jn - 1 and are not used
+    for (int jj = wave; jj < kJB; jj += kWsThreads / 64) {
+        const uint16_t* src = a.w1 + static_cast<int64_t>(j0 + min(jj, jn - 1)) * nin;
+        if (l < R / 2)
+            __builtin_amdgcn_global_load_lds((mlp_global_ptr)(src + 2 * l), (mlp_lds_ptr)(&wsl[jj * WSW]), 4, 0, 0);
     }
-    for (int idx = tid; idx < kJB * (R / 8); idx += kWsThreads) {   // 16-byte pieces
-        const int jj = idx / (R / 8), w = idx - jj * (R / 8);
-        const uint16_t* row = a.w1 + static_cast<int64_t>(j0 + min(jj, jn - 1)) * nin;
-        *reinterpret_cast<u32x4*>(&wza[jj * WZ + 8 * w]) = load16(row + R + 8 * w);
-        *reinterpret_cast<u32x4*>(&wzb[jj * WZ + 8 * w]) = load16(row + 2 * R + 8 * w);
+    const float w2v = a.w2[j0 + min(tid, jn - 1)];   // loaded unconditionally: no wait inside a branch
+    // b1 of the lane's unit in the c_p jobs below (a consumer wave's jobs all
+    // cover units 16 (wave % 4) .. + 15), and the logit columns w_la, w_lb of
+    // a producer lane's unit
+    const int ju = min(16 * (wave & 3) + (l & 15), jn - 1);
+    const float b1v = a.b1[j0 + ju];
+    const float wla = bf16_to_f32(a.w1[static_cast<int64_t>(j0 + ju) * nin + 3 * R]);
+    const float wlb = bf16_to_f32(a.w1[static_cast<int64_t>(j0 + ju) * nin + 3 * R + 1]);
+    // a producer wave's W1_za and W1_zb fragments (its 16 units), the same
+    // for every pair (the [hi | lo] halves of z meet the same R / 32 column
+    // fragments), loaded straight into registers
+    constexpr int KD = R >= 32 ? R / 32 : 1;
+    u32x4 bu[KD], bv[KD];
+    if (wave >= kCons) {
+        const uint16_t* wrow = a.w1 + static_cast<int64_t>(j0 + ju) * nin;
+        const int kq = 8 * (l >> 4);
+#pragma unroll
+        for (int d = 0; d < KD; ++d) {
+            const int wcol = (d * 32 + kq) % R;
+            bu[d] = load16(wrow + R + wcol);
+            bv[d] = load16(wrow + 2 * R + wcol);
+        }
     }
     if (tid < kRing) {
         ready[tid] = 0;
@@ -450,6 +467,8 @@ __global__ __launch_bounds__(kWsThreads, 1) void mlp_ws_kernel(MlpArgs a) {
     }
     if (tid < kMaxRun) cpn[tid] = 0;
     if (tid == 0) pbar = 0;
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): every direct load (and the first pair's z rows) has landed
+    if (tid < kJB) w2s[tid] = tid < jn ? w2v * (1.0f / kGeluAlpha) : 0.f;   // see gelu_scaled
     __syncthreads();
 
     // ---- c_p + b1 of every pair of the run (n <= kMaxRun), formed by the
@@ -487,7 +506,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void mlp_ws_kernel(MlpArgs a) {
         }
         acc += __shfl_xor(acc, 16, 64);
         acc += __shfl_xor(acc, 32, 64);
-        if (l < 16) cpr[i][16 * ug + l] = acc + a.b1[j0 + jl];
+        if (l < 16) cpr[i][16 * ug + l] = acc + b1v;
         __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the c_p are in LDS
         asm volatile("" ::: "memory");
         if (l == 0) atomicAdd(&cpn[i], 1);
@@ -511,23 +530,6 @@ __global__ __launch_bounds__(kWsThreads, 1) void mlp_ws_kernel(MlpArgs a) {
         // the block's W1 slices: U and V fragments of the wave's 16 units,
         // and for c_p (thread: unit pt % 64, quarter pt / 64 of r) W1_s words
         const bool tile_on = 16 * pw < jn;
-        const int jl = min(16 * pw + (l & 15), jn - 1);
-        const float wla = bf16_to_f32(a.w1[static_cast<int64_t>(j0 + jl) * nin + 3 * R]);
-        const float wlb = bf16_to_f32(a.w1[static_cast<int64_t>(j0 + jl) * nin + 3 * R + 1]);
-        // the wave's W1_za and W1_zb fragments, the same for every pair (the
-        // [hi | lo] halves of z meet the same R / 32 column fragments)
-        constexpr int KD = R >= 32 ? R / 32 : 1;
-        u32x4 bu[KD], bv[KD];
-        {
-            const int wrow = (16 * pw + (l & 15)) * WZ;   // the lane's unit (rows past jn are not stored)
-            const int kq = 8 * (l >> 4);
-#pragma unroll
-            for (int d = 0; d < KD; ++d) {
-                const int wcol = (d * 32 + kq) % R;
-                bu[d] = *reinterpret_cast<const u32x4*>(&wza[wrow + wcol]);
-                bv[d] = *reinterpret_cast<const u32x4*>(&wzb[wrow + wcol]);
-            }
-        }
         Coord c = first(q_lo);
         for (int u = 0; u < n; ++u) {
             const int slot = u % kRing;
@@ -562,12 +564,20 @@ __global__ __launch_bounds__(kWsThreads, 1) void mlp_ws_kernel(MlpArgs a) {
                 }
             }
             // the buffer is free once every consumer wave is done with its
-            // previous contents (pair u - kRing)
-            spin_until(as_lds(&freed[slot]), kCons * (u / kRing));
-            // P and Q, kept scaled by alpha (see gelu_scaled), P once the
-            // pair's c_p are formed
-            spin_until(as_lds(&cpn[u]), kJB / 16);
-            const float cp = cpr[u][16 * pw + (l & 15)];   // c_p + b1 of the lane's unit
+            // previous contents (pair u - kRing), and P needs the pair's c_p:
+            // both counters and the lane's c_p are read in one round (LDS
+            // requests of a wave complete in order, so a c_p read issued
+            // after a count of 4 was read returns the formed value)
+            float cp = 0.f;
+            for (unsigned it = 0; it < kSpinLimit; ++it) {
+                const int fr = *as_lds(&freed[slot]);
+                const int cn = *as_lds(&cpn[u]);
+                cp = *(__attribute__((address_space(3))) volatile float*)(&cpr[u][16 * pw + (l & 15)]);
+                if (fr >= kCons * (u / kRing) && cn >= kJB / 16) break;
+                __builtin_amdgcn_s_sleep(1);
+            }
+            asm volatile("" ::: "memory");
+            // P and Q, kept scaled by alpha (see gelu_scaled)
             const int jc = 16 * pw + (l & 15);
             if (tile_on && jc < jn) {
                 float* buf = ring + slot * PQ;
