@@ -59,6 +59,18 @@ def test_tiny_rep_widths(r):
     P.check_all(gpu, ora, "tiny/r=%d" % r)
 
 
+@pytest.mark.parametrize("K", [1, 5, 13])
+def test_tiny_small_k(K):
+    """K = 1 (one candidate per slot: every pair a single transition, the walk
+    fixed), and odd K below 16 (the last predecessor and successor tasks of the
+    K <= 16 MLP consumers cut short)."""
+    _log("tiny K=%d" % K)
+    x = P.inputs("tiny", head="stress", K=K, n=2, B=4)
+    gpu = P.gpu_run(x)
+    ora = P.oracle_run(x)
+    P.check_all(gpu, ora, "tiny/K=%d" % K)
+
+
 @pytest.mark.parametrize("K", [37, 64])
 def test_tiny_wide_k(K):
     """K = 37 (three 16-row tiles, the last ragged, in the MLP's U | V
@@ -68,6 +80,19 @@ def test_tiny_wide_k(K):
     gpu = P.gpu_run(x)
     ora = P.oracle_run(x)
     P.check_all(gpu, ora, "tiny/K=%d" % K)
+
+
+@pytest.mark.parametrize("h,K", [(80, 16), (208, 16), (80, 37), (208, 37)])
+def test_tiny_mlp_widths(h, K):
+    """MLP hidden widths whose last block of 64 units is partial (h = 80: 64 +
+    16; h = 208: three full blocks + 16), in both MLP kernels (K <= 16 and
+    K > 16): the finishing step sums several block partials, one of them from
+    a block whose producer tiles and consumer units are cut at h."""
+    _log("tiny h=%d K=%d" % (h, K))
+    x = P.inputs("tiny", head="stress", h=h, K=K, n=2, B=4)
+    gpu = P.gpu_run(x)
+    ora = P.oracle_run(x)
+    P.check_all(gpu, ora, "tiny/h=%d/K=%d" % (h, K))
 
 
 @pytest.mark.parametrize("de", [96, 1056, 2080])
