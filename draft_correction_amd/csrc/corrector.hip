@@ -28,7 +28,7 @@ constexpr int kMaxKernels = 12;
 constexpr size_t kAlign = 256;
 
 struct Layout {
-    size_t part, lse, ids, vals, hproj, upart, z, g, s, vout, vin, mlp_part, scores, total;
+    size_t part, lse, ids, vals, hproj, upart, z, g, s, vout, vin, mlp_part, best, cnt, scores, total;
     int chunks, splits, usplits;
 };
 
@@ -95,6 +95,9 @@ Layout layout(const corrector_desc& d, int32_t n) {
     L.s = take(sizeof(float) * pairs * d.r);
     const bool mlp = d.variant == CORR_VARIANT_MLP;
     L.mlp_part = take(mlp ? sizeof(float) * pairs * mlp_blocks(d.mlp_hidden) * d.k * d.k : 0);
+    const bool split = mlp && finish_split(d.slots, d.k, d.path_rule);
+    L.best = take(split ? sizeof(int32_t) * pairs * d.k : 0);
+    L.cnt = take(split ? sizeof(int) * n : 0);
     const bool cos = d.variant == CORR_VARIANT_COSINE;
     L.vout = take(cos ? sizeof(float) * rows * d.k * d.d_vec : 0);
     L.vin = take(cos ? sizeof(float) * rows * d.k * d.d_vec : 0);
@@ -366,6 +369,8 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
         m.w2 = w.w2;
         m.part = at<float>(ws, L.mlp_part);
         m.m = succ_m(d);
+        const bool split = tokens && finish_split(d.slots, d.k, d.path_rule);
+        m.zero_cnt = split ? at<int>(ws, L.cnt) : nullptr;
         q("mlp", [&] { return launch_mlp(m, q.s); });
         FinishArgs f{};
         f.part = m.part;
@@ -385,6 +390,8 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
         f.rule = d.path_rule;
         f.lam = d.path_lambda;
         f.beam = d.beam_width;
+        f.best = split ? at<int32_t>(ws, L.best) : nullptr;
+        f.cnt = m.zero_cnt;
         q(fused ? (d.path_rule == CORR_PATH_GREEDY ? "finish_walk"
                                                     : (d.path_rule == CORR_PATH_BEAM ? "finish_beam" : "finish_viterbi"))
                 : "finish",

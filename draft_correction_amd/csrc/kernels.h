@@ -162,6 +162,7 @@ struct MlpArgs {
     const float* w2;
     float* part;            // [n*(B-1)][blocks][K][K] partial Delta per hidden-unit block (b < m written)
     int m;                  // successors scored per predecessor (b < m; 1..K)
+    int* zero_cnt;          // K <= 16 and non-null: n counters the launch sets to 0 (for finish_pair_kernel)
 };
 // Most hidden-unit blocks of the MLP (h <= 256 units in blocks of 64).
 constexpr int kMaxMlpBlocks = 4;
@@ -186,8 +187,13 @@ struct FinishArgs {
     int rule;
     float lam;              // the Geometric rule's discount
     int beam;               // the beam rule's width (1..4)
+    int32_t* best;          // [n(B-1)][K] row argmaxes and
+    int* cnt;               // [n] pairs finished per request (zero at launch): with both
+                            // given, the greedy walk for K = 4, 8, 16 runs one wave per pair
 };
 hipError_t launch_finish(const FinishArgs& a, hipStream_t stream);
+// Whether launch_finish splits the work by pair (it then needs best and cnt).
+bool finish_split(int B, int K, int rule);
 
 struct CosArgs {
     const float* vout;      // [n][B][K][dvec]

@@ -370,6 +370,8 @@ __global__ __launch_bounds__(kWsThreads, 1) void mlp_ws_kernel(MlpArgs a) {
     __shared__ int cpn[kMaxRun];                // consumer waves done with each pair's c_p (4 when formed)
 
     const int tid = threadIdx.x, l = tid & 63, wave = tid >> 6;
+    if (a.zero_cnt && blockIdx.x == 0)   // the finishing launch's per-request counts
+        for (int i = tid; i < a.n; i += kWsThreads) a.zero_cnt[i] = 0;
     const int B = a.B, K = a.K, h = a.h;
     const int nj = (h + kJB - 1) / kJB;
     const int P = a.n * (B - 1);

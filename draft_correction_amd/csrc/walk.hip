@@ -512,6 +512,87 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a, int use_lds) 
     path_from_lds(a.rule, a.lam, a.beam, sS, a.ids, req, B, K, a.tokens, a.choice);
 }
 
+// The finishing step with the prefix-first walk, split by pair (K = 4, 8 or
+// 16): one wave per pair forms its K x K scores exactly as finish_kernel does
+// (block partials in block order, + b2, + l_{p+1}(b)), writes them, and takes
+// the argmax of every row (ties to the lowest successor index) into
+// best[pair][a]; the last wave of a request to finish (by the count cnt[req],
+// which the MLP launch zeroed) follows the chain k_1 = 0,
+// k_{p+1} = best[p][k_p] and writes choice and tokens.  A request's pair
+// states thus come from B - 1 CUs at once instead of one.  The hand-off uses
+// agent-scope atomic stores and loads for best and the count (coherent across
+// the chip's L2 caches without a cache write-back), the stores completed
+// before the count is taken.
+__global__ __launch_bounds__(64) void finish_pair_kernel(FinishArgs a) {
+    const int B = a.B, K = a.K, KK = K * K;
+    const int pair = blockIdx.x;
+    const int req = pair / (B - 1), p = pair - req * (B - 1);
+    const int l = lane_id();
+    const int nv = KK / 4;                    // float4 of the pair: 4, 16 or 64
+    const int i4 = min(l, nv - 1);            // lanes past nv repeat the last (not stored)
+    const int e = 4 * i4, aa = e / K, b0 = e - aa * K;
+    const float b2 = a.b2[0];
+    const float* src = a.part + static_cast<int64_t>(pair) * a.nblk * KK + e;
+    float4 t[kMaxMlpBlocks];
+#pragma unroll
+    for (int b = 0; b < kMaxMlpBlocks; ++b)
+        t[b] = *reinterpret_cast<const float4*>(src + (b < a.nblk ? b : a.nblk - 1) * KK);
+    const float4 lv = *reinterpret_cast<const float4*>(a.vals + (static_cast<int64_t>(req) * B + p + 1) * K + b0);
+    float4 acc = t[0];
+#pragma unroll
+    for (int b = 1; b < kMaxMlpBlocks; ++b)
+        if (b < a.nblk) acc = make_float4(acc.x + t[b].x, acc.y + t[b].y, acc.z + t[b].z, acc.w + t[b].w);
+    float4 sv = make_float4(lv.x + (acc.x + b2), lv.y + (acc.y + b2), lv.z + (acc.z + b2), lv.w + (acc.w + b2));
+    if (a.m < K)   // successors b >= m are not scored
+        sv = make_float4(b0 < a.m ? sv.x : -INFINITY, b0 + 1 < a.m ? sv.y : -INFINITY,
+                         b0 + 2 < a.m ? sv.z : -INFINITY, b0 + 3 < a.m ? sv.w : -INFINITY);
+    if (l < nv) reinterpret_cast<float4*>(a.scores + static_cast<int64_t>(pair) * KK)[l] = sv;
+    // row aa's argmax: the lane's four in index order (strict compare), then
+    // across the K / 4 consecutive lanes of the row, ties to the lower index
+    float bv = sv.x;
+    int bi = b0;
+    if (sv.y > bv) { bv = sv.y; bi = b0 + 1; }
+    if (sv.z > bv) { bv = sv.z; bi = b0 + 2; }
+    if (sv.w > bv) { bv = sv.w; bi = b0 + 3; }
+    for (int sh = 1; sh < K / 4; sh <<= 1) {
+        const float ov = __shfl_xor(bv, sh, 64);
+        const int oi = __shfl_xor(bi, sh, 64);
+        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+    }
+    if (l < nv && b0 == 0)
+        __hip_atomic_store(a.best + static_cast<int64_t>(pair) * K + aa, bi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's stores are complete
+    asm volatile("" ::: "memory");
+    int done = 0;
+    if (l == 0) done = __hip_atomic_fetch_add(a.cnt + req, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__shfl(done, 0, 64) != B - 2) return;   // not the request's last pair
+    // the walk: lane q < B - 1 holds best[q][.] packed four bits per entry
+    uint64_t row = 0;
+    {
+        // all K loads issued before any is used (entries past K repeat the
+        // last, and are not read by the chain)
+        const int q = min(l, B - 2);
+        const int32_t* bq = a.best + (static_cast<int64_t>(req) * (B - 1) + q) * K;
+        int32_t bt[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) bt[j] = __hip_atomic_load(bq + min(j, K - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) row |= static_cast<uint64_t>(bt[j] & 15) << (4 * j);
+    }
+    const uint32_t lo = static_cast<uint32_t>(row), hi = static_cast<uint32_t>(row >> 32);
+    int k = 0, mych = 0;   // lane s < B keeps choice[s]
+    for (int q = 0; q + 1 < B; ++q) {
+        const uint32_t w = k < 8 ? __builtin_amdgcn_readlane(lo, q) : __builtin_amdgcn_readlane(hi, q);
+        k = (w >> (4 * (k & 7))) & 15;
+        if (l == q + 1) mych = k;
+    }
+    if (l < B) {
+        const int64_t s = static_cast<int64_t>(req) * B + l;
+        if (a.choice) a.choice[s] = mych;
+        a.tokens[s] = a.ids[s * K + mych];
+    }
+}
+
 // z = hi + lo for each node row of the [hi | lo] layout.
 __global__ void zhl_to_f32_kernel(const uint16_t* __restrict__ zhl, float* __restrict__ z,
                                   int64_t nodes, int r) {
@@ -564,7 +645,17 @@ hipError_t launch_path(const float* scores, const int32_t* ids, int n, int B, in
                   ids, n, B, K, rule, lam, beam, tokens, choice, wl > 0);
 }
 
+bool finish_split(int B, int K, int rule) {
+    return B > 1 && (K == 4 || K == 8 || K == 16) && rule == kPathGreedy;
+}
+
 hipError_t launch_finish(const FinishArgs& a, hipStream_t stream) {
+    const bool aligned =
+        ((reinterpret_cast<uintptr_t>(a.scores) | reinterpret_cast<uintptr_t>(a.vals) | reinterpret_cast<uintptr_t>(a.part)) &
+         15) == 0;
+    if (a.tokens && a.best && a.cnt && aligned && finish_split(a.B, a.K, a.rule))
+        return launch(finish_pair_kernel, dim3(static_cast<unsigned>(static_cast<int64_t>(a.n) * (a.B - 1))), 64, 0,
+                      stream, a);
     const size_t lds = path_lds_bytes(a.B, a.K);
     return launch(finish_kernel, dim3(static_cast<unsigned>(a.n)), 256, static_cast<uint32_t>(lds), stream, a,
                   lds > 0);
