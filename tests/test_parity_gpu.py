@@ -59,11 +59,12 @@ def test_tiny_rep_widths(r):
     P.check_all(gpu, ora, "tiny/r=%d" % r)
 
 
-@pytest.mark.parametrize("K", [1, 5, 13])
+@pytest.mark.parametrize("K", [1, 5, 8, 13])
 def test_tiny_small_k(K):
     """K = 1 (one candidate per slot: every pair a single transition, the walk
-    fixed), and odd K below 16 (the last predecessor and successor tasks of the
-    K <= 16 MLP consumers cut short)."""
+    fixed), odd K below 16 (the last predecessor and successor tasks of the
+    K <= 16 MLP consumers cut short), and K = 8 (the per-pair finishing step
+    with rows of two lanes)."""
     _log("tiny K=%d" % K)
     x = P.inputs("tiny", head="stress", K=K, n=2, B=4)
     gpu = P.gpu_run(x)
