@@ -297,6 +297,7 @@ __global__ __launch_bounds__(kGThreads) void gemm_gather_kernel(GemmJob J) {
 // ------------------------------------------------------------------- cand --
 
 constexpr int kCR = 32;                 // candidate rows per workgroup
+constexpr int kCRSmall = 8;             // the same for calls with few candidates (see launch_cand)
 constexpr int kCT = 512;                // threads of a candidate workgroup
 constexpr int kCW = kCT / kWave;        // its waves
 constexpr int kCRows = 4 * kCW;         // 16-lane rows it processes at a time
@@ -322,10 +323,10 @@ __device__ __forceinline__ void row16_layernorm(float (&v)[R / 16], float eps) {
 }
 
 __host__ __device__ inline int cand_us(int r, int dvec) { return (dvec > r ? dvec : r) + 4; }
-// Distinct slots a group of kCR consecutive candidates can touch.
-__host__ __device__ inline int cand_slots(int K) {
-    const int s = (kCR - 1) / K + 2;
-    return s < kCR ? s : kCR;
+// Distinct slots a group of cr consecutive candidates can touch.
+__host__ __device__ inline int cand_slots(int K, int cr) {
+    const int s = (cr - 1) / K + 2;
+    return s < cr ? s : cr;
 }
 __host__ __device__ inline int cand_as(int r) { return 4 * r + 8; }
 
@@ -406,14 +407,17 @@ __device__ __forceinline__ void store_bf16s(uint16_t* dst, const uint16_t (&v)[N
     }
 }
 
-// One workgroup per kCR consecutive candidates (nodes) of the [rows][K] list:
+// One workgroup per CR consecutive candidates (nodes) of the [rows][K] list:
 //   u = W_cand E[c]   the candidate GEMM's split partials summed in order (or
 //                     a row of the folded table when one is given)
 //   b = LN(u), g = LN(W_ctx h) for the candidate's slot (from hproj)
 //   z = gamma * LN(W_fuse [b; g]) + beta, W_fuse on MFMA over [b; g] hi | lo
 //   stored as bf16 z hi | lo; cosine: unit(W_out z), unit(W_in z).
 // Loops over r are compile-time so each phase issues all of its loads at once.
-template <int R>
+// Every candidate's values are computed the same way whatever CR is (each row
+// of an MFMA tile, and each LayerNorm, depends on its own row only), so the
+// two group sizes give identical results.
+template <int R, int CR>
 __global__ __launch_bounds__(kCT) void cand_kernel(CandArgs a) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     constexpr int NCT = R / 16;
@@ -421,13 +425,13 @@ __global__ __launch_bounds__(kCT) void cand_kernel(CandArgs a) {
     const int l = lane_id();
     const int wave = tid >> 6;
     const int64_t nodes = a.rows * a.K;
-    const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kCR;
-    const int M = static_cast<int>(min(static_cast<int64_t>(kCR), nodes - n0));
+    const int64_t n0 = static_cast<int64_t>(blockIdx.x) * CR;
+    const int M = static_cast<int>(min(static_cast<int64_t>(CR), nodes - n0));
     const int us = cand_us(R, a.vout ? a.dvec : 0);
     const int as = cand_as(R);
-    float* ubuf = reinterpret_cast<float*>(smem_raw);                       // [kCR][us]
-    uint16_t* abuf = reinterpret_cast<uint16_t*>(smem_raw + kCR * us * 4);  // [kCR][as]
-    float* gs = reinterpret_cast<float*>(smem_raw + kCR * us * 4 + kCR * as * 2);  // [cand_slots(K)][R]
+    float* ubuf = reinterpret_cast<float*>(smem_raw);                     // [CR][us]
+    uint16_t* abuf = reinterpret_cast<uint16_t*>(smem_raw + CR * us * 4);  // [CR][as]
+    float* gs = reinterpret_cast<float*>(smem_raw + CR * us * 4 + CR * as * 2);  // [cand_slots(K, CR)][R]
 
     // ---- W_fuse fragments of this wave's column tiles (ct = wave + kCW c),
     // issued first so they arrive with the u loads below
@@ -455,7 +459,7 @@ __global__ __launch_bounds__(kCT) void cand_kernel(CandArgs a) {
     // partials (four consecutive columns per thread and load).  The loads are
     // only issued here; they are summed after the slot-state loads below have
     // been issued too, so all of the prologue's memory latency overlaps.
-    constexpr int PER4 = (kCR * R / 4 + kCT - 1) / kCT;
+    constexpr int PER4 = (CR * R / 4 + kCT - 1) / kCT;
     float4 ut[PER4][kMaxUSplits];
 #pragma unroll
     for (int q = 0; q < PER4; ++q) {
@@ -560,7 +564,9 @@ __global__ __launch_bounds__(kCT) void cand_kernel(CandArgs a) {
         for (int rt = 0; rt < nrt; ++rt) {
             const f32x4 acc = mfma_hilo_tile_w<2 * R>(abuf + rt * 16 * as, as, M - rt * 16, wfr[c]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ubuf[(rt * 16 + 4 * (l >> 4) + i) * us + ct * 16 + (l & 15)] = acc[i];
+            for (int i = 0; i < 4; ++i)
+                if (rt * 16 + 4 * (l >> 4) + i < CR)   // a tile's rows past the group (CR = 8) are not kept
+                    ubuf[(rt * 16 + 4 * (l >> 4) + i) * us + ct * 16 + (l & 15)] = acc[i];
         }
     }
     __syncthreads();
@@ -598,7 +604,9 @@ __global__ __launch_bounds__(kCT) void cand_kernel(CandArgs a) {
             const f32x4 acc = mfma_hilo_tile<R>(abuf + rt * 16 * as, as, M - rt * 16, which ? a.w_in : a.w_out, R,
                                                 ct * 16);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ubuf[(rt * 16 + 4 * (l >> 4) + i) * us + ct * 16 + (l & 15)] = acc[i];
+            for (int i = 0; i < 4; ++i)
+                if (rt * 16 + 4 * (l >> 4) + i < CR)   // a tile's rows past the group (CR = 8) are not kept
+                    ubuf[(rt * 16 + 4 * (l >> 4) + i) * us + ct * 16 + (l & 15)] = acc[i];
         }
         __syncthreads();
         for (int m = rsub; m < M; m += kCRows) {
@@ -653,22 +661,36 @@ hipError_t launch_gemm(const GemmA& A, const GemmW& W, int64_t M, int N, int kdi
     return launch_gemm2(j, none, stream);
 }
 
+static size_t cand_lds_cr(int r, int dvec, int K, int cr) {
+    return sizeof(float) * cr * cand_us(r, dvec) + sizeof(uint16_t) * cr * cand_as(r) +
+           sizeof(float) * cand_slots(K, cr) * r;
+}
+
 size_t cand_lds_bytes(int r, int dvec, int K) {
-    return sizeof(float) * kCR * cand_us(r, dvec) + sizeof(uint16_t) * kCR * cand_as(r) +
-           sizeof(float) * cand_slots(K) * r;
+    const size_t a = cand_lds_cr(r, dvec, K, kCR), b = cand_lds_cr(r, dvec, K, kCRSmall);
+    return a > b ? a : b;
+}
+
+template <int CR>
+static hipError_t launch_cand_cr(const CandArgs& a, int64_t nodes, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>((nodes + CR - 1) / CR));
+    const size_t lds = cand_lds_cr(a.r, a.vout ? a.dvec : 0, a.K, CR);
+    switch (a.r) {
+        case 16: return launch(cand_kernel<16, CR>, grid, kCT, lds, stream, a);
+        case 32: return launch(cand_kernel<32, CR>, grid, kCT, lds, stream, a);
+        case 64: return launch(cand_kernel<64, CR>, grid, kCT, lds, stream, a);
+        case 128: return launch(cand_kernel<128, CR>, grid, kCT, lds, stream, a);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_cand(const CandArgs& a, hipStream_t stream) {
+    // Groups of kCR candidates while they give at least 128 workgroups; fewer
+    // candidates go in groups of kCRSmall, so that more CUs share the
+    // per-group loads (every group reads all of W_fuse)
     const int64_t nodes = a.rows * a.K;
-    const dim3 grid(static_cast<unsigned>((nodes + kCR - 1) / kCR));
-    const size_t lds = cand_lds_bytes(a.r, a.vout ? a.dvec : 0, a.K);
-    switch (a.r) {
-        case 16: return launch(cand_kernel<16>, grid, kCT, lds, stream, a);
-        case 32: return launch(cand_kernel<32>, grid, kCT, lds, stream, a);
-        case 64: return launch(cand_kernel<64>, grid, kCT, lds, stream, a);
-        case 128: return launch(cand_kernel<128>, grid, kCT, lds, stream, a);
-        default: return hipErrorInvalidValue;
-    }
+    return (nodes + kCR - 1) / kCR >= 128 ? launch_cand_cr<kCR>(a, nodes, stream)
+                                          : launch_cand_cr<kCRSmall>(a, nodes, stream);
 }
 
 }  // namespace corr
