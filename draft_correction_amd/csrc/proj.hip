@@ -297,7 +297,8 @@ __global__ __launch_bounds__(kGThreads) void gemm_gather_kernel(GemmJob J) {
 // ------------------------------------------------------------------- cand --
 
 constexpr int kCR = 32;                 // candidate rows per workgroup
-constexpr int kCRSmall = 8;             // the same for calls with few candidates (see launch_cand)
+constexpr int kCRSmall = 4;             // the same for calls with few candidates (see launch_cand),
+constexpr int kCRMid = 8;               // and with somewhat more
 constexpr int kCT = 512;                // threads of a candidate workgroup
 constexpr int kCW = kCT / kWave;        // its waves
 constexpr int kCRows = 4 * kCW;         // 16-lane rows it processes at a time
@@ -667,8 +668,12 @@ static size_t cand_lds_cr(int r, int dvec, int K, int cr) {
 }
 
 size_t cand_lds_bytes(int r, int dvec, int K) {
-    const size_t a = cand_lds_cr(r, dvec, K, kCR), b = cand_lds_cr(r, dvec, K, kCRSmall);
-    return a > b ? a : b;
+    size_t m = cand_lds_cr(r, dvec, K, kCR);
+    for (const int cr : {kCRSmall, kCRMid}) {
+        const size_t b = cand_lds_cr(r, dvec, K, cr);
+        m = b > m ? b : m;
+    }
+    return m;
 }
 
 template <int CR>
@@ -685,12 +690,13 @@ static hipError_t launch_cand_cr(const CandArgs& a, int64_t nodes, hipStream_t s
 }
 
 hipError_t launch_cand(const CandArgs& a, hipStream_t stream) {
-    // Groups of kCR candidates while they give at least 128 workgroups; fewer
-    // candidates go in groups of kCRSmall, so that more CUs share the
-    // per-group loads (every group reads all of W_fuse)
+    // The smallest group (4, 8, else 32 candidates) that still fits one
+    // workgroup per CU: every group reads all of W_fuse, so with few
+    // candidates small groups spread those loads over more CUs
     const int64_t nodes = a.rows * a.K;
-    return (nodes + kCR - 1) / kCR >= 128 ? launch_cand_cr<kCR>(a, nodes, stream)
-                                          : launch_cand_cr<kCRSmall>(a, nodes, stream);
+    if ((nodes + kCRSmall - 1) / kCRSmall <= 256) return launch_cand_cr<kCRSmall>(a, nodes, stream);
+    if ((nodes + kCRMid - 1) / kCRMid <= 256) return launch_cand_cr<kCRMid>(a, nodes, stream);
+    return launch_cand_cr<kCR>(a, nodes, stream);
 }
 
 }  // namespace corr
