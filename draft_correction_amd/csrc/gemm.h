@@ -273,7 +273,7 @@ __device__ __forceinline__ void gemm_small_body(const GemmJob J, int64_t t) {
 #pragma unroll
             for (int i = 0; i < kSmallDepth; ++i)
                 if (ks + i < nks) acc = mfma16x16x32(a0[i], w0[i], acc);
-            ld(ks + 2 * kSmallDepth, a0, w0);
+            if (ks + 2 * kSmallDepth < nks) ld(ks + 2 * kSmallDepth, a0, w0);
 #pragma unroll
             for (int i = 0; i < kSmallDepth; ++i)
                 if (ks + kSmallDepth + i < nks) acc = mfma16x16x32(a1[i], w1[i], acc);
@@ -290,15 +290,18 @@ __device__ __forceinline__ void gemm_small_body(const GemmJob J, int64_t t) {
 }
 
 // Workgroups of 256 threads a GEMM job occupies in a launch (tiled or small).
+// The small form runs one tile per workgroup, on its first wave: the form is
+// for calls with few tiles, whose time is set by how many CUs share the loads.
 __host__ __device__ inline int64_t gemm_blocks_256(const GemmJob& j) {
-    if (j.small) return (((j.M + 15) / 16) * ((j.N + 15) / 16) * j.splits + 3) / 4;
+    if (j.small) return ((j.M + 15) / 16) * ((j.N + 15) / 16) * j.splits;
     return ((j.M + kBM - 1) / kBM) * ((j.N + kBN - 1) / kBN) * j.splits;
 }
 
 // Workgroup lin of a job, tiled or small (256 threads; smem: kGemmSmem bytes).
 __device__ __forceinline__ void gemm_any_body(const GemmJob& J, int64_t lin, unsigned char* smem) {
-    if (J.small)
-        gemm_small_body(J, lin * 4 + (threadIdx.x >> 6));
+    if (J.small) {
+        if (threadIdx.x < 64) gemm_small_body(J, lin);
+    }
     else
         gemm_body(J, lin, smem);
 }
