@@ -77,30 +77,37 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0xF70);
 }
 
-// The candidate projection in its small form: one wave per workgroup and
-// 16 x 16 output tile of one k-split (split fastest), as gemm_small_body, but
-// with every k-step of a round of up to kSmallRound loaded at once straight
-// into LDS (global_load_lds_dwordx4: the lanes' A and W fragments of a k-step,
-// 1 KB each, land lane-linearly, which is also the layout the MFMA reads back,
+// The candidate projection in its small form: workgroups of two waves, each
+// wave one 16 x 16 output tile of one k-split (split fastest), the two tiles
+// side by side (columns), as gemm_small_body, but with every k-step of a
+// round of up to kSmallRound loaded at once straight into LDS
+// (global_load_lds_dwordx4: the lanes' A and W fragments of a k-step, 1 KB
+// each, land lane-linearly, which is also the layout the MFMA reads back,
 // bank-conflict free), so a wave waits for memory once per round instead of
-// once per few k-steps.  Same MFMA sequence per output: identical partials.
-constexpr int kSmallRound = 32;   // k-steps per round (64 KB of LDS)
+// once per few k-steps.  The two waves share the round's A fragments (each
+// loads half of them), so a CU takes in three fragments per k-step for two
+// tiles instead of four.  Same MFMA sequence per output: identical partials.
+constexpr int kSmallRound = 32;   // k-steps per round (96 KB of LDS)
 
-__global__ __launch_bounds__(64) void gemm_small_kernel(GemmJob J) {
-    __shared__ __attribute__((aligned(1024))) uint16_t st[2 * kSmallRound * 512];
-    const int64_t t = blockIdx.x;
-    if (t >= gemm_small_tiles(J)) return;
+__global__ __launch_bounds__(128) void gemm_small_kernel(GemmJob J) {
+    // [A | W of wave 0 | W of wave 1], kSmallRound k-steps of 512 bf16 each
+    __shared__ __attribute__((aligned(1024))) uint16_t st[3 * kSmallRound * 512];
     const GemmA& A = J.A;
     const GemmW& W = J.W;
     const int64_t M = J.M;
     const int N = J.N, kdim = J.kdim, splits = J.splits;
-    const int l = threadIdx.x;
+    const int l = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
     const int kper = ((kdim / 32 + splits - 1) / splits) * 32;
     const int ntn = (N + 15) / 16;
+    const int ncp = (ntn + 1) / 2;                // column-tile pairs
+    const int64_t t = blockIdx.x;
     const int split = static_cast<int>(t % splits);
     const int64_t rest = t / splits;
-    const int n0 = static_cast<int>(rest % ntn) * 16;
-    const int64_t m0 = (rest / ntn) * 16;
+    const int ct = static_cast<int>(rest % ncp) * 2 + wave;   // ct == ntn: no tile (odd ntn), loads clamped
+    const int n0 = min(ct, ntn - 1) * 16;
+    const int64_t m0 = (rest / ncp) * 16;
+    if (m0 >= M) return;   // whole workgroup
     const int k_lo = split * kper;
     const int k_hi = min(kdim, k_lo + kper);
     const int nks = k_lo < k_hi ? (k_hi - k_lo) / 32 : 0;
@@ -112,17 +119,17 @@ __global__ __launch_bounds__(64) void gemm_small_kernel(GemmJob J) {
     const uint16_t* wb = b == 0 ? W.base[0] : (b == 1 ? W.base[1] : W.base[2]);
     const int64_t wld = b == 0 ? W.ld[0] : (b == 1 ? W.ld[1] : W.ld[2]);
     const uint16_t* wp = wb + static_cast<int64_t>(nn % W.nb) * wld + k_lo + kq;
+    uint16_t* sa = st;
+    uint16_t* sw = st + (1 + wave) * kSmallRound * 512;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int c0 = 0; c0 < nks; c0 += kSmallRound) {
         const int nc = min(kSmallRound, nks - c0);
-        // the previous round's fragment reads are complete before its LDS is refilled
-        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-        for (int i = 0; i < nc; ++i) {
-            lds_dma16(ap + 32 * (c0 + i), st + i * 512);
-            lds_dma16(wp + 32 * (c0 + i), st + (kSmallRound + i) * 512);
-        }
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the round has landed
-        asm volatile("" ::: "memory");
+        // both waves are done reading the previous round before its LDS is refilled
+        __syncthreads();
+        for (int i = wave; i < nc; i += 2) lds_dma16(ap + 32 * (c0 + i), sa + i * 512);
+        for (int i = 0; i < nc; ++i) lds_dma16(wp + 32 * (c0 + i), sw + i * 512);
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's loads of the round have landed
+        __syncthreads();                       // and the other wave's half of A
         // eight k-steps' fragments read at a time (reads past the round's
         // last k-step stay inside the buffer and are not used)
         for (int i0 = 0; i0 < nc; i0 += 8) {
@@ -130,14 +137,15 @@ __global__ __launch_bounds__(64) void gemm_small_kernel(GemmJob J) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int i = min(i0 + j, kSmallRound - 1);
-                a[j] = *reinterpret_cast<const u32x4*>(st + i * 512 + 8 * l);
-                w[j] = *reinterpret_cast<const u32x4*>(st + (kSmallRound + i) * 512 + 8 * l);
+                a[j] = *reinterpret_cast<const u32x4*>(sa + i * 512 + 8 * l);
+                w[j] = *reinterpret_cast<const u32x4*>(sw + i * 512 + 8 * l);
             }
 #pragma unroll
             for (int j = 0; j < 8; ++j)
                 if (i0 + j < nc) acc = mfma16x16x32(a[j], w[j], acc);
         }
     }
+    if (ct >= ntn) return;
     // lane l holds rows 4 (l / 16) + e of column l % 16
     float* out = J.C + static_cast<int64_t>(split) * M * N;
     const int c = n0 + (l & 15);
@@ -649,7 +657,10 @@ hipError_t launch_gemm2(const GemmJob& j0, const GemmJob& j1, hipStream_t stream
 
 hipError_t launch_gemm_gather(const GemmJob& j, hipStream_t stream) {
     if (j.W.kwrap > 0 || j.kdim % 32 != 0) return hipErrorInvalidValue;
-    if (j.small) return launch(gemm_small_kernel, dim3(static_cast<unsigned>(small_tiles(j))), 64, 0, stream, j);
+    if (j.small) {
+        const int64_t pairs = ((j.M + 15) / 16) * (((j.N + 15) / 16 + 1) / 2) * j.splits;
+        return launch(gemm_small_kernel, dim3(static_cast<unsigned>(pairs)), 128, 0, stream, j);
+    }
     const int64_t blocks = ((j.M + kGM - 1) / kGM) * ((j.N + kGN - 1) / kGN) * j.splits;
     return launch(gemm_gather_kernel, dim3(static_cast<unsigned>(blocks)), kGThreads, 0, stream, j);
 }
