@@ -94,8 +94,11 @@ Layout layout(const corrector_desc& d, int32_t n) {
     L.g = take(sizeof(float) * rows * d.r);
     L.s = take(sizeof(float) * pairs * d.r);
     const bool mlp = d.variant == CORR_VARIANT_MLP;
-    L.mlp_part = take(mlp ? sizeof(float) * pairs * mlp_blocks(d.mlp_hidden) * d.k * d.k : 0);
     const bool split = mlp && finish_split(d.slots, d.k, d.path_rule);
+    // the partials of the 64-unit blocks, or with the split finishing step
+    // those of the 16-unit blocks of mlp_pair16_kernel
+    L.mlp_part = take(mlp ? sizeof(float) * pairs * (split ? d.mlp_hidden / 16 : mlp_blocks(d.mlp_hidden)) * d.k * d.k
+                          : 0);
     L.best = take(split ? sizeof(int32_t) * pairs * d.k : 0);
     L.cnt = take(split ? sizeof(int) * n : 0);
     const bool cos = d.variant == CORR_VARIANT_COSINE;
@@ -371,7 +374,6 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
         m.m = succ_m(d);
         const bool split = tokens && finish_split(d.slots, d.k, d.path_rule);
         m.zero_cnt = split ? at<int>(ws, L.cnt) : nullptr;
-        q("mlp", [&] { return launch_mlp(m, q.s); });
         FinishArgs f{};
         f.part = m.part;
         f.nblk = mlp_blocks(d.mlp_hidden);
@@ -392,6 +394,14 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
         f.beam = d.beam_width;
         f.best = split ? at<int32_t>(ws, L.best) : nullptr;
         f.cnt = m.zero_cnt;
+        // few pairs: one MLP workgroup per (pair, 16 units) when the scores
+        // are finished by pair (which adds its 16-unit partials)
+        if (finish_by_pair(f) && static_cast<int64_t>(n) * (d.slots - 1) * (d.mlp_hidden / 16) <= kMlp16MaxGroups) {
+            m.units16 = 1;
+            f.sub = 1;
+            f.nblk = d.mlp_hidden / 16;
+        }
+        q("mlp", [&] { return launch_mlp(m, q.s); });
         q(fused ? (d.path_rule == CORR_PATH_GREEDY ? "finish_walk"
                                                     : (d.path_rule == CORR_PATH_BEAM ? "finish_beam" : "finish_viterbi"))
                 : "finish",

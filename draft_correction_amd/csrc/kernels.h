@@ -163,9 +163,14 @@ struct MlpArgs {
     float* part;            // [n*(B-1)][blocks][K][K] partial Delta per hidden-unit block (b < m written)
     int m;                  // successors scored per predecessor (b < m; 1..K)
     int* zero_cnt;          // K <= 16 and non-null: n counters the launch sets to 0 (for finish_pair_kernel)
+    int units16;            // K <= 16: one workgroup per (pair, 16 units); part then holds
+                            // [pairs][h/16][K][K] partials, each the first level of a 64-unit block's sum
 };
 // Most hidden-unit blocks of the MLP (h <= 256 units in blocks of 64).
 constexpr int kMaxMlpBlocks = 4;
+// Most (pair, 16-unit block) workgroups for which the MLP takes its 16-unit
+// form: about one per CU.
+constexpr int64_t kMlp16MaxGroups = 256;
 int mlp_blocks(int h);
 hipError_t launch_mlp(const MlpArgs& a, hipStream_t stream);
 
@@ -187,13 +192,17 @@ struct FinishArgs {
     int rule;
     float lam;              // the Geometric rule's discount
     int beam;               // the beam rule's width (1..4)
+    int sub;                // part holds 16-unit partials (nblk of them), added four at a
+                            // time in the 64-unit kernel's tree before the 64-unit blocks' sum
     int32_t* best;          // [n(B-1)][K] row argmaxes and
     int* cnt;               // [n] pairs finished per request (zero at launch): with both
                             // given, the greedy walk for K = 4, 8, 16 runs one wave per pair
 };
 hipError_t launch_finish(const FinishArgs& a, hipStream_t stream);
-// Whether launch_finish splits the work by pair (it then needs best and cnt).
+// Whether launch_finish splits the work by pair for this shape and rule (it
+// then needs best and cnt), and whether it will for these arguments.
 bool finish_split(int B, int K, int rule);
+bool finish_by_pair(const FinishArgs& a);
 
 struct CosArgs {
     const float* vout;      // [n][B][K][dvec]

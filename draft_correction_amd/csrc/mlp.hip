@@ -684,6 +684,147 @@ __global__ __launch_bounds__(kWsThreads, 1) void mlp_ws_kernel(MlpArgs a) {
     }
 }
 
+// ------------------------------------------------- K <= 16, few pairs --
+// For calls with few pairs: one workgroup of 256 threads per (pair, block of
+// 16 hidden units), so that a pair's work and its W1 rows spread over
+// (h / 16) CUs.  Every value is formed exactly as in mlp_ws_kernel: U and V
+// by the same MFMA sequence (z fragments read from memory instead of LDS),
+// c_p + b1 by the same quarter dots and shuffles, P and Q by the same
+// expressions, and each GELU task (predecessor a, successors b and b + 1,
+// eight units) by the same loop.  The ws kernel then adds the eight tasks of
+// a 64-unit block in the tree ((q0 + q1) + (q2 + q3)) + ((q4 + q5) + (q6 + q7))
+// (DPP xor 1, xor 2, half-row mirror); here each workgroup stops after the
+// first level and writes (q0 + q1) of its sixteen units, and the finishing
+// step adds the four of a 64-unit block in the same tree.  The scores are
+// therefore identical to the ws kernel's.
+template <int R>
+__global__ __launch_bounds__(256) void mlp_pair16_kernel(MlpArgs a) {
+    constexpr int KMAX = 16;
+    constexpr int KS = 2 * R / 32;              // 32-wide k-steps over [hi | lo]
+    constexpr int KD = R >= 32 ? R / 32 : 1;    // distinct W1 fragments
+    constexpr int PQ = 2 * KMAX * kPS;
+    __shared__ __attribute__((aligned(16))) float pq[PQ];
+    __shared__ float cps[16];
+    __shared__ float lv[2 * KMAX];
+    __shared__ __attribute__((aligned(16))) float w2s[16];
+    const int tid = threadIdx.x, l = tid & 63, wave = tid >> 6;
+    if (a.zero_cnt && blockIdx.x == 0)           // the finishing launch's per-request counts
+        for (int i = tid; i < a.n; i += 256) a.zero_cnt[i] = 0;
+    const int B = a.B, K = a.K;
+    const int nb = a.h / 16;                     // blocks of 16 units (h is a multiple of 16)
+    const int pair = blockIdx.x / nb, blk = blockIdx.x - pair * nb;
+    const int req = pair / (B - 1), p = pair - req * (B - 1);
+    const int64_t t0 = static_cast<int64_t>(req) * B + p;   // slot row of the predecessor
+    const int j0 = 16 * blk;
+    const int nin = 3 * R + 2;
+    const int ju = j0 + (l & 15);                // the lane's unit (every block is full)
+    const uint16_t* wrow = a.w1 + static_cast<int64_t>(ju) * nin;
+    // every load first: the U (wave 0) or V (wave 1) operands, c_p's W1_s
+    // words and pair state (wave 2), logits, w2
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const int kq = 8 * (l >> 4);
+    if (wave < 2) {
+        const int row = min(l & 15, K - 1);      // rows past K repeat row K - 1 (not stored)
+        const uint16_t* zr = a.zhl + ((t0 + wave) * K + row) * (2 * R) + kq;
+        const uint16_t* wz = wrow + (1 + wave) * R;
+        u32x4 zf[KS], wf[KD];
+#pragma unroll
+        for (int d = 0; d < KD; ++d) wf[d] = load16(wz + (d * 32 + kq) % R);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) zf[ks] = load16(zr + ks * 32);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(zf[ks], wf[ks % KD], acc);
+    } else if (wave == 2) {
+        // lane l: quarter l / 16 of r of unit ju, column order, the quarters
+        // added across lanes l ^ 16 and l ^ 32
+        constexpr int WQ = R / 8;                // words of a quarter
+        const int e4 = l >> 4;
+        const uint32_t* ws = reinterpret_cast<const uint32_t*>(wrow) + e4 * WQ;
+        const float* sq = a.s + static_cast<int64_t>(pair) * R + e4 * (R / 4);
+        float cacc = 0.f;
+#pragma unroll
+        for (int q2 = 0; q2 < WQ / 2; ++q2) {
+            const float4 sv = *reinterpret_cast<const float4*>(sq + 4 * q2);
+            const uint32_t w0 = ws[2 * q2], w1 = ws[2 * q2 + 1];
+            cacc = fmaf(__uint_as_float(w0 << 16), sv.x, cacc);
+            cacc = fmaf(__uint_as_float(w0 & 0xFFFF0000u), sv.y, cacc);
+            cacc = fmaf(__uint_as_float(w1 << 16), sv.z, cacc);
+            cacc = fmaf(__uint_as_float(w1 & 0xFFFF0000u), sv.w, cacc);
+        }
+        cacc += __shfl_xor(cacc, 16, 64);
+        cacc += __shfl_xor(cacc, 32, 64);
+        if (l < 16) cps[l] = cacc + a.b1[ju];
+    } else {
+        if (l < 2 * K) lv[l] = a.vals[t0 * K + l];
+        if (l >= 32 && l < 48) w2s[l - 32] = a.w2[j0 + l - 32] * (1.0f / kGeluAlpha);   // see gelu_scaled
+    }
+    __syncthreads();
+    // P (wave 0) and Q (wave 1), kept scaled by alpha
+    if (wave < 2) {
+        const int jc = l & 15;
+        const float wl = bf16_to_f32(wrow[3 * R + wave]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int m = 4 * (l >> 4) + e;
+            if (m < K) {
+                constexpr float al = kGeluAlpha;
+                if (wave == 0)
+                    pq[static_cast<int>(__umul24(m, kPS)) + jc] = al * (cps[jc] + fmaf(wl, lv[m], acc[e]));
+                else
+                    pq[static_cast<int>(__umul24(KMAX + m, kPS)) + jc] = al * fmaf(wl, lv[K + m], acc[e]);
+            }
+        }
+    }
+    __syncthreads();
+    // one task per thread: (predecessor a, successors b and b + 1, eighth
+    // t % 2 of the sixteen units), as in mlp_ws_kernel
+    const int ms = a.m;
+    const int mh = (ms + 1) / 2;
+    const int T = K * mh * 2;
+    const int q = tid & 1, rest = tid >> 1;
+    const int aa = rest / mh, bb = 2 * (rest - static_cast<int>(__umul24(aa, mh)));
+    const bool two = bb + 1 < ms;
+    const int j = 8 * q;
+    float d0 = 0.f, d1 = 0.f, e0 = 0.f, e1 = 0.f;
+    if (tid < T) {
+        const int pr = static_cast<int>(__umul24(aa, kPS)) + j;
+        const int qr = static_cast<int>(__umul24(KMAX + bb, kPS)) + j;
+        const int qs = qr + (two ? kPS : 0);
+        const float4 pv0 = *reinterpret_cast<const float4*>(&pq[pr]);
+        const float4 pv1 = *reinterpret_cast<const float4*>(&pq[pr + 4]);
+        const float4 wv0 = *reinterpret_cast<const float4*>(&w2s[j]);
+        const float4 wv1 = *reinterpret_cast<const float4*>(&w2s[j + 4]);
+        const float4 qv0 = *reinterpret_cast<const float4*>(&pq[qr]);
+        const float4 qv1 = *reinterpret_cast<const float4*>(&pq[qr + 4]);
+        const float4 sv0 = *reinterpret_cast<const float4*>(&pq[qs]);
+        const float4 sv1 = *reinterpret_cast<const float4*>(&pq[qs + 4]);
+        d0 = fmaf(wv0.x, gelu_scaled(pv0.x + qv0.x), d0);
+        d1 = fmaf(wv0.y, gelu_scaled(pv0.y + qv0.y), d1);
+        d0 = fmaf(wv0.z, gelu_scaled(pv0.z + qv0.z), d0);
+        d1 = fmaf(wv0.w, gelu_scaled(pv0.w + qv0.w), d1);
+        d0 = fmaf(wv1.x, gelu_scaled(pv1.x + qv1.x), d0);
+        d1 = fmaf(wv1.y, gelu_scaled(pv1.y + qv1.y), d1);
+        d0 = fmaf(wv1.z, gelu_scaled(pv1.z + qv1.z), d0);
+        d1 = fmaf(wv1.w, gelu_scaled(pv1.w + qv1.w), d1);
+        e0 = fmaf(wv0.x, gelu_scaled(pv0.x + sv0.x), e0);
+        e1 = fmaf(wv0.y, gelu_scaled(pv0.y + sv0.y), e1);
+        e0 = fmaf(wv0.z, gelu_scaled(pv0.z + sv0.z), e0);
+        e1 = fmaf(wv0.w, gelu_scaled(pv0.w + sv0.w), e1);
+        e0 = fmaf(wv1.x, gelu_scaled(pv1.x + sv1.x), e0);
+        e1 = fmaf(wv1.y, gelu_scaled(pv1.y + sv1.y), e1);
+        e0 = fmaf(wv1.z, gelu_scaled(pv1.z + sv1.z), e0);
+        e1 = fmaf(wv1.w, gelu_scaled(pv1.w + sv1.w), e1);
+    }
+    float v = d0 + d1, w = e0 + e1;
+    v += dpp_f<kDppXor1>(v);
+    w += dpp_f<kDppXor1>(w);
+    if (tid < T && q == 0) {
+        float* out = a.part + (static_cast<int64_t>(pair) * nb + blk) * K * K + static_cast<int>(__umul24(aa, K)) + bb;
+        out[0] = v;
+        if (two) out[1] = w;
+    }
+}
+
 }  // namespace
 
 int mlp_blocks(int h) { return (h + kJB - 1) / kJB; }
@@ -722,6 +863,17 @@ hipError_t launch_mlp_r(const MlpArgs& a, hipStream_t stream) {
 
 hipError_t launch_mlp(const MlpArgs& a, hipStream_t stream) {
     if (a.B < 2 || a.n < 1) return hipSuccess;
+    if (a.units16) {
+        if (a.K > 16 || a.h % 16) return hipErrorInvalidValue;
+        const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.n) * (a.B - 1) * (a.h / 16)));
+        switch (a.r) {
+            case 16: return launch(mlp_pair16_kernel<16>, grid, 256, 0, stream, a);
+            case 32: return launch(mlp_pair16_kernel<32>, grid, 256, 0, stream, a);
+            case 64: return launch(mlp_pair16_kernel<64>, grid, 256, 0, stream, a);
+            case 128: return launch(mlp_pair16_kernel<128>, grid, 256, 0, stream, a);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (a.r) {
         case 16: return launch_mlp_r<16>(a, stream);
         case 32: return launch_mlp_r<32>(a, stream);

@@ -534,14 +534,28 @@ __global__ __launch_bounds__(64) void finish_pair_kernel(FinishArgs a) {
     const float b2 = a.b2[0];
     const float* src = a.part + static_cast<int64_t>(pair) * a.nblk * KK + e;
     float4 t[kMaxMlpBlocks];
+    int nb64 = a.nblk;
+    if (a.sub) {
+        // 16-unit partials: a 64-unit block's value is (P0 + P1) + (P2 + P3),
+        // a missing one counting as +0 (as the 64-unit kernel's empty eighths)
+        nb64 = (a.nblk + 3) / 4;
+        float4 u[4 * kMaxMlpBlocks];
 #pragma unroll
-    for (int b = 0; b < kMaxMlpBlocks; ++b)
-        t[b] = *reinterpret_cast<const float4*>(src + (b < a.nblk ? b : a.nblk - 1) * KK);
+        for (int b = 0; b < 4 * kMaxMlpBlocks; ++b)
+            u[b] = b < a.nblk ? *reinterpret_cast<const float4*>(src + b * KK) : make_float4(0.f, 0.f, 0.f, 0.f);
+        auto add = [](float4 x, float4 y) { return make_float4(x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w); };
+#pragma unroll
+        for (int g = 0; g < kMaxMlpBlocks; ++g) t[g] = add(add(u[4 * g], u[4 * g + 1]), add(u[4 * g + 2], u[4 * g + 3]));
+    } else {
+#pragma unroll
+        for (int b = 0; b < kMaxMlpBlocks; ++b)
+            t[b] = *reinterpret_cast<const float4*>(src + (b < a.nblk ? b : a.nblk - 1) * KK);
+    }
     const float4 lv = *reinterpret_cast<const float4*>(a.vals + (static_cast<int64_t>(req) * B + p + 1) * K + b0);
     float4 acc = t[0];
 #pragma unroll
     for (int b = 1; b < kMaxMlpBlocks; ++b)
-        if (b < a.nblk) acc = make_float4(acc.x + t[b].x, acc.y + t[b].y, acc.z + t[b].z, acc.w + t[b].w);
+        if (b < nb64) acc = make_float4(acc.x + t[b].x, acc.y + t[b].y, acc.z + t[b].z, acc.w + t[b].w);
     float4 sv = make_float4(lv.x + (acc.x + b2), lv.y + (acc.y + b2), lv.z + (acc.z + b2), lv.w + (acc.w + b2));
     if (a.m < K)   // successors b >= m are not scored
         sv = make_float4(b0 < a.m ? sv.x : -INFINITY, b0 + 1 < a.m ? sv.y : -INFINITY,
@@ -649,13 +663,18 @@ bool finish_split(int B, int K, int rule) {
     return B > 1 && (K == 4 || K == 8 || K == 16) && rule == kPathGreedy;
 }
 
-hipError_t launch_finish(const FinishArgs& a, hipStream_t stream) {
+bool finish_by_pair(const FinishArgs& a) {
     const bool aligned =
         ((reinterpret_cast<uintptr_t>(a.scores) | reinterpret_cast<uintptr_t>(a.vals) | reinterpret_cast<uintptr_t>(a.part)) &
          15) == 0;
-    if (a.tokens && a.best && a.cnt && aligned && finish_split(a.B, a.K, a.rule))
+    return a.tokens && a.best && a.cnt && aligned && finish_split(a.B, a.K, a.rule);
+}
+
+hipError_t launch_finish(const FinishArgs& a, hipStream_t stream) {
+    if (finish_by_pair(a))
         return launch(finish_pair_kernel, dim3(static_cast<unsigned>(static_cast<int64_t>(a.n) * (a.B - 1))), 64, 0,
                       stream, a);
+    if (a.sub) return hipErrorInvalidValue;   // 16-unit partials are finished by pair only
     const size_t lds = path_lds_bytes(a.B, a.K);
     return launch(finish_kernel, dim3(static_cast<unsigned>(a.n)), 256, static_cast<uint32_t>(lds), stream, a,
                   lds > 0);
