@@ -342,7 +342,9 @@ __host__ __device__ inline int cand_as(int r) { return 4 * r + 8; }
 // acc = A (16 rows of LDS bf16 [hi | lo], 2 * KIN wide) x W^T for one 16-column
 // tile of W ([*][ldw] bf16, rows w_row0 + 0..15, columns 0..KIN-1).  The hi and
 // lo halves of A meet the same W columns, so acc ~ A_fp32 x W^T.  All W
-// fragments are loaded before the first MFMA.
+// fragments are loaded before the first MFMA.  Rows past M read row M - 1
+// (every fragment read is unconditional, so they are issued together); their
+// results are not used, and a row's results depend on that row only.
 template <int KIN>
 __device__ __forceinline__ f32x4 mfma_hilo_tile(const uint16_t* abuf, int as, int M, const uint16_t* W,
                                                 int ldw, int w_row0) {
@@ -351,16 +353,16 @@ __device__ __forceinline__ f32x4 mfma_hilo_tile(const uint16_t* abuf, int as, in
     const int kq = 8 * (l >> 4);
     const int m = l & 15;
     const uint16_t* wp = W + static_cast<int64_t>(w_row0 + m) * ldw;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
     u32x4 bv[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) bv[ks] = load16(wp + ((ks * 32 + kq) % KIN));
+    const uint16_t* arow = abuf + min(m, M - 1) * as + kq;
+    u32x4 av[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) av[ks] = *reinterpret_cast<const u32x4*>(arow + ks * 32);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 av = m < M ? *reinterpret_cast<const u32x4*>(abuf + m * as + ks * 32 + kq) : zero;
-        acc = mfma16x16x32(av, bv[ks], acc);
-    }
+    for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(av[ks], bv[ks], acc);
     return acc;
 }
 
@@ -372,13 +374,13 @@ __device__ __forceinline__ f32x4 mfma_hilo_tile_w(const uint16_t* abuf, int as, 
     const int l = lane_id();
     const int kq = 8 * (l >> 4);
     const int m = l & 15;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
+    const uint16_t* arow = abuf + min(m, M - 1) * as + kq;
+    u32x4 av[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) av[ks] = *reinterpret_cast<const u32x4*>(arow + ks * 32);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 av = m < M ? *reinterpret_cast<const u32x4*>(abuf + m * as + ks * 32 + kq) : zero;
-        acc = mfma16x16x32(av, bv[ks], acc);
-    }
+    for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(av[ks], bv[ks], acc);
     return acc;
 }
 
@@ -574,7 +576,7 @@ __global__ __launch_bounds__(kCT) void cand_kernel(CandArgs a) {
             const f32x4 acc = mfma_hilo_tile_w<2 * R>(abuf + rt * 16 * as, as, M - rt * 16, wfr[c]);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                if (rt * 16 + 4 * (l >> 4) + i < CR)   // a tile's rows past the group (CR = 8) are not kept
+                if (CR % 16 == 0 || rt * 16 + 4 * (l >> 4) + i < CR)   // a tile's rows past the group (CR = 4, 8) are not kept
                     ubuf[(rt * 16 + 4 * (l >> 4) + i) * us + ct * 16 + (l & 15)] = acc[i];
         }
     }
@@ -608,14 +610,25 @@ __global__ __launch_bounds__(kCT) void cand_kernel(CandArgs a) {
     const int dv = a.dvec;
     const int nvt = dv / 16;
     for (int which = 0; which < 2; ++which) {
-        for (int job = wave; job < nrt * nvt; job += kCW) {
-            const int rt = job / nvt, ct = job % nvt;
-            const f32x4 acc = mfma_hilo_tile<R>(abuf + rt * 16 * as, as, M - rt * 16, which ? a.w_in : a.w_out, R,
-                                                ct * 16);
+        // per column tile of the map: its W fragments loaded once, before the
+        // first MFMA, then every row tile of the group
+        constexpr int KSV = (2 * R + 31) / 32;
+        const uint16_t* wmap = which ? a.w_in : a.w_out;
+        for (int ct = wave; ct < nvt; ct += kCW) {
+            u32x4 bv[KSV];
+            {
+                const uint16_t* wp = wmap + static_cast<int64_t>(ct * 16 + (l & 15)) * R;
+                const int kq = 8 * (l >> 4);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (rt * 16 + 4 * (l >> 4) + i < CR)   // a tile's rows past the group (CR = 8) are not kept
-                    ubuf[(rt * 16 + 4 * (l >> 4) + i) * us + ct * 16 + (l & 15)] = acc[i];
+                for (int ks = 0; ks < KSV; ++ks) bv[ks] = load16(wp + ((ks * 32 + kq) % R));
+            }
+            for (int rt = 0; rt < nrt; ++rt) {
+                const f32x4 acc = mfma_hilo_tile_w<R>(abuf + rt * 16 * as, as, M - rt * 16, bv);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (CR % 16 == 0 || rt * 16 + 4 * (l >> 4) + i < CR)   // a tile's rows past the group (CR = 4, 8) are not kept
+                        ubuf[(rt * 16 + 4 * (l >> 4) + i) * us + ct * 16 + (l & 15)] = acc[i];
+            }
         }
         __syncthreads();
         for (int m = rsub; m < M; m += kCRows) {
