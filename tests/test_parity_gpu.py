@@ -157,6 +157,29 @@ def test_b32_batch_invariance_and_determinism():
             np.testing.assert_array_equal(one[k], sub[k], err_msg="request %d alone: %s" % (i, k))
 
 
+@pytest.mark.parametrize("name,n", [("b32", 32), ("b32", 1), ("tiny", 1)])
+def test_tokens_only(name, n):
+    """corrector_run with only the token output given (choice, ids, values and
+    scores left to the workspace): the same tokens as a run that asks for
+    every output."""
+    _log("tokens only %s n=%d" % (name, n))
+    import torch
+    from draft_correction_amd import device
+    x = P.inputs(name, head="stress")
+    cfg = x["cfg"]
+    full = P.gpu_run(x, n=n)
+    dev = P.dev_inputs(x)
+    corr = device.make_corrector(cfg, dev, max_requests=n)
+    ws = corr.new_workspace(n)
+    st = device.strides(cfg)
+    tokens = torch.full((n, cfg["B"]), -1, dtype=torch.int32, device="cuda")
+    corr.run(n, dev["logits"], st["l_req"], st["l_slot"], dev["hidden"], st["h_req"], st["h_slot"], tokens, ws,
+             l_offset=st["l_off"], h_offset=st["h_off"])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(tokens.cpu().numpy(), full["tokens"])
+    corr.close()
+
+
 def test_workspace_reuse_across_calls():
     """One workspace serves a sequence of calls with different request counts
     and repeated calls: each call's outputs equal those of a fresh workspace
