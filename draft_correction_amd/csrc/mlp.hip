@@ -16,10 +16,12 @@
 //
 // Work is split by (pairs, block of 64 hidden units): for K <= 16 each
 // workgroup streams a run of pairs through a producer / consumer split of its
-// waves (mlp_ws_kernel), for larger K each takes two adjacent pairs
+// waves (mlp_ws_kernel), or, for calls with few pairs, takes one pair and 16
+// units (mlp_pair16_kernel); for larger K each takes two adjacent pairs
 // (mlp_kernel).  Each block writes its partial Delta and the finishing kernel
 // adds the blocks in order, adds b2 and l_{p+1}(b) and walks.  Every sum runs
-// in a fixed order with no atomics: bit-reproducible.
+// in a fixed order, and no value is accumulated with atomics (they only
+// count): bit-reproducible.
 #include "common.h"
 #include "kernels.h"
 
