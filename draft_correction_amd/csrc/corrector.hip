@@ -100,7 +100,7 @@ Layout layout(const corrector_desc& d, int32_t n) {
     L.mlp_part = take(mlp ? sizeof(float) * pairs * (split ? d.mlp_hidden / 16 : mlp_blocks(d.mlp_hidden)) * d.k * d.k
                           : 0);
     L.best = take(split ? sizeof(int32_t) * pairs * d.k : 0);
-    L.cnt = take(split ? sizeof(int) * n : 0);
+    L.cnt = take(split ? sizeof(int) * kCntStride * n : 0);
     const bool cos = d.variant == CORR_VARIANT_COSINE;
     L.vout = take(cos ? sizeof(float) * rows * d.k * d.d_vec : 0);
     L.vin = take(cos ? sizeof(float) * rows * d.k * d.d_vec : 0);

@@ -162,10 +162,14 @@ struct MlpArgs {
     const float* w2;
     float* part;            // [n*(B-1)][blocks][K][K] partial Delta per hidden-unit block (b < m written)
     int m;                  // successors scored per predecessor (b < m; 1..K)
-    int* zero_cnt;          // K <= 16 and non-null: n counters the launch sets to 0 (for finish_pair_kernel)
+    int* zero_cnt;          // K <= 16 and non-null: n counters (kCntStride apart) the launch sets to 0
+                            // (for finish_pair_kernel)
     int units16;            // K <= 16: one workgroup per (pair, 16 units); part then holds
                             // [pairs][h/16][K][K] partials, each the first level of a 64-unit block's sum
 };
+// The finishing step's per-request counters sit kCntStride ints (128 bytes)
+// apart, one cache line each, so the requests' counts do not queue on one line.
+constexpr int kCntStride = 32;
 // Most hidden-unit blocks of the MLP (h <= 256 units in blocks of 64).
 constexpr int kMaxMlpBlocks = 4;
 // Most (pair, 16-unit block) workgroups for which the MLP takes its 16-unit
@@ -195,7 +199,7 @@ struct FinishArgs {
     int sub;                // part holds 16-unit partials (nblk of them), added four at a
                             // time in the 64-unit kernel's tree before the 64-unit blocks' sum
     int32_t* best;          // [n(B-1)][K] row argmaxes and
-    int* cnt;               // [n] pairs finished per request (zero at launch): with both
+    int* cnt;               // [n][kCntStride] pairs finished per request (zero at launch): with both
                             // given, the greedy walk for K = 4, 8, 16 runs one wave per pair
 };
 hipError_t launch_finish(const FinishArgs& a, hipStream_t stream);

@@ -373,7 +373,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void mlp_ws_kernel(MlpArgs a) {
 
     const int tid = threadIdx.x, l = tid & 63, wave = tid >> 6;
     if (a.zero_cnt && blockIdx.x == 0)   // the finishing launch's per-request counts
-        for (int i = tid; i < a.n; i += kWsThreads) a.zero_cnt[i] = 0;
+        for (int i = tid; i < a.n; i += kWsThreads) a.zero_cnt[static_cast<int64_t>(i) * kCntStride] = 0;
     const int B = a.B, K = a.K, h = a.h;
     const int nj = (h + kJB - 1) / kJB;
     const int P = a.n * (B - 1);
@@ -711,7 +711,7 @@ __global__ __launch_bounds__(256) void mlp_pair16_kernel(MlpArgs a) {
     __shared__ __attribute__((aligned(16))) float w2s[16];
     const int tid = threadIdx.x, l = tid & 63, wave = tid >> 6;
     if (a.zero_cnt && blockIdx.x == 0)           // the finishing launch's per-request counts
-        for (int i = tid; i < a.n; i += 256) a.zero_cnt[i] = 0;
+        for (int i = tid; i < a.n; i += 256) a.zero_cnt[static_cast<int64_t>(i) * kCntStride] = 0;
     const int B = a.B, K = a.K;
     const int nb = a.h / 16;                     // blocks of 16 units (h is a multiple of 16)
     const int pair = blockIdx.x / nb, blk = blockIdx.x - pair * nb;

@@ -578,7 +578,9 @@ __global__ __launch_bounds__(64) void finish_pair_kernel(FinishArgs a) {
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's stores are complete
     asm volatile("" ::: "memory");
     int done = 0;
-    if (l == 0) done = __hip_atomic_fetch_add(a.cnt + req, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (l == 0)
+        done = __hip_atomic_fetch_add(a.cnt + static_cast<int64_t>(req) * kCntStride, 1, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
     if (__shfl(done, 0, 64) != B - 2) return;   // not the request's last pair
     // the walk: lane q < B - 1 holds best[q][.] packed four bits per entry
     uint64_t row = 0;
