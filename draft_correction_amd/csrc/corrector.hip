@@ -95,9 +95,10 @@ Layout layout(const corrector_desc& d, int32_t n) {
     L.s = take(sizeof(float) * pairs * d.r);
     const bool mlp = d.variant == CORR_VARIANT_MLP;
     const bool split = mlp && finish_split(d.slots, d.k, d.path_rule);
-    // the partials of the 64-unit blocks, or with the split finishing step
-    // those of the 16-unit blocks of mlp_pair16_kernel
-    L.mlp_part = take(mlp ? sizeof(float) * pairs * (split ? d.mlp_hidden / 16 : mlp_blocks(d.mlp_hidden)) * d.k * d.k
+    // the partials of the 64-unit blocks, or those of the 16-unit blocks of
+    // mlp_pair16_kernel when a call this size may take that form
+    const bool p16 = split && d.k <= 16 && pairs * (d.mlp_hidden / 16) <= kMlp16MaxGroups;
+    L.mlp_part = take(mlp ? sizeof(float) * pairs * (p16 ? d.mlp_hidden / 16 : mlp_blocks(d.mlp_hidden)) * d.k * d.k
                           : 0);
     L.best = take(split ? sizeof(int32_t) * pairs * d.k : 0);
     L.cnt = take(split ? sizeof(int) * kCntStride * n : 0);
