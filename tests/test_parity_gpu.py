@@ -143,6 +143,24 @@ def test_b32(head):
         assert moved > steps // 10
 
 
+@pytest.mark.parametrize("n,first", [(6, 5), (3, 20)])
+def test_b32_mid_batch(n, first):
+    """Middle batch sizes, between the batch-1 and batch-32 forms: n = 6 puts
+    the candidate kernel in groups of 8 (1440 candidates) and n = 3 in groups
+    of 4; the small GEMM forms and the warp-specialised MLP (more than 256
+    pair-block groups) run on uneven runs of pairs."""
+    _log("b32 mid batch n=%d first=%d" % (n, first))
+    x = P.inputs("b32", head="stress")
+    gpu = P.gpu_run(x, n=n, first=first)
+    ora = P.oracle_run(x, n=n, first=first)
+    steps, exempt, moved = P.check_all(gpu, ora, "b32/n=%d" % n)
+    _log("  walk steps %d exempt %d moved %d" % (steps, exempt, moved))
+    full = P.gpu_run(x)
+    sub = P.select(full, first, n)
+    for k in ("ids", "vals", "scores", "tokens", "choice", "z", "s", "g"):
+        np.testing.assert_array_equal(gpu[k], sub[k], err_msg="n=%d against the batch of 32: %s" % (n, k))
+
+
 def test_b32_batch_invariance_and_determinism():
     _log("b32 batch invariance")
     x = P.inputs("b32")
