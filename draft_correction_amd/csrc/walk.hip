@@ -516,10 +516,12 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a, int use_lds) 
 // 16): one wave per pair forms its K x K scores exactly as finish_kernel does
 // (block partials in block order, + b2, + l_{p+1}(b)), writes them, and takes
 // the argmax of every row (ties to the lowest successor index) into
-// best[pair][a]; the last wave of a request to finish (by the count cnt[req],
-// which the MLP launch zeroed) follows the chain k_1 = 0,
-// k_{p+1} = best[p][k_p] and writes choice and tokens.  A request's pair
-// states thus come from B - 1 CUs at once instead of one.  The hand-off uses
+// best[pair][a]; the last wave of a request to finish (by the request's
+// count, which the MLP launch zeroed, one cache line per request) follows the
+// chain k_1 = 0, k_{p+1} = best[p][k_p] and writes choice and tokens.  With
+// the MLP's 16-unit partials (a.sub) it first adds them four at a time in
+// the 64-unit form's tree.  A request's partials are thus read by B - 1 CUs
+// at once instead of one.  The hand-off uses
 // agent-scope atomic stores and loads for best and the count (coherent across
 // the chip's L2 caches without a cache write-back), the stores completed
 // before the count is taken.
