@@ -200,7 +200,8 @@ struct FinishArgs {
                             // time in the 64-unit kernel's tree before the 64-unit blocks' sum
     int32_t* best;          // [n(B-1)][K] row argmaxes and
     int* cnt;               // [n][kCntStride] pairs finished per request (zero at launch): with both
-                            // given, the greedy walk for K = 4, 8, 16 runs one wave per pair
+                            // given, K = 4, 8 or 16 and the scores fitting the path's LDS, the
+                            // launch runs one wave per pair (the request's last one takes the path)
 };
 hipError_t launch_finish(const FinishArgs& a, hipStream_t stream);
 // Whether launch_finish splits the work by pair for this shape and rule (it

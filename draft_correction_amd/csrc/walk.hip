@@ -165,6 +165,76 @@ __device__ __forceinline__ void viterbi_wave(const float* src, uint8_t* from, in
     }
 }
 
+// The same dynamic program for K <= 16 with all 64 lanes at work: lane l
+// takes successor b = l % 16 (lanes with b >= K mirror K - 1) and the four
+// predecessors a = 4g .. 4g + 3 of its group g = l / 16.  Each lane forms its
+// four fmaf(lam^p, S_p(a, b), best[a]) (the same float32 operations as
+// viterbi_wave), their fmaxf and the lowest a reaching it; two exchanges
+// across the groups (lanes l ^ 16, l ^ 32) take the fmaxf of the groups'
+// values and the lowest a among the groups that reach it.  Every b thus ends
+// with viterbi_wave's maximum and predecessor, bit for bit.  The next pair's four scores are
+// loaded while the current pair is reduced; best stays in LDS (vb), which
+// one wave writes after it has read it, in program order.
+__device__ __forceinline__ void viterbi16_wave(const float* src, uint8_t* from, int* chain, float* vb,
+                                               const int32_t* __restrict__ ids, int req, int B, int K, float lam,
+                                               int32_t* __restrict__ tokens, int32_t* __restrict__ choice) {
+    const int l = lane_id();
+    const int g = l >> 4;
+    const int b = min(l & 15, K - 1);
+    if (l < 16) vb[l] = l == 0 ? 0.f : -INFINITY;   // slot 1: the drafter's argmax
+    float s[4];
+    auto load = [&](int p, float (&t)[4]) {
+        const float* Sp = src + static_cast<int64_t>(p) * K * K;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t[i] = Sp[min(4 * g + i, K - 1) * K + b];   // clamped: past K unused
+    };
+    if (B > 1) load(0, s);
+    float m = l == 0 ? 0.f : -INFINITY;
+    float wp = 1.f;
+    for (int p = 0; p + 1 < B; ++p, wp *= lam) {
+        float sn[4];
+        load(min(p + 1, B - 2), sn);
+        wave_lds_sync();
+        const float4 v4 = *reinterpret_cast<const float4*>(vb + 4 * g);
+        const float pv[4] = {v4.x, v4.y, v4.z, v4.w};
+        float c[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c[i] = 4 * g + i < K ? fmaf(wp, s[i], pv[i]) : -INFINITY;
+        m = fmaxf(fmaxf(c[0], c[1]), fmaxf(c[2], c[3]));
+        // the lowest a whose value is the maximum (64: none in this group)
+        int arg = c[0] == m ? 0 : (c[1] == m ? 1 : (c[2] == m ? 2 : (c[3] == m ? 3 : 64 - 4 * g)));
+        arg += 4 * g;
+#pragma unroll
+        for (int sh = 16; sh <= 32; sh <<= 1) {
+            const float om = __shfl_xor(m, sh, 64);
+            const int oa = __shfl_xor(arg, sh, 64);
+            const float mm = fmaxf(m, om);
+            arg = min(m == mm ? arg : 64, om == mm ? oa : 64);
+            m = mm;
+        }
+        if (l < K) from[p * K + l] = static_cast<uint8_t>(arg == 64 ? 0 : arg);
+        if (l < 16) vb[l] = m;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[i] = sn[i];
+    }
+    int k = wave_argmax_lowest(l < K ? m : -INFINITY, K);
+    wave_lds_sync();
+    if (l == 0) {
+        for (int t = B - 1; t >= 1; --t) {
+            chain[t] = k;
+            k = from[(t - 1) * K + k];
+        }
+        chain[0] = 0;
+    }
+    wave_lds_sync();
+    if (l < B) {
+        const int64_t s_ = static_cast<int64_t>(req) * B + l;
+        const int ch = chain[l];
+        if (choice) choice[s_] = ch;
+        tokens[s_] = ids[s_ * K + ch];
+    }
+}
+
 // LDS of a path over scores held in LDS: the scores, then from/best
 // ([B-1][K] bytes), then chain ([B] ints), then vb (K rounded up to 16
 // floats, 16-byte aligned); without the scores, the last three alone.
@@ -291,6 +361,68 @@ __device__ __forceinline__ void beam_wave(const float* src, uint8_t* bp, int* ch
     }
 }
 
+// The same beam search for K <= 16, where the nb * K <= 64 extensions of a
+// pair fit one per lane (extension c = lane): each of the W rounds takes the
+// wave's largest remaining score and the lowest lane holding it, which is
+// beam_wave's choice (its lanes hold only their first extension here), so
+// the kept paths are the same, bit for bit.
+__device__ __forceinline__ void beam16_wave(const float* src, uint8_t* bp, int* chain, const int32_t* __restrict__ ids,
+                                            int req, int B, int K, int W, int32_t* __restrict__ tokens,
+                                            int32_t* __restrict__ choice) {
+    const int l = lane_id();
+    const int i = (l >= K) + (l >= 2 * K) + (l >= 3 * K);   // the lane's beam path
+    const int b = min(l - i * K, K - 1);                    // and successor (clamped past 4K: unused)
+    float g0 = 0.f, g1 = 0.f, g2 = 0.f, g3 = 0.f;
+    int t0 = 0, t1 = 0, t2 = 0, t3 = 0;
+    int nb = 1;
+    for (int p = 0; p + 1 < B; ++p) {
+        const float* Sp = src + static_cast<int64_t>(p) * K * K;
+        const int nc = nb * K;
+        const float gi = i == 0 ? g0 : (i == 1 ? g1 : (i == 2 ? g2 : g3));
+        const int ti = i == 0 ? t0 : (i == 1 ? t1 : (i == 2 ? t2 : t3));
+        bool alive = l < nc;
+        const float cv = alive ? gi + Sp[ti * K + b] : -INFINITY;
+        const int keep = min(W, nc);
+        float ng[4] = {0.f, 0.f, 0.f, 0.f};
+        int nt[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            if (r >= keep) break;
+            const float M = wave_max_all(alive ? cv : -INFINITY);
+            const uint64_t win = ballot(alive && cv == M);
+            const int wl = win ? __ffsll(static_cast<unsigned long long>(win)) - 1 : 0;
+            const int wi = (wl >= K) + (wl >= 2 * K) + (wl >= 3 * K);
+            const int wb = wl - wi * K;
+            ng[r] = M;
+            nt[r] = wb;
+            if (l == 0) {
+                bp[(p * 4 + r) * 2] = static_cast<uint8_t>(wi);
+                bp[(p * 4 + r) * 2 + 1] = static_cast<uint8_t>(wb);
+            }
+            alive = alive && l != wl;
+        }
+        g0 = ng[0]; g1 = ng[1]; g2 = ng[2]; g3 = ng[3];
+        t0 = nt[0]; t1 = nt[1]; t2 = nt[2]; t3 = nt[3];
+        nb = keep;
+    }
+    wave_lds_sync();
+    if (l == 0) {
+        int r = 0;
+        for (int p = B - 2; p >= 0; --p) {
+            chain[p + 1] = bp[(p * 4 + r) * 2 + 1];
+            r = bp[(p * 4 + r) * 2];
+        }
+        chain[0] = 0;
+    }
+    wave_lds_sync();
+    if (l < B) {
+        const int64_t s_ = static_cast<int64_t>(req) * B + l;
+        const int ch = chain[l];
+        if (choice) choice[s_] = ch;
+        tokens[s_] = ids[s_ * K + ch];
+    }
+}
+
 // The request's path from scores in LDS (every thread of the workgroup
 // calls it): the greedy walk uses the whole workgroup, the Global-Sum
 // dynamic program its first wave.
@@ -301,13 +433,23 @@ __device__ __forceinline__ void path_from_lds(int rule, float lam, int beam, flo
     int* chain = reinterpret_cast<int*>(reinterpret_cast<char*>(sS) + path_chain_offset(B, K, true));
     if (rule == kPathBeam) {
         uint8_t* bp = reinterpret_cast<uint8_t*>(reinterpret_cast<char*>(sS) + path_beam_offset(B, K, true));
-        if ((threadIdx.x >> 6) == 0) beam_wave(sS, bp, chain, ids, req, B, K, beam, tokens, choice);
+        if ((threadIdx.x >> 6) == 0) {
+            if (K <= 16)
+                beam16_wave(sS, bp, chain, ids, req, B, K, beam, tokens, choice);
+            else
+                beam_wave(sS, bp, chain, ids, req, B, K, beam, tokens, choice);
+        }
         return;
     }
     if (rule != kPathGreedy) {
         float* vb = reinterpret_cast<float*>(reinterpret_cast<char*>(sS) + path_vb_offset(B, K, true));
-        if ((threadIdx.x >> 6) == 0)
-            viterbi_wave(sS, aux, chain, vb, ids, req, B, K, rule == kPathGeometric ? lam : 1.f, tokens, choice);
+        const float w = rule == kPathGeometric ? lam : 1.f;
+        if ((threadIdx.x >> 6) == 0) {
+            if (K <= 16)
+                viterbi16_wave(sS, aux, chain, vb, ids, req, B, K, w, tokens, choice);
+            else
+                viterbi_wave(sS, aux, chain, vb, ids, req, B, K, w, tokens, choice);
+        }
         return;
     }
     walk_block(sS, aux, chain, ids, req, B, K, tokens, choice);
@@ -352,14 +494,21 @@ __global__ __launch_bounds__(64) void path_kernel(const float* __restrict__ scor
     if (rule == kPathBeam) {
         int* chain = reinterpret_cast<int*>(reinterpret_cast<char*>(sl) + path_chain_offset(B, K, false));
         uint8_t* bp = reinterpret_cast<uint8_t*>(reinterpret_cast<char*>(sl) + path_beam_offset(B, K, false));
-        beam_wave(base, bp, chain, ids, req, B, K, beam, tokens, choice);
+        if (K <= 16)
+            beam16_wave(base, bp, chain, ids, req, B, K, beam, tokens, choice);
+        else
+            beam_wave(base, bp, chain, ids, req, B, K, beam, tokens, choice);
         return;
     }
     if (rule != kPathGreedy) {
         uint8_t* from = reinterpret_cast<uint8_t*>(sl);
         int* chain = reinterpret_cast<int*>(reinterpret_cast<char*>(sl) + path_chain_offset(B, K, false));
         float* vb = reinterpret_cast<float*>(reinterpret_cast<char*>(sl) + path_vb_offset(B, K, false));
-        viterbi_wave(base, from, chain, vb, ids, req, B, K, rule == kPathGeometric ? lam : 1.f, tokens, choice);
+        const float w = rule == kPathGeometric ? lam : 1.f;
+        if (K <= 16)
+            viterbi16_wave(base, from, chain, vb, ids, req, B, K, w, tokens, choice);
+        else
+            viterbi_wave(base, from, chain, vb, ids, req, B, K, w, tokens, choice);
         return;
     }
     walk_wave(base, ids, req, B, K, tokens, choice);
@@ -512,20 +661,29 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a, int use_lds) 
     path_from_lds(a.rule, a.lam, a.beam, sS, a.ids, req, B, K, a.tokens, a.choice);
 }
 
-// The finishing step with the prefix-first walk, split by pair (K = 4, 8 or
-// 16): one wave per pair forms its K x K scores exactly as finish_kernel does
-// (block partials in block order, + b2, + l_{p+1}(b)), writes them, and takes
-// the argmax of every row (ties to the lowest successor index) into
-// best[pair][a]; the last wave of a request to finish (by the request's
-// count, which the MLP launch zeroed, one cache line per request) follows the
-// chain k_1 = 0, k_{p+1} = best[p][k_p] and writes choice and tokens.  With
-// the MLP's 16-unit partials (a.sub) it first adds them four at a time in
-// the 64-unit form's tree.  A request's partials are thus read by B - 1 CUs
-// at once instead of one.  The hand-off uses
-// agent-scope atomic stores and loads for best and the count (coherent across
-// the chip's L2 caches without a cache write-back), the stores completed
-// before the count is taken.
+// The finishing step split by pair (K = 4, 8 or 16): one wave per pair forms
+// its K x K scores exactly as finish_kernel does (block partials in block
+// order, + b2, + l_{p+1}(b)) and writes them; the last wave of a request to
+// finish (by the request's count, which the MLP launch zeroed, one cache line
+// per request) then takes the request's path.  With the MLP's 16-unit
+// partials (a.sub) the wave first adds them four at a time in the 64-unit
+// form's tree.  A request's partials are thus read by B - 1 CUs at once
+// instead of one.
+//   - Prefix-first walk: each wave also takes the argmax of every row of its
+//     pair (ties to the lowest successor index) into best[pair][a]; the last
+//     wave follows the chain k_1 = 0, k_{p+1} = best[p][k_p].
+//   - Global-Sum, Geometric and beam rules: the last wave reads the request's
+//     scores back into LDS (dynamic, path_lds_bytes) and runs the rule there,
+//     as finish_kernel does.
+// The hand-off uses agent-scope atomic stores and loads (coherent across the
+// chip's L2 caches without a cache write-back) for what the last wave reads
+// (best, or the scores) and for the count, the stores completed before the
+// count is taken.
+// kWalk: the instance for the prefix-first walk (a.rule greedy), else the
+// one for the other rules.
+template <bool kWalk>
 __global__ __launch_bounds__(64) void finish_pair_kernel(FinishArgs a) {
+    extern __shared__ __attribute__((aligned(16))) float sS[];
     const int B = a.B, K = a.K, KK = K * K;
     const int pair = blockIdx.x;
     const int req = pair / (B - 1), p = pair - req * (B - 1);
@@ -562,6 +720,41 @@ __global__ __launch_bounds__(64) void finish_pair_kernel(FinishArgs a) {
     if (a.m < K)   // successors b >= m are not scored
         sv = make_float4(b0 < a.m ? sv.x : -INFINITY, b0 + 1 < a.m ? sv.y : -INFINITY,
                          b0 + 2 < a.m ? sv.z : -INFINITY, b0 + 3 < a.m ? sv.w : -INFINITY);
+    if (!kWalk) {
+        // read back by the request's last wave, on any XCD
+        uint64_t* dst = reinterpret_cast<uint64_t*>(a.scores + static_cast<int64_t>(pair) * KK) + 2 * l;
+        const uint64_t lo = static_cast<uint64_t>(__float_as_uint(sv.x)) | static_cast<uint64_t>(__float_as_uint(sv.y)) << 32;
+        const uint64_t hi = static_cast<uint64_t>(__float_as_uint(sv.z)) | static_cast<uint64_t>(__float_as_uint(sv.w)) << 32;
+        if (l < nv) {
+            __hip_atomic_store(dst, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(dst + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's stores are complete
+        asm volatile("" ::: "memory");
+        int done = 0;
+        if (l == 0)
+            done = __hip_atomic_fetch_add(a.cnt + static_cast<int64_t>(req) * kCntStride, 1, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+        if (__shfl(done, 0, 64) != B - 2) return;   // not the request's last pair
+        // the request's (B - 1) K^2 scores into LDS, 64 bits per load, all of
+        // a round's loads issued before any is used
+        const int n2 = (B - 1) * KK / 2;
+        const uint64_t* src2 = reinterpret_cast<const uint64_t*>(a.scores + static_cast<int64_t>(req) * (B - 1) * KK);
+        uint64_t* s2 = reinterpret_cast<uint64_t*>(sS);
+        for (int i0 = 0; i0 < n2; i0 += 32 * kWave) {
+            uint64_t t[32];
+#pragma unroll
+            for (int u = 0; u < 32; ++u)
+                t[u] = __hip_atomic_load(src2 + min(i0 + u * kWave + l, n2 - 1), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);   // clamped: in bounds
+#pragma unroll
+            for (int u = 0; u < 32; ++u)
+                if (i0 + u * kWave + l < n2) s2[i0 + u * kWave + l] = t[u];
+        }
+        wave_lds_sync();
+        path_from_lds(a.rule, a.lam, a.beam, sS, a.ids, req, B, K, a.tokens, a.choice);
+        return;
+    }
     if (l < nv) reinterpret_cast<float4*>(a.scores + static_cast<int64_t>(pair) * KK)[l] = sv;
     // row aa's argmax: the lane's four in index order (strict compare), then
     // across the K / 4 consecutive lanes of the row, ties to the lower index
@@ -664,7 +857,7 @@ hipError_t launch_path(const float* scores, const int32_t* ids, int n, int B, in
 }
 
 bool finish_split(int B, int K, int rule) {
-    return B > 1 && (K == 4 || K == 8 || K == 16) && rule == kPathGreedy;
+    return B > 1 && (K == 4 || K == 8 || K == 16) && (rule == kPathGreedy || path_fits_lds(B, K));
 }
 
 bool finish_by_pair(const FinishArgs& a) {
@@ -675,9 +868,11 @@ bool finish_by_pair(const FinishArgs& a) {
 }
 
 hipError_t launch_finish(const FinishArgs& a, hipStream_t stream) {
-    if (finish_by_pair(a))
-        return launch(finish_pair_kernel, dim3(static_cast<unsigned>(static_cast<int64_t>(a.n) * (a.B - 1))), 64, 0,
-                      stream, a);
+    if (finish_by_pair(a)) {
+        const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.n) * (a.B - 1)));
+        if (a.rule == kPathGreedy) return launch(finish_pair_kernel<true>, grid, 64, 0, stream, a);
+        return launch(finish_pair_kernel<false>, grid, 64, static_cast<uint32_t>(path_lds_bytes(a.B, a.K)), stream, a);
+    }
     if (a.sub) return hipErrorInvalidValue;   // 16-unit partials are finished by pair only
     const size_t lds = path_lds_bytes(a.B, a.K);
     return launch(finish_kernel, dim3(static_cast<unsigned>(a.n)), 256, static_cast<uint32_t>(lds), stream, a,

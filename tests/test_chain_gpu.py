@@ -44,6 +44,23 @@ def test_chain_matches_run(fold):
         np.testing.assert_array_equal(a[k], b[k], err_msg=k)
 
 
+@pytest.mark.parametrize("rule", ["global_sum", "geometric", "beam"])
+@pytest.mark.parametrize("name", ["tiny", "b1", "b32"])
+def test_chain_matches_run_rules(name, rule):
+    """With the Global-Sum, Geometric and beam rules, corrector_run finishes
+    the scores one wave per pair and takes each request's path in the wave of
+    its last pair (K = 4 and 16 here); the split calls form the scores one
+    workgroup per request and take the paths in corrector_walk.  Same scores
+    and paths, bit for bit."""
+    _log("chain vs run %s %s" % (rule, name))
+    lam = 0.75 if rule == "geometric" else 1.0
+    x = P.inputs(name, head="stress", path_rule=rule, path_lambda=lam, beam_width=3)
+    a = P.gpu_chain(x)
+    b = P.gpu_run(x)
+    for k in ("ids", "vals", "scores", "tokens", "choice"):
+        np.testing.assert_array_equal(a[k], b[k], err_msg="%s %s: %s" % (rule, name, k))
+
+
 @pytest.mark.parametrize("fold", [False, True])
 def test_chain_cosine(fold):
     _log("chain cosine fold=%s" % fold)

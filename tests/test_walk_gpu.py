@@ -97,3 +97,27 @@ def test_walk_rules(rule, B, K):
     # index, exactly; the dynamic programs return an optimal path)
     S = g.integers(-2, 3, size=(n, B - 1, K, K)).astype(np.float32)
     _check(S, ids, rule, "ties %s B=%d K=%d" % (rule, B, K), ties=True)
+
+
+@pytest.mark.parametrize("rule", ["global_sum", "geometric", "beam1", "beam2", "beam4"])
+def test_k16_forms_match_general(rule):
+    """For K <= 16 the dynamic program and the beam search run in forms that
+    spread a pair's work over all 64 lanes; they must choose exactly what the
+    general forms choose.  The same scores padded with a 17th candidate whose
+    scores are all -inf (which no path can use) go through the general forms:
+    the choices must be identical, on continuous scores and on tie-heavy
+    integer scores."""
+    print("K=16 forms against K=17 %s" % rule, flush=True)
+    g = np.random.default_rng(1616)
+    n, B, K = 8, 15, 16
+    ids = g.integers(0, 1000, size=(n, B, K)).astype(np.int32)
+    ids17 = np.concatenate([ids, np.zeros((n, B, 1), np.int32)], axis=2)
+    for kind in ("normal", "ties"):
+        S = (g.normal(size=(n, B - 1, K, K)) if kind == "normal"
+             else g.integers(-2, 3, size=(n, B - 1, K, K))).astype(np.float32)
+        S17 = np.full((n, B - 1, K + 1, K + 1), -np.inf, np.float32)
+        S17[:, :, :K, :K] = S
+        t16, c16, _ = _walk(S, ids, rule)
+        t17, c17, _ = _walk(S17, ids17, rule)
+        np.testing.assert_array_equal(c16, c17, err_msg="%s %s" % (rule, kind))
+        np.testing.assert_array_equal(t16, t17, err_msg="%s %s tokens" % (rule, kind))
