@@ -166,21 +166,23 @@ __device__ __forceinline__ void viterbi_wave(const float* src, uint8_t* from, in
 }
 
 // The same dynamic program for K <= 16 with all 64 lanes at work: lane l
-// takes successor b = l % 16 (lanes with b >= K mirror K - 1) and the four
-// predecessors a = 4g .. 4g + 3 of its group g = l / 16.  Each lane forms its
-// four fmaf(lam^p, S_p(a, b), best[a]) (the same float32 operations as
-// viterbi_wave), their fmaxf and the lowest a reaching it; two exchanges
-// across the groups (lanes l ^ 16, l ^ 32) take the fmaxf of the groups'
+// takes successor b = l / 4 and the four predecessors a = 4g .. 4g + 3 of its
+// group g = l % 4, so the four groups of a successor share a quad.  Each lane
+// forms its four fmaf(lam^p, S_p(a, b), best[a]) (the same float32
+// operations as viterbi_wave), their fmaxf and the lowest a reaching it; two
+// quad exchanges (DPP, lanes l ^ 1 and l ^ 2) take the fmaxf of the groups'
 // values and the lowest a among the groups that reach it.  Every b thus ends
-// with viterbi_wave's maximum and predecessor, bit for bit.  The next pair's four scores are
-// loaded while the current pair is reduced; best stays in LDS (vb), which
-// one wave writes after it has read it, in program order.
+// with viterbi_wave's maximum and predecessor, bit for bit.  best stays in LDS
+// (vb), which the one wave writes after it has read it, in program order; a
+// step reads it first and then loads the next pair's scores, which arrive
+// while the step is reduced.
 __device__ __forceinline__ void viterbi16_wave(const float* src, uint8_t* from, int* chain, float* vb,
                                                const int32_t* __restrict__ ids, int req, int B, int K, float lam,
                                                int32_t* __restrict__ tokens, int32_t* __restrict__ choice) {
     const int l = lane_id();
-    const int g = l >> 4;
-    const int b = min(l & 15, K - 1);
+    const int g = l & 3;
+    const int b = min(l >> 2, K - 1);
+    const bool head = (l & 3) == 0 && (l >> 2) < K;   // one lane per successor writes
     if (l < 16) vb[l] = l == 0 ? 0.f : -INFINITY;   // slot 1: the drafter's argmax
     float s[4];
     auto load = [&](int p, float (&t)[4]) {
@@ -189,35 +191,46 @@ __device__ __forceinline__ void viterbi16_wave(const float* src, uint8_t* from, 
         for (int i = 0; i < 4; ++i) t[i] = Sp[min(4 * g + i, K - 1) * K + b];   // clamped: past K unused
     };
     if (B > 1) load(0, s);
-    float m = l == 0 ? 0.f : -INFINITY;
     float wp = 1.f;
     for (int p = 0; p + 1 < B; ++p, wp *= lam) {
-        float sn[4];
-        load(min(p + 1, B - 2), sn);
         wave_lds_sync();
         const float4 v4 = *reinterpret_cast<const float4*>(vb + 4 * g);
+        float sn[4];
+        load(min(p + 1, B - 2), sn);
         const float pv[4] = {v4.x, v4.y, v4.z, v4.w};
         float c[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) c[i] = 4 * g + i < K ? fmaf(wp, s[i], pv[i]) : -INFINITY;
-        m = fmaxf(fmaxf(c[0], c[1]), fmaxf(c[2], c[3]));
+        float m = fmaxf(fmaxf(c[0], c[1]), fmaxf(c[2], c[3]));
         // the lowest a whose value is the maximum (64: none in this group)
-        int arg = c[0] == m ? 0 : (c[1] == m ? 1 : (c[2] == m ? 2 : (c[3] == m ? 3 : 64 - 4 * g)));
-        arg += 4 * g;
-#pragma unroll
-        for (int sh = 16; sh <= 32; sh <<= 1) {
-            const float om = __shfl_xor(m, sh, 64);
-            const int oa = __shfl_xor(arg, sh, 64);
+        int arg = c[3] == m ? 4 * g + 3 : 64;
+        arg = c[2] == m ? 4 * g + 2 : arg;
+        arg = c[1] == m ? 4 * g + 1 : arg;
+        arg = c[0] == m ? 4 * g : arg;
+        {
+            const float om = dpp_f<kDppXor1>(m);
+            const int oa = __builtin_amdgcn_update_dpp(0, arg, kDppXor1, 0xF, 0xF, false);
             const float mm = fmaxf(m, om);
             arg = min(m == mm ? arg : 64, om == mm ? oa : 64);
             m = mm;
         }
-        if (l < K) from[p * K + l] = static_cast<uint8_t>(arg == 64 ? 0 : arg);
-        if (l < 16) vb[l] = m;
+        {
+            const float om = dpp_f<kDppXor2>(m);
+            const int oa = __builtin_amdgcn_update_dpp(0, arg, kDppXor2, 0xF, 0xF, false);
+            const float mm = fmaxf(m, om);
+            arg = min(m == mm ? arg : 64, om == mm ? oa : 64);
+            m = mm;
+        }
+        if (head) {
+            from[p * K + (l >> 2)] = static_cast<uint8_t>(arg == 64 ? 0 : arg);
+            vb[l >> 2] = m;
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) s[i] = sn[i];
     }
-    int k = wave_argmax_lowest(l < K ? m : -INFINITY, K);
+    wave_lds_sync();
+    const float fin = l < K ? vb[l] : -INFINITY;   // best of the last slot (slot 1 when B = 1)
+    int k = wave_argmax_lowest(fin, K);
     wave_lds_sync();
     if (l == 0) {
         for (int t = B - 1; t >= 1; --t) {

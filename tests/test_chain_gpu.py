@@ -61,6 +61,22 @@ def test_chain_matches_run_rules(name, rule):
         np.testing.assert_array_equal(a[k], b[k], err_msg="%s %s: %s" % (rule, name, k))
 
 
+@pytest.mark.parametrize("rule", ["global_sum", "geometric", "beam"])
+def test_chain_matches_run_rules_top_m(rule):
+    """The same comparison with only the first 8 successors of each pair
+    scored (the rest -inf, written by the per-pair finishing waves): same
+    scores and paths, and no path leaves the kept successors."""
+    _log("chain vs run %s top-m 8" % rule)
+    lam = 0.75 if rule == "geometric" else 1.0
+    x = P.inputs("b32", head="stress", path_rule=rule, path_lambda=lam, beam_width=4, succ_top_m=8)
+    a = P.gpu_chain(x)
+    b = P.gpu_run(x)
+    for k in ("scores", "tokens", "choice"):
+        np.testing.assert_array_equal(a[k], b[k], err_msg="%s top-m: %s" % (rule, k))
+    assert np.isneginf(b["scores"][..., 8:]).all()
+    assert (b["choice"][:, 1:] < 8).all()
+
+
 @pytest.mark.parametrize("fold", [False, True])
 def test_chain_cosine(fold):
     _log("chain cosine fold=%s" % fold)
