@@ -94,7 +94,10 @@ Layout layout(const corrector_desc& d, int32_t n) {
     L.g = take(sizeof(float) * rows * d.r);
     L.s = take(sizeof(float) * pairs * d.r);
     const bool mlp = d.variant == CORR_VARIANT_MLP;
-    const bool split = mlp && finish_split(d.slots, d.k, d.path_rule);
+    const bool cos = d.variant == CORR_VARIANT_COSINE;
+    // the MLP's finishing launch or the cosine launch split by pair: row
+    // argmaxes and per-request counts
+    const bool split = (mlp || cos) && finish_split(d.slots, d.k, d.path_rule);
     // the partials of the 64-unit blocks, or those of the 16-unit blocks of
     // mlp_pair16_kernel when a call this size may take that form
     const bool p16 = split && d.k <= 16 && pairs * (d.mlp_hidden / 16) <= kMlp16MaxGroups;
@@ -102,7 +105,6 @@ Layout layout(const corrector_desc& d, int32_t n) {
                           : 0);
     L.best = take(split ? sizeof(int32_t) * pairs * d.k : 0);
     L.cnt = take(split ? sizeof(int) * kCntStride * n : 0);
-    const bool cos = d.variant == CORR_VARIANT_COSINE;
     L.vout = take(cos ? sizeof(float) * rows * d.k * d.d_vec : 0);
     L.vin = take(cos ? sizeof(float) * rows * d.k * d.d_vec : 0);
     L.scores = take(sizeof(float) * pairs * d.k * d.k);
@@ -327,6 +329,11 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
         ca.vout = at<float>(ws, L.vout);
         ca.vin = at<float>(ws, L.vin);
     }
+    // the cosine launch split by pair counts its pairs per request; the
+    // candidate launch zeroes the counts
+    const bool cos_split = cos && tokens && d.slots > 1 && finish_split(d.slots, d.k, d.path_rule);
+    ca.zero_cnt = cos_split ? at<int>(ws, L.cnt) : nullptr;
+    ca.zero_n = n;
     q("cand", [&] { return launch_cand(ca, q.s); });
     if (d.slots < 2) {
         if (tokens) q(path_name(h), [&] { return launch_path_rule(h, scores, ids, n, tokens, choice, q.s); });
@@ -352,6 +359,8 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
         c.rule = d.path_rule;
         c.lam = d.path_lambda;
         c.beam = d.beam_width;
+        c.best = cos_split ? at<int32_t>(ws, L.best) : nullptr;
+        c.cnt = ca.zero_cnt;
         q(fused ? (d.path_rule == CORR_PATH_GREEDY ? "cosine_walk"
                                                     : (d.path_rule == CORR_PATH_BEAM ? "cosine_beam" : "cosine_viterbi"))
                 : "cosine",

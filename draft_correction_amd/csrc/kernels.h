@@ -143,6 +143,10 @@ struct CandArgs {
     int dvec;
     float* vout;
     float* vin;
+    // with zero_cnt given, workgroup 0 zeroes zero_cnt[i * kCntStride], i < zero_n
+    // (the per-request counts of a cosine launch split by pair)
+    int* zero_cnt;
+    int zero_n;
 };
 size_t cand_lds_bytes(int r, int dvec, int K);
 hipError_t launch_cand(const CandArgs& a, hipStream_t stream);
@@ -228,8 +232,12 @@ struct CosArgs {
     int rule;
     float lam;
     int beam;
+    int32_t* best;          // [n(B-1)][K] row argmaxes and [n][kCntStride] pairs finished per
+    int* cnt;               // request (zero at launch): with both given, as for FinishArgs, one
+                            // wave per pair
 };
 hipError_t launch_cosine(const CosArgs& a, hipStream_t stream);
+bool cosine_by_pair(const CosArgs& a);
 
 // ---- paths (walk.hip)
 // Whether a request's scores (plus the path's small arrays) fit one

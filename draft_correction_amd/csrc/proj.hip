@@ -438,6 +438,8 @@ __global__ __launch_bounds__(kCT) void cand_kernel(CandArgs a) {
     const int64_t nodes = a.rows * a.K;
     const int64_t n0 = static_cast<int64_t>(blockIdx.x) * CR;
     const int M = static_cast<int>(min(static_cast<int64_t>(CR), nodes - n0));
+    if (a.zero_cnt && blockIdx.x == 0)   // the cosine launch's per-request counts
+        for (int i = tid; i < a.zero_n; i += kCT) a.zero_cnt[static_cast<int64_t>(i) * kCntStride] = 0;
     const int us = cand_us(R, a.vout ? a.dvec : 0);
     const int as = cand_as(R);
     float* ubuf = reinterpret_cast<float*>(smem_raw);                     // [CR][us]

@@ -590,6 +590,163 @@ __global__ __launch_bounds__(1024) void cosine_kernel(CosArgs a, int use_lds) {
     path_from_lds(a.rule, a.lam, a.beam, sS, a.ids, req, B, K, a.tokens, a.choice);
 }
 
+// ---- the per-request hand-off of the launches split by pair --------------
+// A wave counts itself into its request's counter once its stores have
+// completed (the stores of what the last wave reads are agent-scope atomics:
+// coherent across the chip's L2 caches without a cache write-back).  True in
+// the request's last wave.  The counters are zeroed by the launch before.
+__device__ __forceinline__ bool pair_last_of_request(int* cnt, int req, int B) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's stores are complete
+    asm volatile("" ::: "memory");
+    int done = 0;
+    if (lane_id() == 0)
+        done = __hip_atomic_fetch_add(cnt + static_cast<int64_t>(req) * kCntStride, 1, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+    return __shfl(done, 0, 64) == B - 2;
+}
+
+// The prefix-first walk of the request's last wave from the pairs' row
+// argmaxes best[pair][a] (K <= 16): lane q < B - 1 holds best[q][.] packed
+// four bits per entry, the chain k_1 = 0, k_{p+1} = best[p][k_p] follows by
+// readlane, and lanes s < B write choice and tokens.
+__device__ __forceinline__ void pair_walk(const int32_t* best, int req, int B, int K,
+                                          const int32_t* __restrict__ ids, int32_t* __restrict__ tokens,
+                                          int32_t* __restrict__ choice) {
+    const int l = lane_id();
+    uint64_t row = 0;
+    {
+        // all K loads issued before any is used (entries past K repeat the
+        // last, and are not read by the chain)
+        const int q = min(l, B - 2);
+        const int32_t* bq = best + (static_cast<int64_t>(req) * (B - 1) + q) * K;
+        int32_t bt[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) bt[j] = __hip_atomic_load(bq + min(j, K - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) row |= static_cast<uint64_t>(bt[j] & 15) << (4 * j);
+    }
+    const uint32_t lo = static_cast<uint32_t>(row), hi = static_cast<uint32_t>(row >> 32);
+    int k = 0, mych = 0;   // lane s < B keeps choice[s]
+    for (int q = 0; q + 1 < B; ++q) {
+        const uint32_t w = k < 8 ? __builtin_amdgcn_readlane(lo, q) : __builtin_amdgcn_readlane(hi, q);
+        k = (w >> (4 * (k & 7))) & 15;
+        if (l == q + 1) mych = k;
+    }
+    if (l < B) {
+        const int64_t s = static_cast<int64_t>(req) * B + l;
+        if (choice) choice[s] = mych;
+        tokens[s] = ids[s * K + mych];
+    }
+}
+
+// The Global-Sum, Geometric or beam path of the request's last wave: the
+// request's (B - 1) K^2 scores (stored with agent-scope atomics by the pairs'
+// waves) into LDS, 64 bits per load, all of a round's loads issued before any
+// is used, then the rule as the one-workgroup-per-request kernels run it.
+__device__ __forceinline__ void pair_rule(float* sS, const float* scores, int req, int B, int K, int rule, float lam,
+                                          int beam, const int32_t* __restrict__ ids, int32_t* __restrict__ tokens,
+                                          int32_t* __restrict__ choice) {
+    const int l = lane_id();
+    const int n2 = (B - 1) * K * K / 2;
+    const uint64_t* src2 = reinterpret_cast<const uint64_t*>(scores + static_cast<int64_t>(req) * (B - 1) * K * K);
+    uint64_t* s2 = reinterpret_cast<uint64_t*>(sS);
+    for (int i0 = 0; i0 < n2; i0 += 32 * kWave) {
+        uint64_t t[32];
+#pragma unroll
+        for (int u = 0; u < 32; ++u)
+            t[u] = __hip_atomic_load(src2 + min(i0 + u * kWave + l, n2 - 1), __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);   // clamped: in bounds
+#pragma unroll
+        for (int u = 0; u < 32; ++u)
+            if (i0 + u * kWave + l < n2) s2[i0 + u * kWave + l] = t[u];
+    }
+    wave_lds_sync();
+    path_from_lds(rule, lam, beam, sS, ids, req, B, K, tokens, choice);
+}
+
+// The cosine scores split by pair (K = 4, 8 or 16), as finish_pair_kernel
+// splits the MLP's: one wave per pair forms its 16 x 16 tile exactly as
+// cosine_kernel does (the same loads and fp32 MFMA sequence, then
+// l_{p+1}(b) + sigma * dot) and writes it; the request's last wave takes the
+// path.  A request's out and in vectors are thus read by B - 1 CUs at once
+// instead of one.  kWalk: the prefix-first walk from the rows' argmaxes
+// (lane l holds rows 4 (l / 16) + i of column l % 16, so a row's 16 columns
+// share a DPP row: four (value, index) reductions, ties to the lower
+// column); else the other rules over the scores read back into LDS.
+template <bool kWalk>
+__global__ __launch_bounds__(64) void cosine_pair_kernel(CosArgs a) {
+    extern __shared__ __attribute__((aligned(16))) float sS[];
+    const int B = a.B, K = a.K, dv = a.dvec, KK = K * K;
+    const int pair = blockIdx.x;
+    const int req = pair / (B - 1), p = pair - req * (B - 1);
+    const int l = lane_id();
+    const int g = l >> 4, r16 = l & 15;
+    const int kper = dv / 4;
+    const int64_t tp = static_cast<int64_t>(req) * B + p, tq = tp + 1;
+    const float* orow = a.vout + (tp * K + min(r16, K - 1)) * dv + g * kper;  // clamped rows unused
+    const float* irow = a.vin + (tq * K + min(r16, K - 1)) * dv + g * kper;
+    float4 o4[8], i4[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int j = min(4 * u, kper - 4);
+        o4[u] = *reinterpret_cast<const float4*>(orow + j);
+        i4[u] = *reinterpret_cast<const float4*>(irow + j);
+    }
+    const float lb = a.vals[tq * K + min(r16, K - 1)];
+    // every load lands before the first MFMA (else the compiler sinks each
+    // pair of loads behind the break below: eight dependent round trips)
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+        asm volatile("" ::"v"(o4[u].x), "v"(o4[u].y), "v"(o4[u].z), "v"(o4[u].w), "v"(i4[u].x), "v"(i4[u].y),
+                     "v"(i4[u].z), "v"(i4[u].w));
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        if (4 * u >= kper) break;
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(o4[u].x, i4[u].x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(o4[u].y, i4[u].y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(o4[u].z, i4[u].z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(o4[u].w, i4[u].w, acc, 0, 0, 0);
+    }
+    // lane l holds D[4g + i][r16]: predecessor 4g + i, successor r16
+    const bool col = r16 < K;
+    float sv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sv[i] = r16 < a.m ? lb + a.sigma * acc[i] : -INFINITY;
+    float* srow = a.scores + static_cast<int64_t>(pair) * KK;
+    if (!kWalk) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (col && 4 * g + i < K)
+                __hip_atomic_store(reinterpret_cast<uint32_t*>(srow) + (4 * g + i) * K + r16, __float_as_uint(sv[i]),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (!pair_last_of_request(a.cnt, req, B)) return;
+        pair_rule(sS, a.scores, req, B, K, a.rule, a.lam, a.beam, a.ids, a.tokens, a.choice);
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (col && 4 * g + i < K) srow[(4 * g + i) * K + r16] = sv[i];
+        float bv = col ? sv[i] : -INFINITY;
+        int bi = col ? r16 : 64;
+        auto take = [&](float ov, int oi) {
+            if (ov > bv || (ov == bv && oi < bi)) {
+                bv = ov;
+                bi = oi;
+            }
+        };
+        take(dpp_f<kDppXor1>(bv), __builtin_amdgcn_update_dpp(0, bi, kDppXor1, 0xF, 0xF, false));
+        take(dpp_f<kDppXor2>(bv), __builtin_amdgcn_update_dpp(0, bi, kDppXor2, 0xF, 0xF, false));
+        take(dpp_f<kDppHalfMirror>(bv), __builtin_amdgcn_update_dpp(0, bi, kDppHalfMirror, 0xF, 0xF, false));
+        take(dpp_f<kDppMirror>(bv), __builtin_amdgcn_update_dpp(0, bi, kDppMirror, 0xF, 0xF, false));
+        if (r16 == 0 && 4 * g + i < K)
+            __hip_atomic_store(a.best + static_cast<int64_t>(pair) * K + 4 * g + i, bi, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (!pair_last_of_request(a.cnt, req, B)) return;
+    pair_walk(a.best, req, B, K, a.ids, a.tokens, a.choice);
+}
+
 // One workgroup per request: S = l_{p+1}(b) + (sum of the hidden-block partial
 // Deltas in block order + b2) for all of the request's pairs, written to
 // `scores` (and kept in LDS when it fits); then, with tokens given (only when
@@ -742,30 +899,8 @@ __global__ __launch_bounds__(64) void finish_pair_kernel(FinishArgs a) {
             __hip_atomic_store(dst, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(dst + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's stores are complete
-        asm volatile("" ::: "memory");
-        int done = 0;
-        if (l == 0)
-            done = __hip_atomic_fetch_add(a.cnt + static_cast<int64_t>(req) * kCntStride, 1, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT);
-        if (__shfl(done, 0, 64) != B - 2) return;   // not the request's last pair
-        // the request's (B - 1) K^2 scores into LDS, 64 bits per load, all of
-        // a round's loads issued before any is used
-        const int n2 = (B - 1) * KK / 2;
-        const uint64_t* src2 = reinterpret_cast<const uint64_t*>(a.scores + static_cast<int64_t>(req) * (B - 1) * KK);
-        uint64_t* s2 = reinterpret_cast<uint64_t*>(sS);
-        for (int i0 = 0; i0 < n2; i0 += 32 * kWave) {
-            uint64_t t[32];
-#pragma unroll
-            for (int u = 0; u < 32; ++u)
-                t[u] = __hip_atomic_load(src2 + min(i0 + u * kWave + l, n2 - 1), __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);   // clamped: in bounds
-#pragma unroll
-            for (int u = 0; u < 32; ++u)
-                if (i0 + u * kWave + l < n2) s2[i0 + u * kWave + l] = t[u];
-        }
-        wave_lds_sync();
-        path_from_lds(a.rule, a.lam, a.beam, sS, a.ids, req, B, K, a.tokens, a.choice);
+        if (!pair_last_of_request(a.cnt, req, B)) return;
+        pair_rule(sS, a.scores, req, B, K, a.rule, a.lam, a.beam, a.ids, a.tokens, a.choice);
         return;
     }
     if (l < nv) reinterpret_cast<float4*>(a.scores + static_cast<int64_t>(pair) * KK)[l] = sv;
@@ -783,38 +918,8 @@ __global__ __launch_bounds__(64) void finish_pair_kernel(FinishArgs a) {
     }
     if (l < nv && b0 == 0)
         __hip_atomic_store(a.best + static_cast<int64_t>(pair) * K + aa, bi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's stores are complete
-    asm volatile("" ::: "memory");
-    int done = 0;
-    if (l == 0)
-        done = __hip_atomic_fetch_add(a.cnt + static_cast<int64_t>(req) * kCntStride, 1, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT);
-    if (__shfl(done, 0, 64) != B - 2) return;   // not the request's last pair
-    // the walk: lane q < B - 1 holds best[q][.] packed four bits per entry
-    uint64_t row = 0;
-    {
-        // all K loads issued before any is used (entries past K repeat the
-        // last, and are not read by the chain)
-        const int q = min(l, B - 2);
-        const int32_t* bq = a.best + (static_cast<int64_t>(req) * (B - 1) + q) * K;
-        int32_t bt[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) bt[j] = __hip_atomic_load(bq + min(j, K - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-        for (int j = 0; j < 16; ++j) row |= static_cast<uint64_t>(bt[j] & 15) << (4 * j);
-    }
-    const uint32_t lo = static_cast<uint32_t>(row), hi = static_cast<uint32_t>(row >> 32);
-    int k = 0, mych = 0;   // lane s < B keeps choice[s]
-    for (int q = 0; q + 1 < B; ++q) {
-        const uint32_t w = k < 8 ? __builtin_amdgcn_readlane(lo, q) : __builtin_amdgcn_readlane(hi, q);
-        k = (w >> (4 * (k & 7))) & 15;
-        if (l == q + 1) mych = k;
-    }
-    if (l < B) {
-        const int64_t s = static_cast<int64_t>(req) * B + l;
-        if (a.choice) a.choice[s] = mych;
-        a.tokens[s] = a.ids[s * K + mych];
-    }
+    if (!pair_last_of_request(a.cnt, req, B)) return;
+    pair_walk(a.best, req, B, K, a.ids, a.tokens, a.choice);
 }
 
 // z = hi + lo for each node row of the [hi | lo] layout.
@@ -852,7 +957,17 @@ static size_t path_lds_bytes(int B, int K) {
 
 bool path_fits_lds(int B, int K) { return path_lds_bytes(B, K) > 0; }
 
+bool cosine_by_pair(const CosArgs& a) {
+    return a.tokens && a.best && a.cnt && (reinterpret_cast<uintptr_t>(a.scores) & 7) == 0 &&
+           finish_split(a.B, a.K, a.rule);
+}
+
 hipError_t launch_cosine(const CosArgs& a, hipStream_t stream) {
+    if (cosine_by_pair(a)) {
+        const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.n) * (a.B - 1)));
+        if (a.rule == kPathGreedy) return launch(cosine_pair_kernel<true>, grid, 64, 0, stream, a);
+        return launch(cosine_pair_kernel<false>, grid, 64, static_cast<uint32_t>(path_lds_bytes(a.B, a.K)), stream, a);
+    }
     const size_t lds = path_lds_bytes(a.B, a.K);
     const int nt = (a.K + 15) / 16;
     const int jobs = (a.B - 1) * nt * nt;

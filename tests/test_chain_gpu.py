@@ -77,6 +77,20 @@ def test_chain_matches_run_rules_top_m(rule):
     assert (b["choice"][:, 1:] < 8).all()
 
 
+@pytest.mark.parametrize("rule", ["greedy", "global_sum", "beam"])
+def test_chain_matches_run_cosine(rule):
+    """The cosine variant: corrector_run forms the scores one wave per pair
+    and takes each request's path in the wave of its last pair; the split
+    calls form them one workgroup per request and take the paths in
+    corrector_walk.  Same scores and paths, bit for bit."""
+    _log("chain vs run cosine %s" % rule)
+    x = P.inputs("cosine", sigma=8.0, path_rule=rule, beam_width=3)
+    a = P.gpu_chain(x, n=6, first=5)
+    b = P.gpu_run(x, n=6, first=5)
+    for k in ("ids", "vals", "scores", "tokens", "choice"):
+        np.testing.assert_array_equal(a[k], b[k], err_msg="cosine %s: %s" % (rule, k))
+
+
 @pytest.mark.parametrize("fold", [False, True])
 def test_chain_cosine(fold):
     _log("chain cosine fold=%s" % fold)
