@@ -582,6 +582,21 @@ __global__ __launch_bounds__(kCT) void cand_kernel(CandArgs a) {
                     ubuf[(rt * 16 + 4 * (l >> 4) + i) * us + ct * 16 + (l & 15)] = acc[i];
         }
     }
+    // cosine variant: this wave's W_out and W_in fragments (column tile
+    // ct = wave of each map; dvec <= 16 kCW), issued now so that they arrive
+    // during the LayerNorm of z
+    constexpr int KSV = (2 * R + 31) / 32;
+    const int nvt = a.vout ? a.dvec / 16 : 0;
+    u32x4 bvm[2][KSV];
+    if (wave < nvt) {
+        const int kq = 8 * (l >> 4);
+#pragma unroll
+        for (int which = 0; which < 2; ++which) {
+            const uint16_t* wp = (which ? a.w_in : a.w_out) + static_cast<int64_t>(wave * 16 + (l & 15)) * R;
+#pragma unroll
+            for (int ks = 0; ks < KSV; ++ks) bvm[which][ks] = load16(wp + ((ks * 32 + kq) % R));
+        }
+    }
     __syncthreads();
 
     // ---- z = gamma * LN(y) + beta; stored as bf16 hi | lo (and kept in abuf)
@@ -608,28 +623,18 @@ __global__ __launch_bounds__(kCT) void cand_kernel(CandArgs a) {
     if (!a.vout) return;
     __syncthreads();
 
-    // ---- cosine variant: unit(W_out z) then unit(W_in z), one map at a time
+    // ---- cosine variant: unit(W_out z) then unit(W_in z), one map at a time;
+    // wave w < dvec / 16 forms column tile w of the map over every row tile
     const int dv = a.dvec;
-    const int nvt = dv / 16;
-    for (int which = 0; which < 2; ++which) {
-        // per column tile of the map: its W fragments loaded once, before the
-        // first MFMA, then every row tile of the group
-        constexpr int KSV = (2 * R + 31) / 32;
-        const uint16_t* wmap = which ? a.w_in : a.w_out;
-        for (int ct = wave; ct < nvt; ct += kCW) {
-            u32x4 bv[KSV];
-            {
-                const uint16_t* wp = wmap + static_cast<int64_t>(ct * 16 + (l & 15)) * R;
-                const int kq = 8 * (l >> 4);
 #pragma unroll
-                for (int ks = 0; ks < KSV; ++ks) bv[ks] = load16(wp + ((ks * 32 + kq) % R));
-            }
+    for (int which = 0; which < 2; ++which) {
+        if (wave < nvt) {
             for (int rt = 0; rt < nrt; ++rt) {
-                const f32x4 acc = mfma_hilo_tile_w<R>(abuf + rt * 16 * as, as, M - rt * 16, bv);
+                const f32x4 acc = mfma_hilo_tile_w<R>(abuf + rt * 16 * as, as, M - rt * 16, bvm[which]);
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     if (CR % 16 == 0 || rt * 16 + 4 * (l >> 4) + i < CR)   // a tile's rows past the group (CR = 4, 8) are not kept
-                        ubuf[(rt * 16 + 4 * (l >> 4) + i) * us + ct * 16 + (l & 15)] = acc[i];
+                        ubuf[(rt * 16 + 4 * (l >> 4) + i) * us + wave * 16 + (l & 15)] = acc[i];
             }
         }
         __syncthreads();
