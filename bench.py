@@ -125,6 +125,8 @@ def algorithmic_work(cfg: dict, n: int) -> dict:
     # candidates on MFMA: 2 K h r multiply-adds per pair, small next to these)
     w["mlp"] = dict(bound="alu", gelu=pairs * K * ms * h, flops=2 * pairs * K * ms * h,
                     per_unit=h, units=pairs * K * ms, unit="transition (h GELU evaluations)")
+    # few pairs: the finishing step and the walk run in the MLP's launch
+    w["mlp_walk"] = dict(w["mlp"])
     w["cosine"] = w["cosine_walk"] = w["cosine_viterbi"] = w["cosine_beam"] = dict(
         bound="hbm", bytes=pairs * 2 * K * cfg["dvec"] * 4, per_unit=2 * K * cfg["dvec"] * 4, units=pairs, unit="pair")
     w["walk"] = dict(bound="hbm", bytes=n * (B - 1) * K * 4, per_unit=(B - 1) * K * 4, units=n,
@@ -511,7 +513,8 @@ def main():
         if ent and tr.get("source_hash") == kernel_source_hash() and tr.get("workload") == args.workload:
             traffic = ent.get("bytes_per_launch")
     roof = roofline_of(work, dom, avg[dom], traffic)
-    roof_mlp = roofline_of(work, "mlp", avg["mlp"]) if "mlp" in avg else None
+    mk = "mlp" if "mlp" in avg else ("mlp_walk" if "mlp_walk" in avg else None)
+    roof_mlp = roofline_of(work, mk, avg[mk]) if mk else None
     kernels = kernel_table(work, avg)
 
     # ---- batch 1 (the pages' concurrency-1 serving point), same run

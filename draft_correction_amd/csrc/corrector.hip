@@ -104,7 +104,9 @@ Layout layout(const corrector_desc& d, int32_t n) {
     L.mlp_part = take(mlp ? sizeof(float) * pairs * (p16 ? d.mlp_hidden / 16 : mlp_blocks(d.mlp_hidden)) * d.k * d.k
                           : 0);
     L.best = take(split ? sizeof(int32_t) * pairs * d.k : 0);
-    L.cnt = take(split ? sizeof(int) * kCntStride * n : 0);
+    // per-request counts, then (for the MLP launch that also finishes and
+    // walks) per-pair counts, each on a 128-byte line of its own
+    L.cnt = take(split ? sizeof(int) * kCntStride * (n + pairs) : 0);
     L.vout = take(cos ? sizeof(float) * rows * d.k * d.d_vec : 0);
     L.vin = take(cos ? sizeof(float) * rows * d.k * d.d_vec : 0);
     L.scores = take(sizeof(float) * pairs * d.k * d.k);
@@ -332,8 +334,28 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
     // the cosine launch split by pair counts its pairs per request; the
     // candidate launch zeroes the counts
     const bool cos_split = cos && tokens && d.slots > 1 && finish_split(d.slots, d.k, d.path_rule);
-    ca.zero_cnt = cos_split ? at<int>(ws, L.cnt) : nullptr;
-    ca.zero_n = n;
+    // the MLP variant's finishing step and walk inside the 16-unit MLP launch
+    // (the walk, few pairs, and the finishing step splitting by pair): it
+    // counts blocks per pair and pairs per request, zeroed by the candidate
+    // launch
+    const int64_t npairs = static_cast<int64_t>(n) * (d.slots - 1);
+    bool mlp_walk = false;
+    if (!cos && tokens && d.slots > 1 && d.path_rule == CORR_PATH_GREEDY && d.mlp_hidden % 16 == 0 &&
+        npairs * (d.mlp_hidden / 16) <= kMlp16MaxGroups && path_fits_lds(d.slots, d.k)) {
+        FinishArgs pf{};
+        pf.part = at<float>(ws, L.mlp_part);
+        pf.vals = vals;
+        pf.B = d.slots;
+        pf.K = d.k;
+        pf.scores = scores;
+        pf.tokens = tokens;
+        pf.rule = d.path_rule;
+        pf.best = at<int32_t>(ws, L.best);
+        pf.cnt = at<int>(ws, L.cnt);
+        mlp_walk = finish_by_pair(pf);   // implies the layout holds best and the counts
+    }
+    ca.zero_cnt = cos_split || mlp_walk ? at<int>(ws, L.cnt) : nullptr;
+    ca.zero_n = mlp_walk ? static_cast<int>(n + npairs) : n;
     q("cand", [&] { return launch_cand(ca, q.s); });
     if (d.slots < 2) {
         if (tokens) q(path_name(h), [&] { return launch_path_rule(h, scores, ids, n, tokens, choice, q.s); });
@@ -382,6 +404,20 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
         m.w2 = w.w2;
         m.part = at<float>(ws, L.mlp_part);
         m.m = succ_m(d);
+        if (mlp_walk) {
+            m.units16 = 1;
+            m.fin_walk = 1;
+            m.rcnt = at<int>(ws, L.cnt);
+            m.pcnt = m.rcnt + static_cast<int64_t>(n) * kCntStride;
+            m.b2 = w.b2;
+            m.scores = scores;
+            m.ids = ids;
+            m.tokens = tokens;
+            m.choice = choice;
+            m.best = at<int32_t>(ws, L.best);
+            q("mlp_walk", [&] { return launch_mlp(m, q.s); });
+            return;
+        }
         const bool split = tokens && finish_split(d.slots, d.k, d.path_rule);
         m.zero_cnt = split ? at<int>(ws, L.cnt) : nullptr;
         FinishArgs f{};

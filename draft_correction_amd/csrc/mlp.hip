@@ -23,6 +23,7 @@
 // in a fixed order, and no value is accumulated with atomics (they only
 // count): bit-reproducible.
 #include "common.h"
+#include "handoff.h"
 #include "kernels.h"
 
 namespace corr {
@@ -699,7 +700,13 @@ __global__ __launch_bounds__(kWsThreads, 1) void mlp_ws_kernel(MlpArgs a) {
 // first level and writes (q0 + q1) of its sixteen units, and the finishing
 // step adds the four of a 64-unit block in the same tree.  The scores are
 // therefore identical to the ws kernel's.
-template <int R>
+// kFin: the finishing step and the walk in the same launch (MlpArgs
+// fin_walk): the partials go out as agent-scope atomic stores, the last of a
+// pair's workgroups reads them back the same way and forms the pair's scores
+// and row argmaxes as finish_pair_kernel does (one score per thread; a row's
+// K columns share a DPP row, quad or half-row), and the last pair of a
+// request walks.
+template <int R, bool kFin>
 __global__ __launch_bounds__(256) void mlp_pair16_kernel(MlpArgs a) {
     constexpr int KMAX = 16;
     constexpr int KS = 2 * R / 32;              // 32-wide k-steps over [hi | lo]
@@ -709,8 +716,9 @@ __global__ __launch_bounds__(256) void mlp_pair16_kernel(MlpArgs a) {
     __shared__ float cps[16];
     __shared__ float lv[2 * KMAX];
     __shared__ __attribute__((aligned(16))) float w2s[16];
+    __shared__ int s_count;
     const int tid = threadIdx.x, l = tid & 63, wave = tid >> 6;
-    if (a.zero_cnt && blockIdx.x == 0)           // the finishing launch's per-request counts
+    if (!kFin && a.zero_cnt && blockIdx.x == 0)  // the finishing launch's per-request counts
         for (int i = tid; i < a.n; i += 256) a.zero_cnt[static_cast<int64_t>(i) * kCntStride] = 0;
     const int B = a.B, K = a.K;
     const int nb = a.h / 16;                     // blocks of 16 units (h is a multiple of 16)
@@ -822,9 +830,77 @@ __global__ __launch_bounds__(256) void mlp_pair16_kernel(MlpArgs a) {
     w += dpp_f<kDppXor1>(w);
     if (tid < T && q == 0) {
         float* out = a.part + (static_cast<int64_t>(pair) * nb + blk) * K * K + static_cast<int>(__umul24(aa, K)) + bb;
-        out[0] = v;
-        if (two) out[1] = w;
+        if (kFin) {
+            __hip_atomic_store(reinterpret_cast<uint32_t*>(out), __float_as_uint(v), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            if (two)
+                __hip_atomic_store(reinterpret_cast<uint32_t*>(out) + 1, __float_as_uint(w), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            out[0] = v;
+            if (two) out[1] = w;
+        }
     }
+    if (!kFin) return;
+    // ---- the pair's last workgroup: its scores and row argmaxes
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's stores are complete
+    __syncthreads();
+    if (tid == 0)
+        s_count = __hip_atomic_fetch_add(a.pcnt + static_cast<int64_t>(pair) * kCntStride, 1, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (s_count != nb - 1) return;        // another block of the pair is still running
+    const int KK = K * K;
+    if (wave * 64 < KK) {                 // whole waves: the row reductions below use DPP
+        const int e = min(tid, KK - 1);   // threads past K^2 repeat the last score (not stored)
+        const int ra = e / K, cb = e - ra * K;
+        const float* src = a.part + static_cast<int64_t>(pair) * nb * KK + e;
+        // 16-unit partials: a 64-unit block's value is (P0 + P1) + (P2 + P3),
+        // a missing one counting as +0; the blocks then in order
+        float u[4 * kMaxMlpBlocks];
+#pragma unroll
+        for (int b = 0; b < 4 * kMaxMlpBlocks; ++b)
+            u[b] = b < nb ? __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t*>(src + b * KK),
+                                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+                          : 0.f;
+        const float lvb = a.vals[(t0 + 1) * K + cb];
+        float t4[kMaxMlpBlocks];
+#pragma unroll
+        for (int g = 0; g < kMaxMlpBlocks; ++g) t4[g] = (u[4 * g] + u[4 * g + 1]) + (u[4 * g + 2] + u[4 * g + 3]);
+        const int nb64 = (nb + 3) / 4;
+        float acc = t4[0];
+#pragma unroll
+        for (int g = 1; g < kMaxMlpBlocks; ++g)
+            if (g < nb64) acc += t4[g];
+        float sv = lvb + (acc + a.b2[0]);
+        if (cb >= a.m) sv = -INFINITY;    // successors b >= m are not scored
+        if (tid < KK) a.scores[static_cast<int64_t>(pair) * KK + e] = sv;
+        // row ra's argmax over its K lanes, ties to the lower index
+        float bv = tid < KK ? sv : -INFINITY;
+        int bi = tid < KK ? cb : 64;
+        auto take = [&](float ov, int oi) {
+            if (ov > bv || (ov == bv && oi < bi)) {
+                bv = ov;
+                bi = oi;
+            }
+        };
+        take(dpp_f<kDppXor1>(bv), __builtin_amdgcn_update_dpp(0, bi, kDppXor1, 0xF, 0xF, false));
+        take(dpp_f<kDppXor2>(bv), __builtin_amdgcn_update_dpp(0, bi, kDppXor2, 0xF, 0xF, false));
+        if (K > 4)
+            take(dpp_f<kDppHalfMirror>(bv), __builtin_amdgcn_update_dpp(0, bi, kDppHalfMirror, 0xF, 0xF, false));
+        if (K > 8) take(dpp_f<kDppMirror>(bv), __builtin_amdgcn_update_dpp(0, bi, kDppMirror, 0xF, 0xF, false));
+        if (tid < KK && cb == 0)
+            __hip_atomic_store(a.best + static_cast<int64_t>(pair) * K + ra, bi, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's stores are complete
+    __syncthreads();
+    if (tid == 0)
+        s_count = __hip_atomic_fetch_add(a.rcnt + static_cast<int64_t>(req) * kCntStride, 1, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (s_count != B - 2 || wave != 0) return;   // not the request's last pair
+    pair_walk(a.best, req, B, K, a.ids, a.tokens, a.choice);
 }
 
 }  // namespace
@@ -868,11 +944,23 @@ hipError_t launch_mlp(const MlpArgs& a, hipStream_t stream) {
     if (a.units16) {
         if (a.K > 16 || a.h % 16) return hipErrorInvalidValue;
         const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.n) * (a.B - 1) * (a.h / 16)));
+        if (a.fin_walk) {
+            if ((a.K != 4 && a.K != 8 && a.K != 16) || a.zero_cnt || !a.pcnt || !a.rcnt || !a.best || !a.tokens ||
+                !a.scores)
+                return hipErrorInvalidValue;
+            switch (a.r) {
+                case 16: return launch(mlp_pair16_kernel<16, true>, grid, 256, 0, stream, a);
+                case 32: return launch(mlp_pair16_kernel<32, true>, grid, 256, 0, stream, a);
+                case 64: return launch(mlp_pair16_kernel<64, true>, grid, 256, 0, stream, a);
+                case 128: return launch(mlp_pair16_kernel<128, true>, grid, 256, 0, stream, a);
+                default: return hipErrorInvalidValue;
+            }
+        }
         switch (a.r) {
-            case 16: return launch(mlp_pair16_kernel<16>, grid, 256, 0, stream, a);
-            case 32: return launch(mlp_pair16_kernel<32>, grid, 256, 0, stream, a);
-            case 64: return launch(mlp_pair16_kernel<64>, grid, 256, 0, stream, a);
-            case 128: return launch(mlp_pair16_kernel<128>, grid, 256, 0, stream, a);
+            case 16: return launch(mlp_pair16_kernel<16, false>, grid, 256, 0, stream, a);
+            case 32: return launch(mlp_pair16_kernel<32, false>, grid, 256, 0, stream, a);
+            case 64: return launch(mlp_pair16_kernel<64, false>, grid, 256, 0, stream, a);
+            case 128: return launch(mlp_pair16_kernel<128, false>, grid, 256, 0, stream, a);
             default: return hipErrorInvalidValue;
         }
     }
