@@ -334,14 +334,12 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
     // the cosine launch split by pair counts its pairs per request; the
     // candidate launch zeroes the counts
     const bool cos_split = cos && tokens && d.slots > 1 && finish_split(d.slots, d.k, d.path_rule);
-    // the MLP variant's finishing step and walk inside the 16-unit MLP launch
-    // (the walk, few pairs, and the finishing step splitting by pair): it
-    // counts blocks per pair and pairs per request, zeroed by the candidate
-    // launch
+    // the MLP variant's finishing step and walk inside the MLP launch (the
+    // walk, with the finishing step splitting by pair): it counts blocks per
+    // pair and pairs per request, zeroed by the candidate launch
     const int64_t npairs = static_cast<int64_t>(n) * (d.slots - 1);
     bool mlp_walk = false;
-    if (!cos && tokens && d.slots > 1 && d.path_rule == CORR_PATH_GREEDY && d.mlp_hidden % 16 == 0 &&
-        npairs * (d.mlp_hidden / 16) <= kMlp16MaxGroups && path_fits_lds(d.slots, d.k)) {
+    if (!cos && tokens && d.slots > 1 && d.path_rule == CORR_PATH_GREEDY && path_fits_lds(d.slots, d.k)) {
         FinishArgs pf{};
         pf.part = at<float>(ws, L.mlp_part);
         pf.vals = vals;
@@ -405,7 +403,8 @@ void enqueue_score(Seq& q, const corrector* h, const Layout& L, int32_t n, const
         m.part = at<float>(ws, L.mlp_part);
         m.m = succ_m(d);
         if (mlp_walk) {
-            m.units16 = 1;
+            // few pairs: one workgroup per (pair, 16 units), as below
+            m.units16 = npairs * (d.mlp_hidden / 16) <= kMlp16MaxGroups ? 1 : 0;
             m.fin_walk = 1;
             m.rcnt = at<int>(ws, L.cnt);
             m.pcnt = m.rcnt + static_cast<int64_t>(n) * kCntStride;

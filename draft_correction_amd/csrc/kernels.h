@@ -170,12 +170,12 @@ struct MlpArgs {
                             // (for finish_pair_kernel)
     int units16;            // K <= 16: one workgroup per (pair, 16 units); part then holds
                             // [pairs][h/16][K][K] partials, each the first level of a 64-unit block's sum
-    // With units16 and fin_walk set, the finishing step and the prefix-first
-    // walk run in the same launch: the last of a pair's h/16 workgroups (by
-    // pcnt[pair * kCntStride]) forms the pair's scores exactly as
-    // finish_pair_kernel does and its rows' argmaxes (best), and the last pair
-    // of a request (by rcnt[req * kCntStride]) walks.  The launch before zeroes
-    // both counts; zero_cnt must then be null.
+    // With fin_walk set (K = 4, 8 or 16), the finishing step and the
+    // prefix-first walk run in the same launch: the last of a pair's block
+    // workgroups (by pcnt[pair * kCntStride]) forms the pair's scores exactly
+    // as finish_pair_kernel does and its rows' argmaxes (best), and the last
+    // pair of a request (by rcnt[req * kCntStride]) walks.  The launch before
+    // zeroes both counts; zero_cnt must then be null.
     int fin_walk;
     int* pcnt;
     int* rcnt;

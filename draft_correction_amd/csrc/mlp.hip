@@ -349,7 +349,14 @@ __device__ __forceinline__ void spin_until(lds_counter* c, int target) {
 }
 __device__ __forceinline__ lds_counter* as_lds(int* p) { return (lds_counter*)(p); }
 
-template <int R>
+// kFin: the finishing step and the walk in the same launch (MlpArgs
+// fin_walk): the consumers store their partials with agent-scope atomic
+// stores; once the workgroup's run is done (one barrier), wave i counts pair
+// i of the run into the pair's counter, and the last of the pair's nj block
+// workgroups forms its scores, row argmaxes and count as finish_pair_kernel
+// does (with agent-scope loads of the partials); the request's last pair
+// walks.
+template <int R, bool kFin>
 __global__ __launch_bounds__(kWsThreads, 1) void mlp_ws_kernel(MlpArgs a) {
     constexpr int KMAX = 16;
     constexpr int KS = 2 * R / 32;              // 32-wide k-steps over [hi | lo]
@@ -373,7 +380,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void mlp_ws_kernel(MlpArgs a) {
     __shared__ int cpn[kMaxRun];                // consumer waves done with each pair's c_p (4 when formed)
 
     const int tid = threadIdx.x, l = tid & 63, wave = tid >> 6;
-    if (a.zero_cnt && blockIdx.x == 0)   // the finishing launch's per-request counts
+    if (!kFin && a.zero_cnt && blockIdx.x == 0)   // the finishing launch's per-request counts
         for (int i = tid; i < a.n; i += kWsThreads) a.zero_cnt[static_cast<int64_t>(i) * kCntStride] = 0;
     const int B = a.B, K = a.K, h = a.h;
     const int nj = (h + kJB - 1) / kJB;
@@ -674,8 +681,15 @@ __global__ __launch_bounds__(kWsThreads, 1) void mlp_ws_kernel(MlpArgs a) {
                 v += dpp_f<kDppHalfMirror>(v);
                 w += dpp_f<kDppHalfMirror>(w);
                 if (to[k] < (1 << 30)) {   // the group's first lane stores
-                    out[to[k]] = v;
-                    if (two) out[to[k] + 1] = w;
+                    if (kFin) {
+                        uint32_t* o = reinterpret_cast<uint32_t*>(out + to[k]);
+                        __hip_atomic_store(o, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        if (two)
+                            __hip_atomic_store(o + 1, __float_as_uint(w), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    } else {
+                        out[to[k]] = v;
+                        if (two) out[to[k] + 1] = w;
+                    }
                 }
             }
             // this wave is done reading the buffer
@@ -684,6 +698,22 @@ __global__ __launch_bounds__(kWsThreads, 1) void mlp_ws_kernel(MlpArgs a) {
             if (l == 0) atomicAdd(&freed[slot], 1);
             c = step(c);
         }
+    }
+    if (!kFin) return;
+    // ---- the run's pairs counted in; each pair's last block workgroup
+    // finishes it (every wave of both roles reaches this barrier: every wait
+    // above is bounded)
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's partial stores have completed
+    __syncthreads();
+    for (int i = wave; i < n; i += kWsThreads / 64) {
+        const int pair = q_lo + i;
+        int done = 0;
+        if (l == 0)
+            done = __hip_atomic_fetch_add(a.pcnt + static_cast<int64_t>(pair) * kCntStride, 1, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+        if (__shfl(done, 0, 64) != nj - 1) continue;   // another block of the pair is still running
+        const PairRow4 r = pair_scores4<true>(a.part, nj, 0, a.m, a.vals, a.b2[0], B, K, pair);
+        pair_walk_finish(r, a.scores, a.best, a.rcnt, a.ids, a.tokens, a.choice, B, K, pair);
     }
 }
 
@@ -928,7 +958,9 @@ hipError_t launch_mlp_r(const MlpArgs& a, hipStream_t stream) {
         int64_t per = kMlpGrid / nj;
         if (per * kMaxRun < pairs) per = (pairs + kMaxRun - 1) / kMaxRun;   // runs of at most kMaxRun pairs
         if (per > pairs) per = pairs;
-        return launch(mlp_ws_kernel<R>, dim3(static_cast<unsigned>(per * nj)), kWsThreads, 0, stream, a);
+        if (a.fin_walk)
+            return launch(mlp_ws_kernel<R, true>, dim3(static_cast<unsigned>(per * nj)), kWsThreads, 0, stream, a);
+        return launch(mlp_ws_kernel<R, false>, dim3(static_cast<unsigned>(per * nj)), kWsThreads, 0, stream, a);
     }
     // one workgroup per (group of kMlpPairs pairs, block); groups rounded up to
     // eight so that the blocks of a group share an XCD
@@ -941,13 +973,15 @@ hipError_t launch_mlp_r(const MlpArgs& a, hipStream_t stream) {
 
 hipError_t launch_mlp(const MlpArgs& a, hipStream_t stream) {
     if (a.B < 2 || a.n < 1) return hipSuccess;
+    if (a.fin_walk && ((a.K != 4 && a.K != 8 && a.K != 16) || a.zero_cnt || !a.pcnt || !a.rcnt || !a.best ||
+                       !a.tokens || !a.scores ||
+                       ((reinterpret_cast<uintptr_t>(a.scores) | reinterpret_cast<uintptr_t>(a.vals) |
+                         reinterpret_cast<uintptr_t>(a.part)) & 15)))
+        return hipErrorInvalidValue;
     if (a.units16) {
         if (a.K > 16 || a.h % 16) return hipErrorInvalidValue;
         const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.n) * (a.B - 1) * (a.h / 16)));
         if (a.fin_walk) {
-            if ((a.K != 4 && a.K != 8 && a.K != 16) || a.zero_cnt || !a.pcnt || !a.rcnt || !a.best || !a.tokens ||
-                !a.scores)
-                return hipErrorInvalidValue;
             switch (a.r) {
                 case 16: return launch(mlp_pair16_kernel<16, true>, grid, 256, 0, stream, a);
                 case 32: return launch(mlp_pair16_kernel<32, true>, grid, 256, 0, stream, a);

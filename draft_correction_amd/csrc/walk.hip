@@ -808,46 +808,16 @@ __global__ __launch_bounds__(64) void finish_pair_kernel(FinishArgs a) {
     extern __shared__ __attribute__((aligned(16))) float sS[];
     const int B = a.B, K = a.K, KK = K * K;
     const int pair = blockIdx.x;
-    const int req = pair / (B - 1), p = pair - req * (B - 1);
+    const int req = pair / (B - 1);
     const int l = lane_id();
-    const int nv = KK / 4;                    // float4 of the pair: 4, 16 or 64
-    const int i4 = min(l, nv - 1);            // lanes past nv repeat the last (not stored)
-    const int e = 4 * i4, aa = e / K, b0 = e - aa * K;
-    const float b2 = a.b2[0];
-    const float* src = a.part + static_cast<int64_t>(pair) * a.nblk * KK + e;
-    float4 t[kMaxMlpBlocks];
-    int nb64 = a.nblk;
-    if (a.sub) {
-        // 16-unit partials: a 64-unit block's value is (P0 + P1) + (P2 + P3),
-        // a missing one counting as +0 (as the 64-unit kernel's empty eighths)
-        nb64 = (a.nblk + 3) / 4;
-        float4 u[4 * kMaxMlpBlocks];
-#pragma unroll
-        for (int b = 0; b < 4 * kMaxMlpBlocks; ++b)
-            u[b] = b < a.nblk ? *reinterpret_cast<const float4*>(src + b * KK) : make_float4(0.f, 0.f, 0.f, 0.f);
-        auto add = [](float4 x, float4 y) { return make_float4(x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w); };
-#pragma unroll
-        for (int g = 0; g < kMaxMlpBlocks; ++g) t[g] = add(add(u[4 * g], u[4 * g + 1]), add(u[4 * g + 2], u[4 * g + 3]));
-    } else {
-#pragma unroll
-        for (int b = 0; b < kMaxMlpBlocks; ++b)
-            t[b] = *reinterpret_cast<const float4*>(src + (b < a.nblk ? b : a.nblk - 1) * KK);
-    }
-    const float4 lv = *reinterpret_cast<const float4*>(a.vals + (static_cast<int64_t>(req) * B + p + 1) * K + b0);
-    float4 acc = t[0];
-#pragma unroll
-    for (int b = 1; b < kMaxMlpBlocks; ++b)
-        if (b < nb64) acc = make_float4(acc.x + t[b].x, acc.y + t[b].y, acc.z + t[b].z, acc.w + t[b].w);
-    float4 sv = make_float4(lv.x + (acc.x + b2), lv.y + (acc.y + b2), lv.z + (acc.z + b2), lv.w + (acc.w + b2));
-    if (a.m < K)   // successors b >= m are not scored
-        sv = make_float4(b0 < a.m ? sv.x : -INFINITY, b0 + 1 < a.m ? sv.y : -INFINITY,
-                         b0 + 2 < a.m ? sv.z : -INFINITY, b0 + 3 < a.m ? sv.w : -INFINITY);
+    const PairRow4 r = pair_scores4<false>(a.part, a.nblk, a.sub, a.m, a.vals, a.b2[0], B, K, pair);
     if (!kWalk) {
         // read back by the request's last wave, on any XCD
+        const float4 sv = r.sv;
         uint64_t* dst = reinterpret_cast<uint64_t*>(a.scores + static_cast<int64_t>(pair) * KK) + 2 * l;
         const uint64_t lo = static_cast<uint64_t>(__float_as_uint(sv.x)) | static_cast<uint64_t>(__float_as_uint(sv.y)) << 32;
         const uint64_t hi = static_cast<uint64_t>(__float_as_uint(sv.z)) | static_cast<uint64_t>(__float_as_uint(sv.w)) << 32;
-        if (l < nv) {
+        if (l < r.nv) {
             __hip_atomic_store(dst, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(dst + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -855,23 +825,7 @@ __global__ __launch_bounds__(64) void finish_pair_kernel(FinishArgs a) {
         pair_rule(sS, a.scores, req, B, K, a.rule, a.lam, a.beam, a.ids, a.tokens, a.choice);
         return;
     }
-    if (l < nv) reinterpret_cast<float4*>(a.scores + static_cast<int64_t>(pair) * KK)[l] = sv;
-    // row aa's argmax: the lane's four in index order (strict compare), then
-    // across the K / 4 consecutive lanes of the row, ties to the lower index
-    float bv = sv.x;
-    int bi = b0;
-    if (sv.y > bv) { bv = sv.y; bi = b0 + 1; }
-    if (sv.z > bv) { bv = sv.z; bi = b0 + 2; }
-    if (sv.w > bv) { bv = sv.w; bi = b0 + 3; }
-    for (int sh = 1; sh < K / 4; sh <<= 1) {
-        const float ov = __shfl_xor(bv, sh, 64);
-        const int oi = __shfl_xor(bi, sh, 64);
-        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-    }
-    if (l < nv && b0 == 0)
-        __hip_atomic_store(a.best + static_cast<int64_t>(pair) * K + aa, bi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (!pair_last_of_request(a.cnt, req, B)) return;
-    pair_walk(a.best, req, B, K, a.ids, a.tokens, a.choice);
+    pair_walk_finish(r, a.scores, a.best, a.cnt, a.ids, a.tokens, a.choice, B, K, pair);
 }
 
 // z = hi + lo for each node row of the [hi | lo] layout.
