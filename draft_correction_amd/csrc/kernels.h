@@ -167,13 +167,13 @@ struct MlpArgs {
     float* part;            // [n*(B-1)][blocks][K][K] partial Delta per hidden-unit block (b < m written)
     int m;                  // successors scored per predecessor (b < m; 1..K)
     int* zero_cnt;          // K <= 16 and non-null: n counters (kCntStride apart) the launch sets to 0
-                            // (for finish_pair_kernel)
+                            // (for the per-pair finishing launch)
     int units16;            // K <= 16: one workgroup per (pair, 16 units); part then holds
                             // [pairs][h/16][K][K] partials, each the first level of a 64-unit block's sum
     // With fin_walk set (K = 4, 8 or 16), the finishing step and the
     // prefix-first walk run in the same launch: the last of a pair's block
     // workgroups (by pcnt[pair * kCntStride]) forms the pair's scores exactly
-    // as finish_pair_kernel does and its rows' argmaxes (best), and the last
+    // as the per-pair finishing step does and its rows' argmaxes (best), and the last
     // pair of a request (by rcnt[req * kCntStride]) walks.  The launch before
     // zeroes both counts; zero_cnt must then be null.
     int fin_walk;

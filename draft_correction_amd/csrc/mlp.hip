@@ -353,9 +353,9 @@ __device__ __forceinline__ lds_counter* as_lds(int* p) { return (lds_counter*)(p
 // fin_walk): the consumers store their partials with agent-scope atomic
 // stores; once the workgroup's run is done (one barrier), wave i counts pair
 // i of the run into the pair's counter, and the last of the pair's nj block
-// workgroups forms its scores, row argmaxes and count as finish_pair_kernel
-// does (with agent-scope loads of the partials); the request's last pair
-// walks.
+// workgroups forms its scores, row argmaxes and count with the per-pair
+// finishing code of handoff.h (agent-scope loads of the partials); the
+// request's last pair walks.
 template <int R, bool kFin>
 __global__ __launch_bounds__(kWsThreads, 1) void mlp_ws_kernel(MlpArgs a) {
     constexpr int KMAX = 16;
@@ -733,7 +733,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void mlp_ws_kernel(MlpArgs a) {
 // kFin: the finishing step and the walk in the same launch (MlpArgs
 // fin_walk): the partials go out as agent-scope atomic stores, the last of a
 // pair's workgroups reads them back the same way and forms the pair's scores
-// and row argmaxes as finish_pair_kernel does (one score per thread; a row's
+// and row argmaxes as the per-pair finishing code does (one score per thread; a row's
 // K columns share a DPP row, quad or half-row), and the last pair of a
 // request walks.
 template <int R, bool kFin>

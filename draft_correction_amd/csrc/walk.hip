@@ -616,8 +616,8 @@ __device__ __forceinline__ void pair_rule(float* sS, const float* scores, int re
     path_from_lds(rule, lam, beam, sS, ids, req, B, K, tokens, choice);
 }
 
-// The cosine scores split by pair (K = 4, 8 or 16), as finish_pair_kernel
-// splits the MLP's: one wave per pair forms its 16 x 16 tile exactly as
+// The cosine scores split by pair (K = 4, 8 or 16), as the MLP's finishing
+// step is split: one wave per pair forms its 16 x 16 tile exactly as
 // cosine_kernel does (the same loads and fp32 MFMA sequence, then
 // l_{p+1}(b) + sigma * dot) and writes it; the request's last wave takes the
 // path.  A request's out and in vectors are thus read by B - 1 CUs at once
@@ -783,27 +783,17 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a, int use_lds) 
     path_from_lds(a.rule, a.lam, a.beam, sS, a.ids, req, B, K, a.tokens, a.choice);
 }
 
-// The finishing step split by pair (K = 4, 8 or 16): one wave per pair forms
-// its K x K scores exactly as finish_kernel does (block partials in block
-// order, + b2, + l_{p+1}(b)) and writes them; the last wave of a request to
-// finish (by the request's count, which the MLP launch zeroed, one cache line
-// per request) then takes the request's path.  With the MLP's 16-unit
-// partials (a.sub) the wave first adds them four at a time in the 64-unit
-// form's tree.  A request's partials are thus read by B - 1 CUs at once
-// instead of one.
-//   - Prefix-first walk: each wave also takes the argmax of every row of its
-//     pair (ties to the lowest successor index) into best[pair][a]; the last
-//     wave follows the chain k_1 = 0, k_{p+1} = best[p][k_p].
-//   - Global-Sum, Geometric and beam rules: the last wave reads the request's
-//     scores back into LDS (dynamic, path_lds_bytes) and runs the rule there,
-//     as finish_kernel does.
-// The hand-off uses agent-scope atomic stores and loads (coherent across the
-// chip's L2 caches without a cache write-back) for what the last wave reads
-// (best, or the scores) and for the count, the stores completed before the
-// count is taken.
-// kWalk: the instance for the prefix-first walk (a.rule greedy), else the
-// one for the other rules.
-template <bool kWalk>
+// The finishing step split by pair for the Global-Sum, Geometric and beam
+// rules (K = 4, 8 or 16): one wave per pair forms its K x K scores exactly as
+// finish_kernel does (block partials in block order, + b2, + l_{p+1}(b); with
+// the MLP's 16-unit partials (a.sub) first added four at a time in the
+// 64-unit form's tree) and stores them with agent-scope atomic stores; the
+// last wave of a request to finish (by the request's count, which the MLP
+// launch zeroed, one cache line per request) reads the request's scores back
+// into LDS (dynamic, path_lds_bytes) and runs the rule there, as
+// finish_kernel does.  A request's partials are thus read by B - 1 CUs at
+// once instead of one.  (With the prefix-first walk the same per-pair step
+// runs inside the MLP's launch.)
 __global__ __launch_bounds__(64) void finish_pair_kernel(FinishArgs a) {
     extern __shared__ __attribute__((aligned(16))) float sS[];
     const int B = a.B, K = a.K, KK = K * K;
@@ -811,21 +801,17 @@ __global__ __launch_bounds__(64) void finish_pair_kernel(FinishArgs a) {
     const int req = pair / (B - 1);
     const int l = lane_id();
     const PairRow4 r = pair_scores4<false>(a.part, a.nblk, a.sub, a.m, a.vals, a.b2[0], B, K, pair);
-    if (!kWalk) {
-        // read back by the request's last wave, on any XCD
-        const float4 sv = r.sv;
-        uint64_t* dst = reinterpret_cast<uint64_t*>(a.scores + static_cast<int64_t>(pair) * KK) + 2 * l;
-        const uint64_t lo = static_cast<uint64_t>(__float_as_uint(sv.x)) | static_cast<uint64_t>(__float_as_uint(sv.y)) << 32;
-        const uint64_t hi = static_cast<uint64_t>(__float_as_uint(sv.z)) | static_cast<uint64_t>(__float_as_uint(sv.w)) << 32;
-        if (l < r.nv) {
-            __hip_atomic_store(dst, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(dst + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        if (!pair_last_of_request(a.cnt, req, B)) return;
-        pair_rule(sS, a.scores, req, B, K, a.rule, a.lam, a.beam, a.ids, a.tokens, a.choice);
-        return;
+    // read back by the request's last wave, on any XCD
+    const float4 sv = r.sv;
+    uint64_t* dst = reinterpret_cast<uint64_t*>(a.scores + static_cast<int64_t>(pair) * KK) + 2 * l;
+    const uint64_t lo = static_cast<uint64_t>(__float_as_uint(sv.x)) | static_cast<uint64_t>(__float_as_uint(sv.y)) << 32;
+    const uint64_t hi = static_cast<uint64_t>(__float_as_uint(sv.z)) | static_cast<uint64_t>(__float_as_uint(sv.w)) << 32;
+    if (l < r.nv) {
+        __hip_atomic_store(dst, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(dst + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    pair_walk_finish(r, a.scores, a.best, a.cnt, a.ids, a.tokens, a.choice, B, K, pair);
+    if (!pair_last_of_request(a.cnt, req, B)) return;
+    pair_rule(sS, a.scores, req, B, K, a.rule, a.lam, a.beam, a.ids, a.tokens, a.choice);
 }
 
 // z = hi + lo for each node row of the [hi | lo] layout.
@@ -903,9 +889,10 @@ bool finish_by_pair(const FinishArgs& a) {
 
 hipError_t launch_finish(const FinishArgs& a, hipStream_t stream) {
     if (finish_by_pair(a)) {
+        // the walk's per-pair step runs inside the MLP's launch (fin_walk)
+        if (a.rule == kPathGreedy) return hipErrorInvalidValue;
         const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.n) * (a.B - 1)));
-        if (a.rule == kPathGreedy) return launch(finish_pair_kernel<true>, grid, 64, 0, stream, a);
-        return launch(finish_pair_kernel<false>, grid, 64, static_cast<uint32_t>(path_lds_bytes(a.B, a.K)), stream, a);
+        return launch(finish_pair_kernel, grid, 64, static_cast<uint32_t>(path_lds_bytes(a.B, a.K)), stream, a);
     }
     if (a.sub) return hipErrorInvalidValue;   // 16-unit partials are finished by pair only
     const size_t lds = path_lds_bytes(a.B, a.K);
