@@ -61,6 +61,20 @@ def test_chain_matches_run_rules(name, rule):
         np.testing.assert_array_equal(a[k], b[k], err_msg="%s %s: %s" % (rule, name, k))
 
 
+def test_chain_matches_run_long_runs():
+    """80 requests at the batch-32 shape (V cut to 32768): 1200 pairs, so each
+    workgroup of the MLP launch runs 18 or 19 pairs and its waves count
+    several pairs each before the pairs' last block workgroups finish them and
+    the requests' last pairs walk.  Same scores and paths as the split calls,
+    bit for bit."""
+    _log("chain vs run, 80 requests")
+    x = P.inputs("b32", head="stress", n=80, V=32768)
+    a = P.gpu_chain(x)
+    b = P.gpu_run(x)
+    for k in ("ids", "vals", "scores", "tokens", "choice"):
+        np.testing.assert_array_equal(a[k], b[k], err_msg="80 requests: " + k)
+
+
 @pytest.mark.parametrize("rule", ["global_sum", "geometric", "beam"])
 def test_chain_matches_run_rules_top_m(rule):
     """The same comparison with only the first 8 successors of each pair
