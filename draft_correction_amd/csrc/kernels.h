@@ -220,11 +220,13 @@ struct FinishArgs {
     int32_t* best;          // [n(B-1)][K] row argmaxes and
     int* cnt;               // [n][kCntStride] pairs finished per request (zero at launch): with both
                             // given, K = 4, 8 or 16 and the scores fitting the path's LDS, the
-                            // launch runs one wave per pair (the request's last one takes the path)
+                            // work is split by pair (the request's last pair takes the path); for
+                            // the prefix-first walk that split runs inside the MLP's launch
+                            // (MlpArgs fin_walk), and launch_finish refuses it
 };
 hipError_t launch_finish(const FinishArgs& a, hipStream_t stream);
-// Whether launch_finish splits the work by pair for this shape and rule (it
-// then needs best and cnt), and whether it will for these arguments.
+// Whether the finishing step splits the work by pair for this shape and rule
+// (it then needs best and cnt), and whether it will for these arguments.
 bool finish_split(int B, int K, int rule);
 bool finish_by_pair(const FinishArgs& a);
 
