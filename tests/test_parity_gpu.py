@@ -59,12 +59,12 @@ def test_tiny_rep_widths(r):
     P.check_all(gpu, ora, "tiny/r=%d" % r)
 
 
-@pytest.mark.parametrize("K", [1, 5, 8, 13])
+@pytest.mark.parametrize("K", [1, 4, 5, 8, 13])
 def test_tiny_small_k(K):
     """K = 1 (one candidate per slot: every pair a single transition, the walk
     fixed), odd K below 16 (the last predecessor and successor tasks of the
-    K <= 16 MLP consumers cut short), and K = 8 (the per-pair finishing step
-    with rows of two lanes)."""
+    K <= 16 MLP consumers cut short), and K = 4 and 8 (the per-pair finishing
+    step with rows of one and two lanes)."""
     _log("tiny K=%d" % K)
     x = P.inputs("tiny", head="stress", K=K, n=2, B=4)
     gpu = P.gpu_run(x)
@@ -141,6 +141,26 @@ def test_b32(head):
     _log("  walk steps %d exempt %d moved %d" % (steps, exempt, moved))
     if head == "stress":
         assert moved > steps // 10
+
+
+@pytest.mark.parametrize("K", [4, 8])
+def test_b32_small_k(K):
+    """K = 4 and 8 at the batch-32 shape over 8 blocks (112 pairs): the
+    warp-specialised MLP with each pair's finishing step and the request's
+    walk in its tail, on score rows of one and two lanes; each request run
+    alone (the per-(pair, 16 units) MLP form) gives the same bits."""
+    _log("b32 K=%d n=8" % K)
+    x = P.inputs("b32", head="stress", K=K)
+    gpu = P.gpu_run(x, n=8)
+    ora = P.oracle_run(x, n=8)
+    steps, exempt, moved = P.check_all(gpu, ora, "b32/K=%d" % K)
+    _log("  walk steps %d exempt %d moved %d" % (steps, exempt, moved))
+    assert moved > 0
+    for i in (0, 7):
+        one = P.gpu_run(x, n=1, first=i)
+        sub = P.select(gpu, i, 1)
+        for k in ("ids", "vals", "scores", "tokens", "choice", "z", "s", "g"):
+            np.testing.assert_array_equal(one[k], sub[k], err_msg="K=%d request %d alone: %s" % (K, i, k))
 
 
 @pytest.mark.parametrize("n,first", [(6, 5), (3, 20)])
