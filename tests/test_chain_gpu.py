@@ -112,3 +112,20 @@ def test_chain_cosine(fold):
     gpu = P.gpu_chain(x, n=4, first=9, fold=fold)
     ora = P.oracle_run(x, n=4, first=9)
     P.check_all(gpu, ora, "chain/cosine", variant="cosine")
+
+
+@pytest.mark.parametrize("variant,rule", [("b32", "greedy"), ("b32", "global_sum"), ("b32", "beam"),
+                                          ("cosine", "greedy"), ("cosine", "global_sum")])
+def test_chain_matches_run_k8(variant, rule):
+    """K = 8 (score rows of two lanes in the per-pair finishing waves) over 8
+    blocks, for both variants and the walk, Global-Sum and beam rules: the
+    run's per-pair forms and the split calls' per-request forms give the same
+    scores and paths, bit for bit."""
+    _log("chain vs run K=8 %s %s" % (variant, rule))
+    extra = dict(sigma=8.0) if variant == "cosine" else dict(head="stress")
+    x = P.inputs(variant, K=8, path_rule=rule, beam_width=3, **extra)
+    a = P.gpu_chain(x, n=8)
+    b = P.gpu_run(x, n=8)
+    for k in ("ids", "vals", "scores", "tokens", "choice"):
+        np.testing.assert_array_equal(a[k], b[k], err_msg="K=8 %s %s: %s" % (variant, rule, k))
+    assert (b["choice"] != 0).any()
