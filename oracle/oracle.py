@@ -236,7 +236,10 @@ def confidence(vals, logz) -> np.ndarray:
     vals = np.asarray(vals, dtype=np.float64)
     logz = np.asarray(logz, dtype=np.float64)
     K = vals.shape[-1]
-    logp = vals - logz[..., None]
+    # an infinite logit over an infinite log Z gives a NaN log-probability
+    # (inf - inf), as the definition does; numpy's warning is not needed
+    with np.errstate(invalid="ignore"):
+        logp = vals - logz[..., None]
     out = np.empty(vals.shape + (5,))
     out[..., 0] = logp
     out[..., 1] = np.exp(logp)

@@ -55,7 +55,7 @@ def check_softmax(ids, vals, logz, conf, want_ids, want_vals, want_logz, where="
     dl = logz_tol(want_logz)[..., None] + 2.0 ** -23 * np.abs(np.nan_to_num(want[..., 0], posinf=0, neginf=0))
     ok = np.isfinite(want[..., 0])
     np.testing.assert_array_equal(c[..., 0][~ok], want[..., 0][~ok], err_msg="log-prob (non-finite) " + where)
-    assert (np.abs(c[..., 0] - want[..., 0])[ok] <= dl[ok]).all(), "log-prob " + where
+    assert (np.abs(c[..., 0][ok] - want[..., 0][ok]) <= dl[ok]).all(), "log-prob " + where
     # probability: relative error of exp from the log-prob error, plus float32 rounding
     # (a probability of exactly 0, a -inf candidate, must be 0: its bound is 0,
     # not 0 * inf where log Z's bound is huge)
@@ -67,7 +67,7 @@ def check_softmax(ids, vals, logz, conf, want_ids, want_vals, want_logz, where="
     # gap: one float32 subtraction of two float32-exact logits
     g = want[..., 2]
     gm = np.isfinite(g)
-    assert (np.abs(c[..., 2] - g)[gm] <= 2.0 ** -23 * np.abs(g[gm])).all(), "gap " + where
+    assert (np.abs(c[..., 2][gm] - g[gm]) <= 2.0 ** -23 * np.abs(g[gm])).all(), "gap " + where
     np.testing.assert_array_equal(c[..., 2][~gm], g[~gm], err_msg="gap (non-finite) " + where)
     # rank: one correctly rounded float32 division; top flag exact
     np.testing.assert_allclose(c[..., 3], want[..., 3], rtol=2.0 ** -23, atol=0, err_msg="rank " + where)
