@@ -655,22 +655,32 @@ __global__ __launch_bounds__(256) void topk_partial_f32_kernel(
         for (int bit = 47; bit >= 0; --bit) {
             const uint64_t c = tc | (1ull << bit);
             int cnt = 0;
+            // the composites are formed again on every pass (hoisted out of
+            // the bit loop, they and their index halves would take about a
+            // hundred more registers): 0xFFFF - local = lb - (256 t + j)
+            uint32_t lb = 0xFFFFu - static_cast<uint32_t>(kEPV * l);
+            asm volatile("" : "+v"(lb));
 #pragma unroll
             for (int t = 0; t < kNV; ++t)
 #pragma unroll
                 for (int j = 0; j < kEPV; ++j) {
-                    const uint32_t local = static_cast<uint32_t>((t * kWave + l) * kEPV + j);
-                    cnt += popc64(ballot(((static_cast<uint64_t>(key_of_bits(raw[t][j])) << 16) | (0xFFFFu - local)) >= c));
+                    uint32_t x = raw[t][j];
+                    asm volatile("" : "+v"(x));
+                    const uint32_t inv = lb - static_cast<uint32_t>(t * kWave * kEPV + j);
+                    cnt += popc64(ballot(((static_cast<uint64_t>(key_of_bits(x)) << 16) | inv) >= c));
                 }
             if (cnt >= target) tc = c;
         }
+        uint32_t lb = 0xFFFFu - static_cast<uint32_t>(kEPV * l);
+        asm volatile("" : "+v"(lb));
 #pragma unroll
         for (int t = 0; t < kNV; ++t)
 #pragma unroll
             for (int j = 0; j < kEPV; ++j) {
-                const uint32_t local = static_cast<uint32_t>((t * kWave + l) * kEPV + j);
+                const uint32_t inv = lb - static_cast<uint32_t>(t * kWave * kEPV + j);
+                const uint32_t local = 0xFFFFu - inv;
                 const uint32_t k = key_of_bits(raw[t][j]);
-                const bool p = ((static_cast<uint64_t>(k) << 16) | (0xFFFFu - local)) >= tc && k > kKeyFloor;
+                const bool p = ((static_cast<uint64_t>(k) << 16) | inv) >= tc && k > kKeyFloor;
                 const uint64_t m = ballot(p);
                 const int pos = outn + prefix_count(m);
                 if (p && pos < K) part[obase + pos] = merge_comp(k, c0 + local);
